@@ -1,0 +1,59 @@
+"""CPU oracle for the SmolVLA action-expert denoising loop.
+
+TEST INFRASTRUCTURE ONLY.  Plain, slow, float64 numpy code that states what
+the denoiser computes, one query at a time, in the order the method does it.
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import it.  The GPU library never calls it and shares no code with it; the
+two meet only through the seeded inputs of the ``synth`` package.
+
+Sources (page title, then section):
+  * noeira docs "SmolVLA", Architecture: the expert has 16 layers of width
+    720, even layers self-attend and odd layers cross-attend to the VLM's
+    cached keys/values; 10 Euler steps from Gaussian noise at t = 1 toward
+    t = 0; chunk of 50; the prefix is computed once, the expert ten times;
+    the flow-matching path x_t = t*eps + (1 - t)*a with target eps - a; the
+    block attention mask (the prefix never sees the actions); 32-wide
+    padded action vectors.
+  * "Paper vs hardware 11: SmolVLA", What the paper claims: causal
+    self-attention over the chunk, cross-attention to the VLM keys/values,
+    conditional flow matching, chunk 50; What I ran: prefix overwrite of the
+    first d ~ 7 chunk rows at chunk boundaries.
+  * noeira docs "SmolVLA", Architecture table, language-model row:
+    grouped-query attention 15/5 heads of dim 64, RoPE, SwiGLU, RMSNorm
+    (the expert uses the same block family at width 720).
+  * CSDN "SmolVLA PyTorch official-like 精度排查过程与结论", sections 8 and 12:
+    K/V cache in bf16, Euler update and output in fp32, bf16 values used with
+    fp32 storage ("fake bf16").  The oracle decodes every bf16 input exactly
+    and computes in float64.
+
+Where the pages leave a step open, the reading taken (layer parity, RoPE
+pairing and theta, RMSNorm epsilon, time-embedding form, concat order, biases,
+mask semantics, schedule rounding, overwrite timing) is stated at the
+function that implements it.
+
+Pins (what fixes each function other than itself; all in tests/):
+  rms_norm ........ closed form on constant rows; torch.nn.functional.rms_norm
+  silu ............ closed values; torch.nn.functional.silu
+  rope ............ identity at position 0; unit-vector rotation closed form;
+                    norm preservation; scores depend only on position offset
+  time_embedding .. e(0) = [0..0, 1..1]; sin^2 + cos^2 = 1; quarter-period
+                    closed values
+  attention ....... float64 triple-loop brute force on tiny shapes; one valid
+                    key returns that V row; equal keys give the mean of V;
+                    torch scaled_dot_product_attention with GQA and a mask
+  expert layer .... composition of torch library routines (rms_norm, linear,
+                    scaled_dot_product_attention(enable_gqa), silu) with a
+                    complex-number rotary embedding
+  expert (whole) .. chunk causality, pad invariance (NaN pads), batch
+                    invariance, block-mask joint-pass equivalence, and
+                    degenerate-weight closed forms of the whole loop
+  schedule/Euler .. closed-form trajectories under stub velocity fields
+                    (constant, linear, straight flow-matching path)
+  overwrite ....... closed form under v = 0; fixed point on the straight path
+No function is left parity unpinned.
+"""
+from .expert import (  # noqa: F401
+    bf16_bits_to_float, decode_weights, rms_norm, silu, rope, time_embedding,
+    attention, embed, expert_layer, head, velocity, ExpertConfig,
+)
+from .flow import schedule, overwrite_rows, euler_denoise, denoise_query, denoise_batch  # noqa: F401
