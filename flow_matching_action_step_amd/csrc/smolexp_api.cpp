@@ -1,0 +1,715 @@
+// Host side of the smolexp C ABI: configuration and argument checks, the
+// weight store (bf16 -> exact fp16 re-encoding), the workspace, the launch
+// sequence of one denoising call, and HIP-graph capture and replay of it.
+#include "smolexp.h"
+#include "smolexp_internal.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+using namespace smolexp;
+
+namespace {
+
+struct Mat {
+  half_t* w = nullptr;
+  float scale = 1.f;  // real value = stored fp16 value * scale (a power of two)
+};
+
+struct LayerDev {
+  bool self_attn = false;
+  Mat qkv, o, gu, down;
+  float* g1 = nullptr;
+  float* g2 = nullptr;
+};
+
+// Everything that distinguishes one enqueued call from another.
+struct CallKey {
+  int velocity_mode;
+  int B, P, d;
+  float t_single;
+  const void* kv;
+  const uint8_t* mask;
+  const float* x_in;    // noise (denoise) or x (velocity)
+  float* out;           // out_actions (denoise) or out_v (velocity)
+  const float* prev;
+  float* vel;
+  float* st;
+};
+
+bool same_key(const CallKey& a, const CallKey& b) {
+  return a.velocity_mode == b.velocity_mode && a.B == b.B && a.P == b.P && a.d == b.d &&
+         a.t_single == b.t_single && a.kv == b.kv && a.mask == b.mask && a.x_in == b.x_in &&
+         a.out == b.out && a.prev == b.prev && a.vel == b.vel && a.st == b.st;
+}
+
+struct GraphEntry {
+  CallKey key;
+  hipGraphExec_t exec;
+  uint64_t last_use;
+};
+
+constexpr int kGraphCache = 8;
+
+enum ProbeKind { PR_QKV = 0, PR_ATTN_SELF, PR_ATTN_CROSS, PR_O, PR_GU, PR_DOWN, PR_ACTOUT, PR_COUNT };
+
+}  // namespace
+
+struct smolexp_handle {
+  smolexp_config cfg;
+  int device = 0;
+  bool loaded = false;
+  std::string err;
+  float ts[kMaxSteps];
+  float dt = 0.f;
+
+  // weights
+  void* wmem = nullptr;
+  Mat w_in, w_t1, w_t2, w_out;
+  float *b_in = nullptr, *b_t1 = nullptr, *b_t2 = nullptr, *gf = nullptr, *b_out = nullptr;
+  std::vector<LayerDev> layers;
+
+  // workspace
+  void* wsmem = nullptr;
+  float *x = nullptr, *h = nullptr, *ss = nullptr, *cvec = nullptr;
+  half_t *y16 = nullptr, *s16 = nullptr, *o16 = nullptr, *u16 = nullptr;
+  bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
+  int* nvalid = nullptr;
+  float2* rope = nullptr;
+
+  hipStream_t cap = nullptr;
+  std::vector<GraphEntry> graphs;
+  uint64_t tick = 0;
+
+  bool have_last = false;
+  CallKey last{};
+  bool have_probe = false;
+  CallKey probe_key{};
+  bool probe_ok[PR_COUNT] = {};
+  GemmArgs probe_g[PR_COUNT];
+  AttnArgs probe_a[PR_COUNT];
+  TileCfg probe_tile[PR_COUNT];
+  AMode probe_am[PR_COUNT];
+  EMode probe_em[PR_COUNT];
+};
+
+namespace {
+
+int fail(smolexp_t h, int code, const std::string& msg) {
+  if (h) h->err = msg;
+  return code;
+}
+
+int hip_fail(smolexp_t h, hipError_t e, const char* where) {
+  std::string m = std::string(where) + ": " + hipGetErrorString(e);
+  return fail(h, SMOLEXP_E_HIP, m);
+}
+
+bool check_config(const smolexp_config* c, std::string* why) {
+  if (!c) { *why = "config is NULL"; return false; }
+  if (c->d_model != kD || c->n_q_heads != kHQ || c->n_kv_heads != kHKV || c->head_dim != kHD ||
+      c->ffn != kFFN || c->chunk != kChunk || c->action_dim != kAD) {
+    *why = "architecture fields must be d_model 720, 15/5 heads of dim 64, ffn 2048, chunk 50, action_dim 32";
+    return false;
+  }
+  if (c->n_layers < 1 || c->n_layers > kMaxLayers) { *why = "n_layers must be 1..64"; return false; }
+  if (c->n_steps < 1 || c->n_steps > kMaxSteps) { *why = "n_steps must be 1..64"; return false; }
+  if (c->max_batch < 1 || c->max_batch > 1024) { *why = "max_batch must be 1..1024"; return false; }
+  if (c->max_prefix < 1 || c->max_prefix > 4096) { *why = "max_prefix must be 1..4096"; return false; }
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps > 0.f) || !(c->t_min_period > 0.f) ||
+      !(c->t_max_period > c->t_min_period) || !isfinite(c->rope_theta) || !isfinite(c->t_max_period)) {
+    *why = "rope_theta, rms_eps and 0 < t_min_period < t_max_period must be finite and positive";
+    return false;
+  }
+  return true;
+}
+
+size_t layer_count(bool self_attn) {
+  size_t n = kD + (size_t)kNQ * kD + (size_t)kD * kNQ + kD + 3 * (size_t)kFFN * kD;
+  if (self_attn) n += 2 * (size_t)kNKV * kD;
+  return n;
+}
+
+size_t count_weights(int n_layers) {
+  size_t n = (size_t)kD * kAD + kD + (size_t)kD * 2 * kD + kD + (size_t)kD * kD + kD;
+  for (int l = 0; l < n_layers; ++l) n += layer_count(l % 2 == 0);
+  n += kD + (size_t)kAD * kD + kAD;
+  return n;
+}
+
+float bf2f(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// Power-of-two exponent s so that max|w| * 2^s lies in [2^14, 2^15): every
+// bf16 value (8 significant bits) then maps to an fp16 normal number exactly,
+// down to max|w| * 2^-29; smaller values land on fp16's subnormal grid.
+int pick_shift(const std::vector<std::pair<const uint16_t*, size_t>>& parts) {
+  float mx = 0.f;
+  for (auto& p : parts)
+    for (size_t i = 0; i < p.second; ++i) {
+      const float v = fabsf(bf2f(p.first[i]));
+      if (v > mx) mx = v;
+    }
+  if (!(mx > 0.f) || !isfinite(mx)) return 0;
+  int e;
+  frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+  return 15 - e;
+}
+
+void to_f16(const uint16_t* src, size_t n, int shift, half_t* dst) {
+  const float m = ldexpf(1.f, shift);
+  for (size_t i = 0; i < n; ++i) dst[i] = (half_t)(bf2f(src[i]) * m);
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct CallArgs {
+  bool velocity;
+  const void* kv;
+  const uint8_t* mask;
+  int P;
+  const float* x_in;
+  float* out;
+  int B;
+  const float* prev;
+  int d;
+  float* vel;
+  float* st;
+  float t_single;
+};
+
+CallKey key_of(const CallArgs& c) {
+  CallKey k;
+  memset(&k, 0, sizeof(k));
+  k.velocity_mode = c.velocity;
+  k.B = c.B; k.P = c.P; k.d = c.d; k.t_single = c.velocity ? c.t_single : 0.f;
+  k.kv = c.kv; k.mask = c.mask; k.x_in = c.x_in; k.out = c.out; k.prev = c.prev; k.vel = c.vel; k.st = c.st;
+  return k;
+}
+
+// The launch sequence of one call.
+int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
+  const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
+  const TileCfg tc = M <= 64 ? T_SKINNY : T_MED;
+  const int nt_h = gemm_ntiles(tc, kD);
+  const int n_t = c.velocity ? 1 : h->cfg.n_steps;
+  hipError_t e;
+  if (record_probes) {
+    for (int i = 0; i < PR_COUNT; ++i) h->probe_ok[i] = false;
+    h->probe_key = key_of(c);
+    h->have_probe = true;
+  }
+
+  PrologueArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  pa.B = B;
+  pa.n_t = n_t;
+  for (int k = 0; k < n_t; ++k) pa.t[k] = c.velocity ? c.t_single : h->ts[k];
+  pa.mask = c.mask;
+  pa.P = P;
+  pa.nvalid = h->nvalid;
+  pa.x_in = c.x_in;
+  pa.x = h->x;
+  pa.w_t1 = h->w_t1.w;
+  pa.s_t1 = h->w_t1.scale;
+  pa.b_t1 = h->b_t1;
+  pa.cvec = h->cvec;
+  pa.p_min = h->cfg.t_min_period;
+  pa.p_max = h->cfg.t_max_period;
+  if ((e = launch_prologue(pa, s)) != hipSuccess) return hip_fail(h, e, "prologue launch");
+
+  const size_t kvLayer = (size_t)2 * B * kHKV * (size_t)P * kHD;  // elements per layer
+  const bf16_t* kv = static_cast<const bf16_t*>(c.kv);
+  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g) -> hipError_t {
+    if (record_probes && probe >= 0 && !h->probe_ok[probe]) {
+      h->probe_ok[probe] = true;
+      h->probe_g[probe] = g;
+      h->probe_tile[probe] = tc;
+      h->probe_am[probe] = am;
+      h->probe_em[probe] = em;
+    }
+    return launch_gemm(tc, am, em, g, s);
+  };
+
+  for (int k = 0; k < n_t; ++k) {
+    const float t = pa.t[k];
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.M = M;
+    g.inv_k = 1.0f / kD;
+    g.eps = h->cfg.rms_eps;
+
+    // action_in: y = x W_in^T + b_in   (prefix overwrite applied to x first)
+    GemmArgs ga = g;
+    ga.N = kD; ga.K = kAD; ga.A = h->x; ga.lda = kAD;
+    ga.x = h->x; ga.noise = c.x_in; ga.prev = c.prev; ga.ow_rows = c.velocity ? 0 : c.d; ga.t = t;
+    ga.W = h->w_in.w; ga.ldw = kAD; ga.w_scale = h->w_in.scale; ga.bias = h->b_in;
+    ga.out16 = h->y16; ga.ldo = kD;
+    if ((e = gemm(-1, A_X, E_F16_BIAS, ga)) != hipSuccess) return hip_fail(h, e, "action_in launch");
+
+    // time MLP: s = SiLU(W_t1[:, :720] y + (W_t1[:, 720:] e(t) + b_t1));  h = W_t2 s + b_t2
+    GemmArgs gt = g;
+    gt.N = kD; gt.K = kD; gt.A = h->y16; gt.lda = kD;
+    gt.W = h->w_t1.w; gt.ldw = 2 * kD; gt.w_scale = h->w_t1.scale; gt.bias = h->cvec + (size_t)k * kD;
+    gt.out16 = h->s16; gt.ldo = kD;
+    if ((e = gemm(-1, A_F16, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
+
+    GemmArgs go = g;
+    go.N = kD; go.K = kD; go.A = h->s16; go.lda = kD;
+    go.W = h->w_t2.w; go.ldw = kD; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
+    go.h = h->h; go.ss_out = h->ss;
+    if ((e = gemm(-1, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
+
+    for (int l = 0; l < L; ++l) {
+      const LayerDev& ld = h->layers[l];
+      GemmArgs gq = g;
+      gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD; gq.A = h->h; gq.lda = kD;
+      gq.ss_in = h->ss; gq.ss_nt = nt_h; gq.gain = ld.g1;
+      gq.W = ld.qkv.w; gq.ldw = kD; gq.w_scale = ld.qkv.scale;
+      gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.nvalid = h->nvalid; gq.rope = h->rope;
+      if ((e = gemm(ld.self_attn ? PR_QKV : -1, A_NORM, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
+
+      AttnArgs aa;
+      aa.q = h->q; aa.kc = h->kc; aa.vc = h->vc;
+      aa.pk = kv + (size_t)l * kvLayer;
+      aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2;
+      aa.mask = c.mask; aa.out = h->o16; aa.B = B; aa.P = P;
+      const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
+      if (record_probes && !h->probe_ok[pr]) { h->probe_ok[pr] = true; h->probe_a[pr] = aa; }
+      if ((e = launch_attention(ld.self_attn, aa, s)) != hipSuccess) return hip_fail(h, e, "attention launch");
+
+      GemmArgs gop = g;
+      gop.N = kD; gop.K = kNQ; gop.A = h->o16; gop.lda = kNQ;
+      gop.W = ld.o.w; gop.ldw = kNQ; gop.w_scale = ld.o.scale; gop.h = h->h; gop.ss_out = h->ss;
+      if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
+
+      GemmArgs gg = g;
+      gg.N = kGU; gg.K = kD; gg.A = h->h; gg.lda = kD;
+      gg.ss_in = h->ss; gg.ss_nt = nt_h; gg.gain = ld.g2;
+      gg.W = ld.gu.w; gg.ldw = kD; gg.w_scale = ld.gu.scale; gg.out16 = h->u16; gg.ldo = kFFN;
+      if ((e = gemm(PR_GU, A_NORM, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
+
+      GemmArgs gd = g;
+      gd.N = kD; gd.K = kFFN; gd.A = h->u16; gd.lda = kFFN;
+      gd.W = ld.down.w; gd.ldw = kFFN; gd.w_scale = ld.down.scale; gd.h = h->h; gd.ss_out = h->ss;
+      if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
+    }
+
+    // final RMSNorm + action_out; Euler update x += dt v
+    GemmArgs gv = g;
+    gv.N = kAD; gv.K = kD; gv.A = h->h; gv.lda = kD;
+    gv.ss_in = h->ss; gv.ss_nt = nt_h; gv.gain = h->gf;
+    gv.W = h->w_out.w; gv.ldw = kD; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
+    gv.x = h->x; gv.dt = h->dt;
+    const size_t stepElems = (size_t)B * kChunk * kAD;
+    if (c.velocity) {
+      gv.vel_out = c.out;
+    } else {
+      gv.vel_out = c.vel ? c.vel + (size_t)k * stepElems : nullptr;
+      gv.st_out = c.st ? c.st + (size_t)k * stepElems : nullptr;
+      gv.final_out = (k == n_t - 1) ? c.out : nullptr;
+    }
+    if ((e = gemm(PR_ACTOUT, A_NORM, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
+  }
+  return SMOLEXP_OK;
+}
+
+void drop_graphs(smolexp_t h) {
+  for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
+  h->graphs.clear();
+}
+
+int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
+  const CallKey key = key_of(c);
+  h->last = key;
+  h->have_last = true;
+  if (!h->cfg.use_graphs) return enqueue(h, c, s, true);
+
+  for (auto& g : h->graphs) {
+    if (same_key(g.key, key)) {
+      g.last_use = ++h->tick;
+      hipError_t e = hipGraphLaunch(g.exec, s);
+      if (e != hipSuccess) return hip_fail(h, e, "hipGraphLaunch");
+      return SMOLEXP_OK;
+    }
+  }
+  hipError_t e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamBeginCapture");
+  const int rc = enqueue(h, c, h->cap, true);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(h->cap, &graph);
+  if (rc != SMOLEXP_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
+  if ((int)h->graphs.size() >= kGraphCache) {
+    size_t lru = 0;
+    for (size_t i = 1; i < h->graphs.size(); ++i)
+      if (h->graphs[i].last_use < h->graphs[lru].last_use) lru = i;
+    // the evicted graph may still be running on a caller's stream
+    (void)hipStreamSynchronize(s);
+    (void)hipGraphExecDestroy(h->graphs[lru].exec);
+    h->graphs.erase(h->graphs.begin() + lru);
+  }
+  h->graphs.push_back(GraphEntry{key, exec, ++h->tick});
+  e = hipGraphLaunch(exec, s);
+  if (e != hipSuccess) return hip_fail(h, e, "hipGraphLaunch");
+  return SMOLEXP_OK;
+}
+
+int check_call(smolexp_t h, const void* kv, const uint8_t* mask, int P, const float* x_in, float* out, int B) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!h->loaded) return fail(h, SMOLEXP_E_STATE, "weights are not loaded");
+  if (!kv || !mask || !x_in || !out) return fail(h, SMOLEXP_E_INVAL, "a required pointer is NULL");
+  if (B < 1 || B > h->cfg.max_batch) return fail(h, SMOLEXP_E_INVAL, "batch out of range 1..max_batch");
+  if (P < 1 || P > h->cfg.max_prefix) return fail(h, SMOLEXP_E_INVAL, "prefix_len out of range 1..max_prefix");
+  return SMOLEXP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void smolexp_default_config(smolexp_config* c) {
+  if (!c) return;
+  memset(c, 0, sizeof(*c));
+  c->n_layers = 16;
+  c->d_model = kD;
+  c->n_q_heads = kHQ;
+  c->n_kv_heads = kHKV;
+  c->head_dim = kHD;
+  c->ffn = kFFN;
+  c->chunk = kChunk;
+  c->action_dim = kAD;
+  c->n_steps = 10;
+  c->max_batch = 128;
+  c->max_prefix = 512;
+  c->rope_theta = 10000.f;
+  c->rms_eps = 1e-6f;
+  c->t_min_period = 4e-3f;
+  c->t_max_period = 4.0f;
+  c->use_graphs = 1;
+}
+
+size_t smolexp_weight_count(const smolexp_config* cfg) {
+  std::string why;
+  if (!check_config(cfg, &why)) return 0;
+  return count_weights(cfg->n_layers);
+}
+
+int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out) {
+  std::string why;
+  if (!check_config(cfg, &why) || !t_out) return SMOLEXP_E_INVAL;
+  const float dt = (float)(-1.0 / (double)cfg->n_steps);
+  volatile float t = 1.0f;  // each step rounds to fp32
+  for (int k = 0; k < cfg->n_steps; ++k) {
+    t_out[k] = t;
+    t = t + dt;
+  }
+  if (dt_out) *dt_out = dt;
+  return SMOLEXP_OK;
+}
+
+int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
+  std::string why;
+  if (!out) return SMOLEXP_E_INVAL;
+  if (!check_config(cfg, &why)) return SMOLEXP_E_INVAL;
+  if (hip_device < 0) return SMOLEXP_E_INVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || hip_device >= ndev) return SMOLEXP_E_HIP;
+  if (hipSetDevice(hip_device) != hipSuccess) return SMOLEXP_E_HIP;
+
+  smolexp_t h = new (std::nothrow) smolexp_handle();
+  if (!h) return SMOLEXP_E_NOMEM;
+  h->cfg = *cfg;
+  h->device = hip_device;
+  smolexp_schedule(cfg, h->ts, &h->dt);
+
+  const size_t Mmax = (size_t)cfg->max_batch * kChunk;
+  const int n_pos = cfg->max_prefix + kChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mmax * kD * 4), o_ss = take(Mmax * kSSStride * 4);
+  const size_t o_cv = take((size_t)kMaxSteps * kD * 4);
+  const size_t o_y = take(Mmax * kD * 2), o_s = take(Mmax * kD * 2), o_o = take(Mmax * kNQ * 2);
+  const size_t o_u = take(Mmax * kFFN * 2), o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
+  const size_t o_vc = take(Mmax * kNKV * 2), o_nv = take((size_t)cfg->max_batch * 4);
+  const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
+  hipError_t e = hipMalloc(&h->wsmem, off);
+  if (e != hipSuccess) { delete h; return SMOLEXP_E_NOMEM; }
+  char* base = static_cast<char*>(h->wsmem);
+  h->x = (float*)(base + o_x); h->h = (float*)(base + o_h); h->ss = (float*)(base + o_ss);
+  h->cvec = (float*)(base + o_cv); h->y16 = (half_t*)(base + o_y); h->s16 = (half_t*)(base + o_s);
+  h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->q = (bf16_t*)(base + o_q);
+  h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->nvalid = (int*)(base + o_nv);
+  h->rope = (float2*)(base + o_rope);
+
+  e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
+  if (e == hipSuccess) e = launch_rope_table(h->rope, n_pos, cfg->rope_theta, h->cap);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
+  if (e != hipSuccess) {
+    smolexp_destroy(h);
+    return SMOLEXP_E_HIP;
+  }
+  *out = h;
+  return SMOLEXP_OK;
+}
+
+int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!src) return fail(h, SMOLEXP_E_INVAL, "weight buffer is NULL");
+  const int L = h->cfg.n_layers;
+  if (n_elems != count_weights(L)) return fail(h, SMOLEXP_E_SIZE, "weight count does not match the manifest");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+
+  // Device layout: fp16 matrices (gate/up interleaved in 16-row blocks), fp32 vectors.
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t o_win = take((size_t)kD * kAD * 2), o_wt1 = take((size_t)kD * 2 * kD * 2), o_wt2 = take((size_t)kD * kD * 2);
+  const size_t o_bin = take(kD * 4), o_bt1 = take(kD * 4), o_bt2 = take(kD * 4);
+  std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L), o_g1(L), o_g2(L);
+  for (int l = 0; l < L; ++l) {
+    o_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * kD * 2);
+    o_o[l] = take((size_t)kD * kNQ * 2);
+    o_gu[l] = take((size_t)kGU * kD * 2);
+    o_dn[l] = take((size_t)kD * kFFN * 2);
+    o_g1[l] = take(kD * 4);
+    o_g2[l] = take(kD * 4);
+  }
+  const size_t o_gf = take(kD * 4), o_wout = take((size_t)kAD * kD * 2), o_bout = take(kAD * 4);
+  std::vector<char> hostbuf;
+  try {
+    hostbuf.assign(off, 0);
+  } catch (...) {
+    return fail(h, SMOLEXP_E_NOMEM, "host staging allocation failed");
+  }
+  char* hb = hostbuf.data();
+
+  size_t pos = 0;
+  auto next = [&](size_t n) { const uint16_t* p = src + pos; pos += n; return p; };
+  auto vec32 = [&](const uint16_t* p, size_t n, size_t o) {
+    float* d = (float*)(hb + o);
+    for (size_t i = 0; i < n; ++i) d[i] = bf2f(p[i]);
+  };
+  Mat w_in, w_t1, w_t2, w_out;
+  std::vector<LayerDev> layers(L);
+  std::vector<int> sh_qkv(L), sh_o(L), sh_gu(L), sh_dn(L);
+
+  const uint16_t* p_win = next((size_t)kD * kAD);
+  const uint16_t* p_bin = next(kD);
+  const uint16_t* p_wt1 = next((size_t)kD * 2 * kD);
+  const uint16_t* p_bt1 = next(kD);
+  const uint16_t* p_wt2 = next((size_t)kD * kD);
+  const uint16_t* p_bt2 = next(kD);
+  int s;
+  s = pick_shift({{p_win, (size_t)kD * kAD}}); to_f16(p_win, (size_t)kD * kAD, s, (half_t*)(hb + o_win)); w_in.scale = ldexpf(1.f, -s);
+  s = pick_shift({{p_wt1, (size_t)kD * 2 * kD}}); to_f16(p_wt1, (size_t)kD * 2 * kD, s, (half_t*)(hb + o_wt1)); w_t1.scale = ldexpf(1.f, -s);
+  s = pick_shift({{p_wt2, (size_t)kD * kD}}); to_f16(p_wt2, (size_t)kD * kD, s, (half_t*)(hb + o_wt2)); w_t2.scale = ldexpf(1.f, -s);
+  vec32(p_bin, kD, o_bin); vec32(p_bt1, kD, o_bt1); vec32(p_bt2, kD, o_bt2);
+
+  for (int l = 0; l < L; ++l) {
+    const bool self_attn = l % 2 == 0;
+    LayerDev& ld = layers[l];
+    ld.self_attn = self_attn;
+    const uint16_t* g1 = next(kD);
+    const uint16_t* pq = next((size_t)kNQ * kD);
+    const uint16_t* pk = self_attn ? next((size_t)kNKV * kD) : nullptr;
+    const uint16_t* pvv = self_attn ? next((size_t)kNKV * kD) : nullptr;
+    const uint16_t* po = next((size_t)kD * kNQ);
+    const uint16_t* g2 = next(kD);
+    const uint16_t* pg = next((size_t)kFFN * kD);
+    const uint16_t* pu = next((size_t)kFFN * kD);
+    const uint16_t* pd = next((size_t)kD * kFFN);
+    vec32(g1, kD, o_g1[l]);
+    vec32(g2, kD, o_g2[l]);
+    // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone)
+    if (self_attn) {
+      s = pick_shift({{pq, (size_t)kNQ * kD}, {pk, (size_t)kNKV * kD}, {pvv, (size_t)kNKV * kD}});
+      half_t* d = (half_t*)(hb + o_qkv[l]);
+      to_f16(pq, (size_t)kNQ * kD, s, d);
+      to_f16(pk, (size_t)kNKV * kD, s, d + (size_t)kNQ * kD);
+      to_f16(pvv, (size_t)kNKV * kD, s, d + (size_t)(kNQ + kNKV) * kD);
+    } else {
+      s = pick_shift({{pq, (size_t)kNQ * kD}});
+      to_f16(pq, (size_t)kNQ * kD, s, (half_t*)(hb + o_qkv[l]));
+    }
+    ld.qkv.scale = ldexpf(1.f, -s);
+    s = pick_shift({{po, (size_t)kD * kNQ}});
+    to_f16(po, (size_t)kD * kNQ, s, (half_t*)(hb + o_o[l]));
+    ld.o.scale = ldexpf(1.f, -s);
+    s = pick_shift({{pg, (size_t)kFFN * kD}, {pu, (size_t)kFFN * kD}});
+    {
+      half_t* d = (half_t*)(hb + o_gu[l]);
+      for (int j = 0; j < kFFN / 16; ++j) {  // rows 32j..32j+15 = gate 16j.., 32j+16.. = up 16j..
+        to_f16(pg + (size_t)16 * j * kD, (size_t)16 * kD, s, d + (size_t)32 * j * kD);
+        to_f16(pu + (size_t)16 * j * kD, (size_t)16 * kD, s, d + (size_t)(32 * j + 16) * kD);
+      }
+    }
+    ld.gu.scale = ldexpf(1.f, -s);
+    s = pick_shift({{pd, (size_t)kD * kFFN}});
+    to_f16(pd, (size_t)kD * kFFN, s, (half_t*)(hb + o_dn[l]));
+    ld.down.scale = ldexpf(1.f, -s);
+  }
+  const uint16_t* p_gf = next(kD);
+  const uint16_t* p_wout = next((size_t)kAD * kD);
+  const uint16_t* p_bout = next(kAD);
+  vec32(p_gf, kD, o_gf);
+  s = pick_shift({{p_wout, (size_t)kAD * kD}}); to_f16(p_wout, (size_t)kAD * kD, s, (half_t*)(hb + o_wout)); w_out.scale = ldexpf(1.f, -s);
+  vec32(p_bout, kAD, o_bout);
+
+  if (h->wmem) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->wmem);
+    h->wmem = nullptr;
+    h->loaded = false;
+  }
+  drop_graphs(h);
+  h->have_last = false;
+  hipError_t e = hipMalloc(&h->wmem, off);
+  if (e != hipSuccess) return fail(h, SMOLEXP_E_NOMEM, "device weight allocation failed");
+  e = hipMemcpy(h->wmem, hb, off, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(h, e, "weight upload");
+  char* db = static_cast<char*>(h->wmem);
+  w_in.w = (half_t*)(db + o_win); w_t1.w = (half_t*)(db + o_wt1); w_t2.w = (half_t*)(db + o_wt2); w_out.w = (half_t*)(db + o_wout);
+  h->w_in = w_in; h->w_t1 = w_t1; h->w_t2 = w_t2; h->w_out = w_out;
+  h->b_in = (float*)(db + o_bin); h->b_t1 = (float*)(db + o_bt1); h->b_t2 = (float*)(db + o_bt2);
+  h->gf = (float*)(db + o_gf); h->b_out = (float*)(db + o_bout);
+  for (int l = 0; l < L; ++l) {
+    layers[l].qkv.w = (half_t*)(db + o_qkv[l]);
+    layers[l].o.w = (half_t*)(db + o_o[l]);
+    layers[l].gu.w = (half_t*)(db + o_gu[l]);
+    layers[l].down.w = (half_t*)(db + o_dn[l]);
+    layers[l].g1 = (float*)(db + o_g1[l]);
+    layers[l].g2 = (float*)(db + o_g2[l]);
+  }
+  h->layers = layers;
+  h->loaded = true;
+  return SMOLEXP_OK;
+}
+
+int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                       const float* noise, float* out_actions, int batch, void* hip_stream,
+                       const smolexp_denoise_opts* opts) {
+  int rc = check_call(h, prefix_kv, prefix_mask, prefix_len, noise, out_actions, batch);
+  if (rc != SMOLEXP_OK) return rc;
+  CallArgs c;
+  memset(&c, 0, sizeof(c));
+  c.velocity = false;
+  c.kv = prefix_kv; c.mask = prefix_mask; c.P = prefix_len; c.x_in = noise; c.out = out_actions; c.B = batch;
+  if (opts) {
+    if (opts->overwrite_rows < 0 || opts->overwrite_rows > kChunk)
+      return fail(h, SMOLEXP_E_INVAL, "overwrite_rows out of range 0..50");
+    if (opts->overwrite_rows > 0 && !opts->prev_actions)
+      return fail(h, SMOLEXP_E_INVAL, "overwrite_rows > 0 needs prev_actions");
+    c.d = opts->overwrite_rows;
+    c.prev = c.d > 0 ? opts->prev_actions : nullptr;
+    c.vel = opts->out_velocities;
+    c.st = opts->out_states;
+  }
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  return run_call(h, c, static_cast<hipStream_t>(hip_stream));
+}
+
+int smolexp_denoise(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                    const float* noise, float* out_actions, int batch, void* hip_stream) {
+  return smolexp_denoise_ex(h, prefix_kv, prefix_mask, prefix_len, noise, out_actions, batch, hip_stream, nullptr);
+}
+
+int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                     const float* x, float t, float* out_v, int batch, void* hip_stream) {
+  int rc = check_call(h, prefix_kv, prefix_mask, prefix_len, x, out_v, batch);
+  if (rc != SMOLEXP_OK) return rc;
+  if (!isfinite(t)) return fail(h, SMOLEXP_E_INVAL, "t must be finite");
+  CallArgs c;
+  memset(&c, 0, sizeof(c));
+  c.velocity = true;
+  c.kv = prefix_kv; c.mask = prefix_mask; c.P = prefix_len; c.x_in = x; c.out = out_v; c.B = batch; c.t_single = t;
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  return run_call(h, c, static_cast<hipStream_t>(hip_stream));
+}
+
+int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, float* avg_us) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!avg_us || reps < 1 || kernel < 0 || kernel > PR_COUNT) return fail(h, SMOLEXP_E_INVAL, "bad kernel id, reps or avg_us");
+  if (!h->have_last) return fail(h, SMOLEXP_E_STATE, "no previous denoise call to time");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  CallArgs lastc;
+  memset(&lastc, 0, sizeof(lastc));
+  {
+    const CallKey& k = h->last;
+    lastc.velocity = k.velocity_mode; lastc.kv = k.kv; lastc.mask = k.mask; lastc.P = k.P; lastc.x_in = k.x_in;
+    lastc.out = k.out; lastc.B = k.B; lastc.prev = k.prev; lastc.d = k.d; lastc.vel = k.vel; lastc.st = k.st;
+    lastc.t_single = k.t_single;
+  }
+  if (kernel < PR_COUNT && (!h->have_probe || !same_key(h->probe_key, h->last))) {
+    // the previous call was a graph replay of another key: enqueue it once directly to get its launches
+    int rc0 = enqueue(h, lastc, s, true);
+    if (rc0 != SMOLEXP_OK) return rc0;
+  }
+  if (kernel < PR_COUNT && !h->probe_ok[kernel]) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipEventCreate");
+  hipError_t e = hipEventRecord(e0, s);
+  int rc = SMOLEXP_OK;
+  for (int i = 0; i < reps && e == hipSuccess && rc == SMOLEXP_OK; ++i) {
+    if (kernel == PR_COUNT) {
+      rc = run_call(h, lastc, s);  // the whole loop: replay the previous call
+    } else if (kernel == PR_ATTN_SELF || kernel == PR_ATTN_CROSS) {
+      e = launch_attention(kernel == PR_ATTN_SELF, h->probe_a[kernel], s);
+    } else {
+      e = launch_gemm(h->probe_tile[kernel], h->probe_am[kernel], h->probe_em[kernel], h->probe_g[kernel], s);
+    }
+  }
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != SMOLEXP_OK) return rc;
+  if (e != hipSuccess) return hip_fail(h, e, "kernel timing");
+  *avg_us = ms * 1000.f / reps;
+  return SMOLEXP_OK;
+}
+
+const char* smolexp_strerror(int code) {
+  switch (code) {
+    case SMOLEXP_OK: return "ok";
+    case SMOLEXP_E_INVAL: return "invalid argument";
+    case SMOLEXP_E_STATE: return "call out of order";
+    case SMOLEXP_E_SIZE: return "wrong weight count";
+    case SMOLEXP_E_NOMEM: return "out of memory";
+    case SMOLEXP_E_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+const char* smolexp_last_error(smolexp_t h) { return h ? h->err.c_str() : ""; }
+
+void smolexp_destroy(smolexp_t h) {
+  if (!h) return;
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  drop_graphs(h);
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  if (h->wmem) (void)hipFree(h->wmem);
+  if (h->wsmem) (void)hipFree(h->wsmem);
+  delete h;
+}
+
+}  // extern "C"

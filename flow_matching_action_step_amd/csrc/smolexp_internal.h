@@ -1,0 +1,121 @@
+// Internal declarations shared by the host API (smolexp_api.cpp) and the HIP
+// kernels (kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smolexp {
+
+// SmolVLA action-expert shapes (noeira docs "SmolVLA", Architecture table).
+constexpr int kD = 720;        // model width
+constexpr int kHQ = 15;        // query heads
+constexpr int kHKV = 5;        // key/value heads
+constexpr int kHD = 64;        // head dim
+constexpr int kFFN = 2048;     // SwiGLU width
+constexpr int kChunk = 50;     // actions per chunk
+constexpr int kAD = 32;        // padded action width
+constexpr int kNQ = kHQ * kHD;         // 960
+constexpr int kNKV = kHKV * kHD;       // 320
+constexpr int kNQKV = kNQ + 2 * kNKV;  // 1600
+constexpr int kGU = 2 * kFFN;          // 4096 (gate and up, interleaved in 16-row blocks)
+constexpr int kSSStride = 64;  // partial sums of squares per row (one per producer N-tile)
+constexpr int kMaxSteps = 64;
+constexpr int kMaxLayers = 64;
+
+typedef _Float16 half_t;
+typedef uint16_t bf16_t;       // bf16 bit pattern
+
+// A-operand sources of the GEMM.
+enum AMode : int {
+  A_F16 = 0,    // fp16 [M][lda]
+  A_NORM = 1,   // fp32 residual [M][lda], RMSNorm applied on load (row scale from partial sums, gain)
+  A_X = 2,      // fp32 Euler state [M][32], prefix overwrite applied on load
+};
+
+// GEMM epilogues.
+enum EMode : int {
+  E_F16_BIAS = 0,  // out16 = acc + bias                      (action_in)
+  E_TIMEIN = 1,    // out16 = SiLU(acc + cvec)                (time MLP, first layer)
+  E_H_BIAS = 2,    // h = acc + bias; row sums of squares     (time MLP, second layer)
+  E_H_RESID = 3,   // h += acc; row sums of squares           (o and down projections)
+  E_QKV = 4,       // RoPE on Q and K, scatter to Q/Kc/Vc bf16 (attention input)
+  E_SWIGLU = 5,    // out16 = SiLU(gate) * up                 (FFN)
+  E_ACTOUT = 6,    // v = acc + bias; x += dt * v             (action_out + Euler)
+};
+
+struct GemmArgs {
+  int M, N, K;
+  const void* A;
+  int lda;
+  // A_NORM
+  const float* ss_in;
+  int ss_nt;
+  const float* gain;
+  float inv_k;
+  float eps;
+  // A_X
+  float* x;
+  const float* noise;
+  const float* prev;
+  int ow_rows;
+  float t;
+  // weights [N][ldw] fp16, values scaled by 1 / w_scale
+  const half_t* W;
+  int ldw;
+  float w_scale;
+  // epilogue
+  const float* bias;   // bias, or the per-step time vector for E_TIMEIN
+  half_t* out16;
+  int ldo;
+  float* h;
+  float* ss_out;
+  bf16_t* q;
+  bf16_t* kc;
+  bf16_t* vc;
+  const int* nvalid;
+  const float2* rope;  // [pos][32] (cos, sin)
+  float dt;
+  float* vel_out;
+  float* st_out;
+  float* final_out;
+};
+
+struct AttnArgs {
+  const bf16_t* q;       // [B][15][50][64]
+  const bf16_t* kc;      // [B][5][50][64] (self only)
+  const bf16_t* vc;
+  const bf16_t* pk;      // this layer's prefix K: [B][5][P][64]
+  const bf16_t* pv;      // this layer's prefix V
+  const uint8_t* mask;   // [B][P]
+  half_t* out;           // [B*50][960]
+  int B, P;
+};
+
+struct PrologueArgs {
+  int B;
+  int n_t;                 // number of flow times
+  float t[kMaxSteps];
+  const uint8_t* mask;     // [B][P]
+  int P;
+  int* nvalid;             // out [B]
+  const float* x_in;       // [B][50][32]
+  float* x;                // out: Euler state
+  const half_t* w_t1;      // time_in weight [720][1440] (fp16, scaled)
+  float s_t1;
+  const float* b_t1;
+  float* cvec;             // out [n_t][720] = W_t1[:, 720:] e(t) + b_t1
+  float p_min, p_max;
+};
+
+// Tile configurations of the GEMM.
+enum TileCfg : int { T_SKINNY = 0, T_MED = 1 };
+
+// Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
+hipError_t launch_gemm(TileCfg cfg, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
+int gemm_ntiles(TileCfg cfg, int N);
+hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s);
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+hipError_t launch_rope_table(float2* tab, int n_pos, float theta, hipStream_t s);
+
+}  // namespace smolexp

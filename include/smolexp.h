@@ -1,0 +1,197 @@
+/*
+ * smolexp — the SmolVLA action-expert denoising loop on AMD Instinct MI355X (gfx950).
+ *
+ * Given the VLM's per-layer prefix K/V cache and its pad mask, the library runs
+ * the flow-matching action head: starting from Gaussian noise at t = 1 it takes
+ * n_steps explicit Euler steps x <- x + dt * v(x, t) toward t = 0, where the
+ * velocity v comes from a stack of width-720 transformer layers over the
+ * 50 x 32 action chunk; even layers self-attend over [valid prefix ; causal
+ * chunk], odd layers cross-attend to the valid prefix (noeira docs "SmolVLA",
+ * Architecture: table rows "Action expert" and "Action head", the paragraph on
+ * the query (prefix once, expert ten times), the flow-matching objective and
+ * the block attention mask).
+ *
+ * Conventions for every entry point:
+ *  - Return 0 on success or a negative SMOLEXP_E_* code.  All argument checks
+ *    run on the host before anything is enqueued; a failed check enqueues
+ *    nothing.  smolexp_strerror() names a code, smolexp_last_error() gives
+ *    the handle's last detailed message.
+ *  - "device" pointers are HIP device memory on the handle's device; "host"
+ *    pointers are ordinary host memory.  The library never frees or keeps a
+ *    caller pointer beyond the work it enqueues.
+ *  - Device contents are not checked: NaN in gives NaN out.
+ *  - A handle is not re-entrant: use one handle per concurrent stream.
+ *  - No environment variable changes the library's behaviour.
+ */
+#ifndef SMOLEXP_H
+#define SMOLEXP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct smolexp_handle* smolexp_t;
+
+enum {
+  SMOLEXP_OK = 0,
+  SMOLEXP_E_INVAL = -1,  /* null pointer, size out of range, unsupported config */
+  SMOLEXP_E_STATE = -2,  /* call out of order (e.g. denoise before load_weights) */
+  SMOLEXP_E_SIZE = -3,   /* weight buffer length != smolexp_weight_count(cfg) */
+  SMOLEXP_E_NOMEM = -4,  /* device or host allocation failed */
+  SMOLEXP_E_HIP = -5     /* HIP runtime or launch error; see smolexp_last_error */
+};
+
+/*
+ * Configuration, fixed at create.  The architecture fields must equal the
+ * SmolVLA expert's (d_model 720, 15 query heads over 5 KV heads of dim 64,
+ * SwiGLU width 2048, chunk 50, action width 32); other values return
+ * SMOLEXP_E_INVAL.  n_layers may be 1..64 (16 in SmolVLA; layer l self-attends
+ * when l is even).  n_steps is 1..64 (10 in SmolVLA).  rope_theta, rms_eps and
+ * the time-embedding periods are readings the pages leave open; defaults are
+ * 10000, 1e-6, 4e-3 and 4.0.
+ */
+typedef struct smolexp_config {
+  int n_layers;
+  int d_model;
+  int n_q_heads;
+  int n_kv_heads;
+  int head_dim;
+  int ffn;
+  int chunk;
+  int action_dim;
+  int n_steps;
+  int max_batch;     /* 1..1024: largest batch a call may pass */
+  int max_prefix;    /* 1..4096: largest padded prefix length P a call may pass */
+  float rope_theta;
+  float rms_eps;
+  float t_min_period;
+  float t_max_period;
+  int use_graphs;    /* 1: capture each call's launch sequence once and replay it as a HIP graph */
+} smolexp_config;
+
+/* Fill *cfg with the SmolVLA expert (16 layers, 10 steps, max_batch 128, max_prefix 512). Host only. */
+void smolexp_default_config(smolexp_config* cfg);
+
+/*
+ * Number of bf16 weight elements smolexp_load_weights expects for cfg
+ * (98,210,912 for 16 layers; 25,755,872 for 4), or 0 if cfg is invalid.
+ * Host only; needs no GPU.
+ */
+size_t smolexp_weight_count(const smolexp_config* cfg);
+
+/*
+ * The flow times the loop uses, host only: dt = fl32(-1/n_steps),
+ * t_0 = 1, t_{k+1} = fl32(t_k + dt), exactly n_steps values (noeira docs
+ * "SmolVLA", Architecture: from t = 1 toward t = 0).  t_out has room for
+ * cfg->n_steps floats; dt_out may be NULL.
+ */
+int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out);
+
+/*
+ * Create a handle on HIP device hip_device: validates cfg, allocates the
+ * workspace for max_batch x max_prefix and the weight store, and builds the
+ * RoPE table.  *out is set only on success.  Release with smolexp_destroy.
+ */
+int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out);
+
+/*
+ * Load the expert's weights from one flat host buffer of bf16 bit patterns in
+ * manifest order, every matrix row-major [out, in] (the nn.Linear layout,
+ * noeira docs "SmolVLA", Weights):
+ *   action_in.w [720,32], action_in.b [720], time_in.w [720,1440],
+ *   time_in.b [720], time_out.w [720,720], time_out.b [720];
+ *   per layer l: norm1.g [720], q.w [960,720], (l even only: k.w [320,720],
+ *   v.w [320,720]), o.w [720,960], norm2.g [720], gate.w [2048,720],
+ *   up.w [2048,720], down.w [720,2048];
+ *   final_norm.g [720], action_out.w [32,720], action_out.b [32].
+ * n_elems must equal smolexp_weight_count (else SMOLEXP_E_SIZE).  The data is
+ * copied (matrices re-encoded exactly as fp16 with a power-of-two scale per
+ * matrix); the caller may free bf16_host on return.  Synchronous.
+ */
+int smolexp_load_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems);
+
+/*
+ * Denoise a batch of action chunks (the whole loop, asynchronous on hip_stream;
+ * NULL = the null stream).
+ *   prefix_kv    device bf16, [n_layers][2 (K, V)][batch][5][prefix_len][64]:
+ *                each layer's cached prefix keys (already rotated at their
+ *                prefix positions) and values.  Read only.
+ *   prefix_mask  device uint8 [batch][prefix_len], nonzero = valid token; any
+ *                pattern.  Chunk row i of query b sits at RoPE position
+ *                (number of valid tokens of b) + i.  Masked tokens are left out
+ *                of every softmax (their K/V may hold anything, NaN included).
+ *                A query with no valid token gets zero cross-attention output.
+ *   prefix_len   P, 1..max_prefix.
+ *   noise        device fp32 [batch][50][32]: x at t = 1.  Read only.
+ *   out_actions  device fp32 [batch][50][32]: x after the last step.
+ *   batch        1..max_batch.
+ * The library's workspace is in use until the stream work completes.
+ */
+int smolexp_denoise(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask,
+                    int prefix_len, const float* noise, float* out_actions, int batch,
+                    void* hip_stream);
+
+/*
+ * Options for smolexp_denoise_ex.  Every field may be zero/NULL.
+ *   prev_actions    device fp32 [batch][overwrite_rows][32]: tail of the
+ *                   previous chunk for prefix overwrite ("Paper vs hardware 11:
+ *                   SmolVLA", What I ran).  Before every step k, chunk rows
+ *                   i < overwrite_rows are set to t_k*noise_i + (1-t_k)*prev_i,
+ *                   the flow-matching path point at t_k (noeira docs "SmolVLA",
+ *                   flow-matching objective).  Required when overwrite_rows > 0.
+ *   overwrite_rows  d, 0..50.
+ *   out_velocities  device fp32 [n_steps][batch][50][32] or NULL: v at each step.
+ *   out_states      device fp32 [n_steps][batch][50][32] or NULL: x after each step.
+ */
+typedef struct smolexp_denoise_opts {
+  const float* prev_actions;
+  int overwrite_rows;
+  float* out_velocities;
+  float* out_states;
+} smolexp_denoise_opts;
+
+/* smolexp_denoise with options (opts may be NULL = none). */
+int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask,
+                       int prefix_len, const float* noise, float* out_actions, int batch,
+                       void* hip_stream, const smolexp_denoise_opts* opts);
+
+/*
+ * One evaluation of the velocity field v(x, t | prefix) (the expert's forward
+ * pass, no Euler update).  x and out_v are device fp32 [batch][50][32]; the other
+ * arguments are as for smolexp_denoise.  Used to check a single step against
+ * an oracle on the oracle's own x.  Asynchronous on hip_stream.
+ */
+int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask,
+                     int prefix_len, const float* x, float t, float* out_v, int batch,
+                     void* hip_stream);
+
+/*
+ * Measurement hook: average duration in microseconds of one launch of one
+ * kernel of the loop, timed with HIP events around `reps` back-to-back
+ * launches on hip_stream (synchronous).  It reuses the workspace contents of
+ * the last smolexp_denoise/_ex call, which must have used the same batch and
+ * prefix_len, and leaves that workspace's numbers unspecified.
+ *   kernel: 0 = self-attention layer QKV projection, 1 = self attention,
+ *           2 = cross attention, 3 = o projection, 4 = gate/up projection,
+ *           5 = down projection, 6 = action_out + Euler update,
+ *           7 = the whole loop (one smolexp_denoise call).
+ */
+int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, float* avg_us);
+
+/* Static name of an error code. */
+const char* smolexp_strerror(int code);
+
+/* Last error message recorded on h ("" if none); valid until the next call on h. */
+const char* smolexp_last_error(smolexp_t h);
+
+/* Free everything h owns (waits for its device work first).  NULL is ignored. */
+void smolexp_destroy(smolexp_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOLEXP_H */

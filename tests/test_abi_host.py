@@ -1,0 +1,88 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and its host logic (config checks, weight count, flow-time schedule,
+error codes) behaves as include/smolexp.h states.  No GPU needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import flow_matching_action_step_amd as fm
+import oracle
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "smolexp.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smolexp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", fm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (smolexp_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(fm.raw(), n)
+    assert set(fm.EXPORTED) == set(names)
+
+
+def test_weight_count_matches_manifest():
+    for L in (1, 2, 4, 16):
+        assert fm.smolexp_weight_count(fm.smolexp_default_config(n_layers=L)) == synth.weight_count(L)
+    assert fm.smolexp_weight_count(fm.smolexp_default_config()) == 98_210_912
+
+
+@pytest.mark.parametrize("field,value", [("d_model", 512), ("n_q_heads", 16), ("n_kv_heads", 4), ("head_dim", 128),
+                                         ("ffn", 4096), ("chunk", 32), ("action_dim", 16), ("n_layers", 0),
+                                         ("n_layers", 65), ("n_steps", 0), ("n_steps", 65), ("max_batch", 0),
+                                         ("max_batch", 1025), ("max_prefix", 0), ("rms_eps", 0.0),
+                                         ("rope_theta", -1.0), ("t_max_period", 1e-3)])
+def test_invalid_config_is_rejected_before_any_device_call(field, value):
+    cfg = fm.smolexp_default_config(**{field: value})
+    assert fm.smolexp_weight_count(cfg) == 0
+    h = ctypes.c_void_p()
+    assert fm.raw().smolexp_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == fm.SMOLEXP_E_INVAL
+    assert not h.value
+
+
+def test_schedule_matches_the_oracle_bitwise():
+    for n in (1, 4, 10, 64):
+        ts, dt = fm.smolexp_schedule(fm.smolexp_default_config(n_steps=n))
+        ots, odt = oracle.schedule(n)
+        assert np.array(ts, np.float32).tobytes() == np.array(ots, np.float32).tobytes()
+        assert np.float32(dt) == odt
+
+
+def test_null_handle_and_error_strings():
+    lib = fm.raw()
+    assert lib.smolexp_denoise(None, None, None, 1, None, None, 1, None) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_denoise_ex(None, None, None, 1, None, None, 1, None, None) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_velocity(None, None, None, 1, None, 0.5, None, 1, None) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_load_weights(None, None, 0) == fm.SMOLEXP_E_INVAL
+    us = ctypes.c_float()
+    assert lib.smolexp_time_kernel(None, 0, 1, None, ctypes.byref(us)) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_schedule(None, None, None) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_create(None, 0, None) == fm.SMOLEXP_E_INVAL
+    cfg = fm.smolexp_default_config()
+    assert lib.smolexp_create(ctypes.byref(cfg), -1, ctypes.byref(ctypes.c_void_p())) == fm.SMOLEXP_E_INVAL
+    assert fm.smolexp_last_error(None) == ""
+    lib.smolexp_destroy(None)
+    names = {fm.smolexp_strerror(c) for c in (0, -1, -2, -3, -4, -5)}
+    assert len(names) == 6 and fm.smolexp_strerror(-99) == "unknown error code"
+
+
+def test_create_without_a_gpu_reports_a_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = fm.smolexp_default_config()
+    h = ctypes.c_void_p()
+    assert fm.raw().smolexp_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == fm.SMOLEXP_E_HIP
+    assert not h.value

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Tolerances (tests/gpu_util.py): per-step velocities within 1e-2 norm-relative,
+final actions within 2e-2 max-abs.  Workloads are the five seeded synthetic
+ones; at batch 64 and 128 the oracle computes a sample of queries (queries are
+independent) while the GPU runs the whole batch in the benchmark's launch
+configuration.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import flow_matching_action_step_amd as fm
+import oracle
+import synth
+from gpu_util import Expert, to_device, run_gpu, run_oracle, compare, VEL_RTOL, ACT_ATOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def ex4():
+    _say("create 4-layer expert")
+    e = Expert(4, max_batch=16, max_prefix=512)
+    yield e
+    e.close()
+
+
+@pytest.fixture(scope="module")
+def ex16():
+    _say("create 16-layer expert (max_batch 128)")
+    e = Expert(16, max_batch=128, max_prefix=512)
+    yield e
+    e.close()
+
+
+# ------------------------------------------------------------------ C ABI on a device
+
+def test_abi_errors_on_device():
+    _say("abi errors")
+    lib = fm.raw()
+    cfg = fm.smolexp_default_config(n_layers=2, max_batch=4, max_prefix=64)
+    h = fm.smolexp_create(cfg, 0)
+    try:
+        dev = torch.zeros(16, device="cuda")
+        p = ctypes.c_void_p(dev.data_ptr())
+        assert lib.smolexp_denoise(h, p, p, 8, p, p, 1, None) == fm.SMOLEXP_E_STATE
+        w = np.zeros(synth.weight_count(2) - 1, np.uint16)
+        assert lib.smolexp_load_weights(h, w.ctypes.data_as(ctypes.c_void_p), w.size) == fm.SMOLEXP_E_SIZE
+        w = synth.pack_weights(synth.draw_weights(2), 2)
+        assert lib.smolexp_load_weights(h, w.ctypes.data_as(ctypes.c_void_p), w.size) == 0
+        assert lib.smolexp_denoise(h, p, p, 8, p, p, 0, None) == fm.SMOLEXP_E_INVAL
+        assert lib.smolexp_denoise(h, p, p, 8, p, p, 5, None) == fm.SMOLEXP_E_INVAL
+        assert lib.smolexp_denoise(h, p, p, 0, p, p, 1, None) == fm.SMOLEXP_E_INVAL
+        assert lib.smolexp_denoise(h, p, p, 65, p, p, 1, None) == fm.SMOLEXP_E_INVAL
+        assert lib.smolexp_denoise(h, None, p, 8, p, p, 1, None) == fm.SMOLEXP_E_INVAL
+        assert "NULL" in fm.smolexp_last_error(h)
+        o = fm.smolexp_denoise_opts()
+        o.overwrite_rows = 51
+        assert lib.smolexp_denoise_ex(h, p, p, 8, p, p, 1, None, ctypes.byref(o)) == fm.SMOLEXP_E_INVAL
+        o.overwrite_rows = 3
+        assert lib.smolexp_denoise_ex(h, p, p, 8, p, p, 1, None, ctypes.byref(o)) == fm.SMOLEXP_E_INVAL
+        assert lib.smolexp_velocity(h, p, p, 8, p, float("nan"), p, 1, None) == fm.SMOLEXP_E_INVAL
+        us = ctypes.c_float()
+        assert lib.smolexp_time_kernel(h, 0, 1, None, ctypes.byref(us)) == fm.SMOLEXP_E_STATE
+    finally:
+        fm.smolexp_destroy(h)
+
+
+# ------------------------------------------------------------------ teacher-forced single steps
+
+def test_velocity_teacher_forced_4_layers(ex4):
+    _say("velocity, 4 layers, teacher forced")
+    wl = synth.make_workload("expert4_b1_p177", with_weights=False)
+    dev = to_device(wl)
+    orc = run_oracle(ex4, wl, [0])
+    ts, _ = oracle.schedule(10)
+    for k in (0, 5, 9):
+        x_np = wl["noise"][0].astype(np.float64) if k == 0 else orc["st"][k - 1][0]
+        x = torch.from_numpy(x_np.astype(np.float32)[None]).cuda()
+        v = torch.empty_like(x)
+        fm.smolexp_velocity(ex4.h, ex4.cfg, dev["kv"], dev["mask"], x, float(ts[k]), v)
+        torch.cuda.synchronize()
+        want = oracle.velocity(ex4.W, ex4.ocfg, x_np.astype(np.float32).astype(np.float64), ts[k],
+                               oracle.bf16_bits_to_float(wl["prefix_kv"][:, 0, 0]),
+                               oracle.bf16_bits_to_float(wl["prefix_kv"][:, 1, 0]), wl["mask"][0].astype(bool))
+        got = v.cpu().numpy()[0]
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        print(f"[parity] velocity step {k}: rel {rel:.3e}", flush=True)
+        assert rel <= VEL_RTOL
+
+
+# ------------------------------------------------------------------ whole loop, the five workloads
+
+def test_denoise_4_layers_batch1(ex4):
+    _say("denoise expert4_b1_p177")
+    wl = synth.make_workload("expert4_b1_p177", with_weights=False)
+    gpu = run_gpu(ex4, to_device(wl))
+    compare(gpu, run_oracle(ex4, wl, [0]), [0], wl["noise"], "expert4_b1_p177")
+
+
+def test_denoise_16_layers_batch1(ex16):
+    _say("denoise expert16_b1_p177")
+    wl = synth.make_workload("expert16_b1_p177", with_weights=False)
+    gpu = run_gpu(ex16, to_device(wl))
+    compare(gpu, run_oracle(ex16, wl, [0]), [0], wl["noise"], "expert16_b1_p177")
+
+
+def test_denoise_16_layers_batch16_variable_prefix(ex16):
+    _say("denoise expert16_b16_pvar241")
+    wl = synth.make_workload("expert16_b16_pvar241", with_weights=False)
+    gpu = run_gpu(ex16, to_device(wl))
+    # the shortest and the longest prefixes plus two more
+    order = np.argsort(wl["lengths"])
+    q = sorted({int(order[0]), int(order[-1]), 3, 10})
+    compare(gpu, run_oracle(ex16, wl, q), q, wl["noise"], "expert16_b16_pvar241")
+
+
+def test_denoise_16_layers_batch64(ex16):
+    _say("denoise expert16_b64_p257 (sampled queries)")
+    wl = synth.make_workload("expert16_b64_p257", with_weights=False)
+    gpu = run_gpu(ex16, to_device(wl))
+    q = [0, 37, 63]
+    compare(gpu, run_oracle(ex16, wl, q), q, wl["noise"], "expert16_b64_p257")
+
+
+def test_denoise_16_layers_batch128_overwrite(ex16):
+    _say("denoise expert16_b128_p177_ow7 (sampled queries)")
+    wl = synth.make_workload("expert16_b128_p177_ow7", with_weights=False)
+    gpu = run_gpu(ex16, to_device(wl), d=7)
+    q = [0, 64, 127]
+    compare(gpu, run_oracle(ex16, wl, q, d=7), q, wl["noise"], "expert16_b128_p177_ow7")
+    # rows below d after the last step: the overwrite set them before step 9 and one Euler step followed
+    ts, dt = oracle.schedule(10)
+    t9 = float(ts[-1])
+    before = t9 * wl["noise"][q, :7] + (1 - t9) * wl["prev_actions"][q]
+    np.testing.assert_allclose(gpu["out"][q, :7], before + float(dt) * gpu["vel"][-1][q, :7], rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def test_inputs_untouched_and_runs_deterministic(ex4):
+    _say("inputs untouched, determinism")
+    wl = synth.make_workload("expert4_b1_p177", batch=3, with_weights=False)
+    dev = to_device(wl)
+    snap = {k: v.clone() for k, v in dev.items() if v is not None}
+    a = run_gpu(ex4, dev)
+    b = run_gpu(ex4, dev)
+    for k, v in snap.items():
+        assert torch.equal(v, dev[k]), k
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_pad_invariance_with_nan_pads(ex4):
+    _say("pad invariance")
+    wl = synth.make_workload("expert4_b1_p177", batch=3, with_weights=False)
+    wl["mask"][0, 150:] = 0
+    wl["mask"][1, ::3] = 0          # interleaved pads
+    dev = to_device(wl)
+    a = run_gpu(ex4, dev)
+    kv = wl["prefix_kv"].copy()
+    for b, p in zip(*np.nonzero(wl["mask"] == 0)):
+        kv[:, :, b, :, p, :] = 0x7FC0   # bf16 NaN in every masked slot
+    dev["kv"] = torch.from_numpy(kv.view(np.int16)).cuda()
+    b = run_gpu(ex4, dev)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+    q = [0, 1]
+    compare(a, run_oracle(ex4, wl, q), q, wl["noise"], "expert4 pads")
+
+
+def test_chunk_causality(ex4):
+    _say("chunk causality")
+    wl = synth.make_workload("expert4_b1_p177", with_weights=False)
+    dev = to_device(wl)
+    x = dev["noise"].clone()
+    v0 = torch.empty_like(x)
+    fm.smolexp_velocity(ex4.h, ex4.cfg, dev["kv"], dev["mask"], x, 0.6, v0)
+    x[0, 20] += 1.0
+    v1 = torch.empty_like(x)
+    fm.smolexp_velocity(ex4.h, ex4.cfg, dev["kv"], dev["mask"], x, 0.6, v1)
+    torch.cuda.synchronize()
+    assert torch.equal(v0[0, :20], v1[0, :20])
+    assert (v0[0, 20:] - v1[0, 20:]).abs().max() > 1e-4
+
+
+def test_batch_invariance(ex4):
+    _say("batch invariance")
+    wl = synth.make_workload("expert4_b1_p177", batch=5, with_weights=False)
+    wl["mask"][2, 100:] = 0
+    full = run_gpu(ex4, to_device(wl))
+    one = {k: (v[2:3] if k != "prefix_kv" else v[:, :, 2:3]) for k, v in wl.items()
+           if isinstance(v, np.ndarray)}
+    one["prev_actions"] = None
+    alone = run_gpu(ex4, to_device(one))
+    np.testing.assert_allclose(alone["out"][0], full["out"][2], atol=ACT_ATOL / 4)
+    rel = np.linalg.norm(alone["vel"][:, 0] - full["vel"][:, 2]) / np.linalg.norm(full["vel"][:, 2])
+    assert rel < VEL_RTOL / 4
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_edge_single_key_empty_prefix_and_ragged(ex4):
+    _say("edge cases: P=1, empty prefix, ragged P")
+    for P, lens in ((1, [1, 0]), (65, [65, 0]), (130, [3, 129])):
+        wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
+        wl["prefix_kv"] = synth.draw_prefix_kv(4, 2, P)
+        wl["mask"] = synth.make_mask(2, P, lens)
+        wl["prefix_len"] = P
+        gpu = run_gpu(ex4, to_device(wl))
+        compare(gpu, run_oracle(ex4, wl, [0, 1]), [0, 1], wl["noise"], f"P={P} lengths={lens}")
+
+
+def test_edge_full_overwrite_and_four_steps():
+    _say("edge cases: d = 50, 4 Euler steps")
+    ex = Expert(4, n_steps=4, max_batch=4, max_prefix=256)
+    try:
+        wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
+        wl["prev_actions"] = synth.draw_prev_actions(2, 50)
+        gpu = run_gpu(ex, to_device(wl), d=50)
+        compare(gpu, run_oracle(ex, wl, [0, 1], d=50), [0, 1], wl["noise"], "d=50 n=4")
+    finally:
+        ex.close()
+
+
+def test_gain_variant_parity():
+    _say("RMSNorm gains 1 + N(0, 0.1)")
+    ex = Expert(4, max_batch=4, max_prefix=256, gain_seed=synth.gen.SEED_GAINS)
+    try:
+        wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
+        compare(run_gpu(ex, to_device(wl)), run_oracle(ex, wl, [0, 1]), [0, 1], wl["noise"], "gain variant")
+    finally:
+        ex.close()
+
+
+def test_graph_replay_matches_direct_launches(ex4):
+    _say("graph replay vs direct launches")
+    direct = Expert(4, max_batch=16, max_prefix=512, use_graphs=0, with_oracle=False)
+    try:
+        wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
+        dev = to_device(wl)
+        ref = run_gpu(direct, dev)
+        for _ in range(3):
+            got = run_gpu(ex4, dev)
+            junk = torch.randn(1 << 20, device="cuda")
+            (junk * 2).sum().item()          # eager work between replays
+            for k in ref:
+                np.testing.assert_array_equal(got[k], ref[k])
+    finally:
+        direct.close()
+
+
+def test_time_kernel_hook(ex4):
+    _say("time_kernel hook")
+    wl = synth.make_workload("expert4_b1_p177", with_weights=False)
+    run_gpu(ex4, to_device(wl))
+    for k in range(8):
+        us = fm.smolexp_time_kernel(ex4.h, k, 3)
+        assert 0.0 < us < 1e6
