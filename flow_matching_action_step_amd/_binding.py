@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libsmolexp.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m flow_matching_action_step_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python flow_matching_action_step_amd/build.py` "
         "(hipcc, gfx950). There is no fallback implementation.")
 _lib = ctypes.CDLL(LIB_PATH)
 

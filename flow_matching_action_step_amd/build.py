@@ -1,6 +1,7 @@
 """Build libsmolexp.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Run as ``python -m flow_matching_action_step_amd.build``; no GPU is needed.
+Run as ``python flow_matching_action_step_amd/build.py`` (by path: importing the
+package would load the library it is about to rebuild); no GPU is needed.
 """
 import os
 import subprocess
@@ -24,7 +25,7 @@ def build(verbose=False):
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-mcode-object-version=5", "-fPIC", "-shared",
            # no packed-fp32 instructions in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function",
+           "-Wall", "-Wno-unused-function", "-Wl,--no-undefined",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
            "-o", tmp] + SOURCES
     if verbose:

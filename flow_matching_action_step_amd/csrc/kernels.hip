@@ -43,313 +43,409 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 // ----------------------------------------------------------------------------
 // GEMM
 // ----------------------------------------------------------------------------
+// Two kernels share the A-operand loaders and the epilogues:
+//  * gemm_skinny (M <= 64, one query): one 512-thread workgroup per 16 output
+//    columns.  Its 8 waves split K; each wave issues every load it needs (its
+//    weight fragments and A fragments) at once, so the kernel waits for memory
+//    about once, then the waves' partial tiles meet in LDS.
+//  * gemm_tiled (M > 64): 128 x 128 output tiles, four waves of 64 x 64,
+//    BK = 64 slabs double-buffered in LDS.
+// Epilogues run on the finished fp32 tile staged in LDS.
+//
+// Weight row order inside each 16-row block (set by the host when it loads
+// the weights) keeps every pair an epilogue needs in one block:
+//  * Q and K heads: block q of a head holds dims q*8..q*8+7, then 32+q*8..
+//    32+q*8+7, so column e pairs with e+8 for the rotation of (d, d+32);
+//  * gate/up: block j holds gate rows 8j..8j+7, then up rows 8j..8j+7;
+//  * V heads and every other matrix keep their natural order.
 
-// Tile: WM x WN x WK waves (4 in total); each wave owns FM x 4 MFMA 16x16
-// tiles (16*FM rows x 64 columns) and KS/WK of the KS 32-wide k-steps of a
-// BK = 32*KS slab.  With WK > 1 the waves split K and reduce through LDS.
-template <int WM_, int WN_, int WK_, int FM_, int KS_>
-struct TileT {
-  static constexpr int WM = WM_, WN = WN_, WK = WK_, FM = FM_, FN = 4, KS = KS_;
-  static constexpr int BM = WM * FM * 16, BN = WN * FN * 16, BK = KS * 32, LDK = BK + 8;
-  static constexpr int CPR = BK / 8;              // 8-element chunks per slab row
-  static constexpr int GA = BM * BK / 8 / 256;    // A chunks per thread
-  static constexpr int GW = BN * BK / 8 / 256;    // W chunks per thread
-  static constexpr int TILE_BYTES = (BM + BN) * LDK * 2;
-  static constexpr int RED_BYTES = (WK - 1) * WM * WN * FM * FN * 4 * 64 * 4;
-  static constexpr int SMEM = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
-  static_assert(WM * WN * WK == 4, "four waves");
-  static_assert(KS % WK == 0, "k-steps split evenly");
-  static_assert(GA * 256 * 8 == BM * BK && GW * 256 * 8 == BN * BK, "whole chunks per thread");
-};
-using SkinnyTile = TileT<1, 1, 4, 4, 4>;  // 64 x 64, BK 128, K split over the 4 waves
-using MedTile = TileT<2, 2, 1, 2, 2>;     // 64 x 128, BK 64
-
-template <class T, int AM, int EM>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[T::SMEM];
-  __shared__ float sR[T::BM];
-  __shared__ float sSS[T::WN][T::BM];
-  half_t* sA = reinterpret_cast<half_t*>(smem);
-  half_t* sW = sA + T::BM * T::LDK;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wk = wave % T::WK;
-  const int wn = (wave / T::WK) % T::WN;
-  const int wm = wave / (T::WK * T::WN);
-  const int m0 = blockIdx.x * T::BM, n0 = blockIdx.y * T::BN;
-  const int M = a.M, N = a.N, K = a.K;
-
-  if constexpr (AM == A_NORM) {
-    // RMSNorm row scale 1/sqrt(mean(h^2) + eps) from the producer's partial sums.
-    for (int r = tid; r < T::BM; r += 256) {
-      const int row = m0 + r;
-      float s = 0.f;
-      if (row < M)
-        for (int j = 0; j < a.ss_nt; ++j) s += a.ss_in[(size_t)row * kSSStride + j];
-      sR[r] = 1.0f / sqrtf(s * a.inv_k + a.eps);
+// Eight consecutive A elements of row `row`, columns k..k+7, converted to the
+// fp16 MFMA operand (ok = inside the matrix; otherwise zeros).
+template <int AM>
+__device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool ok, float rscale,
+                                         bool write_x) {
+  if constexpr (AM == A_F16) {
+    return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + (size_t)row * a.lda + k)
+              : make_uint4(0, 0, 0, 0);
+  } else if constexpr (AM == A_NORM) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
+      const float4 h0 = *reinterpret_cast<const float4*>(p), h1 = *reinterpret_cast<const float4*>(p + 4);
+      const float4 g0 = *reinterpret_cast<const float4*>(a.gain + k), g1 = *reinterpret_cast<const float4*>(a.gain + k + 4);
+      v[0] = h0.x * rscale * g0.x; v[1] = h0.y * rscale * g0.y; v[2] = h0.z * rscale * g0.z; v[3] = h0.w * rscale * g0.w;
+      v[4] = h1.x * rscale * g1.x; v[5] = h1.y * rscale * g1.y; v[6] = h1.z * rscale * g1.z; v[7] = h1.w * rscale * g1.w;
     }
-    __syncthreads();
-  }
-
-  uint4 ra[T::GA];
-  float4 rf[2 * T::GA];
-  float4 rg[2 * T::GA];
-  uint4 rw[T::GW];
-
-  auto load = [&](int kt) {
-    const int kb = kt * T::BK;
-#pragma unroll
-    for (int i = 0; i < T::GA; ++i) {
-      const int g = tid + 256 * i, r = g / T::CPR, c = (g % T::CPR) * 8;
-      const int row = m0 + r, k = kb + c;
-      const bool ok = row < M && k < K;
-      if constexpr (AM == A_F16) {
-        ra[i] = ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + (size_t)row * a.lda + k)
-                   : make_uint4(0, 0, 0, 0);
-      } else if constexpr (AM == A_NORM) {
-        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-        rf[2 * i] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-        rf[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        rg[2 * i] = ok ? *reinterpret_cast<const float4*>(a.gain + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-        rg[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(a.gain + k + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {  // A_X: Euler state, rows i < ow_rows of each chunk replaced by the flow-path point
-        float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-        if (ok) {
-          const int ci = row % kChunk;
-          if (ci < a.ow_rows) {
-            const int b = row / kChunk;
-            const float* ep = a.noise + (size_t)row * kAD + k;
-            const float* pp = a.prev + ((size_t)b * a.ow_rows + ci) * kAD + k;
-            const float4 e0 = *reinterpret_cast<const float4*>(ep), e1 = *reinterpret_cast<const float4*>(ep + 4);
-            const float4 p0 = *reinterpret_cast<const float4*>(pp), p1 = *reinterpret_cast<const float4*>(pp + 4);
-            const float t = a.t, u = 1.0f - a.t;
-            v0 = make_float4(t * e0.x + u * p0.x, t * e0.y + u * p0.y, t * e0.z + u * p0.z, t * e0.w + u * p0.w);
-            v1 = make_float4(t * e1.x + u * p1.x, t * e1.y + u * p1.y, t * e1.z + u * p1.z, t * e1.w + u * p1.w);
-            if (blockIdx.y == 0) {  // the state itself takes the overwritten rows
-              float* xp = a.x + (size_t)row * kAD + k;
-              *reinterpret_cast<float4*>(xp) = v0;
-              *reinterpret_cast<float4*>(xp + 4) = v1;
-            }
-          } else {
-            const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-            v0 = *reinterpret_cast<const float4*>(p);
-            v1 = *reinterpret_cast<const float4*>(p + 4);
-          }
+    return pack8(v);
+  } else {  // A_X: Euler state; rows i < ow_rows of each chunk take the flow-path point t*eps + (1-t)*prev
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+    if (ok) {
+      const int ci = row % kChunk;
+      if (ci < a.ow_rows) {
+        const int b = row / kChunk;
+        const float* ep = a.noise + (size_t)row * kAD + k;
+        const float* pp = a.prev + ((size_t)b * a.ow_rows + ci) * kAD + k;
+        const float4 e0 = *reinterpret_cast<const float4*>(ep), e1 = *reinterpret_cast<const float4*>(ep + 4);
+        const float4 p0 = *reinterpret_cast<const float4*>(pp), p1 = *reinterpret_cast<const float4*>(pp + 4);
+        const float t = a.t, u = 1.0f - a.t;
+        v0 = make_float4(t * e0.x + u * p0.x, t * e0.y + u * p0.y, t * e0.z + u * p0.z, t * e0.w + u * p0.w);
+        v1 = make_float4(t * e1.x + u * p1.x, t * e1.y + u * p1.y, t * e1.z + u * p1.z, t * e1.w + u * p1.w);
+        if (write_x) {  // one workgroup column stores the overwritten rows into the state
+          float* xp = a.x + (size_t)row * kAD + k;
+          *reinterpret_cast<float4*>(xp) = v0;
+          *reinterpret_cast<float4*>(xp + 4) = v1;
         }
-        rf[2 * i] = v0;
-        rf[2 * i + 1] = v1;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < T::GW; ++i) {
-      const int g = tid + 256 * i, r = g / T::CPR, c = (g % T::CPR) * 8;
-      const int n = n0 + r, k = kb + c;
-      rw[i] = (n < N && k < K) ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * a.ldw + k)
-                               : make_uint4(0, 0, 0, 0);
-    }
-  };
-
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::GA; ++i) {
-      const int g = tid + 256 * i, r = g / T::CPR, c = (g % T::CPR) * 8;
-      uint4* dst = reinterpret_cast<uint4*>(sA + r * T::LDK + c);
-      if constexpr (AM == A_F16) {
-        *dst = ra[i];
       } else {
-        float v[8] = {rf[2 * i].x, rf[2 * i].y, rf[2 * i].z, rf[2 * i].w,
-                      rf[2 * i + 1].x, rf[2 * i + 1].y, rf[2 * i + 1].z, rf[2 * i + 1].w};
-        if constexpr (AM == A_NORM) {
-          const float sc = sR[r];
-          const float gv[8] = {rg[2 * i].x, rg[2 * i].y, rg[2 * i].z, rg[2 * i].w,
-                               rg[2 * i + 1].x, rg[2 * i + 1].y, rg[2 * i + 1].z, rg[2 * i + 1].w};
+        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
+        v0 = *reinterpret_cast<const float4*>(p);
+        v1 = *reinterpret_cast<const float4*>(p + 4);
+      }
+    }
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    return pack8(v);
+  }
+}
+
+// RMSNorm row scales 1/sqrt(mean(h^2) + eps) for rows m0..m0+BM-1 from the
+// producer's per-N-tile partial sums of squares.  NT/BM threads share a row
+// and sum every (NT/BM)-th partial, so the loads are issued side by side.
+template <int BM, int NT>
+__device__ __forceinline__ void row_scales(const GemmArgs& a, int m0, float* sR) {
+  constexpr int TPR = NT / BM;
+  static_assert(TPR >= 1 && TPR <= 64 && (TPR & (TPR - 1)) == 0, "threads per row: a power of two within a wave");
+  const int r = threadIdx.x / TPR, part = threadIdx.x % TPR, row = m0 + r;
+  float s = 0.f;
+  if (row < a.M) {
+    const float* src = a.ss_in + (size_t)row * kSSStride;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = v[e] * sc * gv[e];
+    for (int j0 = 0; j0 < kSSStride; j0 += TPR) {
+      const int j = j0 + part;
+      if (j < a.ss_nt) s += src[j];
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (part == 0) sR[r] = 1.0f / sqrtf(s * a.inv_k + a.eps);
+}
+
+// Epilogue on a finished tile sC[BM][LDC] (fp32, weight scale applied) whose
+// rows start at m0 and columns at n0 (BN a multiple of 16).  Work unit =
+// (row, 16-column block, e < 8) covering columns e and e + 8 of the block;
+// the units of one row are consecutive lanes of one wave.  ntile = this
+// tile's sum-of-squares slot.
+template <int EM, int BM, int BN, int LDC, int NT>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0, int ntile) {
+  constexpr int NB = BN / 16, UPR = NB * 8;
+  static_assert(UPR <= 64 && 64 % UPR == 0 && (BM * UPR) % NT == 0, "rows inside one wave, uniform trip count");
+  const int M = a.M, N = a.N;
+  for (int g = threadIdx.x; g < BM * UPR; g += NT) {
+    const int r = g / UPR, blk = (g % UPR) / 8, e = g % 8;
+    const int row = m0 + r, cb = n0 + blk * 16;
+    const bool ok = row < M && cb < N;
+    const float v1 = sC[r * LDC + blk * 16 + e], v2 = sC[r * LDC + blk * 16 + 8 + e];
+    float ss = 0.f;
+    if (ok) {
+      if constexpr (EM == E_QKV) {
+        const int head = cb / kHD, b = row / kChunk, ci = row % kChunk;
+        bf16_t* dst;
+        if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
+        else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
+        else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
+        if (head < kHQ + kHKV) {  // rotate the pair (d, d + 32) at position n_valid + i
+          const int d = ((cb % kHD) / 16) * 8 + e;
+          const float2 cs = a.rope[(size_t)(a.nvalid[b] + ci) * (kHD / 2) + d];
+          dst[d] = f2bf(v1 * cs.x - v2 * cs.y);
+          dst[d + kHD / 2] = f2bf(v1 * cs.y + v2 * cs.x);
+        } else {
+          const int d = cb % kHD + e;
+          dst[d] = f2bf(v1);
+          dst[d + 8] = f2bf(v2);
         }
-        *dst = pack8(v);
+      } else if constexpr (EM == E_SWIGLU) {
+        a.out16[(size_t)row * a.ldo + cb / 2 + e] = (half_t)(silu(v1) * v2);
+      } else if constexpr (EM == E_F16_BIAS || EM == E_TIMEIN) {
+        const float z1 = v1 + a.bias[cb + e], z2 = v2 + a.bias[cb + 8 + e];
+        half_t* o = a.out16 + (size_t)row * a.ldo + cb + e;
+        o[0] = (half_t)(EM == E_TIMEIN ? silu(z1) : z1);
+        o[8] = (half_t)(EM == E_TIMEIN ? silu(z2) : z2);
+      } else if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
+        float* hp = a.h + (size_t)row * kD + cb + e;
+        const float h1 = (EM == E_H_BIAS) ? v1 + a.bias[cb + e] : hp[0] + v1;
+        const float h2 = (EM == E_H_BIAS) ? v2 + a.bias[cb + 8 + e] : hp[8] + v2;
+        hp[0] = h1;
+        hp[8] = h2;
+        ss = h1 * h1 + h2 * h2;
+      } else if constexpr (EM == E_ACTOUT) {
+        const size_t xi = (size_t)row * kAD + cb + e;
+        const float u1 = v1 + a.bias[cb + e], u2 = v2 + a.bias[cb + 8 + e];
+        const float x1 = a.x[xi] + a.dt * u1, x2 = a.x[xi + 8] + a.dt * u2;
+        a.x[xi] = x1;
+        a.x[xi + 8] = x2;
+        if (a.vel_out) { a.vel_out[xi] = u1; a.vel_out[xi + 8] = u2; }
+        if (a.st_out) { a.st_out[xi] = x1; a.st_out[xi + 8] = x2; }
+        if (a.final_out) { a.final_out[xi] = x1; a.final_out[xi + 8] = x2; }
       }
     }
+    if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
 #pragma unroll
-    for (int i = 0; i < T::GW; ++i) {
-      const int g = tid + 256 * i, r = g / T::CPR, c = (g % T::CPR) * 8;
-      *reinterpret_cast<uint4*>(sW + r * T::LDK + c) = rw[i];
-    }
-  };
-
-  f32x4 acc[T::FM][T::FN];
-#pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = (K + T::BK - 1) / T::BK;
-  load(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    store();
-    __syncthreads();
-    if (kt + 1 < nk) load(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < T::KS / T::WK; ++kk) {
-      const int ks = kk * T::WK + wk;
-      f16x8 af[T::FM], bw[T::FN];
-#pragma unroll
-      for (int fm = 0; fm < T::FM; ++fm)
-        af[fm] = *reinterpret_cast<const f16x8*>(
-            sA + (wm * T::FM * 16 + fm * 16 + (lane & 15)) * T::LDK + ks * 32 + (lane >> 4) * 8);
-#pragma unroll
-      for (int fn = 0; fn < T::FN; ++fn)
-        bw[fn] = *reinterpret_cast<const f16x8*>(
-            sW + (wn * 64 + fn * 16 + (lane & 15)) * T::LDK + ks * 32 + (lane >> 4) * 8);
-#pragma unroll
-      for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  if constexpr (T::WK > 1) {
-    // Waves that split K hand their partial tiles to wave wk == 0 through LDS.
-    float* red = reinterpret_cast<float*>(smem);
-    const int slot = wm * T::WN + wn;
-    constexpr int PER = T::FM * T::FN * 4 * 64;
-    if (wk > 0) {
-      float* dst = red + ((wk - 1) * T::WM * T::WN + slot) * PER;
-#pragma unroll
-      for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[((fm * T::FN + fn) * 4 + r) * 64 + lane] = acc[fm][fn][r];
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int w = 1; w < T::WK; ++w) {
-        const float* src = red + ((w - 1) * T::WM * T::WN + slot) * PER;
-#pragma unroll
-        for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < T::FN; ++fn)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[fm][fn][r] += src[((fm * T::FN + fn) * 4 + r) * 64 + lane];
-      }
-    }
-  }
-
-  // ---------------- epilogue: lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 tile
-  const float ws = a.w_scale;
-  const int cbase = n0 + wn * 64;  // first column of this wave (64 wide)
-  if (wk == 0) {
-#pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * T::FM * 16 + fm * 16 + (lane >> 4) * 4 + r;
-        const int row = m0 + rl;
-        const bool rok = row < M;
-        if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
-          float ss = 0.f;
-#pragma unroll
-          for (int fn = 0; fn < T::FN; ++fn) {
-            const int col = cbase + fn * 16 + (lane & 15);
-            if (rok && col < N) {
-              float* hp = a.h + (size_t)row * kD + col;
-              const float v = acc[fm][fn][r] * ws;
-              const float hv = (EM == E_H_BIAS) ? v + a.bias[col] : *hp + v;
-              *hp = hv;
-              ss += hv * hv;
-            }
-          }
-          ss += __shfl_xor(ss, 1);
-          ss += __shfl_xor(ss, 2);
-          ss += __shfl_xor(ss, 4);
-          ss += __shfl_xor(ss, 8);
-          if ((lane & 15) == 0) sSS[wn][rl] = ss;
-        } else if constexpr (EM == E_F16_BIAS || EM == E_TIMEIN) {
-#pragma unroll
-          for (int fn = 0; fn < T::FN; ++fn) {
-            const int col = cbase + fn * 16 + (lane & 15);
-            if (rok && col < N) {
-              const float z = acc[fm][fn][r] * ws + a.bias[col];
-              a.out16[(size_t)row * a.ldo + col] = (half_t)(EM == E_TIMEIN ? silu(z) : z);
-            }
-          }
-        } else if constexpr (EM == E_QKV) {
-          // The wave's 64 columns are one head: Q heads 0..14, K heads 15..19, V heads 20..24.
-          const int head = cbase / kHD;
-          if (rok && cbase < N) {
-            const int b = row / kChunk, ci = row % kChunk;
-            const int pos = a.nvalid[b] + ci;
-            bf16_t* dst;
-            if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
-            else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
-            else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
-#pragma unroll
-            for (int fn = 0; fn < 2; ++fn) {
-              const int d = fn * 16 + (lane & 15);
-              const float x1 = acc[fm][fn][r] * ws, x2 = acc[fm][fn + 2][r] * ws;
-              float y1 = x1, y2 = x2;
-              if (head < kHQ + kHKV) {  // rotate pairs (d, d + 32)
-                const float2 cs = a.rope[pos * (kHD / 2) + d];
-                y1 = x1 * cs.x - x2 * cs.y;
-                y2 = x1 * cs.y + x2 * cs.x;
-              }
-              dst[d] = f2bf(y1);
-              dst[d + kHD / 2] = f2bf(y2);
-            }
-          }
-        } else if constexpr (EM == E_SWIGLU) {
-          // 16-row blocks alternate gate/up: tiles (0,1) and (2,3) are matching pairs.
-          if (rok && cbase < N) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              const float gt = acc[fm][2 * p][r] * ws, up = acc[fm][2 * p + 1][r] * ws;
-              a.out16[(size_t)row * a.ldo + cbase / 2 + p * 16 + (lane & 15)] = (half_t)(silu(gt) * up);
-            }
-          }
-        } else if constexpr (EM == E_ACTOUT) {
-#pragma unroll
-          for (int fn = 0; fn < T::FN; ++fn) {
-            const int col = cbase + fn * 16 + (lane & 15);
-            if (rok && col < N) {
-              const float v = acc[fm][fn][r] * ws + a.bias[col];
-              const size_t xi = (size_t)row * kAD + col;
-              const float xn = a.x[xi] + a.dt * v;
-              a.x[xi] = xn;
-              if (a.vel_out) a.vel_out[xi] = v;
-              if (a.st_out) a.st_out[xi] = xn;
-              if (a.final_out) a.final_out[xi] = xn;
-            }
-          }
-        }
-      }
-    }
-  }
-  if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
-    __syncthreads();
-    for (int r = tid; r < T::BM; r += 256) {
-      const int row = m0 + r;
-      if (row < M) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < T::WN; ++w) s += sSS[w][r];
-        a.ss_out[(size_t)row * kSSStride + blockIdx.y] = s;
-      }
+      for (int off = UPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      if (g % UPR == 0 && row < M) a.ss_out[(size_t)row * kSSStride + ntile] = ss;
     }
   }
 }
 
-template <class T>
-static hipError_t launch_gemm_t(AMode am, EMode em, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((a.M + T::BM - 1) / T::BM, (a.N + T::BN - 1) / T::BN);
-  const dim3 block(256);
-#define SMOLEXP_GEMM_CASE(AMV, EMV)                                     \
-  if (am == AMV && em == EMV) {                                          \
-    hipLaunchKernelGGL((gemm_kernel<T, AMV, EMV>), grid, block, 0, s, a); \
-    return hipGetLastError();                                            \
+// M <= 64.  One workgroup per 16 output columns; wave w takes k-steps
+// w*KPW .. w*KPW+KPW-1 (32 wide each).
+template <int AM, int EM, int KPW>
+__global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
+  constexpr int NW = 8, LDC = 16;
+  __shared__ float sRed[NW * 64 * 16];
+  __shared__ float sC[64 * LDC];
+  __shared__ float sR[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int M = a.M, N = a.N, K = a.K;
+  const int nks = (K + 31) / 32;
+  const int n = n0 + (lane & 15), kl = (lane >> 4) * 8;
+
+  uint4 wf[KPW];
+  uint4 af[KPW][4];
+  float4 ra[AM == A_NORM ? KPW : 1][4][2];
+  float4 gv[AM == A_NORM ? KPW : 1][2];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int ks = w * KPW + i, k = ks * 32 + kl;
+    const bool kok = ks < nks && k < K;
+    wf[i] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * a.ldw + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const int row = fm * 16 + (lane & 15);
+      const bool ok = kok && row < M;
+      if constexpr (AM == A_NORM) {
+        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
+        ra[i][fm][0] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[i][fm][1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, blockIdx.x == 0);
+      }
+    }
+    if constexpr (AM == A_NORM) {
+      gv[i][0] = kok ? *reinterpret_cast<const float4*>(a.gain + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      gv[i][1] = kok ? *reinterpret_cast<const float4*>(a.gain + k + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
+  if constexpr (AM == A_NORM) {
+    row_scales<64, 512>(a, 0, sR);
+    __syncthreads();
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) acc[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const f16x8 bw = __builtin_bit_cast(f16x8, wf[i]);
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      uint4 frag;
+      if constexpr (AM == A_NORM) {
+        const float sc = sR[fm * 16 + (lane & 15)];
+        const float v[8] = {ra[i][fm][0].x * sc * gv[i][0].x, ra[i][fm][0].y * sc * gv[i][0].y,
+                            ra[i][fm][0].z * sc * gv[i][0].z, ra[i][fm][0].w * sc * gv[i][0].w,
+                            ra[i][fm][1].x * sc * gv[i][1].x, ra[i][fm][1].y * sc * gv[i][1].y,
+                            ra[i][fm][1].z * sc * gv[i][1].z, ra[i][fm][1].w * sc * gv[i][1].w};
+        frag = pack8(v);
+      } else {
+        frag = af[i][fm];
+      }
+      acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, frag), bw, acc[fm], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sRed[(w * 64 + fm * 16 + (lane >> 4) * 4 + r) * 16 + (lane & 15)] = acc[fm][r];
+  __syncthreads();
+  const float ws = a.w_scale;
+  for (int i = tid; i < 64 * 16; i += 512) {
+    float s = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * 64 * 16 + i];
+    sC[(i / 16) * LDC + (i % 16)] = s * ws;
+  }
+  __syncthreads();
+  epilogue_tile<EM, 64, 16, LDC, 512>(a, sC, 0, n0, blockIdx.x);
+}
+
+// FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
+template <int AM, int EM, int FM>
+__global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
+  constexpr int BM = 32 * FM, BN = 128, BK = 64, LDK = BK + 8, LDC = BN + 4, CPR = BK / 8;
+  constexpr int GA = BM * CPR / 256, GW = BN * CPR / 256;
+  constexpr int STAGE = (BM + BN) * LDK;  // halves
+  constexpr int SMEM = 2 * STAGE * 2 > BM * LDC * 4 ? 2 * STAGE * 2 : BM * LDC * 4;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ float sR[BM];
+  __shared__ float sG[AM == A_NORM ? kD : 1];
+  half_t* stage0 = reinterpret_cast<half_t*>(smem);
+  float* sC = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int mt = blockIdx.x, nt = blockIdx.y;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int M = a.M, N = a.N, K = a.K;
+  const int nk = (K + BK - 1) / BK;
+
+  if constexpr (AM == A_NORM) {
+    row_scales<BM, 256>(a, m0, sR);
+    for (int k = tid; k < K; k += 256) sG[k] = a.gain[k];
+    __syncthreads();
+  }
+  uint4 ra[GA], rw[GW];
+  float4 rf[AM == A_NORM ? 2 * GA : 1];  // A_NORM: raw fp32 rows, converted when stored to LDS
+  auto load = [&](int kt) {
+    const int kb = kt * BK;
+#pragma unroll
+    for (int i = 0; i < GA; ++i) {
+      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8, row = m0 + r, k = kb + c;
+      const bool ok = row < M && k < K;
+      if constexpr (AM == A_NORM) {
+        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
+        rf[2 * i] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+        rf[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8, n = n0 + r, k = kb + c;
+      rw[i] = (n < N && k < K) ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * a.ldw + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf, int kt) {
+    half_t* sA = stage0 + buf * STAGE;
+    half_t* sW = sA + BM * LDK;
+    const int kb = kt * BK;
+#pragma unroll
+    for (int i = 0; i < GA; ++i) {
+      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8;
+      uint4 v;
+      if constexpr (AM == A_NORM) {
+        const float sc = sR[r];
+        const int k = kb + c;
+        const bool kin = k < K;
+        float f[8] = {rf[2 * i].x, rf[2 * i].y, rf[2 * i].z, rf[2 * i].w,
+                      rf[2 * i + 1].x, rf[2 * i + 1].y, rf[2 * i + 1].z, rf[2 * i + 1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = kin ? f[e] * sc * sG[k + e] : 0.f;
+        v = pack8(f);
+      } else {
+        v = ra[i];
+      }
+      *reinterpret_cast<uint4*>(sA + r * LDK + c) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int g = tid + 256 * i;
+      *reinterpret_cast<uint4*>(sW + (g / CPR) * LDK + (g % CPR) * 8) = rw[i];
+    }
+  };
+
+  f32x4 acc[FM][4];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  store(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load(kt + 1);
+    const half_t* sA = stage0 + (kt & 1) * STAGE;
+    const half_t* sW = sA + BM * LDK;
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      f16x8 af[FM], bw[4];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *reinterpret_cast<const f16x8*>(sA + (wm * FM * 16 + fm * 16 + (lane & 15)) * LDK + s * 32 + (lane >> 4) * 8);
+#pragma unroll
+      for (int fn = 0; fn < 4; ++fn)
+        bw[fn] = *reinterpret_cast<const f16x8*>(sW + (wn * 64 + fn * 16 + (lane & 15)) * LDK + s * 32 + (lane >> 4) * 8);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store((kt + 1) & 1, kt + 1);
+    __syncthreads();
+  }
+
+  const float ws = a.w_scale;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sC[(wm * FM * 16 + fm * 16 + (lane >> 4) * 4 + r) * LDC + wn * 64 + fn * 16 + (lane & 15)] = acc[fm][fn][r] * ws;
+  __syncthreads();
+  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0, nt);
+}
+
+GemmPlan plan_gemm(int M, int N, int K) {
+  GemmPlan p;
+  const int nks = (K + 31) / 32;
+  p.bm = 64;
+  if (M <= 64) {
+    p.kind = 0;
+    p.ntiles_n = (N + 15) / 16;
+    const int need = (nks + 7) / 8;
+    p.kpw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : need <= 8 ? 8 : 0;
+  } else {
+    p.kind = 1;
+    p.ntiles_n = (N + 127) / 128;
+    p.kpw = 0;
+    p.bm = N <= 1024 ? 64 : 128;  // measured: 64-row tiles fill the chip better for N = 720/960
+  }
+  return p;
+}
+
+template <int AM, int EM>
+static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  if (p.kind == 0) {
+    const dim3 grid(p.ntiles_n), block(512);
+    switch (p.kpw) {
+      case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4>), grid, block, 0, s, a); break;
+      case 6:
+      case 8:
+        // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
+        // variants would not fit their fragments in registers
+        if constexpr (AM == A_F16) {
+          if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6>), grid, block, 0, s, a);
+          else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8>), grid, block, 0, s, a);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;  // K beyond 8 waves x 8 k-steps x 32
+    }
+  } else {
+    const dim3 grid((a.M + p.bm - 1) / p.bm, p.ntiles_n);
+    if (p.bm == 128) hipLaunchKernelGGL((gemm_tiled<AM, EM, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_tiled<AM, EM, 2>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s) {
+#define SMOLEXP_GEMM_CASE(AMV, EMV) \
+  if (am == AMV && em == EMV) return launch_gemm_t<AMV, EMV>(p, a, s);
   SMOLEXP_GEMM_CASE(A_X, E_F16_BIAS)
   SMOLEXP_GEMM_CASE(A_F16, E_TIMEIN)
   SMOLEXP_GEMM_CASE(A_F16, E_H_BIAS)
@@ -359,16 +455,6 @@ static hipError_t launch_gemm_t(AMode am, EMode em, const GemmArgs& a, hipStream
   SMOLEXP_GEMM_CASE(A_NORM, E_ACTOUT)
 #undef SMOLEXP_GEMM_CASE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm(TileCfg cfg, AMode am, EMode em, const GemmArgs& a, hipStream_t s) {
-  if (cfg == T_SKINNY) return launch_gemm_t<SkinnyTile>(am, em, a, s);
-  return launch_gemm_t<MedTile>(am, em, a, s);
-}
-
-int gemm_ntiles(TileCfg cfg, int N) {
-  const int bn = cfg == T_SKINNY ? SkinnyTile::BN : MedTile::BN;
-  return (N + bn - 1) / bn;
 }
 
 // ----------------------------------------------------------------------------
@@ -381,13 +467,20 @@ int gemm_ntiles(TileCfg cfg, int N) {
 // transposed (S^T = K Q^T) so that each lane owns one query row; the output is
 // accumulated transposed as well (O^T += V^T P^T).
 constexpr int kKB = 64;        // keys per block
-constexpr int kALD = kHD + 8;  // LDS row stride (elements)
+constexpr int kALD = kHD + 8;  // LDS row stride of K (elements)
 
-template <bool SELF>
+// NBLK key blocks are staged per round: all of their loads are issued before
+// the first is stored, so a round costs one memory round trip.  Small batches
+// stage five blocks (320 keys: a whole prefix plus the chunk), large batches
+// one block per round and more workgroups per CU.
+template <bool SELF, int NBLK>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[kKB * kALD];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * kALD];
-  __shared__ uint8_t sKind[kKB];  // 0 = no key, 1 = valid prefix key, 2 = chunk key
+  constexpr int RK = NBLK * kKB;     // keys per round
+  constexpr int VLD = RK + 8;        // LDS row stride of V^T (elements)
+  constexpr int NV = NBLK * 2;       // 16-byte vectors per thread for K (and for V) per round
+  __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * VLD];
+  __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];  // 0 = no key, 1 = valid prefix key, 2 = chunk key
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.y, b = blockIdx.z;
@@ -413,7 +506,6 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int NK = P + (SELF ? kChunk : 0);
-  const int nblk = (NK + kKB - 1) / kKB;
   const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
   const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
   const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : nullptr;
@@ -421,102 +513,125 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   const uint8_t* mk = a.mask + (size_t)b * P;
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
 
-  for (int kb = 0; kb < nblk; ++kb) {
-    __syncthreads();
-    if (tid < kKB) {
-      const int j = kb * kKB + tid;
-      sKind[tid] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+  for (int r0 = 0; r0 < NK; r0 += RK) {
+    __syncthreads();  // the previous round's LDS reads are done
+    for (int i = tid; i < RK; i += 256) {
+      const int j = r0 + i;
+      sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
     }
+    // Branch-free staging: every address is clamped into its buffer and the
+    // loaded vector is zeroed afterwards for masked or missing keys, so all
+    // loads of the round are in flight together.
+    uint4 kv[NV], vv[NV];
+    bool kok[NV], vok[NV];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < NV; ++it) {
       const int v = tid + 256 * it;
-      {  // K, row-major: 8 lanes per key row
-        const int jl = v >> 3, c = (v & 7) * 8, j = kb * kKB + jl;
-        uint4 kv = make_uint4(0, 0, 0, 0);
-        if (j < P) {
-          if (mk[j]) kv = *reinterpret_cast<const uint4*>(pk + (size_t)j * kHD + c);
-        } else if (SELF && j - P < kChunk) {
-          kv = *reinterpret_cast<const uint4*>(ck + (size_t)(j - P) * kHD + c);
-        }
-        *reinterpret_cast<uint4*>(sK + jl * kALD + c) = kv;
+      {  // K rows: 8 lanes per key
+        const int j = r0 + (v >> 3), c = (v & 7) * 8;
+        const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+        const bf16_t* src = pre ? pk + (size_t)j * kHD + c
+                                : (chunk ? ck + (size_t)(j - P) * kHD + c : pk + c);
+        kv[it] = *reinterpret_cast<const uint4*>(src);
+        kok[it] = pre ? mk[j] != 0 : chunk;
       }
-      {  // V, stored transposed [d][key]: consecutive lanes take consecutive keys
-        const int jl = v & 63, c = (v >> 6) * 8, j = kb * kKB + jl;
-        uint4 vv = make_uint4(0, 0, 0, 0);
-        if (j < P) {
-          if (mk[j]) vv = *reinterpret_cast<const uint4*>(pv + (size_t)j * kHD + c);
-        } else if (SELF && j - P < kChunk) {
-          vv = *reinterpret_cast<const uint4*>(cv + (size_t)(j - P) * kHD + c);
-        }
-        const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv);
+      {  // V rows for the transposed store: consecutive lanes take consecutive keys
+        const int j = r0 + (v % RK), c = (v / RK) * 8;
+        const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+        const bf16_t* src = pre ? pv + (size_t)j * kHD + c
+                                : (chunk ? cv + (size_t)(j - P) * kHD + c : pv + c);
+        vv[it] = *reinterpret_cast<const uint4*>(src);
+        vok[it] = pre ? mk[j] != 0 : chunk;
+      }
+    }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) sVt[(c + t) * kALD + jl] = e[t];
-      }
+    for (int it = 0; it < NV; ++it) {
+      if (!kok[it]) kv[it] = make_uint4(0, 0, 0, 0);
+      if (!vok[it]) vv[it] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int v = tid + 256 * it;
+      *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
+      const int jl = v % RK, c = (v / RK) * 8;
+      const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv[it]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sVt[(c + t) * VLD + jl] = e[t];
     }
     __syncthreads();
 
-    // S^T[key][row] for the 64 keys of the block (4 tiles of 16 keys)
-    f32x4 s[4];
+    const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
+    for (int blk = 0; blk < nb; ++blk) {
+      const int kb0 = r0 + blk * kKB;  // first key of this block
+      // S^T[key][row] for the 64 keys of the block (4 tiles of 16 keys)
+      f32x4 sc[4];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sub = 0; sub < 4; ++sub) {
+        sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 u = *reinterpret_cast<const uint4*>(sK + (sub * 16 + (lane & 15)) * kALD + kk * 32 + (lane >> 4) * 8);
-        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], s[sub], 0, 0, 0);
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint4 u = *reinterpret_cast<const uint4*>(
+              sK + (blk * kKB + sub * 16 + (lane & 15)) * kALD + kk * 32 + (lane >> 4) * 8);
+          sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], sc[sub], 0, 0, 0);
+        }
       }
-    }
-    float mb = -INFINITY;
+      // masks without branches: four key kinds per 32-bit LDS read, bitwise logic
+      float mb = -INFINITY;
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+      for (int sub = 0; sub < 4; ++sub) {
+        const int jl0 = blk * kKB + sub * 16 + (lane >> 4) * 4;
+        const unsigned k4 = *reinterpret_cast<const unsigned*>(sKind + jl0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jl = sub * 16 + (lane >> 4) * 4 + r;
-        const int kind = sKind[jl];
-        const bool ok = kind == 1 || (kind == 2 && (kb * kKB + jl - P) <= qi);
-        const float val = ok ? s[sub][r] * sl2 : -INFINITY;
-        s[sub][r] = val;
-        mb = fmaxf(mb, val);
+        for (int r = 0; r < 4; ++r) {
+          const unsigned kind = (k4 >> (8 * r)) & 0xffu;
+          const bool ok = (kind == 1u) | ((kind == 2u) & ((r0 + jl0 + r - P) <= qi));
+          const float val = ok ? sc[sub][r] * sl2 : -INFINITY;
+          sc[sub][r] = val;
+          mb = fmaxf(mb, val);
+        }
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float ls = 0.f;
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float m_new = fmaxf(m_run, mb);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      // v_exp_f32 directly: arguments are <= 0 and results that would be
+      // denormal may flush to zero, which a softmax weight can afford
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float ls = 0.f;
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+      for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[sub][r] - m_use);
-        s[sub][r] = p;
-        ls += p;
-      }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_use);
+          sc[sub][r] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) o[m] *= alpha;
+      for (int m = 0; m < 4; ++m) o[m] *= alpha;
 
-    // O^T[d][row] += V^T[d][key] P^T[key][row], 32 keys per MFMA.  The k-slot
-    // order (keys 4q..4q+3 then 16+4q..16+4q+3 for lane group q) is the same
-    // for both operands.
+      // O^T[d][row] += V^T[d][key] P^T[key][row], 32 keys per MFMA.  The k-slot
+      // order (keys 4q..4q+3 then 16+4q..16+4q+3 for lane group q) is the same
+      // for both operands.
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      bf16x8 pb;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 pb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = (__bf16)s[2 * h2][r];
-        pb[4 + r] = (__bf16)s[2 * h2 + 1][r];
-      }
+        for (int r = 0; r < 4; ++r) {
+          pb[r] = (__bf16)sc[2 * h2][r];
+          pb[4 + r] = (__bf16)sc[2 * h2 + 1][r];
+        }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16_t* vp = sVt + (m * 16 + (lane & 15)) * kALD + h2 * 32 + (lane >> 4) * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) {
+          const bf16_t* vp = sVt + (m * 16 + (lane & 15)) * VLD + blk * kKB + h2 * 32 + (lane >> 4) * 4;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+          const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
+        }
       }
     }
   }
@@ -536,8 +651,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
   const dim3 grid(3, kHKV, a.B), block(256);
-  if (self_layer) hipLaunchKernelGGL(attn_kernel<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(attn_kernel<false>, grid, block, 0, s, a);
+  if (a.B <= 8) {
+    if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 5>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<false, 5>), grid, block, 0, s, a);
+  } else {
+    if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<false, 1>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -554,21 +674,40 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
   const int nMaskBlocks = (a.B + 3) / 4;
   if (blockIdx.x < kTimeBlocks) {
     // Sinusoidal time embedding: sin(2 pi t / p_i) for i < 360, cos(...) after,
-    // periods geometric from p_min to p_max; evaluated in fp64.
+    // periods geometric from p_min to p_max (1/p_i precomputed in fp64).  The
+    // angle is reduced to [0, 2 pi) in fp64, then sin/cos run in fp32.
+    // Row j of W_t1[:, 720:] is read once, 8 halves per lane, for every step.
     const int j = blockIdx.x * kTimeRowsPerBlock + (tid >> 4), part = tid & 15;
     const half_t* wr = a.w_t1 + (size_t)j * (2 * kD) + kD;
+    constexpr int CH = kD / 8;                  // 90 chunks of 8
+    constexpr int PER = (CH + 15) / 16;         // 6 chunks per lane
+    uint4 wv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = part + 16 * u;
+      wv[u] = c < CH ? *reinterpret_cast<const uint4*>(wr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
     for (int k = 0; k < a.n_t; ++k) {
       __syncthreads();
       for (int i = tid; i < kD; i += 256) {
         const int halfd = kD / 2, ii = i % halfd;
-        const double frac = (double)ii / (double)(halfd - 1);
-        const double period = (double)a.p_min * pow((double)a.p_max / (double)a.p_min, frac);
-        const double ang = 2.0 * M_PI * (double)a.t[k] / period;
-        se[i] = (float)(i < halfd ? sin(ang) : cos(ang));
+        const double turns = (double)a.t[k] * a.inv_period[ii];
+        const float ang = (float)(6.283185307179586 * (turns - floor(turns)));
+        float sn, cs;
+        sincosf(ang, &sn, &cs);
+        se[i] = i < halfd ? sn : cs;
       }
       __syncthreads();
       float s = 0.f;
-      for (int i = part; i < kD; i += 16) s += (float)wr[i] * se[i];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = part + 16 * u;
+        if (c < CH) {
+          const half_t* w8 = reinterpret_cast<const half_t*>(&wv[u]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += (float)w8[e] * se[c * 8 + e];
+        }
+      }
       s += __shfl_xor(s, 1);
       s += __shfl_xor(s, 2);
       s += __shfl_xor(s, 4);
@@ -596,6 +735,19 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
   const int nCopy = (a.B * kChunk * kAD + 255) / 256;
   const int copyBlocks = nCopy < 64 ? nCopy : 64;
   hipLaunchKernelGGL(prologue_kernel, dim3(kTimeBlocks + nMaskBlocks + copyBlocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Inverse periods of the time embedding: 1 / (p_min (p_max/p_min)^(i/359)), fp64.
+__global__ void inv_period_kernel(double* tab, float p_min, float p_max) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= kD / 2) return;
+  const double frac = (double)i / (double)(kD / 2 - 1);
+  tab[i] = 1.0 / ((double)p_min * pow((double)p_max / (double)p_min, frac));
+}
+
+hipError_t launch_inv_period_table(double* tab, float p_min, float p_max, hipStream_t s) {
+  hipLaunchKernelGGL(inv_period_kernel, dim3((kD / 2 + 255) / 256), dim3(256), 0, s, tab, p_min, p_max);
   return hipGetLastError();
 }
 

@@ -79,6 +79,7 @@ struct smolexp_handle {
   bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
   int* nvalid = nullptr;
   float2* rope = nullptr;
+  double* inv_period = nullptr;
 
   hipStream_t cap = nullptr;
   std::vector<GraphEntry> graphs;
@@ -91,7 +92,7 @@ struct smolexp_handle {
   bool probe_ok[PR_COUNT] = {};
   GemmArgs probe_g[PR_COUNT];
   AttnArgs probe_a[PR_COUNT];
-  TileCfg probe_tile[PR_COUNT];
+  GemmPlan probe_plan[PR_COUNT];
   AMode probe_am[PR_COUNT];
   EMode probe_em[PR_COUNT];
 };
@@ -197,8 +198,7 @@ CallKey key_of(const CallArgs& c) {
 // The launch sequence of one call.
 int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
-  const TileCfg tc = M <= 64 ? T_SKINNY : T_MED;
-  const int nt_h = gemm_ntiles(tc, kD);
+  const int nt_h = plan_gemm(M, kD, kD).ntiles_n;  // sum-of-squares slots of every N = 720 producer
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
   hipError_t e;
   if (record_probes) {
@@ -221,21 +221,22 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   pa.s_t1 = h->w_t1.scale;
   pa.b_t1 = h->b_t1;
   pa.cvec = h->cvec;
-  pa.p_min = h->cfg.t_min_period;
-  pa.p_max = h->cfg.t_max_period;
+  pa.inv_period = h->inv_period;
   if ((e = launch_prologue(pa, s)) != hipSuccess) return hip_fail(h, e, "prologue launch");
 
   const size_t kvLayer = (size_t)2 * B * kHKV * (size_t)P * kHD;  // elements per layer
   const bf16_t* kv = static_cast<const bf16_t*>(c.kv);
-  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g) -> hipError_t {
+  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
+    const GemmArgs& g = g0;
+    const GemmPlan plan = plan_gemm(g.M, g.N, g.K);
     if (record_probes && probe >= 0 && !h->probe_ok[probe]) {
       h->probe_ok[probe] = true;
       h->probe_g[probe] = g;
-      h->probe_tile[probe] = tc;
+      h->probe_plan[probe] = plan;
       h->probe_am[probe] = am;
       h->probe_em[probe] = em;
     }
-    return launch_gemm(tc, am, em, g, s);
+    return launch_gemm(plan, am, em, g, s);
   };
 
   for (int k = 0; k < n_t; ++k) {
@@ -448,6 +449,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   const size_t o_u = take(Mmax * kFFN * 2), o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
   const size_t o_vc = take(Mmax * kNKV * 2), o_nv = take((size_t)cfg->max_batch * 4);
   const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
+  const size_t o_invp = take((size_t)(kD / 2) * sizeof(double));
   hipError_t e = hipMalloc(&h->wsmem, off);
   if (e != hipSuccess) { delete h; return SMOLEXP_E_NOMEM; }
   char* base = static_cast<char*>(h->wsmem);
@@ -456,9 +458,11 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->q = (bf16_t*)(base + o_q);
   h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->nvalid = (int*)(base + o_nv);
   h->rope = (float2*)(base + o_rope);
+  h->inv_period = (double*)(base + o_invp);
 
   e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
   if (e == hipSuccess) e = launch_rope_table(h->rope, n_pos, cfg->rope_theta, h->cap);
+  if (e == hipSuccess) e = launch_inv_period_table(h->inv_period, cfg->t_min_period, cfg->t_max_period, h->cap);
   if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
   if (e != hipSuccess) {
     smolexp_destroy(h);
@@ -536,16 +540,31 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     const uint16_t* pd = next((size_t)kD * kFFN);
     vec32(g1, kD, o_g1[l]);
     vec32(g2, kD, o_g2[l]);
-    // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone)
-    if (self_attn) {
-      s = pick_shift({{pq, (size_t)kNQ * kD}, {pk, (size_t)kNKV * kD}, {pvv, (size_t)kNKV * kD}});
+    // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone).  Inside each
+    // Q and K head, 16-row block q holds dims q*8..q*8+7 then 32+q*8..32+q*8+7, so the
+    // rotation pairs (d, d + 32) share an MFMA tile.
+    {
+      const int nrows = self_attn ? kNQKV : kNQ;
+      const int rot_heads = self_attn ? kHQ + kHKV : kHQ;
+      std::vector<const uint16_t*> row_src(nrows);
+      for (int r = 0; r < kNQ; ++r) row_src[r] = pq + (size_t)r * kD;
+      if (self_attn) {
+        for (int r = 0; r < kNKV; ++r) row_src[kNQ + r] = pk + (size_t)r * kD;
+        for (int r = 0; r < kNKV; ++r) row_src[kNQ + kNKV + r] = pvv + (size_t)r * kD;
+      }
+      std::vector<std::pair<const uint16_t*, size_t>> parts = {{pq, (size_t)kNQ * kD}};
+      if (self_attn) { parts.push_back({pk, (size_t)kNKV * kD}); parts.push_back({pvv, (size_t)kNKV * kD}); }
+      s = pick_shift(parts);
       half_t* d = (half_t*)(hb + o_qkv[l]);
-      to_f16(pq, (size_t)kNQ * kD, s, d);
-      to_f16(pk, (size_t)kNKV * kD, s, d + (size_t)kNQ * kD);
-      to_f16(pvv, (size_t)kNKV * kD, s, d + (size_t)(kNQ + kNKV) * kD);
-    } else {
-      s = pick_shift({{pq, (size_t)kNQ * kD}});
-      to_f16(pq, (size_t)kNQ * kD, s, (half_t*)(hb + o_qkv[l]));
+      for (int r = 0; r < nrows; ++r) {
+        const int head = r / kHD, rr = r % kHD;
+        int src = r;
+        if (head < rot_heads) {
+          const int q = rr / 16, e = rr % 16;
+          src = head * kHD + (e < 8 ? q * 8 + e : kHD / 2 + q * 8 + (e - 8));
+        }
+        to_f16(row_src[src], kD, s, d + (size_t)r * kD);
+      }
     }
     ld.qkv.scale = ldexpf(1.f, -s);
     s = pick_shift({{po, (size_t)kD * kNQ}});
@@ -554,9 +573,9 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     s = pick_shift({{pg, (size_t)kFFN * kD}, {pu, (size_t)kFFN * kD}});
     {
       half_t* d = (half_t*)(hb + o_gu[l]);
-      for (int j = 0; j < kFFN / 16; ++j) {  // rows 32j..32j+15 = gate 16j.., 32j+16.. = up 16j..
-        to_f16(pg + (size_t)16 * j * kD, (size_t)16 * kD, s, d + (size_t)32 * j * kD);
-        to_f16(pu + (size_t)16 * j * kD, (size_t)16 * kD, s, d + (size_t)(32 * j + 16) * kD);
+      for (int j = 0; j < kFFN / 8; ++j) {  // rows 16j..16j+7 = gate 8j.., 16j+8..16j+15 = up 8j..
+        to_f16(pg + (size_t)8 * j * kD, (size_t)8 * kD, s, d + (size_t)16 * j * kD);
+        to_f16(pu + (size_t)8 * j * kD, (size_t)8 * kD, s, d + (size_t)(16 * j + 8) * kD);
       }
     }
     ld.gu.scale = ldexpf(1.f, -s);
@@ -672,7 +691,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     } else if (kernel == PR_ATTN_SELF || kernel == PR_ATTN_CROSS) {
       e = launch_attention(kernel == PR_ATTN_SELF, h->probe_a[kernel], s);
     } else {
-      e = launch_gemm(h->probe_tile[kernel], h->probe_am[kernel], h->probe_em[kernel], h->probe_g[kernel], s);
+      e = launch_gemm(h->probe_plan[kernel], h->probe_am[kernel], h->probe_em[kernel], h->probe_g[kernel], s);
     }
   }
   if (e == hipSuccess) e = hipEventRecord(e1, s);

@@ -105,17 +105,23 @@ struct PrologueArgs {
   float s_t1;
   const float* b_t1;
   float* cvec;             // out [n_t][720] = W_t1[:, 720:] e(t) + b_t1
-  float p_min, p_max;
+  const double* inv_period;  // [360] 1 / p_i of the time embedding
 };
 
-// Tile configurations of the GEMM.
-enum TileCfg : int { T_SKINNY = 0, T_MED = 1 };
+// How one GEMM is cut up (kernels.hip decides, the host sizes workspaces from it).
+struct GemmPlan {
+  int kind;      // 0: skinny (M <= 64): one workgroup per 16 columns; 1: tiled: 128 x 128 tiles
+  int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
+  int bm;        // tiled: rows per tile (64 or 128)
+  int ntiles_n;  // output tiles along N (= sum-of-squares slots written by an N = 720 producer)
+};
+GemmPlan plan_gemm(int M, int N, int K);
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
-hipError_t launch_gemm(TileCfg cfg, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
-int gemm_ntiles(TileCfg cfg, int N);
+hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int n_pos, float theta, hipStream_t s);
+hipError_t launch_inv_period_table(double* tab, float p_min, float p_max, hipStream_t s);
 
 }  // namespace smolexp
