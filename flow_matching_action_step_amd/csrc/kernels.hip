@@ -469,6 +469,137 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 constexpr int kKB = 64;        // keys per block
 constexpr int kALD = kHD + 8;  // LDS row stride of K (elements)
 
+// One 64-key block of the online softmax for the lane's query row (row qi of
+// the chunk).  sKb: the block's K rows [64][kALD]; sVb: its V^T columns
+// (row stride vld); kind: its key kinds; key0 = index of its first key minus P
+// (chunk key j is visible to row qi when j - P <= qi).
+__device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, int vld, const uint8_t* kind,
+                                           int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
+                                           float& l_run, int lane) {
+  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+  // S^T[key][row] for the 64 keys of the block (4 tiles of 16 keys)
+  f32x4 sc[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint4 u = *reinterpret_cast<const uint4*>(sKb + (sub * 16 + (lane & 15)) * kALD + kk * 32 + (lane >> 4) * 8);
+      sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], sc[sub], 0, 0, 0);
+    }
+  }
+  // masks without branches: four key kinds per 32-bit LDS read, bitwise logic
+  float mb = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const int jl0 = sub * 16 + (lane >> 4) * 4;
+    const unsigned k4 = *reinterpret_cast<const unsigned*>(kind + jl0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const unsigned kd = (k4 >> (8 * r)) & 0xffu;
+      const bool ok = (kd == 1u) | ((kd == 2u) & ((key0 + jl0 + r) <= qi));
+      const float val = ok ? sc[sub][r] * sl2 : -INFINITY;
+      sc[sub][r] = val;
+      mb = fmaxf(mb, val);
+    }
+  }
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const float m_new = fmaxf(m_run, mb);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  // v_exp_f32 directly: arguments are <= 0 and results that would be
+  // denormal may flush to zero, which a softmax weight can afford
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+  float ls = 0.f;
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_use);
+      sc[sub][r] = p;
+      ls += p;
+    }
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  l_run = l_run * alpha + ls;
+  m_run = m_new;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o[m] *= alpha;
+  // O^T[d][row] += V^T[d][key] P^T[key][row], 32 keys per MFMA.  The k-slot
+  // order (keys 4q..4q+3 then 16+4q..16+4q+3 for lane group q) is the same for
+  // both operands.
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    bf16x8 pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pb[r] = (__bf16)sc[2 * h2][r];
+      pb[4 + r] = (__bf16)sc[2 * h2 + 1][r];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bf16_t* vp = sVb + (m * 16 + (lane & 15)) * vld + h2 * 32 + (lane >> 4) * 4;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+      const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
+    }
+  }
+}
+
+// Stage keys r0 .. r0 + RK - 1 of one (query, KV head) into LDS: K rows,
+// V transposed, key kinds.  Branch-free: every address is clamped into its
+// buffer and the loaded vector is zeroed afterwards for masked or missing
+// keys, so all loads are in flight together.
+template <bool SELF, int RK>
+__device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int r0, bf16_t* sK, bf16_t* sVt,
+                                           uint8_t* sKind, int nthreads) {
+  constexpr int VLD = RK + 8;
+  constexpr int NV = RK * 8 / 256;  // 16-byte vectors per thread (256 threads)
+  const int tid = threadIdx.x, P = a.P;
+  const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
+  const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
+  const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : pk;
+  const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : pv;
+  const uint8_t* mk = a.mask + (size_t)b * P;
+  (void)nthreads;
+  for (int i = tid; i < RK; i += 256) {
+    const int j = r0 + i;
+    sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+  }
+  uint4 kv[NV], vv[NV];
+  bool kok[NV], vok[NV];
+#pragma unroll
+  for (int it = 0; it < NV; ++it) {
+    const int v = tid + 256 * it;
+    {  // K rows: 8 lanes per key
+      const int j = r0 + (v >> 3), c = (v & 7) * 8;
+      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+      const bf16_t* src = pre ? pk + (size_t)j * kHD + c : (chunk ? ck + (size_t)(j - P) * kHD + c : pk + c);
+      kv[it] = *reinterpret_cast<const uint4*>(src);
+      kok[it] = pre ? mk[j] != 0 : chunk;
+    }
+    {  // V rows for the transposed store: consecutive lanes take consecutive keys
+      const int j = r0 + (v % RK), c = (v / RK) * 8;
+      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+      const bf16_t* src = pre ? pv + (size_t)j * kHD + c : (chunk ? cv + (size_t)(j - P) * kHD + c : pv + c);
+      vv[it] = *reinterpret_cast<const uint4*>(src);
+      vok[it] = pre ? mk[j] != 0 : chunk;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NV; ++it) {
+    if (!kok[it]) kv[it] = make_uint4(0, 0, 0, 0);
+    if (!vok[it]) vv[it] = make_uint4(0, 0, 0, 0);
+    const int v = tid + 256 * it;
+    *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
+    const int jl = v % RK, c = (v / RK) * 8;
+    const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv[it]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sVt[(c + t) * VLD + jl] = e[t];
+  }
+}
+
 // NBLK key blocks are staged per round: all of their loads are issued before
 // the first is stored, so a round costs one memory round trip.  Small batches
 // stage five blocks (320 keys: a whole prefix plus the chunk), large batches
@@ -477,7 +608,6 @@ template <bool SELF, int NBLK>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   constexpr int RK = NBLK * kKB;     // keys per round
   constexpr int VLD = RK + 8;        // LDS row stride of V^T (elements)
-  constexpr int NV = NBLK * 2;       // 16-byte vectors per thread for K (and for V) per round
   __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * VLD];
   __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];  // 0 = no key, 1 = valid prefix key, 2 = chunk key
@@ -506,134 +636,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   const int NK = P + (SELF ? kChunk : 0);
-  const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
-  const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
-  const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : nullptr;
-  const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : nullptr;
-  const uint8_t* mk = a.mask + (size_t)b * P;
-  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
-
   for (int r0 = 0; r0 < NK; r0 += RK) {
     __syncthreads();  // the previous round's LDS reads are done
-    for (int i = tid; i < RK; i += 256) {
-      const int j = r0 + i;
-      sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
-    }
-    // Branch-free staging: every address is clamped into its buffer and the
-    // loaded vector is zeroed afterwards for masked or missing keys, so all
-    // loads of the round are in flight together.
-    uint4 kv[NV], vv[NV];
-    bool kok[NV], vok[NV];
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int v = tid + 256 * it;
-      {  // K rows: 8 lanes per key
-        const int j = r0 + (v >> 3), c = (v & 7) * 8;
-        const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-        const bf16_t* src = pre ? pk + (size_t)j * kHD + c
-                                : (chunk ? ck + (size_t)(j - P) * kHD + c : pk + c);
-        kv[it] = *reinterpret_cast<const uint4*>(src);
-        kok[it] = pre ? mk[j] != 0 : chunk;
-      }
-      {  // V rows for the transposed store: consecutive lanes take consecutive keys
-        const int j = r0 + (v % RK), c = (v / RK) * 8;
-        const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-        const bf16_t* src = pre ? pv + (size_t)j * kHD + c
-                                : (chunk ? cv + (size_t)(j - P) * kHD + c : pv + c);
-        vv[it] = *reinterpret_cast<const uint4*>(src);
-        vok[it] = pre ? mk[j] != 0 : chunk;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      if (!kok[it]) kv[it] = make_uint4(0, 0, 0, 0);
-      if (!vok[it]) vv[it] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int v = tid + 256 * it;
-      *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
-      const int jl = v % RK, c = (v / RK) * 8;
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv[it]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) sVt[(c + t) * VLD + jl] = e[t];
-    }
+    attn_stage<SELF, RK>(a, b, g, r0, sK, sVt, sKind, 256);
     __syncthreads();
 
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
-    for (int blk = 0; blk < nb; ++blk) {
-      const int kb0 = r0 + blk * kKB;  // first key of this block
-      // S^T[key][row] for the 64 keys of the block (4 tiles of 16 keys)
-      f32x4 sc[4];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint4 u = *reinterpret_cast<const uint4*>(
-              sK + (blk * kKB + sub * 16 + (lane & 15)) * kALD + kk * 32 + (lane >> 4) * 8);
-          sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], sc[sub], 0, 0, 0);
-        }
-      }
-      // masks without branches: four key kinds per 32-bit LDS read, bitwise logic
-      float mb = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const int jl0 = blk * kKB + sub * 16 + (lane >> 4) * 4;
-        const unsigned k4 = *reinterpret_cast<const unsigned*>(sKind + jl0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const unsigned kind = (k4 >> (8 * r)) & 0xffu;
-          const bool ok = (kind == 1u) | ((kind == 2u) & ((r0 + jl0 + r - P) <= qi));
-          const float val = ok ? sc[sub][r] * sl2 : -INFINITY;
-          sc[sub][r] = val;
-          mb = fmaxf(mb, val);
-        }
-      }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m_run, mb);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      // v_exp_f32 directly: arguments are <= 0 and results that would be
-      // denormal may flush to zero, which a softmax weight can afford
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float ls = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_use);
-          sc[sub][r] = p;
-          ls += p;
-        }
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) o[m] *= alpha;
-
-      // O^T[d][row] += V^T[d][key] P^T[key][row], 32 keys per MFMA.  The k-slot
-      // order (keys 4q..4q+3 then 16+4q..16+4q+3 for lane group q) is the same
-      // for both operands.
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[r] = (__bf16)sc[2 * h2][r];
-          pb[4 + r] = (__bf16)sc[2 * h2 + 1][r];
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16_t* vp = sVt + (m * 16 + (lane & 15)) * VLD + blk * kKB + h2 * 32 + (lane >> 4) * 4;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-          const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
-        }
-      }
-    }
+    for (int blk = 0; blk < nb; ++blk)
+      attn_block(sK + blk * kKB * kALD, sVt + blk * kKB, VLD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
+                 m_run, l_run, lane);
   }
 
   if (rvalid) {
@@ -649,12 +660,98 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   }
 }
 
+// Small batches: the four waves of a workgroup share 16 query rows and split
+// the key blocks among themselves (wave w takes blocks w, w + 4, ...), then
+// merge their softmax states (running max, running sum, unnormalised output)
+// through LDS.  Five times as many workgroups as attn_kernel at batch 1.
+template <bool SELF>
+__global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
+  constexpr int NBLK = 5, RK = NBLK * kKB, VLD = RK + 8, OLD = kHD + 4;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * VLD];
+  __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];
+  __shared__ float sM[4][16], sL[4][16];
+  float* sO = reinterpret_cast<float*>(sK);  // [4 waves][16 rows][OLD], used after the last round
+  static_assert(4 * 16 * OLD * 4 <= (int)sizeof(sK), "merge buffer fits in the K staging area");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int P = a.P;
+  const int rq = blockIdx.x * 16 + (lane & 15);
+  const bool rvalid = rq < 3 * kChunk;
+  const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
+  const int qi = rvalid ? rq % kChunk : 0;
+
+  bf16x8 qf[2];
+  {
+    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * kChunk + qi) * kHD + (lane >> 4) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  f32x4 o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int NK = P + (SELF ? kChunk : 0);
+  for (int r0 = 0; r0 < NK; r0 += RK) {
+    __syncthreads();
+    attn_stage<SELF, RK>(a, b, g, r0, sK, sVt, sKind, 256);
+    __syncthreads();
+    const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
+    for (int blk = wave; blk < nb; blk += 4)
+      attn_block(sK + blk * kKB * kALD, sVt + blk * kKB, VLD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
+                 m_run, l_run, lane);
+  }
+
+  // merge the four waves' states
+  __syncthreads();
+  if (lane < 16) {
+    sM[wave][lane] = m_run;
+    sL[wave][lane] = l_run;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sO[(wave * 16 + (lane & 15)) * OLD + m * 16 + (lane >> 4) * 4 + r] = o[m][r];
+  __syncthreads();
+  {
+    const int row = tid >> 4, d0 = (tid & 15) * 4;
+    const int rq2 = blockIdx.x * 16 + row;
+    if (rq2 < 3 * kChunk) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sM[w][row]);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(sM[w][row] - mu);
+        l += sL[w][row] * sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += sO[(w * 16 + row) * OLD + d0 + e] * sc;
+      }
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const int hq2 = 3 * g + rq2 / kChunk, qi2 = rq2 % kChunk;
+      union { half_t h[4]; uint2 u; } pk4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk4.h[e] = (half_t)(acc[e] * inv);
+      *reinterpret_cast<uint2*>(a.out + ((size_t)b * kChunk + qi2) * kNQ + hq2 * kHD + d0) = pk4.u;
+    }
+  }
+}
+
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(3, kHKV, a.B), block(256);
+  const dim3 block(256);
   if (a.B <= 8) {
-    if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 5>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<false, 5>), grid, block, 0, s, a);
+    const dim3 grid((3 * kChunk + 15) / 16, kHKV, a.B);
+    if (self_layer) hipLaunchKernelGGL(attn_ksplit_kernel<true>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(attn_ksplit_kernel<false>, grid, block, 0, s, a);
   } else {
+    const dim3 grid(3, kHKV, a.B);
     if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 1>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attn_kernel<false, 1>), grid, block, 0, s, a);
   }
