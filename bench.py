@@ -20,6 +20,77 @@ MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 RIDGE = MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 DEFAULT_WORKLOAD = "expert16_b1_p177"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
+KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed kernel
+    "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_ksplit_kernel<true>", "attn_cross": "attn_ksplit_kernel<false>",
+    "o": "gemm_skinny<0, 3, 4>", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8>",
+    "action_out": "gemm_skinny<1, 6,",
+}
+
+
+def kernel_source_digest():
+    """Digest of the HIP sources: a stored counter reading is only valid for the kernels it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "smolexp_internal.h"):
+        with open(os.path.join(ROOT, "flow_matching_action_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch from profiles/traffic.json, or None if absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            e = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("kernel_source") != kernel_source_digest():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, kernel):
+    """Per-launch HBM bytes of `kernel` from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the same counter reads for the calibration copy of COPY_BYTES."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        # the runtime may split one copy into several dispatches: calibrate on the total of the
+        # three copies (3 * COPY_BYTES read and written)
+        copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        mine = [v for k, vs in vals.items() if KERNEL_SYMBOLS[kernel] in k for v in vs]
+        if not copy or not mine:
+            raise SystemExit(f"{path}: no calibration copy or no {kernel} dispatch with {counter}")
+        copy_kib = sum(copy)
+        scale = (3 * COPY_BYTES / 1024) / copy_kib
+        out[counter] = {"kib_per_launch": sum(mine) / len(mine), "launches": len(mine),
+                        "copy_kib_total": copy_kib, "copy_dispatches": len(copy), "scale": scale,
+                        "bytes_per_launch": sum(mine) / len(mine) * 1024 * scale}
+    entry = {"kernel_source": kernel_source_digest(), "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+             "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allv = json.load(f)
+    except (OSError, ValueError):
+        allv = {}
+    allv.setdefault(workload, {})[kernel] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allv, f, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
 
 
 def kernel_costs(L, B, lengths, P):
@@ -99,7 +170,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="launch kernels one by one instead of graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurement, copy 256 MiB device-to-device three times (HBM counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.summarize_pmc[2])
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the denoising loop runs on a single MI355X and shards by query "
               f"(data parallel, no exchange); --gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -158,7 +236,7 @@ def main():
         achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(args.workload, dom_name)
     roof["kernel"] = dom_name
     roof["avg_us"] = dom["avg_us"]
     roof["algorithmic_bytes_per_launch"] = dom["bytes"]
@@ -194,6 +272,12 @@ def main():
         "kernels": kern,
     }
     fm.smolexp_destroy(h)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, 3 * args.cpu_seconds)
     print(json.dumps(line), flush=True)
