@@ -291,9 +291,17 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int mt = blockIdx.x, nt = blockIdx.y;
-  const int m0 = mt * BM, n0 = nt * BN;
   const int M = a.M, N = a.N, K = a.K;
+  // XCD-aware tile order: workgroups are dispatched to the 8 XCDs round-robin,
+  // so workgroup id goes to XCD id % 8.  XCD x takes the contiguous range
+  // [x * per, (x + 1) * per) of the M-major tile order, i.e. a few row panels of
+  // A with all of their N tiles, and keeps those A panels in its own L2.
+  const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN, T = nM * nN;
+  const int per = (T + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (tile >= T) return;  // uniform per workgroup, before any barrier
+  const int mt = tile / nN, nt = tile % nN;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int nk = (K + BK - 1) / BK;
 
   if constexpr (AM == A_NORM) {
@@ -436,7 +444,8 @@ static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_
       default: return hipErrorInvalidValue;  // K beyond 8 waves x 8 k-steps x 32
     }
   } else {
-    const dim3 grid((a.M + p.bm - 1) / p.bm, p.ntiles_n);
+    const int T = ((a.M + p.bm - 1) / p.bm) * p.ntiles_n;
+    const dim3 grid(8 * ((T + 7) / 8));
     if (p.bm == 128) hipLaunchKernelGGL((gemm_tiled<AM, EM, 4>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gemm_tiled<AM, EM, 2>), grid, dim3(256), 0, s, a);
   }
