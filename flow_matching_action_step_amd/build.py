@@ -25,6 +25,9 @@ def build(verbose=False):
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-mcode-object-version=5", "-fPIC", "-shared",
            # no packed-fp32 instructions in device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in VGPRs: with AGPR accumulators the allocator shuffles
+           # them between loop iterations (hundreds of v_accvgpr moves per k-slab)
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wall", "-Wno-unused-function", "-Wl,--no-undefined",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
            "-o", tmp] + SOURCES

@@ -1,7 +1,9 @@
 // HIP kernels of the action-expert denoising loop, written for gfx950 (CDNA4).
 //
-// GEMMs: C[M,N] = A[M,K] * W[N,K]^T with both operands K-contiguous, on
-//   v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulate).  Weights are the
+// GEMMs: C[M,N] = A[M,K] * W[N,K]^T on v_mfma_f32_16x16x32_f16 (fp16
+//   operands, fp32 accumulate).  Both operands are stored in 16-row x 8-column
+//   micro-tiles (t16_off), so every fragment load and every LDS tile fill
+//   reads whole 256-byte runs.  Weights are the
 //   checkpoint's bf16 values re-encoded exactly in fp16 with a power-of-two
 //   scale per matrix; activations are rounded to fp16 (8x finer than bf16).
 //   The A-operand load fuses RMSNorm (row scale from partial sums of squares
@@ -64,19 +66,11 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 template <int AM>
 __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool ok, float rscale,
                                          bool write_x) {
+  static_assert(AM != A_NORM, "the fp32 residual is loaded by the kernels themselves");
+  (void)rscale;
   if constexpr (AM == A_F16) {
-    return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + (size_t)row * a.lda + k)
+    return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + t16_off(row, k, a.lda >> 3))
               : make_uint4(0, 0, 0, 0);
-  } else if constexpr (AM == A_NORM) {
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-      const float4 h0 = *reinterpret_cast<const float4*>(p), h1 = *reinterpret_cast<const float4*>(p + 4);
-      const float4 g0 = *reinterpret_cast<const float4*>(a.gain + k), g1 = *reinterpret_cast<const float4*>(a.gain + k + 4);
-      v[0] = h0.x * rscale * g0.x; v[1] = h0.y * rscale * g0.y; v[2] = h0.z * rscale * g0.z; v[3] = h0.w * rscale * g0.w;
-      v[4] = h1.x * rscale * g1.x; v[5] = h1.y * rscale * g1.y; v[6] = h1.z * rscale * g1.z; v[7] = h1.w * rscale * g1.w;
-    }
-    return pack8(v);
   } else {  // A_X: Euler state; rows i < ow_rows of each chunk take the flow-path point t*eps + (1-t)*prev
     float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
     if (ok) {
@@ -106,6 +100,17 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
   }
 }
 
+// Columns k..k+7 (k % 8 == 0) of row `row` of the blocked fp32 residual.
+__device__ __forceinline__ void load_h8(const GemmArgs& a, int row, int k, bool ok, float4& lo, float4& hi) {
+  if (ok) {
+    const float* p = static_cast<const float*>(a.A) + t32_off(row, k, a.lda >> 2);
+    lo = *reinterpret_cast<const float4*>(p);
+    hi = *reinterpret_cast<const float4*>(p + 64);  // next 4-column chunk of the same row block
+  } else {
+    lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 // RMSNorm row scales 1/sqrt(mean(h^2) + eps) for rows m0..m0+BM-1 from the
 // producer's per-N-tile partial sums of squares.  NT/BM threads share a row
 // and sum every (NT/BM)-th partial, so the loads are issued side by side.
@@ -129,67 +134,142 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int m0, float* sR)
 }
 
 // Epilogue on a finished tile sC[BM][LDC] (fp32, weight scale applied) whose
-// rows start at m0 and columns at n0 (BN a multiple of 16).  Work unit =
-// (row, 16-column block, e < 8) covering columns e and e + 8 of the block;
-// the units of one row are consecutive lanes of one wave.  ntile = this
-// tile's sum-of-squares slot.
+// rows start at m0 and columns at n0 (BN a multiple of 16).  ntile = this
+// tile's sum-of-squares slot.  The blocked outputs (fp16 activations, the fp32
+// residual) are written with 16 consecutive lanes on 16 consecutive rows of
+// one 16-byte column chunk, i.e. 256 contiguous bytes per store.
 template <int EM, int BM, int BN, int LDC, int NT>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0, int ntile) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0 && (BM * UPR) % NT == 0, "rows inside one wave, uniform trip count");
   const int M = a.M, N = a.N;
-  for (int g = threadIdx.x; g < BM * UPR; g += NT) {
-    const int r = g / UPR, blk = (g % UPR) / 8, e = g % 8;
-    const int row = m0 + r, cb = n0 + blk * 16;
-    const bool ok = row < M && cb < N;
-    const float v1 = sC[r * LDC + blk * 16 + e], v2 = sC[r * LDC + blk * 16 + 8 + e];
-    float ss = 0.f;
-    if (ok) {
-      if constexpr (EM == E_QKV) {
-        const int head = cb / kHD, b = row / kChunk, ci = row % kChunk;
-        bf16_t* dst;
-        if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
-        else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
-        else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
-        if (head < kHQ + kHKV) {  // rotate the pair (d, d + 32) at position n_valid + i
-          const int d = ((cb % kHD) / 16) * 8 + e;
-          const float2 cs = a.rope[(size_t)(a.nvalid[b] + ci) * (kHD / 2) + d];
-          dst[d] = f2bf(v1 * cs.x - v2 * cs.y);
-          dst[d + kHD / 2] = f2bf(v1 * cs.y + v2 * cs.x);
-        } else {
-          const int d = cb % kHD + e;
-          dst[d] = f2bf(v1);
-          dst[d + 8] = f2bf(v2);
+  if constexpr (EM == E_QKV) {
+    // Work unit = (row, 16-column block): the block is 8 rotation pairs of one Q/K
+    // head (dims q*8.. and 32+q*8.., one 16-byte run each) or 16 consecutive V dims.
+    for (int g = threadIdx.x; g < BM * NB; g += NT) {
+      const int r = g / NB, blk = g % NB;
+      const int row = m0 + r, cb = n0 + blk * 16;
+      if (row >= M || cb >= N) continue;
+      const float4* src = reinterpret_cast<const float4*>(sC + r * LDC + blk * 16);
+      const float4 c0 = src[0], c1 = src[1], c2 = src[2], c3 = src[3];
+      const float v1[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float v2[8] = {c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+      const int head = cb / kHD, b = row / kChunk, ci = row % kChunk;
+      bf16_t* dst;
+      if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
+      else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
+      else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
+      union { bf16_t e[8]; uint4 u; } lo, hi;
+      if (head < kHQ + kHKV) {  // rotate the pairs (d, d + 32), d = d0..d0+7, at position n_valid + i
+        const int d0 = ((cb % kHD) / 16) * 8;
+        const float4* cs4 = reinterpret_cast<const float4*>(a.rope + (size_t)(a.nvalid[b] + ci) * (kHD / 2) + d0);
+        const float4 q0 = cs4[0], q1 = cs4[1], q2 = cs4[2], q3 = cs4[3];
+        const float cs[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                              q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = cs[2 * e], sn = cs[2 * e + 1];
+          lo.e[e] = f2bf(v1[e] * c - v2[e] * sn);
+          hi.e[e] = f2bf(v1[e] * sn + v2[e] * c);
         }
-      } else if constexpr (EM == E_SWIGLU) {
-        a.out16[(size_t)row * a.ldo + cb / 2 + e] = (half_t)(silu(v1) * v2);
-      } else if constexpr (EM == E_F16_BIAS || EM == E_TIMEIN) {
-        const float z1 = v1 + a.bias[cb + e], z2 = v2 + a.bias[cb + 8 + e];
-        half_t* o = a.out16 + (size_t)row * a.ldo + cb + e;
-        o[0] = (half_t)(EM == E_TIMEIN ? silu(z1) : z1);
-        o[8] = (half_t)(EM == E_TIMEIN ? silu(z2) : z2);
-      } else if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
-        float* hp = a.h + (size_t)row * kD + cb + e;
-        const float h1 = (EM == E_H_BIAS) ? v1 + a.bias[cb + e] : hp[0] + v1;
-        const float h2 = (EM == E_H_BIAS) ? v2 + a.bias[cb + 8 + e] : hp[8] + v2;
-        hp[0] = h1;
-        hp[8] = h2;
-        ss = h1 * h1 + h2 * h2;
-      } else if constexpr (EM == E_ACTOUT) {
-        const size_t xi = (size_t)row * kAD + cb + e;
-        const float u1 = v1 + a.bias[cb + e], u2 = v2 + a.bias[cb + 8 + e];
-        const float x1 = a.x[xi] + a.dt * u1, x2 = a.x[xi + 8] + a.dt * u2;
-        a.x[xi] = x1;
-        a.x[xi + 8] = x2;
-        if (a.vel_out) { a.vel_out[xi] = u1; a.vel_out[xi + 8] = u2; }
-        if (a.st_out) { a.st_out[xi] = x1; a.st_out[xi + 8] = x2; }
-        if (a.final_out) { a.final_out[xi] = x1; a.final_out[xi + 8] = x2; }
+        *reinterpret_cast<uint4*>(dst + d0) = lo.u;
+        *reinterpret_cast<uint4*>(dst + d0 + kHD / 2) = hi.u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo.e[e] = f2bf(v1[e]);
+          hi.e[e] = f2bf(v2[e]);
+        }
+        *reinterpret_cast<uint4*>(dst + cb % kHD) = lo.u;
+        *reinterpret_cast<uint4*>(dst + cb % kHD + 8) = hi.u;
       }
     }
-    if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
+    return;
+  }
+  if constexpr (EM == E_SWIGLU || EM == E_F16_BIAS || EM == E_TIMEIN) {
+    // Work unit = (row, one 8-column chunk of the fp16 output).  SwiGLU: the
+    // 16-column block c of the tile holds gate (8) then up (8) of output chunk c.
+    constexpr int NC = EM == E_SWIGLU ? BN / 16 : BN / 8;  // output chunks per tile row
+    const int kco = a.ldo >> 3;
+    for (int g = threadIdx.x; g < BM * NC; g += NT) {
+      const int r = (g & 15) + 16 * ((g >> 4) / NC), c = (g >> 4) % NC;
+      const int row = m0 + r;
+      float v[8];
+      int col;
+      if constexpr (EM == E_SWIGLU) {
+        if (row >= M || n0 + c * 16 >= N) continue;
+        col = (n0 + c * 16) / 2;
+        const float4* p = reinterpret_cast<const float4*>(sC + r * LDC + c * 16);
+        const float4 g0 = p[0], g1 = p[1], u0 = p[2], u1 = p[3];
+        const float gt[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float up[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int off = UPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-      if (g % UPR == 0 && row < M) a.ss_out[(size_t)row * kSSStride + ntile] = ss;
+        for (int e = 0; e < 8; ++e) v[e] = silu(gt[e]) * up[e];
+      } else {
+        col = n0 + c * 8;
+        if (row >= M || col >= N) continue;
+        const float4* p = reinterpret_cast<const float4*>(sC + r * LDC + c * 8);
+        const float4* bp = reinterpret_cast<const float4*>(a.bias + col);
+        const float4 a0 = p[0], a1 = p[1], b0 = bp[0], b1 = bp[1];
+        const float z[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w,
+                            a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = EM == E_TIMEIN ? silu(z[e]) : z[e];
+      }
+      *reinterpret_cast<uint4*>(a.out16 + t16_off(row, col, kco)) = pack8(v);
+    }
+    return;
+  }
+  if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
+    // Work unit = (row, one 4-column chunk of the fp32 residual).  Lane = r16 + 16 * part:
+    // a wave owns one 16-row block per pass and its four parts take every fourth chunk,
+    // so a row's partial sum of squares meets inside the wave.
+    constexpr int NC4 = BN / 4, NWV = NT / 64, RB = BM / 16;
+    static_assert(NC4 % 4 == 0 && NT % 64 == 0, "uniform trip counts");
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, part = lane >> 4;
+    for (int rb = wv; rb < RB; rb += NWV) {
+      const int r = rb * 16 + r16, row = m0 + r;
+      const bool live = row < M;
+      float ss = 0.f;
+      for (int c = part; c < NC4; c += 4) {
+        const int col = n0 + c * 4;
+        if (live && col < N) {
+          const float4 v = *reinterpret_cast<const float4*>(sC + r * LDC + c * 4);
+          float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, kD / 4));
+          float4 o;
+          if constexpr (EM == E_H_BIAS) {
+            const float4 b = *reinterpret_cast<const float4*>(a.bias + col);
+            o = make_float4(v.x + b.x, v.y + b.y, v.z + b.z, v.w + b.w);
+          } else {
+            const float4 hv = *hp;
+            o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
+          }
+          *hp = o;
+          ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+        }
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (part == 0 && live) a.ss_out[(size_t)row * kSSStride + ntile] = ss;
+    }
+    return;
+  }
+  if constexpr (EM == E_ACTOUT) {
+    // action_out + Euler update on the row-major state.  Work unit = (row,
+    // 16-column block, e < 8) covering columns e and e + 8 of the block.
+    for (int g = threadIdx.x; g < BM * UPR; g += NT) {
+      const int r = g / UPR, blk = (g % UPR) / 8, e = g % 8;
+      const int row = m0 + r, cb = n0 + blk * 16;
+      if (row >= M || cb >= N) continue;
+      const float v1 = sC[r * LDC + blk * 16 + e], v2 = sC[r * LDC + blk * 16 + 8 + e];
+      const size_t xi = (size_t)row * kAD + cb + e;
+      const float u1 = v1 + a.bias[cb + e], u2 = v2 + a.bias[cb + 8 + e];
+      const float x1 = a.x[xi] + a.dt * u1, x2 = a.x[xi + 8] + a.dt * u2;
+      a.x[xi] = x1;
+      a.x[xi + 8] = x2;
+      if (a.vel_out) { a.vel_out[xi] = u1; a.vel_out[xi + 8] = u2; }
+      if (a.st_out) { a.st_out[xi] = x1; a.st_out[xi + 8] = x2; }
+      if (a.final_out) { a.final_out[xi] = x1; a.final_out[xi + 8] = x2; }
     }
   }
 }
@@ -216,15 +296,13 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   for (int i = 0; i < KPW; ++i) {
     const int ks = w * KPW + i, k = ks * 32 + kl;
     const bool kok = ks < nks && k < K;
-    wf[i] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * a.ldw + k) : make_uint4(0, 0, 0, 0);
+    wf[i] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       const int row = fm * 16 + (lane & 15);
       const bool ok = kok && row < M;
       if constexpr (AM == A_NORM) {
-        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-        ra[i][fm][0] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-        ra[i][fm][1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        load_h8(a, row, k, ok, ra[i][fm][0], ra[i][fm][1]);
       } else {
         af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, blockIdx.x == 0);
       }
@@ -279,9 +357,11 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
 template <int AM, int EM, int FM>
 __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
-  constexpr int BM = 32 * FM, BN = 128, BK = 64, LDK = BK + 8, LDC = BN + 4, CPR = BK / 8;
+  constexpr int BM = 32 * FM, BN = 128, BK = 64, LDC = BN + 4, CPR = BK / 8;
   constexpr int GA = BM * CPR / 256, GW = BN * CPR / 256;
-  constexpr int STAGE = (BM + BN) * LDK;  // halves
+  // LDS tiles keep the blocked layout: (r, c) at ((r / 16) * 8 + c / 8) * 128 + (r % 16) * 8 + c % 8,
+  // so 16-byte piece g of a tile is at g * 8 both in LDS and (within a row block) in memory
+  constexpr int STAGE = (BM + BN) * BK;  // halves
   constexpr int SMEM = 2 * STAGE * 2 > BM * LDC * 4 ? 2 * STAGE * 2 : BM * LDC * 4;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ float sR[BM];
@@ -311,33 +391,34 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   }
   uint4 ra[GA], rw[GW];
   float4 rf[AM == A_NORM ? 2 * GA : 1];  // A_NORM: raw fp32 rows, converted when stored to LDS
+  // piece g of a tile: row (g / 128) * 16 + g % 16, chunk (g / 16) % 8
+  auto prow = [](int g) { return ((g >> 7) << 4) | (g & 15); };
+  auto pcol = [](int g) { return ((g >> 4) & (CPR - 1)) * 8; };
   auto load = [&](int kt) {
     const int kb = kt * BK;
 #pragma unroll
     for (int i = 0; i < GA; ++i) {
-      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8, row = m0 + r, k = kb + c;
+      const int g = tid + 256 * i, row = m0 + prow(g), k = kb + pcol(g);
       const bool ok = row < M && k < K;
       if constexpr (AM == A_NORM) {
-        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-        rf[2 * i] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-        rf[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        load_h8(a, row, k, ok, rf[2 * i], rf[2 * i + 1]);
       } else {
         ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0);
       }
     }
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
-      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8, n = n0 + r, k = kb + c;
-      rw[i] = (n < N && k < K) ? *reinterpret_cast<const uint4*>(a.W + (size_t)n * a.ldw + k) : make_uint4(0, 0, 0, 0);
+      const int g = tid + 256 * i, n = n0 + prow(g), k = kb + pcol(g);
+      rw[i] = (n < N && k < K) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&](int buf, int kt) {
     half_t* sA = stage0 + buf * STAGE;
-    half_t* sW = sA + BM * LDK;
+    half_t* sW = sA + BM * BK;
     const int kb = kt * BK;
 #pragma unroll
     for (int i = 0; i < GA; ++i) {
-      const int g = tid + 256 * i, r = g / CPR, c = (g % CPR) * 8;
+      const int g = tid + 256 * i, r = prow(g), c = pcol(g);
       uint4 v;
       if constexpr (AM == A_NORM) {
         const float sc = sR[r];
@@ -351,12 +432,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
       } else {
         v = ra[i];
       }
-      *reinterpret_cast<uint4*>(sA + r * LDK + c) = v;
+      *reinterpret_cast<uint4*>(sA + g * 8) = v;
     }
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
       const int g = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sW + (g / CPR) * LDK + (g % CPR) * 8) = rw[i];
+      *reinterpret_cast<uint4*>(sW + g * 8) = rw[i];
     }
   };
 
@@ -372,16 +453,17 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) load(kt + 1);
     const half_t* sA = stage0 + (kt & 1) * STAGE;
-    const half_t* sW = sA + BM * LDK;
+    const half_t* sW = sA + BM * BK;
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s) {
+      const int ch = s * 4 + (lane >> 4);
       f16x8 af[FM], bw[4];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *reinterpret_cast<const f16x8*>(sA + (wm * FM * 16 + fm * 16 + (lane & 15)) * LDK + s * 32 + (lane >> 4) * 8);
+        af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * FM + fm) * CPR + ch) * 128 + (lane & 15) * 8);
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn)
-        bw[fn] = *reinterpret_cast<const f16x8*>(sW + (wn * 64 + fn * 16 + (lane & 15)) * LDK + s * 32 + (lane >> 4) * 8);
+        bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * 4 + fn) * CPR + ch) * 128 + (lane & 15) * 8);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -465,6 +547,185 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 #undef SMOLEXP_GEMM_CASE
   return hipErrorInvalidValue;
 }
+
+
+// ----------------------------------------------------------------------------
+// Large-M GEMM with a multi-stage LDS pipeline
+// ----------------------------------------------------------------------------
+// 256 x 128 tiles; four waves each own 64 rows x 128 columns (32 MFMAs per
+// 32-wide k-step).  The k-slabs (BK = 64) rotate through a 3-stage LDS ring
+// that is filled by direct global->LDS loads (global_load_lds_dwordx4: lane l
+// of a wave writes 16 bytes at base + 16 l), so two slabs are in flight while
+// one is multiplied, without staging registers.  One load instruction moves
+// four 16-row x 8-column micro-tiles (1 KB, contiguous in the blocked layout
+// of both operands) and they land in LDS in the same blocked order, where the
+// 16 lanes of a fragment read cover 256 consecutive bytes (no bank conflicts,
+// no swizzle).  Requirements (checked
+// by the launcher): A is fp16 with K % 64 == 0 (K = 720 operands are
+// zero-padded to 768).
+// Waits are explicit: s_waitcnt vmcnt(n) + s_barrier, not __syncthreads
+// (whose fence would wait for every load in flight).
+constexpr int kBigBM = 256, kBigBN = 128, kBigBK = 64, kBigStages = 3;
+
+template <int EM>
+__global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, S = kBigStages, LDC = BN + 4;
+  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
+  constexpr int SMEM = S * STAGE_BYTES > BM * LDC * 4 ? S * STAGE_BYTES : BM * LDC * 4;
+  constexpr int A_LOADS = A_BYTES / 1024 / 4, W_LOADS = W_BYTES / 1024 / 4;  // per wave per stage
+  constexpr int LOADS = A_LOADS + W_LOADS;                                      // 12
+  static_assert(LOADS * (S - 2) < 64, "vmcnt immediate range");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  float* sC = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int M = a.M, N = a.N, K = a.K;
+  const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN, T = nM * nN;
+  const int per = (T + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (tile >= T) return;  // uniform per workgroup, before any barrier
+  const int mt = tile / nN, nt = tile % nN;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int nk = K / BK;
+
+  // Load instruction `blk` of a tile: row block blk / 2, chunks (blk % 2) * 4 .. +3 of the slab;
+  // lane l moves row l % 16 of chunk l / 16 of those.  Row blocks past the last one holding
+  // a row < M (or a column < N) are clamped to it: they only feed outputs that are not stored.
+  const half_t* Ab = static_cast<const half_t*>(a.A);
+  const int kcA = a.lda >> 3, kcW = a.ldw >> 3;
+  const int rbA_last = (M - 1) >> 4, rbW_last = (N - 1) >> 4;
+  auto issue = [&](int kt, int stage) {
+    const int c0 = min(kt, nk - 1) * (BK / 8);  // past the end: reload the last slab (never read)
+    char* base = smem + stage * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int blk = w * A_LOADS + i;
+      const int rb = min((m0 >> 4) + (blk >> 1), rbA_last);
+      const half_t* src = Ab + ((size_t)rb * kcA + c0 + (blk & 1) * 4) * 128 + lane * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i) {
+      const int blk = w * W_LOADS + i;
+      const int nb = min((n0 >> 4) + (blk >> 1), rbW_last);
+      const half_t* src = a.W + ((size_t)nb * kcW + c0 + (blk & 1) * 4) * 128 + lane * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(base + A_BYTES + blk * 1024), 16, 0,
+                                       0);
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st);
+  constexpr int WAIT = (LOADS * (S - 2)) & 15, WAIT_HI = (LOADS * (S - 2)) >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of slab kt are done once at most LOADS*(S-2) newer ones remain
+    __builtin_amdgcn_s_waitcnt(WAIT | (WAIT_HI << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; slab kt-1 is no longer read
+    issue(kt + S - 1, (kt + S - 1) % S);
+    const char* base = smem + (kt % S) * STAGE_BYTES;
+    const half_t* sA = reinterpret_cast<const half_t*>(base);
+    const half_t* sW = reinterpret_cast<const half_t*>(base + A_BYTES);
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      const int ch = s * 4 + (lane >> 4);  // 16-byte chunk of this lane's fragment within the slab
+      f16x8 af[4], bw[8];
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm)
+        af[fm] = *reinterpret_cast<const f16x8*>(sA + ((w * 4 + fm) * 8 + ch) * 128 + (lane & 15) * 8);
+#pragma unroll
+      for (int fn = 0; fn < 8; ++fn)
+        bw[fn] = *reinterpret_cast<const f16x8*>(sW + (fn * 8 + ch) * 128 + (lane & 15) * 8);
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 8; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
+  __syncthreads();
+
+  const float ws = a.w_scale;
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sC[(w * 64 + fm * 16 + (lane >> 4) * 4 + r) * LDC + fn * 16 + (lane & 15)] = acc[fm][fn][r] * ws;
+  __syncthreads();
+  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0, nt);
+}
+
+// RMSNorm to an fp16 operand for the large-M GEMMs: out[row][k] = h[row][k] *
+// r_row * g[k] for k < 720, zero for 720 <= k < ldo (the K padding) and for the
+// rows of the last row block past M.  One workgroup per 16-row block; thread
+// (r, p) = (tid % 16, tid / 16) handles row r, chunks p, p + 16, ...
+__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const GemmArgs a) {
+  __shared__ float sP[16][17];
+  __shared__ float sR[16];
+  const int tid = threadIdx.x, r = tid & 15, part = tid >> 4;
+  const int row = blockIdx.x * 16 + r;
+  const bool live = row < a.M;
+  float s = 0.f;
+  if (live)
+    for (int j = part; j < a.ss_nt; j += 16) s += a.ss_in[(size_t)row * kSSStride + j];
+  sP[r][part] = s;
+  __syncthreads();
+  if (tid < 16) {
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) t += sP[tid][p];
+    sR[tid] = 1.0f / sqrtf(t * a.inv_k + a.eps);
+  }
+  __syncthreads();
+  const float rs = sR[r];
+  const int kc = a.ldo >> 3;
+  for (int c = part; c < kc; c += 16) {
+    const int k = c * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (live && k < kD) {
+      float4 h0, h1;
+      load_h8(a, row, k, true, h0, h1);
+      const float4 g0 = *reinterpret_cast<const float4*>(a.gain + k), g1 = *reinterpret_cast<const float4*>(a.gain + k + 4);
+      v[0] = h0.x * rs * g0.x; v[1] = h0.y * rs * g0.y; v[2] = h0.z * rs * g0.z; v[3] = h0.w * rs * g0.w;
+      v[4] = h1.x * rs * g1.x; v[5] = h1.y * rs * g1.y; v[6] = h1.z * rs * g1.z; v[7] = h1.w * rs * g1.w;
+    }
+    *reinterpret_cast<uint4*>(a.out16 + t16_off(row, k, kc)) = pack8(v);
+  }
+}
+
+hipError_t launch_rmsnorm_f16(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((a.M + 15) / 16), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_big(EMode em, const GemmArgs& a, hipStream_t s) {
+  const int T = ((a.M + kBigBM - 1) / kBigBM) * ((a.N + kBigBN - 1) / kBigBN);
+  const dim3 grid(8 * ((T + 7) / 8)), block(256);
+  if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
+  switch (em) {
+    case E_QKV: hipLaunchKernelGGL(gemm_big<E_QKV>, grid, block, 0, s, a); break;
+    case E_SWIGLU: hipLaunchKernelGGL(gemm_big<E_SWIGLU>, grid, block, 0, s, a); break;
+    case E_H_RESID: hipLaunchKernelGGL(gemm_big<E_H_RESID>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int big_tiles(int M, int N) { return ((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN); }
+
+// Measured on MI355X: with fewer than ~160 tiles of 256 x 128 the large-tile GEMM
+// leaves too many CUs idle and the 64/128-row tiled kernel is faster.
+bool use_big_gemm(int M, int N) { return M > 64 && big_tiles(M, N) >= 160; }
 
 // ----------------------------------------------------------------------------
 // Block-masked grouped-query attention
@@ -658,13 +919,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 
   if (rvalid) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    half_t* op = a.out + ((size_t)b * kChunk + qi) * kNQ + hq * kHD + (lane >> 4) * 4;
+    const int orow = b * kChunk + qi;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
-      *reinterpret_cast<uint2*>(op + m * 16) = pk4.u;
+      *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
     }
   }
 }
@@ -748,7 +1009,7 @@ __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
       union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk4.h[e] = (half_t)(acc[e] * inv);
-      *reinterpret_cast<uint2*>(a.out + ((size_t)b * kChunk + qi2) * kNQ + hq2 * kHD + d0) = pk4.u;
+      *reinterpret_cast<uint2*>(a.out + t16_off(b * kChunk + qi2, hq2 * kHD + d0, kNQ / 8)) = pk4.u;
     }
   }
 }
@@ -784,7 +1045,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
     // angle is reduced to [0, 2 pi) in fp64, then sin/cos run in fp32.
     // Row j of W_t1[:, 720:] is read once, 8 halves per lane, for every step.
     const int j = blockIdx.x * kTimeRowsPerBlock + (tid >> 4), part = tid & 15;
-    const half_t* wr = a.w_t1 + (size_t)j * (2 * kD) + kD;
+    const half_t* wr = a.w_t1e + (size_t)j * kD;
     constexpr int CH = kD / 8;                  // 90 chunks of 8
     constexpr int PER = (CH + 15) / 16;         // 6 chunks per lane
     uint4 wv[PER];

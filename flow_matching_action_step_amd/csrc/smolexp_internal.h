@@ -26,11 +26,28 @@ constexpr int kMaxLayers = 64;
 typedef _Float16 half_t;
 typedef uint16_t bf16_t;       // bf16 bit pattern
 
+// Blocked layout of every GEMM operand (weights [N][K] and the fp16
+// activations [M][K]): 16-row x 8-column micro-tiles of 256 bytes, row block
+// major, so element (r, k) of a matrix stored with KC = K / 8 column chunks
+// sits at ((r / 16) * KC + k / 8) * 128 + (r % 16) * 8 + k % 8.  The 16 rows
+// of one chunk are contiguous, which is exactly what one MFMA fragment load
+// (lane l: row l % 16, chunk l / 16) reads: four 256-byte runs, 1 KB in a row.
+// Row counts are padded to a multiple of 16.
+__host__ __device__ inline size_t t16_off(int r, int k, int kc) {
+  return ((size_t)(r >> 4) * kc + (k >> 3)) * 128 + (r & 15) * 8 + (k & 7);
+}
+// The fp32 residual stream uses the same idea with 16-row x 4-column tiles:
+// element (r, k) with K4 = K / 4 column chunks at ((r / 16) * K4 + k / 4) * 64 + (r % 16) * 4 + k % 4.
+__host__ __device__ inline size_t t32_off(int r, int k, int k4) {
+  return ((size_t)(r >> 4) * k4 + (k >> 2)) * 64 + (r & 15) * 4 + (k & 3);
+}
+
 // A-operand sources of the GEMM.
 enum AMode : int {
-  A_F16 = 0,    // fp16 [M][lda]
-  A_NORM = 1,   // fp32 residual [M][lda], RMSNorm applied on load (row scale from partial sums, gain)
-  A_X = 2,      // fp32 Euler state [M][32], prefix overwrite applied on load
+  A_F16 = 0,    // fp16, blocked (t16_off), lda = stored K (multiple of 8)
+  A_NORM = 1,   // fp32 residual, blocked (t32_off), lda = 720; RMSNorm applied on load (row scale
+                // from partial sums, gain)
+  A_X = 2,      // fp32 Euler state, row-major [M][32]; prefix overwrite applied on load
 };
 
 // GEMM epilogues.
@@ -60,15 +77,15 @@ struct GemmArgs {
   const float* prev;
   int ow_rows;
   float t;
-  // weights [N][ldw] fp16, values scaled by 1 / w_scale
+  // weights: fp16 [N][K] blocked (t16_off) with ldw = stored K, values scaled by 1 / w_scale
   const half_t* W;
   int ldw;
   float w_scale;
   // epilogue
   const float* bias;   // bias, or the per-step time vector for E_TIMEIN
-  half_t* out16;
+  half_t* out16;       // fp16 activations, blocked (t16_off), ldo = stored K
   int ldo;
-  float* h;
+  float* h;            // fp32 residual stream, blocked (t32_off), K = 720
   float* ss_out;
   bf16_t* q;
   bf16_t* kc;
@@ -88,7 +105,7 @@ struct AttnArgs {
   const bf16_t* pk;      // this layer's prefix K: [B][5][P][64]
   const bf16_t* pv;      // this layer's prefix V
   const uint8_t* mask;   // [B][P]
-  half_t* out;           // [B*50][960]
+  half_t* out;           // [B*50][960] fp16, blocked (t16_off)
   int B, P;
 };
 
@@ -101,7 +118,7 @@ struct PrologueArgs {
   int* nvalid;             // out [B]
   const float* x_in;       // [B][50][32]
   float* x;                // out: Euler state
-  const half_t* w_t1;      // time_in weight [720][1440] (fp16, scaled)
+  const half_t* w_t1e;     // time_in weight, its time-embedding half [720][720] row-major (fp16, scaled)
   float s_t1;
   const float* b_t1;
   float* cvec;             // out [n_t][720] = W_t1[:, 720:] e(t) + b_t1
@@ -110,12 +127,21 @@ struct PrologueArgs {
 
 // How one GEMM is cut up (kernels.hip decides, the host sizes workspaces from it).
 struct GemmPlan {
-  int kind;      // 0: skinny (M <= 64): one workgroup per 16 columns; 1: tiled: 128 x 128 tiles
+  int kind;      // 0: skinny (M <= 64): one workgroup per 16 columns; 1: tiled: 128 x 128 tiles;
+                 // 2: large-tile GEMM on a pre-normalised operand (recorded for timing only)
   int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
   int bm;        // tiled: rows per tile (64 or 128)
   int ntiles_n;  // output tiles along N (= sum-of-squares slots written by an N = 720 producer)
 };
 GemmPlan plan_gemm(int M, int N, int K);
+
+// Large-M GEMM (fp16 A, K % 64 == 0; epilogues E_QKV, E_SWIGLU, E_H_RESID) and the
+// RMSNorm -> fp16 pre-pass that feeds it (a.A = h, a.out16/a.ldo = destination).
+hipError_t launch_gemm_big(EMode em, const GemmArgs& a, hipStream_t s);
+hipError_t launch_rmsnorm_f16(const GemmArgs& a, hipStream_t s);
+int big_tiles(int M, int N);
+bool use_big_gemm(int M, int N);  // RMSNorm pre-pass + large-tile GEMM for this Q/K/V or gate/up shape
+constexpr int kKPad = 768;  // K = 720 operands of the large-M GEMM, zero-padded to a multiple of 64
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
