@@ -6,10 +6,13 @@
 //   reads whole 256-byte runs.  Weights are the
 //   checkpoint's bf16 values re-encoded exactly in fp16 with a power-of-two
 //   scale per matrix; activations are rounded to fp16 (8x finer than bf16).
-//   The A-operand load fuses RMSNorm (row scale from partial sums of squares
-//   that the producer of the residual stream wrote) or the prefix overwrite;
-//   epilogues fuse bias, SiLU, RoPE, SwiGLU, the residual add and the Euler
-//   update.
+//   RMSNorm is fused: its gain is folded into the columns of the weight that
+//   follows it (host side), and the row scale 1/rms(h) multiplies either the
+//   operand as it is loaded (large M: from per-tile partial sums of squares
+//   written by the producer of the residual stream) or the accumulated sums
+//   (M <= 64: from the rows the workgroup loads anyway).  The A-operand load
+//   also fuses the prefix overwrite; epilogues fuse bias, SiLU, RoPE, SwiGLU,
+//   the residual add and the Euler update.
 // Attention: block-masked grouped-query attention on v_mfma_f32_16x16x32_bf16
 //   over the bf16 prefix K/V cache and the chunk's own K/V, with an online
 //   softmax in fp32 and 64-key blocks staged in LDS.
@@ -66,9 +69,8 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 template <int AM>
 __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool ok, float rscale,
                                          bool write_x) {
-  static_assert(AM != A_NORM, "the fp32 residual is loaded by the kernels themselves");
   (void)rscale;
-  if constexpr (AM == A_F16) {
+  if constexpr (AM == A_F16 || AM == A_NORM) {
     return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + t16_off(row, k, a.lda >> 3))
               : make_uint4(0, 0, 0, 0);
   } else {  // A_X: Euler state; rows i < ow_rows of each chunk take the flow-path point t*eps + (1-t)*prev
@@ -100,46 +102,24 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
   }
 }
 
-// Columns k..k+7 (k % 8 == 0) of row `row` of the blocked fp32 residual.
-__device__ __forceinline__ void load_h8(const GemmArgs& a, int row, int k, bool ok, float4& lo, float4& hi) {
-  if (ok) {
-    const float* p = static_cast<const float*>(a.A) + t32_off(row, k, a.lda >> 2);
-    lo = *reinterpret_cast<const float4*>(p);
-    hi = *reinterpret_cast<const float4*>(p + 64);  // next 4-column chunk of the same row block
-  } else {
-    lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+// Sum of squares of the 8 fp16 values of one MFMA A fragment.
+__device__ __forceinline__ float sumsq8(const f16x8& u) {
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q += (float)u[e] * (float)u[e];
+  return q;
 }
 
-// RMSNorm row scales 1/sqrt(mean(h^2) + eps) for rows m0..m0+BM-1 from the
-// producer's per-N-tile partial sums of squares.  NT/BM threads share a row
-// and sum every (NT/BM)-th partial, so the loads are issued side by side.
-template <int BM, int NT>
-__device__ __forceinline__ void row_scales(const GemmArgs& a, int m0, float* sR) {
-  constexpr int TPR = NT / BM;
-  static_assert(TPR >= 1 && TPR <= 64 && (TPR & (TPR - 1)) == 0, "threads per row: a power of two within a wave");
-  const int r = threadIdx.x / TPR, part = threadIdx.x % TPR, row = m0 + r;
-  float s = 0.f;
-  if (row < a.M) {
-    const float* src = a.ss_in + (size_t)row * kSSStride;
-#pragma unroll
-    for (int j0 = 0; j0 < kSSStride; j0 += TPR) {
-      const int j = j0 + part;
-      if (j < a.ss_nt) s += src[j];
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (part == 0) sR[r] = 1.0f / sqrtf(s * a.inv_k + a.eps);
-}
+// 1/rms of a row from its sum of squares.
+__device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { return 1.0f / sqrtf(sumsq * a.inv_k + a.eps); }
 
-// Epilogue on a finished tile sC[BM][LDC] (fp32, weight scale applied) whose
-// rows start at m0 and columns at n0 (BN a multiple of 16).  ntile = this
-// tile's sum-of-squares slot.  The blocked outputs (fp16 activations, the fp32
-// residual) are written with 16 consecutive lanes on 16 consecutive rows of
-// one 16-byte column chunk, i.e. 256 contiguous bytes per store.
+// Epilogue on a finished tile sC[BM][LDC] (fp32, weight and row scales
+// applied) whose rows start at m0 and columns at n0 (BN a multiple of 16).
+// The blocked outputs (fp16 activations, the fp32 residual and its fp16 copy)
+// are written with 16 consecutive lanes on 16 consecutive rows of one column
+// chunk, i.e. contiguous runs of 256 (128) bytes per store.
 template <int EM, int BM, int BN, int LDC, int NT>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0, int ntile) {
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0 && (BM * UPR) % NT == 0, "rows inside one wave, uniform trip count");
   const int M = a.M, N = a.N;
@@ -221,16 +201,15 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     return;
   }
   if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
-    // Work unit = (row, one 4-column chunk of the fp32 residual).  Lane = r16 + 16 * part:
-    // a wave owns one 16-row block per pass and its four parts take every fourth chunk,
-    // so a row's partial sum of squares meets inside the wave.
+    // Work unit = (row, one 4-column chunk of the fp32 residual and of its fp16 copy).
+    // Lane = r16 + 16 * part: a wave owns one 16-row block per pass and its four parts
+    // take every fourth chunk.
     constexpr int NC4 = BN / 4, NWV = NT / 64, RB = BM / 16;
     static_assert(NC4 % 4 == 0 && NT % 64 == 0, "uniform trip counts");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, part = lane >> 4;
     for (int rb = wv; rb < RB; rb += NWV) {
       const int r = rb * 16 + r16, row = m0 + r;
       const bool live = row < M;
-      float ss = 0.f;
       for (int c = part; c < NC4; c += 4) {
         const int col = n0 + c * 4;
         if (live && col < N) {
@@ -245,12 +224,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
             o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
           }
           *hp = o;
-          ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+          union { half_t e[4]; uint2 u; } o16;
+          o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
+          *reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)) = o16.u;
         }
       }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      if (part == 0 && live) a.ss_out[(size_t)row * kSSStride + ntile] = ss;
     }
     return;
   }
@@ -275,13 +253,16 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 }
 
 // M <= 64.  One workgroup per 16 output columns; wave w takes k-steps
-// w*KPW .. w*KPW+KPW-1 (32 wide each).
+// w*KPW .. w*KPW+KPW-1 (32 wide each).  A_NORM: the rows of fp16(h) go to
+// the MFMA unscaled, so no load waits on the row scale; each wave also sums
+// the squares of its slice of every row, and 1/rms(row) scales the finished
+// sums (a per-row constant, so this equals normalising first up to rounding).
 template <int AM, int EM, int KPW>
 __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   constexpr int NW = 8, LDC = 16;
   __shared__ float sRed[NW * 64 * 16];
   __shared__ float sC[64 * LDC];
-  __shared__ float sR[64];
+  __shared__ float sQ[AM == A_NORM ? NW : 1][64];  // per-wave partial sums of squares of the rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n0 = blockIdx.x * 16;
   const int M = a.M, N = a.N, K = a.K;
@@ -290,8 +271,6 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
 
   uint4 wf[KPW];
   uint4 af[KPW][4];
-  float4 ra[AM == A_NORM ? KPW : 1][4][2];
-  float4 gv[AM == A_NORM ? KPW : 1][2];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = w * KPW + i, k = ks * 32 + kl;
@@ -301,20 +280,8 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     for (int fm = 0; fm < 4; ++fm) {
       const int row = fm * 16 + (lane & 15);
       const bool ok = kok && row < M;
-      if constexpr (AM == A_NORM) {
-        load_h8(a, row, k, ok, ra[i][fm][0], ra[i][fm][1]);
-      } else {
-        af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, blockIdx.x == 0);
-      }
+      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, blockIdx.x == 0);
     }
-    if constexpr (AM == A_NORM) {
-      gv[i][0] = kok ? *reinterpret_cast<const float4*>(a.gain + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-      gv[i][1] = kok ? *reinterpret_cast<const float4*>(a.gain + k + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  if constexpr (AM == A_NORM) {
-    row_scales<64, 512>(a, 0, sR);
-    __syncthreads();
   }
   f32x4 acc[4];
 #pragma unroll
@@ -324,18 +291,19 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     const f16x8 bw = __builtin_bit_cast(f16x8, wf[i]);
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
-      uint4 frag;
-      if constexpr (AM == A_NORM) {
-        const float sc = sR[fm * 16 + (lane & 15)];
-        const float v[8] = {ra[i][fm][0].x * sc * gv[i][0].x, ra[i][fm][0].y * sc * gv[i][0].y,
-                            ra[i][fm][0].z * sc * gv[i][0].z, ra[i][fm][0].w * sc * gv[i][0].w,
-                            ra[i][fm][1].x * sc * gv[i][1].x, ra[i][fm][1].y * sc * gv[i][1].y,
-                            ra[i][fm][1].z * sc * gv[i][1].z, ra[i][fm][1].w * sc * gv[i][1].w};
-        frag = pack8(v);
-      } else {
-        frag = af[i][fm];
-      }
-      acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, frag), bw, acc[fm], 0, 0, 0);
+      acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i][fm]), bw, acc[fm], 0, 0, 0);
+    }
+  }
+  if constexpr (AM == A_NORM) {
+    // this wave's share of each row's sum of squares (lanes l, l+16, l+32, l+48 hold row l % 16)
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPW; ++i) q += sumsq8(__builtin_bit_cast(f16x8, af[i][fm]));
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+      if (lane < 16) sQ[w][fm * 16 + lane] = q;
     }
   }
 #pragma unroll
@@ -348,10 +316,17 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * 64 * 16 + i];
-    sC[(i / 16) * LDC + (i % 16)] = s * ws;
+    float sc = ws;
+    if constexpr (AM == A_NORM) {  // RMSNorm: rows were multiplied unscaled, 1/rms(h) applied here
+      float q = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) q += sQ[w2][i / 16];
+      sc *= rms_scale(a, q);
+    }
+    sC[(i / 16) * LDC + (i % 16)] = s * sc;
   }
   __syncthreads();
-  epilogue_tile<EM, 64, 16, LDC, 512>(a, sC, 0, n0, blockIdx.x);
+  epilogue_tile<EM, 64, 16, LDC, 512>(a, sC, 0, n0);
 }
 
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
@@ -364,8 +339,6 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   constexpr int STAGE = (BM + BN) * BK;  // halves
   constexpr int SMEM = 2 * STAGE * 2 > BM * LDC * 4 ? 2 * STAGE * 2 : BM * LDC * 4;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  __shared__ float sR[BM];
-  __shared__ float sG[AM == A_NORM ? kD : 1];
   half_t* stage0 = reinterpret_cast<half_t*>(smem);
   float* sC = reinterpret_cast<float*>(smem);
 
@@ -384,13 +357,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk = (K + BK - 1) / BK;
 
-  if constexpr (AM == A_NORM) {
-    row_scales<BM, 256>(a, m0, sR);
-    for (int k = tid; k < K; k += 256) sG[k] = a.gain[k];
-    __syncthreads();
-  }
   uint4 ra[GA], rw[GW];
-  float4 rf[AM == A_NORM ? 2 * GA : 1];  // A_NORM: raw fp32 rows, converted when stored to LDS
   // piece g of a tile: row (g / 128) * 16 + g % 16, chunk (g / 16) % 8
   auto prow = [](int g) { return ((g >> 7) << 4) | (g & 15); };
   auto pcol = [](int g) { return ((g >> 4) & (CPR - 1)) * 8; };
@@ -400,11 +367,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
     for (int i = 0; i < GA; ++i) {
       const int g = tid + 256 * i, row = m0 + prow(g), k = kb + pcol(g);
       const bool ok = row < M && k < K;
-      if constexpr (AM == A_NORM) {
-        load_h8(a, row, k, ok, rf[2 * i], rf[2 * i + 1]);
-      } else {
-        ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0);
-      }
+      ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0);
     }
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
@@ -412,27 +375,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
       rw[i] = (n < N && k < K) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store = [&](int buf, int kt) {
+  auto store = [&](int buf) {
     half_t* sA = stage0 + buf * STAGE;
     half_t* sW = sA + BM * BK;
-    const int kb = kt * BK;
 #pragma unroll
     for (int i = 0; i < GA; ++i) {
-      const int g = tid + 256 * i, r = prow(g), c = pcol(g);
-      uint4 v;
-      if constexpr (AM == A_NORM) {
-        const float sc = sR[r];
-        const int k = kb + c;
-        const bool kin = k < K;
-        float f[8] = {rf[2 * i].x, rf[2 * i].y, rf[2 * i].z, rf[2 * i].w,
-                      rf[2 * i + 1].x, rf[2 * i + 1].y, rf[2 * i + 1].z, rf[2 * i + 1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = kin ? f[e] * sc * sG[k + e] : 0.f;
-        v = pack8(f);
-      } else {
-        v = ra[i];
-      }
-      *reinterpret_cast<uint4*>(sA + g * 8) = v;
+      const int g = tid + 256 * i;
+      *reinterpret_cast<uint4*>(sA + g * 8) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
@@ -442,13 +391,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   };
 
   f32x4 acc[FM][4];
+  float q[FM];  // A_NORM: this lane's share of the sum of squares of row (lane % 16) of each fm tile
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fm = 0; fm < FM; ++fm) {
+    q[fm] = 0.f;
 #pragma unroll
     for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   load(0);
-  store(0, 0);
+  store(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) load(kt + 1);
@@ -469,21 +421,35 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+      if constexpr (AM == A_NORM) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) q[fm] += sumsq8(af[fm]);
+      }
     }
-    if (kt + 1 < nk) store((kt + 1) & 1, kt + 1);
+    if (kt + 1 < nk) store((kt + 1) & 1);
     __syncthreads();
   }
 
   const float ws = a.w_scale;
+  if constexpr (AM == A_NORM) {  // whole-row sums: the four lane groups hold the four k-chunks
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      q[fm] += __shfl_xor(q[fm], 16);
+      q[fm] += __shfl_xor(q[fm], 32);
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
+    for (int r = 0; r < 4; ++r) {
+      const int rl = wm * FM * 16 + fm * 16 + (lane >> 4) * 4 + r;
+      // row rl's sum of squares sits in the lanes whose lane % 16 is rl % 16
+      const float sc = AM == A_NORM ? ws * rms_scale(a, __shfl(q[fm], (lane >> 4) * 4 + r)) : ws;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sC[(wm * FM * 16 + fm * 16 + (lane >> 4) * 4 + r) * LDC + wn * 64 + fn * 16 + (lane & 15)] = acc[fm][fn][r] * ws;
+      for (int fn = 0; fn < 4; ++fn) sC[rl * LDC + wn * 64 + fn * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
+    }
   __syncthreads();
-  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0, nt);
+  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0);
 }
 
 GemmPlan plan_gemm(int M, int N, int K) {
@@ -567,7 +533,7 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 // (whose fence would wait for every load in flight).
 constexpr int kBigBM = 256, kBigBN = 128, kBigBK = 64, kBigStages = 3;
 
-template <int EM>
+template <int EM, bool NORM>
 __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
   constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, S = kBigStages, LDC = BN + 4;
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
@@ -587,6 +553,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
   const int mt = tile / nN, nt = tile % nN;
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk = K / BK;
+  // NORM: A is fp16(h) unnormalised; each wave sums the squares of its 64 rows as their
+  // fragments go by, and 1/rms of each row scales the finished sums.
 
   // Load instruction `blk` of a tile: row block blk / 2, chunks (blk % 2) * 4 .. +3 of the slab;
   // lane l moves row l % 16 of chunk l / 16 of those.  Row blocks past the last one holding
@@ -617,6 +585,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
   };
 
   f32x4 acc[4][8];
+  float q[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
@@ -648,74 +617,53 @@ __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
 #pragma unroll
         for (int fn = 0; fn < 8; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) q[fm] += sumsq8(af[fm]);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
   __syncthreads();
 
   const float ws = a.w_scale;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      q[fm] += __shfl_xor(q[fm], 16);
+      q[fm] += __shfl_xor(q[fm], 32);
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 8; ++fn)
+    for (int r = 0; r < 4; ++r) {
+      const int rl = w * 64 + fm * 16 + (lane >> 4) * 4 + r;
+      const float sc = NORM ? ws * rms_scale(a, __shfl(q[fm], (lane >> 4) * 4 + r)) : ws;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sC[(w * 64 + fm * 16 + (lane >> 4) * 4 + r) * LDC + fn * 16 + (lane & 15)] = acc[fm][fn][r] * ws;
-  __syncthreads();
-  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0, nt);
-}
-
-// RMSNorm to an fp16 operand for the large-M GEMMs: out[row][k] = h[row][k] *
-// r_row * g[k] for k < 720, zero for 720 <= k < ldo (the K padding) and for the
-// rows of the last row block past M.  One workgroup per 16-row block; thread
-// (r, p) = (tid % 16, tid / 16) handles row r, chunks p, p + 16, ...
-__global__ __launch_bounds__(256) void rmsnorm_f16_kernel(const GemmArgs a) {
-  __shared__ float sP[16][17];
-  __shared__ float sR[16];
-  const int tid = threadIdx.x, r = tid & 15, part = tid >> 4;
-  const int row = blockIdx.x * 16 + r;
-  const bool live = row < a.M;
-  float s = 0.f;
-  if (live)
-    for (int j = part; j < a.ss_nt; j += 16) s += a.ss_in[(size_t)row * kSSStride + j];
-  sP[r][part] = s;
-  __syncthreads();
-  if (tid < 16) {
-    float t = 0.f;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) t += sP[tid][p];
-    sR[tid] = 1.0f / sqrtf(t * a.inv_k + a.eps);
-  }
-  __syncthreads();
-  const float rs = sR[r];
-  const int kc = a.ldo >> 3;
-  for (int c = part; c < kc; c += 16) {
-    const int k = c * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (live && k < kD) {
-      float4 h0, h1;
-      load_h8(a, row, k, true, h0, h1);
-      const float4 g0 = *reinterpret_cast<const float4*>(a.gain + k), g1 = *reinterpret_cast<const float4*>(a.gain + k + 4);
-      v[0] = h0.x * rs * g0.x; v[1] = h0.y * rs * g0.y; v[2] = h0.z * rs * g0.z; v[3] = h0.w * rs * g0.w;
-      v[4] = h1.x * rs * g1.x; v[5] = h1.y * rs * g1.y; v[6] = h1.z * rs * g1.z; v[7] = h1.w * rs * g1.w;
+      for (int fn = 0; fn < 8; ++fn) sC[rl * LDC + fn * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
-    *reinterpret_cast<uint4*>(a.out16 + t16_off(row, k, kc)) = pack8(v);
-  }
+  __syncthreads();
+  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0);
 }
 
-hipError_t launch_rmsnorm_f16(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_f16_kernel, dim3((a.M + 15) / 16), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_big(EMode em, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
   const int T = ((a.M + kBigBM - 1) / kBigBM) * ((a.N + kBigBN - 1) / kBigBN);
   const dim3 grid(8 * ((T + 7) / 8)), block(256);
   if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
   switch (em) {
-    case E_QKV: hipLaunchKernelGGL(gemm_big<E_QKV>, grid, block, 0, s, a); break;
-    case E_SWIGLU: hipLaunchKernelGGL(gemm_big<E_SWIGLU>, grid, block, 0, s, a); break;
-    case E_H_RESID: hipLaunchKernelGGL(gemm_big<E_H_RESID>, grid, block, 0, s, a); break;
+    case E_QKV:
+      if (!norm) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_big<E_QKV, true>), grid, block, 0, s, a);
+      break;
+    case E_SWIGLU:
+      if (!norm) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_big<E_SWIGLU, true>), grid, block, 0, s, a);
+      break;
+    case E_H_RESID:
+      if (norm) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_big<E_H_RESID, false>), grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -23,8 +23,6 @@ struct Mat {
 struct LayerDev {
   bool self_attn = false;
   Mat qkv, o, gu, down;
-  float* g1 = nullptr;
-  float* g2 = nullptr;
 };
 
 // Everything that distinguishes one enqueued call from another.
@@ -71,13 +69,13 @@ struct smolexp_handle {
   void* wmem = nullptr;
   Mat w_in, w_t1, w_t2, w_out;
   half_t* w_t1e = nullptr;  // W_t1[:, 720:] row-major, same scale as w_t1 (read by the prologue)
-  float *b_in = nullptr, *b_t1 = nullptr, *b_t2 = nullptr, *gf = nullptr, *b_out = nullptr;
+  float *b_in = nullptr, *b_t1 = nullptr, *b_t2 = nullptr, *b_out = nullptr;
   std::vector<LayerDev> layers;
 
   // workspace
   void* wsmem = nullptr;
-  float *x = nullptr, *h = nullptr, *ss = nullptr, *cvec = nullptr;
-  half_t *y16 = nullptr, *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *n16 = nullptr;
+  float *x = nullptr, *h = nullptr, *cvec = nullptr;
+  half_t *y16 = nullptr, *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *h16 = nullptr;
   bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
   int* nvalid = nullptr;
   float2* rope = nullptr;
@@ -153,6 +151,13 @@ float bf2f(uint16_t b) {
 // Power-of-two exponent s so that max|w| * 2^s lies in [2^14, 2^15): every
 // bf16 value (8 significant bits) then maps to an fp16 normal number exactly,
 // down to max|w| * 2^-29; smaller values land on fp16's subnormal grid.
+int shift_for(float mx) {
+  if (!(mx > 0.f) || !isfinite(mx)) return 0;
+  int e;
+  frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+  return 15 - e;
+}
+
 int pick_shift(const std::vector<std::pair<const uint16_t*, size_t>>& parts) {
   float mx = 0.f;
   for (auto& p : parts)
@@ -160,10 +165,7 @@ int pick_shift(const std::vector<std::pair<const uint16_t*, size_t>>& parts) {
       const float v = fabsf(bf2f(p.first[i]));
       if (v > mx) mx = v;
     }
-  if (!(mx > 0.f) || !isfinite(mx)) return 0;
-  int e;
-  frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-  return 15 - e;
+  return shift_for(mx);
 }
 
 void to_f16(const uint16_t* src, size_t n, int shift, half_t* dst) {
@@ -177,6 +179,22 @@ void pack_t16(const std::vector<const uint16_t*>& rows, int K, int kstore, int s
   const float m = ldexpf(1.f, shift);
   for (size_t n = 0; n < rows.size(); ++n)
     for (int k = 0; k < K; ++k) dst[t16_off((int)n, k, kstore / 8)] = (half_t)(bf2f(rows[n][k]) * m);
+}
+
+// A weight that follows an RMSNorm, with the norm's gain g folded into its columns:
+// W'[n][k] = W[n][k] * g[k] (exact in fp32: two 8-bit significands), stored like
+// pack_t16 with the shift chosen for max |W'| and rounded once to fp16.  Returns the shift.
+int pack_t16_gain(const std::vector<const uint16_t*>& rows, int K, int kstore, const uint16_t* gain, half_t* dst) {
+  std::vector<float> g(K);
+  for (int k = 0; k < K; ++k) g[k] = bf2f(gain[k]);
+  float mx = 0.f;
+  for (size_t n = 0; n < rows.size(); ++n)
+    for (int k = 0; k < K; ++k) mx = fmaxf(mx, fabsf(bf2f(rows[n][k]) * g[k]));
+  const int shift = shift_for(mx);
+  const float m = ldexpf(1.f, shift);
+  for (size_t n = 0; n < rows.size(); ++n)
+    for (int k = 0; k < K; ++k) dst[t16_off((int)n, k, kstore / 8)] = (half_t)(bf2f(rows[n][k]) * g[k] * m);
+  return shift;
 }
 
 // Row pointers of a row-major [N][ld] bf16 matrix, starting at column c0.
@@ -217,7 +235,6 @@ CallKey key_of(const CallArgs& c) {
 // The launch sequence of one call.
 int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
-  const int nt_h = plan_gemm(M, kD, kD).ntiles_n;  // sum-of-squares slots of every N = 720 producer
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
   hipError_t e;
   if (record_probes) {
@@ -259,21 +276,18 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     record(probe, plan, am, em, g);
     return launch_gemm(plan, am, em, g, s);
   };
-  // RMSNorm'd projections (Q/K/V, gate/up): at large M the normalised fp16 operand is
-  // written once (n16, K padded to 768) and multiplied by the large-tile GEMM.
-  auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t {
-    if (!use_big_gemm(g.M, g.N)) return gemm(probe, A_NORM, em, g);
-    GemmArgs gn = g;
-    gn.out16 = h->n16; gn.ldo = kKPad;
-    hipError_t e2 = launch_rmsnorm_f16(gn, s);
-    if (e2 != hipSuccess) return e2;
-    GemmArgs gb = g;
-    gb.A = h->n16; gb.lda = kKPad; gb.K = kKPad;
+  // RMSNorm'd projections (Q/K/V, gate/up, action_out) read h16 = fp16(h); at large M
+  // Q/K/V and gate/up run on the large-tile GEMM over the zero-padded K = 768.
+  auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g0) -> hipError_t {
+    GemmArgs g = g0;
+    g.A = h->h16; g.lda = kKPad;
+    if (em == E_ACTOUT || !use_big_gemm(g.M, g.N)) return gemm(probe, A_NORM, em, g);
+    g.K = kKPad;
     GemmPlan plan;
     memset(&plan, 0, sizeof(plan));
     plan.kind = 2;
-    record(probe, plan, A_F16, em, gb);
-    return launch_gemm_big(em, gb, s);
+    record(probe, plan, A_NORM, em, g);
+    return launch_gemm_big(em, true, g, s);
   };
 
   for (int k = 0; k < n_t; ++k) {
@@ -302,14 +316,13 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     GemmArgs go = g;
     go.N = kD; go.K = kD; go.A = h->s16; go.lda = kD;
     go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
-    go.h = h->h; go.ss_out = h->ss;
+    go.h = h->h; go.h16 = h->h16;
     if ((e = gemm(-1, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
 
     for (int l = 0; l < L; ++l) {
       const LayerDev& ld = h->layers[l];
       GemmArgs gq = g;
-      gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD; gq.A = h->h; gq.lda = kD;
-      gq.ss_in = h->ss; gq.ss_nt = nt_h; gq.gain = ld.g1;
+      gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
       gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
       gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.nvalid = h->nvalid; gq.rope = h->rope;
       if ((e = norm_gemm(ld.self_attn ? PR_QKV : -1, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
@@ -325,25 +338,23 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
 
       GemmArgs gop = g;
       gop.N = kD; gop.K = kNQ; gop.A = h->o16; gop.lda = kNQ;
-      gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = h->h; gop.ss_out = h->ss;
+      gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = h->h; gop.h16 = h->h16;
       if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
 
       GemmArgs gg = g;
-      gg.N = kGU; gg.K = kD; gg.A = h->h; gg.lda = kD;
-      gg.ss_in = h->ss; gg.ss_nt = nt_h; gg.gain = ld.g2;
+      gg.N = kGU; gg.K = kD;
       gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = h->u16; gg.ldo = kFFN;
       if ((e = norm_gemm(PR_GU, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
 
       GemmArgs gd = g;
       gd.N = kD; gd.K = kFFN; gd.A = h->u16; gd.lda = kFFN;
-      gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = h->h; gd.ss_out = h->ss;
+      gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = h->h; gd.h16 = h->h16;
       if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
     }
 
     // final RMSNorm + action_out; Euler update x += dt v
     GemmArgs gv = g;
-    gv.N = kAD; gv.K = kD; gv.A = h->h; gv.lda = kD;
-    gv.ss_in = h->ss; gv.ss_nt = nt_h; gv.gain = h->gf;
+    gv.N = kAD; gv.K = kD;
     gv.W = h->w_out.w; gv.ldw = h->w_out.ld; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
     gv.x = h->x; gv.dt = h->dt;
     const size_t stepElems = (size_t)B * kChunk * kAD;
@@ -354,7 +365,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
       gv.st_out = c.st ? c.st + (size_t)k * stepElems : nullptr;
       gv.final_out = (k == n_t - 1) ? c.out : nullptr;
     }
-    if ((e = gemm(PR_ACTOUT, A_NORM, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
+    if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
   }
   return SMOLEXP_OK;
 }
@@ -481,10 +492,10 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   const int n_pos = cfg->max_prefix + kChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mpad * kD * 4), o_ss = take(Mmax * kSSStride * 4);
+  const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mpad * kD * 4);
   const size_t o_cv = take((size_t)kMaxSteps * kD * 4);
   const size_t o_y = take(Mpad * kD * 2), o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
-  const size_t o_u = take(Mpad * kFFN * 2), o_n = take(Mpad * kKPad * 2);
+  const size_t o_u = take(Mpad * kFFN * 2), o_h16 = take(Mpad * kKPad * 2);
   const size_t o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
   const size_t o_vc = take(Mmax * kNKV * 2), o_nv = take((size_t)cfg->max_batch * 4);
   const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
@@ -492,15 +503,17 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   hipError_t e = hipMalloc(&h->wsmem, off);
   if (e != hipSuccess) { delete h; return SMOLEXP_E_NOMEM; }
   char* base = static_cast<char*>(h->wsmem);
-  h->x = (float*)(base + o_x); h->h = (float*)(base + o_h); h->ss = (float*)(base + o_ss);
+  h->x = (float*)(base + o_x); h->h = (float*)(base + o_h);
   h->cvec = (float*)(base + o_cv); h->y16 = (half_t*)(base + o_y); h->s16 = (half_t*)(base + o_s);
-  h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->n16 = (half_t*)(base + o_n);
+  h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->h16 = (half_t*)(base + o_h16);
   h->q = (bf16_t*)(base + o_q);
   h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->nvalid = (int*)(base + o_nv);
   h->rope = (float2*)(base + o_rope);
   h->inv_period = (double*)(base + o_invp);
 
   e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
+  // the columns 720..767 of h16 are read by the K = 768 GEMM and never written: zero them once
+  if (e == hipSuccess) e = hipMemsetAsync(h->h16, 0, Mpad * kKPad * 2, h->cap);
   if (e == hipSuccess) e = launch_rope_table(h->rope, n_pos, cfg->rope_theta, h->cap);
   if (e == hipSuccess) e = launch_inv_period_table(h->inv_period, cfg->t_min_period, cfg->t_max_period, h->cap);
   if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
@@ -522,22 +535,21 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
 
   // Device layout: fp16 GEMM matrices in the blocked layout (gate/up interleaved in 16-row
   // blocks, Q/K rows permuted per head; Q/K/V and gate/up with K padded to 768 for the
-  // large-M GEMM), the time-embedding half of W_t1 row-major for the prologue, fp32 vectors.
+  // large-M GEMM; the RMSNorm gains folded into Q/K/V, gate/up and action_out), the
+  // time-embedding half of W_t1 row-major for the prologue, fp32 biases.
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t o_win = take((size_t)kD * kAD * 2), o_wt1 = take((size_t)kD * kD * 2), o_wt1e = take((size_t)kD * kD * 2);
   const size_t o_wt2 = take((size_t)kD * kD * 2);
   const size_t o_bin = take(kD * 4), o_bt1 = take(kD * 4), o_bt2 = take(kD * 4);
-  std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L), o_g1(L), o_g2(L);
+  std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L);
   for (int l = 0; l < L; ++l) {
     o_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * kKPad * 2);
     o_o[l] = take((size_t)kD * kNQ * 2);
     o_gu[l] = take((size_t)kGU * kKPad * 2);
     o_dn[l] = take((size_t)kD * kFFN * 2);
-    o_g1[l] = take(kD * 4);
-    o_g2[l] = take(kD * 4);
   }
-  const size_t o_gf = take(kD * 4), o_wout = take((size_t)kAD * kD * 2), o_bout = take(kAD * 4);
+  const size_t o_wout = take((size_t)kAD * kD * 2), o_bout = take(kAD * 4);
   std::vector<char> hostbuf;
   try {
     hostbuf.assign(off, 0);
@@ -588,8 +600,6 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     const uint16_t* pg = next((size_t)kFFN * kD);
     const uint16_t* pu = next((size_t)kFFN * kD);
     const uint16_t* pd = next((size_t)kD * kFFN);
-    vec32(g1, kD, o_g1[l]);
-    vec32(g2, kD, o_g2[l]);
     // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone).  Inside each
     // Q and K head, 16-row block q holds dims q*8..q*8+7 then 32+q*8..32+q*8+7, so the
     // rotation pairs (d, d + 32) share an MFMA tile.
@@ -602,9 +612,6 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
         for (int r = 0; r < kNKV; ++r) row_src[kNQ + r] = pk + (size_t)r * kD;
         for (int r = 0; r < kNKV; ++r) row_src[kNQ + kNKV + r] = pvv + (size_t)r * kD;
       }
-      std::vector<std::pair<const uint16_t*, size_t>> parts = {{pq, (size_t)kNQ * kD}};
-      if (self_attn) { parts.push_back({pk, (size_t)kNKV * kD}); parts.push_back({pvv, (size_t)kNKV * kD}); }
-      s = pick_shift(parts);
       std::vector<const uint16_t*> perm(nrows);
       for (int r = 0; r < nrows; ++r) {
         const int head = r / kHD, rr = r % kHD;
@@ -615,13 +622,12 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
         }
         perm[r] = row_src[src];
       }
-      pack_t16(perm, kD, kKPad, s, (half_t*)(hb + o_qkv[l]));
+      s = pack_t16_gain(perm, kD, kKPad, g1, (half_t*)(hb + o_qkv[l]));
     }
     ld.qkv.scale = ldexpf(1.f, -s); ld.qkv.ld = kKPad;
     s = pick_shift({{po, (size_t)kD * kNQ}});
     pack_t16(rows_of(po, kD, kNQ), kNQ, kNQ, s, (half_t*)(hb + o_o[l]));
     ld.o.scale = ldexpf(1.f, -s); ld.o.ld = kNQ;
-    s = pick_shift({{pg, (size_t)kFFN * kD}, {pu, (size_t)kFFN * kD}});
     {
       std::vector<const uint16_t*> gu(kGU);
       for (int j = 0; j < kFFN / 8; ++j)  // rows 16j..16j+7 = gate 8j.., 16j+8..16j+15 = up 8j..
@@ -629,7 +635,7 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
           gu[16 * j + e] = pg + (size_t)(8 * j + e) * kD;
           gu[16 * j + 8 + e] = pu + (size_t)(8 * j + e) * kD;
         }
-      pack_t16(gu, kD, kKPad, s, (half_t*)(hb + o_gu[l]));
+      s = pack_t16_gain(gu, kD, kKPad, g2, (half_t*)(hb + o_gu[l]));
     }
     ld.gu.scale = ldexpf(1.f, -s); ld.gu.ld = kKPad;
     s = pick_shift({{pd, (size_t)kD * kFFN}});
@@ -639,9 +645,7 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   const uint16_t* p_gf = next(kD);
   const uint16_t* p_wout = next((size_t)kAD * kD);
   const uint16_t* p_bout = next(kAD);
-  vec32(p_gf, kD, o_gf);
-  s = pick_shift({{p_wout, (size_t)kAD * kD}});
-  pack_t16(rows_of(p_wout, kAD, kD), kD, kD, s, (half_t*)(hb + o_wout));
+  s = pack_t16_gain(rows_of(p_wout, kAD, kD), kD, kD, p_gf, (half_t*)(hb + o_wout));
   w_out.scale = ldexpf(1.f, -s); w_out.ld = kD;
   vec32(p_bout, kAD, o_bout);
 
@@ -662,14 +666,12 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   h->w_in = w_in; h->w_t1 = w_t1; h->w_t2 = w_t2; h->w_out = w_out;
   h->w_t1e = (half_t*)(db + o_wt1e);
   h->b_in = (float*)(db + o_bin); h->b_t1 = (float*)(db + o_bt1); h->b_t2 = (float*)(db + o_bt2);
-  h->gf = (float*)(db + o_gf); h->b_out = (float*)(db + o_bout);
+  h->b_out = (float*)(db + o_bout);
   for (int l = 0; l < L; ++l) {
     layers[l].qkv.w = (half_t*)(db + o_qkv[l]);
     layers[l].o.w = (half_t*)(db + o_o[l]);
     layers[l].gu.w = (half_t*)(db + o_gu[l]);
     layers[l].down.w = (half_t*)(db + o_dn[l]);
-    layers[l].g1 = (float*)(db + o_g1[l]);
-    layers[l].g2 = (float*)(db + o_g2[l]);
   }
   h->layers = layers;
   h->loaded = true;
@@ -747,7 +749,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     } else if (kernel == PR_ATTN_SELF || kernel == PR_ATTN_CROSS) {
       e = launch_attention(kernel == PR_ATTN_SELF, h->probe_a[kernel], s);
     } else if (h->probe_plan[kernel].kind == 2) {
-      e = launch_gemm_big(h->probe_em[kernel], h->probe_g[kernel], s);
+      e = launch_gemm_big(h->probe_em[kernel], h->probe_am[kernel] == A_NORM, h->probe_g[kernel], s);
     } else {
       e = launch_gemm(h->probe_plan[kernel], h->probe_am[kernel], h->probe_em[kernel], h->probe_g[kernel], s);
     }

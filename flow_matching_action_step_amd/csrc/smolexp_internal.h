@@ -19,7 +19,6 @@ constexpr int kNQ = kHQ * kHD;         // 960
 constexpr int kNKV = kHKV * kHD;       // 320
 constexpr int kNQKV = kNQ + 2 * kNKV;  // 1600
 constexpr int kGU = 2 * kFFN;          // 4096 (gate and up, interleaved in 16-row blocks)
-constexpr int kSSStride = 64;  // partial sums of squares per row (one per producer N-tile)
 constexpr int kMaxSteps = 64;
 constexpr int kMaxLayers = 64;
 
@@ -45,8 +44,9 @@ __host__ __device__ inline size_t t32_off(int r, int k, int k4) {
 // A-operand sources of the GEMM.
 enum AMode : int {
   A_F16 = 0,    // fp16, blocked (t16_off), lda = stored K (multiple of 8)
-  A_NORM = 1,   // fp32 residual, blocked (t32_off), lda = 720; RMSNorm applied on load (row scale
-                // from partial sums, gain)
+  A_NORM = 1,   // fp16(h), blocked, lda = 768: RMSNorm'd with the gain folded into W and the row
+                // scale 1/rms applied to the sums; each kernel sums the squares of the rows it
+                // streams (fp16 values)
   A_X = 2,      // fp32 Euler state, row-major [M][32]; prefix overwrite applied on load
 };
 
@@ -54,8 +54,8 @@ enum AMode : int {
 enum EMode : int {
   E_F16_BIAS = 0,  // out16 = acc + bias                      (action_in)
   E_TIMEIN = 1,    // out16 = SiLU(acc + cvec)                (time MLP, first layer)
-  E_H_BIAS = 2,    // h = acc + bias; row sums of squares     (time MLP, second layer)
-  E_H_RESID = 3,   // h += acc; row sums of squares           (o and down projections)
+  E_H_BIAS = 2,    // h = acc + bias; h16 = fp16(h)           (time MLP, second layer)
+  E_H_RESID = 3,   // h += acc; h16 = fp16(h)                 (o and down projections)
   E_QKV = 4,       // RoPE on Q and K, scatter to Q/Kc/Vc bf16 (attention input)
   E_SWIGLU = 5,    // out16 = SiLU(gate) * up                 (FFN)
   E_ACTOUT = 6,    // v = acc + bias; x += dt * v             (action_out + Euler)
@@ -66,9 +66,6 @@ struct GemmArgs {
   const void* A;
   int lda;
   // A_NORM
-  const float* ss_in;
-  int ss_nt;
-  const float* gain;
   float inv_k;
   float eps;
   // A_X
@@ -86,7 +83,7 @@ struct GemmArgs {
   half_t* out16;       // fp16 activations, blocked (t16_off), ldo = stored K
   int ldo;
   float* h;            // fp32 residual stream, blocked (t32_off), K = 720
-  float* ss_out;
+  half_t* h16;         // its fp16 copy, blocked (t16_off), 768 stored columns (720.. stay zero)
   bf16_t* q;
   bf16_t* kc;
   bf16_t* vc;
@@ -131,17 +128,16 @@ struct GemmPlan {
                  // 2: large-tile GEMM on a pre-normalised operand (recorded for timing only)
   int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
   int bm;        // tiled: rows per tile (64 or 128)
-  int ntiles_n;  // output tiles along N (= sum-of-squares slots written by an N = 720 producer)
+  int ntiles_n;  // output tiles (workgroups) along N
 };
 GemmPlan plan_gemm(int M, int N, int K);
 
-// Large-M GEMM (fp16 A, K % 64 == 0; epilogues E_QKV, E_SWIGLU, E_H_RESID) and the
-// RMSNorm -> fp16 pre-pass that feeds it (a.A = h, a.out16/a.ldo = destination).
-hipError_t launch_gemm_big(EMode em, const GemmArgs& a, hipStream_t s);
-hipError_t launch_rmsnorm_f16(const GemmArgs& a, hipStream_t s);
+// Large-M GEMM (fp16 A, K % 64 == 0): E_QKV and E_SWIGLU on the RMSNorm'd residual
+// (norm = true: A = h16), E_H_RESID on a plain fp16 operand.
+hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s);
 int big_tiles(int M, int N);
-bool use_big_gemm(int M, int N);  // RMSNorm pre-pass + large-tile GEMM for this Q/K/V or gate/up shape
-constexpr int kKPad = 768;  // K = 720 operands of the large-M GEMM, zero-padded to a multiple of 64
+bool use_big_gemm(int M, int N);  // large-tile GEMM for this Q/K/V or gate/up shape
+constexpr int kKPad = 768;  // stored columns of h16 and of the weights that read it (a multiple of 64)
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
