@@ -102,11 +102,16 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
   }
 }
 
-// Sum of squares of the 8 fp16 values of one MFMA A fragment.
+// Sum of squares of the 8 fp16 values of one MFMA A fragment (v_dot2_f32_f16:
+// fp16 products are exact in fp32, accumulated in fp32).
 __device__ __forceinline__ float sumsq8(const f16x8& u) {
+  typedef half_t h2 __attribute__((ext_vector_type(2)));
   float q = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) q += (float)u[e] * (float)u[e];
+  for (int e = 0; e < 8; e += 2) {
+    const h2 p = {u[e], u[e + 1]};
+    q = __builtin_amdgcn_fdot2(p, p, q, false);
+  }
   return q;
 }
 
@@ -683,15 +688,27 @@ bool use_big_gemm(int M, int N) { return M > 64 && big_tiles(M, N) >= 160; }
 // prefix tokens 0..P-1 (valid where the mask says so) followed, in self layers,
 // by the 50 chunk keys, of which row i sees j <= i.  Scores are computed
 // transposed (S^T = K Q^T) so that each lane owns one query row; the output is
-// accumulated transposed as well (O^T += V^T P^T).
+// accumulated transposed as well (O^T += V^T P^T).  K and V are staged in LDS
+// row-major ([key][dim]); the V^T operand comes from transposing LDS reads.
 constexpr int kKB = 64;        // keys per block
-constexpr int kALD = kHD + 8;  // LDS row stride of K (elements)
+constexpr int kALD = kHD + 8;  // LDS row stride of K and V (elements)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte chunks addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and
+// i / 4 + 12 of its group (checked on the device).  When lane s of a group
+// addresses V[key0 + s / 4][d0 + 4 * (s % 4)], lane i therefore gets
+// V[key0 .. key0 + 3][d0 + i]: four consecutive keys of one dimension.
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
 
 // One 64-key block of the online softmax for the lane's query row (row qi of
-// the chunk).  sKb: the block's K rows [64][kALD]; sVb: its V^T columns
-// (row stride vld); kind: its key kinds; key0 = index of its first key minus P
-// (chunk key j is visible to row qi when j - P <= qi).
-__device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, int vld, const uint8_t* kind,
+// the chunk).  sKb, sVb: the block's K and V rows [64][kALD]; kind: its key
+// kinds; key0 = index of its first key minus P (chunk key j is visible to row
+// qi when j - P <= qi).
+__device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
                                            int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
                                            float& l_run, int lane) {
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
@@ -756,23 +773,23 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const bf16_t* vp = sVb + (m * 16 + (lane & 15)) * vld + h2 * 32 + (lane >> 4) * 4;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-      const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      // V^T fragment: dims m*16 + (lane % 16), keys h2*32 + 4q .. +3 and +16 .. +19 (q = lane / 16)
+      const int sl = lane & 15;
+      const bf16_t* vp = sVb + (h2 * 32 + 4 * (lane >> 4) + (sl >> 2)) * kALD + m * 16 + 4 * (sl & 3);
+      const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 16 * kALD);
+      const s16x4 u[2] = {lo, hi};
       o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
     }
   }
 }
 
 // Stage keys r0 .. r0 + RK - 1 of one (query, KV head) into LDS: K rows,
-// V transposed, key kinds.  Branch-free: every address is clamped into its
+// V rows, key kinds.  Branch-free: every address is clamped into its
 // buffer and the loaded vector is zeroed afterwards for masked or missing
 // keys, so all loads are in flight together.
 template <bool SELF, int RK>
-__device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int r0, bf16_t* sK, bf16_t* sVt,
+__device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int r0, bf16_t* sK, bf16_t* sV,
                                            uint8_t* sKind, int nthreads) {
-  constexpr int VLD = RK + 8;
   constexpr int NV = RK * 8 / 256;  // 16-byte vectors per thread (256 threads)
   const int tid = threadIdx.x, P = a.P;
   const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
@@ -786,35 +803,24 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int 
     sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
   }
   uint4 kv[NV], vv[NV];
-  bool kok[NV], vok[NV];
+  bool kok[NV];
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
     const int v = tid + 256 * it;
-    {  // K rows: 8 lanes per key
-      const int j = r0 + (v >> 3), c = (v & 7) * 8;
-      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-      const bf16_t* src = pre ? pk + (size_t)j * kHD + c : (chunk ? ck + (size_t)(j - P) * kHD + c : pk + c);
-      kv[it] = *reinterpret_cast<const uint4*>(src);
-      kok[it] = pre ? mk[j] != 0 : chunk;
-    }
-    {  // V rows for the transposed store: consecutive lanes take consecutive keys
-      const int j = r0 + (v % RK), c = (v / RK) * 8;
-      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-      const bf16_t* src = pre ? pv + (size_t)j * kHD + c : (chunk ? cv + (size_t)(j - P) * kHD + c : pv + c);
-      vv[it] = *reinterpret_cast<const uint4*>(src);
-      vok[it] = pre ? mk[j] != 0 : chunk;
-    }
+    // K and V rows: 8 lanes per key (whole 128-byte rows)
+    const int j = r0 + (v >> 3), c = (v & 7) * 8;
+    const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+    const size_t po = pre ? (size_t)j * kHD + c : c, co = (size_t)(j - P) * kHD + c;
+    kv[it] = *reinterpret_cast<const uint4*>(chunk ? ck + co : pk + po);
+    vv[it] = *reinterpret_cast<const uint4*>(chunk ? cv + co : pv + po);
+    kok[it] = pre ? mk[j] != 0 : chunk;
   }
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
-    if (!kok[it]) kv[it] = make_uint4(0, 0, 0, 0);
-    if (!vok[it]) vv[it] = make_uint4(0, 0, 0, 0);
+    if (!kok[it]) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
     const int v = tid + 256 * it;
     *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
-    const int jl = v % RK, c = (v / RK) * 8;
-    const bf16_t* e = reinterpret_cast<const bf16_t*>(&vv[it]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) sVt[(c + t) * VLD + jl] = e[t];
+    *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
   }
 }
 
@@ -825,9 +831,8 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int 
 template <bool SELF, int NBLK>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   constexpr int RK = NBLK * kKB;     // keys per round
-  constexpr int VLD = RK + 8;        // LDS row stride of V^T (elements)
   __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * VLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[RK * kALD];
   __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];  // 0 = no key, 1 = valid prefix key, 2 = chunk key
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -856,12 +861,12 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
     __syncthreads();  // the previous round's LDS reads are done
-    attn_stage<SELF, RK>(a, b, g, r0, sK, sVt, sKind, 256);
+    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind, 256);
     __syncthreads();
 
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
     for (int blk = 0; blk < nb; ++blk)
-      attn_block(sK + blk * kKB * kALD, sVt + blk * kKB, VLD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
+      attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
                  m_run, l_run, lane);
   }
 
@@ -884,9 +889,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 // through LDS.  Five times as many workgroups as attn_kernel at batch 1.
 template <bool SELF>
 __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
-  constexpr int NBLK = 5, RK = NBLK * kKB, VLD = RK + 8, OLD = kHD + 4;
+  constexpr int NBLK = 5, RK = NBLK * kKB, OLD = kHD + 4;
   __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[kHD * VLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[RK * kALD];
   __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];
   __shared__ float sM[4][16], sL[4][16];
   float* sO = reinterpret_cast<float*>(sK);  // [4 waves][16 rows][OLD], used after the last round
@@ -917,11 +922,11 @@ __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
     __syncthreads();
-    attn_stage<SELF, RK>(a, b, g, r0, sK, sVt, sKind, 256);
+    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind, 256);
     __syncthreads();
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
     for (int blk = wave; blk < nb; blk += 4)
-      attn_block(sK + blk * kKB * kALD, sVt + blk * kKB, VLD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
+      attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
                  m_run, l_run, lane);
   }
 
