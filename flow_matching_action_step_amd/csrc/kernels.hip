@@ -123,8 +123,12 @@ __device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { ret
 // The blocked outputs (fp16 activations, the fp32 residual and its fp16 copy)
 // are written with 16 consecutive lanes on 16 consecutive rows of one column
 // chunk, i.e. contiguous runs of 256 (128) bytes per store.
-template <int EM, int BM, int BN, int LDC, int NT>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0) {
+// PRE (one work unit per thread, as in the M <= 64 kernel): the unit's global
+// inputs were loaded at kernel start into pre[] (E_QKV: the 16 cos/sin values
+// of a rotated block; E_H_RESID: the 4 residual values).
+template <int EM, int BM, int BN, int LDC, int NT, bool PRE = false>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0,
+                                              const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0 && (BM * UPR) % NT == 0, "rows inside one wave, uniform trip count");
   const int M = a.M, N = a.N;
@@ -140,15 +144,21 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
       const float v1[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       const float v2[8] = {c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
       const int head = cb / kHD, b = row / kChunk, ci = row % kChunk;
+      (void)pre;
       bf16_t* dst;
       if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
       else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
       else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
       union { bf16_t e[8]; uint4 u; } lo, hi;
-      if (head < kHQ + kHKV) {  // rotate the pairs (d, d + 32), d = d0..d0+7, at position n_valid + i
+      if (head < kHQ + kHKV) {  // rotate the pairs (d, d + 32), d = d0..d0+7, at this row's position
         const int d0 = ((cb % kHD) / 16) * 8;
-        const float4* cs4 = reinterpret_cast<const float4*>(a.rope + (size_t)(a.nvalid[b] + ci) * (kHD / 2) + d0);
-        const float4 q0 = cs4[0], q1 = cs4[1], q2 = cs4[2], q3 = cs4[3];
+        float4 q0, q1, q2, q3;
+        if constexpr (PRE) {
+          q0 = pre[0]; q1 = pre[1]; q2 = pre[2]; q3 = pre[3];
+        } else {
+          const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)row * (kHD / 2) + d0);
+          q0 = cs4[0]; q1 = cs4[1]; q2 = cs4[2]; q3 = cs4[3];
+        }
         const float cs[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                               q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
 #pragma unroll
@@ -225,7 +235,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
             const float4 b = *reinterpret_cast<const float4*>(a.bias + col);
             o = make_float4(v.x + b.x, v.y + b.y, v.z + b.z, v.w + b.w);
           } else {
-            const float4 hv = *hp;
+            const float4 hv = PRE ? pre[0] : *hp;
             o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
           }
           *hp = o;
@@ -274,6 +284,22 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   const int nks = (K + 31) / 32;
   const int n = n0 + (lane & 15), kl = (lane >> 4) * 8;
 
+  // epilogue inputs, loaded with the operands (see epilogue_tile's unit mapping: E_QKV thread
+  // t < 64 owns row t; E_H_RESID lane r + 16 p of wave w < 4 owns row 16 w + r, columns n0 + 4 p..)
+  constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
+  float4 pre[4];
+  if constexpr (EM == E_QKV) {
+    const int d0 = ((n0 % kHD) / 16) * 8;
+    const bool rot = n0 / kHD < kHQ + kHKV;
+    if (tid < M && rot) {
+      const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)tid * (kHD / 2) + d0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pre[j] = cs4[j];
+    }
+  } else if constexpr (EM == E_H_RESID) {
+    const int row = w * 16 + (lane & 15), col = n0 + (lane >> 4) * 4;
+    if (w < 4 && row < M && col < N) pre[0] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+  }
   uint4 wf[KPW];
   uint4 af[KPW][4];
 #pragma unroll
@@ -331,7 +357,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     sC[(i / 16) * LDC + (i % 16)] = s * sc;
   }
   __syncthreads();
-  epilogue_tile<EM, 64, 16, LDC, 512>(a, sC, 0, n0);
+  epilogue_tile<EM, 64, 16, LDC, 512, PRE>(a, sC, 0, n0, pre);
 }
 
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
@@ -887,9 +913,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 // the key blocks among themselves (wave w takes blocks w, w + 4, ...), then
 // merge their softmax states (running max, running sum, unnormalised output)
 // through LDS.  Five times as many workgroups as attn_kernel at batch 1.
-template <bool SELF>
+template <bool SELF, int NBLK>
 __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
-  constexpr int NBLK = 5, RK = NBLK * kKB, OLD = kHD + 4;
+  constexpr int RK = NBLK * kKB, OLD = kHD + 4;
   __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[RK * kALD];
   __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];
@@ -967,12 +993,25 @@ __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
   }
 }
 
+template <bool SELF>
+static void launch_ksplit(const AttnArgs& a, hipStream_t s) {
+  // key blocks staged per round: the whole key range when it fits in five blocks
+  const int nk = a.P + (SELF ? kChunk : 0);
+  const int nblk = min(5, max(2, (nk + kKB - 1) / kKB));
+  const dim3 grid((3 * kChunk + 15) / 16, kHKV, a.B), block(256);
+  switch (nblk) {
+    case 2: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 3>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 5>), grid, block, 0, s, a); break;
+  }
+}
+
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
   const dim3 block(256);
   if (a.B <= 8) {
-    const dim3 grid((3 * kChunk + 15) / 16, kHKV, a.B);
-    if (self_layer) hipLaunchKernelGGL(attn_ksplit_kernel<true>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(attn_ksplit_kernel<false>, grid, block, 0, s, a);
+    if (self_layer) launch_ksplit<true>(a, s);
+    else launch_ksplit<false>(a, s);
   } else {
     const dim3 grid(3, kHKV, a.B);
     if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 1>), grid, block, 0, s, a);
@@ -983,7 +1022,8 @@ hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
 
 // ----------------------------------------------------------------------------
 // Per-call prologue: the time vectors W_t1[:, 720:] e(t_k) + b_t1 for every
-// step, the number of valid prefix tokens per query, and x <- the caller's x.
+// step, the RoPE rows of every chunk row (position = the query's number of
+// valid prefix tokens + i), and x <- the caller's x.
 // ----------------------------------------------------------------------------
 constexpr int kTimeRowsPerBlock = 16;
 constexpr int kTimeBlocks = kD / kTimeRowsPerBlock;  // 45
@@ -1035,13 +1075,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
       if (part == 0) a.cvec[(size_t)k * kD + j] = s * a.s_t1 + a.b_t1[j];
     }
   } else if ((int)blockIdx.x < kTimeBlocks + nMaskBlocks) {
+    // query b: its valid prefix count n, then the RoPE rows of chunk positions n .. n + 49
     const int b = (blockIdx.x - kTimeBlocks) * 4 + (tid >> 6), lane = tid & 63;
     if (b < a.B) {
       int c = 0;
       for (int j = lane; j < a.P; j += 64) c += a.mask[(size_t)b * a.P + j] != 0;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-      if (lane == 0) a.nvalid[b] = c;
+      for (int i = lane; i < kChunk * (kHD / 2); i += 64)
+        a.ropeq[((size_t)b * kChunk) * (kHD / 2) + i] = a.rope[(size_t)c * (kHD / 2) + i];
     }
   } else {
     const int first = kTimeBlocks + nMaskBlocks;

@@ -77,8 +77,8 @@ struct smolexp_handle {
   float *x = nullptr, *h = nullptr, *cvec = nullptr;
   half_t *y16 = nullptr, *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *h16 = nullptr;
   bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
-  int* nvalid = nullptr;
-  float2* rope = nullptr;
+  float2* rope = nullptr;   // [max_prefix + 50][32] (cos, sin) by position
+  float2* ropeq = nullptr;  // [B*50][32] per call: the rope rows of each chunk row's position
   double* inv_period = nullptr;
 
   hipStream_t cap = nullptr;
@@ -250,7 +250,8 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   for (int k = 0; k < n_t; ++k) pa.t[k] = c.velocity ? c.t_single : h->ts[k];
   pa.mask = c.mask;
   pa.P = P;
-  pa.nvalid = h->nvalid;
+  pa.rope = h->rope;
+  pa.ropeq = h->ropeq;
   pa.x_in = c.x_in;
   pa.x = h->x;
   pa.w_t1e = h->w_t1e;
@@ -324,7 +325,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
       GemmArgs gq = g;
       gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
       gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
-      gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.nvalid = h->nvalid; gq.rope = h->rope;
+      gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.ropeq = h->ropeq;
       if ((e = norm_gemm(ld.self_attn ? PR_QKV : -1, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
 
       AttnArgs aa;
@@ -497,7 +498,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   const size_t o_y = take(Mpad * kD * 2), o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
   const size_t o_u = take(Mpad * kFFN * 2), o_h16 = take(Mpad * kKPad * 2);
   const size_t o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
-  const size_t o_vc = take(Mmax * kNKV * 2), o_nv = take((size_t)cfg->max_batch * 4);
+  const size_t o_vc = take(Mmax * kNKV * 2), o_rq = take(Mmax * (kHD / 2) * sizeof(float2));
   const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
   const size_t o_invp = take((size_t)(kD / 2) * sizeof(double));
   hipError_t e = hipMalloc(&h->wsmem, off);
@@ -507,7 +508,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   h->cvec = (float*)(base + o_cv); h->y16 = (half_t*)(base + o_y); h->s16 = (half_t*)(base + o_s);
   h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->h16 = (half_t*)(base + o_h16);
   h->q = (bf16_t*)(base + o_q);
-  h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->nvalid = (int*)(base + o_nv);
+  h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->ropeq = (float2*)(base + o_rq);
   h->rope = (float2*)(base + o_rope);
   h->inv_period = (double*)(base + o_invp);
 

@@ -87,8 +87,7 @@ struct GemmArgs {
   bf16_t* q;
   bf16_t* kc;
   bf16_t* vc;
-  const int* nvalid;
-  const float2* rope;  // [pos][32] (cos, sin)
+  const float2* ropeq;  // [row][32] (cos, sin) of each chunk row's position (valid prefix count + i)
   float dt;
   float* vel_out;
   float* st_out;
@@ -112,7 +111,8 @@ struct PrologueArgs {
   float t[kMaxSteps];
   const uint8_t* mask;     // [B][P]
   int P;
-  int* nvalid;             // out [B]
+  const float2* rope;      // [pos][32] (cos, sin) by position
+  float2* ropeq;           // out [B*50][32]: the rows of rope at positions n_valid(b) + i
   const float* x_in;       // [B][50][32]
   float* x;                // out: Euler state
   const half_t* w_t1e;     // time_in weight, its time-embedding half [720][720] row-major (fp16, scaled)
