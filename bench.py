@@ -96,24 +96,26 @@ def summarize_pmc(fetch_csv, write_csv, workload, kernel):
 def kernel_costs(L, B, lengths, P):
     """Algorithmic (bytes, flops) of ONE launch of each timed kernel, and launches per call per step.
 
-    Bytes count each operand once: fp16 weights as stored (2 B/element), the
-    activation the kernel reads, the activation it writes (read-modify-write
-    of the fp32 residual counts twice), valid prefix K/V tokens only.  Flops
-    are 2 per multiply-add; attention counts unmasked keys only.
+    Bytes count each operand once: fp16 weights (2 B/element, without the K
+    padding), the activation the kernel reads (the normed projections read the
+    fp16 copy of the residual), the activations it writes (o and down
+    read-modify-write the fp32 residual and write its fp16 copy), valid prefix
+    K/V tokens only.  Flops are 2 per multiply-add; attention counts unmasked
+    keys only.
     """
     M = 50 * B
     sum_nb = float(sum(lengths))
     c = {}
-    c["qkv_self"] = (1600 * 720 * 2 + M * 720 * 4 + M * 1600 * 2, 2.0 * M * 1600 * 720)
+    c["qkv_self"] = (1600 * 720 * 2 + M * 720 * 2 + M * 1600 * 2, 2.0 * M * 1600 * 720)
     kv_self = 5 * 64 * 2 * 2 * (sum_nb + 50 * B)
     keys_self = 50 * sum_nb + 1275 * B
     c["attn_self"] = (M * 960 * 2 + kv_self + M * 960 * 2, 4.0 * 64 * 15 * keys_self)
     kv_cross = 5 * 64 * 2 * 2 * sum_nb
     c["attn_cross"] = (M * 960 * 2 + kv_cross + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
-    c["o"] = (720 * 960 * 2 + M * 960 * 2 + M * 720 * 8, 2.0 * M * 720 * 960)
-    c["gate_up"] = (4096 * 720 * 2 + M * 720 * 4 + M * 2048 * 2, 2.0 * M * 4096 * 720)
-    c["down"] = (720 * 2048 * 2 + M * 2048 * 2 + M * 720 * 8, 2.0 * M * 720 * 2048)
-    c["action_out"] = (32 * 720 * 2 + M * 720 * 4 + M * 32 * 8, 2.0 * M * 32 * 720)
+    c["o"] = (720 * 960 * 2 + M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
+    c["gate_up"] = (4096 * 720 * 2 + M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
+    c["down"] = (720 * 2048 * 2 + M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
+    c["action_out"] = (32 * 720 * 2 + M * 720 * 2 + M * 32 * 8, 2.0 * M * 32 * 720)
     per_step = {"qkv_self": L // 2 + L % 2, "attn_self": L // 2 + L % 2, "attn_cross": L // 2, "o": L,
                 "gate_up": L, "down": L, "action_out": 1}
     return c, per_step
@@ -261,8 +263,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "precision": "GEMM operands fp16 (bf16 weights re-encoded exactly), attention bf16, fp32 accumulate, "
-                     "fp32 residual/norm/softmax/Euler",
+        "precision": "GEMM operands fp16 (bf16 weights re-encoded exactly; RMSNorm gains folded into the "
+                     "following weights, rounded once), attention bf16, fp32 accumulate, fp32 residual/norm "
+                     "scale/softmax/Euler",
         "data": "synthetic (seeded: weights N(0,0.02) bf16, prefix K/V N(0,1) bf16, noise N(0,1))",
         "config": {"workload": args.workload, "n_layers": L, "batch": B, "prefix_len": P,
                    "n_steps": cfg.n_steps, "chunk": 50, "action_dim": 32, "overwrite_rows": d,
