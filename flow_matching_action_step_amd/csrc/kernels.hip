@@ -102,21 +102,22 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
   }
 }
 
-// Sum of squares of the 8 fp16 values of one MFMA A fragment (v_dot2_f32_f16:
-// fp16 products are exact in fp32, accumulated in fp32).
-__device__ __forceinline__ float sumsq8(const f16x8& u) {
-  typedef half_t h2 __attribute__((ext_vector_type(2)));
-  float q = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const h2 p = {u[e], u[e + 1]};
-    q = __builtin_amdgcn_fdot2(p, p, q, false);
-  }
-  return q;
+// Row sums of squares on the matrix cores: with one A fragment (16 rows x 32 k)
+// as both operands the MFMA accumulates A A^T, whose diagonal holds the sum of
+// squares of each row (fp16 products are exact in fp32).  One MFMA per 16 rows
+// per k-step, far cheaper than VALU dot products interleaved with the GEMM.
+__device__ __forceinline__ f32x4 sumsq_mfma(const f16x8& af, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(af, af, acc, 0, 0, 0);
+}
+// Row m (0..15) of a 16-row tile has its diagonal element in lane 16 (m / 4) + m,
+// register m % 4; every lane reads the one for row 4 (lane / 16) + r (the rows
+// whose accumulators it holds in register r).
+__device__ __forceinline__ float diag_for_row(const f32x4& sq, int r, int lane) {
+  return __shfl(sq[r], 20 * (lane >> 4) + r);
 }
 
 // 1/rms of a row from its sum of squares.
-__device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { return 1.0f / sqrtf(sumsq * a.inv_k + a.eps); }
+__device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { return rsqrtf(sumsq * a.inv_k + a.eps); }
 
 // Epilogue on a finished tile sC[BM][LDC] (fp32, weight and row scales
 // applied) whose rows start at m0 and columns at n0 (BN a multiple of 16).
@@ -326,15 +327,13 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     }
   }
   if constexpr (AM == A_NORM) {
-    // this wave's share of each row's sum of squares (lanes l, l+16, l+32, l+48 hold row l % 16)
+    // this wave's share of each row's sum of squares, from the diagonal of A A^T over its K slice
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
-      float q = 0.f;
+      f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < KPW; ++i) q += sumsq8(__builtin_bit_cast(f16x8, af[i][fm]));
-      q += __shfl_xor(q, 16);
-      q += __shfl_xor(q, 32);
-      if (lane < 16) sQ[w][fm * 16 + lane] = q;
+      for (int i = 0; i < KPW; ++i) sq = sumsq_mfma(__builtin_bit_cast(f16x8, af[i][fm]), sq);
+      if (((lane & 15) >> 2) == (lane >> 4)) sQ[w][fm * 16 + (lane & 15)] = sq[lane & 3];
     }
   }
 #pragma unroll
@@ -422,10 +421,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   };
 
   f32x4 acc[FM][4];
-  float q[FM];  // A_NORM: this lane's share of the sum of squares of row (lane % 16) of each fm tile
+  f32x4 sq[AM == A_NORM ? FM : 1];  // A_NORM: A A^T of each fm tile (row sums of squares on the diagonal)
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    q[fm] = 0.f;
+    if constexpr (AM == A_NORM) sq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -454,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
       if constexpr (AM == A_NORM) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) q[fm] += sumsq8(af[fm]);
+        for (int fm = 0; fm < FM; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
       }
     }
     if (kt + 1 < nk) store((kt + 1) & 1);
@@ -462,20 +461,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   }
 
   const float ws = a.w_scale;
-  if constexpr (AM == A_NORM) {  // whole-row sums: the four lane groups hold the four k-chunks
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      q[fm] += __shfl_xor(q[fm], 16);
-      q[fm] += __shfl_xor(q[fm], 32);
-    }
-  }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = wm * FM * 16 + fm * 16 + (lane >> 4) * 4 + r;
-      // row rl's sum of squares sits in the lanes whose lane % 16 is rl % 16
-      const float sc = AM == A_NORM ? ws * rms_scale(a, __shfl(q[fm], (lane >> 4) * 4 + r)) : ws;
+      float sc = ws;
+      if constexpr (AM == A_NORM) sc *= rms_scale(a, diag_for_row(sq[fm], r, lane));
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) sC[rl * LDC + wn * 64 + fn * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
@@ -564,18 +556,20 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 // (whose fence would wait for every load in flight).
 constexpr int kBigBM = 256, kBigBN = 128, kBigBK = 64, kBigStages = 3;
 
-template <int EM, bool NORM>
-__global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
+// WN = waves along N: four waves of 64 x 128 (WN = 1) or eight of 64 x 64 (WN = 2).
+template <int EM, bool NORM, int WN>
+__global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
   constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, S = kBigStages, LDC = BN + 4;
+  constexpr int NW = 4 * WN, FN = BN / 16 / WN;
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
   constexpr int SMEM = S * STAGE_BYTES > BM * LDC * 4 ? S * STAGE_BYTES : BM * LDC * 4;
-  constexpr int A_LOADS = A_BYTES / 1024 / 4, W_LOADS = W_BYTES / 1024 / 4;  // per wave per stage
-  constexpr int LOADS = A_LOADS + W_LOADS;                                      // 12
+  constexpr int A_LOADS = A_BYTES / 1024 / NW, W_LOADS = W_BYTES / 1024 / NW;  // per wave per stage
+  constexpr int LOADS = A_LOADS + W_LOADS;
   static_assert(LOADS * (S - 2) < 64, "vmcnt immediate range");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   float* sC = reinterpret_cast<float*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
   const int M = a.M, N = a.N, K = a.K;
   const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN, T = nM * nN;
   const int per = (T + 7) / 8;
@@ -584,8 +578,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
   const int mt = tile / nN, nt = tile % nN;
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk = K / BK;
-  // NORM: A is fp16(h) unnormalised; each wave sums the squares of its 64 rows as their
-  // fragments go by, and 1/rms of each row scales the finished sums.
+  // NORM: A is fp16(h) unnormalised; each wave accumulates A A^T of its 64 rows on the
+  // matrix cores (row sums of squares on the diagonal), and 1/rms of each row scales the
+  // finished sums.
 
   // Load instruction `blk` of a tile: row block blk / 2, chunks (blk % 2) * 4 .. +3 of the slab;
   // lane l moves row l % 16 of chunk l / 16 of those.  Row blocks past the last one holding
@@ -615,85 +610,103 @@ __global__ __launch_bounds__(256, 1) void gemm_big(const GemmArgs a) {
     }
   };
 
-  f32x4 acc[4][8];
-  float q[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4][FN];
+  f32x4 sq[4];  // NORM: A A^T of each fm tile (row sums of squares on the diagonal)
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 8; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = sq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(st, st);
-  constexpr int WAIT = (LOADS * (S - 2)) & 15, WAIT_HI = (LOADS * (S - 2)) >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of slab kt are done once at most LOADS*(S-2) newer ones remain
-    __builtin_amdgcn_s_waitcnt(WAIT | (WAIT_HI << 14) | (7 << 4) | (15 << 8));
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; slab kt-1 is no longer read
-    issue(kt + S - 1, (kt + S - 1) % S);
+  // Fragments of one 32-wide k-step, read from LDS into one of two register sets: the reads
+  // of the next k-step are issued before the MFMAs of the current one (sched_barrier keeps
+  // that order), so LDS latency hides behind 4 x FN MFMAs.
+  auto read_frags = [&](int kt, int s, f16x8* af, f16x8* bw) {
     const char* base = smem + (kt % S) * STAGE_BYTES;
     const half_t* sA = reinterpret_cast<const half_t*>(base);
     const half_t* sW = reinterpret_cast<const half_t*>(base + A_BYTES);
+    const int ch = s * 4 + (lane >> 4);  // 16-byte chunk of this lane's fragment within the slab
 #pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      const int ch = s * 4 + (lane >> 4);  // 16-byte chunk of this lane's fragment within the slab
-      f16x8 af[4], bw[8];
+    for (int fm = 0; fm < 4; ++fm)
+      af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * 4 + fm) * 8 + ch) * 128 + (lane & 15) * 8);
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-        af[fm] = *reinterpret_cast<const f16x8*>(sA + ((w * 4 + fm) * 8 + ch) * 128 + (lane & 15) * 8);
+    for (int fn = 0; fn < FN; ++fn)
+      bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * FN + fn) * 8 + ch) * 128 + (lane & 15) * 8);
+  };
+  auto mma = [&](const f16x8* af, const f16x8* bw) {
 #pragma unroll
-      for (int fn = 0; fn < 8; ++fn)
-        bw[fn] = *reinterpret_cast<const f16x8*>(sW + (fn * 8 + ch) * 128 + (lane & 15) * 8);
+    for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    if constexpr (NORM) {
 #pragma unroll
-        for (int fn = 0; fn < 8; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
-      if constexpr (NORM) {
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm) q[fm] += sumsq8(af[fm]);
-      }
+      for (int fm = 0; fm < 4; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
     }
+  };
+  static_assert(BK == 64, "two k-steps per slab");
+  // Slabs kt .. kt+2 are in flight while slab kt is multiplied; slab kt + 3 is issued into
+  // slab kt's stage once every wave has finished reading it.  Past the end, issue() reloads
+  // the last slab into a stage nobody reads any more, which keeps the counts uniform.
+  constexpr int WAIT1 = LOADS * (S - 2), WAIT2 = LOADS * (S - 1);
+  static_assert(WAIT2 < 64, "vmcnt immediate range");
+  constexpr int VM1 = (WAIT1 & 15) | ((WAIT1 >> 4) << 14), VM2 = (WAIT2 & 15) | ((WAIT2 >> 4) << 14);
+#pragma unroll
+  for (int st = 0; st < S; ++st) issue(st, st);
+  __builtin_amdgcn_s_waitcnt(VM2 | (7 << 4) | (15 << 8));  // this wave's slab 0 landed
+  __builtin_amdgcn_s_barrier();                            // ... every wave's
+  f16x8 a0[4], b0[FN], a1[4], b1[FN];
+  read_frags(0, 0, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read_frags(kt, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      // this wave's reads of slab kt are done and its slab kt + 1 landed; then every wave's
+      __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + S, kt % S);
+      read_frags(kt + 1, 0, a0, b0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
   __syncthreads();
 
   const float ws = a.w_scale;
-  if constexpr (NORM) {
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      q[fm] += __shfl_xor(q[fm], 16);
-      q[fm] += __shfl_xor(q[fm], 32);
-    }
-  }
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = w * 64 + fm * 16 + (lane >> 4) * 4 + r;
-      const float sc = NORM ? ws * rms_scale(a, __shfl(q[fm], (lane >> 4) * 4 + r)) : ws;
+      const int rl = wm * 64 + fm * 16 + (lane >> 4) * 4 + r;
+      float sc = ws;
+      if constexpr (NORM) sc *= rms_scale(a, diag_for_row(sq[fm], r, lane));
 #pragma unroll
-      for (int fn = 0; fn < 8; ++fn) sC[rl * LDC + fn * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
+      for (int fn = 0; fn < FN; ++fn) sC[rl * LDC + (wn * FN + fn) * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
   __syncthreads();
-  epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0);
+  epilogue_tile<EM, BM, BN, LDC, 64 * NW>(a, sC, m0, n0);
 }
 
 hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
   const int T = ((a.M + kBigBM - 1) / kBigBM) * ((a.N + kBigBN - 1) / kBigBN);
-  const dim3 grid(8 * ((T + 7) / 8)), block(256);
+  constexpr int WN = 2;
+  const dim3 grid(8 * ((T + 7) / 8)), block(256 * WN);
   if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
   switch (em) {
     case E_QKV:
       if (!norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_QKV, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_big<E_QKV, true, WN>), grid, block, 0, s, a);
       break;
     case E_SWIGLU:
       if (!norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_SWIGLU, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_big<E_SWIGLU, true, WN>), grid, block, 0, s, a);
       break;
     case E_H_RESID:
       if (norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_H_RESID, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_big<E_H_RESID, false, WN>), grid, block, 0, s, a);
       break;
     default: return hipErrorInvalidValue;
   }
