@@ -36,7 +36,12 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each):
+// the IEEE division sequence would dominate the SwiGLU epilogue.  Large -z gives
+// exp2 -> inf, rcp -> 0, result -0; large z gives z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 __device__ __forceinline__ uint4 pack8(const float* v) {
   union { half_t h[8]; uint4 u; } p;
