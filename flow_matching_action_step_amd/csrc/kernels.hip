@@ -546,31 +546,30 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 // ----------------------------------------------------------------------------
 // Large-M GEMM with a multi-stage LDS pipeline
 // ----------------------------------------------------------------------------
-// 256 x 128 tiles; four waves each own 64 rows x 128 columns (32 MFMAs per
-// 32-wide k-step).  The k-slabs (BK = 64) rotate through a 3-stage LDS ring
-// that is filled by direct global->LDS loads (global_load_lds_dwordx4: lane l
-// of a wave writes 16 bytes at base + 16 l), so two slabs are in flight while
-// one is multiplied, without staging registers.  One load instruction moves
-// four 16-row x 8-column micro-tiles (1 KB, contiguous in the blocked layout
-// of both operands) and they land in LDS in the same blocked order, where the
-// 16 lanes of a fragment read cover 256 consecutive bytes (no bank conflicts,
-// no swizzle).  Requirements (checked
-// by the launcher): A is fp16 with K % 64 == 0 (K = 720 operands are
-// zero-padded to 768).
-// Waits are explicit: s_waitcnt vmcnt(n) + s_barrier, not __syncthreads
-// (whose fence would wait for every load in flight).
-constexpr int kBigBM = 256, kBigBN = 128, kBigBK = 64, kBigStages = 3;
+// BM x 128 tiles; each wave owns 16 FMW rows x 128 / WN columns.  The k-slabs
+// (BK = 64) rotate through an S-stage LDS ring filled by direct global->LDS
+// loads (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
+// base + 16 l), so the next slabs are in flight while one is multiplied,
+// without staging registers.  One load instruction moves four 16-row x
+// 8-column micro-tiles (1 KB, contiguous in the blocked layout of both
+// operands) and they land in LDS in the same blocked order, where the 16 lanes
+// of a fragment read cover 256 consecutive bytes (no bank conflicts, no
+// swizzle).  Requirements (checked by the launcher): A is fp16 with
+// K % 64 == 0 (K = 720 operands are zero-padded to 768).  Waits are explicit:
+// s_waitcnt vmcnt(n) + s_barrier, not __syncthreads (whose fence would wait
+// for every load in flight).
+constexpr int kBigBN = 128, kBigBK = 64;
 
-// WN = waves along N: four waves of 64 x 128 (WN = 1) or eight of 64 x 64 (WN = 2).
-template <int EM, bool NORM, int WN>
-__global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
-  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, S = kBigStages, LDC = BN + 4;
-  constexpr int NW = 4 * WN, FN = BN / 16 / WN;
+template <int EM, bool NORM, int BM, int FMW, int WN, int S>
+__global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const GemmArgs a) {
+  constexpr int BN = kBigBN, BK = kBigBK, LDC = BN + 4;
+  constexpr int WM = BM / (16 * FMW), NW = WM * WN, FN = BN / 16 / WN;
+  static_assert(WM * 16 * FMW == BM && FN * 16 * WN == BN, "waves tile the block");
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
   constexpr int SMEM = S * STAGE_BYTES > BM * LDC * 4 ? S * STAGE_BYTES : BM * LDC * 4;
   constexpr int A_LOADS = A_BYTES / 1024 / NW, W_LOADS = W_BYTES / 1024 / NW;  // per wave per stage
   constexpr int LOADS = A_LOADS + W_LOADS;
-  static_assert(LOADS * (S - 2) < 64, "vmcnt immediate range");
+  static_assert(A_LOADS * NW * 1024 == A_BYTES && W_LOADS * NW * 1024 == W_BYTES, "whole load instructions per wave");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   float* sC = reinterpret_cast<float*>(smem);
 
@@ -583,7 +582,7 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
   const int mt = tile / nN, nt = tile % nN;
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk = K / BK;
-  // NORM: A is fp16(h) unnormalised; each wave accumulates A A^T of its 64 rows on the
+  // NORM: A is fp16(h) unnormalised; each wave accumulates A A^T of its rows on the
   // matrix cores (row sums of squares on the diagonal), and 1/rms of each row scales the
   // finished sums.
 
@@ -615,10 +614,10 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
     }
   };
 
-  f32x4 acc[4][FN];
-  f32x4 sq[4];  // NORM: A A^T of each fm tile (row sums of squares on the diagonal)
+  f32x4 acc[FMW][FN];
+  f32x4 sq[FMW];  // NORM: A A^T of each fm tile (row sums of squares on the diagonal)
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < FMW; ++fm)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = sq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -631,21 +630,21 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
     const half_t* sW = reinterpret_cast<const half_t*>(base + A_BYTES);
     const int ch = s * 4 + (lane >> 4);  // 16-byte chunk of this lane's fragment within the slab
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-      af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * 4 + fm) * 8 + ch) * 128 + (lane & 15) * 8);
+    for (int fm = 0; fm < FMW; ++fm)
+      af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * FMW + fm) * 8 + ch) * 128 + (lane & 15) * 8);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
       bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * FN + fn) * 8 + ch) * 128 + (lane & 15) * 8);
   };
   auto mma = [&](const f16x8* af, const f16x8* bw) {
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
+    for (int fm = 0; fm < FMW; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
     if constexpr (NORM) {
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
+      for (int fm = 0; fm < FMW; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
     }
   };
   static_assert(BK == 64, "two k-steps per slab");
@@ -659,7 +658,7 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
   for (int st = 0; st < S; ++st) issue(st, st);
   __builtin_amdgcn_s_waitcnt(VM2 | (7 << 4) | (15 << 8));  // this wave's slab 0 landed
   __builtin_amdgcn_s_barrier();                            // ... every wave's
-  f16x8 a0[4], b0[FN], a1[4], b1[FN];
+  f16x8 a0[FMW], b0[FN], a1[FMW], b1[FN];
   read_frags(0, 0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
     read_frags(kt, 1, a1, b1);
@@ -682,10 +681,10 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
 
   const float ws = a.w_scale;
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < FMW; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = wm * 64 + fm * 16 + (lane >> 4) * 4 + r;
+      const int rl = wm * 16 * FMW + fm * 16 + (lane >> 4) * 4 + r;
       float sc = ws;
       if constexpr (NORM) sc *= rms_scale(a, diag_for_row(sq[fm], r, lane));
 #pragma unroll
@@ -695,34 +694,39 @@ __global__ __launch_bounds__(256 * WN, 1) void gemm_big(const GemmArgs a) {
   epilogue_tile<EM, BM, BN, LDC, 64 * NW>(a, sC, m0, n0);
 }
 
-hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
-  const int T = ((a.M + kBigBM - 1) / kBigBM) * ((a.N + kBigBN - 1) / kBigBN);
-  constexpr int WN = 2;
-  const dim3 grid(8 * ((T + 7) / 8)), block(256 * WN);
+template <int EM, bool NORM, int BM, int FMW, int WN, int S>
+static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
+  constexpr int NT = 64 * (BM / (16 * FMW)) * WN;
+  const int T = ((a.M + BM - 1) / BM) * ((a.N + kBigBN - 1) / kBigBN);
   if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
-  switch (em) {
-    case E_QKV:
-      if (!norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_QKV, true, WN>), grid, block, 0, s, a);
-      break;
-    case E_SWIGLU:
-      if (!norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_SWIGLU, true, WN>), grid, block, 0, s, a);
-      break;
-    case E_H_RESID:
-      if (norm) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemm_big<E_H_RESID, false, WN>), grid, block, 0, s, a);
-      break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S>), dim3(8 * ((T + 7) / 8)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-int big_tiles(int M, int N) { return ((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN); }
+// The configuration in use: 128 x 128 tiles, eight waves of 32 x 64, a 2-stage ring
+// (64 KB of LDS, two workgroups per CU).  Measured on MI355X against 256-row tiles,
+// 3-stage rings and four-wave shapes, and against the register-staged tiled kernel,
+// for the four projections at M = 100 .. 6400: it was fastest or within 5 % everywhere
+// (gate/up at M = 3200: 30 us against 35-36 us).
+hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
+  switch (em) {
+    case E_QKV:
+      if (!norm) return hipErrorInvalidValue;
+      return launch_gemm_dma<E_QKV, true, 128, 2, 2, 2>(a, s);
+    case E_SWIGLU:
+      if (!norm) return hipErrorInvalidValue;
+      return launch_gemm_dma<E_SWIGLU, true, 128, 2, 2, 2>(a, s);
+    case E_H_RESID:
+      if (norm) return hipErrorInvalidValue;
+      return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 2>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
-// Measured on MI355X: with fewer than ~160 tiles of 256 x 128 the large-tile GEMM
-// leaves too many CUs idle and the 64/128-row tiled kernel is faster.
-bool use_big_gemm(int M, int N) { return M > 64 && big_tiles(M, N) >= 160; }
+// Measured on MI355X (see launch_gemm_big): the pipelined kernel for every large-M
+// projection whose stored K is a multiple of 64, except the cross layers' Q (N = 960)
+// below M = 3200, where the tiled kernel is a few percent faster.
+bool use_big_gemm(int M, int N, int K) { return M > 64 && K % kBigBK == 0 && !(N == kNQ && M < 3200); }
 
 // ----------------------------------------------------------------------------
 // Block-masked grouped-query attention

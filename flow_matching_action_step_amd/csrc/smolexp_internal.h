@@ -132,11 +132,10 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int M, int N, int K);
 
-// Large-M GEMM (fp16 A, K % 64 == 0): E_QKV and E_SWIGLU on the RMSNorm'd residual
-// (norm = true: A = h16), E_H_RESID on a plain fp16 operand.
+// Large-M GEMM with an LDS-DMA ring (fp16 A, K % 64 == 0): E_QKV and E_SWIGLU on the
+// RMSNorm'd residual (norm = true: A = h16), E_H_RESID on a plain fp16 operand.
 hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s);
-int big_tiles(int M, int N);
-bool use_big_gemm(int M, int N);  // large-tile GEMM for this Q/K/V or gate/up shape
+bool use_big_gemm(int M, int N, int K);  // pipelined LDS-DMA GEMM for this shape (K as stored)
 constexpr int kKPad = 768;  // stored columns of h16 and of the weights that read it (a multiple of 64)
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
