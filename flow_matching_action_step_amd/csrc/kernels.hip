@@ -835,18 +835,17 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
 // V rows, key kinds.  Branch-free: every address is clamped into its
 // buffer and the loaded vector is zeroed afterwards for masked or missing
 // keys, so all loads are in flight together.
-template <bool SELF, int RK>
+template <bool SELF, int RK, int NT = 256>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int r0, bf16_t* sK, bf16_t* sV,
-                                           uint8_t* sKind, int nthreads) {
-  constexpr int NV = RK * 8 / 256;  // 16-byte vectors per thread (256 threads)
+                                           uint8_t* sKind) {
+  constexpr int NV = (RK * 8 + NT - 1) / NT;  // 16-byte vectors of K (and of V) per thread
   const int tid = threadIdx.x, P = a.P;
   const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
   const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
   const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : pk;
   const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : pv;
   const uint8_t* mk = a.mask + (size_t)b * P;
-  (void)nthreads;
-  for (int i = tid; i < RK; i += 256) {
+  for (int i = tid; i < RK; i += NT) {
     const int j = r0 + i;
     sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
   }
@@ -854,7 +853,7 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int 
   bool kok[NV];
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
-    const int v = tid + 256 * it;
+    const int v = min(tid + NT * it, RK * 8 - 1);  // past the end: repeat the last vector (not stored)
     // K and V rows: 8 lanes per key (whole 128-byte rows)
     const int j = r0 + (v >> 3), c = (v & 7) * 8;
     const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
@@ -866,9 +865,11 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int 
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
     if (!kok[it]) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
-    const int v = tid + 256 * it;
-    *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
-    *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
+    const int v = tid + NT * it;
+    if (NV * NT == RK * 8 || v < RK * 8) {
+      *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
+      *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
+    }
   }
 }
 
@@ -909,7 +910,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
     __syncthreads();  // the previous round's LDS reads are done
-    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind, 256);
+    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind);
     __syncthreads();
 
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
@@ -931,24 +932,26 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   }
 }
 
-// Small batches: the four waves of a workgroup share 16 query rows and split
-// the key blocks among themselves (wave w takes blocks w, w + 4, ...), then
-// merge their softmax states (running max, running sum, unnormalised output)
-// through LDS.  Five times as many workgroups as attn_kernel at batch 1.
-template <bool SELF, int NBLK>
-__global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
-  constexpr int RK = NBLK * kKB, OLD = kHD + 4;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[RK * kALD];
+// Small batches: a workgroup takes QG groups of 16 query rows of one KV head
+// (of its 3 x 50) and KS waves per group split the staged key blocks among
+// themselves (wave (q, k) takes blocks k, k + KS, ...); with KS > 1 each
+// group's softmax states (running max, running sum, unnormalised output) are
+// merged through LDS.  All QG x KS waves share one staging of the keys.
+template <bool SELF, int NBLK, int QG, int KS>
+__global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs a) {
+  constexpr int NT = 64 * QG * KS, RK = NBLK * kKB, OLD = kHD + 4;
+  constexpr int KV_BYTES = 2 * RK * kALD * 2, MERGE_BYTES = KS > 1 ? QG * KS * 16 * OLD * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];
-  __shared__ float sM[4][16], sL[4][16];
-  float* sO = reinterpret_cast<float*>(sK);  // [4 waves][16 rows][OLD], used after the last round
-  static_assert(4 * 16 * OLD * 4 <= (int)sizeof(sK), "merge buffer fits in the K staging area");
+  __shared__ float sM[QG][KS][16], sL[QG][KS][16];
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem);  // K rows, then V rows
+  bf16_t* sV = sK + RK * kALD;
+  float* sO = reinterpret_cast<float*>(smem);    // [QG][KS][16][OLD], used after the last round
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qg = wave / KS, ks = wave % KS;
   const int g = blockIdx.y, b = blockIdx.z;
   const int P = a.P;
-  const int rq = blockIdx.x * 16 + (lane & 15);
+  const int rq = blockIdx.x * (16 * QG) + qg * 16 + (lane & 15);
   const bool rvalid = rq < 3 * kChunk;
   const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
   const int qi = rvalid ? rq % kChunk : 0;
@@ -970,40 +973,54 @@ __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
     __syncthreads();
-    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind, 256);
+    attn_stage<SELF, RK, NT>(a, b, g, r0, sK, sV, sKind);
     __syncthreads();
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
-    for (int blk = wave; blk < nb; blk += 4)
+    for (int blk = ks; blk < nb; blk += KS)
       attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
                  m_run, l_run, lane);
   }
 
-  // merge the four waves' states
-  __syncthreads();
-  if (lane < 16) {
-    sM[wave][lane] = m_run;
-    sL[wave][lane] = l_run;
-  }
+  if constexpr (KS == 1) {
+    if (rvalid) {
+      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      const int orow = b * kChunk + qi;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m) {
+        union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(wave * 16 + (lane & 15)) * OLD + m * 16 + (lane >> 4) * 4 + r] = o[m][r];
-  __syncthreads();
-  {
-    const int row = tid >> 4, d0 = (tid & 15) * 4;
-    const int rq2 = blockIdx.x * 16 + row;
-    if (rq2 < 3 * kChunk) {
+        for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
+        *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
+      }
+    }
+  } else {
+    // merge the KS waves' states of each query group
+    __syncthreads();
+    if (lane < 16) {
+      sM[qg][ks][lane] = m_run;
+      sL[qg][ks][lane] = l_run;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sO[((qg * KS + ks) * 16 + (lane & 15)) * OLD + m * 16 + (lane >> 4) * 4 + r] = o[m][r];
+    __syncthreads();
+    for (int u = tid; u < QG * 16 * 16; u += NT) {
+      const int q2 = u >> 8, row = (u >> 4) & 15, d0 = (u & 15) * 4;
+      const int rq2 = blockIdx.x * (16 * QG) + q2 * 16 + row;
+      if (rq2 >= 3 * kChunk) continue;
       float mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sM[w][row]);
+      for (int w = 0; w < KS; ++w) mx = fmaxf(mx, sM[q2][w][row]);
       const float mu = mx == -INFINITY ? 0.f : mx;
       float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(sM[w][row] - mu);
-        l += sL[w][row] * sc;
+      for (int w = 0; w < KS; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(sM[q2][w][row] - mu);
+        l += sL[q2][w][row] * sc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += sO[(w * 16 + row) * OLD + d0 + e] * sc;
+        for (int e = 0; e < 4; ++e) acc[e] += sO[((q2 * KS + w) * 16 + row) * OLD + d0 + e] * sc;
       }
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       const int hq2 = 3 * g + rq2 / kChunk, qi2 = rq2 % kChunk;
@@ -1015,18 +1032,27 @@ __global__ __launch_bounds__(256) void attn_ksplit_kernel(const AttnArgs a) {
   }
 }
 
-template <bool SELF>
-static void launch_ksplit(const AttnArgs& a, hipStream_t s) {
+template <bool SELF, int QG, int KS>
+static void launch_small(const AttnArgs& a, hipStream_t s) {
   // key blocks staged per round: the whole key range when it fits in five blocks
   const int nk = a.P + (SELF ? kChunk : 0);
   const int nblk = min(5, max(2, (nk + kKB - 1) / kKB));
-  const dim3 grid((3 * kChunk + 15) / 16, kHKV, a.B), block(256);
+  const dim3 grid((3 * kChunk + 16 * QG - 1) / (16 * QG), kHKV, a.B), block(64 * QG * KS);
   switch (nblk) {
-    case 2: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_ksplit_kernel<SELF, 5>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_small_kernel<SELF, 2, QG, KS>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_small_kernel<SELF, 3, QG, KS>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_small_kernel<SELF, 4, QG, KS>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_small_kernel<SELF, 5, QG, KS>), grid, block, 0, s, a); break;
   }
+}
+
+// Measured at batch 1 (graph replay, P = 177): four key-split waves per query group beat
+// fewer, wider workgroups; self layers gain a little from two query groups per workgroup
+// (4.9 against 5.1 us), cross layers do not.
+template <bool SELF>
+static void launch_ksplit(const AttnArgs& a, hipStream_t s) {
+  if constexpr (SELF) launch_small<SELF, 2, 4>(a, s);
+  else launch_small<SELF, 1, 4>(a, s);
 }
 
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
