@@ -53,13 +53,16 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 // ----------------------------------------------------------------------------
 // GEMM
 // ----------------------------------------------------------------------------
-// Two kernels share the A-operand loaders and the epilogues:
+// Three kernels share the A-operand loaders and the epilogues:
 //  * gemm_skinny (M <= 64, one query): one 512-thread workgroup per 16 output
-//    columns.  Its 8 waves split K; each wave issues every load it needs (its
-//    weight fragments and A fragments) at once, so the kernel waits for memory
-//    about once, then the waves' partial tiles meet in LDS.
-//  * gemm_tiled (M > 64): 128 x 128 output tiles, four waves of 64 x 64,
-//    BK = 64 slabs double-buffered in LDS.
+//    columns and 16-row block.  Its 8 waves split K; each wave issues every
+//    load it needs (its weight fragments and A fragments) at once, so the
+//    kernel waits for memory about once, then the waves' partial tiles meet in
+//    LDS.
+//  * gemm_tiled (M > 64): 64/128 x 128 output tiles, four waves, BK = 64 slabs
+//    double-buffered in LDS through registers.
+//  * gemm_big (M > 64, K % 64 == 0): 128 x 128 tiles, eight waves, an LDS ring
+//    filled by direct global->LDS loads.
 // Epilogues run on the finished fp32 tile staged in LDS.
 //
 // Weight row order inside each 16-row block (set by the host when it loads
@@ -136,7 +139,8 @@ template <int EM, int BM, int BN, int LDC, int NT, bool PRE = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0,
                                               const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
-  static_assert(UPR <= 64 && 64 % UPR == 0 && (BM * UPR) % NT == 0, "rows inside one wave, uniform trip count");
+  static_assert(UPR <= 64 && 64 % UPR == 0, "rows inside one wave");
+  static_assert(!PRE || (BM * NB <= NT && BN == 16 && BM / 16 <= NT / 64), "PRE: at most one work unit per thread");
   const int M = a.M, N = a.N;
   if constexpr (EM == E_QKV) {
     // Work unit = (row, 16-column block): the block is 8 rotation pairs of one Q/K
@@ -273,68 +277,79 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
   }
 }
 
-// M <= 64.  One workgroup per 16 output columns; wave w takes k-steps
-// w*KPW .. w*KPW+KPW-1 (32 wide each).  A_NORM: the rows of fp16(h) go to
-// the MFMA unscaled, so no load waits on the row scale; each wave also sums
-// the squares of its slice of every row, and 1/rms(row) scales the finished
-// sums (a per-row constant, so this equals normalising first up to rounding).
-template <int AM, int EM, int KPW>
+// M <= 64.  A workgroup computes 16 output columns for RB 16-row blocks
+// (rows m0 .. m0 + 16 RB - 1); wave w takes k-steps w*KPW .. w*KPW+KPW-1 (32
+// wide each).  What bounds these launches is the bytes one workgroup streams
+// through its CU (A rows + 16 weight rows), so the rows of a small batch are
+// split over 64 / (16 RB) workgroups per column block.  The workgroups of one
+// column block sit on one XCD (workgroup i runs on XCD i % 8), so that XCD's
+// L2 fetches those weight rows once.  A_NORM: the rows of fp16(h) go to the
+// MFMA unscaled, so no load waits on the row scale; each wave also sums the
+// squares of its slice of every row, and 1/rms(row) scales the finished sums
+// (a per-row constant, so this equals normalising first up to rounding).
+template <int AM, int EM, int KPW, int RB>
 __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
-  constexpr int NW = 8, LDC = 16;
-  __shared__ float sRed[NW * 64 * 16];
-  __shared__ float sC[64 * LDC];
-  __shared__ float sQ[AM == A_NORM ? NW : 1][64];  // per-wave partial sums of squares of the rows
+  constexpr int NW = 8, LDC = 16, BM = 16 * RB, SPLIT = 4 / RB;
+  static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks per workgroup");
+  __shared__ float sRed[NW * BM * 16];
+  __shared__ float sC[BM * LDC];
+  __shared__ float sQ[AM == A_NORM ? NW : 1][BM];  // per-wave partial sums of squares of the rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n0 = blockIdx.x * 16;
+  // workgroup -> (column block, row split): XCD = blockIdx.x % 8 = column block % 8
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int nb = xcd + 8 * (j / SPLIT), m0 = (j % SPLIT) * BM;
   const int M = a.M, N = a.N, K = a.K;
+  const int n0 = nb * 16;
+  if (n0 >= N || m0 >= M) return;  // grid padded to whole XCD rounds; no barrier before this
   const int nks = (K + 31) / 32;
   const int n = n0 + (lane & 15), kl = (lane >> 4) * 8;
 
   // epilogue inputs, loaded with the operands (see epilogue_tile's unit mapping: E_QKV thread
-  // t < 64 owns row t; E_H_RESID lane r + 16 p of wave w < 4 owns row 16 w + r, columns n0 + 4 p..)
+  // t < BM owns row m0 + t; E_H_RESID lane r + 16 p of wave w < RB owns row m0 + 16 w + r,
+  // columns n0 + 4 p..)
   constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
   float4 pre[4];
   if constexpr (EM == E_QKV) {
     const int d0 = ((n0 % kHD) / 16) * 8;
     const bool rot = n0 / kHD < kHQ + kHKV;
-    if (tid < M && rot) {
-      const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)tid * (kHD / 2) + d0);
+    if (tid < BM && m0 + tid < M && rot) {
+      const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)(m0 + tid) * (kHD / 2) + d0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pre[j] = cs4[j];
+      for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
     }
   } else if constexpr (EM == E_H_RESID) {
-    const int row = w * 16 + (lane & 15), col = n0 + (lane >> 4) * 4;
-    if (w < 4 && row < M && col < N) pre[0] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+    const int row = m0 + w * 16 + (lane & 15), col = n0 + (lane >> 4) * 4;
+    if (w < RB && row < M && col < N) pre[0] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
   }
   uint4 wf[KPW];
-  uint4 af[KPW][4];
+  uint4 af[KPW][RB];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = w * KPW + i, k = ks * 32 + kl;
     const bool kok = ks < nks && k < K;
     wf[i] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const int row = fm * 16 + (lane & 15);
+    for (int fm = 0; fm < RB; ++fm) {
+      const int row = m0 + fm * 16 + (lane & 15);
       const bool ok = kok && row < M;
-      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, blockIdx.x == 0);
+      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, nb == 0);
     }
   }
-  f32x4 acc[4];
+  f32x4 acc[RB];
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm) acc[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int fm = 0; fm < RB; ++fm) acc[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const f16x8 bw = __builtin_bit_cast(f16x8, wf[i]);
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
+    for (int fm = 0; fm < RB; ++fm) {
       acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i][fm]), bw, acc[fm], 0, 0, 0);
     }
   }
   if constexpr (AM == A_NORM) {
     // this wave's share of each row's sum of squares, from the diagonal of A A^T over its K slice
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
+    for (int fm = 0; fm < RB; ++fm) {
       f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KPW; ++i) sq = sumsq_mfma(__builtin_bit_cast(f16x8, af[i][fm]), sq);
@@ -342,15 +357,15 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     }
   }
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
+  for (int fm = 0; fm < RB; ++fm)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sRed[(w * 64 + fm * 16 + (lane >> 4) * 4 + r) * 16 + (lane & 15)] = acc[fm][r];
+    for (int r = 0; r < 4; ++r) sRed[(w * BM + fm * 16 + (lane >> 4) * 4 + r) * 16 + (lane & 15)] = acc[fm][r];
   __syncthreads();
   const float ws = a.w_scale;
-  for (int i = tid; i < 64 * 16; i += 512) {
+  for (int i = tid; i < BM * 16; i += 512) {
     float s = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * 64 * 16 + i];
+    for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * BM * 16 + i];
     float sc = ws;
     if constexpr (AM == A_NORM) {  // RMSNorm: rows were multiplied unscaled, 1/rms(h) applied here
       float q = 0.f;
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     sC[(i / 16) * LDC + (i % 16)] = s * sc;
   }
   __syncthreads();
-  epilogue_tile<EM, 64, 16, LDC, 512, PRE>(a, sC, 0, n0, pre);
+  epilogue_tile<EM, BM, 16, LDC, 512, PRE>(a, sC, m0, n0, pre);
 }
 
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
@@ -484,11 +499,16 @@ GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p;
   const int nks = (K + 31) / 32;
   p.bm = 64;
+  p.rb = 4;
   if (M <= 64) {
     p.kind = 0;
     p.ntiles_n = (N + 15) / 16;
     const int need = (nks + 7) / 8;
     p.kpw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : need <= 8 ? 8 : 0;
+    // measured at 16 and 50 rows, with the operand just written by another kernel: one
+    // 16-row block per workgroup is fastest for every projection (down 3.9 us against 5.8
+    // with all rows in one workgroup, o 2.8 against 3.8, gate/up 4.2 against 4.6)
+    p.rb = 1;
   } else {
     p.kind = 1;
     p.ntiles_n = (N + 127) / 128;
@@ -498,26 +518,39 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return p;
 }
 
+template <int AM, int EM, int RB>
+static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  // column blocks rounded up to whole XCD rounds, times the row splits (see gemm_skinny)
+  const dim3 grid(8 * ((p.ntiles_n + 7) / 8) * (4 / RB)), block(512);
+  switch (p.kpw) {
+    case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3, RB>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4, RB>), grid, block, 0, s, a); break;
+    case 6:
+    case 8:
+      // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
+      // variants would not fit their fragments in registers
+      if constexpr (AM == A_F16) {
+        if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // K beyond 8 waves x 8 k-steps x 32
+  }
+  return hipGetLastError();
+}
+
 template <int AM, int EM>
 static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   if (p.kind == 0) {
-    const dim3 grid(p.ntiles_n), block(512);
-    switch (p.kpw) {
-      case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3>), grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4>), grid, block, 0, s, a); break;
-      case 6:
-      case 8:
-        // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
-        // variants would not fit their fragments in registers
-        if constexpr (AM == A_F16) {
-          if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6>), grid, block, 0, s, a);
-          else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8>), grid, block, 0, s, a);
-          break;
-        }
-        return hipErrorInvalidValue;
-      default: return hipErrorInvalidValue;  // K beyond 8 waves x 8 k-steps x 32
+    if (a.M > 64) return hipErrorInvalidValue;
+    switch (p.rb) {
+      case 4: return launch_skinny<AM, EM, 4>(p, a, s);
+      case 2: return launch_skinny<AM, EM, 2>(p, a, s);
+      case 1: return launch_skinny<AM, EM, 1>(p, a, s);
+      default: return hipErrorInvalidValue;
     }
   } else {
     const int T = ((a.M + p.bm - 1) / p.bm) * p.ntiles_n;

@@ -128,6 +128,7 @@ struct GemmPlan {
                  // 2: large-tile GEMM on a pre-normalised operand (recorded for timing only)
   int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
   int bm;        // tiled: rows per tile (64 or 128)
+  int rb;        // skinny: 16-row blocks per workgroup (4, 2 or 1: the rows split over 4 / rb workgroups)
   int ntiles_n;  // output tiles (workgroups) along N
 };
 GemmPlan plan_gemm(int M, int N, int K);
