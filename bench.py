@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
 KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed kernel
-    "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_small_kernel<true,", "attn_cross": "attn_small_kernel<false,",
+    "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_small_kernel<true,", "attn_cross": "attn_cross_q_kernel<",
     "o": "gemm_skinny<0, 3, 4>", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8>",
     "action_out": "gemm_skinny<1, 6,",
 }
@@ -111,7 +111,11 @@ def kernel_costs(L, B, lengths, P):
     keys_self = 50 * sum_nb + 1275 * B
     c["attn_self"] = (M * 960 * 2 + kv_self + M * 960 * 2, 4.0 * 64 * 15 * keys_self)
     kv_cross = 5 * 64 * 2 * 2 * sum_nb
-    c["attn_cross"] = (M * 960 * 2 + kv_cross + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
+    if B <= CROSS_Q_MAX_BATCH:  # the cross layers' Q projection runs inside the attention launch
+        c["attn_cross"] = (960 * 720 * 2 + M * 720 * 2 + kv_cross + M * 960 * 2,
+                           2.0 * M * 960 * 720 + 4.0 * 64 * 15 * 50 * sum_nb)
+    else:
+        c["attn_cross"] = (M * 960 * 2 + kv_cross + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
     c["o"] = (720 * 960 * 2 + M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
     c["gate_up"] = (4096 * 720 * 2 + M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
     c["down"] = (720 * 2048 * 2 + M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
@@ -121,6 +125,7 @@ def kernel_costs(L, B, lengths, P):
     return c, per_step
 
 
+CROSS_Q_MAX_BATCH = 8  # largest batch whose cross layers fold the Q projection into attention (library constant)
 KERNEL_IDS = {"qkv_self": 0, "attn_self": 1, "attn_cross": 2, "o": 3, "gate_up": 4, "down": 5, "action_out": 6}
 
 

@@ -125,7 +125,8 @@ __device__ __forceinline__ float diag_for_row(const f32x4& sq, int r, int lane) 
 }
 
 // 1/rms of a row from its sum of squares.
-__device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { return rsqrtf(sumsq * a.inv_k + a.eps); }
+__device__ __forceinline__ float rms_scale_qk(float inv_k, float eps, float sumsq) { return rsqrtf(sumsq * inv_k + eps); }
+__device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { return rms_scale_qk(a.inv_k, a.eps, sumsq); }
 
 // Epilogue on a finished tile sC[BM][LDC] (fp32, weight and row scales
 // applied) whose rows start at m0 and columns at n0 (BN a multiple of 16).
@@ -867,43 +868,63 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
 // Stage keys r0 .. r0 + RK - 1 of one (query, KV head) into LDS: K rows,
 // V rows, key kinds.  Branch-free: every address is clamped into its
 // buffer and the loaded vector is zeroed afterwards for masked or missing
-// keys, so all loads are in flight together.
+// keys, so all loads are in flight together.  Split in two so that a caller
+// can issue the loads early and store them to LDS later.
+template <bool SELF, int RK, int NT>
+struct AttnStage {
+  static constexpr int NV = (RK * 8 + NT - 1) / NT;  // 16-byte vectors of K (and of V) per thread
+  static constexpr int NKIND = (RK + NT - 1) / NT;
+  uint4 kv[NV], vv[NV];
+  bool kok[NV];
+  uint8_t kind[NKIND];
+
+  __device__ __forceinline__ void issue(const AttnArgs& a, int b, int g, int r0) {
+    const int tid = threadIdx.x, P = a.P;
+    const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
+    const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
+    const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : pk;
+    const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : pv;
+    const uint8_t* mk = a.mask + (size_t)b * P;
+#pragma unroll
+    for (int it = 0; it < NKIND; ++it) {
+      const int j = r0 + tid + NT * it;
+      kind[it] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int v = min(tid + NT * it, RK * 8 - 1);  // past the end: repeat the last vector (not stored)
+      // K and V rows: 8 lanes per key (whole 128-byte rows)
+      const int j = r0 + (v >> 3), c = (v & 7) * 8;
+      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+      const size_t po = pre ? (size_t)j * kHD + c : c, co = (size_t)(j - P) * kHD + c;
+      kv[it] = *reinterpret_cast<const uint4*>(chunk ? ck + co : pk + po);
+      vv[it] = *reinterpret_cast<const uint4*>(chunk ? cv + co : pv + po);
+      kok[it] = pre ? mk[j] != 0 : chunk;
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* sK, bf16_t* sV, uint8_t* sKind) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < NKIND; ++it)
+      if (tid + NT * it < RK) sKind[tid + NT * it] = kind[it];
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      if (!kok[it]) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
+      const int v = tid + NT * it;
+      if (NV * NT == RK * 8 || v < RK * 8) {
+        *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
+        *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
+      }
+    }
+  }
+};
+
 template <bool SELF, int RK, int NT = 256>
 __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int r0, bf16_t* sK, bf16_t* sV,
                                            uint8_t* sKind) {
-  constexpr int NV = (RK * 8 + NT - 1) / NT;  // 16-byte vectors of K (and of V) per thread
-  const int tid = threadIdx.x, P = a.P;
-  const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
-  const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
-  const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : pk;
-  const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : pv;
-  const uint8_t* mk = a.mask + (size_t)b * P;
-  for (int i = tid; i < RK; i += NT) {
-    const int j = r0 + i;
-    sKind[i] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
-  }
-  uint4 kv[NV], vv[NV];
-  bool kok[NV];
-#pragma unroll
-  for (int it = 0; it < NV; ++it) {
-    const int v = min(tid + NT * it, RK * 8 - 1);  // past the end: repeat the last vector (not stored)
-    // K and V rows: 8 lanes per key (whole 128-byte rows)
-    const int j = r0 + (v >> 3), c = (v & 7) * 8;
-    const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-    const size_t po = pre ? (size_t)j * kHD + c : c, co = (size_t)(j - P) * kHD + c;
-    kv[it] = *reinterpret_cast<const uint4*>(chunk ? ck + co : pk + po);
-    vv[it] = *reinterpret_cast<const uint4*>(chunk ? cv + co : pv + po);
-    kok[it] = pre ? mk[j] != 0 : chunk;
-  }
-#pragma unroll
-  for (int it = 0; it < NV; ++it) {
-    if (!kok[it]) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
-    const int v = tid + NT * it;
-    if (NV * NT == RK * 8 || v < RK * 8) {
-      *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
-      *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
-    }
-  }
+  AttnStage<SELF, RK, NT> st;
+  st.issue(a, b, g, r0);
+  st.store(sK, sV, sKind);
 }
 
 // NBLK key blocks are staged per round: all of their loads are issued before
@@ -1088,8 +1109,174 @@ static void launch_ksplit(const AttnArgs& a, hipStream_t s) {
   else launch_small<SELF, 1, 4>(a, s);
 }
 
+// Cross-attention layer of a small batch with its own query projection: the
+// keys of a cross layer come only from the prefix cache, so the Q/K/V GEMM of
+// that layer (which computes only Q there) needs no other workgroup's results
+// and one launch does both.  A workgroup takes 16 rows of one query head:
+//  (1) it issues the loads of its projection operands (16 rows of fp16(h),
+//      the head's 64 weight rows, 8 waves splitting K = 768 as the M <= 64
+//      GEMM does) together with the first round of prefix K/V;
+//  (2) the projection runs on the matrix cores, the row sums of squares from
+//      A A^T; the waves' partials meet in LDS, where the 1/rms scale and the
+//      rotary embedding are applied and Q is rounded to bf16;
+//  (3) the 8 waves split the staged key blocks (online softmax as above) and
+//      merge their states in LDS.
+// The Q values equal those of the separate GEMM launch (same K split, same
+// order of the sums).
+template <int NBLK>
+__global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
+  constexpr int NT = 512, NW = 8, RK = NBLK * kKB, OLD = kHD + 4, QLD = kHD + 8;
+  constexpr int KPW = kKPad / 32 / NW;  // k-steps per wave
+  static_assert(KPW * 32 * NW == kKPad, "K split");
+  constexpr int KV_BYTES = 2 * RK * kALD * 2;
+  constexpr int RED_BYTES = NW * 16 * kHD * 4, MERGE_BYTES = NW * 16 * OLD * 4;
+  __shared__ __attribute__((aligned(16))) char sKV[KV_BYTES];
+  __shared__ __attribute__((aligned(16))) char sR[RED_BYTES > MERGE_BYTES ? RED_BYTES : MERGE_BYTES];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[16 * QLD];
+  __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];
+  __shared__ float sQ[NW][16], sM[NW][16], sL[NW][16];
+  bf16_t* sK = reinterpret_cast<bf16_t*>(sKV);
+  bf16_t* sV = sK + RK * kALD;
+  float* sRed = reinterpret_cast<float*>(sR);  // [wave][row][64] projection partials
+  float* sO = reinterpret_cast<float*>(sR);    // [wave][row][OLD] after the last round
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, g = hq / 3;
+  const int P = a.P;
+
+  // (1) projection operands of this wave's K slice, then the first round of keys
+  const int qa = rb * 16 + (lane & 15);  // chunk row of this lane's A fragment
+  const bool aok = qa < kChunk;
+  uint4 af[KPW], wf[KPW][4];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int k = (w * KPW + i) * 32 + (lane >> 4) * 8;
+    af[i] = aok ? *reinterpret_cast<const uint4*>(a.h16 + t16_off(b * kChunk + qa, k, kKPad / 8)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      wf[i][cb] = *reinterpret_cast<const uint4*>(a.wq + t16_off(hq * kHD + cb * 16 + (lane & 15), k, a.ldw >> 3));
+  }
+  AttnStage<false, RK, NT> st;
+  st.issue(a, b, g, 0);
+
+  // (2) Q = fp16(h) W'^T on the matrix cores, and the rows' sums of squares
+  f32x4 acc[4], sq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const f16x8 av = __builtin_bit_cast(f16x8, af[i]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, wf[i][cb]), acc[cb], 0, 0, 0);
+    sq = sumsq_mfma(av, sq);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sRed[(w * 16 + (lane >> 4) * 4 + r) * kHD + cb * 16 + (lane & 15)] = acc[cb][r];
+  if (((lane & 15) >> 2) == (lane >> 4)) sQ[w][lane & 15] = sq[lane & 3];
+  st.store(sK, sV, sKind);
+  __syncthreads();
+  {
+    // thread -> (row, rotation pair d): weight rows of block d / 8 hold dims d0..d0+7 then d0+32..
+    const int r = tid >> 5, d = tid & 31, qr = rb * 16 + r;
+    const int c1 = (d >> 3) * 16 + (d & 7), c2 = c1 + 8;
+    float s1 = 0.f, s2 = 0.f, q = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      s1 += sRed[(w2 * 16 + r) * kHD + c1];
+      s2 += sRed[(w2 * 16 + r) * kHD + c2];
+      q += sQ[w2][r];
+    }
+    bf16_t lo = 0, hi = 0;
+    if (qr < kChunk) {
+      const float sc = a.w_scale * rms_scale_qk(a.inv_k, a.eps, q);
+      const float v1 = s1 * sc, v2 = s2 * sc;
+      const float2 cs = a.ropeq[(size_t)(b * kChunk + qr) * (kHD / 2) + d];
+      lo = f2bf(v1 * cs.x - v2 * cs.y);
+      hi = f2bf(v1 * cs.y + v2 * cs.x);
+    }
+    sQt[r * QLD + d] = lo;
+    sQt[r * QLD + d + kHD / 2] = hi;
+  }
+  __syncthreads();
+
+  // (3) attention of the 16 rows over the prefix keys
+  const int qi = rb * 16 + (lane & 15);
+  bf16x8 qf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sQt + (lane & 15) * QLD + kk * 32 + (lane >> 4) * 8));
+  f32x4 o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int r0 = 0; r0 < P; r0 += RK) {
+    if (r0 > 0) {
+      __syncthreads();
+      attn_stage<false, RK, NT>(a, b, g, r0, sK, sV, sKind);
+      __syncthreads();
+    }
+    const int nb = min(NBLK, (P - r0 + kKB - 1) / kKB);
+    for (int blk = w; blk < nb; blk += NW)
+      attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
+                 m_run, l_run, lane);
+  }
+  __syncthreads();
+  if (lane < 16) {
+    sM[w][lane] = m_run;
+    sL[w][lane] = l_run;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sO[(w * 16 + (lane & 15)) * OLD + m * 16 + (lane >> 4) * 4 + r] = o[m][r];
+  __syncthreads();
+  if (tid < 16 * 16) {
+    const int row = tid >> 4, d0 = (tid & 15) * 4, qr = rb * 16 + row;
+    if (qr < kChunk) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) mx = fmaxf(mx, sM[w2][row]);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float l = 0.f, acc4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float sc = __builtin_amdgcn_exp2f(sM[w2][row] - mu);
+        l += sL[w2][row] * sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc4[e] += sO[(w2 * 16 + row) * OLD + d0 + e] * sc;
+      }
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      union { half_t h[4]; uint2 u; } pk4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk4.h[e] = (half_t)(acc4[e] * inv);
+      *reinterpret_cast<uint2*>(a.out + t16_off(b * kChunk + qr, hq * kHD + d0, kNQ / 8)) = pk4.u;
+    }
+  }
+}
+
+static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
+  const int nblk = min(5, max(2, (a.P + kKB - 1) / kKB));
+  const dim3 grid((kChunk + 15) / 16, kHQ, a.B), block(512);
+  switch (nblk) {
+    case 2: hipLaunchKernelGGL((attn_cross_q_kernel<2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_cross_q_kernel<3>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_cross_q_kernel<4>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_cross_q_kernel<5>), grid, block, 0, s, a); break;
+  }
+}
+
+bool use_cross_q(int B) { return B <= kCrossQMaxBatch; }
+
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
   const dim3 block(256);
+  if (!self_layer && a.wq) {  // cross layer with its query projection
+    if (!use_cross_q(a.B) || !a.h16 || !a.ropeq || a.ldw != kKPad) return hipErrorInvalidValue;
+    launch_cross_q(a, s);
+    return hipGetLastError();
+  }
   if (a.B <= 8) {
     if (self_layer) launch_ksplit<true>(a, s);
     else launch_ksplit<false>(a, s);

@@ -329,17 +329,26 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
 
     for (int l = 0; l < L; ++l) {
       const LayerDev& ld = h->layers[l];
-      GemmArgs gq = g;
-      gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
-      gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
-      gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.ropeq = h->ropeq;
-      if ((e = norm_gemm(ld.self_attn ? PR_QKV : -1, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
+      // cross layers of a small batch: the Q projection runs inside the attention launch
+      const bool fold_q = !ld.self_attn && use_cross_q(B);
+      if (!fold_q) {
+        GemmArgs gq = g;
+        gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
+        gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
+        gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.ropeq = h->ropeq;
+        if ((e = norm_gemm(ld.self_attn ? PR_QKV : -1, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
+      }
 
       AttnArgs aa;
+      memset(&aa, 0, sizeof(aa));
       aa.q = h->q; aa.kc = h->kc; aa.vc = h->vc;
       aa.pk = kv + (size_t)l * kvLayer;
       aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2;
       aa.mask = c.mask; aa.out = h->o16; aa.B = B; aa.P = P;
+      if (fold_q) {
+        aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale;
+        aa.h16 = h->h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = h->ropeq;
+      }
       const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
       if (record_probes && !h->probe_ok[pr]) { h->probe_ok[pr] = true; h->probe_a[pr] = aa; }
       if ((e = launch_attention(ld.self_attn, aa, s)) != hipSuccess) return hip_fail(h, e, "attention launch");

@@ -103,7 +103,19 @@ struct AttnArgs {
   const uint8_t* mask;   // [B][P]
   half_t* out;           // [B*50][960] fp16, blocked (t16_off)
   int B, P;
+  // cross layers of a small batch (use_cross_q): the query projection runs in the
+  // attention launch.  wq = the layer's Q weight ([960][768] blocked, RMSNorm gain
+  // folded, values scaled by 1 / w_scale); h16 = fp16 residual [B*50][768] blocked.
+  // wq == nullptr: Q comes from q.
+  const half_t* wq;
+  int ldw;
+  float w_scale;
+  const half_t* h16;
+  float inv_k, eps;
+  const float2* ropeq;
 };
+constexpr int kCrossQMaxBatch = 8;
+bool use_cross_q(int B);  // the cross layers of this batch size fold the Q projection into attention
 
 struct PrologueArgs {
   int B;
