@@ -87,14 +87,19 @@ struct smolexp_handle {
 
   bool have_last = false;
   CallKey last{};
+  // launches of the timed kernels in the first step of the last directly enqueued call,
+  // one per layer (smolexp_time_kernel replays them)
+  struct Probe {
+    bool attn;
+    GemmArgs g;
+    AttnArgs a;
+    GemmPlan plan;
+    AMode am;
+    EMode em;
+  };
   bool have_probe = false;
   CallKey probe_key{};
-  bool probe_ok[PR_COUNT] = {};
-  GemmArgs probe_g[PR_COUNT];
-  AttnArgs probe_a[PR_COUNT];
-  GemmPlan probe_plan[PR_COUNT];
-  AMode probe_am[PR_COUNT];
-  EMode probe_em[PR_COUNT];
+  std::vector<Probe> probes[PR_COUNT];
 };
 
 namespace {
@@ -238,10 +243,11 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
   hipError_t e;
   if (record_probes) {
-    for (int i = 0; i < PR_COUNT; ++i) h->probe_ok[i] = false;
+    for (int i = 0; i < PR_COUNT; ++i) h->probes[i].clear();
     h->probe_key = key_of(c);
     h->have_probe = true;
   }
+  bool first_step = true;  // probes are recorded in the first step only
 
   PrologueArgs pa;
   memset(&pa, 0, sizeof(pa));
@@ -264,12 +270,11 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   const size_t kvLayer = (size_t)2 * B * kHKV * (size_t)P * kHD;  // elements per layer
   const bf16_t* kv = static_cast<const bf16_t*>(c.kv);
   auto record = [&](int probe, const GemmPlan& plan, AMode am, EMode em, const GemmArgs& g) {
-    if (record_probes && probe >= 0 && !h->probe_ok[probe]) {
-      h->probe_ok[probe] = true;
-      h->probe_g[probe] = g;
-      h->probe_plan[probe] = plan;
-      h->probe_am[probe] = am;
-      h->probe_em[probe] = em;
+    if (record_probes && first_step && probe >= 0) {
+      smolexp_handle::Probe p;
+      memset(&p, 0, sizeof(p));
+      p.attn = false; p.g = g; p.plan = plan; p.am = am; p.em = em;
+      h->probes[probe].push_back(p);
     }
   };
   auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g) -> hipError_t {
@@ -350,7 +355,12 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
         aa.h16 = h->h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = h->ropeq;
       }
       const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
-      if (record_probes && !h->probe_ok[pr]) { h->probe_ok[pr] = true; h->probe_a[pr] = aa; }
+      if (record_probes && first_step) {
+        smolexp_handle::Probe p;
+        memset(&p, 0, sizeof(p));
+        p.attn = true; p.a = aa;
+        h->probes[pr].push_back(p);
+      }
       if ((e = launch_attention(ld.self_attn, aa, s)) != hipSuccess) return hip_fail(h, e, "attention launch");
 
       GemmArgs gop = g;
@@ -383,6 +393,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
       gv.final_out = (k == n_t - 1) ? c.out : nullptr;
     }
     if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
+    first_step = false;
   }
   return SMOLEXP_OK;
 }
@@ -739,7 +750,8 @@ int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_m
 int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, float* avg_us) {
   if (!h) return SMOLEXP_E_INVAL;
   h->err.clear();
-  if (!avg_us || reps < 1 || kernel < 0 || kernel > PR_COUNT) return fail(h, SMOLEXP_E_INVAL, "bad kernel id, reps or avg_us");
+  if (!avg_us || reps < 1 || reps > 100000 || kernel < 0 || kernel > PR_COUNT)
+    return fail(h, SMOLEXP_E_INVAL, "bad kernel id, reps or avg_us");
   if (!h->have_last) return fail(h, SMOLEXP_E_STATE, "no previous denoise call to time");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   CallArgs lastc;
@@ -755,20 +767,51 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     int rc0 = enqueue(h, lastc, s, true);
     if (rc0 != SMOLEXP_OK) return rc0;
   }
-  if (kernel < PR_COUNT && !h->probe_ok[kernel]) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");
+  if (kernel < PR_COUNT && h->probes[kernel].empty()) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");
+  // launch i replays the (i mod n)-th recorded instance: every layer's weights in turn, as in the loop
+  auto launch = [&](int i, hipStream_t st) -> hipError_t {
+    const std::vector<smolexp_handle::Probe>& v = h->probes[kernel];
+    const smolexp_handle::Probe& p = v[(size_t)i % v.size()];
+    if (p.attn) return launch_attention(kernel == PR_ATTN_SELF, p.a, st);
+    if (p.plan.kind == 2) return launch_gemm_big(p.em, p.am == A_NORM, p.g, st);
+    return launch_gemm(p.plan, p.am, p.em, p.g, st);
+  };
+  hipGraphExec_t exec = nullptr;
+  if (kernel < PR_COUNT && h->cfg.use_graphs) {
+    // one graph of `reps` launches (the loop itself runs as a graph)
+    hipError_t e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamBeginCapture");
+    hipError_t el = hipSuccess;
+    for (int i = 0; i < reps && el == hipSuccess; ++i) el = launch(i, h->cap);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(h->cap, &graph);
+    if (el != hipSuccess || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return hip_fail(h, el != hipSuccess ? el : e, "kernel timing capture");
+    }
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(h, e, "kernel timing graph");
+    e = hipGraphLaunch(exec, s);  // untimed pass
+    if (e != hipSuccess) {
+      (void)hipStreamSynchronize(s);
+      (void)hipGraphExecDestroy(exec);
+      return hip_fail(h, e, "kernel timing graph launch");
+    }
+  }
   hipEvent_t e0, e1;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipEventCreate");
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (exec) { (void)hipStreamSynchronize(s); (void)hipGraphExecDestroy(exec); }
+    return fail(h, SMOLEXP_E_HIP, "hipEventCreate");
+  }
   hipError_t e = hipEventRecord(e0, s);
   int rc = SMOLEXP_OK;
-  for (int i = 0; i < reps && e == hipSuccess && rc == SMOLEXP_OK; ++i) {
-    if (kernel == PR_COUNT) {
-      rc = run_call(h, lastc, s);  // the whole loop: replay the previous call
-    } else if (kernel == PR_ATTN_SELF || kernel == PR_ATTN_CROSS) {
-      e = launch_attention(kernel == PR_ATTN_SELF, h->probe_a[kernel], s);
-    } else if (h->probe_plan[kernel].kind == 2) {
-      e = launch_gemm_big(h->probe_em[kernel], h->probe_am[kernel] == A_NORM, h->probe_g[kernel], s);
-    } else {
-      e = launch_gemm(h->probe_plan[kernel], h->probe_am[kernel], h->probe_em[kernel], h->probe_g[kernel], s);
+  if (exec) {
+    if (e == hipSuccess) e = hipGraphLaunch(exec, s);
+  } else {
+    for (int i = 0; i < reps && e == hipSuccess && rc == SMOLEXP_OK; ++i) {
+      if (kernel == PR_COUNT) rc = run_call(h, lastc, s);  // the whole loop: replay the previous call
+      else e = launch(i, s);
     }
   }
   if (e == hipSuccess) e = hipEventRecord(e1, s);
@@ -777,6 +820,10 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  if (exec) {
+    (void)hipStreamSynchronize(s);
+    (void)hipGraphExecDestroy(exec);
+  }
   if (rc != SMOLEXP_OK) return rc;
   if (e != hipSuccess) return hip_fail(h, e, "kernel timing");
   *avg_us = ms * 1000.f / reps;

@@ -170,9 +170,13 @@ int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_m
 
 /*
  * Measurement hook: average duration in microseconds of one launch of one
- * kernel of the loop, timed with HIP events around `reps` back-to-back
- * launches on hip_stream (synchronous).  It reuses the workspace contents of
- * the last smolexp_denoise/_ex call, which must have used the same batch and
+ * kernel of the loop, timed with HIP events on hip_stream (synchronous) around
+ * `reps` (1..100000) back-to-back launches.  Launch i repeats the (i mod n)-th
+ * launch of that kernel in the first step of the last call (n = one per layer
+ * that uses it), so the weights change from launch to launch as in the loop.
+ * With graphs enabled the launches are captured as one HIP graph, replayed once
+ * untimed and once timed.  It reuses the workspace contents of the last
+ * smolexp_denoise/_ex call, which must have used the same batch and
  * prefix_len, and leaves that workspace's numbers unspecified.
  *   kernel: 0 = self-attention layer QKV projection, 1 = self attention,
  *           2 = cross attention, 3 = o projection, 4 = gate/up projection,
