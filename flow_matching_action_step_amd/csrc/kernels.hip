@@ -288,27 +288,28 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 // MFMA unscaled, so no load waits on the row scale; each wave also sums the
 // squares of its slice of every row, and 1/rms(row) scales the finished sums
 // (a per-row constant, so this equals normalising first up to rounding).
-template <int AM, int EM, int KPW, int RB>
+template <int AM, int EM, int KPW, int RB, int CB = 1>
 __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
-  constexpr int NW = 8, LDC = 16, BM = 16 * RB, SPLIT = 4 / RB;
+  constexpr int NW = 8, BM = 16 * RB, BN = 16 * CB, LDC = BN, SPLIT = 4 / RB;
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks per workgroup");
-  __shared__ float sRed[NW * BM * 16];
+  constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
+  static_assert(CB == 1 || !PRE, "several column blocks only for epilogues without preloads");
+  __shared__ float sRed[NW * BM * BN];
   __shared__ float sC[BM * LDC];
   __shared__ float sQ[AM == A_NORM ? NW : 1][BM];  // per-wave partial sums of squares of the rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // workgroup -> (column block, row split): XCD = blockIdx.x % 8 = column block % 8
+  // workgroup -> (column block group, row split): XCD = blockIdx.x % 8 = group % 8
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int nb = xcd + 8 * (j / SPLIT), m0 = (j % SPLIT) * BM;
   const int M = a.M, N = a.N, K = a.K;
-  const int n0 = nb * 16;
+  const int n0 = nb * BN;
   if (n0 >= N || m0 >= M) return;  // grid padded to whole XCD rounds; no barrier before this
   const int nks = (K + 31) / 32;
-  const int n = n0 + (lane & 15), kl = (lane >> 4) * 8;
+  const int kl = (lane >> 4) * 8;
 
   // epilogue inputs, loaded with the operands (see epilogue_tile's unit mapping: E_QKV thread
   // t < BM owns row m0 + t; E_H_RESID lane r + 16 p of wave w < RB owns row m0 + 16 w + r,
   // columns n0 + 4 p..)
-  constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
   float4 pre[4];
   if constexpr (EM == E_QKV) {
     const int d0 = ((n0 % kHD) / 16) * 8;
@@ -322,13 +323,17 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     const int row = m0 + w * 16 + (lane & 15), col = n0 + (lane >> 4) * 4;
     if (w < RB && row < M && col < N) pre[0] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
   }
-  uint4 wf[KPW];
+  uint4 wf[KPW][CB];
   uint4 af[KPW][RB];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = w * KPW + i, k = ks * 32 + kl;
     const bool kok = ks < nks && k < K;
-    wf[i] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = n0 + cb * 16 + (lane & 15);
+      wf[i][cb] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int fm = 0; fm < RB; ++fm) {
       const int row = m0 + fm * 16 + (lane & 15);
@@ -336,15 +341,19 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
       af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, nb == 0);
     }
   }
-  f32x4 acc[RB];
+  f32x4 acc[RB][CB];
 #pragma unroll
-  for (int fm = 0; fm < RB; ++fm) acc[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int fm = 0; fm < RB; ++fm)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[fm][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
-    const f16x8 bw = __builtin_bit_cast(f16x8, wf[i]);
 #pragma unroll
-    for (int fm = 0; fm < RB; ++fm) {
-      acc[fm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i][fm]), bw, acc[fm], 0, 0, 0);
+    for (int cb = 0; cb < CB; ++cb) {
+      const f16x8 bw = __builtin_bit_cast(f16x8, wf[i][cb]);
+#pragma unroll
+      for (int fm = 0; fm < RB; ++fm)
+        acc[fm][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i][fm]), bw, acc[fm][cb], 0, 0, 0);
     }
   }
   if constexpr (AM == A_NORM) {
@@ -360,24 +369,27 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
 #pragma unroll
   for (int fm = 0; fm < RB; ++fm)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sRed[(w * BM + fm * 16 + (lane >> 4) * 4 + r) * 16 + (lane & 15)] = acc[fm][r];
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sRed[(w * BM + fm * 16 + (lane >> 4) * 4 + r) * BN + cb * 16 + (lane & 15)] = acc[fm][cb][r];
   __syncthreads();
   const float ws = a.w_scale;
-  for (int i = tid; i < BM * 16; i += 512) {
+  for (int i = tid; i < BM * BN; i += 512) {
     float s = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * BM * 16 + i];
+    for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * BM * BN + i];
     float sc = ws;
     if constexpr (AM == A_NORM) {  // RMSNorm: rows were multiplied unscaled, 1/rms(h) applied here
       float q = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) q += sQ[w2][i / 16];
+      for (int w2 = 0; w2 < NW; ++w2) q += sQ[w2][i / BN];
       sc *= rms_scale(a, q);
     }
-    sC[(i / 16) * LDC + (i % 16)] = s * sc;
+    sC[i] = s * sc;
   }
   __syncthreads();
-  epilogue_tile<EM, BM, 16, LDC, 512, PRE>(a, sC, m0, n0, pre);
+  epilogue_tile<EM, BM, BN, LDC, 512, PRE>(a, sC, m0, n0, pre);
 }
 
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
@@ -501,6 +513,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   const int nks = (K + 31) / 32;
   p.bm = 64;
   p.rb = 4;
+  p.cb = 1;
   if (M <= 64) {
     p.kind = 0;
     p.ntiles_n = (N + 15) / 16;
@@ -510,6 +523,9 @@ GemmPlan plan_gemm(int M, int N, int K) {
     // 16-row block per workgroup is fastest for every projection (down 3.9 us against 5.8
     // with all rows in one workgroup, o 2.8 against 3.8, gate/up 4.2 against 4.6)
     p.rb = 1;
+    // gate/up (N = 4096, weights from the last-level cache): two column blocks per workgroup
+    // share the activation reads, 4.0 against 4.3 us (four: 4.1)
+    p.cb = N >= 4096 ? 2 : 1;
   } else {
     p.kind = 1;
     p.ntiles_n = (N + 127) / 128;
@@ -519,22 +535,23 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return p;
 }
 
-template <int AM, int EM, int RB>
+template <int AM, int EM, int RB, int CB>
 static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-  // column blocks rounded up to whole XCD rounds, times the row splits (see gemm_skinny)
-  const dim3 grid(8 * ((p.ntiles_n + 7) / 8) * (4 / RB)), block(512);
+  // column block groups rounded up to whole XCD rounds, times the row splits (see gemm_skinny)
+  const int groups = (p.ntiles_n + CB - 1) / CB;
+  const dim3 grid(8 * ((groups + 7) / 8) * (4 / RB)), block(512);
   switch (p.kpw) {
-    case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3, RB>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4, RB>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB, CB>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB, CB>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3, RB, CB>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4, RB, CB>), grid, block, 0, s, a); break;
     case 6:
     case 8:
       // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
       // variants would not fit their fragments in registers
-      if constexpr (AM == A_F16) {
-        if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB>), grid, block, 0, s, a);
+      if constexpr (AM == A_F16 && CB == 1) {
+        if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB, CB>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB, CB>), grid, block, 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -543,14 +560,24 @@ static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_
   return hipGetLastError();
 }
 
+template <int AM, int EM, int RB>
+static hipError_t launch_skinny_cb(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  // several column blocks per workgroup: epilogues without per-unit preloads only
+  if constexpr (EM == E_SWIGLU) {
+    if (p.cb == 2) return launch_skinny<AM, EM, RB, 2>(p, a, s);
+    if (p.cb == 4) return launch_skinny<AM, EM, RB, 4>(p, a, s);
+  }
+  return launch_skinny<AM, EM, RB, 1>(p, a, s);
+}
+
 template <int AM, int EM>
 static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   if (p.kind == 0) {
     if (a.M > 64) return hipErrorInvalidValue;
     switch (p.rb) {
-      case 4: return launch_skinny<AM, EM, 4>(p, a, s);
-      case 2: return launch_skinny<AM, EM, 2>(p, a, s);
-      case 1: return launch_skinny<AM, EM, 1>(p, a, s);
+      case 4: return launch_skinny_cb<AM, EM, 4>(p, a, s);
+      case 2: return launch_skinny_cb<AM, EM, 2>(p, a, s);
+      case 1: return launch_skinny_cb<AM, EM, 1>(p, a, s);
       default: return hipErrorInvalidValue;
     }
   } else {

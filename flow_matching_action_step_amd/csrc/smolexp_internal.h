@@ -141,6 +141,7 @@ struct GemmPlan {
   int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
   int bm;        // tiled: rows per tile (64 or 128)
   int rb;        // skinny: 16-row blocks per workgroup (4, 2 or 1: the rows split over 4 / rb workgroups)
+  int cb;        // skinny: 16-column blocks per workgroup (1, 2 or 4; more than 1 for the SwiGLU epilogue only)
   int ntiles_n;  // output tiles (workgroups) along N
 };
 GemmPlan plan_gemm(int M, int N, int K);
