@@ -25,7 +25,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
 KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed kernel
     "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_small_kernel<true,", "attn_cross": "attn_cross_q_kernel<",
-    "o": "gemm_skinny<0, 3, 4>", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8>",
+    "o": "gemm_skinny<0, 3, 4,", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8,",
     "action_out": "gemm_skinny<1, 6,",
 }
 
