@@ -141,7 +141,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
                                               const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0, "rows inside one wave");
-  static_assert(!PRE || (BM * NB <= NT && BN == 16 && BM / 16 <= NT / 64), "PRE: at most one work unit per thread");
+  static_assert(!PRE || (BM * NB <= NT && NB <= 4 && BM / 16 <= NT / 64), "PRE: the units of one thread fit pre[]");
   const int M = a.M, N = a.N;
   if constexpr (EM == E_QKV) {
     // Work unit = (row, 16-column block): the block is 8 rotation pairs of one Q/K
@@ -236,8 +236,9 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     for (int rb = wv; rb < RB; rb += NWV) {
       const int r = rb * 16 + r16, row = m0 + r;
       const bool live = row < M;
-      for (int c = part; c < NC4; c += 4) {
-        const int col = n0 + c * 4;
+#pragma unroll
+      for (int t = 0; t < NC4 / 4; ++t) {
+        const int c = part + 4 * t, col = n0 + c * 4;
         if (live && col < N) {
           const float4 v = *reinterpret_cast<const float4*>(sC + r * LDC + c * 4);
           float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, kD / 4));
@@ -246,7 +247,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
             const float4 b = *reinterpret_cast<const float4*>(a.bias + col);
             o = make_float4(v.x + b.x, v.y + b.y, v.z + b.z, v.w + b.w);
           } else {
-            const float4 hv = PRE ? pre[0] : *hp;
+            const float4 hv = PRE ? pre[t] : *hp;
             o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
           }
           *hp = o;
@@ -290,38 +291,46 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 // (a per-row constant, so this equals normalising first up to rounding).
 template <int AM, int EM, int KPW, int RB, int CB = 1>
 __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
-  constexpr int NW = 8, BM = 16 * RB, BN = 16 * CB, LDC = BN, SPLIT = 4 / RB;
+  constexpr int NW = 8, BM = 16 * RB, BN = 16 * CB, LDC = BN;
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks per workgroup");
+  static_assert(CB == 1 || CB == 2 || CB == 4, "column blocks per workgroup");
   constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
-  static_assert(CB == 1 || !PRE, "several column blocks only for epilogues without preloads");
   __shared__ float sRed[NW * BM * BN];
   __shared__ float sC[BM * LDC];
   __shared__ float sQ[AM == A_NORM ? NW : 1][BM];  // per-wave partial sums of squares of the rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // workgroup -> (column block group, row split): XCD = blockIdx.x % 8 = group % 8
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int nb = xcd + 8 * (j / SPLIT), m0 = (j % SPLIT) * BM;
   const int M = a.M, N = a.N, K = a.K;
+  // workgroup -> (column block group, row tile): the row tiles of one group are consecutive
+  // in j and share XCD = blockIdx.x % 8 = group % 8
+  const int nrt = (M + BM - 1) / BM;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int nb = xcd + 8 * (j / nrt), m0 = (j % nrt) * BM;
   const int n0 = nb * BN;
-  if (n0 >= N || m0 >= M) return;  // grid padded to whole XCD rounds; no barrier before this
+  if (n0 >= N) return;  // grid padded to whole XCD rounds; no barrier before this
   const int nks = (K + 31) / 32;
   const int kl = (lane >> 4) * 8;
 
-  // epilogue inputs, loaded with the operands (see epilogue_tile's unit mapping: E_QKV thread
-  // t < BM owns row m0 + t; E_H_RESID lane r + 16 p of wave w < RB owns row m0 + 16 w + r,
-  // columns n0 + 4 p..)
+  // epilogue inputs, loaded with the operands, in epilogue_tile's unit mapping: E_QKV thread
+  // g < BM * CB owns row m0 + g / CB, column block g % CB; E_H_RESID lane r + 16 p of wave
+  // w < RB owns row m0 + 16 w + r, columns n0 + 4 (p + 4 t).. for t < CB
   float4 pre[4];
   if constexpr (EM == E_QKV) {
-    const int d0 = ((n0 % kHD) / 16) * 8;
-    const bool rot = n0 / kHD < kHQ + kHKV;
-    if (tid < BM && m0 + tid < M && rot) {
-      const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)(m0 + tid) * (kHD / 2) + d0);
+    if (tid < BM * CB) {
+      const int row = m0 + tid / CB, cb0 = n0 + (tid % CB) * 16;
+      const int d0 = ((cb0 % kHD) / 16) * 8;
+      if (row < M && cb0 < N && cb0 / kHD < kHQ + kHKV) {
+        const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)row * (kHD / 2) + d0);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
+        for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
+      }
     }
   } else if constexpr (EM == E_H_RESID) {
-    const int row = m0 + w * 16 + (lane & 15), col = n0 + (lane >> 4) * 4;
-    if (w < RB && row < M && col < N) pre[0] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+    const int row = m0 + w * 16 + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+      const int col = n0 + ((lane >> 4) + 4 * t) * 4;
+      if (w < RB && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+    }
   }
   uint4 wf[KPW][CB];
   uint4 af[KPW][RB];
@@ -537,9 +546,9 @@ GemmPlan plan_gemm(int M, int N, int K) {
 
 template <int AM, int EM, int RB, int CB>
 static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-  // column block groups rounded up to whole XCD rounds, times the row splits (see gemm_skinny)
-  const int groups = (p.ntiles_n + CB - 1) / CB;
-  const dim3 grid(8 * ((groups + 7) / 8) * (4 / RB)), block(512);
+  // column block groups rounded up to whole XCD rounds, times the row tiles (see gemm_skinny)
+  const int groups = (p.ntiles_n + CB - 1) / CB, nrt = (a.M + 16 * RB - 1) / (16 * RB);
+  const dim3 grid(8 * ((groups + 7) / 8) * nrt), block(512);
   switch (p.kpw) {
     case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB, CB>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB, CB>), grid, block, 0, s, a); break;
@@ -549,7 +558,8 @@ static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_
     case 8:
       // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
       // variants would not fit their fragments in registers
-      if constexpr (AM == A_F16 && CB == 1) {
+      // (64 x 64 tiles at K = 2048 would not fit their fragments in registers either)
+      if constexpr (AM == A_F16 && RB * CB < 16) {
         if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB, CB>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB, CB>), grid, block, 0, s, a);
         break;
@@ -562,18 +572,17 @@ static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_
 
 template <int AM, int EM, int RB>
 static hipError_t launch_skinny_cb(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-  // several column blocks per workgroup: epilogues without per-unit preloads only
-  if constexpr (EM == E_SWIGLU) {
-    if (p.cb == 2) return launch_skinny<AM, EM, RB, 2>(p, a, s);
-    if (p.cb == 4) return launch_skinny<AM, EM, RB, 4>(p, a, s);
+  switch (p.cb) {
+    case 1: return launch_skinny<AM, EM, RB, 1>(p, a, s);
+    case 2: return launch_skinny<AM, EM, RB, 2>(p, a, s);
+    case 4: return launch_skinny<AM, EM, RB, 4>(p, a, s);
+    default: return hipErrorInvalidValue;
   }
-  return launch_skinny<AM, EM, RB, 1>(p, a, s);
 }
 
 template <int AM, int EM>
 static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   if (p.kind == 0) {
-    if (a.M > 64) return hipErrorInvalidValue;
     switch (p.rb) {
       case 4: return launch_skinny_cb<AM, EM, 4>(p, a, s);
       case 2: return launch_skinny_cb<AM, EM, 2>(p, a, s);
@@ -784,10 +793,48 @@ hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s
   }
 }
 
-// Measured on MI355X (see launch_gemm_big): the pipelined kernel for every large-M
-// projection whose stored K is a multiple of 64, except the cross layers' Q (N = 960)
-// below M = 3200, where the tiled kernel is a few percent faster.
-bool use_big_gemm(int M, int N, int K) { return M > 64 && K % kBigBK == 0 && !(N == kNQ && M < 3200); }
+// The plan of one projection of the loop, from measurements at M = 50..3200 rows with the
+// weights cycling through a 250 MB footprint, as in the loop (us per launch, best kernel):
+//  * the register-resident K split (skinny) wins up to about 1600 rows for every projection
+//    (down at 800 rows: 12.0 us against 25.5 on 128 x 128 pipelined tiles, whose 42
+//    workgroups leave most CUs idle; o 6.6 against 12.9; Q/K/V 10.2 against 14.3);
+//  * the pipelined kernel wins from 1600-3200 rows on (gate/up from 800);
+//  * the register-staged tiled kernel only for the time MLP and action_in at 3200 rows and more.
+GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
+  GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);  // skinny base: k-steps per wave, column blocks
+  auto skinny = [&](int rb, int cb) {
+    p.kind = 0; p.rb = rb; p.cb = cb;
+    return p;
+  };
+  auto big = [&]() {
+    GemmPlan b = p;
+    b.kind = 2;
+    return b;
+  };
+  if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
+  (void)am;
+  switch (em) {
+    case E_QKV:
+      if (N == kNQ) {  // cross layers: Q only
+        if (M <= 1000) return skinny(2, 4);
+        if (M <= 2400) return skinny(2, 2);
+      } else if (M <= 1200) {
+        return skinny(2, 2);
+      }
+      return big();
+    case E_SWIGLU:
+      return M <= 600 ? skinny(2, 2) : big();
+    case E_H_RESID:
+      if (K > 1024 && M <= 200) return skinny(2, 1);
+      if (M <= 400) return skinny(2, 2);
+      return M <= 2400 ? skinny(4, 2) : big();
+    case E_ACTOUT:
+      if (M <= 2400) return skinny(1, 1);
+      return M <= 4800 ? skinny(4, 2) : plan_gemm(M, N, K);
+    default:  // time MLP, action_in
+      return M <= 2400 ? skinny(2, 2) : plan_gemm(M, N, K);
+  }
+}
 
 // ----------------------------------------------------------------------------
 // Block-masked grouped-query attention

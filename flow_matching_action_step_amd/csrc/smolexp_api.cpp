@@ -277,31 +277,21 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
       h->probes[probe].push_back(p);
     }
   };
-  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g) -> hipError_t {
-    if (em == E_H_RESID && use_big_gemm(g.M, g.N, g.K)) {  // o and down of a large batch
-      GemmPlan plan;
-      memset(&plan, 0, sizeof(plan));
-      plan.kind = 2;
+  // every projection: the planned kernel (plan_for); RMSNorm'd projections (Q/K/V,
+  // gate/up, action_out) read h16 = fp16(h), over the zero-padded K = 768 on the pipelined GEMM
+  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
+    GemmArgs g = g0;
+    if (am == A_NORM) { g.A = h->h16; g.lda = kKPad; }
+    const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em);
+    if (plan.kind == 2) {
+      if (am == A_NORM) g.K = kKPad;
       record(probe, plan, am, em, g);
-      return launch_gemm_big(em, false, g, s);
+      return launch_gemm_big(em, am == A_NORM, g, s);
     }
-    const GemmPlan plan = plan_gemm(g.M, g.N, g.K);
     record(probe, plan, am, em, g);
     return launch_gemm(plan, am, em, g, s);
   };
-  // RMSNorm'd projections (Q/K/V, gate/up, action_out) read h16 = fp16(h); at large M
-  // Q/K/V and gate/up run on the pipelined GEMM over the zero-padded K = 768.
-  auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g0) -> hipError_t {
-    GemmArgs g = g0;
-    g.A = h->h16; g.lda = kKPad;
-    if (em == E_ACTOUT || !use_big_gemm(g.M, g.N, kKPad)) return gemm(probe, A_NORM, em, g);
-    g.K = kKPad;
-    GemmPlan plan;
-    memset(&plan, 0, sizeof(plan));
-    plan.kind = 2;
-    record(probe, plan, A_NORM, em, g);
-    return launch_gemm_big(em, true, g, s);
-  };
+  auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t { return gemm(probe, A_NORM, em, g); };
 
   for (int k = 0; k < n_t; ++k) {
     const float t = pa.t[k];

@@ -136,12 +136,12 @@ struct PrologueArgs {
 
 // How one GEMM is cut up (kernels.hip decides, the host sizes workspaces from it).
 struct GemmPlan {
-  int kind;      // 0: skinny (M <= 64): one workgroup per 16 columns; 1: tiled: 128 x 128 tiles;
-                 // 2: large-tile GEMM on a pre-normalised operand (recorded for timing only)
+  int kind;      // 0: register-resident K split (skinny): 16 rb x 16 cb tiles, 8 waves split K;
+                 // 1: register-staged tiles (64 or 128 x 128); 2: pipelined LDS-DMA GEMM
   int kpw;       // skinny: 32-wide k-steps per wave (8 waves)
   int bm;        // tiled: rows per tile (64 or 128)
   int rb;        // skinny: 16-row blocks per workgroup (4, 2 or 1: the rows split over 4 / rb workgroups)
-  int cb;        // skinny: 16-column blocks per workgroup (1, 2 or 4; more than 1 for the SwiGLU epilogue only)
+  int cb;        // skinny: 16-column blocks per workgroup (1, 2 or 4)
   int ntiles_n;  // output tiles (workgroups) along N
 };
 GemmPlan plan_gemm(int M, int N, int K);
@@ -149,7 +149,9 @@ GemmPlan plan_gemm(int M, int N, int K);
 // Large-M GEMM with an LDS-DMA ring (fp16 A, K % 64 == 0): E_QKV and E_SWIGLU on the
 // RMSNorm'd residual (norm = true: A = h16), E_H_RESID on a plain fp16 operand.
 hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s);
-bool use_big_gemm(int M, int N, int K);  // pipelined LDS-DMA GEMM for this shape (K as stored)
+// The kernel and tiles for one projection of the loop (K = logical width).  kind 2 = the
+// pipelined GEMM, which reads RMSNorm'd operands over K = kKPad stored columns.
+GemmPlan plan_for(int M, int N, int K, AMode am, EMode em);
 constexpr int kKPad = 768;  // stored columns of h16 and of the weights that read it (a multiple of 64)
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
