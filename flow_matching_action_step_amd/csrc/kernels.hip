@@ -863,10 +863,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
 // One 64-key block of the online softmax for the lane's query row (row qi of
 // the chunk).  sKb, sVb: the block's K and V rows [64][kALD]; kind: its key
 // kinds; key0 = index of its first key minus P (chunk key j is visible to row
-// qi when j - P <= qi).
-__device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
-                                           int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
-                                           float& l_run, int lane) {
+// qi when j - P <= qi).  MODE (uniform over the wave, from block_mode): 0 =
+// every key is a valid prefix key (no mask), 1 = prefix keys only (valid or
+// not), 2 = chunk keys too (causal test).  m_run: running max of the scaled
+// scores (log2 domain); l_acc: running sum of the weights, accumulated on the
+// matrix cores (an all-ones operand against the weights, so it sums exactly
+// the bf16 weights that multiply V); every register holds it.
+template <int MODE>
+__device__ __forceinline__ void attn_block_m(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
+                                             int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
+                                             f32x4& l_acc, int lane) {
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   // S^T[key][row] for the 64 keys of the block (4 tiles of 16 keys)
   f32x4 sc[4];
@@ -879,46 +885,45 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
       sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], sc[sub], 0, 0, 0);
     }
   }
-  // masks without branches: four key kinds per 32-bit LDS read, bitwise logic
-  float mb = -INFINITY;
+  // masks (raw scores; the scale is positive, so the max commutes with it)
+  if constexpr (MODE != 0) {
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
-    const int jl0 = sub * 16 + (lane >> 4) * 4;
-    const unsigned k4 = *reinterpret_cast<const unsigned*>(kind + jl0);
+    for (int sub = 0; sub < 4; ++sub) {
+      const int jl0 = sub * 16 + (lane >> 4) * 4;
+      const unsigned k4 = *reinterpret_cast<const unsigned*>(kind + jl0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const unsigned kd = (k4 >> (8 * r)) & 0xffu;
-      const bool ok = (kd == 1u) | ((kd == 2u) & ((key0 + jl0 + r) <= qi));
-      const float val = ok ? sc[sub][r] * sl2 : -INFINITY;
-      sc[sub][r] = val;
-      mb = fmaxf(mb, val);
+      for (int r = 0; r < 4; ++r) {
+        const unsigned kd = (k4 >> (8 * r)) & 0xffu;
+        bool ok;
+        if constexpr (MODE == 1) ok = kd == 1u;
+        else ok = (kd == 1u) | ((kd == 2u) & ((key0 + jl0 + r) <= qi));
+        sc[sub][r] = ok ? sc[sub][r] : -INFINITY;
+      }
     }
   }
+  float mb = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+#pragma unroll
+  for (int sub = 1; sub < 4; ++sub) mb = fmaxf(fmaxf(mb, sc[sub][0]), fmaxf(fmaxf(sc[sub][1], sc[sub][2]), sc[sub][3]));
   mb = fmaxf(mb, __shfl_xor(mb, 16));
   mb = fmaxf(mb, __shfl_xor(mb, 32));
-  const float m_new = fmaxf(m_run, mb);
+  const float m_new = fmaxf(m_run, mb * sl2);
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
   // v_exp_f32 directly: arguments are <= 0 and results that would be
   // denormal may flush to zero, which a softmax weight can afford
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-  float ls = 0.f;
 #pragma unroll
   for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_use);
-      sc[sub][r] = p;
-      ls += p;
-    }
-  ls += __shfl_xor(ls, 16);
-  ls += __shfl_xor(ls, 32);
-  l_run = l_run * alpha + ls;
+    for (int r = 0; r < 4; ++r) sc[sub][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][r], sl2, -m_use));
   m_run = m_new;
 #pragma unroll
   for (int m = 0; m < 4; ++m) o[m] *= alpha;
+  l_acc[0] *= alpha;  // only register 0 is read back; the others are left to drift
   // O^T[d][row] += V^T[d][key] P^T[key][row], 32 keys per MFMA.  The k-slot
   // order (keys 4q..4q+3 then 16+4q..16+4q+3 for lane group q) is the same for
   // both operands.
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     bf16x8 pb;
@@ -936,7 +941,25 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
       const s16x4 u[2] = {lo, hi};
       o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
     }
+    l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, l_acc, 0, 0, 0);
   }
+}
+
+// How much masking a staged 64-key block needs (uniform over the wave): 0 when
+// every key is a valid prefix key, 1 when all are prefix keys, 2 with chunk keys.
+__device__ __forceinline__ int block_mode(const uint8_t* kind, int lane) {
+  const unsigned k = kind[lane];
+  if (__ballot(k == 2u) != 0ull) return 2;
+  return __ballot(k != 1u) != 0ull ? 1 : 0;
+}
+
+__device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
+                                           int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
+                                           f32x4& l_acc, int lane) {
+  const int mode = block_mode(kind, lane);
+  if (mode == 0) attn_block_m<0>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
+  else if (mode == 1) attn_block_m<1>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
+  else attn_block_m<2>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
 }
 
 // Stage keys r0 .. r0 + RK - 1 of one (query, KV head) into LDS: K rows,
@@ -1033,7 +1056,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   f32x4 o[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
@@ -1044,10 +1068,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
     for (int blk = 0; blk < nb; ++blk)
       attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
-                 m_run, l_run, lane);
+                 m_run, l_acc, lane);
   }
 
   if (rvalid) {
+    const float l_run = l_acc[0];
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     const int orow = b * kChunk + qi;
 #pragma unroll
@@ -1096,7 +1121,8 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
   f32x4 o[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
@@ -1106,11 +1132,12 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
     for (int blk = ks; blk < nb; blk += KS)
       attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
-                 m_run, l_run, lane);
+                 m_run, l_acc, lane);
   }
 
   if constexpr (KS == 1) {
     if (rvalid) {
+      const float l_run = l_acc[0];
       const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
       const int orow = b * kChunk + qi;
 #pragma unroll
@@ -1126,7 +1153,7 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
     __syncthreads();
     if (lane < 16) {
       sM[qg][ks][lane] = m_run;
-      sL[qg][ks][lane] = l_run;
+      sL[qg][ks][lane] = l_acc[0];
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -1285,7 +1312,8 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   f32x4 o[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int r0 = 0; r0 < P; r0 += RK) {
     if (r0 > 0) {
       __syncthreads();
@@ -1295,12 +1323,12 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
     const int nb = min(NBLK, (P - r0 + kKB - 1) / kKB);
     for (int blk = w; blk < nb; blk += NW)
       attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
-                 m_run, l_run, lane);
+                 m_run, l_acc, lane);
   }
   __syncthreads();
   if (lane < 16) {
     sM[w][lane] = m_run;
-    sL[w][lane] = l_run;
+    sL[w][lane] = l_acc[0];
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m)
