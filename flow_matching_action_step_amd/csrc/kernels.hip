@@ -523,6 +523,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   p.bm = 64;
   p.rb = 4;
   p.cb = 1;
+  p.stages = 2;
   if (M <= 64) {
     p.kind = 0;
     p.ntiles_n = (N + 15) / 16;
@@ -773,12 +774,14 @@ static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The configuration in use: 128 x 128 tiles, eight waves of 32 x 64, a 2-stage ring
-// (64 KB of LDS, two workgroups per CU).  Measured on MI355X against 256-row tiles,
-// 3-stage rings and four-wave shapes, and against the register-staged tiled kernel,
-// for the four projections at M = 100 .. 6400: it was fastest or within 5 % everywhere
-// (gate/up at M = 3200: 30 us against 35-36 us).
-hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
+// Configurations: BM x 128 tiles of waves of 32 x 64 (eight waves at BM = 128, four at 64)
+// and an S-stage ring.  Measured with the weights cycling through a 250 MB footprint,
+// against 256-row tiles, four-wave 64 x 64 shapes and 3/4-stage rings: 128 rows and two
+// stages (64 KB of LDS, two workgroups per CU) for Q/K/V and gate/up everywhere (gate/up at
+// M = 3200: 29 us against 39 with a 4-stage ring); for o and down, whose 720 columns give few
+// tiles, a 4-stage ring up to M = 4800 (down at 3200: 21.8 against 24.1 us) and 64-row tiles
+// at M <= 2400 (down at 1600: 19.7 against 23.2).
+hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
   switch (em) {
     case E_QKV:
       if (!norm) return hipErrorInvalidValue;
@@ -788,6 +791,10 @@ hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s
       return launch_gemm_dma<E_SWIGLU, true, 128, 2, 2, 2>(a, s);
     case E_H_RESID:
       if (norm) return hipErrorInvalidValue;
+      if (p.stages == 4) {
+        if (p.bm == 64) return launch_gemm_dma<E_H_RESID, false, 64, 2, 2, 4>(a, s);
+        return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4>(a, s);
+      }
       return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
@@ -806,9 +813,9 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
     p.kind = 0; p.rb = rb; p.cb = cb;
     return p;
   };
-  auto big = [&]() {
+  auto big = [&](int bm = 128, int stages = 2) {
     GemmPlan b = p;
-    b.kind = 2;
+    b.kind = 2; b.bm = bm; b.stages = stages;
     return b;
   };
   if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
@@ -825,9 +832,16 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
     case E_SWIGLU:
       return M <= 600 ? skinny(2, 2) : big();
     case E_H_RESID:
-      if (K > 1024 && M <= 200) return skinny(2, 1);
-      if (M <= 400) return skinny(2, 2);
-      return M <= 2400 ? skinny(4, 2) : big();
+      if (K > 1024) {  // down
+        if (M <= 100) return skinny(2, 1);
+        if (M <= 200) return skinny(2, 2);
+        if (M <= 1000) return skinny(4, 2);
+        if (M <= 2400) return big(64, 4);
+      } else {  // o
+        if (M <= 400) return skinny(2, 2);
+        if (M <= 2400) return skinny(4, 2);
+      }
+      return M <= 4800 ? big(128, 4) : big();
     case E_ACTOUT:
       if (M <= 2400) return skinny(1, 1);
       return M <= 4800 ? skinny(4, 2) : plan_gemm(M, N, K);

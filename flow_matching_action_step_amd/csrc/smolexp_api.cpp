@@ -286,7 +286,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     if (plan.kind == 2) {
       if (am == A_NORM) g.K = kKPad;
       record(probe, plan, am, em, g);
-      return launch_gemm_big(em, am == A_NORM, g, s);
+      return launch_gemm_big(plan, em, am == A_NORM, g, s);
     }
     record(probe, plan, am, em, g);
     return launch_gemm(plan, am, em, g, s);
@@ -763,7 +763,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     const std::vector<smolexp_handle::Probe>& v = h->probes[kernel];
     const smolexp_handle::Probe& p = v[(size_t)i % v.size()];
     if (p.attn) return launch_attention(kernel == PR_ATTN_SELF, p.a, st);
-    if (p.plan.kind == 2) return launch_gemm_big(p.em, p.am == A_NORM, p.g, st);
+    if (p.plan.kind == 2) return launch_gemm_big(p.plan, p.em, p.am == A_NORM, p.g, st);
     return launch_gemm(p.plan, p.am, p.em, p.g, st);
   };
   hipGraphExec_t exec = nullptr;

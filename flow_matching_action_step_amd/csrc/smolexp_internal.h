@@ -142,13 +142,14 @@ struct GemmPlan {
   int bm;        // tiled: rows per tile (64 or 128)
   int rb;        // skinny: 16-row blocks per workgroup (4, 2 or 1: the rows split over 4 / rb workgroups)
   int cb;        // skinny: 16-column blocks per workgroup (1, 2 or 4)
+  int stages;    // pipelined: LDS ring depth (2 or 4); bm = tile rows (64 or 128)
   int ntiles_n;  // output tiles (workgroups) along N
 };
 GemmPlan plan_gemm(int M, int N, int K);
 
 // Large-M GEMM with an LDS-DMA ring (fp16 A, K % 64 == 0): E_QKV and E_SWIGLU on the
 // RMSNorm'd residual (norm = true: A = h16), E_H_RESID on a plain fp16 operand.
-hipError_t launch_gemm_big(EMode em, bool norm, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArgs& a, hipStream_t s);
 // The kernel and tiles for one projection of the loop (K = logical width).  kind 2 = the
 // pipelined GEMM, which reads RMSNorm'd operands over K = kKPad stored columns.
 GemmPlan plan_for(int M, int N, int K, AMode am, EMode em);
