@@ -883,7 +883,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t* p) {
 // scores (log2 domain); l_acc: running sum of the weights, accumulated on the
 // matrix cores (an all-ones operand against the weights, so it sums exactly
 // the bf16 weights that multiply V); every register holds it.
-template <int MODE>
+// Element (row, col) of a staged K or V block.  Padded layout: rows of kALD
+// elements.  Swizzled layout (SWZ, filled by direct global->LDS loads that
+// cannot pad): rows of 128 bytes whose 16-byte chunk c sits at c ^ (row % 8),
+// so the 16 rows one fragment read touches spread over the banks.
+template <bool SWZ>
+__device__ __forceinline__ const bf16_t* kv_at(const bf16_t* base, int row, int col) {
+  if constexpr (SWZ)
+    return reinterpret_cast<const bf16_t*>(reinterpret_cast<const char*>(base) + row * 128 +
+                                           ((((col >> 3) ^ row) & 7) << 4) + (col & 7) * 2);
+  else
+    return base + row * kALD + col;
+}
+
+template <int MODE, bool SWZ = false>
 __device__ __forceinline__ void attn_block_m(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
                                              int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
                                              f32x4& l_acc, int lane) {
@@ -895,7 +908,7 @@ __device__ __forceinline__ void attn_block_m(const bf16_t* sKb, const bf16_t* sV
     sc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint4 u = *reinterpret_cast<const uint4*>(sKb + (sub * 16 + (lane & 15)) * kALD + kk * 32 + (lane >> 4) * 8);
+      const uint4 u = *reinterpret_cast<const uint4*>(kv_at<SWZ>(sKb, sub * 16 + (lane & 15), kk * 32 + (lane >> 4) * 8));
       sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), qf[kk], sc[sub], 0, 0, 0);
     }
   }
@@ -950,8 +963,8 @@ __device__ __forceinline__ void attn_block_m(const bf16_t* sKb, const bf16_t* sV
     for (int m = 0; m < 4; ++m) {
       // V^T fragment: dims m*16 + (lane % 16), keys h2*32 + 4q .. +3 and +16 .. +19 (q = lane / 16)
       const int sl = lane & 15;
-      const bf16_t* vp = sVb + (h2 * 32 + 4 * (lane >> 4) + (sl >> 2)) * kALD + m * 16 + 4 * (sl & 3);
-      const s16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 16 * kALD);
+      const int vr = h2 * 32 + 4 * (lane >> 4) + (sl >> 2), vc = m * 16 + 4 * (sl & 3);
+      const s16x4 lo = lds_read_tr16(kv_at<SWZ>(sVb, vr, vc)), hi = lds_read_tr16(kv_at<SWZ>(sVb, vr + 16, vc));
       const s16x4 u[2] = {lo, hi};
       o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, u), pb, o[m], 0, 0, 0);
     }
@@ -967,13 +980,14 @@ __device__ __forceinline__ int block_mode(const uint8_t* kind, int lane) {
   return __ballot(k != 1u) != 0ull ? 1 : 0;
 }
 
+template <bool SWZ = false>
 __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb, const uint8_t* kind,
                                            int key0, int qi, const bf16x8* qf, f32x4* o, float& m_run,
                                            f32x4& l_acc, int lane) {
   const int mode = block_mode(kind, lane);
-  if (mode == 0) attn_block_m<0>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
-  else if (mode == 1) attn_block_m<1>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
-  else attn_block_m<2>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
+  if (mode == 0) attn_block_m<0, SWZ>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
+  else if (mode == 1) attn_block_m<1, SWZ>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
+  else attn_block_m<2, SWZ>(sKb, sVb, kind, key0, qi, qf, o, m_run, l_acc, lane);
 }
 
 // Stage keys r0 .. r0 + RK - 1 of one (query, KV head) into LDS: K rows,
@@ -1373,6 +1387,125 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   }
 }
 
+// Batches above 8: one workgroup per (64 query rows, KV head g, query b), as in
+// attn_kernel, with the 64-key blocks streamed through an S-stage LDS ring by
+// direct global->LDS loads (swizzled rows, kv_at<true>): while block j is
+// multiplied, the loads of blocks j+1 .. j+S-1 are in flight, so a block costs
+// about one barrier instead of one memory round trip.  The kinds of all keys
+// are staged once.  A block holding keys that are not attended (masked prefix
+// keys, or the clamped keys past the end) has their V rows zeroed in LDS before
+// use: their weights are 0, but 0 x NaN would not be.
+constexpr int kMaxKeys = 4096 + 64;  // max_prefix + the chunk, in whole blocks
+
+template <bool SELF, int S>
+__global__ __launch_bounds__(256) void attn_pipe_kernel(const AttnArgs a) {
+  constexpr int NT = 256, NW = 4, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
+  constexpr int LPW = STAGE / 1024 / NW;  // 1 KB load instructions per wave per stage
+  static_assert(LPW * NW * 1024 == STAGE && S >= 2, "whole load instructions per wave");
+  constexpr int WAITN = (S - 2) * LPW;    // this wave's loads still allowed in flight
+  constexpr int VMW = (WAITN & 15) | ((WAITN >> 4) << 14);
+  __shared__ __attribute__((aligned(1024))) char ring[S * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sKind[kMaxKeys];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = blockIdx.y, b = blockIdx.z, P = a.P;
+  const int NK = P + (SELF ? kChunk : 0), nblk = (NK + kKB - 1) / kKB;
+  const int rq = blockIdx.x * 64 + w * 16 + (lane & 15);
+  const bool rvalid = rq < 3 * kChunk;
+  const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
+  const int qi = rvalid ? rq % kChunk : 0;
+
+  // key kinds: 0 = none, 1 = valid prefix key, 2 = chunk key
+  const uint8_t* mk = a.mask + (size_t)b * P;
+  for (int j = tid; j < nblk * kKB; j += NT)
+    sKind[j] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+
+  // element offsets from pk: the V rows of the prefix, the chunk's K rows and their V rows
+  const size_t head = (size_t)b * kHKV + g;
+  const bf16_t* pk = a.pk + head * (size_t)P * kHD;
+  const ptrdiff_t pv_off = (a.pv + head * (size_t)P * kHD) - pk;
+  const ptrdiff_t ck_off = SELF ? (a.kc + head * kChunk * kHD) - pk : 0;
+  const ptrdiff_t cv_off = SELF ? (a.vc + head * kChunk * kHD) - pk : 0;
+  // Load instruction i of a stage (wave w issues i = w LPW .. w LPW + LPW - 1): part i / 8
+  // (K, then V), LDS rows 8 (i % 8) .. +7; lane l fills LDS row 8 (i % 8) + l / 8, chunk
+  // l % 8, i.e. global chunk (l % 8) ^ (row % 8) of that key.  Keys past the last are
+  // clamped to it (kind 0).  Blocks past the last reload the last one (never read).
+  auto issue = [&](int blk, int stage) {
+    const int bb = min(blk, nblk - 1);
+    char* base = ring + stage * STAGE;
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const int i = w * LPW + t, part = i >> 3;
+      const int row = (i & 7) * 8 + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+      const int key = min(bb * kKB + row, NK - 1);
+      const bool pre = !SELF || key < P;
+      const ptrdiff_t off = (pre ? (part ? pv_off : 0) + (ptrdiff_t)key * kHD
+                                 : (part ? cv_off : ck_off) + (ptrdiff_t)(key - P) * kHD) + chunk * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pk + off),
+                                       (__attribute__((address_space(3))) void*)(base + part * BLK_BYTES + (i & 7) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  bf16x8 qf[2];
+  {
+    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * kChunk + qi) * kHD + (lane >> 4) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  f32x4 o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st);
+  for (int j = 0; j < nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(VMW | (7 << 4) | (0 << 8));  // this wave's loads of block j (and LDS writes) done
+    __builtin_amdgcn_s_barrier();                           // everyone's; block j - 1 finished everywhere
+    const uint8_t* kb = sKind + j * kKB;
+    const bf16_t* sK = reinterpret_cast<const bf16_t*>(ring + (j % S) * STAGE);
+    const bf16_t* sV = sK + BLK_BYTES / 2;
+    if (__ballot(kb[lane] == 0u) != 0ull) {  // uniform: some keys of this block are not attended
+      for (int u = tid; u < kKB * 8; u += NT)
+        if (kb[u >> 3] == 0u)
+          *reinterpret_cast<uint4*>(ring + (j % S) * STAGE + BLK_BYTES + (u >> 3) * 128 + (u & 7) * 16) = make_uint4(0, 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(VMW | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+    }
+    issue(j + S - 1, (j + S - 1) % S);  // into the stage block j - 1 used
+    attn_block<true>(sK, sV, kb, j * kKB - P, qi, qf, o, m_run, l_acc, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) loads land before the LDS is released
+
+  if (rvalid) {
+    const float l_run = l_acc[0];
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    const int orow = b * kChunk + qi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      union { half_t h[4]; uint2 u; } pk4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
+      *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
+    }
+  }
+}
+
+// Measured at P = 257 (graph replay): the ring beats one block per round up to batch 32
+// (batch 16: self 8.3 against 10.0 us with three stages, cross 7.1 against 8.1 with two);
+// from batch 64 on, attn_kernel's smaller footprint keeps more waves per SIMD and wins
+// (18.8 against 21.3 us).
+template <bool SELF>
+static void launch_pipe(const AttnArgs& a, hipStream_t s) {
+  if constexpr (SELF) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), dim3(3, kHKV, a.B), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_pipe_kernel<false, 2>), dim3(3, kHKV, a.B), dim3(256), 0, s, a);
+}
+
 static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
   const int nblk = min(5, max(2, (a.P + kKB - 1) / kKB));
   const dim3 grid((kChunk + 15) / 16, kHQ, a.B), block(512);
@@ -1396,6 +1529,9 @@ hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
   if (a.B <= 8) {
     if (self_layer) launch_ksplit<true>(a, s);
     else launch_ksplit<false>(a, s);
+  } else if (a.B <= 32) {
+    if (self_layer) launch_pipe<true>(a, s);
+    else launch_pipe<false>(a, s);
   } else {
     const dim3 grid(3, kHKV, a.B);
     if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 1>), grid, block, 0, s, a);

@@ -122,6 +122,17 @@ def test_denoise_16_layers_batch16_variable_prefix(ex16):
     compare(gpu, run_oracle(ex16, wl, q), q, wl["noise"], "expert16_b16_pvar241")
 
 
+def test_denoise_16_layers_batch24_variable_prefix(ex16):
+    # 1200 chunk rows: the K-split GEMM at its largest tiles for Q/K/V and o, the pipelined
+    # GEMM with 64-row tiles and a 4-stage ring for down, the streamed-ring attention
+    _say("denoise expert16_b16_pvar241 at batch 24")
+    wl = synth.make_workload("expert16_b16_pvar241", batch=24, with_weights=False)
+    gpu = run_gpu(ex16, to_device(wl))
+    order = np.argsort(wl["lengths"])
+    q = sorted({int(order[0]), int(order[-1]), 17})
+    compare(gpu, run_oracle(ex16, wl, q), q, wl["noise"], "expert16_b24_pvar241")
+
+
 def test_denoise_16_layers_batch64(ex16):
     _say("denoise expert16_b64_p257 (sampled queries)")
     wl = synth.make_workload("expert16_b64_p257", with_weights=False)
