@@ -853,10 +853,10 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
 // ----------------------------------------------------------------------------
 // Block-masked grouped-query attention
 // ----------------------------------------------------------------------------
-// One workgroup per (query tile of 64 rows, KV head g, query b).  The 150
-// query rows of KV head g are its 3 query heads x 50 chunk rows.  Keys are the
-// prefix tokens 0..P-1 (valid where the mask says so) followed, in self layers,
-// by the 50 chunk keys, of which row i sees j <= i.  Scores are computed
+// The 150 query rows of KV head g are its 3 query heads x 50 chunk rows; a
+// workgroup takes groups of 16 of them (one wave's tile) of one (query, KV
+// head).  Keys are the prefix tokens 0..P-1 (valid where the mask says so)
+// followed, in self layers, by the 50 chunk keys, of which row i sees j <= i.  Scores are computed
 // transposed (S^T = K Q^T) so that each lane owns one query row; the output is
 // accumulated transposed as well (O^T += V^T P^T).  K and V are staged in LDS
 // row-major ([key][dim]); the V^T operand comes from transposing LDS reads.
@@ -1050,67 +1050,6 @@ __device__ __forceinline__ void attn_stage(const AttnArgs& a, int b, int g, int 
   AttnStage<SELF, RK, NT> st;
   st.issue(a, b, g, r0);
   st.store(sK, sV, sKind);
-}
-
-// NBLK key blocks are staged per round: all of their loads are issued before
-// the first is stored, so a round costs one memory round trip.  Small batches
-// stage five blocks (320 keys: a whole prefix plus the chunk), large batches
-// one block per round and more workgroups per CU.
-template <bool SELF, int NBLK>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  constexpr int RK = NBLK * kKB;     // keys per round
-  __shared__ __attribute__((aligned(16))) bf16_t sK[RK * kALD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[RK * kALD];
-  __shared__ __attribute__((aligned(16))) uint8_t sKind[RK];  // 0 = no key, 1 = valid prefix key, 2 = chunk key
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int P = a.P;
-  const int rq = blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const bool rvalid = rq < 3 * kChunk;
-  const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
-  const int qi = rvalid ? rq % kChunk : 0;
-
-  bf16x8 qf[2];
-  {
-    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * kChunk + qi) * kHD + (lane >> 4) * 8;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  f32x4 o[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int NK = P + (SELF ? kChunk : 0);
-  for (int r0 = 0; r0 < NK; r0 += RK) {
-    __syncthreads();  // the previous round's LDS reads are done
-    attn_stage<SELF, RK>(a, b, g, r0, sK, sV, sKind);
-    __syncthreads();
-
-    const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
-    for (int blk = 0; blk < nb; ++blk)
-      attn_block(sK + blk * kKB * kALD, sV + blk * kKB * kALD, sKind + blk * kKB, r0 + blk * kKB - P, qi, qf, o,
-                 m_run, l_acc, lane);
-  }
-
-  if (rvalid) {
-    const float l_run = l_acc[0];
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    const int orow = b * kChunk + qi;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      union { half_t h[4]; uint2 u; } pk4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
-      *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
-    }
-  }
 }
 
 // Small batches: a workgroup takes QG groups of 16 query rows of one KV head
@@ -1387,18 +1326,21 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   }
 }
 
-// Batches above 8: one workgroup per (64 query rows, KV head g, query b), as in
-// attn_kernel, with the 64-key blocks streamed through an S-stage LDS ring by
+// Batches above 8: one workgroup per (64 query rows, KV head g, query b); its
+// four waves take 16 rows each (the 150 rows of KV head g are its 3 query heads
+// x 50 chunk rows).  The 64-key blocks stream through an S-stage LDS ring by
 // direct global->LDS loads (swizzled rows, kv_at<true>): while block j is
 // multiplied, the loads of blocks j+1 .. j+S-1 are in flight, so a block costs
-// about one barrier instead of one memory round trip.  The kinds of all keys
+// about one barrier instead of one memory round trip (staging one block per
+// round through registers, as the small-batch kernels do, cost half the time of
+// a batch-64 launch: 19 us with it, 10 with the staging loads switched off).  The kinds of all keys
 // are staged once.  A block holding keys that are not attended (masked prefix
 // keys, or the clamped keys past the end) has their V rows zeroed in LDS before
 // use: their weights are 0, but 0 x NaN would not be.
 constexpr int kMaxKeys = 4096 + 64;  // max_prefix + the chunk, in whole blocks
 
-template <bool SELF, int S>
-__global__ __launch_bounds__(256) void attn_pipe_kernel(const AttnArgs a) {
+template <bool SELF, int S, int MINB = 1>
+__global__ __launch_bounds__(256, MINB) void attn_pipe_kernel(const AttnArgs a) {
   constexpr int NT = 256, NW = 4, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
   constexpr int LPW = STAGE / 1024 / NW;  // 1 KB load instructions per wave per stage
   static_assert(LPW * NW * 1024 == STAGE && S >= 2, "whole load instructions per wave");
@@ -1496,14 +1438,16 @@ __global__ __launch_bounds__(256) void attn_pipe_kernel(const AttnArgs a) {
   }
 }
 
-// Measured at P = 257 (graph replay): the ring beats one block per round up to batch 32
-// (batch 16: self 8.3 against 10.0 us with three stages, cross 7.1 against 8.1 with two);
-// from batch 64 on, attn_kernel's smaller footprint keeps more waves per SIMD and wins
-// (18.8 against 21.3 us).
+// Measured at P = 257 (graph replay) against staging one block per round through
+// registers: batch 16 self 8.4 against 10.1 us (three stages), cross 7.1 against 8.1 (two);
+// from batch 32 on two stages with registers capped at 128 (four waves per SIMD, the
+// footprint of the register-staged kernel): batch 64 self 18.5 against 18.9, batch 128
+// 32.3 against 32.6.
 template <bool SELF>
 static void launch_pipe(const AttnArgs& a, hipStream_t s) {
-  if constexpr (SELF) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), dim3(3, kHKV, a.B), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_pipe_kernel<false, 2>), dim3(3, kHKV, a.B), dim3(256), 0, s, a);
+  const dim3 grid(3, kHKV, a.B), block(256);
+  if (SELF && a.B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), grid, block, 0, s, a);
 }
 
 static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
@@ -1520,7 +1464,6 @@ static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
 bool use_cross_q(int B) { return B <= kCrossQMaxBatch; }
 
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
-  const dim3 block(256);
   if (!self_layer && a.wq) {  // cross layer with its query projection
     if (!use_cross_q(a.B) || !a.h16 || !a.ropeq || a.ldw != kKPad) return hipErrorInvalidValue;
     launch_cross_q(a, s);
@@ -1529,13 +1472,9 @@ hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
   if (a.B <= 8) {
     if (self_layer) launch_ksplit<true>(a, s);
     else launch_ksplit<false>(a, s);
-  } else if (a.B <= 32) {
+  } else {
     if (self_layer) launch_pipe<true>(a, s);
     else launch_pipe<false>(a, s);
-  } else {
-    const dim3 grid(3, kHKV, a.B);
-    if (self_layer) hipLaunchKernelGGL((attn_kernel<true, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<false, 1>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
