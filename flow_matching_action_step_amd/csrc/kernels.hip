@@ -1326,9 +1326,9 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   }
 }
 
-// Batches above 8: one workgroup per (64 query rows, KV head g, query b); its
-// four waves take 16 rows each (the 150 rows of KV head g are its 3 query heads
-// x 50 chunk rows).  The 64-key blocks stream through an S-stage LDS ring by
+// Batches above 8: one workgroup per (16 NW query rows, KV head g, query b);
+// its NW waves take 16 rows each (the 150 rows of KV head g are its 3 query
+// heads x 50 chunk rows; NW = 10 takes them all).  The 64-key blocks stream through an S-stage LDS ring by
 // direct global->LDS loads (swizzled rows, kv_at<true>): while block j is
 // multiplied, the loads of blocks j+1 .. j+S-1 are in flight, so a block costs
 // about one barrier instead of one memory round trip (staging one block per
@@ -1339,11 +1339,12 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
 // use: their weights are 0, but 0 x NaN would not be.
 constexpr int kMaxKeys = 4096 + 64;  // max_prefix + the chunk, in whole blocks
 
-template <bool SELF, int S, int MINB = 1>
-__global__ __launch_bounds__(256, MINB) void attn_pipe_kernel(const AttnArgs a) {
-  constexpr int NT = 256, NW = 4, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
-  constexpr int LPW = STAGE / 1024 / NW;  // 1 KB load instructions per wave per stage
-  static_assert(LPW * NW * 1024 == STAGE && S >= 2, "whole load instructions per wave");
+template <bool SELF, int S, int MINB = 1, int NW = 4>
+__global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs a) {
+  constexpr int NT = 64 * NW, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
+  constexpr int NLOAD = STAGE / 1024;              // 1 KB load instructions per stage
+  constexpr int LPW = (NLOAD + NW - 1) / NW;      // per wave (the last waves may issue fewer)
+  static_assert(S >= 2, "ring depth");
   constexpr int WAITN = (S - 2) * LPW;    // this wave's loads still allowed in flight
   constexpr int VMW = (WAITN & 15) | ((WAITN >> 4) << 14);
   __shared__ __attribute__((aligned(1024))) char ring[S * STAGE];
@@ -1352,7 +1353,7 @@ __global__ __launch_bounds__(256, MINB) void attn_pipe_kernel(const AttnArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = blockIdx.y, b = blockIdx.z, P = a.P;
   const int NK = P + (SELF ? kChunk : 0), nblk = (NK + kKB - 1) / kKB;
-  const int rq = blockIdx.x * 64 + w * 16 + (lane & 15);
+  const int rq = blockIdx.x * (16 * NW) + w * 16 + (lane & 15);
   const bool rvalid = rq < 3 * kChunk;
   const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
   const int qi = rvalid ? rq % kChunk : 0;
@@ -1378,6 +1379,7 @@ __global__ __launch_bounds__(256, MINB) void attn_pipe_kernel(const AttnArgs a) 
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
       const int i = w * LPW + t, part = i >> 3;
+      if (NLOAD % NW != 0 && i >= NLOAD) break;  // uniform per wave
       const int row = (i & 7) * 8 + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
       const int key = min(bb * kKB + row, NK - 1);
       const bool pre = !SELF || key < P;
@@ -1439,14 +1441,21 @@ __global__ __launch_bounds__(256, MINB) void attn_pipe_kernel(const AttnArgs a) 
 }
 
 // Measured at P = 257 (graph replay) against staging one block per round through
-// registers: batch 16 self 8.4 against 10.1 us (three stages), cross 7.1 against 8.1 (two);
-// from batch 32 on two stages with registers capped at 128 (four waves per SIMD, the
-// footprint of the register-staged kernel): batch 64 self 18.5 against 18.9, batch 128
-// 32.3 against 32.6.
+// registers: batch 16 self 8.4 against 10.1 us (four waves, three stages), cross 7.1
+// against 8.1 (two stages).  Ten waves (all 150 rows of a KV head in one workgroup, so
+// each block is loaded once instead of three times) win where 5 B workgroups fill the
+// CUs in whole rounds: batch 32 self 9.6 against 11.4 us, batch 128 28.6 against 32.2;
+// at batch 64 (320 workgroups on 256 CUs) four waves with registers capped at 128 (four
+// waves per SIMD) stay ahead, 18.5 against 18.9 (the register-staged kernel: 18.9).
 template <bool SELF>
 static void launch_pipe(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(3, kHKV, a.B), block(256);
-  if (SELF && a.B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), grid, block, 0, s, a);
+  const int B = a.B;
+  if ((B > 16 && B <= 48) || B >= 96) {
+    hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 1, 10>), dim3(1, kHKV, B), dim3(640), 0, s, a);
+    return;
+  }
+  const dim3 grid(3, kHKV, B), block(256);
+  if (SELF && B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), grid, block, 0, s, a);
 }
 
