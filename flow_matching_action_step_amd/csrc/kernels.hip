@@ -1489,9 +1489,10 @@ hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------------------
-// Per-call prologue: the time vectors W_t1[:, 720:] e(t_k) + b_t1 for every
-// step, the RoPE rows of every chunk row (position = the query's number of
-// valid prefix tokens + i), and x <- the caller's x.
+// Prologue: the time vectors W_t1[:, 720:] e(t_k) + b_t1 for n_t flow times
+// (the schedule's once, when the weights are loaded; one per velocity call),
+// and per call the RoPE rows of every chunk row (position = the query's number
+// of valid prefix tokens + i) and x <- the caller's x.
 // ----------------------------------------------------------------------------
 constexpr int kTimeRowsPerBlock = 16;
 constexpr int kTimeBlocks = kD / kTimeRowsPerBlock;  // 45
@@ -1500,7 +1501,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
   __shared__ float se[kD];
   const int tid = threadIdx.x;
   const int nMaskBlocks = (a.B + 3) / 4;
-  if (blockIdx.x < kTimeBlocks) {
+  const int timeBlocks = a.n_t > 0 ? kTimeBlocks : 0;
+  if ((int)blockIdx.x < timeBlocks) {
     // Sinusoidal time embedding: sin(2 pi t / p_i) for i < 360, cos(...) after,
     // periods geometric from p_min to p_max (1/p_i precomputed in fp64).  The
     // angle is reduced to [0, 2 pi) in fp64, then sin/cos run in fp32.
@@ -1542,9 +1544,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
       s += __shfl_xor(s, 8);
       if (part == 0) a.cvec[(size_t)k * kD + j] = s * a.s_t1 + a.b_t1[j];
     }
-  } else if ((int)blockIdx.x < kTimeBlocks + nMaskBlocks) {
+  } else if ((int)blockIdx.x < timeBlocks + nMaskBlocks) {
     // query b: its valid prefix count n, then the RoPE rows of chunk positions n .. n + 49
-    const int b = (blockIdx.x - kTimeBlocks) * 4 + (tid >> 6), lane = tid & 63;
+    const int b = (blockIdx.x - timeBlocks) * 4 + (tid >> 6), lane = tid & 63;
     if (b < a.B) {
       int c = 0;
       for (int j = lane; j < a.P; j += 64) c += a.mask[(size_t)b * a.P + j] != 0;
@@ -1554,7 +1556,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
         a.ropeq[((size_t)b * kChunk) * (kHD / 2) + i] = a.rope[(size_t)c * (kHD / 2) + i];
     }
   } else {
-    const int first = kTimeBlocks + nMaskBlocks;
+    const int first = timeBlocks + nMaskBlocks;
     const int n = a.B * kChunk * kAD;
     for (int i = (blockIdx.x - first) * 256 + tid; i < n; i += (gridDim.x - first) * 256) a.x[i] = a.x_in[i];
   }
@@ -1564,7 +1566,9 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
   const int nMaskBlocks = (a.B + 3) / 4;
   const int nCopy = (a.B * kChunk * kAD + 255) / 256;
   const int copyBlocks = nCopy < 64 ? nCopy : 64;
-  hipLaunchKernelGGL(prologue_kernel, dim3(kTimeBlocks + nMaskBlocks + copyBlocks), dim3(256), 0, s, a);
+  const int blocks = (a.n_t > 0 ? kTimeBlocks : 0) + nMaskBlocks + copyBlocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -241,6 +241,9 @@ CallKey key_of(const CallArgs& c) {
 int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
+  // time vectors: the schedule's were computed when the weights were loaded; a velocity
+  // call computes its own (one t) into the row after them
+  float* const cvec = c.velocity ? h->cvec + (size_t)kMaxSteps * kD : h->cvec;
   hipError_t e;
   if (record_probes) {
     for (int i = 0; i < PR_COUNT; ++i) h->probes[i].clear();
@@ -252,8 +255,8 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   PrologueArgs pa;
   memset(&pa, 0, sizeof(pa));
   pa.B = B;
-  pa.n_t = n_t;
-  for (int k = 0; k < n_t; ++k) pa.t[k] = c.velocity ? c.t_single : h->ts[k];
+  pa.n_t = c.velocity ? 1 : 0;
+  pa.t[0] = c.t_single;
   pa.mask = c.mask;
   pa.P = P;
   pa.rope = h->rope;
@@ -263,7 +266,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   pa.w_t1e = h->w_t1e;
   pa.s_t1 = h->w_t1.scale;
   pa.b_t1 = h->b_t1;
-  pa.cvec = h->cvec;
+  pa.cvec = cvec;
   pa.inv_period = h->inv_period;
   if ((e = launch_prologue(pa, s)) != hipSuccess) return hip_fail(h, e, "prologue launch");
 
@@ -294,7 +297,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t { return gemm(probe, A_NORM, em, g); };
 
   for (int k = 0; k < n_t; ++k) {
-    const float t = pa.t[k];
+    const float t = c.velocity ? c.t_single : h->ts[k];
     GemmArgs g;
     memset(&g, 0, sizeof(g));
     g.M = M;
@@ -312,7 +315,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     // time MLP: s = SiLU(W_t1[:, :720] y + (W_t1[:, 720:] e(t) + b_t1));  h = W_t2 s + b_t2
     GemmArgs gt = g;
     gt.N = kD; gt.K = kD; gt.A = h->y16; gt.lda = kD;
-    gt.W = h->w_t1.w; gt.ldw = h->w_t1.ld; gt.w_scale = h->w_t1.scale; gt.bias = h->cvec + (size_t)k * kD;
+    gt.W = h->w_t1.w; gt.ldw = h->w_t1.ld; gt.w_scale = h->w_t1.scale; gt.bias = cvec + (size_t)k * kD;
     gt.out16 = h->s16; gt.ldo = kD;
     if ((e = gemm(-1, A_F16, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
 
@@ -511,7 +514,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mpad * kD * 4);
-  const size_t o_cv = take((size_t)kMaxSteps * kD * 4);
+  const size_t o_cv = take((size_t)(kMaxSteps + 1) * kD * 4);  // the schedule's time vectors + one for velocity calls
   const size_t o_y = take(Mpad * kD * 2), o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
   const size_t o_u = take(Mpad * kFFN * 2), o_h16 = take(Mpad * kKPad * 2);
   const size_t o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
@@ -692,6 +695,21 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     layers[l].down.w = (half_t*)(db + o_dn[l]);
   }
   h->layers = layers;
+  // the time vectors of the schedule: W_t1[:, 720:] e(t_k) + b_t1 depends on the weights
+  // and the fixed flow times only, so it is computed here once, not in every call
+  PrologueArgs pa;
+  memset(&pa, 0, sizeof(pa));
+  pa.B = 0;
+  pa.n_t = h->cfg.n_steps;
+  for (int k = 0; k < pa.n_t; ++k) pa.t[k] = h->ts[k];
+  pa.w_t1e = h->w_t1e;
+  pa.s_t1 = h->w_t1.scale;
+  pa.b_t1 = h->b_t1;
+  pa.cvec = h->cvec;
+  pa.inv_period = h->inv_period;
+  e = launch_prologue(pa, h->cap);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
+  if (e != hipSuccess) return hip_fail(h, e, "time vectors");
   h->loaded = true;
   return SMOLEXP_OK;
 }

@@ -118,8 +118,8 @@ constexpr int kCrossQMaxBatch = 8;
 bool use_cross_q(int B);  // the cross layers of this batch size fold the Q projection into attention
 
 struct PrologueArgs {
-  int B;
-  int n_t;                 // number of flow times
+  int B;                   // queries (0: time vectors only)
+  int n_t;                 // number of flow times whose time vectors are computed (0: none)
   float t[kMaxSteps];
   const uint8_t* mask;     // [B][P]
   int P;
