@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the SmolVLA action-expert denoising loop on one MI355X.
 
-One "step" is one smolexp_denoise call: the whole 10-step Euler loop of the
-16-layer expert over one batch of synthetic inputs already resident in HBM.
+One "step" is one smolexp_denoise call: the whole Euler loop (10 steps, or
+--n-steps) of the 16-layer expert over one batch of synthetic inputs already
+resident in HBM.
 Prints one JSON line: chunks/s, ms per call, the roofline of the dominant
 kernel (timed live with HIP events on the library's stream), the whole-loop
 roofline, and the CPU oracle timed on the host as a baseline.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--n-steps N]
 """
 import argparse
 import json
@@ -144,7 +145,7 @@ def loop_algorithmic(L, B, lengths, n_steps):
     return n_steps * (wbytes + kvbytes), n_steps * flops
 
 
-def cpu_baseline(wl, min_seconds, max_seconds):
+def cpu_baseline(wl, n_steps, min_seconds, max_seconds):
     """The float64 numpy oracle on the host, on whole chunks of the workload's first queries."""
     import numpy as np
     import threadpoolctl
@@ -155,7 +156,7 @@ def cpu_baseline(wl, min_seconds, max_seconds):
     done, t0 = 0, time.perf_counter()
     while True:
         b = done % B
-        oracle.denoise_batch(W, cfg, wl["prefix_kv"], wl["mask"], wl["noise"], n_steps=10,
+        oracle.denoise_batch(W, cfg, wl["prefix_kv"], wl["mask"], wl["noise"], n_steps=n_steps,
                              prev=wl["prev_actions"], d=wl["overwrite_rows"], queries=[b])
         done += 1
         el = time.perf_counter() - t0
@@ -163,7 +164,7 @@ def cpu_baseline(wl, min_seconds, max_seconds):
             break
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {"value": done / el, "unit": "chunks/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} whole 10-step chunk(s) of the first {min(done, B)} quer(ies), {el:.1f} s, "
+            "sample": f"{done} whole {n_steps}-step chunk(s) of the first {min(done, B)} quer(ies), {el:.1f} s, "
                       f"float64 numpy, {threads} BLAS thread(s), host {os.cpu_count()} logical CPUs"}
 
 
@@ -173,6 +174,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--n-steps", type=int, default=10, help="Euler steps per chunk (dt = -1/n)")
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -197,7 +199,8 @@ def main():
 
     wl = synth.make_workload(args.workload)
     L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
-    cfg = fm.smolexp_default_config(n_layers=L, max_batch=B, max_prefix=P, use_graphs=0 if args.no_graphs else 1)
+    cfg = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps, max_batch=B, max_prefix=P,
+                                    use_graphs=0 if args.no_graphs else 1)
     h = fm.smolexp_create(cfg, 0)
     fm.smolexp_load_weights(h, synth.pack_weights(wl["weights"], L))
     kv = torch.from_numpy(np.ascontiguousarray(wl["prefix_kv"]).view(np.int16)).cuda()
@@ -257,7 +260,7 @@ def main():
             "event_ms_per_call": ev_ms / args.steps, "replay_us_per_call": loop_us}
 
     line = {
-        "metric": "action chunks/sec (50x32, 10 Euler steps) + ms/chunk at B=1; % HBM/MFMA roofline",
+        "metric": f"action chunks/sec (50x32, {cfg.n_steps} Euler steps) + ms/chunk at B=1; % HBM/MFMA roofline",
         "value": B * args.steps / wall,
         "unit": "chunks/s",
         "n_gpus": 1,
@@ -287,7 +290,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, 3 * args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, cfg.n_steps, args.cpu_seconds, 3 * args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -133,15 +133,17 @@ __device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { ret
 // The blocked outputs (fp16 activations, the fp32 residual and its fp16 copy)
 // are written with 16 consecutive lanes on 16 consecutive rows of one column
 // chunk, i.e. contiguous runs of 256 (128) bytes per store.
-// PRE (one work unit per thread, as in the M <= 64 kernel): the unit's global
-// inputs were loaded at kernel start into pre[] (E_QKV: the 16 cos/sin values
-// of a rotated block; E_H_RESID: the 4 residual values).
+// PRE: the global inputs of the thread's units were loaded at kernel start into
+// pre[] (E_QKV, one unit per thread: the 16 cos/sin values of a rotated block;
+// E_H_RESID, one row block per wave: the residual values of chunk t in pre[t],
+// BN / 16 of them).
 template <int EM, int BM, int BN, int LDC, int NT, bool PRE = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0,
                                               const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0, "rows inside one wave");
-  static_assert(!PRE || (BM * NB <= NT && NB <= 4 && BM / 16 <= NT / 64), "PRE: the units of one thread fit pre[]");
+  static_assert(!PRE || EM != E_QKV || (BM * NB <= NT && NB <= 4), "PRE: one E_QKV unit per thread");
+  static_assert(!PRE || EM != E_H_RESID || BM / 16 <= NT / 64, "PRE: one E_H_RESID row block per wave");
   const int M = a.M, N = a.N;
   if constexpr (EM == E_QKV) {
     // Work unit = (row, 16-column block): the block is 8 rotation pairs of one Q/K
@@ -630,6 +632,8 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 // s_waitcnt vmcnt(n) + s_barrier, not __syncthreads (whose fence would wait
 // for every load in flight).
 constexpr int kBigBN = 128, kBigBK = 64;
+// Column groups of the tile -> XCD map (the rows are cut into 8 / GC groups).
+__host__ __device__ constexpr int tile_col_groups(int em) { return em == E_SWIGLU ? 4 : 1; }
 
 template <int EM, bool NORM, int BM, int FMW, int WN, int S>
 __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const GemmArgs a) {
@@ -646,13 +650,48 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WN, wn = w % WN;
   const int M = a.M, N = a.N, K = a.K;
-  const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN, T = nM * nN;
-  const int per = (T + 7) / 8;
-  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (tile >= T) return;  // uniform per workgroup, before any barrier
-  const int mt = tile / nN, nt = tile % nN;
+  const int nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN;
+  // Tile -> XCD (workgroup i runs on XCD i % 8; j = i / 8 indexes that XCD's tiles).  GC = 1:
+  // XCD x takes the x-th eighth of the tiles in row-major order.  GC > 1: the tile grid is
+  // cut into 8 / GC row groups x GC column groups, one per XCD, each walked row by row;
+  // gate/up (N = 4096) takes column quarters, so one XCD's L2 serves a 1.6 MB quarter of the
+  // weights instead of streaming all 6.3 MB per row band.  Returns are uniform per
+  // workgroup and come before any barrier.
+  constexpr int GC = tile_col_groups(EM), GR = 8 / GC;
+  const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  int mt, nt;
+  if constexpr (GC == 1) {
+    const int T = nM * nN, tile = xcd * ((T + 7) / 8) + j;
+    if (tile >= T) return;
+    mt = tile / nN;
+    nt = tile % nN;
+  } else {
+    const int cg = xcd % GC, rg = xcd / GC;
+    const int c_lo = cg * nN / GC, c_hi = (cg + 1) * nN / GC, r_lo = rg * nM / GR, r_hi = (rg + 1) * nM / GR;
+    const int cw = c_hi - c_lo;
+    if (cw <= 0 || j >= cw * (r_hi - r_lo)) return;
+    mt = r_lo + j / cw;
+    nt = c_lo + j % cw;
+  }
   const int m0 = mt * BM, n0 = nt * BN;
   const int nk = K / BK;
+  // E_H_RESID: the residual values this thread adds in the epilogue (its unit mapping: lane
+  // r + 16 p of wave w owns row m0 + 16 w + r, columns n0 + 4 (p + 4 t)), loaded now so that
+  // their latency hides behind the main loop.  Issued before the ring, they are the oldest
+  // loads and the ring's vmcnt waits stay exact.  Only with the 4-stage ring, whose LDS
+  // holds one workgroup per CU anyway: the 32 registers would halve the 2-stage ring's
+  // occupancy (two workgroups per CU, 96 -> 132 VGPRs).
+  constexpr bool PRE = EM == E_H_RESID && S > 2;
+  float4 pre[PRE ? BN / 16 : 1];
+  if constexpr (PRE) {
+    static_assert(BM / 16 <= NW, "one row block per wave");
+    const int row = m0 + w * 16 + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      const int col = n0 + ((lane >> 4) + 4 * t) * 4;
+      if (w < BM / 16 && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+    }
+  }
   // NORM: A is fp16(h) unnormalised; each wave accumulates A A^T of its rows on the
   // matrix cores (row sums of squares on the diagonal), and 1/rms of each row scales the
   // finished sums.
@@ -762,15 +801,17 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
       for (int fn = 0; fn < FN; ++fn) sC[rl * LDC + (wn * FN + fn) * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
   __syncthreads();
-  epilogue_tile<EM, BM, BN, LDC, 64 * NW>(a, sC, m0, n0);
+  epilogue_tile<EM, BM, BN, LDC, 64 * NW, PRE>(a, sC, m0, n0, pre);
 }
 
 template <int EM, bool NORM, int BM, int FMW, int WN, int S>
 static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
-  constexpr int NT = 64 * (BM / (16 * FMW)) * WN;
-  const int T = ((a.M + BM - 1) / BM) * ((a.N + kBigBN - 1) / kBigBN);
+  constexpr int NT = 64 * (BM / (16 * FMW)) * WN, GC = tile_col_groups(EM), GR = 8 / GC;
+  const int nM = (a.M + BM - 1) / BM, nN = (a.N + kBigBN - 1) / kBigBN;
   if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S>), dim3(8 * ((T + 7) / 8)), dim3(NT), 0, s, a);
+  // every XCD gets as many workgroups as its largest share of tiles
+  const int per = GC == 1 ? (nM * nN + 7) / 8 : ((nN + GC - 1) / GC) * ((nM + GR - 1) / GR);
+  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S>), dim3(8 * per), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -25,6 +25,16 @@ class Expert:
         self.W = oracle.decode_weights(self.named) if with_oracle else None
         self.ocfg = oracle.ExpertConfig(n_layers=n_layers)
 
+    def sibling(self, n_steps, max_batch=4, max_prefix=256):
+        """Another handle on the same weights with a different number of Euler steps."""
+        e = object.__new__(Expert)
+        e.cfg = fm.smolexp_default_config(n_layers=self.cfg.n_layers, n_steps=n_steps, max_batch=max_batch,
+                                          max_prefix=max_prefix, use_graphs=self.cfg.use_graphs)
+        e.named, e.W, e.ocfg = self.named, self.W, self.ocfg
+        e.h = fm.smolexp_create(e.cfg, 0)
+        fm.smolexp_load_weights(e.h, synth.pack_weights(self.named, self.cfg.n_layers))
+        return e
+
     def close(self):
         if self.h is not None:
             fm.smolexp_destroy(self.h)

@@ -112,6 +112,19 @@ def test_denoise_16_layers_batch1(ex16):
     compare(gpu, run_oracle(ex16, wl, [0]), [0], wl["noise"], "expert16_b1_p177")
 
 
+def test_denoise_16_layers_four_steps(ex16):
+    # the step-count variant (dt = -1/4) on the 16-layer expert, as `bench.py --n-steps 4` runs it
+    _say("denoise expert16_b1_p177 with 4 Euler steps")
+    ex = ex16.sibling(4)
+    try:
+        wl = synth.make_workload("expert16_b1_p177", batch=2, with_weights=False)
+        gpu = run_gpu(ex, to_device(wl))
+        assert gpu["vel"].shape[0] == 4
+        compare(gpu, run_oracle(ex, wl, [0, 1]), [0, 1], wl["noise"], "expert16_b1_p177 n=4")
+    finally:
+        ex.close()
+
+
 def test_denoise_16_layers_batch16_variable_prefix(ex16):
     _say("denoise expert16_b16_pvar241")
     wl = synth.make_workload("expert16_b16_pvar241", with_weights=False)
