@@ -1392,9 +1392,17 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
   __shared__ __attribute__((aligned(16))) uint8_t sKind[kMaxKeys];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = blockIdx.y, b = blockIdx.z, P = a.P;
+  // One-dimensional grid: workgroup i runs on XCD i % 8, and the RG row groups of one
+  // (query, KV head) unit u get the same i % 8, so they stage the same K/V blocks through
+  // one L2 (fetched from memory once, not once per row group).  The return is uniform per
+  // workgroup and comes before any barrier.
+  constexpr int RG = (3 * kChunk + 16 * NW - 1) / (16 * NW);
+  const int xcd = (int)(blockIdx.x & 7), jx = (int)(blockIdx.x >> 3);
+  const int u = 8 * (jx / RG) + xcd, rgi = jx % RG;
+  if (u >= kHKV * a.B) return;
+  const int g = u % kHKV, b = u / kHKV, P = a.P;
   const int NK = P + (SELF ? kChunk : 0), nblk = (NK + kKB - 1) / kKB;
-  const int rq = blockIdx.x * (16 * NW) + w * 16 + (lane & 15);
+  const int rq = rgi * (16 * NW) + w * 16 + (lane & 15);
   const bool rvalid = rq < 3 * kChunk;
   const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
   const int qi = rvalid ? rq % kChunk : 0;
@@ -1481,23 +1489,30 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
   }
 }
 
-// Measured at P = 257 (graph replay) against staging one block per round through
-// registers: batch 16 self 8.4 against 10.1 us (four waves, three stages), cross 7.1
-// against 8.1 (two stages).  Ten waves (all 150 rows of a KV head in one workgroup, so
-// each block is loaded once instead of three times) win where 5 B workgroups fill the
-// CUs in whole rounds: batch 32 self 9.6 against 11.4 us, batch 128 28.6 against 32.2;
-// at batch 64 (320 workgroups on 256 CUs) four waves with registers capped at 128 (four
-// waves per SIMD) stay ahead, 18.5 against 18.9 (the register-staged kernel: 18.9).
+// Grid of attn_pipe_kernel: 8 XCD lanes x RG row groups x ceil(5 B / 8) units.
+static dim3 pipe_grid(int B, int NW) {
+  const int RG = (3 * kChunk + 16 * NW - 1) / (16 * NW);
+  return dim3(8 * RG * ((kHKV * B + 7) / 8));
+}
+
+// Variants by batch, from a sweep at P = 177 and 257 with the one-dimensional
+// XCD-grouped grid (us per launch, self / cross at P = 177): four waves and a 3-stage
+// ring up to batch 16 (7.2 / 5.2); five waves, two workgroups per CU at 24 (7.4 / 5.8
+// against 8.6 / 6.6 with ten); ten waves (each block loaded once for all 150 rows of a
+// KV head) at 33-48 and 65-96 rows of queries, where 5 B such workgroups fill the CUs
+// in whole rounds (batch 48: 9.1 / 7.0 against 10.9 / 7.8); otherwise four waves with
+// registers capped for four workgroups per CU (batch 64: 13.2 / 9.7 against 16.5 /
+// 12.3 with ten; batch 128: 23.5 / 17.5 against 25.2 / 19.4).  Before the grid kept
+// the row groups of a (query, KV head) on one XCD, batch 64 took 20.0 / 19.1 us at
+// P = 257 in the loop against 15.8 / 14.5 now.
 template <bool SELF>
 static void launch_pipe(const AttnArgs& a, hipStream_t s) {
   const int B = a.B;
-  if ((B > 16 && B <= 48) || B >= 96) {
-    hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 1, 10>), dim3(1, kHKV, B), dim3(640), 0, s, a);
-    return;
-  }
-  const dim3 grid(3, kHKV, B), block(256);
-  if (SELF && B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<true, 3>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), grid, block, 0, s, a);
+  if (B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<SELF, 3>), pipe_grid(B, 4), dim3(256), 0, s, a);
+  else if (B <= 24) hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 2, 5>), pipe_grid(B, 5), dim3(320), 0, s, a);
+  else if ((B > 32 && B <= 48) || (B > 64 && B <= 96))
+    hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 1, 10>), pipe_grid(B, 10), dim3(640), 0, s, a);
+  else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), pipe_grid(B, 4), dim3(256), 0, s, a);
 }
 
 static void launch_cross_q(const AttnArgs& a, hipStream_t s) {

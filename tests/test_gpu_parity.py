@@ -146,6 +146,20 @@ def test_denoise_16_layers_batch24_variable_prefix(ex16):
     compare(gpu, run_oracle(ex16, wl, q), q, wl["noise"], "expert16_b24_pvar241")
 
 
+def test_streamed_attention_variants_4_layers():
+    # batch 28 (four-wave workgroups, four per CU) and 40 (ten waves: all 150 rows of a
+    # KV head in one workgroup), the streamed-attention variants no other test batch takes
+    _say("4 layers at batch 28 and 40 (streamed attention variants)")
+    ex = Expert(4, max_batch=40, max_prefix=256)
+    try:
+        for B, q in ((28, [0, 27]), (40, [5, 39])):
+            wl = synth.make_workload("expert4_b1_p177", batch=B, with_weights=False)
+            gpu = run_gpu(ex, to_device(wl))
+            compare(gpu, run_oracle(ex, wl, q), q, wl["noise"], f"expert4 batch {B}")
+    finally:
+        ex.close()
+
+
 def test_denoise_16_layers_batch64(ex16):
     _say("denoise expert16_b64_p257 (sampled queries)")
     wl = synth.make_workload("expert16_b64_p257", with_weights=False)
