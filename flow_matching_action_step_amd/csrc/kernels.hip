@@ -194,7 +194,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     }
     return;
   }
-  if constexpr (EM == E_SWIGLU || EM == E_F16_BIAS || EM == E_TIMEIN) {
+  if constexpr (EM == E_SWIGLU || EM == E_TIMEIN) {
     // Work unit = (row, one 8-column chunk of the fp16 output).  SwiGLU: the
     // 16-column block c of the tile holds gate (8) then up (8) of output chunk c.
     constexpr int NC = EM == E_SWIGLU ? BN / 16 : BN / 8;  // output chunks per tile row
@@ -222,7 +222,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
         const float z[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w,
                             a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = EM == E_TIMEIN ? silu(z[e]) : z[e];
+        for (int e = 0; e < 8; ++e) v[e] = silu(z[e]);
       }
       *reinterpret_cast<uint4*>(a.out16 + t16_off(row, col, kco)) = pack8(v);
     }
@@ -604,8 +604,7 @@ static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s) {
 #define SMOLEXP_GEMM_CASE(AMV, EMV) \
   if (am == AMV && em == EMV) return launch_gemm_t<AMV, EMV>(p, a, s);
-  SMOLEXP_GEMM_CASE(A_X, E_F16_BIAS)
-  SMOLEXP_GEMM_CASE(A_F16, E_TIMEIN)
+  SMOLEXP_GEMM_CASE(A_X, E_TIMEIN)
   SMOLEXP_GEMM_CASE(A_F16, E_H_BIAS)
   SMOLEXP_GEMM_CASE(A_NORM, E_QKV)
   SMOLEXP_GEMM_CASE(A_F16, E_H_RESID)
@@ -847,7 +846,7 @@ hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArg
 //    (down at 800 rows: 12.0 us against 25.5 on 128 x 128 pipelined tiles, whose 42
 //    workgroups leave most CUs idle; o 6.6 against 12.9; Q/K/V 10.2 against 14.3);
 //  * the pipelined kernel wins from 1600-3200 rows on (gate/up from 800);
-//  * the register-staged tiled kernel only for the time MLP and action_in at 3200 rows and more.
+//  * the register-staged tiled kernel only for the time MLP at 3200 rows and more.
 GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
   GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);  // skinny base: k-steps per wave, column blocks
   auto skinny = [&](int rb, int cb) {
@@ -886,7 +885,7 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
     case E_ACTOUT:
       if (M <= 2400) return skinny(1, 1);
       return M <= 4800 ? skinny(4, 2) : plan_gemm(M, N, K);
-    default:  // time MLP, action_in
+    default:  // time MLP
       return M <= 2400 ? skinny(2, 2) : plan_gemm(M, N, K);
   }
 }

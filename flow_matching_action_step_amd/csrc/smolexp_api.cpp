@@ -67,15 +67,16 @@ struct smolexp_handle {
 
   // weights
   void* wmem = nullptr;
-  Mat w_in, w_t1, w_t2, w_out;
-  half_t* w_t1e = nullptr;  // W_t1[:, 720:] row-major, same scale as w_t1 (read by the prologue)
-  float *b_in = nullptr, *b_t1 = nullptr, *b_t2 = nullptr, *b_out = nullptr;
+  Mat w_tin, w_t2, w_out;   // w_tin: the time MLP's first layer with action_in folded in, [720][32]
+  half_t* w_t1e = nullptr;  // W_t1[:, 720:] row-major, fp16 x 2^-s_t1e (read by the prologue)
+  float s_t1e = 1.f;
+  float *b_t1 = nullptr, *b_t2 = nullptr, *b_out = nullptr;  // b_t1 holds b_t1 + W_t1[:, :720] b_in
   std::vector<LayerDev> layers;
 
   // workspace
   void* wsmem = nullptr;
   float *x = nullptr, *h = nullptr, *cvec = nullptr;
-  half_t *y16 = nullptr, *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *h16 = nullptr;
+  half_t *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *h16 = nullptr;
   bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
   float2* rope = nullptr;   // [max_prefix + 50][32] (cos, sin) by position
   float2* ropeq = nullptr;  // [B*50][32] per call: the rope rows of each chunk row's position
@@ -264,7 +265,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   pa.x_in = c.x_in;
   pa.x = h->x;
   pa.w_t1e = h->w_t1e;
-  pa.s_t1 = h->w_t1.scale;
+  pa.s_t1 = h->s_t1e;
   pa.b_t1 = h->b_t1;
   pa.cvec = cvec;
   pa.inv_period = h->inv_period;
@@ -304,20 +305,16 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     g.inv_k = 1.0f / kD;
     g.eps = h->cfg.rms_eps;
 
-    // action_in: y = x W_in^T + b_in   (prefix overwrite applied to x first)
-    GemmArgs ga = g;
-    ga.N = kD; ga.K = kAD; ga.A = h->x; ga.lda = kAD;
-    ga.x = h->x; ga.noise = c.x_in; ga.prev = c.prev; ga.ow_rows = c.velocity ? 0 : c.d; ga.t = t;
-    ga.W = h->w_in.w; ga.ldw = h->w_in.ld; ga.w_scale = h->w_in.scale; ga.bias = h->b_in;
-    ga.out16 = h->y16; ga.ldo = kD;
-    if ((e = gemm(-1, A_X, E_F16_BIAS, ga)) != hipSuccess) return hip_fail(h, e, "action_in launch");
-
-    // time MLP: s = SiLU(W_t1[:, :720] y + (W_t1[:, 720:] e(t) + b_t1));  h = W_t2 s + b_t2
+    // action_in + time MLP, first layer: s = SiLU(W_t1[:, :720] (W_in x + b_in) + W_t1[:, 720:] e(t)
+    // + b_t1), computed as (W_t1[:, :720] W_in) x + the step's time vector (whose bias holds
+    // W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read and stored back
+    // into the state.  Then h = W_t2 s + b_t2.
     GemmArgs gt = g;
-    gt.N = kD; gt.K = kD; gt.A = h->y16; gt.lda = kD;
-    gt.W = h->w_t1.w; gt.ldw = h->w_t1.ld; gt.w_scale = h->w_t1.scale; gt.bias = cvec + (size_t)k * kD;
+    gt.N = kD; gt.K = kAD; gt.A = h->x; gt.lda = kAD;
+    gt.x = h->x; gt.noise = c.x_in; gt.prev = c.prev; gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
+    gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
     gt.out16 = h->s16; gt.ldo = kD;
-    if ((e = gemm(-1, A_F16, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
+    if ((e = gemm(-1, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
 
     GemmArgs go = g;
     go.N = kD; go.K = kD; go.A = h->s16; go.lda = kD;
@@ -515,7 +512,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mpad * kD * 4);
   const size_t o_cv = take((size_t)(kMaxSteps + 1) * kD * 4);  // the schedule's time vectors + one for velocity calls
-  const size_t o_y = take(Mpad * kD * 2), o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
+  const size_t o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
   const size_t o_u = take(Mpad * kFFN * 2), o_h16 = take(Mpad * kKPad * 2);
   const size_t o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
   const size_t o_vc = take(Mmax * kNKV * 2), o_rq = take(Mmax * (kHD / 2) * sizeof(float2));
@@ -525,7 +522,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   if (e != hipSuccess) { delete h; return SMOLEXP_E_NOMEM; }
   char* base = static_cast<char*>(h->wsmem);
   h->x = (float*)(base + o_x); h->h = (float*)(base + o_h);
-  h->cvec = (float*)(base + o_cv); h->y16 = (half_t*)(base + o_y); h->s16 = (half_t*)(base + o_s);
+  h->cvec = (float*)(base + o_cv); h->s16 = (half_t*)(base + o_s);
   h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->h16 = (half_t*)(base + o_h16);
   h->q = (bf16_t*)(base + o_q);
   h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->ropeq = (float2*)(base + o_rq);
@@ -560,9 +557,9 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   // time-embedding half of W_t1 row-major for the prologue, fp32 biases.
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const size_t o_win = take((size_t)kD * kAD * 2), o_wt1 = take((size_t)kD * kD * 2), o_wt1e = take((size_t)kD * kD * 2);
+  const size_t o_wtin = take((size_t)kD * kAD * 2), o_wt1e = take((size_t)kD * kD * 2);
   const size_t o_wt2 = take((size_t)kD * kD * 2);
-  const size_t o_bin = take(kD * 4), o_bt1 = take(kD * 4), o_bt2 = take(kD * 4);
+  const size_t o_bt1 = take(kD * 4), o_bt2 = take(kD * 4);
   std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L);
   for (int l = 0; l < L; ++l) {
     o_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * kKPad * 2);
@@ -585,7 +582,7 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     float* d = (float*)(hb + o);
     for (size_t i = 0; i < n; ++i) d[i] = bf2f(p[i]);
   };
-  Mat w_in, w_t1, w_t2, w_out;
+  Mat w_tin, w_t2, w_out;
   std::vector<LayerDev> layers(L);
   std::vector<int> sh_qkv(L), sh_o(L), sh_gu(L), sh_dn(L);
 
@@ -596,17 +593,51 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   const uint16_t* p_wt2 = next((size_t)kD * kD);
   const uint16_t* p_bt2 = next(kD);
   int s;
-  s = pick_shift({{p_win, (size_t)kD * kAD}});
-  pack_t16(rows_of(p_win, kD, kAD), kAD, kAD, s, (half_t*)(hb + o_win));
-  w_in.scale = ldexpf(1.f, -s); w_in.ld = kAD;
-  s = pick_shift({{p_wt1, (size_t)kD * 2 * kD}});
-  pack_t16(rows_of(p_wt1, kD, 2 * kD), kD, kD, s, (half_t*)(hb + o_wt1));  // columns 0..719: the action part
-  for (int j = 0; j < kD; ++j) to_f16(p_wt1 + (size_t)j * 2 * kD + kD, kD, s, (half_t*)(hb + o_wt1e) + (size_t)j * kD);
-  w_t1.scale = ldexpf(1.f, -s); w_t1.ld = kD;
+  // action_in feeds only the action half of the time MLP's first layer, a linear map:
+  // W_t1[:, :720] (W_in x + b_in) = (W_t1[:, :720] W_in) x + W_t1[:, :720] b_in.  The
+  // [720][32] product and the bias term depend on the weights alone, so they are formed
+  // here once (fp64 sums of the bf16 values; the product rounded once to fp16) and the
+  // layer reads the Euler state directly.
+  {
+    std::vector<double> win((size_t)kD * kAD), bin(kD), acc(kAD);
+    for (size_t i = 0; i < win.size(); ++i) win[i] = bf2f(p_win[i]);
+    for (int i = 0; i < kD; ++i) bin[i] = bf2f(p_bin[i]);
+    std::vector<float> wtin((size_t)kD * kAD);
+    float* bt1 = (float*)(hb + o_bt1);
+    float mx = 0.f;
+    for (int j = 0; j < kD; ++j) {
+      const uint16_t* wr = p_wt1 + (size_t)j * 2 * kD;  // row j, columns 0..719: the action half
+      std::fill(acc.begin(), acc.end(), 0.0);
+      double bsum = bf2f(p_bt1[j]);
+      for (int i = 0; i < kD; ++i) {
+        const double w = bf2f(wr[i]);
+        const double* ir = win.data() + (size_t)i * kAD;
+        for (int c = 0; c < kAD; ++c) acc[c] += w * ir[c];
+        bsum += w * bin[i];
+      }
+      for (int c = 0; c < kAD; ++c) {
+        wtin[(size_t)j * kAD + c] = (float)acc[c];
+        mx = fmaxf(mx, fabsf((float)acc[c]));
+      }
+      bt1[j] = (float)bsum;
+    }
+    s = shift_for(mx);
+    const float m = ldexpf(1.f, s);
+    half_t* dst = (half_t*)(hb + o_wtin);
+    for (int j = 0; j < kD; ++j)
+      for (int c = 0; c < kAD; ++c) dst[t16_off(j, c, kAD / 8)] = (half_t)(wtin[(size_t)j * kAD + c] * m);
+    w_tin.scale = ldexpf(1.f, -s); w_tin.ld = kAD;
+  }
+  // the time-embedding half, row-major for the prologue, with a scale of its own
+  std::vector<std::pair<const uint16_t*, size_t>> t1e_rows(kD);
+  for (int j = 0; j < kD; ++j) t1e_rows[j] = {p_wt1 + (size_t)j * 2 * kD + kD, (size_t)kD};
+  s = pick_shift(t1e_rows);
+  for (int j = 0; j < kD; ++j) to_f16(t1e_rows[j].first, kD, s, (half_t*)(hb + o_wt1e) + (size_t)j * kD);
+  const float s_t1e = ldexpf(1.f, -s);
   s = pick_shift({{p_wt2, (size_t)kD * kD}});
   pack_t16(rows_of(p_wt2, kD, kD), kD, kD, s, (half_t*)(hb + o_wt2));
   w_t2.scale = ldexpf(1.f, -s); w_t2.ld = kD;
-  vec32(p_bin, kD, o_bin); vec32(p_bt1, kD, o_bt1); vec32(p_bt2, kD, o_bt2);
+  vec32(p_bt2, kD, o_bt2);
 
   for (int l = 0; l < L; ++l) {
     const bool self_attn = l % 2 == 0;
@@ -683,10 +714,11 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   e = hipMemcpy(h->wmem, hb, off, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(h, e, "weight upload");
   char* db = static_cast<char*>(h->wmem);
-  w_in.w = (half_t*)(db + o_win); w_t1.w = (half_t*)(db + o_wt1); w_t2.w = (half_t*)(db + o_wt2); w_out.w = (half_t*)(db + o_wout);
-  h->w_in = w_in; h->w_t1 = w_t1; h->w_t2 = w_t2; h->w_out = w_out;
+  w_tin.w = (half_t*)(db + o_wtin); w_t2.w = (half_t*)(db + o_wt2); w_out.w = (half_t*)(db + o_wout);
+  h->w_tin = w_tin; h->w_t2 = w_t2; h->w_out = w_out;
   h->w_t1e = (half_t*)(db + o_wt1e);
-  h->b_in = (float*)(db + o_bin); h->b_t1 = (float*)(db + o_bt1); h->b_t2 = (float*)(db + o_bt2);
+  h->s_t1e = s_t1e;
+  h->b_t1 = (float*)(db + o_bt1); h->b_t2 = (float*)(db + o_bt2);
   h->b_out = (float*)(db + o_bout);
   for (int l = 0; l < L; ++l) {
     layers[l].qkv.w = (half_t*)(db + o_qkv[l]);
@@ -703,7 +735,7 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   pa.n_t = h->cfg.n_steps;
   for (int k = 0; k < pa.n_t; ++k) pa.t[k] = h->ts[k];
   pa.w_t1e = h->w_t1e;
-  pa.s_t1 = h->w_t1.scale;
+  pa.s_t1 = h->s_t1e;
   pa.b_t1 = h->b_t1;
   pa.cvec = h->cvec;
   pa.inv_period = h->inv_period;

@@ -52,8 +52,7 @@ enum AMode : int {
 
 // GEMM epilogues.
 enum EMode : int {
-  E_F16_BIAS = 0,  // out16 = acc + bias                      (action_in)
-  E_TIMEIN = 1,    // out16 = SiLU(acc + cvec)                (time MLP, first layer)
+  E_TIMEIN = 1,    // out16 = SiLU(acc + cvec)                (action_in + time MLP, first layer)
   E_H_BIAS = 2,    // h = acc + bias; h16 = fp16(h)           (time MLP, second layer)
   E_H_RESID = 3,   // h += acc; h16 = fp16(h)                 (o and down projections)
   E_QKV = 4,       // RoPE on Q and K, scatter to Q/Kc/Vc bf16 (attention input)

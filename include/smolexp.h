@@ -109,7 +109,11 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out);
  *   final_norm.g [720], action_out.w [32,720], action_out.b [32].
  * n_elems must equal smolexp_weight_count (else SMOLEXP_E_SIZE).  The data is
  * copied (matrices re-encoded exactly as fp16 with a power-of-two scale per
- * matrix); the caller may free bf16_host on return.  Synchronous.
+ * matrix; RMSNorm gains folded into the matrix that follows; action_in folded
+ * into the action half of time_in, whose product with it is a weight-only
+ * [720,32] matrix, rounded once to fp16, plus a bias term), and the time
+ * vectors of the configured schedule are computed; the caller may free
+ * bf16_host on return.  Synchronous.
  */
 int smolexp_load_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems);
 
