@@ -137,7 +137,18 @@ __device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { ret
 // pre[] (E_QKV, one unit per thread: the 16 cos/sin values of a rotated block;
 // E_H_RESID, one row block per wave: the residual values of chunk t in pre[t],
 // BN / 16 of them).
-template <int EM, int BM, int BN, int LDC, int NT, bool PRE = false>
+// Store of a 4-, 8- or 16-byte value, nontemporal when NTS.
+template <bool NTS, typename T>
+__device__ __forceinline__ void st_out(T* p, const T& v) {
+  if constexpr (NTS) {
+    typedef unsigned V __attribute__((ext_vector_type(sizeof(T) / 4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(V, v), reinterpret_cast<V*>(p));
+  } else {
+    *p = v;
+  }
+}
+
+template <int EM, int BM, int BN, int LDC, int NT, bool PRE = false, bool NTS = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC, int m0, int n0,
                                               const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
@@ -180,16 +191,16 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
           lo.e[e] = f2bf(v1[e] * c - v2[e] * sn);
           hi.e[e] = f2bf(v1[e] * sn + v2[e] * c);
         }
-        *reinterpret_cast<uint4*>(dst + d0) = lo.u;
-        *reinterpret_cast<uint4*>(dst + d0 + kHD / 2) = hi.u;
+        st_out<NTS>(reinterpret_cast<uint4*>(dst + d0), lo.u);
+        st_out<NTS>(reinterpret_cast<uint4*>(dst + d0 + kHD / 2), hi.u);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           lo.e[e] = f2bf(v1[e]);
           hi.e[e] = f2bf(v2[e]);
         }
-        *reinterpret_cast<uint4*>(dst + cb % kHD) = lo.u;
-        *reinterpret_cast<uint4*>(dst + cb % kHD + 8) = hi.u;
+        st_out<NTS>(reinterpret_cast<uint4*>(dst + cb % kHD), lo.u);
+        st_out<NTS>(reinterpret_cast<uint4*>(dst + cb % kHD + 8), hi.u);
       }
     }
     return;
@@ -224,7 +235,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = silu(z[e]);
       }
-      *reinterpret_cast<uint4*>(a.out16 + t16_off(row, col, kco)) = pack8(v);
+      st_out<NTS>(reinterpret_cast<uint4*>(a.out16 + t16_off(row, col, kco)), pack8(v));
     }
     return;
   }
@@ -252,10 +263,10 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
             const float4 hv = PRE ? pre[t] : *hp;
             o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
           }
-          *hp = o;
+          st_out<NTS>(hp, o);
           union { half_t e[4]; uint2 u; } o16;
           o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
-          *reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)) = o16.u;
+          st_out<NTS>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)), o16.u);
         }
       }
     }
@@ -800,7 +811,10 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
       for (int fn = 0; fn < FN; ++fn) sC[rl * LDC + (wn * FN + fn) * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
   __syncthreads();
-  epilogue_tile<EM, BM, BN, LDC, 64 * NW, PRE>(a, sC, m0, n0, pre);
+  // nontemporal stores: the outputs of a round of tiles (megabytes) stream out instead of
+  // sitting dirty in L2 until the end of the launch (batch 64 loop: 17.6 -> 16.4 ms; the
+  // same stores in the small-batch kernels and the attention were slower or equal)
+  epilogue_tile<EM, BM, BN, LDC, 64 * NW, PRE, true>(a, sC, m0, n0, pre);
 }
 
 template <int EM, bool NORM, int BM, int FMW, int WN, int S>
