@@ -26,7 +26,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 SMOLEXP_OK, SMOLEXP_E_INVAL, SMOLEXP_E_STATE, SMOLEXP_E_SIZE, SMOLEXP_E_NOMEM, SMOLEXP_E_HIP = 0, -1, -2, -3, -4, -5
 
 # kernel ids of smolexp_time_kernel
-K_QKV, K_ATTN_SELF, K_ATTN_CROSS, K_O, K_GATE_UP, K_DOWN, K_ACTION_OUT, K_WHOLE_LOOP = range(8)
+(K_QKV, K_ATTN_SELF, K_ATTN_CROSS, K_O, K_GATE_UP, K_DOWN, K_ACTION_OUT, K_WHOLE_LOOP, K_Q_CROSS, K_TIME_IN,
+ K_TIME_OUT) = range(11)
 
 
 class smolexp_config(ctypes.Structure):

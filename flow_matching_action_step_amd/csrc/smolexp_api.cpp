@@ -53,7 +53,9 @@ struct GraphEntry {
 
 constexpr int kGraphCache = 8;
 
-enum ProbeKind { PR_QKV = 0, PR_ATTN_SELF, PR_ATTN_CROSS, PR_O, PR_GU, PR_DOWN, PR_ACTOUT, PR_COUNT };
+// Kernel ids of smolexp_time_kernel; PR_LOOP (the whole call) records no launches.
+enum ProbeKind { PR_QKV = 0, PR_ATTN_SELF, PR_ATTN_CROSS, PR_O, PR_GU, PR_DOWN, PR_ACTOUT, PR_LOOP, PR_QCROSS, PR_TIN, PR_TOUT,
+                 PR_COUNT };
 
 }  // namespace
 
@@ -314,13 +316,13 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     gt.x = h->x; gt.noise = c.x_in; gt.prev = c.prev; gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
     gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
     gt.out16 = h->s16; gt.ldo = kD;
-    if ((e = gemm(-1, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
+    if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
 
     GemmArgs go = g;
     go.N = kD; go.K = kD; go.A = h->s16; go.lda = kD;
     go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
     go.h = h->h; go.h16 = h->h16;
-    if ((e = gemm(-1, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
+    if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
 
     for (int l = 0; l < L; ++l) {
       const LayerDev& ld = h->layers[l];
@@ -331,7 +333,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
         gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
         gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
         gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.ropeq = h->ropeq;
-        if ((e = norm_gemm(ld.self_attn ? PR_QKV : -1, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
+        if ((e = norm_gemm(ld.self_attn ? PR_QKV : PR_QCROSS, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
       }
 
       AttnArgs aa;
@@ -790,7 +792,7 @@ int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_m
 int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, float* avg_us) {
   if (!h) return SMOLEXP_E_INVAL;
   h->err.clear();
-  if (!avg_us || reps < 1 || reps > 100000 || kernel < 0 || kernel > PR_COUNT)
+  if (!avg_us || reps < 1 || reps > 100000 || kernel < 0 || kernel >= PR_COUNT)
     return fail(h, SMOLEXP_E_INVAL, "bad kernel id, reps or avg_us");
   if (!h->have_last) return fail(h, SMOLEXP_E_STATE, "no previous denoise call to time");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -802,12 +804,12 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     lastc.out = k.out; lastc.B = k.B; lastc.prev = k.prev; lastc.d = k.d; lastc.vel = k.vel; lastc.st = k.st;
     lastc.t_single = k.t_single;
   }
-  if (kernel < PR_COUNT && (!h->have_probe || !same_key(h->probe_key, h->last))) {
+  if (kernel != PR_LOOP && (!h->have_probe || !same_key(h->probe_key, h->last))) {
     // the previous call was a graph replay of another key: enqueue it once directly to get its launches
     int rc0 = enqueue(h, lastc, s, true);
     if (rc0 != SMOLEXP_OK) return rc0;
   }
-  if (kernel < PR_COUNT && h->probes[kernel].empty()) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");
+  if (kernel != PR_LOOP && h->probes[kernel].empty()) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");
   // launch i replays the (i mod n)-th recorded instance: every layer's weights in turn, as in the loop
   auto launch = [&](int i, hipStream_t st) -> hipError_t {
     const std::vector<smolexp_handle::Probe>& v = h->probes[kernel];
@@ -817,7 +819,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     return launch_gemm(p.plan, p.am, p.em, p.g, st);
   };
   hipGraphExec_t exec = nullptr;
-  if (kernel < PR_COUNT && h->cfg.use_graphs) {
+  if (kernel != PR_LOOP && h->cfg.use_graphs) {
     // one graph of `reps` launches (the loop itself runs as a graph)
     hipError_t e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamBeginCapture");
@@ -850,7 +852,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     if (e == hipSuccess) e = hipGraphLaunch(exec, s);
   } else {
     for (int i = 0; i < reps && e == hipSuccess && rc == SMOLEXP_OK; ++i) {
-      if (kernel == PR_COUNT) rc = run_call(h, lastc, s);  // the whole loop: replay the previous call
+      if (kernel == PR_LOOP) rc = run_call(h, lastc, s);  // the whole loop: replay the previous call
       else e = launch(i, s);
     }
   }

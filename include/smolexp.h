@@ -183,9 +183,16 @@ int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_m
  * smolexp_denoise/_ex call, which must have used the same batch and
  * prefix_len, and leaves that workspace's numbers unspecified.
  *   kernel: 0 = self-attention layer QKV projection, 1 = self attention,
- *           2 = cross attention, 3 = o projection, 4 = gate/up projection,
- *           5 = down projection, 6 = action_out + Euler update,
- *           7 = the whole loop (one smolexp_denoise call).
+ *           2 = cross attention (with the layer's Q projection at batch <= 8),
+ *           3 = o projection, 4 = gate/up projection, 5 = down projection,
+ *           6 = action_out + Euler update, 7 = the whole loop (one
+ *           smolexp_denoise call), 8 = cross-attention layer Q projection
+ *           (its own launch above batch 8; at batch <= 8 it is part of
+ *           kernel 2 and this id returns SMOLEXP_E_STATE), 9 = the time MLP's
+ *           first layer (action_in folded in) + SiLU, 10 = the time MLP's
+ *           second layer into the residual stream.
+ * SMOLEXP_E_INVAL for other ids, SMOLEXP_E_STATE without a previous call or
+ * for a kernel that call did not launch.
  */
 int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, float* avg_us);
 

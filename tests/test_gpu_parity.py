@@ -299,6 +299,10 @@ def test_time_kernel_hook(ex4):
     _say("time_kernel hook")
     wl = synth.make_workload("expert4_b1_p177", with_weights=False)
     run_gpu(ex4, to_device(wl))
-    for k in range(8):
+    for k in (0, 1, 2, 3, 4, 5, 6, 7, 9, 10):
         us = fm.smolexp_time_kernel(ex4.h, k, 3)
         assert 0.0 < us < 1e6
+    # batch 1: the cross layers' Q projection runs inside the attention launch
+    us = ctypes.c_float()
+    assert fm.raw().smolexp_time_kernel(ex4.h, fm.K_Q_CROSS, 3, None, ctypes.byref(us)) == fm.SMOLEXP_E_STATE
+    assert fm.raw().smolexp_time_kernel(ex4.h, 11, 3, None, ctypes.byref(us)) == fm.SMOLEXP_E_INVAL
