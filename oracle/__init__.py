@@ -50,6 +50,17 @@ Pins (what fixes each function other than itself; all in tests/):
   schedule/Euler .. closed-form trajectories under stub velocity fields
                     (constant, linear, straight flow-matching path)
   overwrite ....... closed form under v = 0; fixed point on the straight path
+  prefill (prefill.py: the prefix language model's per-layer keys/values)
+    layer ......... composition of torch library routines (rms_norm, linear,
+                    scaled_dot_product_attention(enable_gqa) with the key
+                    mask, silu), complex-number rotary embedding, positions
+                    from torch's cumulative sum
+    positions ..... closed values
+    whole prefill . NaN-pad invariance; removing the pads leaves the valid
+                    tokens' keys/values unchanged; bidirectional within the
+                    prefix (layer-1 keys of token 0 depend on the last token,
+                    layer-0 keys do not); one-token closed form; batch layout
+    bf16 rounding . closed values (ties to even, subnormals)
 No function is left parity unpinned.
 """
 from .expert import (  # noqa: F401
@@ -57,3 +68,6 @@ from .expert import (  # noqa: F401
     attention, embed, expert_layer, head, velocity, ExpertConfig,
 )
 from .flow import schedule, overwrite_rows, euler_denoise, denoise_query, denoise_batch  # noqa: F401
+from .prefill import (  # noqa: F401
+    PrefillConfig, prefix_positions, prefill_layer, prefill, prefill_batch, round_to_bf16_bits,
+)

@@ -11,6 +11,11 @@ kind of tensor, so that changing one input never shifts another:
     lengths        seed 3   valid prefix length per query, U{lo..hi}
     prev. actions  seed 4   N(0, 0.5) fp32 (std 0.5), [B, d, 32]
     gain variant   seed 5   RMSNorm gains 1 + N(0, 0.1), only when asked for
+    LM weights     seed 6   the prefix language model's weights, as the
+                            expert's (N(0, 0.02), gains 1), in its manifest order
+    embeddings     seed 7   prefix token embeddings N(0, 1) rounded to bf16,
+                            [B, P, 960] (what the vision connector and the text
+                            embedding table would produce)
 
 Floating-point draws are made in float32 and rounded to bf16 with
 round-to-nearest-even where the tensor is stored as bf16.  Everything is
@@ -34,6 +39,13 @@ ACTION_DIM = 32     # padded action vector width
 TIME_DIM = 720      # sinusoidal time-embedding width
 
 SEED_WEIGHTS, SEED_NOISE, SEED_KV, SEED_LENGTHS, SEED_PREV, SEED_GAINS = 0, 1, 2, 3, 4, 5
+SEED_LM_WEIGHTS, SEED_EMB = 6, 7
+
+# The language model that fills the prefix cache (noeira docs "SmolVLA",
+# Architecture table: SmolLM2, 16 layers of width 960, the same grouped-query
+# layout).  Its SwiGLU width is not on the pages; 2560 is SmolLM2-360M's.
+LM_D_MODEL = 960
+LM_FFN = 2560
 
 # The five synthetic workloads.  `prefix_len` is the padded prefix length P;
 # `lengths` is None (all P tokens valid) or the (lo, hi) range of valid
@@ -101,16 +113,44 @@ def f32_to_bf16_bits(a):
     return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
-def draw_weights(n_layers, seed=SEED_WEIGHTS, gain_seed=None, std=0.02):
+def lm_manifest(n_layers):
+    """Ordered (name, shape, kind) list of the prefix language model's tensors.
+
+    Every layer is a pre-norm GQA block (q, k, v, o, then a SwiGLU MLP); no
+    biases.  Only the layers whose keys/values the expert reads are listed.
+    """
+    m = []
+    for l in range(n_layers):
+        p = f"lm.{l}."
+        m += [
+            (p + "norm1.g", (LM_D_MODEL,), "g"),
+            (p + "q.w", (N_Q * HEAD_DIM, LM_D_MODEL), "w"),
+            (p + "k.w", (N_KV * HEAD_DIM, LM_D_MODEL), "w"),
+            (p + "v.w", (N_KV * HEAD_DIM, LM_D_MODEL), "w"),
+            (p + "o.w", (LM_D_MODEL, N_Q * HEAD_DIM), "w"),
+            (p + "norm2.g", (LM_D_MODEL,), "g"),
+            (p + "gate.w", (LM_FFN, LM_D_MODEL), "w"),
+            (p + "up.w", (LM_FFN, LM_D_MODEL), "w"),
+            (p + "down.w", (LM_D_MODEL, LM_FFN), "w"),
+        ]
+    return m
+
+
+def lm_weight_count(n_layers):
+    return int(sum(int(np.prod(s)) for _, s, _ in lm_manifest(n_layers)))
+
+
+def draw_weights(n_layers, seed=SEED_WEIGHTS, gain_seed=None, std=0.02, which=None):
     """Named bf16 weights (uint16 bit patterns), drawn in manifest order.
 
     With gain_seed set, RMSNorm gains become 1 + N(0, 0.1) from that seed
     (a variant that makes a kernel ignoring the gain fail); otherwise 1.
+    which: the manifest function (the expert's by default).
     """
     rng = np.random.default_rng(seed)
     grng = np.random.default_rng(gain_seed) if gain_seed is not None else None
     out = {}
-    for name, shape, kind in manifest(n_layers):
+    for name, shape, kind in (which or manifest)(n_layers):
         if kind == "g":
             if grng is None:
                 vals = np.ones(shape, np.float32)
@@ -122,15 +162,30 @@ def draw_weights(n_layers, seed=SEED_WEIGHTS, gain_seed=None, std=0.02):
     return out
 
 
-def pack_weights(named, n_layers):
+def draw_lm_weights(n_layers, seed=SEED_LM_WEIGHTS, gain_seed=None, std=0.02):
+    """Named bf16 weights of the prefix language model, drawn in its manifest order."""
+    return draw_weights(n_layers, seed=seed, gain_seed=gain_seed, std=std, which=lm_manifest)
+
+
+def pack_weights(named, n_layers, which=None):
     """Concatenate named bf16 tensors into one flat uint16 buffer in manifest order."""
     parts = []
-    for name, shape, _ in manifest(n_layers):
+    for name, shape, _ in (which or manifest)(n_layers):
         a = named[name]
         if tuple(a.shape) != tuple(shape):
             raise ValueError(f"{name}: shape {a.shape} != manifest {shape}")
         parts.append(a.reshape(-1))
     return np.concatenate(parts)
+
+
+def pack_lm_weights(named, n_layers):
+    return pack_weights(named, n_layers, which=lm_manifest)
+
+
+def draw_prefix_embeddings(batch, prefix_len, seed=SEED_EMB):
+    """Prefix token embeddings, bf16 N(0, 1), [B][P][960]; pad positions are drawn too."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((batch, prefix_len, LM_D_MODEL), dtype=np.float32))
 
 
 def draw_prefix_kv(n_layers, batch, prefix_len, seed=SEED_KV):
