@@ -56,6 +56,9 @@ _sig = {
                                           ctypes.POINTER(smolexp_denoise_opts)]),
     "smolexp_velocity": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, ctypes.c_float, _P, ctypes.c_int, _P]),
     "smolexp_time_kernel": (ctypes.c_int, [_H, ctypes.c_int, ctypes.c_int, _P, ctypes.POINTER(ctypes.c_float)]),
+    "smolexp_lm_weight_count": (ctypes.c_size_t, [ctypes.POINTER(smolexp_config)]),
+    "smolexp_load_lm_weights": (ctypes.c_int, [_H, _P, ctypes.c_size_t]),
+    "smolexp_prefill": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P]),
     "smolexp_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "smolexp_last_error": (ctypes.c_char_p, [_H]),
     "smolexp_destroy": (None, [_H]),
@@ -175,6 +178,33 @@ def smolexp_velocity(h, cfg, prefix_kv, prefix_mask, x, t, out_v, stream=None):
     rc = _lib.smolexp_velocity(h, _ptr(prefix_kv), _ptr(prefix_mask), P, _ptr(x), float(t), _ptr(out_v), B,
                                _stream(stream))
     _check(rc, h, "smolexp_velocity")
+
+
+def smolexp_lm_weight_count(cfg):
+    return int(_lib.smolexp_lm_weight_count(ctypes.byref(cfg)))
+
+
+def smolexp_load_lm_weights(h, bf16_flat):
+    """bf16_flat: numpy uint16 array (bf16 bit patterns) in the language model's manifest order."""
+    import numpy as np
+    a = np.ascontiguousarray(bf16_flat, dtype=np.uint16)
+    _check(_lib.smolexp_load_lm_weights(h, a.ctypes.data_as(ctypes.c_void_p), a.size), h,
+           "smolexp_load_lm_weights")
+
+
+def smolexp_prefill(h, cfg, prefix_emb, prefix_mask, out_kv, stream=None):
+    """prefix_emb: bf16 (or its uint16/int16 bits) [B,P,960]; prefix_mask uint8 [B,P];
+    out_kv: bf16 bits [L,2,B,5,P,64], written."""
+    import torch
+    B, P = prefix_mask.shape
+    _need(prefix_mask, "prefix_mask", torch.uint8)
+    for name, t in (("prefix_emb", prefix_emb), ("out_kv", out_kv)):
+        if t.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+            raise ValueError(f"{name} must hold bf16 values")
+    _need(prefix_emb, "prefix_emb", prefix_emb.dtype, (B, P, 960))
+    _need(out_kv, "out_kv", out_kv.dtype, _kv_shape(cfg, B, P))
+    rc = _lib.smolexp_prefill(h, _ptr(prefix_emb), _ptr(prefix_mask), P, _ptr(out_kv), B, _stream(stream))
+    _check(rc, h, "smolexp_prefill")
 
 
 def smolexp_time_kernel(h, kernel, reps, stream=None):

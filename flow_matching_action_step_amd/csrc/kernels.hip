@@ -137,6 +137,11 @@ __device__ __forceinline__ float rms_scale(const GemmArgs& a, float sumsq) { ret
 // pre[] (E_QKV, one unit per thread: the 16 cos/sin values of a rotated block;
 // E_H_RESID, one row block per wave: the residual values of chunk t in pre[t],
 // BN / 16 of them).
+// Column chunks of the fp32 residual (t32_off) and of its fp16 copy (t16_off) by epilogue:
+// the expert's 720 (its copy stored over 768 columns), or the prefix model's 960.
+__host__ __device__ constexpr int resid_k4(int em) { return em == E_PF_RESID ? kLmD / 4 : kD / 4; }
+__host__ __device__ constexpr int resid16_kc(int em) { return em == E_PF_RESID ? kLmD / 8 : kKPad / 8; }
+
 // Store of a 4-, 8- or 16-byte value, nontemporal when NTS.
 template <bool NTS, typename T>
 __device__ __forceinline__ void st_out(T* p, const T& v) {
@@ -153,10 +158,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
                                               const float4* pre = nullptr) {
   constexpr int NB = BN / 16, UPR = NB * 8;
   static_assert(UPR <= 64 && 64 % UPR == 0, "rows inside one wave");
-  static_assert(!PRE || EM != E_QKV || (BM * NB <= NT && NB <= 4), "PRE: one E_QKV unit per thread");
-  static_assert(!PRE || EM != E_H_RESID || BM / 16 <= NT / 64, "PRE: one E_H_RESID row block per wave");
+  static_assert(!PRE || (EM != E_QKV && EM != E_PF_QKV) || (BM * NB <= NT && NB <= 4), "PRE: one E_QKV unit per thread");
+  static_assert(!PRE || (EM != E_H_RESID && EM != E_PF_RESID) || BM / 16 <= NT / 64,
+                "PRE: one E_H_RESID row block per wave");
   const int M = a.M, N = a.N;
-  if constexpr (EM == E_QKV) {
+  if constexpr (EM == E_QKV || EM == E_PF_QKV) {
     // Work unit = (row, 16-column block): the block is 8 rotation pairs of one Q/K
     // head (dims q*8.. and 32+q*8.., one 16-byte run each) or 16 consecutive V dims.
     for (int g = threadIdx.x; g < BM * NB; g += NT) {
@@ -167,12 +173,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
       const float4 c0 = src[0], c1 = src[1], c2 = src[2], c3 = src[3];
       const float v1[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       const float v2[8] = {c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
-      const int head = cb / kHD, b = row / kChunk, ci = row % kChunk;
+      const int seq = EM == E_PF_QKV ? a.seq : kChunk;  // rows per query
+      const int head = cb / kHD, b = row / seq, ci = row % seq;
       (void)pre;
       bf16_t* dst;
-      if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * kChunk + ci) * kHD;
-      else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * kChunk + ci) * kHD;
-      else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * kChunk + ci) * kHD;
+      if (head < kHQ) dst = a.q + (((size_t)b * kHQ + head) * seq + ci) * kHD;
+      else if (head < kHQ + kHKV) dst = a.kc + (((size_t)b * kHKV + head - kHQ) * seq + ci) * kHD;
+      else dst = a.vc + (((size_t)b * kHKV + head - kHQ - kHKV) * seq + ci) * kHD;
       union { bf16_t e[8]; uint4 u; } lo, hi;
       if (head < kHQ + kHKV) {  // rotate the pairs (d, d + 32), d = d0..d0+7, at this row's position
         const int d0 = ((cb % kHD) / 16) * 8;
@@ -239,7 +246,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     }
     return;
   }
-  if constexpr (EM == E_H_BIAS || EM == E_H_RESID) {
+  if constexpr (EM == E_H_BIAS || EM == E_H_RESID || EM == E_PF_RESID) {
     // Work unit = (row, one 4-column chunk of the fp32 residual and of its fp16 copy).
     // Lane = r16 + 16 * part: a wave owns one 16-row block per pass and its four parts
     // take every fourth chunk.
@@ -254,7 +261,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
         const int c = part + 4 * t, col = n0 + c * 4;
         if (live && col < N) {
           const float4 v = *reinterpret_cast<const float4*>(sC + r * LDC + c * 4);
-          float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, kD / 4));
+          float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, resid_k4(EM)));
           float4 o;
           if constexpr (EM == E_H_BIAS) {
             const float4 b = *reinterpret_cast<const float4*>(a.bias + col);
@@ -266,7 +273,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
           st_out<NTS>(hp, o);
           union { half_t e[4]; uint2 u; } o16;
           o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
-          st_out<NTS>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)), o16.u);
+          st_out<NTS>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, resid16_kc(EM))), o16.u);
         }
       }
     }
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   constexpr int NW = 8, BM = 16 * RB, BN = 16 * CB, LDC = BN;
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks per workgroup");
   static_assert(CB == 1 || CB == 2 || CB == 4, "column blocks per workgroup");
-  constexpr bool PRE = EM == E_QKV || EM == E_H_RESID;
+  constexpr bool PRE = EM == E_QKV || EM == E_PF_QKV || EM == E_H_RESID || EM == E_PF_RESID;
   __shared__ float sRed[NW * BM * BN];
   __shared__ float sC[BM * LDC];
   __shared__ float sQ[AM == A_NORM ? NW : 1][BM];  // per-wave partial sums of squares of the rows
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   // g < BM * CB owns row m0 + g / CB, column block g % CB; E_H_RESID lane r + 16 p of wave
   // w < RB owns row m0 + 16 w + r, columns n0 + 4 (p + 4 t).. for t < CB
   float4 pre[4];
-  if constexpr (EM == E_QKV) {
+  if constexpr (EM == E_QKV || EM == E_PF_QKV) {
     if (tid < BM * CB) {
       const int row = m0 + tid / CB, cb0 = n0 + (tid % CB) * 16;
       const int d0 = ((cb0 % kHD) / 16) * 8;
@@ -337,12 +344,12 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
         for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
       }
     }
-  } else if constexpr (EM == E_H_RESID) {
+  } else if constexpr (EM == E_H_RESID || EM == E_PF_RESID) {
     const int row = m0 + w * 16 + (lane & 15);
 #pragma unroll
     for (int t = 0; t < CB; ++t) {
       const int col = n0 + ((lane >> 4) + 4 * t) * 4;
-      if (w < RB && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+      if (w < RB && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, resid_k4(EM)));
     }
   }
   uint4 wf[KPW][CB];
@@ -541,7 +548,8 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.kind = 0;
     p.ntiles_n = (N + 15) / 16;
     const int need = (nks + 7) / 8;
-    p.kpw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : need <= 8 ? 8 : 0;
+    p.kpw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : need <= 8 ? 8
+          : need <= 10 ? 10 : 0;
     // measured at 16 and 50 rows, with the operand just written by another kernel: one
     // 16-row block per workgroup is fastest for every projection (down 3.9 us against 5.8
     // with all rows in one workgroup, o 2.8 against 3.8, gate/up 4.2 against 4.6)
@@ -576,6 +584,12 @@ static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_
       if constexpr (AM == A_F16 && RB * CB < 16) {
         if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB, CB>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB, CB>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case 10:  // the prefix model's down projection (K = 2560), at most two 16 x 16 tiles per workgroup
+      if constexpr (AM == A_F16 && EM == E_PF_RESID && RB * CB <= 2) {
+        hipLaunchKernelGGL((gemm_skinny<AM, EM, 10, RB, CB>), grid, block, 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -621,6 +635,8 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
   SMOLEXP_GEMM_CASE(A_F16, E_H_RESID)
   SMOLEXP_GEMM_CASE(A_NORM, E_SWIGLU)
   SMOLEXP_GEMM_CASE(A_NORM, E_ACTOUT)
+  SMOLEXP_GEMM_CASE(A_NORM, E_PF_QKV)
+  SMOLEXP_GEMM_CASE(A_F16, E_PF_RESID)
 #undef SMOLEXP_GEMM_CASE
   return hipErrorInvalidValue;
 }
@@ -691,7 +707,7 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   // loads and the ring's vmcnt waits stay exact.  Only with the 4-stage ring, whose LDS
   // holds one workgroup per CU anyway: the 32 registers would halve the 2-stage ring's
   // occupancy (two workgroups per CU, 96 -> 132 VGPRs).
-  constexpr bool PRE = EM == E_H_RESID && S > 2;
+  constexpr bool PRE = (EM == E_H_RESID || EM == E_PF_RESID) && S > 2;
   float4 pre[PRE ? BN / 16 : 1];
   if constexpr (PRE) {
     static_assert(BM / 16 <= NW, "one row block per wave");
@@ -699,7 +715,7 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       const int col = n0 + ((lane >> 4) + 4 * t) * 4;
-      if (w < BM / 16 && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, kD / 4));
+      if (w < BM / 16 && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, resid_k4(EM)));
     }
   }
   // NORM: A is fp16(h) unnormalised; each wave accumulates A A^T of its rows on the
@@ -850,6 +866,16 @@ hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArg
         return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4>(a, s);
       }
       return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 2>(a, s);
+    case E_PF_QKV:
+      if (!norm) return hipErrorInvalidValue;
+      return launch_gemm_dma<E_PF_QKV, true, 128, 2, 2, 2>(a, s);
+    case E_PF_RESID:
+      if (norm) return hipErrorInvalidValue;
+      if (p.stages == 4) {
+        if (p.bm == 64) return launch_gemm_dma<E_PF_RESID, false, 64, 2, 2, 4>(a, s);
+        return launch_gemm_dma<E_PF_RESID, false, 128, 2, 2, 4>(a, s);
+      }
+      return launch_gemm_dma<E_PF_RESID, false, 128, 2, 2, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1393,8 +1419,9 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
 // use: their weights are 0, but 0 x NaN would not be.
 constexpr int kMaxKeys = 4096 + 64;  // max_prefix + the chunk, in whole blocks
 
-template <bool SELF, int S, int MINB = 1, int NW = 4>
+template <bool SELF, int S, int MINB = 1, int NW = 4, bool PF = false>
 __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs a) {
+  static_assert(!(PF && SELF), "a prefill's keys are the prefix alone");
   constexpr int NT = 64 * NW, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
   constexpr int NLOAD = STAGE / 1024;              // 1 KB load instructions per stage
   constexpr int LPW = (NLOAD + NW - 1) / NW;      // per wave (the last waves may issue fewer)
@@ -1408,17 +1435,19 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
   // One-dimensional grid: workgroup i runs on XCD i % 8, and the RG row groups of one
   // (query, KV head) unit u get the same i % 8, so they stage the same K/V blocks through
   // one L2 (fetched from memory once, not once per row group).  The return is uniform per
-  // workgroup and comes before any barrier.
-  constexpr int RG = (3 * kChunk + 16 * NW - 1) / (16 * NW);
+  // workgroup and comes before any barrier.  The query rows of a KV head are its 3 query
+  // heads x seq rows: the chunk's 50, or (PF) the P prefix tokens of a prefill.
+  const int seq = PF ? a.seq : kChunk;
+  const int RG = PF ? (3 * seq + 16 * NW - 1) / (16 * NW) : (3 * kChunk + 16 * NW - 1) / (16 * NW);
   const int xcd = (int)(blockIdx.x & 7), jx = (int)(blockIdx.x >> 3);
   const int u = 8 * (jx / RG) + xcd, rgi = jx % RG;
   if (u >= kHKV * a.B) return;
   const int g = u % kHKV, b = u / kHKV, P = a.P;
   const int NK = P + (SELF ? kChunk : 0), nblk = (NK + kKB - 1) / kKB;
   const int rq = rgi * (16 * NW) + w * 16 + (lane & 15);
-  const bool rvalid = rq < 3 * kChunk;
-  const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
-  const int qi = rvalid ? rq % kChunk : 0;
+  const bool rvalid = rq < 3 * seq;
+  const int hq = 3 * g + (rvalid ? rq / seq : 0);
+  const int qi = rvalid ? rq % seq : 0;
 
   // key kinds: 0 = none, 1 = valid prefix key, 2 = chunk key
   const uint8_t* mk = a.mask + (size_t)b * P;
@@ -1455,7 +1484,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
 
   bf16x8 qf[2];
   {
-    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * kChunk + qi) * kHD + (lane >> 4) * 8;
+    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * seq + qi) * kHD + (lane >> 4) * 8;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
@@ -1491,7 +1520,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
   if (rvalid) {
     const float l_run = l_acc[0];
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    const int orow = b * kChunk + qi;
+    const int orow = b * seq + qi;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       union { half_t h[4]; uint2 u; } pk4;
@@ -1503,8 +1532,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
 }
 
 // Grid of attn_pipe_kernel: 8 XCD lanes x RG row groups x ceil(5 B / 8) units.
-static dim3 pipe_grid(int B, int NW) {
-  const int RG = (3 * kChunk + 16 * NW - 1) / (16 * NW);
+static dim3 pipe_grid(int B, int NW, int seq = kChunk) {
+  const int RG = (3 * seq + 16 * NW - 1) / (16 * NW);
   return dim3(8 * RG * ((kHKV * B + 7) / 8));
 }
 
@@ -1526,6 +1555,15 @@ static void launch_pipe(const AttnArgs& a, hipStream_t s) {
   else if ((B > 32 && B <= 48) || (B > 64 && B <= 96))
     hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 1, 10>), pipe_grid(B, 10), dim3(640), 0, s, a);
   else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), pipe_grid(B, 4), dim3(256), 0, s, a);
+}
+
+// A prefill's prefix self-attention: 3 P query rows per KV head, four-wave workgroups of
+// 64 rows, keys = the valid prefix tokens in both directions (the prefix is one block of the
+// block mask).
+hipError_t launch_prefix_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.P < 1 || a.seq != a.P || a.P + kKB > kMaxKeys) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_pipe_kernel<false, 2, 4, 4, true>), pipe_grid(a.B, 4, a.seq), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
@@ -1639,6 +1677,82 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(prologue_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Prefill of the prefix language model
+// ----------------------------------------------------------------------------
+// Prologue: workgroup (x, b) takes prefix tokens j0 = 64 x .. j0 + 63 of query b.  It writes
+// each token's RoPE row at its position (the number of valid tokens before it in the query:
+// a count of the mask before j0, then a running sum over the 64) and converts its bf16
+// embedding to the fp32 residual and its fp16 copy (blocked, 960 columns).
+__global__ __launch_bounds__(256) void prefill_prologue_kernel(const PrefillPrologueArgs a) {
+  const int b = blockIdx.y, j0 = blockIdx.x * 64, tid = threadIdx.x, P = a.P;
+  const uint8_t* mk = a.mask + (size_t)b * P;
+  __shared__ int sCnt[256];
+  __shared__ int sPos[64];
+  int c = 0;
+  for (int j = tid; j < j0; j += 256) c += mk[j] ? 1 : 0;
+  sCnt[tid] = c;
+  if (tid < 64) sPos[tid] = (j0 + tid < P && mk[j0 + tid]) ? 1 : 0;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sCnt[tid] += sCnt[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int run = sCnt[0];
+    for (int i = 0; i < 64; ++i) {
+      const int f = sPos[i];
+      sPos[i] = run;
+      run += f;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * (kHD / 2); e += 256) {
+    const int i = e / (kHD / 2), d = e % (kHD / 2), j = j0 + i;
+    if (j < P) a.ropeq[((size_t)b * P + j) * (kHD / 2) + d] = a.rope[(size_t)sPos[i] * (kHD / 2) + d];
+  }
+  for (int e = tid; e < 64 * (kLmD / 4); e += 256) {
+    const int i = e / (kLmD / 4), c4 = e % (kLmD / 4), j = j0 + i;
+    if (j >= P) continue;
+    const int row = b * P + j;
+    const uint2 raw = *reinterpret_cast<const uint2*>(a.emb + (size_t)row * kLmD + c4 * 4);
+    const float4 v = make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                                 __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u));
+    *reinterpret_cast<float4*>(a.h + t32_off(row, c4 * 4, kLmD / 4)) = v;
+    union { half_t e[4]; uint2 u; } o16;
+    o16.e[0] = (half_t)v.x; o16.e[1] = (half_t)v.y; o16.e[2] = (half_t)v.z; o16.e[3] = (half_t)v.w;
+    *reinterpret_cast<uint2*>(a.h16 + t16_off(row, c4 * 4, kLmD / 8)) = o16.u;
+  }
+}
+
+hipError_t launch_prefill_prologue(const PrefillPrologueArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.P < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_prologue_kernel, dim3((a.P + 63) / 64, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// The prefill's projections, M = B P rows: skinny kernels up to 1200 rows (600 for gate/up),
+// the pipelined kernel above (down at K = 2560 takes two 16 x 16 tiles at most per
+// workgroup in the skinny kernel, whose waves then hold 10 k-steps each).
+GemmPlan plan_prefill(int M, int N, int K, EMode em) {
+  GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);
+  auto skinny = [&](int rb, int cb) {
+    p.kind = 0; p.rb = rb; p.cb = cb;
+    return p;
+  };
+  auto big = [&](int bm, int stages) {
+    GemmPlan b = p;
+    b.kind = 2; b.bm = bm; b.stages = stages;
+    return b;
+  };
+  const bool down = em == E_PF_RESID && K > kLmD;
+  if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
+  if (em == E_SWIGLU) return M <= 600 ? skinny(2, 2) : big(128, 2);
+  if (M <= 1200) return down ? skinny(2, 1) : skinny(2, 2);
+  if (em == E_PF_RESID) return M <= 2400 ? big(64, 4) : M <= 4800 ? big(128, 4) : big(128, 2);
+  return big(128, 2);
 }
 
 // Inverse periods of the time embedding: 1 / (p_min (p_max/p_min)^(i/359)), fp64.

@@ -25,6 +25,11 @@ struct LayerDev {
   Mat qkv, o, gu, down;
 };
 
+// One layer of the prefix language model on the device.
+struct LmLayerDev {
+  Mat qkv, o, gu, down;
+};
+
 // Everything that distinguishes one enqueued call from another.
 struct CallKey {
   int velocity_mode;
@@ -103,6 +108,17 @@ struct smolexp_handle {
   bool have_probe = false;
   CallKey probe_key{};
   std::vector<Probe> probes[PR_COUNT];
+
+  // prefix language model (smolexp_prefill)
+  void* lmem = nullptr;
+  std::vector<LmLayerDev> lm;
+  bool lm_loaded = false;
+  void* pfmem = nullptr;   // its workspace, grown to the largest B x P seen
+  size_t pf_rows = 0;
+  float* pf_h = nullptr;
+  half_t *pf_h16 = nullptr, *pf_o16 = nullptr, *pf_u16 = nullptr;
+  bf16_t* pf_q = nullptr;
+  float2* pf_ropeq = nullptr;
 };
 
 namespace {
@@ -140,6 +156,12 @@ size_t layer_count(bool self_attn) {
   size_t n = kD + (size_t)kNQ * kD + (size_t)kD * kNQ + kD + 3 * (size_t)kFFN * kD;
   if (self_attn) n += 2 * (size_t)kNKV * kD;
   return n;
+}
+
+// Elements of one layer of the prefix language model (manifest order: norm1.g, q, k, v, o,
+// norm2.g, gate, up, down).
+size_t lm_layer_count() {
+  return kLmD + (size_t)kNQKV * kLmD + (size_t)kLmD * kNQ + kLmD + 3 * (size_t)kLmFFN * kLmD;
 }
 
 size_t count_weights(int n_layers) {
@@ -210,6 +232,43 @@ std::vector<const uint16_t*> rows_of(const uint16_t* p, int N, int ld, int c0 = 
   std::vector<const uint16_t*> r(N);
   for (int n = 0; n < N; ++n) r[n] = p + (size_t)n * ld + c0;
   return r;
+}
+
+// Rows of a layer's [Q; K; V] projection ([960 or 1600][K], V absent for cross layers) in
+// the order the kernels use: inside each Q and K head, 16-row block q holds dims q*8..q*8+7
+// then 32+q*8..32+q*8+7, so the rotation pairs (d, d + 32) share an MFMA tile.
+std::vector<const uint16_t*> rope_paired_rows(const uint16_t* pq, const uint16_t* pk, const uint16_t* pv, int K) {
+  const bool kv = pk != nullptr;
+  const int nrows = kv ? kNQKV : kNQ, rot_heads = kv ? kHQ + kHKV : kHQ;
+  std::vector<const uint16_t*> row_src(nrows);
+  for (int r = 0; r < kNQ; ++r) row_src[r] = pq + (size_t)r * K;
+  if (kv) {
+    for (int r = 0; r < kNKV; ++r) row_src[kNQ + r] = pk + (size_t)r * K;
+    for (int r = 0; r < kNKV; ++r) row_src[kNQ + kNKV + r] = pv + (size_t)r * K;
+  }
+  std::vector<const uint16_t*> perm(nrows);
+  for (int r = 0; r < nrows; ++r) {
+    const int head = r / kHD, rr = r % kHD;
+    int src = r;
+    if (head < rot_heads) {
+      const int q = rr / 16, e = rr % 16;
+      src = head * kHD + (e < 8 ? q * 8 + e : kHD / 2 + q * 8 + (e - 8));
+    }
+    perm[r] = row_src[src];
+  }
+  return perm;
+}
+
+// Rows of the [gate; up] projection ([2 F][K]) interleaved in 16-row blocks: block j holds
+// gate rows 8j..8j+7, then up rows 8j..8j+7 (the SwiGLU epilogue pairs them).
+std::vector<const uint16_t*> gate_up_rows(const uint16_t* pg, const uint16_t* pu, int F, int K) {
+  std::vector<const uint16_t*> gu(2 * (size_t)F);
+  for (int j = 0; j < F / 8; ++j)
+    for (int e = 0; e < 8; ++e) {
+      gu[16 * j + e] = pg + (size_t)(8 * j + e) * K;
+      gu[16 * j + 8 + e] = pu + (size_t)(8 * j + e) * K;
+    }
+  return gu;
 }
 
 int round16(int n) { return (n + 15) & ~15; }
@@ -448,6 +507,92 @@ int check_call(smolexp_t h, const void* kv, const uint8_t* mask, int P, const fl
   return SMOLEXP_OK;
 }
 
+// Grow the prefill workspace to hold `rows` = B P rows (synchronous; blocked operands are
+// padded to whole 16-row blocks).
+int ensure_prefill_workspace(smolexp_t h, size_t rows) {
+  if (rows <= h->pf_rows) return SMOLEXP_OK;
+  if (h->pfmem) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->pfmem);
+    h->pfmem = nullptr;
+    h->pf_rows = 0;
+  }
+  const size_t rp = (rows + 15) & ~(size_t)15;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t o_h = take(rp * kLmD * 4), o_h16 = take(rp * kLmD * 2), o_q = take(rows * kNQ * 2);
+  const size_t o_o = take(rp * kNQ * 2), o_u = take(rp * kLmFFN * 2), o_rq = take(rows * (kHD / 2) * sizeof(float2));
+  hipError_t e = hipMalloc(&h->pfmem, off);
+  if (e != hipSuccess) return fail(h, SMOLEXP_E_NOMEM, "prefill workspace allocation failed");
+  char* base = static_cast<char*>(h->pfmem);
+  h->pf_h = (float*)(base + o_h);
+  h->pf_h16 = (half_t*)(base + o_h16);
+  h->pf_q = (bf16_t*)(base + o_q);
+  h->pf_o16 = (half_t*)(base + o_o);
+  h->pf_u16 = (half_t*)(base + o_u);
+  h->pf_ropeq = (float2*)(base + o_rq);
+  h->pf_rows = rows;
+  return SMOLEXP_OK;
+}
+
+// The launch sequence of one prefill: per layer, RMSNorm'd Q/K/V with RoPE (K and V straight
+// into the cache), and for every layer but the last the prefix self-attention, o, gate/up
+// and down.
+int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, bf16_t* kv, int B, hipStream_t s) {
+  const int L = h->cfg.n_layers, M = B * P;
+  hipError_t e;
+  PrefillPrologueArgs pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.B = B; pp.P = P; pp.emb = emb; pp.mask = mask; pp.rope = h->rope;
+  pp.h = h->pf_h; pp.h16 = h->pf_h16; pp.ropeq = h->pf_ropeq;
+  if ((e = launch_prefill_prologue(pp, s)) != hipSuccess) return hip_fail(h, e, "prefill prologue launch");
+  auto gemm = [&](AMode am, EMode em, const GemmArgs& g) -> hipError_t {
+    const GemmPlan plan = plan_prefill(g.M, g.N, g.K, em);
+    if (plan.kind == 2) return launch_gemm_big(plan, em, am == A_NORM, g, s);
+    return launch_gemm(plan, am, em, g, s);
+  };
+  const size_t kvLayer = (size_t)2 * B * kHKV * (size_t)P * kHD;
+  for (int l = 0; l < L; ++l) {
+    const LmLayerDev& ld = h->lm[l];
+    bf16_t* kcache = kv + (size_t)l * kvLayer;
+    bf16_t* vcache = kcache + kvLayer / 2;
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.M = M;
+    g.inv_k = 1.0f / kLmD;
+    g.eps = h->cfg.rms_eps;
+
+    GemmArgs gq = g;
+    gq.N = kNQKV; gq.K = kLmD; gq.A = h->pf_h16; gq.lda = kLmD;
+    gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
+    gq.q = h->pf_q; gq.kc = kcache; gq.vc = vcache; gq.seq = P; gq.ropeq = h->pf_ropeq;
+    if ((e = gemm(A_NORM, E_PF_QKV, gq)) != hipSuccess) return hip_fail(h, e, "prefill qkv launch");
+    if (l == L - 1) break;  // the last layer's keys and values are all the cache needs
+
+    AttnArgs aa;
+    memset(&aa, 0, sizeof(aa));
+    aa.q = h->pf_q; aa.pk = kcache; aa.pv = vcache; aa.mask = mask; aa.out = h->pf_o16;
+    aa.B = B; aa.P = P; aa.seq = P;
+    if ((e = launch_prefix_attention(aa, s)) != hipSuccess) return hip_fail(h, e, "prefill attention launch");
+
+    GemmArgs go = g;
+    go.N = kLmD; go.K = kNQ; go.A = h->pf_o16; go.lda = kNQ;
+    go.W = ld.o.w; go.ldw = ld.o.ld; go.w_scale = ld.o.scale; go.h = h->pf_h; go.h16 = h->pf_h16;
+    if ((e = gemm(A_F16, E_PF_RESID, go)) != hipSuccess) return hip_fail(h, e, "prefill o launch");
+
+    GemmArgs gg = g;
+    gg.N = kLmGU; gg.K = kLmD; gg.A = h->pf_h16; gg.lda = kLmD;
+    gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = h->pf_u16; gg.ldo = kLmFFN;
+    if ((e = gemm(A_NORM, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "prefill gate/up launch");
+
+    GemmArgs gd = g;
+    gd.N = kLmD; gd.K = kLmFFN; gd.A = h->pf_u16; gd.lda = kLmFFN;
+    gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = h->pf_h; gd.h16 = h->pf_h16;
+    if ((e = gemm(A_F16, E_PF_RESID, gd)) != hipSuccess) return hip_fail(h, e, "prefill down launch");
+  }
+  return SMOLEXP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -654,43 +799,13 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     const uint16_t* pg = next((size_t)kFFN * kD);
     const uint16_t* pu = next((size_t)kFFN * kD);
     const uint16_t* pd = next((size_t)kD * kFFN);
-    // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone).  Inside each
-    // Q and K head, 16-row block q holds dims q*8..q*8+7 then 32+q*8..32+q*8+7, so the
-    // rotation pairs (d, d + 32) share an MFMA tile.
-    {
-      const int nrows = self_attn ? kNQKV : kNQ;
-      const int rot_heads = self_attn ? kHQ + kHKV : kHQ;
-      std::vector<const uint16_t*> row_src(nrows);
-      for (int r = 0; r < kNQ; ++r) row_src[r] = pq + (size_t)r * kD;
-      if (self_attn) {
-        for (int r = 0; r < kNKV; ++r) row_src[kNQ + r] = pk + (size_t)r * kD;
-        for (int r = 0; r < kNKV; ++r) row_src[kNQ + kNKV + r] = pvv + (size_t)r * kD;
-      }
-      std::vector<const uint16_t*> perm(nrows);
-      for (int r = 0; r < nrows; ++r) {
-        const int head = r / kHD, rr = r % kHD;
-        int src = r;
-        if (head < rot_heads) {
-          const int q = rr / 16, e = rr % 16;
-          src = head * kHD + (e < 8 ? q * 8 + e : kHD / 2 + q * 8 + (e - 8));
-        }
-        perm[r] = row_src[src];
-      }
-      s = pack_t16_gain(perm, kD, kKPad, g1, (half_t*)(hb + o_qkv[l]));
-    }
+    // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone)
+    s = pack_t16_gain(rope_paired_rows(pq, pk, pvv, kD), kD, kKPad, g1, (half_t*)(hb + o_qkv[l]));
     ld.qkv.scale = ldexpf(1.f, -s); ld.qkv.ld = kKPad;
     s = pick_shift({{po, (size_t)kD * kNQ}});
     pack_t16(rows_of(po, kD, kNQ), kNQ, kNQ, s, (half_t*)(hb + o_o[l]));
     ld.o.scale = ldexpf(1.f, -s); ld.o.ld = kNQ;
-    {
-      std::vector<const uint16_t*> gu(kGU);
-      for (int j = 0; j < kFFN / 8; ++j)  // rows 16j..16j+7 = gate 8j.., 16j+8..16j+15 = up 8j..
-        for (int e = 0; e < 8; ++e) {
-          gu[16 * j + e] = pg + (size_t)(8 * j + e) * kD;
-          gu[16 * j + 8 + e] = pu + (size_t)(8 * j + e) * kD;
-        }
-      s = pack_t16_gain(gu, kD, kKPad, g2, (half_t*)(hb + o_gu[l]));
-    }
+    s = pack_t16_gain(gate_up_rows(pg, pu, kFFN, kD), kD, kKPad, g2, (half_t*)(hb + o_gu[l]));
     ld.gu.scale = ldexpf(1.f, -s); ld.gu.ld = kKPad;
     s = pick_shift({{pd, (size_t)kD * kFFN}});
     pack_t16(rows_of(pd, kD, kFFN), kFFN, kFFN, s, (half_t*)(hb + o_dn[l]));
@@ -746,6 +861,103 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   if (e != hipSuccess) return hip_fail(h, e, "time vectors");
   h->loaded = true;
   return SMOLEXP_OK;
+}
+
+size_t smolexp_lm_weight_count(const smolexp_config* cfg) {
+  std::string why;
+  if (!check_config(cfg, &why)) return 0;
+  return (size_t)cfg->n_layers * lm_layer_count();
+}
+
+int smolexp_load_lm_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!bf16_host) return fail(h, SMOLEXP_E_INVAL, "weights pointer is NULL");
+  const int L = h->cfg.n_layers;
+  if (n_elems != (size_t)L * lm_layer_count())
+    return fail(h, SMOLEXP_E_SIZE, "weight count does not match the language model's manifest");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  const uint16_t* src = bf16_host;
+  // device layout per layer: [Q; K; V] rope-paired with norm1's gain folded, o, gate/up
+  // interleaved with norm2's gain folded, down; all fp16 blocked, K stored as is (960 and
+  // 2560 are multiples of 64)
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L);
+  for (int l = 0; l < L; ++l) {
+    o_qkv[l] = take((size_t)kNQKV * kLmD * 2);
+    o_o[l] = take((size_t)kLmD * kNQ * 2);
+    o_gu[l] = take((size_t)kLmGU * kLmD * 2);
+    o_dn[l] = take((size_t)kLmD * kLmFFN * 2);
+  }
+  std::vector<char> hostbuf;
+  try {
+    hostbuf.assign(off, 0);
+  } catch (...) {
+    return fail(h, SMOLEXP_E_NOMEM, "host staging allocation failed");
+  }
+  char* hb = hostbuf.data();
+  size_t pos = 0;
+  auto next = [&](size_t n) { const uint16_t* p = src + pos; pos += n; return p; };
+  std::vector<LmLayerDev> layers(L);
+  for (int l = 0; l < L; ++l) {
+    LmLayerDev& ld = layers[l];
+    const uint16_t* g1 = next(kLmD);
+    const uint16_t* pq = next((size_t)kNQ * kLmD);
+    const uint16_t* pk = next((size_t)kNKV * kLmD);
+    const uint16_t* pv = next((size_t)kNKV * kLmD);
+    const uint16_t* po = next((size_t)kLmD * kNQ);
+    const uint16_t* g2 = next(kLmD);
+    const uint16_t* pg = next((size_t)kLmFFN * kLmD);
+    const uint16_t* pu = next((size_t)kLmFFN * kLmD);
+    const uint16_t* pd = next((size_t)kLmD * kLmFFN);
+    int s = pack_t16_gain(rope_paired_rows(pq, pk, pv, kLmD), kLmD, kLmD, g1, (half_t*)(hb + o_qkv[l]));
+    ld.qkv.scale = ldexpf(1.f, -s); ld.qkv.ld = kLmD;
+    s = pick_shift({{po, (size_t)kLmD * kNQ}});
+    pack_t16(rows_of(po, kLmD, kNQ), kNQ, kNQ, s, (half_t*)(hb + o_o[l]));
+    ld.o.scale = ldexpf(1.f, -s); ld.o.ld = kNQ;
+    s = pack_t16_gain(gate_up_rows(pg, pu, kLmFFN, kLmD), kLmD, kLmD, g2, (half_t*)(hb + o_gu[l]));
+    ld.gu.scale = ldexpf(1.f, -s); ld.gu.ld = kLmD;
+    s = pick_shift({{pd, (size_t)kLmD * kLmFFN}});
+    pack_t16(rows_of(pd, kLmD, kLmFFN), kLmFFN, kLmFFN, s, (half_t*)(hb + o_dn[l]));
+    ld.down.scale = ldexpf(1.f, -s); ld.down.ld = kLmFFN;
+  }
+  if (h->lmem) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->lmem);
+    h->lmem = nullptr;
+    h->lm_loaded = false;
+  }
+  hipError_t e = hipMalloc(&h->lmem, off);
+  if (e != hipSuccess) return fail(h, SMOLEXP_E_NOMEM, "device weight allocation failed");
+  e = hipMemcpy(h->lmem, hb, off, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(h, e, "weight upload");
+  char* db = static_cast<char*>(h->lmem);
+  for (int l = 0; l < L; ++l) {
+    layers[l].qkv.w = (half_t*)(db + o_qkv[l]);
+    layers[l].o.w = (half_t*)(db + o_o[l]);
+    layers[l].gu.w = (half_t*)(db + o_gu[l]);
+    layers[l].down.w = (half_t*)(db + o_dn[l]);
+  }
+  h->lm = layers;
+  h->lm_loaded = true;
+  return SMOLEXP_OK;
+}
+
+int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_mask, int prefix_len,
+                    void* out_kv, int batch, void* hip_stream) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!h->lm_loaded) return fail(h, SMOLEXP_E_STATE, "language-model weights are not loaded");
+  if (!prefix_emb || !prefix_mask || !out_kv) return fail(h, SMOLEXP_E_INVAL, "a required pointer is NULL");
+  if (batch < 1 || batch > h->cfg.max_batch) return fail(h, SMOLEXP_E_INVAL, "batch out of range 1..max_batch");
+  if (prefix_len < 1 || prefix_len > h->cfg.max_prefix)
+    return fail(h, SMOLEXP_E_INVAL, "prefix_len out of range 1..max_prefix");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  const int rc = ensure_prefill_workspace(h, (size_t)batch * prefix_len);
+  if (rc != SMOLEXP_OK) return rc;
+  return enqueue_prefill(h, static_cast<const bf16_t*>(prefix_emb), prefix_mask, prefix_len,
+                         static_cast<bf16_t*>(out_kv), batch, static_cast<hipStream_t>(hip_stream));
 }
 
 int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
@@ -894,6 +1106,8 @@ void smolexp_destroy(smolexp_t h) {
   if (h->cap) (void)hipStreamDestroy(h->cap);
   if (h->wmem) (void)hipFree(h->wmem);
   if (h->wsmem) (void)hipFree(h->wsmem);
+  if (h->lmem) (void)hipFree(h->lmem);
+  if (h->pfmem) (void)hipFree(h->pfmem);
   delete h;
 }
 

@@ -21,6 +21,11 @@ constexpr int kNQKV = kNQ + 2 * kNKV;  // 1600
 constexpr int kGU = 2 * kFFN;          // 4096 (gate and up, interleaved in 16-row blocks)
 constexpr int kMaxSteps = 64;
 constexpr int kMaxLayers = 64;
+// The prefix language model that fills the per-layer K/V cache (SmolLM2 layers: width 960,
+// the same 15 / 5 heads of dim 64; the SwiGLU width is not on the pages, 2560 is SmolLM2-360M's).
+constexpr int kLmD = 960;
+constexpr int kLmFFN = 2560;
+constexpr int kLmGU = 2 * kLmFFN;      // 5120 (gate and up, interleaved in 16-row blocks)
 
 typedef _Float16 half_t;
 typedef uint16_t bf16_t;       // bf16 bit pattern
@@ -58,6 +63,8 @@ enum EMode : int {
   E_QKV = 4,       // RoPE on Q and K, scatter to Q/Kc/Vc bf16 (attention input)
   E_SWIGLU = 5,    // out16 = SiLU(gate) * up                 (FFN)
   E_ACTOUT = 6,    // v = acc + bias; x += dt * v             (action_out + Euler)
+  E_PF_QKV = 7,    // as E_QKV with `seq` rows per query: Q, and K/V into the cache (prefill)
+  E_PF_RESID = 8,  // as E_H_RESID at the prefix model's width (960 stored columns)
 };
 
 struct GemmArgs {
@@ -83,10 +90,11 @@ struct GemmArgs {
   int ldo;
   float* h;            // fp32 residual stream, blocked (t32_off), K = 720
   half_t* h16;         // its fp16 copy, blocked (t16_off), 768 stored columns (720.. stay zero)
-  bf16_t* q;
-  bf16_t* kc;
+  bf16_t* q;            // [B][15][seq][64]
+  bf16_t* kc;           // [B][5][seq][64]: the chunk's K (E_QKV), a cache layer's K (E_PF_QKV)
   bf16_t* vc;
-  const float2* ropeq;  // [row][32] (cos, sin) of each chunk row's position (valid prefix count + i)
+  int seq;              // rows per query (E_PF_QKV; E_QKV: the chunk, 50)
+  const float2* ropeq;  // [row][32] (cos, sin) of each row's position
   float dt;
   float* vel_out;
   float* st_out;
@@ -94,14 +102,15 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
-  const bf16_t* q;       // [B][15][50][64]
+  const bf16_t* q;       // [B][15][seq][64]
   const bf16_t* kc;      // [B][5][50][64] (self only)
   const bf16_t* vc;
   const bf16_t* pk;      // this layer's prefix K: [B][5][P][64]
   const bf16_t* pv;      // this layer's prefix V
   const uint8_t* mask;   // [B][P]
-  half_t* out;           // [B*50][960] fp16, blocked (t16_off)
+  half_t* out;           // [B*seq][960] fp16, blocked (t16_off)
   int B, P;
+  int seq;               // query rows per query head: the chunk (50), or the prefix (P) in a prefill
   // cross layers of a small batch (use_cross_q): the query projection runs in the
   // attention launch.  wq = the layer's Q weight ([960][768] blocked, RMSNorm gain
   // folded, values scaled by 1 / w_scale); h16 = fp16 residual [B*50][768] blocked.
@@ -160,5 +169,21 @@ hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int n_pos, float theta, hipStream_t s);
 hipError_t launch_inv_period_table(double* tab, float p_min, float p_max, hipStream_t s);
+
+// Prefill of the prefix language model.
+struct PrefillPrologueArgs {
+  int B, P;
+  const bf16_t* emb;       // [B][P][960] token embeddings
+  const uint8_t* mask;     // [B][P]
+  const float2* rope;      // [pos][32] (cos, sin) by position
+  float* h;                // out: fp32 residual [B*P][960], blocked (t32_off)
+  half_t* h16;             // out: its fp16 copy [B*P][960], blocked (t16_off)
+  float2* ropeq;           // out [B*P][32]: the rope rows at each token's position (valid tokens before it)
+};
+hipError_t launch_prefill_prologue(const PrefillPrologueArgs& a, hipStream_t s);
+// Prefix self-attention of a prefill: seq = P query rows per head, keys = the valid prefix tokens.
+hipError_t launch_prefix_attention(const AttnArgs& a, hipStream_t s);
+// The prefill's projections (M = B*P rows): skinny or pipelined kernels by size.
+GemmPlan plan_prefill(int M, int N, int K, EMode em);
 
 }  // namespace smolexp

@@ -173,6 +173,48 @@ int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_m
                      void* hip_stream);
 
 /*
+ * Prefix prefill: the step before the denoising loop, which fills the per-layer
+ * K/V cache that smolexp_denoise reads (noeira docs "SmolVLA", Architecture: the
+ * language model, SmolLM2, 16 layers of width 960 with grouped-query attention of
+ * 15 query heads over 5 KV heads of dim 64, RoPE, SwiGLU and RMSNorm, run once
+ * over the prefix; the block attention mask keeps the prefix from seeing the
+ * actions).  The handle's n_layers language-model layers fill n_layers cache
+ * layers.  Readings where the pages are silent: the prefix attends to itself in
+ * both directions (one block of the mask), pads are not keys; a token's RoPE
+ * position is the number of valid tokens before it (the chunk continues at
+ * n_valid + i), with the handle's rope_theta and rms_eps; SwiGLU width 2560; no
+ * biases.
+ *
+ * smolexp_lm_weight_count: elements of the language model's flat bf16 buffer,
+ * 9,832,320 per layer (0 for an invalid config).
+ *
+ * smolexp_load_lm_weights: bf16 bit patterns in manifest order, every matrix
+ * row-major [out, in]; per layer l: norm1.g [960], q.w [960,960],
+ * k.w [320,960], v.w [320,960], o.w [960,960], norm2.g [960],
+ * gate.w [2560,960], up.w [2560,960], down.w [960,2560].  Copied and re-encoded
+ * as for smolexp_load_weights; n_elems must equal smolexp_lm_weight_count (else
+ * SMOLEXP_E_SIZE).  Synchronous.
+ *
+ * smolexp_prefill (asynchronous on hip_stream; NULL = the null stream):
+ *   prefix_emb   device bf16 [batch][prefix_len][960]: the prefix token
+ *                embeddings (vision connector output, text embeddings, the
+ *                state token).  Read only.  Masked rows may hold anything.
+ *   prefix_mask  device uint8 [batch][prefix_len], nonzero = valid token.
+ *   out_kv       device bf16 [n_layers][2 (K, V)][batch][5][prefix_len][64]:
+ *                written; K after the rotation at each token's position.  This
+ *                is smolexp_denoise's prefix_kv.  Rows of masked tokens are
+ *                written but unspecified (they are never attended).
+ * The library keeps a workspace for batch x prefix_len rows; a call with more
+ * rows than any before it grows that workspace first, which synchronizes the
+ * device.  SMOLEXP_E_STATE before smolexp_load_lm_weights; SMOLEXP_E_INVAL for
+ * NULL pointers or batch / prefix_len outside 1..max_batch / 1..max_prefix.
+ */
+size_t smolexp_lm_weight_count(const smolexp_config* cfg);
+int smolexp_load_lm_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems);
+int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_mask, int prefix_len,
+                    void* out_kv, int batch, void* hip_stream);
+
+/*
  * Measurement hook: average duration in microseconds of one launch of one
  * kernel of the loop, timed with HIP events on hip_stream (synchronous) around
  * `reps` (1..100000) back-to-back launches.  Launch i repeats the (i mod n)-th

@@ -33,6 +33,21 @@ def test_library_exports_every_declared_symbol():
     assert set(fm.EXPORTED) == set(names)
 
 
+def test_lm_weight_count_matches_manifest():
+    for L in (1, 4, 16):
+        assert fm.smolexp_lm_weight_count(fm.smolexp_default_config(n_layers=L)) == synth.lm_weight_count(L)
+    assert fm.smolexp_lm_weight_count(fm.smolexp_default_config()) == 16 * 9_832_320
+    bad = fm.smolexp_default_config()
+    bad.head_dim = 32
+    assert fm.smolexp_lm_weight_count(bad) == 0
+
+
+def test_prefill_checks_arguments_before_any_launch():
+    lib = fm.raw()
+    assert lib.smolexp_prefill(None, None, None, 1, None, 1, None) == fm.SMOLEXP_E_INVAL
+    assert lib.smolexp_load_lm_weights(None, None, 0) == fm.SMOLEXP_E_INVAL
+
+
 def test_weight_count_matches_manifest():
     for L in (1, 2, 4, 16):
         assert fm.smolexp_weight_count(fm.smolexp_default_config(n_layers=L)) == synth.weight_count(L)

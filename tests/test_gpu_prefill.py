@@ -1,0 +1,177 @@
+"""GPU parity of the prefix prefill (smolexp_prefill), called through the C ABI,
+against the CPU oracle (oracle/prefill.py).
+
+Tolerance: per layer, K and V separately, ||gpu - oracle||_F / ||oracle||_F <= 1e-2
+over the valid tokens of the compared queries -- the bar of the expert's per-step
+velocities.  Storing the cache in bf16 alone costs ~2e-3 of it (relative RMS of
+bf16 rounding), the fp16 GEMM operands and bf16 attention of the 16 layers the rest.
+Rows of masked tokens are unspecified and not compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+import flow_matching_action_step_amd as fm
+import oracle
+import synth
+from gpu_util import Expert, to_device, run_gpu, compare
+
+pytestmark = pytest.mark.gpu
+
+KV_RTOL = 1e-2
+
+
+def _say(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+class Lm:
+    """A handle with the language model's weights (and optionally the expert's)."""
+
+    def __init__(self, n_layers, max_batch=8, max_prefix=256, expert=None):
+        self.cfg = fm.smolexp_default_config(n_layers=n_layers, max_batch=max_batch, max_prefix=max_prefix)
+        self.named = synth.draw_lm_weights(n_layers)
+        self.W = oracle.decode_weights(self.named)
+        self.ocfg = oracle.PrefillConfig(n_layers=n_layers)
+        self.h = fm.smolexp_create(self.cfg, 0)
+        fm.smolexp_load_lm_weights(self.h, synth.pack_lm_weights(self.named, n_layers))
+        if expert is not None:
+            fm.smolexp_load_weights(self.h, synth.pack_weights(expert, n_layers))
+
+    def prefill(self, emb_bits, mask):
+        B, P = mask.shape
+        L = self.cfg.n_layers
+        out = torch.full((L, 2, B, 5, P, 64), 0x7FC0, dtype=torch.int16, device="cuda")  # NaN bits
+        emb = torch.from_numpy(np.ascontiguousarray(emb_bits).view(np.int16)).cuda()
+        m = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+        fm.smolexp_prefill(self.h, self.cfg, emb, m, out)
+        torch.cuda.synchronize()
+        return out, out.cpu().numpy().view(np.uint16)
+
+    def close(self):
+        if self.h is not None:
+            fm.smolexp_destroy(self.h)
+            self.h = None
+
+
+def _check_kv(gpu_bits, orc, mask, queries, label):
+    """gpu_bits [L,2,B,5,P,64] bf16 bits; orc [L,2,len(queries),5,P,64] float64."""
+    g = oracle.bf16_bits_to_float(gpu_bits)
+    worst = 0.0
+    for l in range(orc.shape[0]):
+        for kv in range(2):
+            num = den = 0.0
+            for i, b in enumerate(queries):
+                v = mask[b].astype(bool)
+                d = g[l, kv, b][:, v] - orc[l, kv, i][:, v]
+                num += float(np.sum(d * d))
+                den += float(np.sum(orc[l, kv, i][:, v] ** 2))
+                assert np.isfinite(g[l, kv, b][:, v]).all(), f"{label} layer {l}: non-finite valid rows"
+            rel = np.sqrt(num / den)
+            worst = max(worst, rel)
+            assert rel <= KV_RTOL, f"{label} layer {l} {'KV'[kv]}: rel. error {rel:.3e} > {KV_RTOL}"
+    print(f"[parity] {label}: worst per-layer K/V rel. error {worst:.2e}", flush=True)
+    return worst
+
+
+def test_prefill_variable_prefixes_with_nan_pads():
+    _say("prefill, 4 layers, batch 3, P = 70, NaN pads")
+    lm = Lm(4)
+    try:
+        B, P = 3, 70
+        emb = synth.draw_prefix_embeddings(B, P)
+        mask = synth.make_mask(B, P, [70, 33, 1])
+        mask[0, [5, 6, 40]] = 0  # interleaved pads too
+        emb[mask == 0] = 0x7FC0  # NaN embeddings on every pad
+        _, got = lm.prefill(emb, mask)
+        orc = oracle.prefill_batch(lm.W, lm.ocfg, emb, mask)
+        _check_kv(got, orc, mask, [0, 1, 2], "prefill4 b3 p70")
+    finally:
+        lm.close()
+
+
+def test_prefill_16_layers_batch1():
+    _say("prefill, 16 layers, batch 1, P = 177")
+    lm = Lm(16, max_batch=1, max_prefix=177)
+    try:
+        emb = synth.draw_prefix_embeddings(1, 177)
+        mask = synth.make_mask(1, 177)
+        _, got = lm.prefill(emb, mask)
+        orc = oracle.prefill_batch(lm.W, lm.ocfg, emb, mask)
+        _check_kv(got, orc, mask, [0], "prefill16 b1 p177")
+    finally:
+        lm.close()
+
+
+def test_prefill_pipelined_gemm_sizes():
+    # batch 8 x 177 tokens = 1416 rows: the pipelined GEMM for every projection
+    _say("prefill, 4 layers, batch 8, P = 177 (sampled queries)")
+    lm = Lm(4, max_batch=8, max_prefix=177)
+    try:
+        B, P = 8, 177
+        emb = synth.draw_prefix_embeddings(B, P)
+        mask = synth.make_mask(B, P, synth.draw_lengths(B, 120, 177))
+        _, got = lm.prefill(emb, mask)
+        q = [0, 7]
+        orc = oracle.prefill_batch(lm.W, lm.ocfg, emb, mask, queries=q)
+        _check_kv(got, orc, mask, q, "prefill4 b8 p177")
+    finally:
+        lm.close()
+
+
+def test_prefill_then_denoise_end_to_end():
+    """The GPU cache feeds the GPU denoiser; the oracle's cache (rounded to bf16, as stored)
+    feeds the oracle's denoiser."""
+    _say("prefill + denoise, 4 layers, batch 2")
+    L, B, P = 4, 2, 90
+    expert = synth.draw_weights(L)
+    lm = Lm(L, max_batch=B, max_prefix=P, expert=expert)
+    try:
+        emb = synth.draw_prefix_embeddings(B, P)
+        mask = synth.make_mask(B, P, [90, 61])
+        kv_dev, kv_bits = lm.prefill(emb, mask)
+        noise = synth.draw_noise(B)
+        dev = {"kv": kv_dev, "mask": torch.from_numpy(mask).cuda(), "noise": torch.from_numpy(noise).cuda(),
+               "prev": None}
+        ex = object.__new__(Expert)
+        ex.h, ex.cfg = lm.h, lm.cfg
+        gpu = run_gpu(ex, dev)
+        orc_kv = oracle.round_to_bf16_bits(oracle.prefill_batch(lm.W, lm.ocfg, emb, mask))
+        Wx = oracle.decode_weights(expert)
+        x, vs, xs = oracle.denoise_batch(Wx, oracle.ExpertConfig(n_layers=L), orc_kv, mask, noise, n_steps=10,
+                                         record=True)
+        compare(gpu, {"out": x, "vel": vs, "st": xs}, [0, 1], noise, "prefill + denoise")
+        # the cache itself, at the valid tokens
+        _check_kv(kv_bits, oracle.prefill_batch(lm.W, lm.ocfg, emb, mask), mask, [0, 1], "prefill4 b2 p90")
+    finally:
+        lm.close()
+
+
+def test_prefill_inputs_untouched_deterministic_and_state_error():
+    _say("prefill: inputs untouched, determinism, errors")
+    lm = Lm(2, max_batch=2, max_prefix=64)
+    try:
+        emb = synth.draw_prefix_embeddings(2, 64)
+        mask = synth.make_mask(2, 64, [64, 20])
+        e_dev = torch.from_numpy(emb.view(np.int16)).cuda()
+        m_dev = torch.from_numpy(mask).cuda()
+        e0, m0 = e_dev.clone(), m_dev.clone()
+        outs = []
+        for _ in range(2):
+            out = torch.zeros((2, 2, 2, 5, 64, 64), dtype=torch.int16, device="cuda")
+            fm.smolexp_prefill(lm.h, lm.cfg, e_dev, m_dev, out)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert torch.equal(e_dev, e0) and torch.equal(m_dev, m0)
+        np.testing.assert_array_equal(outs[0], outs[1])
+        # the expert's weights were never loaded: denoise says so; a fresh handle refuses to prefill
+        cfg = fm.smolexp_default_config(n_layers=2, max_batch=2, max_prefix=64)
+        h2 = fm.smolexp_create(cfg, 0)
+        try:
+            import ctypes
+            p = ctypes.c_void_p(out.data_ptr())
+            assert fm.raw().smolexp_prefill(h2, p, p, 64, p, 2, None) == fm.SMOLEXP_E_STATE
+        finally:
+            fm.smolexp_destroy(h2)
+    finally:
+        lm.close()
