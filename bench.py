@@ -177,6 +177,100 @@ def cpu_baseline(wl, n_steps, min_seconds, max_seconds):
                       f"float64 numpy, {threads} BLAS thread(s), host {os.cpu_count()} logical CPUs"}
 
 
+def prefill_algorithmic(L, B, lengths, P):
+    """Bytes and flops of one prefill call, counted on the valid tokens: the language model's
+    weights once (bf16; the last layer needs only its K and V projections), embeddings read and
+    the K/V cache written (2 bytes each); projections 2 flops per multiply-add per token,
+    attention over valid keys for valid queries."""
+    n = [int(x) for x in lengths]
+    tok = float(sum(n))
+    macs_layer = 1600 * 960 + 960 * 960 + 5120 * 960 + 960 * 2560
+    macs_last = 640 * 960
+    wbytes = 2 * ((L - 1) * macs_layer + macs_last + L * 2 * 960)
+    io = 2 * tok * 960 + L * 2 * 5 * 64 * 2 * tok
+    flops = 2.0 * tok * ((L - 1) * macs_layer + macs_last) + 4.0 * 64 * 15 * (L - 1) * sum(x * x for x in n)
+    return wbytes + io, flops
+
+
+def run_prefill_stage(args):
+    """Time smolexp_prefill on the workload's batch and prefix (one JSON line)."""
+    import numpy as np
+    import torch
+    import synth
+    import flow_matching_action_step_amd as fm
+
+    wl = synth.make_workload(args.workload, with_weights=False)
+    L, B, P = wl["n_layers"], wl["batch"], wl["prefix_len"]
+    cfg = fm.smolexp_default_config(n_layers=L, max_batch=B, max_prefix=P)
+    h = fm.smolexp_create(cfg, 0)
+    named = synth.draw_lm_weights(L)
+    fm.smolexp_load_lm_weights(h, synth.pack_lm_weights(named, L))
+    emb_bits = synth.draw_prefix_embeddings(B, P)
+    emb = torch.from_numpy(emb_bits.view(np.int16)).cuda()
+    mask = torch.from_numpy(wl["mask"]).cuda()
+    out = torch.empty((L, 2, B, 5, P, 64), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fm.smolexp_prefill(h, cfg, emb, mask, out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms = wall / args.steps * 1e3
+    byt, fl = prefill_algorithmic(L, B, wl["lengths"], P)
+    intensity = fl / byt
+    if intensity < RIDGE:
+        roof = {"bound": "hbm", "achieved": byt / (ev_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fl / (ev_ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "whole prefill call (HIP events around the calls)"
+    roof["algorithmic_bytes_per_call"] = byt
+    roof["algorithmic_flops_per_call"] = fl
+    line = {
+        "metric": "prefix prefills/sec (language model, K/V cache of every layer)",
+        "value": B * args.steps / wall, "unit": "prefills/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "precision": "GEMM operands fp16 (bf16 weights re-encoded exactly; RMSNorm gains folded), attention bf16, "
+                     "fp32 accumulate and residual, K/V cache bf16",
+        "data": "synthetic (seeded: weights N(0,0.02) bf16, embeddings N(0,1) bf16)",
+        "config": {"workload": args.workload, "stage": "prefill", "n_layers": L, "batch": B, "prefix_len": P,
+                   "width": 960, "ffn": 2560},
+        "roofline": roof,
+        "event_ms_per_call": ev_ms,
+    }
+    fm.smolexp_destroy(h)
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        import oracle
+        W = oracle.decode_weights(named)
+        ocfg = oracle.PrefillConfig(n_layers=L)
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.prefill_batch(W, ocfg, emb_bits, wl["mask"], queries=[done % B])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el + el / done > 3 * args.cpu_seconds:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        line["cpu_baseline"] = {"value": done / el, "unit": "prefills/s", "cores": threads, "kind": "oracle",
+                                "sample": f"{done} whole prefill(s) of the first {min(done, B)} quer(ies), "
+                                          f"{el:.1f} s, float64 numpy, {threads} BLAS thread(s)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +278,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--n-steps", type=int, default=10, help="Euler steps per chunk (dt = -1/n)")
+    ap.add_argument("--stage", choices=("denoise", "prefill"), default="denoise",
+                    help="prefill: time the prefix language model that fills the K/V cache instead")
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -200,6 +296,10 @@ def main():
         print(f"bench.py measures one GPU: the denoising loop runs on a single MI355X and shards by query "
               f"(data parallel, no exchange); --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
+
+    if args.stage == "prefill":
+        run_prefill_stage(args)
+        return
 
     import numpy as np
     import torch

@@ -1682,11 +1682,10 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ----------------------------------------------------------------------------
 // Prefill of the prefix language model
 // ----------------------------------------------------------------------------
-// Prologue: workgroup (x, b) takes prefix tokens j0 = 64 x .. j0 + 63 of query b.  It writes
-// each token's RoPE row at its position (the number of valid tokens before it in the query:
-// a count of the mask before j0, then a running sum over the 64) and converts its bf16
-// embedding to the fp32 residual and its fp16 copy (blocked, 960 columns).
-__global__ __launch_bounds__(256) void prefill_prologue_kernel(const PrefillPrologueArgs a) {
+// Prologue, positions: workgroup (x, b) takes prefix tokens j0 = 64 x .. j0 + 63 of query b
+// and writes each token's RoPE row at its position (the number of valid tokens before it in
+// the query: a count of the mask before j0, then a running sum over the 64).
+__global__ __launch_bounds__(256) void prefill_rope_rows_kernel(const PrefillPrologueArgs a) {
   const int b = blockIdx.y, j0 = blockIdx.x * 64, tid = threadIdx.x, P = a.P;
   const uint8_t* mk = a.mask + (size_t)b * P;
   __shared__ int sCnt[256];
@@ -1713,29 +1712,45 @@ __global__ __launch_bounds__(256) void prefill_prologue_kernel(const PrefillProl
     const int i = e / (kHD / 2), d = e % (kHD / 2), j = j0 + i;
     if (j < P) a.ropeq[((size_t)b * P + j) * (kHD / 2) + d] = a.rope[(size_t)sPos[i] * (kHD / 2) + d];
   }
-  for (int e = tid; e < 64 * (kLmD / 4); e += 256) {
-    const int i = e / (kLmD / 4), c4 = e % (kLmD / 4), j = j0 + i;
-    if (j >= P) continue;
-    const int row = b * P + j;
-    const uint2 raw = *reinterpret_cast<const uint2*>(a.emb + (size_t)row * kLmD + c4 * 4);
+}
+
+// Prologue, residual: each thread converts 4 consecutive columns of one token's bf16
+// embedding to the fp32 residual and its fp16 copy (blocked, 960 columns); 16 consecutive
+// lanes take 16 consecutive rows of one column chunk, as the blocked layouts store them.
+__global__ __launch_bounds__(256) void prefill_embed_kernel(const PrefillPrologueArgs a) {
+  const size_t rows = (size_t)a.B * a.P, units = ((rows + 15) / 16) * 16 * (kLmD / 4);
+  for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (size_t)gridDim.x * 256) {
+    const size_t blk = u / (16 * (kLmD / 4)), rem = u % (16 * (kLmD / 4));
+    const int c4 = (int)(rem / 16);
+    const size_t row = blk * 16 + rem % 16;
+    if (row >= rows) continue;
+    const uint2 raw = *reinterpret_cast<const uint2*>(a.emb + row * kLmD + c4 * 4);
     const float4 v = make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                                  __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u));
-    *reinterpret_cast<float4*>(a.h + t32_off(row, c4 * 4, kLmD / 4)) = v;
+    *reinterpret_cast<float4*>(a.h + t32_off((int)row, c4 * 4, kLmD / 4)) = v;
     union { half_t e[4]; uint2 u; } o16;
     o16.e[0] = (half_t)v.x; o16.e[1] = (half_t)v.y; o16.e[2] = (half_t)v.z; o16.e[3] = (half_t)v.w;
-    *reinterpret_cast<uint2*>(a.h16 + t16_off(row, c4 * 4, kLmD / 8)) = o16.u;
+    *reinterpret_cast<uint2*>(a.h16 + t16_off((int)row, c4 * 4, kLmD / 8)) = o16.u;
   }
 }
 
 hipError_t launch_prefill_prologue(const PrefillPrologueArgs& a, hipStream_t s) {
   if (a.B < 1 || a.P < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_prologue_kernel, dim3((a.P + 63) / 64, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_rope_rows_kernel, dim3((a.P + 63) / 64, a.B), dim3(256), 0, s, a);
+  const size_t units = (((size_t)a.B * a.P + 15) / 16) * 16 * (kLmD / 4);
+  const size_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(prefill_embed_kernel, dim3(blocks < 4096 ? (unsigned)blocks : 4096u), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// The prefill's projections, M = B P rows: skinny kernels up to 1200 rows (600 for gate/up),
-// the pipelined kernel above (down at K = 2560 takes two 16 x 16 tiles at most per
-// workgroup in the skinny kernel, whose waves then hold 10 k-steps each).
+// The prefill's projections, M = B P rows, from a sweep at 177-2832 rows (us per launch,
+// weights rotating; skinny rb x cb against the pipelined kernel): Q/K/V skinny 2 x 2 up to 600
+// rows (177: 5.7), pipelined above (708: 12.8, 2832: 18.4, where 2 x 2 takes 47); o 2 x 2 up
+// to 400, 4 x 2 up to 1000 (708: 6.8), then 64-row and 128-row 4-stage tiles (1416: 10.1,
+// 2832: 13.1); gate/up 2 x 4 up to 300 rows (177: 7.7 against 12.0 pipelined), pipelined
+// above (1416: 18.2 against 34.0); down (K = 2560, ten k-steps per wave, at most two tiles
+// per workgroup) 1 x 2 up to 800 rows (708: 19.9), then 64-row and 128-row 4-stage tiles;
+// beyond 4800 rows o and down take the 2-stage ring as in the expert (two workgroups per CU).
 GemmPlan plan_prefill(int M, int N, int K, EMode em) {
   GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);
   auto skinny = [&](int rb, int cb) {
@@ -1747,12 +1762,23 @@ GemmPlan plan_prefill(int M, int N, int K, EMode em) {
     b.kind = 2; b.bm = bm; b.stages = stages;
     return b;
   };
-  const bool down = em == E_PF_RESID && K > kLmD;
   if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
-  if (em == E_SWIGLU) return M <= 600 ? skinny(2, 2) : big(128, 2);
-  if (M <= 1200) return down ? skinny(2, 1) : skinny(2, 2);
-  if (em == E_PF_RESID) return M <= 2400 ? big(64, 4) : M <= 4800 ? big(128, 4) : big(128, 2);
-  return big(128, 2);
+  switch (em) {
+    case E_PF_QKV:
+      return M <= 600 ? skinny(2, 2) : big(128, 2);
+    case E_SWIGLU:
+      return M <= 300 ? skinny(2, 4) : big(128, 2);
+    case E_PF_RESID:
+      if (K > kLmD) {  // down
+        if (M <= 800) return skinny(1, 2);
+      } else {  // o
+        if (M <= 400) return skinny(2, 2);
+        if (M <= 1000) return skinny(4, 2);
+      }
+      return M <= 2400 ? big(64, 4) : M <= 4800 ? big(128, 4) : big(128, 2);  // many tiles: two workgroups per CU
+    default:
+      return big(128, 2);
+  }
 }
 
 // Inverse periods of the time embedding: 1 / (p_min (p_max/p_min)^(i/359)), fp64.
