@@ -1149,9 +1149,16 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
   float* sO = reinterpret_cast<float*>(smem);    // [QG][KS][16][OLD], used after the last round
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qg = wave / KS, ks = wave % KS;
-  const int g = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid: the RG row groups of one (query, KV head) unit get the same
+  // i % 8 (workgroup i runs on XCD i % 8), so the K/V they all stage come through one L2;
+  // the return is uniform per workgroup and comes before any barrier
+  constexpr int RG = (3 * kChunk + 16 * QG - 1) / (16 * QG);
+  const int xcd = (int)(blockIdx.x & 7), jx = (int)(blockIdx.x >> 3);
+  const int u = 8 * (jx / RG) + xcd, rgx = jx % RG;
+  if (u >= kHKV * a.B) return;
+  const int g = u % kHKV, b = u / kHKV;
   const int P = a.P;
-  const int rq = blockIdx.x * (16 * QG) + qg * 16 + (lane & 15);
+  const int rq = rgx * (16 * QG) + qg * 16 + (lane & 15);
   const bool rvalid = rq < 3 * kChunk;
   const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
   const int qi = rvalid ? rq % kChunk : 0;
@@ -1210,7 +1217,7 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
     __syncthreads();
     for (int u = tid; u < QG * 16 * 16; u += NT) {
       const int q2 = u >> 8, row = (u >> 4) & 15, d0 = (u & 15) * 4;
-      const int rq2 = blockIdx.x * (16 * QG) + q2 * 16 + row;
+      const int rq2 = rgx * (16 * QG) + q2 * 16 + row;
       if (rq2 >= 3 * kChunk) continue;
       float mx = -INFINITY;
 #pragma unroll
@@ -1239,7 +1246,8 @@ static void launch_small(const AttnArgs& a, hipStream_t s) {
   // key blocks staged per round: the whole key range when it fits in five blocks
   const int nk = a.P + (SELF ? kChunk : 0);
   const int nblk = min(5, max(2, (nk + kKB - 1) / kKB));
-  const dim3 grid((3 * kChunk + 16 * QG - 1) / (16 * QG), kHKV, a.B), block(64 * QG * KS);
+  const int RG = (3 * kChunk + 16 * QG - 1) / (16 * QG);
+  const dim3 grid(8 * RG * ((kHKV * a.B + 7) / 8)), block(64 * QG * KS);
   switch (nblk) {
     case 2: hipLaunchKernelGGL((attn_small_kernel<SELF, 2, QG, KS>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((attn_small_kernel<SELF, 3, QG, KS>), grid, block, 0, s, a); break;
@@ -1289,7 +1297,14 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   float* sO = reinterpret_cast<float*>(sR);    // [wave][row][OLD] after the last round
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int rb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, g = hq / 3;
+  // one-dimensional grid: the 3 heads x RB row blocks of one (query, KV head) unit get the
+  // same i % 8 (workgroup i runs on XCD i % 8): each head's weight slice and the unit's K/V
+  // come through one L2; the return is uniform per workgroup and comes before any barrier
+  constexpr int RB = (kChunk + 15) / 16;
+  const int xcd = (int)(blockIdx.x & 7), jx = (int)(blockIdx.x >> 3);
+  const int u = 8 * (jx / (3 * RB)) + xcd, rr = jx % (3 * RB);
+  if (u >= kHKV * a.B) return;
+  const int g = u % kHKV, b = u / kHKV, hq = 3 * g + rr / RB, rb = rr % RB;
   const int P = a.P;
 
   // (1) projection operands of this wave's K slice, then the first round of keys
@@ -1568,7 +1583,8 @@ hipError_t launch_prefix_attention(const AttnArgs& a, hipStream_t s) {
 
 static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
   const int nblk = min(5, max(2, (a.P + kKB - 1) / kKB));
-  const dim3 grid((kChunk + 15) / 16, kHQ, a.B), block(512);
+  const int RB = (kChunk + 15) / 16;
+  const dim3 grid(8 * 3 * RB * ((kHKV * a.B + 7) / 8)), block(512);
   switch (nblk) {
     case 2: hipLaunchKernelGGL((attn_cross_q_kernel<2>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((attn_cross_q_kernel<3>), grid, block, 0, s, a); break;
