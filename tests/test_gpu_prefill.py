@@ -90,6 +90,25 @@ def test_prefill_variable_prefixes_with_nan_pads():
         lm.close()
 
 
+def test_prefill_edge_cases():
+    # P = 1 with one query that has no valid token (its rows are unspecified, the other
+    # query's must be exact), and ragged prefixes around a 64-key block edge at max_prefix
+    _say("prefill edge cases: P = 1, an empty query, P = max_prefix with ragged lengths")
+    lm = Lm(2, max_batch=3, max_prefix=130)
+    try:
+        emb = synth.draw_prefix_embeddings(2, 1)
+        mask = np.array([[1], [0]], np.uint8)
+        emb[1] = 0x7FC0  # NaN: the empty query must not leak into the other
+        _, got = lm.prefill(emb, mask)
+        _check_kv(got, oracle.prefill_batch(lm.W, lm.ocfg, emb, mask, queries=[0]), mask, [0], "P=1 [1, 0]")
+        emb = synth.draw_prefix_embeddings(3, 130)
+        mask = synth.make_mask(3, 130, [130, 64, 65])
+        _, got = lm.prefill(emb, mask)
+        _check_kv(got, oracle.prefill_batch(lm.W, lm.ocfg, emb, mask), mask, [0, 1, 2], "P=130 [130, 64, 65]")
+    finally:
+        lm.close()
+
+
 def test_prefill_16_layers_batch1():
     _say("prefill, 16 layers, batch 1, P = 177")
     lm = Lm(16, max_batch=1, max_prefix=177)
