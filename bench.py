@@ -31,6 +31,51 @@ KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed
 }
 
 
+class GpuStateSampler:
+    """Shader clock (the current level of pp_dpm_sclk) and board power (hwmon power1_input)
+    read from sysfs by a background thread every few milliseconds while the timed calls run;
+    None where the files are not readable."""
+
+    def __init__(self, period=0.005):
+        import glob
+        import threading
+        self.period = period
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk = cards[0] if cards else None
+        dev = os.path.dirname(cards[0]) if cards else None
+        pw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input"))) if dev else []
+        self.power = pw[0] if pw else None
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            if self.sclk:
+                for line in open(self.sclk):
+                    if line.rstrip().endswith("*"):
+                        self.mhz.append(float(line.split(":")[1].strip().split("Mhz")[0]))
+            if self.power:
+                self.watts.append(float(open(self.power).read()) / 1e6)
+        except (OSError, ValueError, IndexError):
+            pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            self._stop.wait(self.period)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join()
+        stat = lambda v: {"mean": sum(v) / len(v), "min": min(v), "max": max(v)} if v else None
+        return {"sclk_mhz": stat(self.mhz), "board_power_w": stat(self.watts), "samples": len(self.mhz)}
+
+
 def kernel_source_digest():
     """Digest of the HIP sources: a stored counter reading is only valid for the kernels it was taken on."""
     import hashlib
@@ -218,6 +263,7 @@ def run_prefill_stage(args):
         call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = GpuStateSampler().start()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -225,6 +271,7 @@ def run_prefill_stage(args):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_state = sampler.stop()
     ev_ms = e0.elapsed_time(e1) / args.steps
     ms = wall / args.steps * 1e3
     byt, fl = prefill_algorithmic(L, B, wl["lengths"], P)
@@ -250,6 +297,7 @@ def run_prefill_stage(args):
                    "width": 960, "ffn": 2560},
         "roofline": roof,
         "event_ms_per_call": ev_ms,
+        "gpu_state": gpu_state,
     }
     fm.smolexp_destroy(h)
     if not args.no_cpu_baseline:
@@ -326,6 +374,7 @@ def main():
         call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = GpuStateSampler().start()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -333,6 +382,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_state = sampler.stop()
     ev_ms = e0.elapsed_time(e1)
     assert torch.isfinite(out).all().item(), "non-finite actions"
 
@@ -392,6 +442,7 @@ def main():
         "roofline": roof,
         "loop_roofline": loop,
         "kernels": kern,
+        "gpu_state": gpu_state,
     }
     fm.smolexp_destroy(h)
     if args.copy_calibration:
