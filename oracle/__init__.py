@@ -46,7 +46,9 @@ Pins (what fixes each function other than itself; all in tests/):
                     complex-number rotary embedding
   expert (whole) .. chunk causality, pad invariance (NaN pads), batch
                     invariance, block-mask joint-pass equivalence, and
-                    degenerate-weight closed forms of the whole loop
+                    degenerate-weight closed forms of the whole loop; its own
+                    rounding (activations held in float32 move the velocity
+                    by < 1e-5 relative, far below the 1e-2 tolerance)
   schedule/Euler .. closed-form trajectories under stub velocity fields
                     (constant, linear, straight flow-matching path)
   overwrite ....... closed form under v = 0; fixed point on the straight path

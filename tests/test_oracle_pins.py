@@ -328,6 +328,19 @@ def test_expert_pad_invariance_with_nan_pads(small_model):
     np.testing.assert_allclose(v_perm, v0, rtol=1e-12, atol=1e-13)
 
 
+def test_oracle_float32_rounding_gap_is_far_below_the_tolerance(small_model):
+    """Every activation of the velocity field rounded to float32 (as a float32 evaluation
+    would hold it) moves the float64 result by orders of magnitude less than the 1e-2
+    velocity tolerance: the oracle's own rounding does not use up the parity budget."""
+    W, cfg, kv, mask, noise = small_model
+    pk, pv, pm = _query(kv, mask, 2)
+    x = noise[2].astype(np.float64)
+    v64 = oracle.velocity(W, cfg, x, 0.55, pk, pv, pm)
+    v32 = oracle.velocity(W, cfg, x, 0.55, pk, pv, pm, act_round=lambda a: a.astype(np.float32).astype(np.float64))
+    rel = np.linalg.norm(v32 - v64) / np.linalg.norm(v64)
+    assert 0.0 < rel < 1e-5, rel
+
+
 def test_expert_batch_invariance(small_model):
     W, cfg, kv, mask, noise = small_model
     xb = oracle.denoise_batch(W, cfg, kv, mask, noise, n_steps=2)
