@@ -96,6 +96,39 @@ def test_velocity_teacher_forced_4_layers(ex4):
         assert rel <= VEL_RTOL
 
 
+@pytest.mark.parametrize("n_layers", [1, 2])
+def test_velocity_one_self_layer_then_a_cross_layer(n_layers):
+    """One evaluation of v_theta with a single self-attention layer (embedding, RMSNorm'd
+    Q/K/V + RoPE, attention over prefix + causal chunk, o, SwiGLU MLP, head), then with the
+    cross-attention layer added, at batch 3 with ragged prefixes and random x and t: the layer
+    types in isolation, through the C ABI."""
+    _say(f"velocity, {n_layers} layer(s), batch 3, ragged prefixes")
+    ex = Expert(n_layers, max_batch=3, max_prefix=130, gain_seed=synth.gen.SEED_GAINS)
+    try:
+        B, P = 3, 130
+        kv = synth.draw_prefix_kv(n_layers, B, P)
+        mask = synth.make_mask(B, P, [130, 64, 1])
+        rng = np.random.default_rng(40 + n_layers)
+        x_np = rng.standard_normal((B, 50, 32)).astype(np.float32)
+        kv_d = torch.from_numpy(kv.view(np.int16)).cuda()
+        mask_d = torch.from_numpy(mask).cuda()
+        for t in (1.0, 0.37):
+            x = torch.from_numpy(x_np).cuda()
+            v = torch.empty_like(x)
+            fm.smolexp_velocity(ex.h, ex.cfg, kv_d, mask_d, x, t, v)
+            torch.cuda.synchronize()
+            got = v.cpu().numpy()
+            for b in range(B):
+                want = oracle.velocity(ex.W, ex.ocfg, x_np[b].astype(np.float64), np.float32(t),
+                                       oracle.bf16_bits_to_float(kv[:, 0, b]), oracle.bf16_bits_to_float(kv[:, 1, b]),
+                                       mask[b].astype(bool))
+                rel = np.linalg.norm(got[b] - want) / np.linalg.norm(want)
+                print(f"[parity] velocity L={n_layers} t={t} query {b}: rel {rel:.3e}", flush=True)
+                assert rel <= VEL_RTOL
+    finally:
+        ex.close()
+
+
 # ------------------------------------------------------------------ whole loop, the five workloads
 
 def test_denoise_4_layers_batch1(ex4):
