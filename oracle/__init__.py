@@ -63,6 +63,15 @@ Pins (what fixes each function other than itself; all in tests/):
                     prefix (layer-1 keys of token 0 depend on the last token,
                     layer-0 keys do not); one-token closed form; batch layout
     bf16 rounding . closed values (ties to even, subnormals)
+  training step (train.py: the flow-matching loss and the expert's weight gradients)
+    per-op derivatives  central finite differences (SiLU, RMSNorm, masked
+                    attention with empty and single-key rows); the rotary
+                    backward is the transpose (adjoint identity)
+    whole step .... central finite differences of the float64 batch loss along
+                    a random direction in every manifest tensor; torch autograd
+                    through a composition of torch library routines; closed
+                    form with a zero action_out matrix; the forward's velocity
+                    is expert.velocity's; query shares add up to the batch
 No function is left parity unpinned.
 """
 from .expert import (  # noqa: F401
@@ -72,4 +81,7 @@ from .expert import (  # noqa: F401
 from .flow import schedule, overwrite_rows, euler_denoise, denoise_query, denoise_batch  # noqa: F401
 from .prefill import (  # noqa: F401
     PrefillConfig, prefix_positions, prefill_layer, prefill, prefill_batch, round_to_bf16_bits,
+)
+from .train import (  # noqa: F401
+    silu_grad, linear_bwd, rms_norm_bwd, rope_bwd, attention_bwd, query_loss_and_grads, train_batch,
 )

@@ -16,6 +16,9 @@ kind of tensor, so that changing one input never shifts another:
     embeddings     seed 7   prefix token embeddings N(0, 1) rounded to bf16,
                             [B, P, 960] (what the vision connector and the text
                             embedding table would produce)
+    actions        seed 8   training targets: action chunks N(0, 1) fp32,
+                            [B, 50, 32] (normalised actions)
+    flow times     seed 9   training flow times, one per query, U(0, 1) fp32
 
 Floating-point draws are made in float32 and rounded to bf16 with
 round-to-nearest-even where the tensor is stored as bf16.  Everything is
@@ -40,6 +43,7 @@ TIME_DIM = 720      # sinusoidal time-embedding width
 
 SEED_WEIGHTS, SEED_NOISE, SEED_KV, SEED_LENGTHS, SEED_PREV, SEED_GAINS = 0, 1, 2, 3, 4, 5
 SEED_LM_WEIGHTS, SEED_EMB = 6, 7
+SEED_ACTIONS, SEED_TIMES = 8, 9
 
 # The language model that fills the prefix cache (noeira docs "SmolVLA",
 # Architecture table: SmolLM2, 16 layers of width 960, the same grouped-query
@@ -224,6 +228,16 @@ def draw_prev_actions(batch, rows, seed=SEED_PREV):
     """Tail of the previous chunk for prefix overwrite, N(0, 0.5) fp32 [B, d, 32]."""
     rng = np.random.default_rng(seed)
     return (np.float32(0.5) * rng.standard_normal((batch, rows, ACTION_DIM), dtype=np.float32)).astype(np.float32)
+
+
+def draw_actions(batch, seed=SEED_ACTIONS):
+    """Training action chunks a, N(0, 1) float32 [B, 50, 32]."""
+    return np.random.default_rng(seed).standard_normal((batch, CHUNK, ACTION_DIM), dtype=np.float32)
+
+
+def draw_flow_times(batch, seed=SEED_TIMES):
+    """Training flow times, one per query, uniform on [0, 1) float32 [B]."""
+    return np.random.default_rng(seed).random(batch, dtype=np.float32)
 
 
 def make_workload(name, batch=None, with_weights=True, gain_seed=None):
