@@ -59,6 +59,7 @@ _sig = {
     "smolexp_lm_weight_count": (ctypes.c_size_t, [ctypes.POINTER(smolexp_config)]),
     "smolexp_load_lm_weights": (ctypes.c_int, [_H, _P, ctypes.c_size_t]),
     "smolexp_prefill": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, ctypes.c_int, _P]),
+    "smolexp_train_step": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P]),
     "smolexp_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "smolexp_last_error": (ctypes.c_char_p, [_H]),
     "smolexp_destroy": (None, [_H]),
@@ -205,6 +206,25 @@ def smolexp_prefill(h, cfg, prefix_emb, prefix_mask, out_kv, stream=None):
     _need(out_kv, "out_kv", out_kv.dtype, _kv_shape(cfg, B, P))
     rc = _lib.smolexp_prefill(h, _ptr(prefix_emb), _ptr(prefix_mask), P, _ptr(out_kv), B, _stream(stream))
     _check(rc, h, "smolexp_prefill")
+
+
+def smolexp_train_step(h, cfg, prefix_kv, prefix_mask, actions, noise, t, out_grads, out_loss, stream=None):
+    """prefix_kv bf16 bits [L,2,B,5,P,64]; prefix_mask uint8 [B,P]; actions, noise fp32 [B,50,32];
+    t fp32 [B]; out_grads fp32 [weight_count] and out_loss fp32 [1], written."""
+    import torch
+    B, P = prefix_mask.shape
+    _need(prefix_mask, "prefix_mask", torch.uint8)
+    if prefix_kv.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise ValueError("prefix_kv must hold bf16 values")
+    _need(prefix_kv, "prefix_kv", prefix_kv.dtype, _kv_shape(cfg, B, P))
+    for name, x in (("actions", actions), ("noise", noise)):
+        _need(x, name, torch.float32, (B, 50, 32))
+    _need(t, "t", torch.float32, (B,))
+    _need(out_grads, "out_grads", torch.float32, (smolexp_weight_count(cfg),))
+    _need(out_loss, "out_loss", torch.float32, (1,))
+    rc = _lib.smolexp_train_step(h, _ptr(prefix_kv), _ptr(prefix_mask), P, _ptr(actions), _ptr(noise), _ptr(t),
+                                 _ptr(out_grads), _ptr(out_loss), B, _stream(stream))
+    _check(rc, h, "smolexp_train_step")
 
 
 def smolexp_time_kernel(h, kernel, reps, stream=None):

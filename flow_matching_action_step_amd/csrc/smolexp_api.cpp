@@ -3,6 +3,7 @@
 // sequence of one denoising call, and HIP-graph capture and replay of it.
 #include "smolexp.h"
 #include "smolexp_internal.h"
+#include "smolexp_train.h"
 
 #include <math.h>
 #include <string.h>
@@ -119,6 +120,14 @@ struct smolexp_handle {
   half_t *pf_h16 = nullptr, *pf_o16 = nullptr, *pf_u16 = nullptr;
   bf16_t* pf_q = nullptr;
   float2* pf_ropeq = nullptr;
+
+  // training step (smolexp_train_step): the manifest as loaded (bf16, row-major), the four
+  // biases widened to fp32, and the activation workspace grown to the largest batch seen
+  bf16_t* wraw = nullptr;
+  float* bias32 = nullptr;
+  void* trmem = nullptr;
+  int tr_B = 0, tr_P = 0;
+  TrainWs tws{};
 };
 
 namespace {
@@ -859,6 +868,30 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   e = launch_prologue(pa, h->cap);
   if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
   if (e != hipSuccess) return hip_fail(h, e, "time vectors");
+  // the training step reads the manifest as given, plus its biases in fp32
+  if (!h->wraw) {
+    if (hipMalloc(&h->wraw, n_elems * 2) != hipSuccess) return fail(h, SMOLEXP_E_NOMEM, "weight copy allocation failed");
+    if (hipMalloc(&h->bias32, (3 * kD + kAD) * sizeof(float)) != hipSuccess)
+      return fail(h, SMOLEXP_E_NOMEM, "bias copy allocation failed");
+  }
+  {
+    TrOffsets to;
+    train_offsets(L, 0, &to);
+    std::vector<float> b32(3 * kD + kAD);
+    auto widen = [&](size_t off, int n, float* dst) {
+      for (int i = 0; i < n; ++i) {
+        const uint32_t u = (uint32_t)src[off + i] << 16;
+        memcpy(&dst[i], &u, 4);
+      }
+    };
+    widen(to.ain_b, kD, b32.data());
+    widen(to.tin_b, kD, b32.data() + kD);
+    widen(to.tout_b, kD, b32.data() + 2 * kD);
+    widen(to.aout_b, kAD, b32.data() + 3 * kD);
+    e = hipMemcpy(h->wraw, src, n_elems * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(h->bias32, b32.data(), b32.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(h, e, "weight copy upload");
+  }
   h->loaded = true;
   return SMOLEXP_OK;
 }
@@ -958,6 +991,46 @@ int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_m
   if (rc != SMOLEXP_OK) return rc;
   return enqueue_prefill(h, static_cast<const bf16_t*>(prefix_emb), prefix_mask, prefix_len,
                          static_cast<bf16_t*>(out_kv), batch, static_cast<hipStream_t>(hip_stream));
+}
+
+int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                       const float* actions, const float* noise, const float* t, float* out_grads, float* out_loss,
+                       int batch, void* hip_stream) {
+  if (!h) return SMOLEXP_E_INVAL;
+  h->err.clear();
+  if (!h->loaded) return fail(h, SMOLEXP_E_STATE, "weights are not loaded");
+  if (!prefix_kv || !prefix_mask || !actions || !noise || !t || !out_grads || !out_loss)
+    return fail(h, SMOLEXP_E_INVAL, "a required pointer is NULL");
+  if (batch < 1 || batch > h->cfg.max_batch) return fail(h, SMOLEXP_E_INVAL, "batch out of range 1..max_batch");
+  if (prefix_len < 1 || prefix_len > h->cfg.max_prefix)
+    return fail(h, SMOLEXP_E_INVAL, "prefix_len out of range 1..max_prefix");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  const int L = h->cfg.n_layers;
+  if (batch > h->tr_B || prefix_len > h->tr_P) {
+    const int nb = batch > h->tr_B ? batch : h->tr_B, np = prefix_len > h->tr_P ? prefix_len : h->tr_P;
+    if (h->trmem) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(h->trmem);
+      h->trmem = nullptr;
+      h->tr_B = h->tr_P = 0;
+    }
+    if (hipMalloc(&h->trmem, train_workspace_bytes(nb, np, L)) != hipSuccess)
+      return fail(h, SMOLEXP_E_NOMEM, "training workspace allocation failed");
+    h->tr_B = nb;
+    h->tr_P = np;
+  }
+  TrainArgs ta;
+  memset(&ta, 0, sizeof(ta));
+  ta.B = batch; ta.P = prefix_len; ta.L = L;
+  ta.kv = static_cast<const bf16_t*>(prefix_kv); ta.mask = prefix_mask;
+  ta.actions = actions; ta.noise = noise; ta.t = t; ta.grads = out_grads; ta.loss = out_loss;
+  ta.w = h->wraw; ta.bias32 = h->bias32; ta.rope = h->rope; ta.inv_period = h->inv_period;
+  ta.rms_eps = h->cfg.rms_eps;
+  // the workspace is carved for this call's batch and prefix length (it holds at least that)
+  train_carve(static_cast<char*>(h->trmem), batch, prefix_len, L, &ta.ws);
+  const hipError_t e = train_enqueue(ta, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(h, e, "training step launch");
+  return SMOLEXP_OK;
 }
 
 int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
@@ -1108,6 +1181,9 @@ void smolexp_destroy(smolexp_t h) {
   if (h->wsmem) (void)hipFree(h->wsmem);
   if (h->lmem) (void)hipFree(h->lmem);
   if (h->pfmem) (void)hipFree(h->pfmem);
+  if (h->trmem) (void)hipFree(h->trmem);
+  if (h->wraw) (void)hipFree(h->wraw);
+  if (h->bias32) (void)hipFree(h->bias32);
   delete h;
 }
 

@@ -1,0 +1,843 @@
+// The expert's flow-matching training step on gfx950: forward with the activations kept,
+// the loss, and the backward pass to every weight gradient.
+//
+// noeira docs "SmolVLA", Architecture: a training sample is x_t = t eps + (1 - t) a and the
+// expert's velocity at (x_t, t) is regressed onto eps - a with a squared error; Fine-tuning:
+// only the expert trains, so the prefix keys/values are frozen inputs.  The loss is the mean
+// over the batch's B x 50 x 32 elements.
+//
+// Data layout: every activation is fp32 row-major [rows][columns] with rows = query * 50 +
+// chunk row; the weights are the manifest's bf16 matrices as given ([out][in] row-major); the
+// gradients are fp32 in manifest order.  All matrix products run on one bf16 MFMA kernel
+// (fp32 accumulate) that reads either operand along or across its contraction axis, so the
+// forward (x W^T), the input gradient (dy W) and the weight gradient (dy^T x) need no
+// transposed copies.  Attention keeps its scores in LDS and recomputes them in the backward
+// pass from the saved log-sum-exp; the prefix keys of a query are read through a compacted
+// list of its valid positions, so pads are never touched.
+#include "smolexp_internal.h"
+#include "smolexp_train.h"
+
+namespace smolexp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t bf16_bits(float f) {  // round to nearest, ties to even (finite inputs)
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+// four consecutive operand values as four bf16 (two per 32-bit word, low half first)
+__device__ inline uint2 load4(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return make_uint2(bf16_bits(v.x) | (bf16_bits(v.y) << 16), bf16_bits(v.z) | (bf16_bits(v.w) << 16));
+}
+__device__ inline uint2 load4(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// ------------------------------------------------------------------------------------------
+// C[m][n] = alpha sum_k A(m,k) B(n,k) (+ Cin[m][n]) (+ bias[n])
+//   A(m,k) = A[m lda + k] (AK) or A[k lda + m];  B(n,k) = B[n ldb + k] (BK) or B[k ldb + n].
+// 128 x 128 tiles, 32-deep k-slabs staged through LDS as bf16 (rows of 32 + 8 pad), four
+// waves of 64 x 64 (4 x 4 MFMA 16x16x32 tiles).  Each thread moves four 4-wide vectors per
+// operand per slab along the operand's contiguous axis; the next slab's loads are issued
+// before the current slab's MFMAs.  Out-of-range rows and k read as zero.
+constexpr int GBM = 128, GBN = 128, GBK = 32, GLD = GBK + 8;
+
+template <typename TA, bool AK, typename TB, bool BK>
+__global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[GBN * GLD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int M = g.M, N = g.N, K = g.K;
+  // tiles of one column stripe go to one XCD (workgroup i runs on XCD i % 8), so the
+  // B stripe it shares is read into one L2
+  const int nN = (N + GBN - 1) / GBN, nM = (M + GBM - 1) / GBM, T = nM * nN;
+  const int bid = blockIdx.x, xcd = bid & 7, j8 = bid >> 3, per = (T + 7) >> 3;
+  const int tile = xcd * per + j8;
+  if (tile >= T) return;
+  const int n0 = (tile / nM) * GBN, m0 = (tile % nM) * GBM;
+  const TA* A = static_cast<const TA*>(g.A);
+  const TB* Bm = static_cast<const TB*>(g.B);
+  uint2 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      if constexpr (AK) {
+        const int m = m0 + (idx >> 3), k = k0 + (idx & 7) * 4;
+        ra[i] = (m < M && k < K) ? load4(A + (size_t)m * g.lda + k) : make_uint2(0, 0);
+      } else {
+        const int k = k0 + (idx >> 5), m = m0 + (idx & 31) * 4;
+        ra[i] = (m < M && k < K) ? load4(A + (size_t)k * g.lda + m) : make_uint2(0, 0);
+      }
+      if constexpr (BK) {
+        const int n = n0 + (idx >> 3), k = k0 + (idx & 7) * 4;
+        rb[i] = (n < N && k < K) ? load4(Bm + (size_t)n * g.ldb + k) : make_uint2(0, 0);
+      } else {
+        const int k = k0 + (idx >> 5), n = n0 + (idx & 31) * 4;
+        rb[i] = (n < N && k < K) ? load4(Bm + (size_t)k * g.ldb + n) : make_uint2(0, 0);
+      }
+    }
+  };
+  auto put = [&](uint16_t* s, uint2 v, int idx, bool kcont) {
+    if (kcont) {
+      *reinterpret_cast<uint2*>(s + (idx >> 3) * GLD + (idx & 7) * 4) = v;
+    } else {
+      const int k = idx >> 5, r = (idx & 31) * 4;
+      s[(r + 0) * GLD + k] = (uint16_t)(v.x & 0xFFFF);
+      s[(r + 1) * GLD + k] = (uint16_t)(v.x >> 16);
+      s[(r + 2) * GLD + k] = (uint16_t)(v.y & 0xFFFF);
+      s[(r + 3) * GLD + k] = (uint16_t)(v.y >> 16);
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+  for (int k0 = 0; k0 < K; k0 += GBK) {
+    __syncthreads();  // every wave is done reading the previous slab
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      put(sA, ra[i], tid + 256 * i, AK);
+      put(sB, rb[i], tid + 256 * i, BK);
+    }
+    __syncthreads();
+    if (k0 + GBK < K) gload(k0 + GBK);
+    bf16x8 af[4], bw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + (lane & 15)) * GLD + (lane >> 4) * 8);
+      bw[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + i * 16 + (lane & 15)) * GLD + (lane >> 4) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+  }
+  // lane l of a 16 x 16 tile holds rows 4 (l / 16) + r, column l % 16
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r, col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (row < M && col < N) {
+          float v = g.alpha * acc[i][j][r];
+          if (g.Cin) v += g.Cin[(size_t)row * g.ldc + col];
+          if (g.bias) v += g.bias[col];
+          g.C[(size_t)row * g.ldc + col] = v;
+        }
+      }
+}
+
+// ------------------------------------------------------------------------------------------
+// Per query: the compacted list of valid prefix positions and their count.
+__global__ __launch_bounds__(64) void tr_prep_kernel(const uint8_t* mask, int P, int* vidx, int* nval) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int n = 0;
+  for (int j0 = 0; j0 < P; j0 += 64) {
+    const int j = j0 + lane;
+    const bool v = j < P && mask[(size_t)b * P + j] != 0;
+    const uint64_t bal = __ballot(v);
+    if (v) vidx[(size_t)b * P + n + __popcll(bal & ((1ull << lane) - 1))] = j;
+    n += __popcll(bal);
+  }
+  if (lane == 0) nval[b] = n;
+}
+
+// Training inputs of one chunk row: x_t = t eps + (1 - t) a, the target eps - a, and the
+// time embedding e(t) of the row's query in columns 720.. of z (z = [action_in(x_t) ; e(t)]).
+__global__ __launch_bounds__(256) void tr_input_kernel(const float* act, const float* noise, const float* t,
+                                                       const double* inv_period, float* xt, float* target, float* z) {
+  const int row = blockIdx.x, b = row / kChunk, tid = threadIdx.x;
+  const float tb = t[b];
+  if (tid < kAD) {
+    const size_t o = (size_t)row * kAD + tid;
+    const float e = noise[o], a = act[o];
+    xt[o] = tb * e + (1.f - tb) * a;
+    target[o] = e - a;
+  }
+  for (int k = tid; k < kD; k += 256) {
+    const int half = kD / 2, kk = k % half;
+    const double ang = 6.283185307179586 * (double)tb * inv_period[kk];
+    z[(size_t)row * (2 * kD) + kD + k] = (float)(k < half ? sin(ang) : cos(ang));
+  }
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// RMSNorm of 720-wide rows, one wave per row: n = h r g with r = (mean(h^2) + eps)^(-1/2).
+__global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const bf16_t* g, float eps, int M, float* n,
+                                                         float* rstd) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const float* hr = h + (size_t)row * kD;
+  float ss = 0.f;
+  for (int c = lane; c < kD; c += 64) ss += hr[c] * hr[c];
+  const float r = rsqrtf(wave_sum(ss) / kD + eps);
+  for (int c = lane; c < kD; c += 64) n[(size_t)row * kD + c] = hr[c] * r * bf16_val(g[c]);
+  if (lane == 0) rstd[row] = r;
+}
+
+// Backward of the RMSNorm above over 32 rows per workgroup:
+//   dh = r (u - hat mean(u hat)) (+ resid), u = dy g, hat = h r;
+//   part[blk][c] = sum over the block's rows of dy hat (the gain's gradient, before the
+//   sum over blocks).  dh may alias resid.
+constexpr int kRB = 32;
+__global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, const float* h, const float* rstd,
+                                                             const bf16_t* g, const float* resid, float* dh, int M,
+                                                             float* part) {
+  const int blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int rr = w; rr < kRB; rr += 4) {
+    const int row = blk * kRB + rr;
+    if (row >= M) break;
+    const float r = rstd[row];
+    const float* dyr = dy + (size_t)row * kD;
+    const float* hr = h + (size_t)row * kD;
+    float s = 0.f;
+    for (int c = lane; c < kD; c += 64) s += dyr[c] * bf16_val(g[c]) * hr[c] * r;
+    const float mean = wave_sum(s) / kD;
+    for (int c = lane; c < kD; c += 64) {
+      const float hat = hr[c] * r;
+      float v = r * (dyr[c] * bf16_val(g[c]) - hat * mean);
+      if (resid) v += resid[(size_t)row * kD + c];
+      dh[(size_t)row * kD + c] = v;
+    }
+  }
+  for (int c = tid; c < kD; c += 256) {
+    float s = 0.f;
+    for (int rr = 0; rr < kRB; ++rr) {
+      const int row = blk * kRB + rr;
+      if (row >= M) break;
+      s += dy[(size_t)row * kD + c] * h[(size_t)row * kD + c] * rstd[row];
+    }
+    part[(size_t)blk * kD + c] = s;
+  }
+}
+
+// Column sums of x [M][N] over blocks of 32 rows: part[blk][c].
+__global__ __launch_bounds__(256) void tr_colsum_kernel(const float* x, int M, int N, float* part) {
+  const int c = blockIdx.x * 256 + threadIdx.x, blk = blockIdx.y;
+  if (c >= N) return;
+  float s = 0.f;
+  for (int rr = 0; rr < kRB; ++rr) {
+    const int row = blk * kRB + rr;
+    if (row >= M) break;
+    s += x[(size_t)row * N + c];
+  }
+  part[(size_t)blk * N + c] = s;
+}
+
+// out[c] = sum over blocks of part[blk][c], in block order (deterministic).
+__global__ __launch_bounds__(256) void tr_reduce_kernel(const float* part, int nblk, int N, float* out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
+  float s = 0.f;
+  for (int b = 0; b < nblk; ++b) s += part[(size_t)b * N + c];
+  out[c] = s;
+}
+
+__device__ inline float silu_f(float z) { return z / (1.f + __expf(-z)); }
+__device__ inline float silu_grad_f(float z) {
+  const float s = 1.f / (1.f + __expf(-z));
+  return s * (1.f + z * (1.f - s));
+}
+
+__global__ __launch_bounds__(256) void tr_silu_kernel(const float* s, float* out, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = silu_f(s[i]);
+}
+__global__ __launch_bounds__(256) void tr_silu_bwd_kernel(const float* d, const float* s, float* out, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = d[i] * silu_grad_f(s[i]);
+}
+
+// gu [M][4096] = [gate | up]; act = SiLU(gate) up.
+__global__ __launch_bounds__(256) void tr_swiglu_kernel(const float* gu, float* act, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t row = i / kFFN, c = i % kFFN;
+    act[i] = silu_f(gu[row * kGU + c]) * gu[row * kGU + kFFN + c];
+  }
+}
+__global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, const float* gu, float* dgu, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t row = i / kFFN, c = i % kFFN;
+    const float gt = gu[row * kGU + c], up = gu[row * kGU + kFFN + c], d = dact[i];
+    dgu[row * kGU + c] = d * up * silu_grad_f(gt);
+    dgu[row * kGU + kFFN + c] = d * silu_f(gt);
+  }
+}
+
+// RoPE (pairs d, d + 32) on the Q heads (and the self layers' K heads) of qkv rows, in place,
+// at position n_valid(b) + i.  dir = +1 rotates, -1 applies the transpose (the backward).
+__global__ __launch_bounds__(256) void tr_rope_kernel(float* qkv, int ldq, int n_heads, const int* nval,
+                                                      const float2* rope, float dir) {
+  const int row = blockIdx.x, b = row / kChunk, i = row % kChunk;
+  const float2* cs = rope + (size_t)(nval[b] + i) * (kHD / 2);
+  for (int p = threadIdx.x; p < n_heads * (kHD / 2); p += 256) {
+    const int hd = p / (kHD / 2), k = p % (kHD / 2);
+    float* x = qkv + (size_t)row * ldq + hd * kHD;
+    const float c = cs[k].x, s = dir * cs[k].y;
+    const float x1 = x[k], x2 = x[k + kHD / 2];
+    x[k] = x1 * c - x2 * s;
+    x[k + kHD / 2] = x1 * s + x2 * c;
+  }
+}
+
+// Self layers: the chunk keys' gradients, summed over the three query heads of each KV head
+// from the per-head parts dkv [B][15][2][50][64], into columns 960.. (K, rotated back) and
+// 1280.. (V) of dqkv.
+__global__ __launch_bounds__(256) void tr_kv_grad_kernel(const float* dkv, const int* nval, const float2* rope,
+                                                         float* dqkv) {
+  const int row = blockIdx.x, b = row / kChunk, i = row % kChunk;
+  const float2* cs = rope + (size_t)(nval[b] + i) * (kHD / 2);
+  auto part = [&](int h, int kv, int d) {
+    return dkv[((((size_t)b * kHQ + h) * 2 + kv) * kChunk + i) * kHD + d];
+  };
+  const int grp = kHQ / kHKV;
+  for (int p = threadIdx.x; p < kHKV * (kHD / 2); p += 256) {
+    const int g = p / (kHD / 2), k = p % (kHD / 2);
+    float y1 = 0.f, y2 = 0.f;
+    for (int u = 0; u < grp; ++u) {
+      y1 += part(g * grp + u, 0, k);
+      y2 += part(g * grp + u, 0, k + kHD / 2);
+    }
+    const float c = cs[k].x, s = cs[k].y;
+    float* x = dqkv + (size_t)row * kNQKV + kNQ + g * kHD;
+    x[k] = y1 * c + y2 * s;
+    x[k + kHD / 2] = -y1 * s + y2 * c;
+  }
+  for (int p = threadIdx.x; p < kNKV; p += 256) {
+    const int g = p / kHD, d = p % kHD;
+    float y = 0.f;
+    for (int u = 0; u < grp; ++u) y += part(g * grp + u, 1, d);
+    dqkv[(size_t)row * kNQKV + kNQ + kNKV + p] = y;
+  }
+}
+
+// Loss terms over 8 rows per workgroup: err = v - target, dv = 2 err / n_total, and the
+// block's sum of err^2.
+__global__ __launch_bounds__(256) void tr_loss_kernel(const float* v, const float* target, int M, float inv_n,
+                                                      float* dv, float* part) {
+  __shared__ float red[4];
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5), c = threadIdx.x & 31;
+  float e2 = 0.f;
+  if (row < M) {
+    const size_t o = (size_t)row * kAD + c;
+    const float err = v[o] - target[o];
+    dv[o] = 2.f * err * inv_n;
+    e2 = err * err;
+  }
+  e2 = wave_sum(e2);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = e2;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void tr_scale_kernel(float* x, float s) { *x *= s; }
+
+// ------------------------------------------------------------------------------------------
+// Attention of one (query, Q head) per workgroup over its keys: the valid prefix keys (from
+// the compacted position list), then, in self layers, the chunk's keys j <= i.  Scores in
+// fp32 from fp32 Q/K (bf16 prefix keys widened), exact two-pass softmax: pass 1 the row
+// maxima and sums (saved as log-sum-exp), pass 2 P = exp(S - lse) and O = P V.
+constexpr int kKB = 64;  // keys per block
+constexpr int kRows = kChunk;
+constexpr int kRPT = (kRows + 3) / 4;  // rows per thread (4 waves stride the 50 rows)
+
+struct AttnSmem {
+  float q[kRows * kHD];
+  float k[kKB * (kHD + 1)];
+  float v[kKB * (kHD + 1)];
+  float s[kRows * (kKB + 1)];
+  float m[kRows], l[kRows];
+};
+
+template <bool SELF>
+__device__ inline void load_keys(const TrAttn& a, int b, int g, int nb, int kb, float* sk, float* sv, bool want_v) {
+  const int tid = threadIdx.x, j = tid >> 2, d0 = (tid & 3) * 16, kidx = kb * kKB + j;
+  float kk[16], vv[16];
+  if (kidx < nb) {
+    const size_t o = (((size_t)b * kHKV + g) * a.P + a.vidx[(size_t)b * a.P + kidx]) * kHD + d0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      kk[u] = bf16_val(a.pk[o + u]);
+      vv[u] = want_v ? bf16_val(a.pv[o + u]) : 0.f;
+    }
+  } else if (SELF && kidx < nb + kChunk) {
+    const float* src = a.qkv + (size_t)(b * kChunk + kidx - nb) * a.ldq;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      kk[u] = src[kNQ + g * kHD + d0 + u];
+      vv[u] = want_v ? src[kNQ + kNKV + g * kHD + d0 + u] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) kk[u] = vv[u] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    sk[j * (kHD + 1) + d0 + u] = kk[u];
+    sv[j * (kHD + 1) + d0 + u] = vv[u];
+  }
+}
+
+template <bool SELF>
+__device__ inline bool key_ok(int kidx, int nb, int i) {
+  return kidx < nb || (SELF && kidx < nb + kChunk && kidx - nb <= i);
+}
+
+template <bool SELF>
+__global__ __launch_bounds__(256) void tr_attn_fwd_kernel(const TrAttn a) {
+  __shared__ AttnSmem sm;
+  const int h = blockIdx.x, b = blockIdx.y, g = h / (kHQ / kHKV);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = a.nval[b], nk = nb + (SELF ? kChunk : 0), nblk = (nk + kKB - 1) / kKB;
+  const float scale = 0.125f;
+  for (int e = tid; e < kRows * kHD; e += 256) {
+    const int i = e / kHD, d = e % kHD;
+    sm.q[e] = a.qkv[(size_t)(b * kChunk + i) * a.ldq + h * kHD + d] * scale;
+  }
+  if (tid < kRows) {
+    sm.m[tid] = -INFINITY;
+    sm.l[tid] = 0.f;
+  }
+  float kr[kHD];
+  // pass 1: row maxima and sums
+  for (int kb = 0; kb < nblk; ++kb) {
+    __syncthreads();
+    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, false);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kHD; ++d) kr[d] = sm.k[lane * (kHD + 1) + d];
+    const int kidx = kb * kKB + lane;
+    for (int r = 0; r < kRPT; ++r) {
+      const int i = w + 4 * r;
+      if (i >= kRows) break;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHD; ++d) s += sm.q[i * kHD + d] * kr[d];
+      const bool ok = key_ok<SELF>(kidx, nb, i);
+      const float mb = wave_max(ok ? s : -INFINITY);
+      if (mb != -INFINITY) {
+        const float sum = wave_sum(ok ? __expf(s - mb) : 0.f);
+        if (lane == 0) {
+          const float mo = sm.m[i], mn = fmaxf(mo, mb);
+          sm.l[i] = sm.l[i] * __expf(mo - mn) + sum * __expf(mb - mn);
+          sm.m[i] = mn;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kRows) {
+    const float lse = sm.l[tid] > 0.f ? sm.m[tid] + __logf(sm.l[tid]) : INFINITY;  // no key: P = 0
+    sm.m[tid] = lse;
+    a.lse[((size_t)b * kHQ + h) * kRows + tid] = lse;
+  }
+  // pass 2: O = exp(S - lse) V
+  float o[kRPT];
+#pragma unroll
+  for (int r = 0; r < kRPT; ++r) o[r] = 0.f;
+  for (int kb = 0; kb < nblk; ++kb) {
+    __syncthreads();
+    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, true);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kHD; ++d) kr[d] = sm.k[lane * (kHD + 1) + d];
+    const int kidx = kb * kKB + lane;
+    for (int r = 0; r < kRPT; ++r) {
+      const int i = w + 4 * r;
+      if (i >= kRows) break;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHD; ++d) s += sm.q[i * kHD + d] * kr[d];
+      sm.s[i * (kKB + 1) + lane] = key_ok<SELF>(kidx, nb, i) ? __expf(s - sm.m[i]) : 0.f;
+    }
+    __syncthreads();
+    const int kn = min(kKB, nk - kb * kKB);
+#pragma unroll
+    for (int r = 0; r < kRPT; ++r) {
+      const int i = w + 4 * r;
+      if (i < kRows) {
+        float acc = 0.f;
+        for (int j = 0; j < kn; ++j) acc += sm.s[i * (kKB + 1) + j] * sm.v[j * (kHD + 1) + lane];
+        o[r] += acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRPT; ++r) {
+    const int i = w + 4 * r;
+    if (i < kRows) a.o[(size_t)(b * kChunk + i) * kNQ + h * kHD + lane] = o[r];
+  }
+}
+
+// Backward of the attention above, one (query, Q head) per workgroup.  D_i = dO_i . O_i;
+// per key block: P = exp(S - lse), dP = dO V^T, dS = P (dP - D); dQ += dS K; the chunk's keys
+// (self layers) get this head's dK = dS^T Q and dV = P^T dO in dkv.  Q is held pre-scaled, so
+// S and dK carry the 1/8 already; dQ takes it at the end.
+struct AttnBwdSmem {
+  float q[kRows * kHD];
+  float dout[kRows * kHD];
+  float k[kKB * (kHD + 1)];
+  float v[kKB * (kHD + 1)];
+  float p[kRows * (kKB + 1)];
+  float ds[kRows * (kKB + 1)];
+  float dd[kRows], lse[kRows];
+};
+
+template <bool SELF>
+__global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
+  __shared__ AttnBwdSmem sm;
+  const int h = blockIdx.x, b = blockIdx.y, g = h / (kHQ / kHKV);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = a.nval[b], nk = nb + (SELF ? kChunk : 0), nblk = (nk + kKB - 1) / kKB;
+  const float scale = 0.125f;
+  for (int e = tid; e < kRows * kHD; e += 256) {
+    const int i = e / kHD, d = e % kHD;
+    const size_t row = (size_t)(b * kChunk + i);
+    sm.q[e] = a.qkv[row * a.ldq + h * kHD + d] * scale;
+    sm.dout[e] = a.dout[row * kNQ + h * kHD + d];
+  }
+  for (int i = w; i < kRows; i += 4) {
+    const size_t row = (size_t)(b * kChunk + i);
+    const float s = wave_sum(a.dout[row * kNQ + h * kHD + lane] * a.o[row * kNQ + h * kHD + lane]);
+    if (lane == 0) {
+      sm.dd[i] = s;
+      sm.lse[i] = a.lse[((size_t)b * kHQ + h) * kRows + i];
+    }
+  }
+  float dq[kRPT];
+#pragma unroll
+  for (int r = 0; r < kRPT; ++r) dq[r] = 0.f;
+  float kr[kHD], vr[kHD];
+  for (int kb = 0; kb < nblk; ++kb) {
+    __syncthreads();
+    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, true);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kHD; ++d) {
+      kr[d] = sm.k[lane * (kHD + 1) + d];
+      vr[d] = sm.v[lane * (kHD + 1) + d];
+    }
+    const int kidx = kb * kKB + lane;
+    for (int r = 0; r < kRPT; ++r) {
+      const int i = w + 4 * r;
+      if (i >= kRows) break;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < kHD; ++d) {
+        s += sm.q[i * kHD + d] * kr[d];
+        dp += sm.dout[i * kHD + d] * vr[d];
+      }
+      const float p = key_ok<SELF>(kidx, nb, i) ? __expf(s - sm.lse[i]) : 0.f;
+      sm.p[i * (kKB + 1) + lane] = p;
+      sm.ds[i * (kKB + 1) + lane] = p * (dp - sm.dd[i]);
+    }
+    __syncthreads();
+    const int kn = min(kKB, nk - kb * kKB);
+#pragma unroll
+    for (int r = 0; r < kRPT; ++r) {
+      const int i = w + 4 * r;
+      if (i < kRows) {
+        float acc = 0.f;
+        for (int j = 0; j < kn; ++j) acc += sm.ds[i * (kKB + 1) + j] * sm.k[j * (kHD + 1) + lane];
+        dq[r] += acc;
+      }
+    }
+    if constexpr (SELF) {
+      for (int j = w; j < kn; j += 4) {
+        const int c = kb * kKB + j - nb;  // chunk key index
+        if (c < 0) continue;
+        float dk = 0.f, dv = 0.f;
+        for (int i = c; i < kRows; ++i) {  // only rows i >= c see chunk key c
+          dk += sm.ds[i * (kKB + 1) + j] * sm.q[i * kHD + lane];
+          dv += sm.p[i * (kKB + 1) + j] * sm.dout[i * kHD + lane];
+        }
+        const size_t o = ((((size_t)b * kHQ + h) * 2) * kChunk + c) * kHD + lane;
+        a.dkv[o] = dk;
+        a.dkv[o + (size_t)kChunk * kHD] = dv;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRPT; ++r) {
+    const int i = w + 4 * r;
+    if (i < kRows) a.dq[(size_t)(b * kChunk + i) * a.ldq + h * kHD + lane] = dq[r] * scale;
+  }
+}
+
+inline int ew_grid(size_t n) { return (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kcont, bool b_bf16, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  // every operand is read in 4-wide vectors along its contiguous axis: that axis's length and
+  // every leading dimension must be multiples of 4 (the vectors never straddle an edge)
+  if ((a_kcont ? g.K : g.M) % 4 || (b_kcont ? g.K : g.N) % 4 || g.lda % 4 || g.ldb % 4 || g.K <= 0)
+    return hipErrorInvalidValue;
+  const int T = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
+  const dim3 grid(8 * ((T + 7) / 8)), block(256);
+  if (!a_bf16 && a_kcont && b_bf16 && b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, true>), grid, block, 0, s, g);
+  else if (!a_bf16 && a_kcont && b_bf16 && !b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, false>), grid, block, 0, s, g);
+  else if (!a_bf16 && !a_kcont && !b_bf16 && !b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<float, false, float, false>), grid, block, 0, s, g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+size_t train_manifest_count(int L) {
+  TrOffsets o;
+  return train_offsets(L, 0, &o);
+}
+
+// Offsets (elements) of every tensor in the weight manifest; returns the total.
+size_t train_offsets(int L, int layer, TrOffsets* o) {
+  size_t off = 0;
+  auto take = [&](size_t n) { size_t v = off; off += n; return v; };
+  o->ain_w = take((size_t)kD * kAD);
+  o->ain_b = take(kD);
+  o->tin_w = take((size_t)kD * 2 * kD);
+  o->tin_b = take(kD);
+  o->tout_w = take((size_t)kD * kD);
+  o->tout_b = take(kD);
+  for (int l = 0; l < L; ++l) {
+    const bool self = l % 2 == 0;
+    TrLayerOffsets lo;
+    lo.norm1 = take(kD);
+    lo.qkv = take((size_t)(self ? kNQKV : kNQ) * kD);  // q, then k and v: one [1600|960][720] matrix
+    lo.o = take((size_t)kD * kNQ);
+    lo.norm2 = take(kD);
+    lo.gu = take((size_t)kGU * kD);  // gate, then up: one [4096][720] matrix
+    lo.down = take((size_t)kD * kFFN);
+    if (l == layer) o->layer = lo;
+  }
+  o->fnorm = take(kD);
+  o->aout_w = take((size_t)kAD * kD);
+  o->aout_b = take(kAD);
+  return off;
+}
+
+size_t train_workspace_bytes(int B, int P, int L) {
+  TrainWs w;
+  return train_carve(nullptr, B, P, L, &w);
+}
+
+size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
+  const size_t M = (size_t)B * kChunk, nblk = (M + kRB - 1) / kRB;
+  size_t off = 0;
+  auto f = [&](size_t n) { size_t o = off; off += (n * 4 + 255) & ~(size_t)255; return base ? (float*)(base + o) : nullptr; };
+  w->xt = f(M * kAD);
+  w->target = f(M * kAD);
+  w->z = f(M * 2 * kD);
+  w->s = f(M * kD);
+  w->sil = f(M * kD);
+  w->H = f((size_t)(L + 1) * M * kD);
+  w->N1 = f((size_t)L * M * kD);
+  w->R1 = f((size_t)L * M);
+  w->QKV = f((size_t)L * M * kNQKV);
+  w->O = f((size_t)L * M * kNQ);
+  w->LSE = f((size_t)L * B * kHQ * kChunk);
+  w->HM = f((size_t)L * M * kD);
+  w->N2 = f((size_t)L * M * kD);
+  w->R2 = f((size_t)L * M);
+  w->GU = f((size_t)L * M * kGU);
+  w->ACT = f((size_t)L * M * kFFN);
+  w->NF = f(M * kD);
+  w->RF = f(M);
+  w->V = f(M * kAD);
+  w->dv = f(M * kAD);
+  w->dh = f(M * kD);
+  w->dn = f(M * kD);
+  w->dact = f(M * kFFN);
+  w->dgu = f(M * kGU);
+  w->dout = f(M * kNQ);
+  w->dqkv = f(M * kNQKV);
+  w->dkv = f((size_t)B * kHQ * 2 * kChunk * kHD);
+  w->part = f(nblk * kGU + M);
+  w->vidx = (int*)f((size_t)B * P);
+  w->nval = (int*)f(B);
+  return off;
+}
+
+hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
+  const int B = t.B, L = t.L, M = B * kChunk, nblk = (M + kRB - 1) / kRB;
+  const TrainWs& w = t.ws;
+  const bf16_t* W = t.w;
+  float* G = t.grads;
+  TrOffsets off;
+  train_offsets(L, 0, &off);
+  hipError_t e;
+#define TR_CHECK() do { if ((e = hipGetLastError()) != hipSuccess) return e; } while (0)
+  auto gemm = [&](int m, int n, int k, const void* A, int lda, bool ak, bool abf, const void* Bp, int ldb, bool bk,
+                  bool bbf, float* C, int ldc, const float* cin, const float* bias) {
+    TrGemm g;
+    g.M = m; g.N = n; g.K = k; g.A = A; g.lda = lda; g.B = Bp; g.ldb = ldb; g.C = C; g.ldc = ldc;
+    g.Cin = cin; g.bias = bias; g.alpha = 1.f;
+    return launch_tr_gemm(g, ak, abf, bk, bbf, st);
+  };
+  // y W^T (+ cin) (+ bias): activations fp32 along k, weights bf16 [out][in]
+  auto fwd = [&](const float* x, int ldx, size_t woff, int n, int k, float* y, int ldy, const float* cin,
+                 const float* bias) { return gemm(M, n, k, x, ldx, true, false, W + woff, k, true, true, y, ldy, cin, bias); };
+  // dx = dy W: W [n_out][k_in] read across its rows
+  auto bwd_x = [&](const float* dy, int n_out, size_t woff, int k_in, int ldw, float* dx) {
+    return gemm(M, k_in, n_out, dy, n_out, true, false, W + woff, ldw, false, true, dx, k_in, nullptr, nullptr);
+  };
+  // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide)
+  auto bwd_w = [&](const float* dy, int ldy, int n_out, const float* x, int k_in, size_t goff) {
+    return gemm(n_out, k_in, M, dy, ldy, false, false, x, k_in, false, false, G + goff, k_in, nullptr, nullptr);
+  };
+  auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
+    hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, w.part, nblk, n, out);
+    return hipGetLastError();
+  };
+  auto norm_bwd = [&](const float* dy, const float* h, const float* r, size_t goff, const float* resid, float* dh) -> hipError_t {
+    hipLaunchKernelGGL(tr_rmsnorm_bwd_kernel, dim3(nblk), dim3(256), 0, st, dy, h, r, W + goff, resid, dh, M, w.part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 255) / 256), dim3(256), 0, st, w.part, nblk, kD, G + goff);
+    return hipGetLastError();
+  };
+  auto Hl = [&](int l) { return w.H + (size_t)l * M * kD; };
+  auto lay = [&](float* base, int l, size_t per_row) { return base + (size_t)l * M * per_row; };
+
+  // ---- forward
+  hipLaunchKernelGGL(tr_prep_kernel, dim3(B), dim3(64), 0, st, t.mask, t.P, w.vidx, w.nval);
+  TR_CHECK();
+  hipLaunchKernelGGL(tr_input_kernel, dim3(M), dim3(256), 0, st, t.actions, t.noise, t.t, t.inv_period, w.xt,
+                     w.target, w.z);
+  TR_CHECK();
+  // the four biases come widened to fp32 (bias32: b_in, b_t1, b_t2, b_out)
+  if ((e = fwd(w.xt, kAD, off.ain_w, kD, kAD, w.z, 2 * kD, nullptr, t.bias32 + 0)) != hipSuccess) return e;
+  if ((e = fwd(w.z, 2 * kD, off.tin_w, kD, 2 * kD, w.s, kD, nullptr, t.bias32 + kD)) != hipSuccess) return e;
+  hipLaunchKernelGGL(tr_silu_kernel, dim3(ew_grid((size_t)M * kD)), dim3(256), 0, st, w.s, w.sil, (size_t)M * kD);
+  TR_CHECK();
+  if ((e = fwd(w.sil, kD, off.tout_w, kD, kD, Hl(0), kD, nullptr, t.bias32 + 2 * kD)) != hipSuccess) return e;
+  for (int l = 0; l < L; ++l) {
+    TrOffsets ol;
+    train_offsets(L, l, &ol);
+    const TrLayerOffsets& lo = ol.layer;
+    const bool self = l % 2 == 0;
+    const int nq = self ? kNQKV : kNQ;
+    float *n1 = lay(w.N1, l, kD), *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
+    float *hm = lay(w.HM, l, kD), *n2 = lay(w.N2, l, kD), *r2 = w.R2 + (size_t)l * M;
+    float *gu = lay(w.GU, l, kGU), *act = lay(w.ACT, l, kFFN);
+    hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, Hl(l), W + lo.norm1, t.rms_eps, M, n1, r1);
+    TR_CHECK();
+    if ((e = fwd(n1, kD, lo.qkv, nq, kD, qkv, kNQKV, nullptr, nullptr)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, qkv, kNQKV, self ? kHQ + kHKV : kHQ, w.nval, t.rope, 1.f);
+    TR_CHECK();
+    TrAttn aa;
+    aa.qkv = qkv; aa.ldq = kNQKV;
+    aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
+    aa.pv = aa.pk + (size_t)B * kHKV * t.P * kHD;
+    aa.vidx = w.vidx; aa.nval = w.nval; aa.P = t.P;
+    aa.o = o; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
+    aa.dout = nullptr; aa.dq = nullptr; aa.dkv = nullptr;
+    if (self) hipLaunchKernelGGL(tr_attn_fwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
+    else hipLaunchKernelGGL(tr_attn_fwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
+    TR_CHECK();
+    if ((e = fwd(o, kNQ, lo.o, kD, kNQ, hm, kD, Hl(l), nullptr)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, hm, W + lo.norm2, t.rms_eps, M, n2, r2);
+    TR_CHECK();
+    if ((e = fwd(n2, kD, lo.gu, kGU, kD, gu, kGU, nullptr, nullptr)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_swiglu_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, gu, act, (size_t)M * kFFN);
+    TR_CHECK();
+    if ((e = fwd(act, kFFN, lo.down, kD, kFFN, Hl(l + 1), kD, hm, nullptr)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, Hl(L), W + off.fnorm, t.rms_eps, M, w.NF, w.RF);
+  TR_CHECK();
+  if ((e = fwd(w.NF, kD, off.aout_w, kAD, kD, w.V, kAD, nullptr, t.bias32 + 3 * kD)) != hipSuccess) return e;
+  // ---- loss
+  const int lblk = (M + 7) / 8;
+  hipLaunchKernelGGL(tr_loss_kernel, dim3(lblk), dim3(256), 0, st, w.V, w.target, M, 1.f / ((float)M * kAD), w.dv,
+                     w.part);
+  TR_CHECK();
+  hipLaunchKernelGGL(tr_reduce_kernel, dim3(1), dim3(256), 0, st, w.part, lblk, 1, t.loss);
+  TR_CHECK();
+  hipLaunchKernelGGL(tr_scale_kernel, dim3(1), dim3(1), 0, st, t.loss, 1.f / ((float)M * kAD));
+  TR_CHECK();
+  // ---- backward
+  if ((e = bwd_w(w.dv, kAD, kAD, w.NF, kD, off.aout_w)) != hipSuccess) return e;
+  if ((e = colsum(w.dv, kAD, G + off.aout_b)) != hipSuccess) return e;
+  if ((e = bwd_x(w.dv, kAD, off.aout_w, kD, kD, w.dn)) != hipSuccess) return e;
+  if ((e = norm_bwd(w.dn, Hl(L), w.RF, off.fnorm, nullptr, w.dh)) != hipSuccess) return e;
+  for (int l = L - 1; l >= 0; --l) {
+    TrOffsets ol;
+    train_offsets(L, l, &ol);
+    const TrLayerOffsets& lo = ol.layer;
+    const bool self = l % 2 == 0;
+    const int nq = self ? kNQKV : kNQ;
+    float *n1 = lay(w.N1, l, kD), *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
+    float *hm = lay(w.HM, l, kD), *n2 = lay(w.N2, l, kD), *r2 = w.R2 + (size_t)l * M;
+    float *gu = lay(w.GU, l, kGU), *act = lay(w.ACT, l, kFFN);
+    // MLP
+    if ((e = bwd_x(w.dh, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh, kD, kD, act, kFFN, lo.down)) != hipSuccess) return e;
+    hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, w.dact, gu, w.dgu,
+                       (size_t)M * kFFN);
+    TR_CHECK();
+    if ((e = bwd_x(w.dgu, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dgu, kGU, kGU, n2, kD, lo.gu)) != hipSuccess) return e;
+    if ((e = norm_bwd(w.dn, hm, r2, lo.norm2, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(hm)
+    // attention
+    if ((e = bwd_x(w.dh, kD, lo.o, kNQ, kNQ, w.dout)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh, kD, kD, o, kNQ, lo.o)) != hipSuccess) return e;
+    TrAttn aa;
+    aa.qkv = qkv; aa.ldq = kNQKV;
+    aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
+    aa.pv = aa.pk + (size_t)B * kHKV * t.P * kHD;
+    aa.vidx = w.vidx; aa.nval = w.nval; aa.P = t.P;
+    aa.o = o; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
+    aa.dout = w.dout; aa.dq = w.dqkv; aa.dkv = w.dkv;
+    if (self) hipLaunchKernelGGL(tr_attn_bwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
+    else hipLaunchKernelGGL(tr_attn_bwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
+    TR_CHECK();
+    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, w.dqkv, kNQKV, kHQ, w.nval, t.rope, -1.f);
+    TR_CHECK();
+    if (self) {
+      hipLaunchKernelGGL(tr_kv_grad_kernel, dim3(M), dim3(256), 0, st, w.dkv, w.nval, t.rope, w.dqkv);
+      TR_CHECK();
+    }
+    if ((e = gemm(M, kD, nq, w.dqkv, kNQKV, true, false, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
+      return e;
+    if ((e = bwd_w(w.dqkv, kNQKV, nq, n1, kD, lo.qkv)) != hipSuccess) return e;
+    if ((e = norm_bwd(w.dn, Hl(l), r1, lo.norm1, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(h_l)
+  }
+  // time MLP and action_in (dh = d h0)
+  if ((e = bwd_w(w.dh, kD, kD, w.sil, kD, off.tout_w)) != hipSuccess) return e;
+  if ((e = colsum(w.dh, kD, G + off.tout_b)) != hipSuccess) return e;
+  if ((e = bwd_x(w.dh, kD, off.tout_w, kD, kD, w.dn)) != hipSuccess) return e;
+  hipLaunchKernelGGL(tr_silu_bwd_kernel, dim3(ew_grid((size_t)M * kD)), dim3(256), 0, st, w.dn, w.s, w.dn, (size_t)M * kD);
+  TR_CHECK();
+  if ((e = bwd_w(w.dn, kD, kD, w.z, 2 * kD, off.tin_w)) != hipSuccess) return e;
+  if ((e = colsum(w.dn, kD, G + off.tin_b)) != hipSuccess) return e;
+  // dy = ds W_t1[:, :720]
+  if ((e = gemm(M, kD, kD, w.dn, kD, true, false, W + off.tin_w, 2 * kD, false, true, w.dh, kD, nullptr, nullptr)) != hipSuccess)
+    return e;
+  if ((e = bwd_w(w.dh, kD, kD, w.xt, kAD, off.ain_w)) != hipSuccess) return e;
+  if ((e = colsum(w.dh, kD, G + off.ain_b)) != hipSuccess) return e;
+#undef TR_CHECK
+  return hipSuccess;
+}
+
+}  // namespace smolexp

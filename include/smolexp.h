@@ -215,6 +215,35 @@ int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_m
                     void* out_kv, int batch, void* hip_stream);
 
 /*
+ * Flow-matching training step of the expert: the loss of one batch and the
+ * gradient of every expert tensor (noeira docs "SmolVLA", Architecture: the
+ * fine-tuning objective, x_t = t eps + (1 - t) a and the squared error of
+ * v_theta(x_t, t | prefix) against eps - a; Fine-tuning: only the expert trains,
+ * so the prefix K/V is a frozen input).  Readings where the pages are silent:
+ * the loss is the mean over the batch's B x 50 x 32 elements; t and eps are
+ * drawn by the caller; no optimizer update is applied.  The weights are those of
+ * the last smolexp_load_weights (the library keeps them as given, bf16).
+ *   prefix_kv, prefix_mask, prefix_len  as for smolexp_denoise (read only).
+ *   actions    device fp32 [batch][50][32]: the target chunks a.  Read only.
+ *   noise      device fp32 [batch][50][32]: eps.  Read only.
+ *   t          device fp32 [batch]: each query's flow time.  Read only.
+ *   out_grads  device fp32 [smolexp_weight_count]: written (not accumulated),
+ *              d loss / d weight in manifest order, one value per weight.
+ *   out_loss   device fp32 [1]: written.
+ * Precision: matrix products take bf16 operands with fp32 accumulation; norms,
+ * softmax, the loss and every activation kept for the backward pass are fp32.
+ * Deterministic (no atomics).  The library keeps a workspace of about 46 KB per
+ * chunk row per layer (fp32 activations) for the largest batch x prefix_len
+ * seen; a call that needs more grows it first, which synchronizes the device.
+ * Asynchronous on hip_stream otherwise.  SMOLEXP_E_STATE before
+ * smolexp_load_weights; SMOLEXP_E_INVAL for NULL pointers or batch /
+ * prefix_len out of range.
+ */
+int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                       const float* actions, const float* noise, const float* t, float* out_grads,
+                       float* out_loss, int batch, void* hip_stream);
+
+/*
  * Measurement hook: average duration in microseconds of one launch of one
  * kernel of the loop, timed with HIP events on hip_stream (synchronous) around
  * `reps` (1..100000) back-to-back launches.  Launch i repeats the (i mod n)-th
