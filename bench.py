@@ -319,6 +319,122 @@ def run_prefill_stage(args):
     print(json.dumps(line), flush=True)
 
 
+def train_algorithmic(L, B, lengths):
+    """Matrix-core flops of one training step (forward, input gradients, weight gradients)
+    and its minimum HBM bytes.
+
+    Projections: 2 flops per multiply-add per chunk row; the backward pass computes every
+    weight gradient (the forward's flops again) and every input gradient except those of the
+    data (x_t) and of the time embedding (half of time_in).  Attention, per row, head and
+    allowed key: forward QK^T and PV (4 x 64), backward dP, dS K, dS^T Q and P^T dO (8 x 64);
+    allowed keys are the n_b valid prefix tokens plus, in self layers, chunk keys j <= i.
+    Bytes: the bf16 weights read three times (forward, input and weight gradients), the fp32
+    gradients written once, the valid prefix K/V read twice (forward, backward).
+    """
+    D, F, A, C = 720, 2048, 32, 50
+    per_row = 2 * (A * D + 2 * D * D + D * D + A * D)  # action_in, time_in, time_out, action_out
+    for l in range(L):
+        nq = 1600 if l % 2 == 0 else 960
+        per_row += 2 * (D * nq + 960 * D + D * 2 * F + F * D)
+    dx_skip = 2 * (A * D + D * D)
+    gemm = B * C * (3 * per_row - dx_skip)
+    n_self, n_cross = (L + 1) // 2, L // 2
+    attn = 0
+    for nb in lengths:
+        keys_self = C * nb + C * (C + 1) // 2
+        keys_cross = C * nb
+        attn += 15 * (n_self * keys_self + n_cross * keys_cross) * 12 * 64
+    n_w = 0
+    for l in range(L):
+        nq = 1600 if l % 2 == 0 else 960
+        n_w += 2 * D + nq * D + D * 960 + 3 * F * D
+    n_w += A * D + D + 2 * D * D + D + D * D + D + D + A * D + A
+    byt = 3 * 2 * n_w + 4 * n_w + 2 * L * sum(lengths) * 5 * 64 * 2 * 2
+    return byt, gemm + attn
+
+
+def run_train_stage(args):
+    """Time smolexp_train_step on the workload's batch and prefix (one JSON line)."""
+    import numpy as np
+    import torch
+    import synth
+    import flow_matching_action_step_amd as fm
+
+    wl = synth.make_workload(args.workload)
+    L, B, P = wl["n_layers"], wl["batch"], wl["prefix_len"]
+    cfg = fm.smolexp_default_config(n_layers=L, max_batch=B, max_prefix=P)
+    h = fm.smolexp_create(cfg, 0)
+    fm.smolexp_load_weights(h, synth.pack_weights(wl["weights"], L))
+    kv = torch.from_numpy(np.ascontiguousarray(wl["prefix_kv"]).view(np.int16)).cuda()
+    mask = torch.from_numpy(wl["mask"]).cuda()
+    acts_np, t_np = synth.draw_actions(B), synth.draw_flow_times(B)
+    acts = torch.from_numpy(acts_np).cuda()
+    noise = torch.from_numpy(wl["noise"]).cuda()
+    t = torch.from_numpy(t_np).cuda()
+    grads = torch.empty(fm.smolexp_weight_count(cfg), dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        fm.smolexp_train_step(h, cfg, kv, mask, acts, noise, t, grads, loss)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sampler = GpuStateSampler().start()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_state = sampler.stop()
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms = wall / args.steps * 1e3
+    lengths = [int(x) for x in wl["mask"].sum(axis=1)]
+    byt, fl = train_algorithmic(L, B, lengths)
+    roof = {"bound": "mfma", "achieved": fl / (ev_ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "whole training step (HIP events around the calls)"
+    roof["algorithmic_flops_per_call"] = fl
+    roof["algorithmic_bytes_per_call"] = byt
+    line = {
+        "metric": "training samples/sec (flow-matching loss and every expert weight gradient)",
+        "value": B * args.steps / wall, "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "precision": "GEMM operands bf16, fp32 accumulate; attention, norms, loss and saved activations fp32",
+        "data": "synthetic (seeded: weights N(0,0.02) bf16, K/V N(0,1) bf16, actions and noise N(0,1), t U(0,1))",
+        "config": {"workload": args.workload, "stage": "train", "n_layers": L, "batch": B, "prefix_len": P},
+        "roofline": roof,
+        "event_ms_per_call": ev_ms,
+        "loss": float(loss.cpu()[0]),
+        "gpu_state": gpu_state,
+    }
+    fm.smolexp_destroy(h)
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        import oracle
+        W = oracle.decode_weights(wl["weights"])
+        ocfg = oracle.ExpertConfig(n_layers=L)
+        a64, e64, t64 = acts_np.astype(np.float64), wl["noise"].astype(np.float64), t_np.astype(np.float64)
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.train_batch(W, ocfg, wl["prefix_kv"], wl["mask"], a64, e64, t64, queries=[done % B])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el + el / done > 3 * args.cpu_seconds:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        line["cpu_baseline"] = {"value": done / el, "unit": "samples/s", "cores": threads, "kind": "oracle",
+                                "sample": f"{done} sample(s) (forward and backward of one query each), "
+                                          f"{el:.1f} s, float64 numpy, {threads} BLAS thread(s)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,8 +442,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--n-steps", type=int, default=10, help="Euler steps per chunk (dt = -1/n)")
-    ap.add_argument("--stage", choices=("denoise", "prefill"), default="denoise",
-                    help="prefill: time the prefix language model that fills the K/V cache instead")
+    ap.add_argument("--stage", choices=("denoise", "prefill", "train"), default="denoise",
+                    help="prefill: time the prefix language model that fills the K/V cache instead; "
+                         "train: the flow-matching training step (loss and weight gradients)")
     ap.add_argument("--kernel-reps", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -347,6 +464,9 @@ def main():
 
     if args.stage == "prefill":
         run_prefill_stage(args)
+        return
+    if args.stage == "train":
+        run_train_stage(args)
         return
 
     import numpy as np

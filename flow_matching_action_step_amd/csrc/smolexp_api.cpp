@@ -1028,6 +1028,7 @@ int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
   ta.rms_eps = h->cfg.rms_eps;
   // the workspace is carved for this call's batch and prefix length (it holds at least that)
   train_carve(static_cast<char*>(h->trmem), batch, prefix_len, L, &ta.ws);
+  ta.split_cap = train_split_cap(batch);
   const hipError_t e = train_enqueue(ta, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(h, e, "training step launch");
   return SMOLEXP_OK;

@@ -18,6 +18,8 @@ struct TrGemm {
   const float* Cin;
   const float* bias;
   float alpha;
+  float* part;        // k-split scratch (NULL: no split)
+  size_t part_cap;    // its capacity in floats
 };
 
 struct TrAttn {
@@ -52,9 +54,11 @@ struct TrainWs {
   float *N1, *R1, *QKV, *O, *LSE, *HM, *N2, *R2, *GU, *ACT;  // per layer
   float *NF, *RF, *V;
   float *dv, *dh, *dn, *dact, *dgu, *dout, *dqkv, *dkv, *part;
+  float *split;             // k-split partial sums of the matrix products
   int *vidx, *nval;
 };
 size_t train_workspace_bytes(int B, int P, int L);
+size_t train_split_cap(int B);  // floats of TrainWs::split
 size_t train_carve(char* base, int B, int P, int L, TrainWs* w);  // base NULL: sizes only
 
 struct TrainArgs {
@@ -71,6 +75,7 @@ struct TrainArgs {
   const float2* rope;      // [pos][32] (cos, sin)
   const double* inv_period;  // [360]
   float rms_eps;
+  size_t split_cap;        // floats of ws.split (the workspace's batch)
   TrainWs ws;
 };
 hipError_t train_enqueue(const TrainArgs& t, hipStream_t s);

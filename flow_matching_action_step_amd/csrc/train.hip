@@ -17,6 +17,8 @@
 #include "smolexp_internal.h"
 #include "smolexp_train.h"
 
+#include <algorithm>
+
 namespace smolexp {
 namespace {
 
@@ -39,84 +41,116 @@ __device__ inline uint2 load4(const bf16_t* p) { return *reinterpret_cast<const 
 // ------------------------------------------------------------------------------------------
 // C[m][n] = alpha sum_k A(m,k) B(n,k) (+ Cin[m][n]) (+ bias[n])
 //   A(m,k) = A[m lda + k] (AK) or A[k lda + m];  B(n,k) = B[n ldb + k] (BK) or B[k ldb + n].
-// 128 x 128 tiles, 32-deep k-slabs staged through LDS as bf16 (rows of 32 + 8 pad), four
-// waves of 64 x 64 (4 x 4 MFMA 16x16x32 tiles).  Each thread moves four 4-wide vectors per
-// operand per slab along the operand's contiguous axis; the next slab's loads are issued
-// before the current slab's MFMAs.  Out-of-range rows and k read as zero.
-constexpr int GBM = 128, GBN = 128, GBK = 32, GLD = GBK + 8;
+// 128 x 128 tiles, 64-deep k-slabs staged through LDS as bf16 rows of 64 (+ 8 pad), four
+// waves of 64 x 64 (4 x 4 MFMA 16x16x32 tiles, two k-steps per slab).  An operand stored
+// along k moves in 4-wide vectors; one stored across k is read 4 rows at a time (each load
+// coalesced across the lanes) and transposed in registers, so every LDS write is 8 bytes
+// either way.  The next slab's loads are issued before the current
+// slab's MFMAs.  Out-of-range rows and k read as zero.  With a k-split (gridDim > tiles)
+// workgroup group s covers k-slabs [s kc, (s + 1) kc) and writes raw partial sums to
+// part[s][M][N]; tr_split_sum_kernel finishes them.
+constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
+
+// four consecutive values of one row, as floats
+__device__ inline float4 row4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 row4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_val(u.x & 0xFFFF), bf16_val(u.x >> 16), bf16_val(u.y & 0xFFFF), bf16_val(u.y >> 16));
+}
+
+// One operand's share of a slab, as 8 x 4 bf16 per thread.  Stored along k (KC): 4-wide
+// vectors of one row.  Stored across k: a 4 x 4 block (4 k-rows of 4 consecutive operand
+// rows, each a 16-byte load coalesced across the lanes), transposed in registers into 4
+// rows of 4 k-values; thread t takes operand rows 4 (t % 32) .. +3 and k-quads t / 32 and
+// t / 32 + 8.  R (the operand's row count) is a multiple of 4 there.
+template <typename T, bool KC>
+__device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int K, int tid, uint2 (&v)[8]) {
+  if constexpr (KC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, r = r0 + (idx >> 4), k = k0 + (idx & 15) * 4;
+      v[i] = (r < R && k < K) ? load4(X + (size_t)r * ld + k) : make_uint2(0, 0);
+    }
+  } else {
+    const int r = r0 + (tid & 31) * 4;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int kb = k0 + (tid >> 5) * 4 + blk * 32;
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = (r < R && kb + u < K) ? row4(X + (size_t)(kb + u) * ld + r) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[blk * 4 + 0] = make_uint2(bf16_bits(x[0].x) | (bf16_bits(x[1].x) << 16), bf16_bits(x[2].x) | (bf16_bits(x[3].x) << 16));
+      v[blk * 4 + 1] = make_uint2(bf16_bits(x[0].y) | (bf16_bits(x[1].y) << 16), bf16_bits(x[2].y) | (bf16_bits(x[3].y) << 16));
+      v[blk * 4 + 2] = make_uint2(bf16_bits(x[0].z) | (bf16_bits(x[1].z) << 16), bf16_bits(x[2].z) | (bf16_bits(x[3].z) << 16));
+      v[blk * 4 + 3] = make_uint2(bf16_bits(x[0].w) | (bf16_bits(x[1].w) << 16), bf16_bits(x[2].w) | (bf16_bits(x[3].w) << 16));
+    }
+  }
+}
+
+template <bool KC>
+__device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int r, k;
+    if constexpr (KC) {
+      const int idx = tid + 256 * i;
+      r = idx >> 4;
+      k = (idx & 15) * 4;
+    } else {
+      r = (tid & 31) * 4 + (i & 3);
+      k = (tid >> 5) * 4 + (i >> 2) * 32;
+    }
+    *reinterpret_cast<uint2*>(s + r * GLD + k) = v[i];
+  }
+}
 
 template <typename TA, bool AK, typename TB, bool BK>
-__global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g) {
+__global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits, int kc, float* part) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[GBM * GLD];
   __shared__ __attribute__((aligned(16))) uint16_t sB[GBN * GLD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int M = g.M, N = g.N, K = g.K;
+  const int M = g.M, N = g.N;
   // tiles of one column stripe go to one XCD (workgroup i runs on XCD i % 8), so the
-  // B stripe it shares is read into one L2
-  const int nN = (N + GBN - 1) / GBN, nM = (M + GBM - 1) / GBM, T = nM * nN;
-  const int bid = blockIdx.x, xcd = bid & 7, j8 = bid >> 3, per = (T + 7) >> 3;
-  const int tile = xcd * per + j8;
+  // B stripe they share is read into one L2
+  const int nN = (N + GBN - 1) / GBN, nM = (M + GBM - 1) / GBM, T = nM * nN, per = (T + 7) >> 3;
+  const int sidx = (int)blockIdx.x / (8 * per), bid = (int)blockIdx.x % (8 * per);
+  const int tile = (bid & 7) * per + (bid >> 3);
   if (tile >= T) return;
   const int n0 = (tile / nM) * GBN, m0 = (tile % nM) * GBM;
+  const int kbeg = sidx * kc, kend = min(g.K, kbeg + kc);
   const TA* A = static_cast<const TA*>(g.A);
   const TB* Bm = static_cast<const TB*>(g.B);
-  uint2 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      if constexpr (AK) {
-        const int m = m0 + (idx >> 3), k = k0 + (idx & 7) * 4;
-        ra[i] = (m < M && k < K) ? load4(A + (size_t)m * g.lda + k) : make_uint2(0, 0);
-      } else {
-        const int k = k0 + (idx >> 5), m = m0 + (idx & 31) * 4;
-        ra[i] = (m < M && k < K) ? load4(A + (size_t)k * g.lda + m) : make_uint2(0, 0);
-      }
-      if constexpr (BK) {
-        const int n = n0 + (idx >> 3), k = k0 + (idx & 7) * 4;
-        rb[i] = (n < N && k < K) ? load4(Bm + (size_t)n * g.ldb + k) : make_uint2(0, 0);
-      } else {
-        const int k = k0 + (idx >> 5), n = n0 + (idx & 31) * 4;
-        rb[i] = (n < N && k < K) ? load4(Bm + (size_t)k * g.ldb + n) : make_uint2(0, 0);
-      }
-    }
-  };
-  auto put = [&](uint16_t* s, uint2 v, int idx, bool kcont) {
-    if (kcont) {
-      *reinterpret_cast<uint2*>(s + (idx >> 3) * GLD + (idx & 7) * 4) = v;
-    } else {
-      const int k = idx >> 5, r = (idx & 31) * 4;
-      s[(r + 0) * GLD + k] = (uint16_t)(v.x & 0xFFFF);
-      s[(r + 1) * GLD + k] = (uint16_t)(v.x >> 16);
-      s[(r + 2) * GLD + k] = (uint16_t)(v.y & 0xFFFF);
-      s[(r + 3) * GLD + k] = (uint16_t)(v.y >> 16);
-    }
-  };
+  uint2 ra[8], rb[8];
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gload(0);
-  for (int k0 = 0; k0 < K; k0 += GBK) {
+  load_slab<TA, AK>(A, g.lda, m0, M, kbeg, kend, tid, ra);
+  load_slab<TB, BK>(Bm, g.ldb, n0, N, kbeg, kend, tid, rb);
+  for (int k0 = kbeg; k0 < kend; k0 += GBK) {
     __syncthreads();  // every wave is done reading the previous slab
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      put(sA, ra[i], tid + 256 * i, AK);
-      put(sB, rb[i], tid + 256 * i, BK);
-    }
+    store_slab<AK>(sA, tid, ra);
+    store_slab<BK>(sB, tid, rb);
     __syncthreads();
-    if (k0 + GBK < K) gload(k0 + GBK);
-    bf16x8 af[4], bw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + (lane & 15)) * GLD + (lane >> 4) * 8);
-      bw[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + i * 16 + (lane & 15)) * GLD + (lane >> 4) * 8);
+    if (k0 + GBK < kend) {
+      load_slab<TA, AK>(A, g.lda, m0, M, k0 + GBK, kend, tid, ra);
+      load_slab<TB, BK>(Bm, g.ldb, n0, N, k0 + GBK, kend, tid, rb);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[4], bw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + (lane & 15)) * GLD + ks * 32 + (lane >> 4) * 8);
+        bw[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + i * 16 + (lane & 15)) * GLD + ks * 32 + (lane >> 4) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+    }
   }
   // lane l of a 16 x 16 tile holds rows 4 (l / 16) + r, column l % 16
 #pragma unroll
@@ -127,12 +161,30 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g) {
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r, col = n0 + wn * 64 + j * 16 + (lane & 15);
         if (row < M && col < N) {
-          float v = g.alpha * acc[i][j][r];
-          if (g.Cin) v += g.Cin[(size_t)row * g.ldc + col];
-          if (g.bias) v += g.bias[col];
-          g.C[(size_t)row * g.ldc + col] = v;
+          if (splits > 1) {
+            part[((size_t)sidx * M + row) * N + col] = acc[i][j][r];
+          } else {
+            float v = g.alpha * acc[i][j][r];
+            if (g.Cin) v += g.Cin[(size_t)row * g.ldc + col];
+            if (g.bias) v += g.bias[col];
+            g.C[(size_t)row * g.ldc + col] = v;
+          }
         }
       }
+}
+
+// C[m][n] = alpha sum_s part[s][m][n] (+ Cin) (+ bias), the parts added in order.
+__global__ __launch_bounds__(256) void tr_split_sum_kernel(const TrGemm g, int splits, const float* part) {
+  const size_t n = (size_t)g.M * g.N;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += part[(size_t)s * n + e];
+    const size_t row = e / g.N, col = e % g.N;
+    v *= g.alpha;
+    if (g.Cin) v += g.Cin[row * g.ldc + col];
+    if (g.bias) v += g.bias[col];
+    g.C[row * g.ldc + col] = v;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -197,7 +249,7 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
 //   dh = r (u - hat mean(u hat)) (+ resid), u = dy g, hat = h r;
 //   part[blk][c] = sum over the block's rows of dy hat (the gain's gradient, before the
 //   sum over blocks).  dh may alias resid.
-constexpr int kRB = 32;
+constexpr int kRB = 16;
 __global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, const float* h, const float* rstd,
                                                              const bf16_t* g, const float* resid, float* dh, int M,
                                                              float* part) {
@@ -242,13 +294,17 @@ __global__ __launch_bounds__(256) void tr_colsum_kernel(const float* x, int M, i
   part[(size_t)blk * N + c] = s;
 }
 
-// out[c] = sum over blocks of part[blk][c], in block order (deterministic).
+// out[c] = sum over blocks of part[blk][c]: 64 columns per workgroup, wave w adds the
+// blocks blk = w mod 4 in order, and the four sums are added in wave order (deterministic).
 __global__ __launch_bounds__(256) void tr_reduce_kernel(const float* part, int nblk, int N, float* out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= N) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int b = 0; b < nblk; ++b) s += part[(size_t)b * N + c];
-  out[c] = s;
+  if (c < N)
+    for (int b = w; b < nblk; b += 4) s += part[(size_t)b * N + c];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < N) out[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 __device__ inline float silu_f(float z) { return z / (1.f + __expf(-z)); }
@@ -587,20 +643,36 @@ inline int ew_grid(size_t n) { return (int)((n + 255) / 256 < 8192 ? (n + 255) /
 // ------------------------------------------------------------------------------------------
 hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kcont, bool b_bf16, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  // every operand is read in 4-wide vectors along its contiguous axis: that axis's length and
-  // every leading dimension must be multiples of 4 (the vectors never straddle an edge)
-  if ((a_kcont ? g.K : g.M) % 4 || (b_kcont ? g.K : g.N) % 4 || g.lda % 4 || g.ldb % 4 || g.K <= 0)
+  // operands are read in 4-wide vectors along their contiguous axis (K, or the operand's
+  // rows M / N when stored across k): that length and the leading dimension must be
+  // multiples of 4, so a vector never straddles an edge
+  if (g.K <= 0 || g.lda % 4 || g.ldb % 4 || (a_kcont ? g.K : g.M) % 4 || (b_kcont ? g.K : g.N) % 4)
     return hipErrorInvalidValue;
-  const int T = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN);
-  const dim3 grid(8 * ((T + 7) / 8)), block(256);
+  const int T = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN), per = (T + 7) / 8;
+  const int nslab = (g.K + GBK - 1) / GBK;
+  // k-split: enough workgroups for two per CU, at least 4 slabs each, parts within the scratch
+  int splits = 1;
+  if (g.part && T < 512) {
+    splits = (512 + T - 1) / T;
+    splits = min(splits, max(1, nslab / 4));
+    while (splits > 1 && (size_t)splits * g.M * g.N > g.part_cap) --splits;
+  }
+  const int kc = ((nslab + splits - 1) / splits) * GBK;
+  splits = (g.K + kc - 1) / kc;
+  const dim3 grid(8 * per * splits), block(256);
   if (!a_bf16 && a_kcont && b_bf16 && b_kcont)
-    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, true>), grid, block, 0, s, g, splits, kc, g.part);
   else if (!a_bf16 && a_kcont && b_bf16 && !b_kcont)
-    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
   else if (!a_bf16 && !a_kcont && !b_bf16 && !b_kcont)
-    hipLaunchKernelGGL((tr_gemm_kernel<float, false, float, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((tr_gemm_kernel<float, false, float, false>), grid, block, 0, s, g, splits, kc, g.part);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const size_t n = (size_t)g.M * g.N;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(tr_split_sum_kernel, dim3(blocks), dim3(256), 0, s, g, splits, g.part);
   return hipGetLastError();
 }
 
@@ -634,6 +706,12 @@ size_t train_offsets(int L, int layer, TrOffsets* o) {
   o->aout_w = take((size_t)kAD * kD);
   o->aout_b = take(kAD);
   return off;
+}
+
+// k-split partial sums: up to four parts of the largest product output (M x 2048 or 4096 x 720)
+size_t train_split_cap(int B) {
+  const size_t M = (size_t)B * kChunk;
+  return 4 * std::max(M * kFFN, (size_t)kGU * kD);
 }
 
 size_t train_workspace_bytes(int B, int P, int L) {
@@ -673,6 +751,7 @@ size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
   w->dqkv = f(M * kNQKV);
   w->dkv = f((size_t)B * kHQ * 2 * kChunk * kHD);
   w->part = f(nblk * kGU + M);
+  w->split = f(train_split_cap(B));
   w->vidx = (int*)f((size_t)B * P);
   w->nval = (int*)f(B);
   return off;
@@ -691,7 +770,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
                   bool bbf, float* C, int ldc, const float* cin, const float* bias) {
     TrGemm g;
     g.M = m; g.N = n; g.K = k; g.A = A; g.lda = lda; g.B = Bp; g.ldb = ldb; g.C = C; g.ldc = ldc;
-    g.Cin = cin; g.bias = bias; g.alpha = 1.f;
+    g.Cin = cin; g.bias = bias; g.alpha = 1.f; g.part = w.split; g.part_cap = t.split_cap;
     return launch_tr_gemm(g, ak, abf, bk, bbf, st);
   };
   // y W^T (+ cin) (+ bias): activations fp32 along k, weights bf16 [out][in]
@@ -708,13 +787,13 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
     hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, w.part, nblk, n, out);
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((n + 63) / 64), dim3(256), 0, st, w.part, nblk, n, out);
     return hipGetLastError();
   };
   auto norm_bwd = [&](const float* dy, const float* h, const float* r, size_t goff, const float* resid, float* dh) -> hipError_t {
     hipLaunchKernelGGL(tr_rmsnorm_bwd_kernel, dim3(nblk), dim3(256), 0, st, dy, h, r, W + goff, resid, dh, M, w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 255) / 256), dim3(256), 0, st, w.part, nblk, kD, G + goff);
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 63) / 64), dim3(256), 0, st, w.part, nblk, kD, G + goff);
     return hipGetLastError();
   };
   auto Hl = [&](int l) { return w.H + (size_t)l * M * kD; };
