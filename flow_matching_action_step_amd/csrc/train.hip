@@ -406,215 +406,278 @@ __global__ void tr_scale_kernel(float* x, float s) { *x *= s; }
 
 // ------------------------------------------------------------------------------------------
 // Attention of one (query, Q head) per workgroup over its keys: the valid prefix keys (from
-// the compacted position list), then, in self layers, the chunk's keys j <= i.  Scores in
-// fp32 from fp32 Q/K (bf16 prefix keys widened), exact two-pass softmax: pass 1 the row
-// maxima and sums (saved as log-sum-exp), pass 2 P = exp(S - lse) and O = P V.
-constexpr int kKB = 64;  // keys per block
+// the compacted position list), then, in self layers, the chunk's keys j <= i.  Four waves
+// of 16 query rows (rows 50..63 are padding).  Scores and products run on bf16 MFMA
+// 16x16x32 with fp32 accumulation: S = Q K^T per 64-key block (Q pre-scaled by 1/8), an
+// online softmax in fp32 (running row maximum and sum, kept as the log-sum-exp for the
+// backward pass), and O += P V with V transposed in LDS and P passed through a per-wave
+// LDS tile from the accumulator layout to the operand layout.
+constexpr int kKB = 64;      // keys per block
 constexpr int kRows = kChunk;
-constexpr int kRPT = (kRows + 3) / 4;  // rows per thread (4 waves stride the 50 rows)
+constexpr int KLD = kHD + 8;  // bf16 row stride of the LDS tiles (144 bytes)
 
-struct AttnSmem {
-  float q[kRows * kHD];
-  float k[kKB * (kHD + 1)];
-  float v[kKB * (kHD + 1)];
-  float s[kRows * (kKB + 1)];
-  float m[kRows], l[kRows];
-};
+// lane l of an MFMA 16x16 accumulator tile holds rows 4 (l / 16) + r, column l % 16; an
+// operand fragment holds row l % 16, k = 8 (l / 16) .. +7
+__device__ inline bf16x8 frag_ld(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+__device__ inline bf16x8 frag_from_f32(const float* p) {  // 8 consecutive fp32 values -> bf16x8
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  uint4 u;
+  u.x = bf16_bits(a.x) | (bf16_bits(a.y) << 16);
+  u.y = bf16_bits(a.z) | (bf16_bits(a.w) << 16);
+  u.z = bf16_bits(b.x) | (bf16_bits(b.y) << 16);
+  u.w = bf16_bits(b.z) | (bf16_bits(b.w) << 16);
+  return *reinterpret_cast<const bf16x8*>(&u);
+}
+
+// One 64-key block into LDS as bf16: K and V by key ([key][dim]) and, when asked, K or V
+// transposed ([dim][key]).  Thread t moves key t / 4, dims 16 (t % 4) .. +15; keys past
+// the last one are zero.
 template <bool SELF>
-__device__ inline void load_keys(const TrAttn& a, int b, int g, int nb, int kb, float* sk, float* sv, bool want_v) {
+__device__ inline void load_block(const TrAttn& a, int b, int g, int nb, int kb, uint16_t* sk, uint16_t* sv,
+                                  uint16_t* skt, uint16_t* svt) {
   const int tid = threadIdx.x, j = tid >> 2, d0 = (tid & 3) * 16, kidx = kb * kKB + j;
-  float kk[16], vv[16];
+  uint32_t kk[16], vv[16];
   if (kidx < nb) {
     const size_t o = (((size_t)b * kHKV + g) * a.P + a.vidx[(size_t)b * a.P + kidx]) * kHD + d0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      kk[u] = bf16_val(a.pk[o + u]);
-      vv[u] = want_v ? bf16_val(a.pv[o + u]) : 0.f;
+      kk[u] = a.pk[o + u];
+      vv[u] = a.pv[o + u];
     }
   } else if (SELF && kidx < nb + kChunk) {
     const float* src = a.qkv + (size_t)(b * kChunk + kidx - nb) * a.ldq;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      kk[u] = src[kNQ + g * kHD + d0 + u];
-      vv[u] = want_v ? src[kNQ + kNKV + g * kHD + d0 + u] : 0.f;
+      kk[u] = bf16_bits(src[kNQ + g * kHD + d0 + u]);
+      vv[u] = bf16_bits(src[kNQ + kNKV + g * kHD + d0 + u]);
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) kk[u] = vv[u] = 0.f;
+    for (int u = 0; u < 16; ++u) kk[u] = vv[u] = 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < 16; u += 8) {
+    uint4 pk, pv;
+    pk.x = kk[u] | (kk[u + 1] << 16); pk.y = kk[u + 2] | (kk[u + 3] << 16);
+    pk.z = kk[u + 4] | (kk[u + 5] << 16); pk.w = kk[u + 6] | (kk[u + 7] << 16);
+    pv.x = vv[u] | (vv[u + 1] << 16); pv.y = vv[u + 2] | (vv[u + 3] << 16);
+    pv.z = vv[u + 4] | (vv[u + 5] << 16); pv.w = vv[u + 6] | (vv[u + 7] << 16);
+    if (sk) *reinterpret_cast<uint4*>(sk + j * KLD + d0 + u) = pk;
+    if (sv) *reinterpret_cast<uint4*>(sv + j * KLD + d0 + u) = pv;
   }
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    sk[j * (kHD + 1) + d0 + u] = kk[u];
-    sv[j * (kHD + 1) + d0 + u] = vv[u];
+    if (skt) skt[(d0 + u) * KLD + j] = (uint16_t)kk[u];
+    if (svt) svt[(d0 + u) * KLD + j] = (uint16_t)vv[u];
   }
 }
 
 template <bool SELF>
 __device__ inline bool key_ok(int kidx, int nb, int i) {
-  return kidx < nb || (SELF && kidx < nb + kChunk && kidx - nb <= i);
+  return i < kRows && (kidx < nb || (SELF && kidx < nb + kChunk && kidx - nb <= i));
 }
+
+// Q (pre-scaled) or dO rows of this wave as the two operand fragments of a 64-deep product.
+__device__ inline void row_frags(const float* src, size_t ld, int b, int col0, int w, int lane, float scale,
+                                 bf16x8 (&f)[2]) {
+  const int i = 16 * w + (lane & 15);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (i < kRows) {
+      float x[8];
+      const float* p = src + (size_t)(b * kChunk + i) * ld + col0 + ks * 32 + (lane >> 4) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = p[u] * scale;
+      f[ks] = frag_from_f32(x);
+    } else {
+      f[ks] = bf16x8{};
+    }
+  }
+}
+
+struct AttnSmem {
+  uint16_t k[kKB * KLD];
+  uint16_t vt[kHD * KLD];
+  uint16_t p[4][16 * KLD];
+};
 
 template <bool SELF>
 __global__ __launch_bounds__(256) void tr_attn_fwd_kernel(const TrAttn a) {
-  __shared__ AttnSmem sm;
+  __shared__ __attribute__((aligned(16))) AttnSmem sm;
   const int h = blockIdx.x, b = blockIdx.y, g = h / (kHQ / kHKV);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
   const int nb = a.nval[b], nk = nb + (SELF ? kChunk : 0), nblk = (nk + kKB - 1) / kKB;
-  const float scale = 0.125f;
-  for (int e = tid; e < kRows * kHD; e += 256) {
-    const int i = e / kHD, d = e % kHD;
-    sm.q[e] = a.qkv[(size_t)(b * kChunk + i) * a.ldq + h * kHD + d] * scale;
+  bf16x8 qf[2];
+  row_frags(a.qkv, a.ldq, b, h * kHD, w, lane, 0.125f, qf);
+  float m[4], l[4];
+  f32x4 o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+    o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (tid < kRows) {
-    sm.m[tid] = -INFINITY;
-    sm.l[tid] = 0.f;
-  }
-  float kr[kHD];
-  // pass 1: row maxima and sums
+  uint16_t* sp = sm.p[w];
   for (int kb = 0; kb < nblk; ++kb) {
     __syncthreads();
-    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, false);
+    load_block<SELF>(a, b, g, nb, kb, sm.k, nullptr, nullptr, sm.vt);
     __syncthreads();
+    f32x4 s[4];
 #pragma unroll
-    for (int d = 0; d < kHD; ++d) kr[d] = sm.k[lane * (kHD + 1) + d];
-    const int kidx = kb * kKB + lane;
-    for (int r = 0; r < kRPT; ++r) {
-      const int i = w + 4 * r;
-      if (i >= kRows) break;
-      float s = 0.f;
+    for (int jt = 0; jt < 4; ++jt) {
+      s[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < kHD; ++d) s += sm.q[i * kHD + d] * kr[d];
-      const bool ok = key_ok<SELF>(kidx, nb, i);
-      const float mb = wave_max(ok ? s : -INFINITY);
-      if (mb != -INFINITY) {
-        const float sum = wave_sum(ok ? __expf(s - mb) : 0.f);
-        if (lane == 0) {
-          const float mo = sm.m[i], mn = fmaxf(mo, mb);
-          sm.l[i] = sm.l[i] * __expf(mo - mn) + sum * __expf(mb - mn);
-          sm.m[i] = mn;
-        }
+      for (int ks = 0; ks < 2; ++ks)
+        s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], frag_ld(sm.k + (jt * 16 + c16) * KLD + ks * 32 + q4 * 8),
+                                                       s[jt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * q4 + r;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        if (!key_ok<SELF>(kb * kKB + jt * 16 + c16, nb, i)) s[jt][r] = -INFINITY;
+        mx = fmaxf(mx, s[jt][r]);
       }
-    }
-  }
-  __syncthreads();
-  if (tid < kRows) {
-    const float lse = sm.l[tid] > 0.f ? sm.m[tid] + __logf(sm.l[tid]) : INFINITY;  // no key: P = 0
-    sm.m[tid] = lse;
-    a.lse[((size_t)b * kHQ + h) * kRows + tid] = lse;
-  }
-  // pass 2: O = exp(S - lse) V
-  float o[kRPT];
 #pragma unroll
-  for (int r = 0; r < kRPT; ++r) o[r] = 0.f;
-  for (int kb = 0; kb < nblk; ++kb) {
-    __syncthreads();
-    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, true);
-    __syncthreads();
+      for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(m[r], mx);
+      const float corr = mn == -INFINITY ? 1.f : __expf(m[r] - mn);
+      float sum = 0.f;
 #pragma unroll
-    for (int d = 0; d < kHD; ++d) kr[d] = sm.k[lane * (kHD + 1) + d];
-    const int kidx = kb * kKB + lane;
-    for (int r = 0; r < kRPT; ++r) {
-      const int i = w + 4 * r;
-      if (i >= kRows) break;
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < kHD; ++d) s += sm.q[i * kHD + d] * kr[d];
-      sm.s[i * (kKB + 1) + lane] = key_ok<SELF>(kidx, nb, i) ? __expf(s - sm.m[i]) : 0.f;
-    }
-    __syncthreads();
-    const int kn = min(kKB, nk - kb * kKB);
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      const int i = w + 4 * r;
-      if (i < kRows) {
-        float acc = 0.f;
-        for (int j = 0; j < kn; ++j) acc += sm.s[i * (kKB + 1) + j] * sm.v[j * (kHD + 1) + lane];
-        o[r] += acc;
+      for (int jt = 0; jt < 4; ++jt) {
+        const float p = s[jt][r] == -INFINITY ? 0.f : __expf(s[jt][r] - mn);
+        sum += p;
+        sp[(4 * q4 + r) * KLD + jt * 16 + c16] = (uint16_t)bf16_bits(p);
       }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+      l[r] = l[r] * corr + sum;
+      m[r] = mn;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][r] *= corr;
+    }
+    __syncthreads();  // this wave's P tile is written
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pf = frag_ld(sp + c16 * KLD + ks * 32 + q4 * 8);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, frag_ld(sm.vt + (dt * 16 + c16) * KLD + ks * 32 + q4 * 8),
+                                                       o[dt], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRPT; ++r) {
-    const int i = w + 4 * r;
-    if (i < kRows) a.o[(size_t)(b * kChunk + i) * kNQ + h * kHD + lane] = o[r];
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * w + 4 * q4 + r;
+    if (i < kRows) {
+      const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) a.o[(size_t)(b * kChunk + i) * kNQ + h * kHD + dt * 16 + c16] = o[dt][r] * inv;
+      if (c16 == 0) a.lse[((size_t)b * kHQ + h) * kRows + i] = l[r] > 0.f ? m[r] + __logf(l[r]) : INFINITY;
+    }
   }
 }
 
 // Backward of the attention above, one (query, Q head) per workgroup.  D_i = dO_i . O_i;
-// per key block: P = exp(S - lse), dP = dO V^T, dS = P (dP - D); dQ += dS K; the chunk's keys
-// (self layers) get this head's dK = dS^T Q and dV = P^T dO in dkv.  Q is held pre-scaled, so
-// S and dK carry the 1/8 already; dQ takes it at the end.
+// per key block: S = Q K^T and dP = dO V^T on MFMA, P = exp(S - lse), dS = P (dP - D);
+// dQ += dS K on MFMA (K transposed in LDS); the chunk's keys (self layers) get this head's
+// dK = dS^T Q and dV = P^T dO (fp32, at most 50 keys) in dkv.  Q is pre-scaled, so S and dK
+// carry the 1/8 already; dQ takes it at the end.
 struct AttnBwdSmem {
-  float q[kRows * kHD];
+  uint16_t k[kKB * KLD];
+  uint16_t v[kKB * KLD];
+  uint16_t kt[kHD * KLD];
+  uint16_t ds16[64 * KLD];
+  float q[kRows * kHD];      // fp32 Q (scaled) and dO for the chunk keys' dK, dV
   float dout[kRows * kHD];
-  float k[kKB * (kHD + 1)];
-  float v[kKB * (kHD + 1)];
-  float p[kRows * (kKB + 1)];
-  float ds[kRows * (kKB + 1)];
-  float dd[kRows], lse[kRows];
+  float p[64 * (kKB + 1)];
+  float ds[64 * (kKB + 1)];
+  float dd[64], lse[64];
 };
 
 template <bool SELF>
 __global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
-  __shared__ AttnBwdSmem sm;
+  __shared__ __attribute__((aligned(16))) AttnBwdSmem sm;
   const int h = blockIdx.x, b = blockIdx.y, g = h / (kHQ / kHKV);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q4 = lane >> 4, c16 = lane & 15;
   const int nb = a.nval[b], nk = nb + (SELF ? kChunk : 0), nblk = (nk + kKB - 1) / kKB;
   const float scale = 0.125f;
-  for (int e = tid; e < kRows * kHD; e += 256) {
-    const int i = e / kHD, d = e % kHD;
-    const size_t row = (size_t)(b * kChunk + i);
-    sm.q[e] = a.qkv[row * a.ldq + h * kHD + d] * scale;
-    sm.dout[e] = a.dout[row * kNQ + h * kHD + d];
+  if (SELF) {
+    for (int e = tid; e < kRows * kHD; e += 256) {
+      const int i = e / kHD, d = e % kHD;
+      const size_t row = (size_t)(b * kChunk + i);
+      sm.q[e] = a.qkv[row * a.ldq + h * kHD + d] * scale;
+      sm.dout[e] = a.dout[row * kNQ + h * kHD + d];
+    }
   }
-  for (int i = w; i < kRows; i += 4) {
-    const size_t row = (size_t)(b * kChunk + i);
-    const float s = wave_sum(a.dout[row * kNQ + h * kHD + lane] * a.o[row * kNQ + h * kHD + lane]);
+  for (int i = w; i < 64; i += 4) {
+    float s = 0.f;
+    if (i < kRows) {
+      const size_t row = (size_t)(b * kChunk + i);
+      s = wave_sum(a.dout[row * kNQ + h * kHD + lane] * a.o[row * kNQ + h * kHD + lane]);
+    }
     if (lane == 0) {
       sm.dd[i] = s;
-      sm.lse[i] = a.lse[((size_t)b * kHQ + h) * kRows + i];
+      sm.lse[i] = i < kRows ? a.lse[((size_t)b * kHQ + h) * kRows + i] : INFINITY;
     }
   }
-  float dq[kRPT];
+  bf16x8 qf[2], df[2];
+  row_frags(a.qkv, a.ldq, b, h * kHD, w, lane, scale, qf);
+  row_frags(a.dout, kNQ, b, h * kHD, w, lane, 1.f, df);
+  f32x4 dq[4];
 #pragma unroll
-  for (int r = 0; r < kRPT; ++r) dq[r] = 0.f;
-  float kr[kHD], vr[kHD];
+  for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  float lse_r[4], dd_r[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    lse_r[r] = sm.lse[16 * w + 4 * q4 + r];
+    dd_r[r] = sm.dd[16 * w + 4 * q4 + r];
+  }
   for (int kb = 0; kb < nblk; ++kb) {
     __syncthreads();
-    load_keys<SELF>(a, b, g, nb, kb, sm.k, sm.v, true);
+    load_block<SELF>(a, b, g, nb, kb, sm.k, sm.v, sm.kt, nullptr);
+    __syncthreads();
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      s[jt] = dp[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int off = (jt * 16 + c16) * KLD + ks * 32 + q4 * 8;
+        s[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], frag_ld(sm.k + off), s[jt], 0, 0, 0);
+        dp[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], frag_ld(sm.v + off), dp[jt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * q4 + r;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = jt * 16 + c16;
+        const float p = key_ok<SELF>(kb * kKB + j, nb, i) ? __expf(s[jt][r] - lse_r[r]) : 0.f;
+        const float d = p * (dp[jt][r] - dd_r[r]);
+        sm.ds16[i * KLD + j] = (uint16_t)bf16_bits(d);
+        if (SELF) {
+          sm.p[i * (kKB + 1) + j] = p;
+          sm.ds[i * (kKB + 1) + j] = d;
+        }
+      }
+    }
     __syncthreads();
 #pragma unroll
-    for (int d = 0; d < kHD; ++d) {
-      kr[d] = sm.k[lane * (kHD + 1) + d];
-      vr[d] = sm.v[lane * (kHD + 1) + d];
-    }
-    const int kidx = kb * kKB + lane;
-    for (int r = 0; r < kRPT; ++r) {
-      const int i = w + 4 * r;
-      if (i >= kRows) break;
-      float s = 0.f, dp = 0.f;
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 dsf = frag_ld(sm.ds16 + (16 * w + c16) * KLD + ks * 32 + q4 * 8);
 #pragma unroll
-      for (int d = 0; d < kHD; ++d) {
-        s += sm.q[i * kHD + d] * kr[d];
-        dp += sm.dout[i * kHD + d] * vr[d];
-      }
-      const float p = key_ok<SELF>(kidx, nb, i) ? __expf(s - sm.lse[i]) : 0.f;
-      sm.p[i * (kKB + 1) + lane] = p;
-      sm.ds[i * (kKB + 1) + lane] = p * (dp - sm.dd[i]);
-    }
-    __syncthreads();
-    const int kn = min(kKB, nk - kb * kKB);
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      const int i = w + 4 * r;
-      if (i < kRows) {
-        float acc = 0.f;
-        for (int j = 0; j < kn; ++j) acc += sm.ds[i * (kKB + 1) + j] * sm.k[j * (kHD + 1) + lane];
-        dq[r] += acc;
-      }
+      for (int dt = 0; dt < 4; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsf, frag_ld(sm.kt + (dt * 16 + c16) * KLD + ks * 32 + q4 * 8),
+                                                        dq[dt], 0, 0, 0);
     }
     if constexpr (SELF) {
+      const int kn = min(kKB, nk - kb * kKB);
       for (int j = w; j < kn; j += 4) {
         const int c = kb * kKB + j - nb;  // chunk key index
         if (c < 0) continue;
@@ -630,9 +693,11 @@ __global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRPT; ++r) {
-    const int i = w + 4 * r;
-    if (i < kRows) a.dq[(size_t)(b * kChunk + i) * a.ldq + h * kHD + lane] = dq[r] * scale;
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * w + 4 * q4 + r;
+    if (i < kRows)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) a.dq[(size_t)(b * kChunk + i) * a.ldq + h * kHD + dt * 16 + c16] = dq[dt][r] * scale;
   }
 }
 
