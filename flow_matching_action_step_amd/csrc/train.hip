@@ -245,43 +245,68 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
   if (lane == 0) rstd[row] = r;
 }
 
-// Backward of the RMSNorm above over 32 rows per workgroup:
+// Backward of the RMSNorm above over 16 rows per workgroup:
 //   dh = r (u - hat mean(u hat)) (+ resid), u = dy g, hat = h r;
 //   part[blk][c] = sum over the block's rows of dy hat (the gain's gradient, before the
-//   sum over blocks).  dh may alias resid.
+//   sum over blocks).  dh may alias resid.  Phase 1: each wave forms mean(u hat) of 4 rows
+//   (4-wide loads); phase 2: thread t takes columns 4t .. 4t + 3 of all 16 rows (the second
+//   read of dy and h comes from L2).
 constexpr int kRB = 16;
 __global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, const float* h, const float* rstd,
                                                              const bf16_t* g, const float* resid, float* dh, int M,
                                                              float* part) {
+  __shared__ float smean[kRB];
   const int blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int Q = kD / 4;  // 180 column quads
   for (int rr = w; rr < kRB; rr += 4) {
     const int row = blk * kRB + rr;
-    if (row >= M) break;
-    const float r = rstd[row];
-    const float* dyr = dy + (size_t)row * kD;
-    const float* hr = h + (size_t)row * kD;
     float s = 0.f;
-    for (int c = lane; c < kD; c += 64) s += dyr[c] * bf16_val(g[c]) * hr[c] * r;
-    const float mean = wave_sum(s) / kD;
-    for (int c = lane; c < kD; c += 64) {
-      const float hat = hr[c] * r;
-      float v = r * (dyr[c] * bf16_val(g[c]) - hat * mean);
-      if (resid) v += resid[(size_t)row * kD + c];
-      dh[(size_t)row * kD + c] = v;
+    if (row < M) {
+      const float r = rstd[row];
+      for (int c4 = lane; c4 < Q; c4 += 64) {
+        const float4 d = *reinterpret_cast<const float4*>(dy + (size_t)row * kD + 4 * c4);
+        const float4 x = *reinterpret_cast<const float4*>(h + (size_t)row * kD + 4 * c4);
+        const uint2 gg = *reinterpret_cast<const uint2*>(g + 4 * c4);
+        s += d.x * bf16_val(gg.x & 0xFFFF) * x.x + d.y * bf16_val(gg.x >> 16) * x.y +
+             d.z * bf16_val(gg.y & 0xFFFF) * x.z + d.w * bf16_val(gg.y >> 16) * x.w;
+      }
+      s = wave_sum(s) * r / kD;
     }
+    if (lane == 0) smean[rr] = s;
   }
-  for (int c = tid; c < kD; c += 256) {
-    float s = 0.f;
+  __syncthreads();
+  if (tid < Q) {
+    const uint2 gg = *reinterpret_cast<const uint2*>(g + 4 * tid);
+    const float g0 = bf16_val(gg.x & 0xFFFF), g1 = bf16_val(gg.x >> 16), g2 = bf16_val(gg.y & 0xFFFF),
+                g3 = bf16_val(gg.y >> 16);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int rr = 0; rr < kRB; ++rr) {
       const int row = blk * kRB + rr;
       if (row >= M) break;
-      s += dy[(size_t)row * kD + c] * h[(size_t)row * kD + c] * rstd[row];
+      const float r = rstd[row], mean = smean[rr];
+      const size_t o = (size_t)row * kD + 4 * tid;
+      const float4 d = *reinterpret_cast<const float4*>(dy + o);
+      const float4 x = *reinterpret_cast<const float4*>(h + o);
+      float4 v;
+      v.x = r * (d.x * g0 - x.x * r * mean);
+      v.y = r * (d.y * g1 - x.y * r * mean);
+      v.z = r * (d.z * g2 - x.z * r * mean);
+      v.w = r * (d.w * g3 - x.w * r * mean);
+      if (resid) {
+        const float4 q = *reinterpret_cast<const float4*>(resid + o);
+        v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+      }
+      *reinterpret_cast<float4*>(dh + o) = v;
+      acc.x += d.x * x.x * r;
+      acc.y += d.y * x.y * r;
+      acc.z += d.z * x.z * r;
+      acc.w += d.w * x.w * r;
     }
-    part[(size_t)blk * kD + c] = s;
+    *reinterpret_cast<float4*>(part + (size_t)blk * kD + 4 * tid) = acc;
   }
 }
 
-// Column sums of x [M][N] over blocks of 32 rows: part[blk][c].
+// Column sums of x [M][N] over blocks of kRB rows: part[blk][c].
 __global__ __launch_bounds__(256) void tr_colsum_kernel(const float* x, int M, int N, float* part) {
   const int c = blockIdx.x * 256 + threadIdx.x, blk = blockIdx.y;
   if (c >= N) return;
@@ -716,6 +741,7 @@ hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kco
   const int T = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN), per = (T + 7) / 8;
   const int nslab = (g.K + GBK - 1) / GBK;
   // k-split: enough workgroups for two per CU, at least 4 slabs each, parts within the scratch
+  // (one per CU measured slower: the 128 x 128 tiles are latency-bound at 2 waves per SIMD)
   int splits = 1;
   if (g.part && T < 512) {
     splits = (512 + T - 1) / T;
