@@ -48,6 +48,19 @@ def test_prefill_checks_arguments_before_any_launch():
     assert lib.smolexp_load_lm_weights(None, None, 0) == fm.SMOLEXP_E_INVAL
 
 
+def test_train_step_checks_arguments_before_any_launch():
+    lib = fm.raw()
+    assert lib.smolexp_train_step(None, None, None, 1, None, None, None, None, None, 1, None) == fm.SMOLEXP_E_INVAL
+    # the binding refuses host tensors before calling the library
+    import torch
+    cfg = fm.smolexp_default_config(n_layers=2, max_batch=1, max_prefix=4)
+    x = torch.zeros((1, 50, 32))
+    with pytest.raises(ValueError):
+        fm.smolexp_train_step(None, cfg, torch.zeros((2, 2, 1, 5, 4, 64), dtype=torch.int16),
+                              torch.ones((1, 4), dtype=torch.uint8), x, x, torch.zeros(1),
+                              torch.zeros(fm.smolexp_weight_count(cfg)), torch.zeros(1))
+
+
 def test_weight_count_matches_manifest():
     for L in (1, 2, 4, 16):
         assert fm.smolexp_weight_count(fm.smolexp_default_config(n_layers=L)) == synth.weight_count(L)
