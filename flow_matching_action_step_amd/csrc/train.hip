@@ -58,23 +58,25 @@ __device__ inline float4 row4(const bf16_t* p) {
   return make_float4(bf16_val(u.x & 0xFFFF), bf16_val(u.x >> 16), bf16_val(u.y & 0xFFFF), bf16_val(u.y >> 16));
 }
 
-// One operand's share of a slab, as 8 x 4 bf16 per thread.  Stored along k (KC): 4-wide
-// vectors of one row.  Stored across k: a 4 x 4 block (4 k-rows of 4 consecutive operand
+// One operand's share of a slab, as NV x 4 bf16 per thread.  Stored along k (KC): 4-wide
+// vectors of one row.  Stored across k: 4 x 4 blocks (4 k-rows of 4 consecutive operand
 // rows, each a 16-byte load coalesced across the lanes), transposed in registers into 4
-// rows of 4 k-values; thread t takes operand rows 4 (t % 32) .. +3 and k-quads t / 32 and
-// t / 32 + 8.  R (the operand's row count) is a multiple of 4 there.
+// rows of 4 k-values; thread t takes operand rows 4 (t % 32) .. +3 and k-quads t / 32 + 8 q.
+// R (the operand's row count) is a multiple of 4 there.
+constexpr int NV = GBM * GBK / 4 / 256;  // 4-wide vectors per thread per operand and slab
+
 template <typename T, bool KC>
-__device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int K, int tid, uint2 (&v)[8]) {
+__device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int K, int tid, uint2 (&v)[NV]) {
   if constexpr (KC) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i, r = r0 + (idx >> 4), k = k0 + (idx & 15) * 4;
+    for (int i = 0; i < NV; ++i) {
+      const int idx = tid + 256 * i, r = r0 + idx / (GBK / 4), k = k0 + (idx % (GBK / 4)) * 4;
       v[i] = (r < R && k < K) ? load4(X + (size_t)r * ld + k) : make_uint2(0, 0);
     }
   } else {
     const int r = r0 + (tid & 31) * 4;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < NV / 4; ++blk) {
       const int kb = k0 + (tid >> 5) * 4 + blk * 32;
       float4 x[4];
 #pragma unroll
@@ -89,14 +91,14 @@ __device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int 
 }
 
 template <bool KC>
-__device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[8]) {
+__device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[NV]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int r, k;
     if constexpr (KC) {
       const int idx = tid + 256 * i;
-      r = idx >> 4;
-      k = (idx & 15) * 4;
+      r = idx / (GBK / 4);
+      k = (idx % (GBK / 4)) * 4;
     } else {
       r = (tid & 31) * 4 + (i & 3);
       k = (tid >> 5) * 4 + (i >> 2) * 32;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits
   const int kbeg = sidx * kc, kend = min(g.K, kbeg + kc);
   const TA* A = static_cast<const TA*>(g.A);
   const TB* Bm = static_cast<const TB*>(g.B);
-  uint2 ra[8], rb[8];
+  uint2 ra[NV], rb[NV];
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits
       load_slab<TB, BK>(Bm, g.ldb, n0, N, k0 + GBK, kend, tid, rb);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < GBK / 32; ++ks) {
       bf16x8 af[4], bw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -183,3 +183,49 @@ def test_train_step_deterministic_inputs_untouched_and_errors():
             fm.smolexp_destroy(h2)
     finally:
         tr.close()
+
+
+def test_train_step_full_size_b64_p257():
+    """The benchmarked configuration (16 layers, 64 samples, prefix 257): the loss against the
+    oracle's forward pass for every sample, and the batch's gradients against the mean of the
+    gradients of its two halves (the loss is a per-element mean, so that identity holds
+    exactly in exact arithmetic; it exercises the full-size k-split and workspace).
+
+    The two GPU results are not bitwise related: the k-split of a product depends on its
+    row count, so the halves sum in another fp32 order, and the chain of bf16 roundings turns
+    any 1-ulp difference into another draw of the same rounding noise (a perturbation d
+    flips about d / 2^-9 of the roundings of the next bf16 operand, an RMS change of about
+    sqrt(d 2^-9); a few such stages reach the full noise level).  Each side is within the
+    parity bound of the exact gradient, so they differ by at most twice that bound.
+    """
+    _say("train step at the bench size: 16 layers, batch 64, P = 257")
+    L, B, P = 16, 64, 257
+    wl = synth.make_workload("expert16_b64_p257", with_weights=False)
+    tr = Trainer(L, B, P, gain_seed=None)
+    try:
+        kv, mask = wl["prefix_kv"], wl["mask"]
+        a, eps, t = synth.draw_actions(B), wl["noise"], synth.draw_flow_times(B)
+        loss, flat, _ = tr.step(kv, mask, a, eps, t)
+        assert np.isfinite(flat).all()
+        halves = []
+        for sl in (slice(0, 32), slice(32, 64)):
+            halves.append(tr.step(np.ascontiguousarray(kv[:, :, sl]), mask[sl], a[sl], eps[sl], t[sl]))
+        g_half = 0.5 * (halves[0][1] + halves[1][1])
+        l_half = 0.5 * (halves[0][0] + halves[1][0])
+        got, want = _unpack(flat, L), _unpack(g_half, L)
+        worst = max(np.linalg.norm(got[n] - want[n]) / np.linalg.norm(want[n]) for n in got)
+        # the oracle's loss: each sample's velocity from the float64 forward pass
+        se = 0.0
+        for b in range(B):
+            pk, pv = oracle.bf16_bits_to_float(kv[:, 0, b]), oracle.bf16_bits_to_float(kv[:, 1, b])
+            x = float(t[b]) * eps[b].astype(np.float64) + (1 - float(t[b])) * a[b].astype(np.float64)
+            v = oracle.velocity(tr.W, tr.ocfg, x, float(t[b]), pk, pv, mask[b].astype(bool))
+            se += float(np.sum((v - (eps[b].astype(np.float64) - a[b])) ** 2))
+        ol = se / (B * 50 * 32)
+        print(f"[parity] train16 b64 p257: loss {loss:.6f} vs oracle {ol:.6f} (rel {abs(loss - ol) / ol:.1e}); "
+              f"halves: loss {l_half:.6f}, worst gradient rel {worst:.2e}", flush=True)
+        assert abs(loss - ol) <= LOSS_RTOL * ol
+        assert abs(loss - l_half) <= 1e-5 * ol
+        assert worst <= 2 * G_RTOL
+    finally:
+        tr.close()
