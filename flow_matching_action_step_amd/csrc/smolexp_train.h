@@ -31,6 +31,7 @@ struct TrAttn {
   const int* nval;      // [B]
   int P;
   float* o;             // [M][960] attention output (forward), read by the backward
+  bf16_t* o16;          // forward: the same output in bf16 (the o projection's operand)
   float* lse;           // [B][15][50] log-sum-exp of each score row (INFINITY: no key)
   const float* dout;    // backward: dO [M][960]
   float* dq;            // backward: dQ [M][ldq] at 64 h (rotated space)
@@ -49,10 +50,13 @@ size_t train_manifest_count(int L);
 
 // Activations kept for the backward pass (fp32, [rows][columns], rows = 50 B) and its scratch.
 struct TrainWs {
-  float *xt, *target, *z, *s, *sil;
+  float *xt, *target, *z, *s;
+  bf16_t* sil;              // SiLU of the time MLP's first layer (an operand only: bf16)
   float *H;                 // [L + 1][M][720] layer inputs (H[0] = time MLP output), H[L] the last output
-  float *N1, *R1, *QKV, *O, *LSE, *HM, *N2, *R2, *GU, *ACT;  // per layer
-  float *NF, *RF, *V;
+  float *R1, *QKV, *O, *LSE, *HM, *R2, *GU;  // per layer
+  bf16_t *N1, *N2, *ACT, *O16;  // per layer, matrix-product operands only: stored as the bf16 the products read
+  bf16_t* NF;
+  float *RF, *V;
   float *dv, *dh, *dn, *dact, *dgu, *dout, *dqkv, *dkv, *part;
   float *split;             // k-split partial sums of the matrix products
   int *vidx, *nval;

@@ -73,6 +73,22 @@ __device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int 
       const int idx = tid + 256 * i, r = r0 + idx / (GBK / 4), k = k0 + (idx % (GBK / 4)) * 4;
       v[i] = (r < R && k < K) ? load4(X + (size_t)r * ld + k) : make_uint2(0, 0);
     }
+  } else if constexpr (sizeof(T) == 2) {
+    // bf16 across k: 4 k-rows x 8 operand rows per thread (16-byte loads), rows 8 (t % 16)
+    // .. +7, k-quad t / 16; R is a multiple of 8 here
+    static_assert(GBK == 64 && NV == 8, "one 4 x 8 block per thread covers the slab");
+    const int r = r0 + (tid & 15) * 8, kb = k0 + (tid >> 4) * 4;
+    uint4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      x[u] = (r < R && kb + u < K) ? *reinterpret_cast<const uint4*>(X + (size_t)(kb + u) * ld + r) : make_uint4(0, 0, 0, 0);
+    auto h = [&](const uint4& q, int c) -> uint32_t {  // bf16 c of the 8 in q
+      const uint32_t word = (c >> 1) == 0 ? q.x : (c >> 1) == 1 ? q.y : (c >> 1) == 2 ? q.z : q.w;
+      return (c & 1) ? (word >> 16) : (word & 0xFFFF);
+    };
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      v[c] = make_uint2(h(x[0], c) | (h(x[1], c) << 16), h(x[2], c) | (h(x[3], c) << 16));
   } else {
     const int r = r0 + (tid & 31) * 4;
 #pragma unroll
@@ -90,7 +106,7 @@ __device__ inline void load_slab(const T* X, int ld, int r0, int R, int k0, int 
   }
 }
 
-template <bool KC>
+template <bool KC, bool H8>
 __device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[NV]) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -99,6 +115,9 @@ __device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[NV]) {
       const int idx = tid + 256 * i;
       r = idx / (GBK / 4);
       k = (idx % (GBK / 4)) * 4;
+    } else if constexpr (H8) {
+      r = (tid & 15) * 8 + i;
+      k = (tid >> 4) * 4;
     } else {
       r = (tid & 31) * 4 + (i & 3);
       k = (tid >> 5) * 4 + (i >> 2) * 32;
@@ -133,8 +152,8 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits
   load_slab<TB, BK>(Bm, g.ldb, n0, N, kbeg, kend, tid, rb);
   for (int k0 = kbeg; k0 < kend; k0 += GBK) {
     __syncthreads();  // every wave is done reading the previous slab
-    store_slab<AK>(sA, tid, ra);
-    store_slab<BK>(sB, tid, rb);
+    store_slab<AK, sizeof(TA) == 2>(sA, tid, ra);
+    store_slab<BK, sizeof(TB) == 2>(sB, tid, rb);
     __syncthreads();
     if (k0 + GBK < kend) {
       load_slab<TA, AK>(A, g.lda, m0, M, k0 + GBK, kend, tid, ra);
@@ -235,7 +254,7 @@ __device__ inline float wave_max(float v) {
 }
 
 // RMSNorm of 720-wide rows, one wave per row: n = h r g with r = (mean(h^2) + eps)^(-1/2).
-__global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const bf16_t* g, float eps, int M, float* n,
+__global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const bf16_t* g, float eps, int M, bf16_t* n,
                                                          float* rstd) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -243,7 +262,7 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
   float ss = 0.f;
   for (int c = lane; c < kD; c += 64) ss += hr[c] * hr[c];
   const float r = rsqrtf(wave_sum(ss) / kD + eps);
-  for (int c = lane; c < kD; c += 64) n[(size_t)row * kD + c] = hr[c] * r * bf16_val(g[c]);
+  for (int c = lane; c < kD; c += 64) n[(size_t)row * kD + c] = (bf16_t)bf16_bits(hr[c] * r * bf16_val(g[c]));
   if (lane == 0) rstd[row] = r;
 }
 
@@ -340,18 +359,18 @@ __device__ inline float silu_grad_f(float z) {
   return s * (1.f + z * (1.f - s));
 }
 
-__global__ __launch_bounds__(256) void tr_silu_kernel(const float* s, float* out, size_t n) {
-  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = silu_f(s[i]);
+__global__ __launch_bounds__(256) void tr_silu_kernel(const float* s, bf16_t* out, size_t n) {
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = (bf16_t)bf16_bits(silu_f(s[i]));
 }
 __global__ __launch_bounds__(256) void tr_silu_bwd_kernel(const float* d, const float* s, float* out, size_t n) {
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = d[i] * silu_grad_f(s[i]);
 }
 
 // gu [M][4096] = [gate | up]; act = SiLU(gate) up.
-__global__ __launch_bounds__(256) void tr_swiglu_kernel(const float* gu, float* act, size_t n) {
+__global__ __launch_bounds__(256) void tr_swiglu_kernel(const float* gu, bf16_t* act, size_t n) {
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const size_t row = i / kFFN, c = i % kFFN;
-    act[i] = silu_f(gu[row * kGU + c]) * gu[row * kGU + kFFN + c];
+    act[i] = (bf16_t)bf16_bits(silu_f(gu[row * kGU + c]) * gu[row * kGU + kFFN + c]);
   }
 }
 __global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, const float* gu, float* dgu, size_t n) {
@@ -602,7 +621,11 @@ __global__ __launch_bounds__(256) void tr_attn_fwd_kernel(const TrAttn a) {
     if (i < kRows) {
       const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) a.o[(size_t)(b * kChunk + i) * kNQ + h * kHD + dt * 16 + c16] = o[dt][r] * inv;
+      for (int dt = 0; dt < 4; ++dt) {
+        const size_t e = (size_t)(b * kChunk + i) * kNQ + h * kHD + dt * 16 + c16;
+        a.o[e] = o[dt][r] * inv;
+        a.o16[e] = (bf16_t)bf16_bits(o[dt][r] * inv);
+      }
       if (c16 == 0) a.lse[((size_t)b * kHQ + h) * kRows + i] = l[r] > 0.f ? m[r] + __logf(l[r]) : INFINITY;
     }
   }
@@ -736,9 +759,10 @@ inline int ew_grid(size_t n) { return (int)((n + 255) / 256 < 8192 ? (n + 255) /
 hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kcont, bool b_bf16, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   // operands are read in 4-wide vectors along their contiguous axis (K, or the operand's
-  // rows M / N when stored across k): that length and the leading dimension must be
-  // multiples of 4, so a vector never straddles an edge
-  if (g.K <= 0 || g.lda % 4 || g.ldb % 4 || (a_kcont ? g.K : g.M) % 4 || (b_kcont ? g.K : g.N) % 4)
+  // rows M / N when stored across k; 8-wide for bf16 stored across k): that length and the
+  // leading dimension must be multiples of the width, so a vector never straddles an edge
+  const int wa = (!a_kcont && a_bf16) ? 8 : 4, wb = (!b_kcont && b_bf16) ? 8 : 4;
+  if (g.K <= 0 || g.lda % wa || g.ldb % wb || (a_kcont ? g.K : g.M) % wa || (b_kcont ? g.K : g.N) % wb)
     return hipErrorInvalidValue;
   const int T = ((g.M + GBM - 1) / GBM) * ((g.N + GBN - 1) / GBN), per = (T + 7) / 8;
   const int nslab = (g.K + GBK - 1) / GBK;
@@ -759,6 +783,10 @@ hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kco
     hipLaunchKernelGGL((tr_gemm_kernel<float, true, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
   else if (!a_bf16 && !a_kcont && !b_bf16 && !b_kcont)
     hipLaunchKernelGGL((tr_gemm_kernel<float, false, float, false>), grid, block, 0, s, g, splits, kc, g.part);
+  else if (a_bf16 && a_kcont && b_bf16 && b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<bf16_t, true, bf16_t, true>), grid, block, 0, s, g, splits, kc, g.part);
+  else if (!a_bf16 && !a_kcont && b_bf16 && !b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<float, false, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
@@ -816,23 +844,25 @@ size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
   const size_t M = (size_t)B * kChunk, nblk = (M + kRB - 1) / kRB;
   size_t off = 0;
   auto f = [&](size_t n) { size_t o = off; off += (n * 4 + 255) & ~(size_t)255; return base ? (float*)(base + o) : nullptr; };
+  auto hb = [&](size_t n) { size_t o = off; off += (n * 2 + 255) & ~(size_t)255; return base ? (bf16_t*)(base + o) : nullptr; };
   w->xt = f(M * kAD);
   w->target = f(M * kAD);
   w->z = f(M * 2 * kD);
   w->s = f(M * kD);
-  w->sil = f(M * kD);
+  w->sil = hb(M * kD);
   w->H = f((size_t)(L + 1) * M * kD);
-  w->N1 = f((size_t)L * M * kD);
+  w->N1 = hb((size_t)L * M * kD);
   w->R1 = f((size_t)L * M);
   w->QKV = f((size_t)L * M * kNQKV);
   w->O = f((size_t)L * M * kNQ);
+  w->O16 = hb((size_t)L * M * kNQ);
   w->LSE = f((size_t)L * B * kHQ * kChunk);
   w->HM = f((size_t)L * M * kD);
-  w->N2 = f((size_t)L * M * kD);
+  w->N2 = hb((size_t)L * M * kD);
   w->R2 = f((size_t)L * M);
   w->GU = f((size_t)L * M * kGU);
-  w->ACT = f((size_t)L * M * kFFN);
-  w->NF = f(M * kD);
+  w->ACT = hb((size_t)L * M * kFFN);
+  w->NF = hb(M * kD);
   w->RF = f(M);
   w->V = f(M * kAD);
   w->dv = f(M * kAD);
@@ -866,16 +896,16 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     g.Cin = cin; g.bias = bias; g.alpha = 1.f; g.part = w.split; g.part_cap = t.split_cap;
     return launch_tr_gemm(g, ak, abf, bk, bbf, st);
   };
-  // y W^T (+ cin) (+ bias): activations fp32 along k, weights bf16 [out][in]
-  auto fwd = [&](const float* x, int ldx, size_t woff, int n, int k, float* y, int ldy, const float* cin,
-                 const float* bias) { return gemm(M, n, k, x, ldx, true, false, W + woff, k, true, true, y, ldy, cin, bias); };
+  // y W^T (+ cin) (+ bias): activations (fp32, or the bf16 the product reads) along k, weights bf16 [out][in]
+  auto fwd = [&](const void* x, bool xbf, int ldx, size_t woff, int n, int k, float* y, int ldy, const float* cin,
+                 const float* bias) { return gemm(M, n, k, x, ldx, true, xbf, W + woff, k, true, true, y, ldy, cin, bias); };
   // dx = dy W: W [n_out][k_in] read across its rows
   auto bwd_x = [&](const float* dy, int n_out, size_t woff, int k_in, int ldw, float* dx) {
     return gemm(M, k_in, n_out, dy, n_out, true, false, W + woff, ldw, false, true, dx, k_in, nullptr, nullptr);
   };
-  // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide)
-  auto bwd_w = [&](const float* dy, int ldy, int n_out, const float* x, int k_in, size_t goff) {
-    return gemm(n_out, k_in, M, dy, ldy, false, false, x, k_in, false, false, G + goff, k_in, nullptr, nullptr);
+  // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide; x fp32 or bf16)
+  auto bwd_w = [&](const float* dy, int ldy, int n_out, const void* x, bool xbf, int k_in, size_t goff) {
+    return gemm(n_out, k_in, M, dy, ldy, false, false, x, k_in, false, xbf, G + goff, k_in, nullptr, nullptr);
   };
   auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
     hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
@@ -891,6 +921,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   };
   auto Hl = [&](int l) { return w.H + (size_t)l * M * kD; };
   auto lay = [&](float* base, int l, size_t per_row) { return base + (size_t)l * M * per_row; };
+  auto lay16 = [&](bf16_t* base, int l, size_t per_row) { return base + (size_t)l * M * per_row; };
 
   // ---- forward
   hipLaunchKernelGGL(tr_prep_kernel, dim3(B), dim3(64), 0, st, t.mask, t.P, w.vidx, w.nval);
@@ -899,23 +930,23 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
                      w.target, w.z);
   TR_CHECK();
   // the four biases come widened to fp32 (bias32: b_in, b_t1, b_t2, b_out)
-  if ((e = fwd(w.xt, kAD, off.ain_w, kD, kAD, w.z, 2 * kD, nullptr, t.bias32 + 0)) != hipSuccess) return e;
-  if ((e = fwd(w.z, 2 * kD, off.tin_w, kD, 2 * kD, w.s, kD, nullptr, t.bias32 + kD)) != hipSuccess) return e;
+  if ((e = fwd(w.xt, false, kAD, off.ain_w, kD, kAD, w.z, 2 * kD, nullptr, t.bias32 + 0)) != hipSuccess) return e;
+  if ((e = fwd(w.z, false, 2 * kD, off.tin_w, kD, 2 * kD, w.s, kD, nullptr, t.bias32 + kD)) != hipSuccess) return e;
   hipLaunchKernelGGL(tr_silu_kernel, dim3(ew_grid((size_t)M * kD)), dim3(256), 0, st, w.s, w.sil, (size_t)M * kD);
   TR_CHECK();
-  if ((e = fwd(w.sil, kD, off.tout_w, kD, kD, Hl(0), kD, nullptr, t.bias32 + 2 * kD)) != hipSuccess) return e;
+  if ((e = fwd(w.sil, true, kD, off.tout_w, kD, kD, Hl(0), kD, nullptr, t.bias32 + 2 * kD)) != hipSuccess) return e;
   for (int l = 0; l < L; ++l) {
     TrOffsets ol;
     train_offsets(L, l, &ol);
     const TrLayerOffsets& lo = ol.layer;
     const bool self = l % 2 == 0;
     const int nq = self ? kNQKV : kNQ;
-    float *n1 = lay(w.N1, l, kD), *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
-    float *hm = lay(w.HM, l, kD), *n2 = lay(w.N2, l, kD), *r2 = w.R2 + (size_t)l * M;
-    float *gu = lay(w.GU, l, kGU), *act = lay(w.ACT, l, kFFN);
+    float *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
+    float *hm = lay(w.HM, l, kD), *r2 = w.R2 + (size_t)l * M, *gu = lay(w.GU, l, kGU);
+    bf16_t *n1 = lay16(w.N1, l, kD), *n2 = lay16(w.N2, l, kD), *act = lay16(w.ACT, l, kFFN), *o16 = lay16(w.O16, l, kNQ);
     hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, Hl(l), W + lo.norm1, t.rms_eps, M, n1, r1);
     TR_CHECK();
-    if ((e = fwd(n1, kD, lo.qkv, nq, kD, qkv, kNQKV, nullptr, nullptr)) != hipSuccess) return e;
+    if ((e = fwd(n1, true, kD, lo.qkv, nq, kD, qkv, kNQKV, nullptr, nullptr)) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, qkv, kNQKV, self ? kHQ + kHKV : kHQ, w.nval, t.rope, 1.f);
     TR_CHECK();
     TrAttn aa;
@@ -923,22 +954,22 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
     aa.pv = aa.pk + (size_t)B * kHKV * t.P * kHD;
     aa.vidx = w.vidx; aa.nval = w.nval; aa.P = t.P;
-    aa.o = o; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
+    aa.o = o; aa.o16 = o16; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
     aa.dout = nullptr; aa.dq = nullptr; aa.dkv = nullptr;
     if (self) hipLaunchKernelGGL(tr_attn_fwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
     else hipLaunchKernelGGL(tr_attn_fwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
     TR_CHECK();
-    if ((e = fwd(o, kNQ, lo.o, kD, kNQ, hm, kD, Hl(l), nullptr)) != hipSuccess) return e;
+    if ((e = fwd(o16, true, kNQ, lo.o, kD, kNQ, hm, kD, Hl(l), nullptr)) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, hm, W + lo.norm2, t.rms_eps, M, n2, r2);
     TR_CHECK();
-    if ((e = fwd(n2, kD, lo.gu, kGU, kD, gu, kGU, nullptr, nullptr)) != hipSuccess) return e;
+    if ((e = fwd(n2, true, kD, lo.gu, kGU, kD, gu, kGU, nullptr, nullptr)) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_swiglu_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, gu, act, (size_t)M * kFFN);
     TR_CHECK();
-    if ((e = fwd(act, kFFN, lo.down, kD, kFFN, Hl(l + 1), kD, hm, nullptr)) != hipSuccess) return e;
+    if ((e = fwd(act, true, kFFN, lo.down, kD, kFFN, Hl(l + 1), kD, hm, nullptr)) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, Hl(L), W + off.fnorm, t.rms_eps, M, w.NF, w.RF);
   TR_CHECK();
-  if ((e = fwd(w.NF, kD, off.aout_w, kAD, kD, w.V, kAD, nullptr, t.bias32 + 3 * kD)) != hipSuccess) return e;
+  if ((e = fwd(w.NF, true, kD, off.aout_w, kAD, kD, w.V, kAD, nullptr, t.bias32 + 3 * kD)) != hipSuccess) return e;
   // ---- loss
   const int lblk = (M + 7) / 8;
   hipLaunchKernelGGL(tr_loss_kernel, dim3(lblk), dim3(256), 0, st, w.V, w.target, M, 1.f / ((float)M * kAD), w.dv,
@@ -949,7 +980,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   hipLaunchKernelGGL(tr_scale_kernel, dim3(1), dim3(1), 0, st, t.loss, 1.f / ((float)M * kAD));
   TR_CHECK();
   // ---- backward
-  if ((e = bwd_w(w.dv, kAD, kAD, w.NF, kD, off.aout_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dv, kAD, kAD, w.NF, true, kD, off.aout_w)) != hipSuccess) return e;
   if ((e = colsum(w.dv, kAD, G + off.aout_b)) != hipSuccess) return e;
   if ((e = bwd_x(w.dv, kAD, off.aout_w, kD, kD, w.dn)) != hipSuccess) return e;
   if ((e = norm_bwd(w.dn, Hl(L), w.RF, off.fnorm, nullptr, w.dh)) != hipSuccess) return e;
@@ -959,27 +990,27 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     const TrLayerOffsets& lo = ol.layer;
     const bool self = l % 2 == 0;
     const int nq = self ? kNQKV : kNQ;
-    float *n1 = lay(w.N1, l, kD), *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
-    float *hm = lay(w.HM, l, kD), *n2 = lay(w.N2, l, kD), *r2 = w.R2 + (size_t)l * M;
-    float *gu = lay(w.GU, l, kGU), *act = lay(w.ACT, l, kFFN);
+    float *r1 = w.R1 + (size_t)l * M, *qkv = lay(w.QKV, l, kNQKV), *o = lay(w.O, l, kNQ);
+    float *hm = lay(w.HM, l, kD), *r2 = w.R2 + (size_t)l * M, *gu = lay(w.GU, l, kGU);
+    bf16_t *n1 = lay16(w.N1, l, kD), *n2 = lay16(w.N2, l, kD), *act = lay16(w.ACT, l, kFFN), *o16 = lay16(w.O16, l, kNQ);
     // MLP
     if ((e = bwd_x(w.dh, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh, kD, kD, act, kFFN, lo.down)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh, kD, kD, act, true, kFFN, lo.down)) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, w.dact, gu, w.dgu,
                        (size_t)M * kFFN);
     TR_CHECK();
     if ((e = bwd_x(w.dgu, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dgu, kGU, kGU, n2, kD, lo.gu)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dgu, kGU, kGU, n2, true, kD, lo.gu)) != hipSuccess) return e;
     if ((e = norm_bwd(w.dn, hm, r2, lo.norm2, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(hm)
     // attention
     if ((e = bwd_x(w.dh, kD, lo.o, kNQ, kNQ, w.dout)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh, kD, kD, o, kNQ, lo.o)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh, kD, kD, o16, true, kNQ, lo.o)) != hipSuccess) return e;
     TrAttn aa;
     aa.qkv = qkv; aa.ldq = kNQKV;
     aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
     aa.pv = aa.pk + (size_t)B * kHKV * t.P * kHD;
     aa.vidx = w.vidx; aa.nval = w.nval; aa.P = t.P;
-    aa.o = o; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
+    aa.o = o; aa.o16 = nullptr; aa.lse = w.LSE + (size_t)l * B * kHQ * kChunk;
     aa.dout = w.dout; aa.dq = w.dqkv; aa.dkv = w.dkv;
     if (self) hipLaunchKernelGGL(tr_attn_bwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
     else hipLaunchKernelGGL(tr_attn_bwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
@@ -992,21 +1023,21 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     }
     if ((e = gemm(M, kD, nq, w.dqkv, kNQKV, true, false, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
       return e;
-    if ((e = bwd_w(w.dqkv, kNQKV, nq, n1, kD, lo.qkv)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dqkv, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
     if ((e = norm_bwd(w.dn, Hl(l), r1, lo.norm1, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(h_l)
   }
   // time MLP and action_in (dh = d h0)
-  if ((e = bwd_w(w.dh, kD, kD, w.sil, kD, off.tout_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dh, kD, kD, w.sil, true, kD, off.tout_w)) != hipSuccess) return e;
   if ((e = colsum(w.dh, kD, G + off.tout_b)) != hipSuccess) return e;
   if ((e = bwd_x(w.dh, kD, off.tout_w, kD, kD, w.dn)) != hipSuccess) return e;
   hipLaunchKernelGGL(tr_silu_bwd_kernel, dim3(ew_grid((size_t)M * kD)), dim3(256), 0, st, w.dn, w.s, w.dn, (size_t)M * kD);
   TR_CHECK();
-  if ((e = bwd_w(w.dn, kD, kD, w.z, 2 * kD, off.tin_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dn, kD, kD, w.z, false, 2 * kD, off.tin_w)) != hipSuccess) return e;
   if ((e = colsum(w.dn, kD, G + off.tin_b)) != hipSuccess) return e;
   // dy = ds W_t1[:, :720]
   if ((e = gemm(M, kD, kD, w.dn, kD, true, false, W + off.tin_w, 2 * kD, false, true, w.dh, kD, nullptr, nullptr)) != hipSuccess)
     return e;
-  if ((e = bwd_w(w.dh, kD, kD, w.xt, kAD, off.ain_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dh, kD, kD, w.xt, false, kAD, off.ain_w)) != hipSuccess) return e;
   if ((e = colsum(w.dh, kD, G + off.ain_b)) != hipSuccess) return e;
 #undef TR_CHECK
   return hipSuccess;
