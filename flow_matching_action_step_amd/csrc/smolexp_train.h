@@ -57,7 +57,8 @@ struct TrainWs {
   bf16_t *N1, *N2, *ACT, *O16;  // per layer, matrix-product operands only: stored as the bf16 the products read
   bf16_t* NF;
   float *RF, *V;
-  float *dv, *dh, *dn, *dact, *dgu, *dout, *dqkv, *dkv, *part;
+  float *dv, *dh, *dn, *dact, *dout, *dqkv, *dkv, *part;
+  bf16_t *dh16, *dgu;       // bf16 copy of dh, and the SwiGLU gradient (matrix-product operands only)
   float *split;             // k-split partial sums of the matrix products
   int *vidx, *nval;
 };

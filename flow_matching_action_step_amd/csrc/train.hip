@@ -269,13 +269,13 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
 // Backward of the RMSNorm above over 16 rows per workgroup:
 //   dh = r (u - hat mean(u hat)) (+ resid), u = dy g, hat = h r;
 //   part[blk][c] = sum over the block's rows of dy hat (the gain's gradient, before the
-//   sum over blocks).  dh may alias resid.  Phase 1: each wave forms mean(u hat) of 4 rows
+//   sum over blocks).  dh may alias resid; dh16 receives dh in bf16 (a product operand).  Phase 1: each wave forms mean(u hat) of 4 rows
 //   (4-wide loads); phase 2: thread t takes columns 4t .. 4t + 3 of all 16 rows (the second
 //   read of dy and h comes from L2).
 constexpr int kRB = 16;
 __global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, const float* h, const float* rstd,
-                                                             const bf16_t* g, const float* resid, float* dh, int M,
-                                                             float* part) {
+                                                             const bf16_t* g, const float* resid, float* dh,
+                                                             bf16_t* dh16, int M, float* part) {
   __shared__ float smean[kRB];
   const int blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int Q = kD / 4;  // 180 column quads
@@ -318,6 +318,8 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, co
         v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
       }
       *reinterpret_cast<float4*>(dh + o) = v;
+      *reinterpret_cast<uint2*>(dh16 + o) =
+          make_uint2(bf16_bits(v.x) | (bf16_bits(v.y) << 16), bf16_bits(v.z) | (bf16_bits(v.w) << 16));
       acc.x += d.x * x.x * r;
       acc.y += d.y * x.y * r;
       acc.z += d.z * x.z * r;
@@ -373,12 +375,12 @@ __global__ __launch_bounds__(256) void tr_swiglu_kernel(const float* gu, bf16_t*
     act[i] = (bf16_t)bf16_bits(silu_f(gu[row * kGU + c]) * gu[row * kGU + kFFN + c]);
   }
 }
-__global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, const float* gu, float* dgu, size_t n) {
+__global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, const float* gu, bf16_t* dgu, size_t n) {
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     const size_t row = i / kFFN, c = i % kFFN;
     const float gt = gu[row * kGU + c], up = gu[row * kGU + kFFN + c], d = dact[i];
-    dgu[row * kGU + c] = d * up * silu_grad_f(gt);
-    dgu[row * kGU + kFFN + c] = d * silu_f(gt);
+    dgu[row * kGU + c] = (bf16_t)bf16_bits(d * up * silu_grad_f(gt));
+    dgu[row * kGU + kFFN + c] = (bf16_t)bf16_bits(d * silu_f(gt));
   }
 }
 
@@ -787,6 +789,10 @@ hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kco
     hipLaunchKernelGGL((tr_gemm_kernel<bf16_t, true, bf16_t, true>), grid, block, 0, s, g, splits, kc, g.part);
   else if (!a_bf16 && !a_kcont && b_bf16 && !b_kcont)
     hipLaunchKernelGGL((tr_gemm_kernel<float, false, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
+  else if (a_bf16 && a_kcont && b_bf16 && !b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<bf16_t, true, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
+  else if (a_bf16 && !a_kcont && b_bf16 && !b_kcont)
+    hipLaunchKernelGGL((tr_gemm_kernel<bf16_t, false, bf16_t, false>), grid, block, 0, s, g, splits, kc, g.part);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
@@ -869,7 +875,8 @@ size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
   w->dh = f(M * kD);
   w->dn = f(M * kD);
   w->dact = f(M * kFFN);
-  w->dgu = f(M * kGU);
+  w->dgu = hb(M * kGU);
+  w->dh16 = hb(M * kD);
   w->dout = f(M * kNQ);
   w->dqkv = f(M * kNQKV);
   w->dkv = f((size_t)B * kHQ * 2 * kChunk * kHD);
@@ -899,13 +906,13 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   // y W^T (+ cin) (+ bias): activations (fp32, or the bf16 the product reads) along k, weights bf16 [out][in]
   auto fwd = [&](const void* x, bool xbf, int ldx, size_t woff, int n, int k, float* y, int ldy, const float* cin,
                  const float* bias) { return gemm(M, n, k, x, ldx, true, xbf, W + woff, k, true, true, y, ldy, cin, bias); };
-  // dx = dy W: W [n_out][k_in] read across its rows
-  auto bwd_x = [&](const float* dy, int n_out, size_t woff, int k_in, int ldw, float* dx) {
-    return gemm(M, k_in, n_out, dy, n_out, true, false, W + woff, ldw, false, true, dx, k_in, nullptr, nullptr);
+  // dx = dy W: W [n_out][k_in] read across its rows; dy fp32 or bf16
+  auto bwd_x = [&](const void* dy, bool dybf, int n_out, size_t woff, int k_in, int ldw, float* dx) {
+    return gemm(M, k_in, n_out, dy, n_out, true, dybf, W + woff, ldw, false, true, dx, k_in, nullptr, nullptr);
   };
-  // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide; x fp32 or bf16)
-  auto bwd_w = [&](const float* dy, int ldy, int n_out, const void* x, bool xbf, int k_in, size_t goff) {
-    return gemm(n_out, k_in, M, dy, ldy, false, false, x, k_in, false, xbf, G + goff, k_in, nullptr, nullptr);
+  // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide; dy and x fp32 or bf16)
+  auto bwd_w = [&](const void* dy, bool dybf, int ldy, int n_out, const void* x, bool xbf, int k_in, size_t goff) {
+    return gemm(n_out, k_in, M, dy, ldy, false, dybf, x, k_in, false, xbf, G + goff, k_in, nullptr, nullptr);
   };
   auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
     hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
@@ -914,7 +921,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     return hipGetLastError();
   };
   auto norm_bwd = [&](const float* dy, const float* h, const float* r, size_t goff, const float* resid, float* dh) -> hipError_t {
-    hipLaunchKernelGGL(tr_rmsnorm_bwd_kernel, dim3(nblk), dim3(256), 0, st, dy, h, r, W + goff, resid, dh, M, w.part);
+    hipLaunchKernelGGL(tr_rmsnorm_bwd_kernel, dim3(nblk), dim3(256), 0, st, dy, h, r, W + goff, resid, dh, w.dh16, M, w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 63) / 64), dim3(256), 0, st, w.part, nblk, kD, G + goff);
     return hipGetLastError();
@@ -980,9 +987,9 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   hipLaunchKernelGGL(tr_scale_kernel, dim3(1), dim3(1), 0, st, t.loss, 1.f / ((float)M * kAD));
   TR_CHECK();
   // ---- backward
-  if ((e = bwd_w(w.dv, kAD, kAD, w.NF, true, kD, off.aout_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dv, false, kAD, kAD, w.NF, true, kD, off.aout_w)) != hipSuccess) return e;
   if ((e = colsum(w.dv, kAD, G + off.aout_b)) != hipSuccess) return e;
-  if ((e = bwd_x(w.dv, kAD, off.aout_w, kD, kD, w.dn)) != hipSuccess) return e;
+  if ((e = bwd_x(w.dv, false, kAD, off.aout_w, kD, kD, w.dn)) != hipSuccess) return e;
   if ((e = norm_bwd(w.dn, Hl(L), w.RF, off.fnorm, nullptr, w.dh)) != hipSuccess) return e;
   for (int l = L - 1; l >= 0; --l) {
     TrOffsets ol;
@@ -994,17 +1001,17 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     float *hm = lay(w.HM, l, kD), *r2 = w.R2 + (size_t)l * M, *gu = lay(w.GU, l, kGU);
     bf16_t *n1 = lay16(w.N1, l, kD), *n2 = lay16(w.N2, l, kD), *act = lay16(w.ACT, l, kFFN), *o16 = lay16(w.O16, l, kNQ);
     // MLP
-    if ((e = bwd_x(w.dh, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh, kD, kD, act, true, kFFN, lo.down)) != hipSuccess) return e;
+    if ((e = bwd_x(w.dh16, true, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh16, true, kD, kD, act, true, kFFN, lo.down)) != hipSuccess) return e;
     hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, w.dact, gu, w.dgu,
                        (size_t)M * kFFN);
     TR_CHECK();
-    if ((e = bwd_x(w.dgu, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dgu, kGU, kGU, n2, true, kD, lo.gu)) != hipSuccess) return e;
+    if ((e = bwd_x(w.dgu, true, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dgu, true, kGU, kGU, n2, true, kD, lo.gu)) != hipSuccess) return e;
     if ((e = norm_bwd(w.dn, hm, r2, lo.norm2, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(hm)
     // attention
-    if ((e = bwd_x(w.dh, kD, lo.o, kNQ, kNQ, w.dout)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh, kD, kD, o16, true, kNQ, lo.o)) != hipSuccess) return e;
+    if ((e = bwd_x(w.dh16, true, kD, lo.o, kNQ, kNQ, w.dout)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dh16, true, kD, kD, o16, true, kNQ, lo.o)) != hipSuccess) return e;
     TrAttn aa;
     aa.qkv = qkv; aa.ldq = kNQKV;
     aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
@@ -1023,21 +1030,21 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     }
     if ((e = gemm(M, kD, nq, w.dqkv, kNQKV, true, false, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
       return e;
-    if ((e = bwd_w(w.dqkv, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dqkv, false, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
     if ((e = norm_bwd(w.dn, Hl(l), r1, lo.norm1, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(h_l)
   }
   // time MLP and action_in (dh = d h0)
-  if ((e = bwd_w(w.dh, kD, kD, w.sil, true, kD, off.tout_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dh16, true, kD, kD, w.sil, true, kD, off.tout_w)) != hipSuccess) return e;
   if ((e = colsum(w.dh, kD, G + off.tout_b)) != hipSuccess) return e;
-  if ((e = bwd_x(w.dh, kD, off.tout_w, kD, kD, w.dn)) != hipSuccess) return e;
+  if ((e = bwd_x(w.dh16, true, kD, off.tout_w, kD, kD, w.dn)) != hipSuccess) return e;
   hipLaunchKernelGGL(tr_silu_bwd_kernel, dim3(ew_grid((size_t)M * kD)), dim3(256), 0, st, w.dn, w.s, w.dn, (size_t)M * kD);
   TR_CHECK();
-  if ((e = bwd_w(w.dn, kD, kD, w.z, false, 2 * kD, off.tin_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dn, false, kD, kD, w.z, false, 2 * kD, off.tin_w)) != hipSuccess) return e;
   if ((e = colsum(w.dn, kD, G + off.tin_b)) != hipSuccess) return e;
   // dy = ds W_t1[:, :720]
   if ((e = gemm(M, kD, kD, w.dn, kD, true, false, W + off.tin_w, 2 * kD, false, true, w.dh, kD, nullptr, nullptr)) != hipSuccess)
     return e;
-  if ((e = bwd_w(w.dh, kD, kD, w.xt, false, kAD, off.ain_w)) != hipSuccess) return e;
+  if ((e = bwd_w(w.dh, false, kD, kD, w.xt, false, kAD, off.ain_w)) != hipSuccess) return e;
   if ((e = colsum(w.dh, kD, G + off.ain_b)) != hipSuccess) return e;
 #undef TR_CHECK
   return hipSuccess;
