@@ -406,7 +406,7 @@ def run_train_stage(args):
         "value": B * args.steps / wall, "unit": "samples/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
-        "precision": "GEMM operands bf16, fp32 accumulate; attention, norms, loss and saved activations fp32",
+        "precision": "GEMM and attention operands bf16, fp32 accumulate; softmax, norms, loss and residual fp32",
         "data": "synthetic (seeded: weights N(0,0.02) bf16, K/V N(0,1) bf16, actions and noise N(0,1), t U(0,1))",
         "config": {"workload": args.workload, "stage": "train", "n_layers": L, "batch": B, "prefix_len": P},
         "roofline": roof,

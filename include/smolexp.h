@@ -231,9 +231,10 @@ int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_m
  *              d loss / d weight in manifest order, one value per weight.
  *   out_loss   device fp32 [1]: written.
  * Precision: matrix products take bf16 operands with fp32 accumulation; norms,
- * softmax, the loss and every activation kept for the backward pass are fp32.
- * Deterministic (no atomics).  The library keeps a workspace of about 46 KB per
- * chunk row per layer (fp32 activations) for the largest batch x prefix_len
+ * softmax, the loss and the residual stream are fp32; activations that only
+ * feed products are kept in bf16, as the products read them.
+ * Deterministic (no atomics).  The library keeps a workspace of about 41 KB per
+ * chunk row per layer (the activations) for the largest batch x prefix_len
  * seen; a call that needs more grows it first, which synchronizes the device.
  * Asynchronous on hip_stream otherwise.  SMOLEXP_E_STATE before
  * smolexp_load_weights; SMOLEXP_E_INVAL for NULL pointers or batch /
