@@ -636,17 +636,19 @@ __global__ __launch_bounds__(256) void tr_attn_fwd_kernel(const TrAttn a) {
 // Backward of the attention above, one (query, Q head) per workgroup.  D_i = dO_i . O_i;
 // per key block: S = Q K^T and dP = dO V^T on MFMA, P = exp(S - lse), dS = P (dP - D);
 // dQ += dS K on MFMA (K transposed in LDS); the chunk's keys (self layers) get this head's
-// dK = dS^T Q and dV = P^T dO (fp32, at most 50 keys) in dkv.  Q is pre-scaled, so S and dK
+// dK = dS^T Q and dV = P^T dO in dkv, on MFMA too (dS, P, Q and dO transposed in LDS).  Q is pre-scaled, so S and dK
 // carry the 1/8 already; dQ takes it at the end.
 struct AttnBwdSmem {
   uint16_t k[kKB * KLD];
   uint16_t v[kKB * KLD];
   uint16_t kt[kHD * KLD];
-  uint16_t ds16[64 * KLD];
-  float q[kRows * kHD];      // fp32 Q (scaled) and dO for the chunk keys' dK, dV
-  float dout[kRows * kHD];
-  float p[64 * (kKB + 1)];
-  float ds[64 * (kKB + 1)];
+  uint16_t ds16[64 * KLD];   // dS by row ([row][key]): the operand of dQ = dS K
+  // self layers: the chunk keys' dK = dS^T Q and dV = P^T dO on MFMA need dS and P by key
+  // and Q (scaled) and dO by dimension ([.][row], rows 50..63 zero)
+  uint16_t dst[kKB * KLD];
+  uint16_t pt[kKB * KLD];
+  uint16_t qt[kHD * KLD];
+  uint16_t dot[kHD * KLD];
   float dd[64], lse[64];
 };
 
@@ -658,11 +660,11 @@ __global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
   const int nb = a.nval[b], nk = nb + (SELF ? kChunk : 0), nblk = (nk + kKB - 1) / kKB;
   const float scale = 0.125f;
   if (SELF) {
-    for (int e = tid; e < kRows * kHD; e += 256) {
+    for (int e = tid; e < 64 * kHD; e += 256) {
       const int i = e / kHD, d = e % kHD;
       const size_t row = (size_t)(b * kChunk + i);
-      sm.q[e] = a.qkv[row * a.ldq + h * kHD + d] * scale;
-      sm.dout[e] = a.dout[row * kNQ + h * kHD + d];
+      sm.qt[d * KLD + i] = i < kRows ? (uint16_t)bf16_bits(a.qkv[row * a.ldq + h * kHD + d] * scale) : 0;
+      sm.dot[d * KLD + i] = i < kRows ? (uint16_t)bf16_bits(a.dout[row * kNQ + h * kHD + d]) : 0;
     }
   }
   for (int i = w; i < 64; i += 4) {
@@ -714,8 +716,8 @@ __global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
         const float d = p * (dp[jt][r] - dd_r[r]);
         sm.ds16[i * KLD + j] = (uint16_t)bf16_bits(d);
         if (SELF) {
-          sm.p[i * (kKB + 1) + j] = p;
-          sm.ds[i * (kKB + 1) + j] = d;
+          sm.pt[j * KLD + i] = (uint16_t)bf16_bits(p);
+          sm.dst[j * KLD + i] = (uint16_t)bf16_bits(d);
         }
       }
     }
@@ -729,18 +731,35 @@ __global__ __launch_bounds__(256) void tr_attn_bwd_kernel(const TrAttn a) {
                                                         dq[dt], 0, 0, 0);
     }
     if constexpr (SELF) {
-      const int kn = min(kKB, nk - kb * kKB);
-      for (int j = w; j < kn; j += 4) {
-        const int c = kb * kKB + j - nb;  // chunk key index
-        if (c < 0) continue;
-        float dk = 0.f, dv = 0.f;
-        for (int i = c; i < kRows; ++i) {  // only rows i >= c see chunk key c
-          dk += sm.ds[i * (kKB + 1) + j] * sm.q[i * kHD + lane];
-          dv += sm.p[i * (kKB + 1) + j] * sm.dout[i * kHD + lane];
+      // chunk keys in this block: wave w takes keys 16 w .. 16 w + 15 of it
+      const int c0 = kb * kKB + 16 * w - nb;  // chunk index of the wave's first key
+      if (c0 + 16 > 0 && c0 < kChunk) {
+        f32x4 dk[4], dv[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = (16 * w + c16) * KLD + ks * 32 + q4 * 8;
+          const bf16x8 dsf = frag_ld(sm.dst + off), pf = frag_ld(sm.pt + off);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int offd = (dt * 16 + c16) * KLD + ks * 32 + q4 * 8;
+            dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsf, frag_ld(sm.qt + offd), dk[dt], 0, 0, 0);
+            dv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, frag_ld(sm.dot + offd), dv[dt], 0, 0, 0);
+          }
         }
-        const size_t o = ((((size_t)b * kHQ + h) * 2) * kChunk + c) * kHD + lane;
-        a.dkv[o] = dk;
-        a.dkv[o + (size_t)kChunk * kHD] = dv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = c0 + 4 * q4 + r;
+          if (c >= 0 && c < kChunk) {
+            const size_t o = ((((size_t)b * kHQ + h) * 2) * kChunk + c) * kHD + c16;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              a.dkv[o + dt * 16] = dk[dt][r];
+              a.dkv[o + (size_t)kChunk * kHD + dt * 16] = dv[dt][r];
+            }
+          }
+        }
       }
     }
   }
