@@ -194,17 +194,30 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits
       }
 }
 
-// C[m][n] = alpha sum_s part[s][m][n] (+ Cin) (+ bias), the parts added in order.
+// C[m][n] = alpha sum_s part[s][m][n] (+ Cin) (+ bias), the parts added in order; four
+// columns per thread (N and ldc are multiples of 4).
 __global__ __launch_bounds__(256) void tr_split_sum_kernel(const TrGemm g, int splits, const float* part) {
-  const size_t n = (size_t)g.M * g.N;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[(size_t)s * n + e];
-    const size_t row = e / g.N, col = e % g.N;
-    v *= g.alpha;
-    if (g.Cin) v += g.Cin[row * g.ldc + col];
-    if (g.bias) v += g.bias[col];
-    g.C[row * g.ldc + col] = v;
+  const int n4 = g.N >> 2, total = g.M * n4;
+  const size_t stride = (size_t)g.M * g.N;
+  for (int q = blockIdx.x * 256 + threadIdx.x; q < total; q += gridDim.x * 256) {
+    const int row = q / n4, c = (q - row * n4) * 4;
+    const size_t e = (size_t)row * g.N + c;
+    float4 v = *reinterpret_cast<const float4*>(part + e);
+    for (int s = 1; s < splits; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(part + (size_t)s * stride + e);
+      v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+    }
+    v.x *= g.alpha; v.y *= g.alpha; v.z *= g.alpha; v.w *= g.alpha;
+    const size_t o = (size_t)row * g.ldc + c;
+    if (g.Cin) {
+      const float4 x = *reinterpret_cast<const float4*>(g.Cin + o);
+      v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+    }
+    if (g.bias) {
+      const float4 x = *reinterpret_cast<const float4*>(g.bias + c);
+      v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+    }
+    *reinterpret_cast<float4*>(g.C + o) = v;
   }
 }
 
@@ -342,17 +355,23 @@ __global__ __launch_bounds__(256) void tr_colsum_kernel(const float* x, int M, i
   part[(size_t)blk * N + c] = s;
 }
 
-// out[c] = sum over blocks of part[blk][c]: 64 columns per workgroup, wave w adds the
-// blocks blk = w mod 4 in order, and the four sums are added in wave order (deterministic).
+// out[c] = sum over blocks of part[blk][c]: 16 columns per workgroup, thread group u of 16
+// adds the blocks blk = u mod 16 in order, and the 16 sums are added in group order
+// (deterministic).
 __global__ __launch_bounds__(256) void tr_reduce_kernel(const float* part, int nblk, int N, float* out) {
-  __shared__ float red[4][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = blockIdx.x * 64 + lane;
+  __shared__ float red[16][17];
+  const int cl = threadIdx.x & 15, u = threadIdx.x >> 4, c = blockIdx.x * 16 + cl;
   float s = 0.f;
   if (c < N)
-    for (int b = w; b < nblk; b += 4) s += part[(size_t)b * N + c];
-  red[w][lane] = s;
+    for (int b = u; b < nblk; b += 16) s += part[(size_t)b * N + c];
+  red[u][cl] = s;
   __syncthreads();
-  if (w == 0 && c < N) out[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  if (u == 0 && c < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][cl];
+    out[c] = t;
+  }
 }
 
 __device__ inline float silu_f(float z) { return z / (1.f + __expf(-z)); }
@@ -816,8 +835,8 @@ hipError_t launch_tr_gemm(const TrGemm& g, bool a_kcont, bool a_bf16, bool b_kco
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  const size_t n = (size_t)g.M * g.N;
-  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  const size_t n4 = (size_t)g.M * g.N / 4;
+  const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 4096);
   hipLaunchKernelGGL(tr_split_sum_kernel, dim3(blocks), dim3(256), 0, s, g, splits, g.part);
   return hipGetLastError();
 }
@@ -936,13 +955,13 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
     hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_reduce_kernel, dim3((n + 63) / 64), dim3(256), 0, st, w.part, nblk, n, out);
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((n + 15) / 16), dim3(256), 0, st, w.part, nblk, n, out);
     return hipGetLastError();
   };
   auto norm_bwd = [&](const float* dy, const float* h, const float* r, size_t goff, const float* resid, float* dh) -> hipError_t {
     hipLaunchKernelGGL(tr_rmsnorm_bwd_kernel, dim3(nblk), dim3(256), 0, st, dy, h, r, W + goff, resid, dh, w.dh16, M, w.part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 63) / 64), dim3(256), 0, st, w.part, nblk, kD, G + goff);
+    hipLaunchKernelGGL(tr_reduce_kernel, dim3((kD + 15) / 16), dim3(256), 0, st, w.part, nblk, kD, G + goff);
     return hipGetLastError();
   };
   auto Hl = [&](int l) { return w.H + (size_t)l * M * kD; };
