@@ -51,6 +51,11 @@ __device__ inline uint2 load4(const bf16_t* p) { return *reinterpret_cast<const 
 // part[s][M][N]; tr_split_sum_kernel finishes them.
 constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
 
+// LDS element offset of (row r, k) in a slab: the 16-byte chunks of a row are permuted by
+// the row's group of 8 (chunk ^ (r / 8) % 8), so that the transposed stores, which write
+// rows 8 (or 4) apart, spread over the banks; the operand reads apply the same map.
+__device__ inline int slab_off(int r, int k) { return r * GLD + ((((k >> 3) ^ (r >> 3)) & 7) << 3) + (k & 7); }
+
 // four consecutive values of one row, as floats
 __device__ inline float4 row4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ inline float4 row4(const bf16_t* p) {
@@ -122,7 +127,7 @@ __device__ inline void store_slab(uint16_t* s, int tid, const uint2 (&v)[NV]) {
       r = (tid & 31) * 4 + (i & 3);
       k = (tid >> 5) * 4 + (i >> 2) * 32;
     }
-    *reinterpret_cast<uint2*>(s + r * GLD + k) = v[i];
+    *reinterpret_cast<uint2*>(s + slab_off(r, k)) = v[i];
   }
 }
 
@@ -164,8 +169,8 @@ __global__ __launch_bounds__(256) void tr_gemm_kernel(const TrGemm g, int splits
       bf16x8 af[4], bw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 64 + i * 16 + (lane & 15)) * GLD + ks * 32 + (lane >> 4) * 8);
-        bw[i] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + i * 16 + (lane & 15)) * GLD + ks * 32 + (lane >> 4) * 8);
+        af[i] = *reinterpret_cast<const bf16x8*>(sA + slab_off(wm * 64 + i * 16 + (lane & 15), ks * 32 + (lane >> 4) * 8));
+        bw[i] = *reinterpret_cast<const bf16x8*>(sB + slab_off(wn * 64 + i * 16 + (lane & 15), ks * 32 + (lane >> 4) * 8));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
