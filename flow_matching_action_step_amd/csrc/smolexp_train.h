@@ -59,6 +59,7 @@ struct TrainWs {
   float *RF, *V;
   float *dv, *dh, *dn, *dact, *dout, *dqkv, *dkv, *part;
   bf16_t *dh16, *dgu;       // bf16 copy of dh, and the SwiGLU gradient (matrix-product operands only)
+  bf16_t* dqkv16;           // the Q/K/V gradient after the rotation's transpose, bf16 (a product operand)
   float *split;             // k-split partial sums of the matrix products
   int *vidx, *nval;
 };

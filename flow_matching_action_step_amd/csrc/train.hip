@@ -284,13 +284,14 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
   if (lane == 0) rstd[row] = r;
 }
 
-// Backward of the RMSNorm above over 16 rows per workgroup:
+// Backward of the RMSNorm above over kRB rows per workgroup:
 //   dh = r (u - hat mean(u hat)) (+ resid), u = dy g, hat = h r;
 //   part[blk][c] = sum over the block's rows of dy hat (the gain's gradient, before the
-//   sum over blocks).  dh may alias resid; dh16 receives dh in bf16 (a product operand).  Phase 1: each wave forms mean(u hat) of 4 rows
-//   (4-wide loads); phase 2: thread t takes columns 4t .. 4t + 3 of all 16 rows (the second
+//   sum over blocks).  dh may alias resid; dh16 receives dh in bf16 (a product operand).
+//   Phase 1: each wave forms mean(u hat) of its rows (4-wide loads); phase 2: thread t
+//   takes columns 4t .. 4t + 3 of all kRB rows (the second
 //   read of dy and h comes from L2).
-constexpr int kRB = 16;
+constexpr int kRB = 8;
 __global__ __launch_bounds__(256) void tr_rmsnorm_bwd_kernel(const float* dy, const float* h, const float* rstd,
                                                              const bf16_t* g, const float* resid, float* dh,
                                                              bf16_t* dh16, int M, float* part) {
@@ -409,26 +410,33 @@ __global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, c
 }
 
 // RoPE (pairs d, d + 32) on the Q heads (and the self layers' K heads) of qkv rows, in place,
-// at position n_valid(b) + i.  dir = +1 rotates, -1 applies the transpose (the backward).
+// at position n_valid(b) + i.  dir = +1 rotates, -1 applies the transpose (the backward);
+// out16 non-NULL: the result goes there in bf16 instead of back into qkv.
 __global__ __launch_bounds__(256) void tr_rope_kernel(float* qkv, int ldq, int n_heads, const int* nval,
-                                                      const float2* rope, float dir) {
+                                                      const float2* rope, float dir, bf16_t* out16) {
   const int row = blockIdx.x, b = row / kChunk, i = row % kChunk;
   const float2* cs = rope + (size_t)(nval[b] + i) * (kHD / 2);
   for (int p = threadIdx.x; p < n_heads * (kHD / 2); p += 256) {
     const int hd = p / (kHD / 2), k = p % (kHD / 2);
     float* x = qkv + (size_t)row * ldq + hd * kHD;
     const float c = cs[k].x, s = dir * cs[k].y;
-    const float x1 = x[k], x2 = x[k + kHD / 2];
-    x[k] = x1 * c - x2 * s;
-    x[k + kHD / 2] = x1 * s + x2 * c;
+    const float x1 = x[k], x2 = x[k + kHD / 2], y1 = x1 * c - x2 * s, y2 = x1 * s + x2 * c;
+    if (out16) {  // the backward: the rotated gradient goes to its bf16 copy (a product operand)
+      bf16_t* y = out16 + (size_t)row * ldq + hd * kHD;
+      y[k] = (bf16_t)bf16_bits(y1);
+      y[k + kHD / 2] = (bf16_t)bf16_bits(y2);
+    } else {
+      x[k] = y1;
+      x[k + kHD / 2] = y2;
+    }
   }
 }
 
 // Self layers: the chunk keys' gradients, summed over the three query heads of each KV head
 // from the per-head parts dkv [B][15][2][50][64], into columns 960.. (K, rotated back) and
-// 1280.. (V) of dqkv.
+// 1280.. (V) of dqkv's bf16 copy.
 __global__ __launch_bounds__(256) void tr_kv_grad_kernel(const float* dkv, const int* nval, const float2* rope,
-                                                         float* dqkv) {
+                                                         bf16_t* dqkv) {
   const int row = blockIdx.x, b = row / kChunk, i = row % kChunk;
   const float2* cs = rope + (size_t)(nval[b] + i) * (kHD / 2);
   auto part = [&](int h, int kv, int d) {
@@ -443,15 +451,15 @@ __global__ __launch_bounds__(256) void tr_kv_grad_kernel(const float* dkv, const
       y2 += part(g * grp + u, 0, k + kHD / 2);
     }
     const float c = cs[k].x, s = cs[k].y;
-    float* x = dqkv + (size_t)row * kNQKV + kNQ + g * kHD;
-    x[k] = y1 * c + y2 * s;
-    x[k + kHD / 2] = -y1 * s + y2 * c;
+    bf16_t* x = dqkv + (size_t)row * kNQKV + kNQ + g * kHD;
+    x[k] = (bf16_t)bf16_bits(y1 * c + y2 * s);
+    x[k + kHD / 2] = (bf16_t)bf16_bits(-y1 * s + y2 * c);
   }
   for (int p = threadIdx.x; p < kNKV; p += 256) {
     const int g = p / kHD, d = p % kHD;
     float y = 0.f;
     for (int u = 0; u < grp; ++u) y += part(g * grp + u, 1, d);
-    dqkv[(size_t)row * kNQKV + kNQ + kNKV + p] = y;
+    dqkv[(size_t)row * kNQKV + kNQ + kNKV + p] = (bf16_t)bf16_bits(y);
   }
 }
 
@@ -920,6 +928,7 @@ size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
   w->dact = f(M * kFFN);
   w->dgu = hb(M * kGU);
   w->dh16 = hb(M * kD);
+  w->dqkv16 = hb(M * kNQKV);
   w->dout = f(M * kNQ);
   w->dqkv = f(M * kNQKV);
   w->dkv = f((size_t)B * kHQ * 2 * kChunk * kHD);
@@ -997,7 +1006,8 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, Hl(l), W + lo.norm1, t.rms_eps, M, n1, r1);
     TR_CHECK();
     if ((e = fwd(n1, true, kD, lo.qkv, nq, kD, qkv, kNQKV, nullptr, nullptr)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, qkv, kNQKV, self ? kHQ + kHKV : kHQ, w.nval, t.rope, 1.f);
+    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, qkv, kNQKV, self ? kHQ + kHKV : kHQ, w.nval, t.rope, 1.f,
+                       nullptr);
     TR_CHECK();
     TrAttn aa;
     aa.qkv = qkv; aa.ldq = kNQKV;
@@ -1065,15 +1075,15 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     if (self) hipLaunchKernelGGL(tr_attn_bwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
     else hipLaunchKernelGGL(tr_attn_bwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
     TR_CHECK();
-    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, w.dqkv, kNQKV, kHQ, w.nval, t.rope, -1.f);
+    hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, w.dqkv, kNQKV, kHQ, w.nval, t.rope, -1.f, w.dqkv16);
     TR_CHECK();
     if (self) {
-      hipLaunchKernelGGL(tr_kv_grad_kernel, dim3(M), dim3(256), 0, st, w.dkv, w.nval, t.rope, w.dqkv);
+      hipLaunchKernelGGL(tr_kv_grad_kernel, dim3(M), dim3(256), 0, st, w.dkv, w.nval, t.rope, w.dqkv16);
       TR_CHECK();
     }
-    if ((e = gemm(M, kD, nq, w.dqkv, kNQKV, true, false, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
+    if ((e = gemm(M, kD, nq, w.dqkv16, kNQKV, true, true, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
       return e;
-    if ((e = bwd_w(w.dqkv, false, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
+    if ((e = bwd_w(w.dqkv16, true, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
     if ((e = norm_bwd(w.dn, Hl(l), r1, lo.norm1, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(h_l)
   }
   // time MLP and action_in (dh = d h0)
