@@ -6,14 +6,17 @@
 // only the expert trains, so the prefix keys/values are frozen inputs.  The loss is the mean
 // over the batch's B x 50 x 32 elements.
 //
-// Data layout: every activation is fp32 row-major [rows][columns] with rows = query * 50 +
-// chunk row; the weights are the manifest's bf16 matrices as given ([out][in] row-major); the
-// gradients are fp32 in manifest order.  All matrix products run on one bf16 MFMA kernel
-// (fp32 accumulate) that reads either operand along or across its contraction axis, so the
-// forward (x W^T), the input gradient (dy W) and the weight gradient (dy^T x) need no
-// transposed copies.  Attention keeps its scores in LDS and recomputes them in the backward
-// pass from the saved log-sum-exp; the prefix keys of a query are read through a compacted
-// list of its valid positions, so pads are never touched.
+// Data layout: activations are row-major [rows][columns] with rows = query * 50 + chunk row,
+// fp32 where an elementwise step reads them (residual stream, norms, SwiGLU inputs,
+// attention output) and bf16 where only matrix products do (norm outputs, SwiGLU output,
+// the gradients that feed products: rounding them when written gives the bits the product
+// would form).  The weights are the manifest's bf16 matrices as given ([out][in] row-major);
+// the gradients are fp32 in manifest order.  All matrix products run on one bf16 MFMA
+// kernel (fp32 accumulate) that reads either operand along or across its contraction axis,
+// so the forward (x W^T), the input gradient (dy W) and the weight gradient (dy^T x) need
+// no transposed copies.  Attention recomputes its scores in the backward pass from the
+// saved log-sum-exp; the prefix keys of a query are read through a compacted list of its
+// valid positions, so pads are never touched.
 #include "smolexp_internal.h"
 #include "smolexp_train.h"
 
