@@ -279,11 +279,27 @@ __global__ __launch_bounds__(256) void tr_rmsnorm_kernel(const float* h, const b
                                                          float* rstd) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;
-  const float* hr = h + (size_t)row * kD;
+  constexpr int Q = kD / 4;  // 180 column quads; lane takes quads lane, lane + 64, lane + 128
+  const float4* hr = reinterpret_cast<const float4*>(h + (size_t)row * kD);
+  float4 x[3];
   float ss = 0.f;
-  for (int c = lane; c < kD; c += 64) ss += hr[c] * hr[c];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int c4 = lane + 64 * u;
+    x[u] = c4 < Q ? hr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += x[u].x * x[u].x + x[u].y * x[u].y + x[u].z * x[u].z + x[u].w * x[u].w;
+  }
   const float r = rsqrtf(wave_sum(ss) / kD + eps);
-  for (int c = lane; c < kD; c += 64) n[(size_t)row * kD + c] = (bf16_t)bf16_bits(hr[c] * r * bf16_val(g[c]));
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int c4 = lane + 64 * u;
+    if (c4 < Q) {
+      const uint2 gg = *reinterpret_cast<const uint2*>(g + 4 * c4);
+      *reinterpret_cast<uint2*>(n + (size_t)row * kD + 4 * c4) =
+          make_uint2(bf16_bits(x[u].x * r * bf16_val(gg.x & 0xFFFF)) | (bf16_bits(x[u].y * r * bf16_val(gg.x >> 16)) << 16),
+                     bf16_bits(x[u].z * r * bf16_val(gg.y & 0xFFFF)) | (bf16_bits(x[u].w * r * bf16_val(gg.y >> 16)) << 16));
+    }
+  }
   if (lane == 0) rstd[row] = r;
 }
 
@@ -396,19 +412,29 @@ __global__ __launch_bounds__(256) void tr_silu_bwd_kernel(const float* d, const 
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) out[i] = d[i] * silu_grad_f(s[i]);
 }
 
-// gu [M][4096] = [gate | up]; act = SiLU(gate) up.
+// gu [M][4096] = [gate | up]; act = SiLU(gate) up.  Four columns per thread.
 __global__ __launch_bounds__(256) void tr_swiglu_kernel(const float* gu, bf16_t* act, size_t n) {
-  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const size_t row = i / kFFN, c = i % kFFN;
-    act[i] = (bf16_t)bf16_bits(silu_f(gu[row * kGU + c]) * gu[row * kGU + kFFN + c]);
+  for (size_t q = blockIdx.x * 256 + threadIdx.x; q < n / 4; q += (size_t)gridDim.x * 256) {
+    const size_t row = q / (kFFN / 4), c = (q % (kFFN / 4)) * 4;
+    const float4 gt = *reinterpret_cast<const float4*>(gu + row * kGU + c);
+    const float4 up = *reinterpret_cast<const float4*>(gu + row * kGU + kFFN + c);
+    *reinterpret_cast<uint2*>(act + row * kFFN + c) =
+        make_uint2(bf16_bits(silu_f(gt.x) * up.x) | (bf16_bits(silu_f(gt.y) * up.y) << 16),
+                   bf16_bits(silu_f(gt.z) * up.z) | (bf16_bits(silu_f(gt.w) * up.w) << 16));
   }
 }
 __global__ __launch_bounds__(256) void tr_swiglu_bwd_kernel(const float* dact, const float* gu, bf16_t* dgu, size_t n) {
-  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const size_t row = i / kFFN, c = i % kFFN;
-    const float gt = gu[row * kGU + c], up = gu[row * kGU + kFFN + c], d = dact[i];
-    dgu[row * kGU + c] = (bf16_t)bf16_bits(d * up * silu_grad_f(gt));
-    dgu[row * kGU + kFFN + c] = (bf16_t)bf16_bits(d * silu_f(gt));
+  for (size_t q = blockIdx.x * 256 + threadIdx.x; q < n / 4; q += (size_t)gridDim.x * 256) {
+    const size_t row = q / (kFFN / 4), c = (q % (kFFN / 4)) * 4;
+    const float4 gt = *reinterpret_cast<const float4*>(gu + row * kGU + c);
+    const float4 up = *reinterpret_cast<const float4*>(gu + row * kGU + kFFN + c);
+    const float4 d = *reinterpret_cast<const float4*>(dact + row * kFFN + c);
+    *reinterpret_cast<uint2*>(dgu + row * kGU + c) =
+        make_uint2(bf16_bits(d.x * up.x * silu_grad_f(gt.x)) | (bf16_bits(d.y * up.y * silu_grad_f(gt.y)) << 16),
+                   bf16_bits(d.z * up.z * silu_grad_f(gt.z)) | (bf16_bits(d.w * up.w * silu_grad_f(gt.w)) << 16));
+    *reinterpret_cast<uint2*>(dgu + row * kGU + kFFN + c) =
+        make_uint2(bf16_bits(d.x * silu_f(gt.x)) | (bf16_bits(d.y * silu_f(gt.y)) << 16),
+                   bf16_bits(d.z * silu_f(gt.z)) | (bf16_bits(d.w * silu_f(gt.w)) << 16));
   }
 }
 
@@ -523,17 +549,25 @@ __device__ inline void load_block(const TrAttn& a, int b, int g, int nb, int kb,
   uint32_t kk[16], vv[16];
   if (kidx < nb) {
     const size_t o = (((size_t)b * kHKV + g) * a.P + a.vidx[(size_t)b * a.P + kidx]) * kHD + d0;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(a.pk + o), k1 = *reinterpret_cast<const uint4*>(a.pk + o + 8);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(a.pv + o), v1 = *reinterpret_cast<const uint4*>(a.pv + o + 8);
+    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      kk[u] = a.pk[o + u];
-      vv[u] = a.pv[o + u];
+    for (int u = 0; u < 8; ++u) {
+      kk[2 * u] = kw[u] & 0xFFFF;
+      kk[2 * u + 1] = kw[u] >> 16;
+      vv[2 * u] = vw[u] & 0xFFFF;
+      vv[2 * u + 1] = vw[u] >> 16;
     }
   } else if (SELF && kidx < nb + kChunk) {
     const float* src = a.qkv + (size_t)(b * kChunk + kidx - nb) * a.ldq;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      kk[u] = bf16_bits(src[kNQ + g * kHD + d0 + u]);
-      vv[u] = bf16_bits(src[kNQ + kNKV + g * kHD + d0 + u]);
+    for (int u = 0; u < 16; u += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + kNQ + g * kHD + d0 + u);
+      const float4 y = *reinterpret_cast<const float4*>(src + kNQ + kNKV + g * kHD + d0 + u);
+      kk[u] = bf16_bits(x.x); kk[u + 1] = bf16_bits(x.y); kk[u + 2] = bf16_bits(x.z); kk[u + 3] = bf16_bits(x.w);
+      vv[u] = bf16_bits(y.x); vv[u + 1] = bf16_bits(y.y); vv[u + 2] = bf16_bits(y.z); vv[u + 3] = bf16_bits(y.w);
     }
   } else {
 #pragma unroll
@@ -1026,7 +1060,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     hipLaunchKernelGGL(tr_rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, hm, W + lo.norm2, t.rms_eps, M, n2, r2);
     TR_CHECK();
     if ((e = fwd(n2, true, kD, lo.gu, kGU, kD, gu, kGU, nullptr, nullptr)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_swiglu_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, gu, act, (size_t)M * kFFN);
+    hipLaunchKernelGGL(tr_swiglu_kernel, dim3(ew_grid((size_t)M * kFFN / 4)), dim3(256), 0, st, gu, act, (size_t)M * kFFN);
     TR_CHECK();
     if ((e = fwd(act, true, kFFN, lo.down, kD, kFFN, Hl(l + 1), kD, hm, nullptr)) != hipSuccess) return e;
   }
@@ -1059,7 +1093,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     // MLP
     if ((e = bwd_x(w.dh16, true, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
     if ((e = bwd_w(w.dh16, true, kD, kD, act, true, kFFN, lo.down)) != hipSuccess) return e;
-    hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN)), dim3(256), 0, st, w.dact, gu, w.dgu,
+    hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN / 4)), dim3(256), 0, st, w.dact, gu, w.dgu,
                        (size_t)M * kFFN);
     TR_CHECK();
     if ((e = bwd_x(w.dgu, true, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
