@@ -55,9 +55,11 @@ __device__ inline uint2 load4(const bf16_t* p) { return *reinterpret_cast<const 
 constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
 
 // LDS element offset of (row r, k) in a slab: the 16-byte chunks of a row are permuted by
-// the row's group of 8 (chunk ^ (r / 8) % 8), so that the transposed stores, which write
-// rows 8 (or 4) apart, spread over the banks; the operand reads apply the same map.
-__device__ inline int slab_off(int r, int k) { return r * GLD + ((((k >> 3) ^ (r >> 3)) & 7) << 3) + (k & 7); }
+// the row's group of 16 (chunk ^ (r / 16) % 8).  The transposed stores write rows 8 apart,
+// which with the 144-byte row stride land on only two bank groups unpermuted; with the
+// permutation the 16 rows of one store spread over all 64 banks.  The operand reads take
+// 16 consecutive rows, one permutation, so they keep the stride's conflict-free pattern.
+__device__ inline int slab_off(int r, int k) { return r * GLD + ((((k >> 3) ^ (r >> 4)) & 7) << 3) + (k & 7); }
 
 // four consecutive values of one row, as floats
 __device__ inline float4 row4(const float* p) { return *reinterpret_cast<const float4*>(p); }
