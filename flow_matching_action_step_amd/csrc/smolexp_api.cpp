@@ -463,12 +463,10 @@ void drop_graphs(smolexp_t h) {
   h->graphs.clear();
 }
 
-int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
-  const CallKey key = key_of(c);
-  h->last = key;
-  h->have_last = true;
-  if (!h->cfg.use_graphs) return enqueue(h, c, s, true);
-
+// Replays the cached graph of `key`, or captures enq's launches into a new one (least
+// recently used evicted beyond kGraphCache) and launches it on s.
+template <class Enq>
+int run_cached(smolexp_t h, const CallKey& key, hipStream_t s, Enq enq) {
   for (auto& g : h->graphs) {
     if (same_key(g.key, key)) {
       g.last_use = ++h->tick;
@@ -479,7 +477,7 @@ int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
   }
   hipError_t e = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return hip_fail(h, e, "hipStreamBeginCapture");
-  const int rc = enqueue(h, c, h->cap, true);
+  const int rc = enq(h->cap);
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(h->cap, &graph);
   if (rc != SMOLEXP_OK) {
@@ -504,6 +502,14 @@ int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
   e = hipGraphLaunch(exec, s);
   if (e != hipSuccess) return hip_fail(h, e, "hipGraphLaunch");
   return SMOLEXP_OK;
+}
+
+int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
+  const CallKey key = key_of(c);
+  h->last = key;
+  h->have_last = true;
+  if (!h->cfg.use_graphs) return enqueue(h, c, s, true);
+  return run_cached(h, key, s, [&](hipStream_t cs) { return enqueue(h, c, cs, true); });
 }
 
 int check_call(smolexp_t h, const void* kv, const uint8_t* mask, int P, const float* x_in, float* out, int B) {
@@ -1010,6 +1016,7 @@ int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
     const int nb = batch > h->tr_B ? batch : h->tr_B, np = prefix_len > h->tr_P ? prefix_len : h->tr_P;
     if (h->trmem) {
       (void)hipDeviceSynchronize();
+      drop_graphs(h);
       (void)hipFree(h->trmem);
       h->trmem = nullptr;
       h->tr_B = h->tr_P = 0;
@@ -1029,9 +1036,21 @@ int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
   // the workspace is carved for this call's batch and prefix length (it holds at least that)
   train_carve(static_cast<char*>(h->trmem), batch, prefix_len, L, &ta.ws);
   ta.split_cap = train_split_cap(batch);
-  const hipError_t e = train_enqueue(ta, static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return hip_fail(h, e, "training step launch");
-  return SMOLEXP_OK;
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  auto enq = [&](hipStream_t cs) -> int {
+    const hipError_t e = train_enqueue(ta, cs);
+    return e == hipSuccess ? SMOLEXP_OK : hip_fail(h, e, "training step launch");
+  };
+  if (!h->cfg.use_graphs) return enq(st);
+  // one graph per call signature, as for the denoiser (velocity_mode 2 marks a training step;
+  // the graphs hold the workspace's addresses, so growing it drops them)
+  CallKey key;
+  memset(&key, 0, sizeof(key));
+  key.velocity_mode = 2;
+  key.B = batch; key.P = prefix_len;
+  key.kv = prefix_kv; key.mask = prefix_mask; key.x_in = noise; key.prev = actions;
+  key.out = out_grads; key.vel = out_loss; key.st = const_cast<float*>(t);
+  return run_cached(h, key, st, enq);
 }
 
 int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,

@@ -235,8 +235,10 @@ int smolexp_prefill(smolexp_t h, const void* prefix_emb, const uint8_t* prefix_m
  * feed products are kept in bf16, as the products read them.
  * Deterministic (no atomics).  The library keeps a workspace of about 41 KB per
  * chunk row per layer (the activations) for the largest batch x prefix_len
- * seen; a call that needs more grows it first, which synchronizes the device.
- * Asynchronous on hip_stream otherwise.  SMOLEXP_E_STATE before
+ * seen; a call that needs more grows it first, which synchronizes the device
+ * and drops the handle's cached graphs.  With use_graphs the launch sequence is
+ * captured once per call signature (pointers, batch, prefix_len) and replayed,
+ * as for smolexp_denoise.  Asynchronous on hip_stream otherwise.  SMOLEXP_E_STATE before
  * smolexp_load_weights; SMOLEXP_E_INVAL for NULL pointers or batch /
  * prefix_len out of range.
  */

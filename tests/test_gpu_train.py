@@ -229,3 +229,46 @@ def test_train_step_full_size_b64_p257():
         assert worst <= 2 * G_RTOL
     finally:
         tr.close()
+
+
+def test_train_step_graph_replays_match_eager():
+    """With graphs on (the default) a training step is captured once per call signature and
+    replayed; every replay, with other device work in between, must equal the eager launches
+    bit for bit."""
+    _say("train step: graph replays vs eager launches")
+    L, B, P = 2, 3, 48
+    named = synth.draw_weights(L, gain_seed=synth.gen.SEED_GAINS)
+    hs = []
+    try:
+        for graphs in (1, 0):
+            cfg = fm.smolexp_default_config(n_layers=L, max_batch=B, max_prefix=P, use_graphs=graphs)
+            h = fm.smolexp_create(cfg, 0)
+            hs.append((h, cfg))
+            fm.smolexp_load_weights(h, synth.pack_weights(named, L))
+        kv = synth.draw_prefix_kv(L, B, P)
+        mask = synth.make_mask(B, P, [48, 30, 7])
+        d = [torch.from_numpy(np.ascontiguousarray(x)).cuda()
+             for x in (kv.view(np.int16), mask, synth.draw_actions(B), synth.draw_noise(B), synth.draw_flow_times(B))]
+        n = fm.smolexp_weight_count(hs[0][1])
+        ge, le = torch.empty(n, device="cuda"), torch.empty(1, device="cuda")
+        fm.smolexp_train_step(hs[1][0], hs[1][1], *d, ge, le)
+        torch.cuda.synchronize()
+        want_g, want_l = ge.cpu().numpy(), le.cpu().numpy()
+        for rep in range(3):
+            gg, lg = torch.full((n,), float("nan"), device="cuda"), torch.full((1,), float("nan"), device="cuda")
+            fm.smolexp_train_step(hs[0][0], hs[0][1], *d, gg, lg)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(gg.cpu().numpy(), want_g, err_msg=f"replay {rep}")
+            np.testing.assert_array_equal(lg.cpu().numpy(), want_l)
+            # eager work between replays (another step on the eager handle, a torch reduction)
+            fm.smolexp_train_step(hs[1][0], hs[1][1], *d, ge, le)
+            _ = float((ge * 2).sum())
+            torch.cuda.synchronize()
+            # copies of the inputs at other addresses: a second graph, the same results
+            d2 = [x.clone() for x in d]
+            fm.smolexp_train_step(hs[0][0], hs[0][1], *d2, gg, lg)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(gg.cpu().numpy(), want_g)
+    finally:
+        for h, _ in hs:
+            fm.smolexp_destroy(h)
