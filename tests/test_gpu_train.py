@@ -186,8 +186,9 @@ def test_train_step_deterministic_inputs_untouched_and_errors():
 
 
 def test_train_step_full_size_b64_p257():
-    """The benchmarked configuration (16 layers, 64 samples, prefix 257): the loss against the
-    oracle's forward pass for every sample, and the batch's gradients against the mean of the
+    """The benchmarked configuration (16 layers, 64 samples, prefix 257): the loss and the
+    gradient of action_out.b (2 / n times the column sums of v - target) against the oracle's
+    forward pass for every sample, and the batch's gradients against the mean of the
     gradients of its two halves (the loss is a per-element mean, so that identity holds
     exactly in exact arithmetic; it exercises the full-size k-split and workspace).
 
@@ -215,16 +216,23 @@ def test_train_step_full_size_b64_p257():
         got, want = _unpack(flat, L), _unpack(g_half, L)
         worst = max(np.linalg.norm(got[n] - want[n]) / np.linalg.norm(want[n]) for n in got)
         # the oracle's loss: each sample's velocity from the float64 forward pass
-        se = 0.0
+        se, err_sum = 0.0, np.zeros(32)
         for b in range(B):
             pk, pv = oracle.bf16_bits_to_float(kv[:, 0, b]), oracle.bf16_bits_to_float(kv[:, 1, b])
             x = float(t[b]) * eps[b].astype(np.float64) + (1 - float(t[b])) * a[b].astype(np.float64)
             v = oracle.velocity(tr.W, tr.ocfg, x, float(t[b]), pk, pv, mask[b].astype(bool))
-            se += float(np.sum((v - (eps[b].astype(np.float64) - a[b])) ** 2))
-        ol = se / (B * 50 * 32)
+            err = v - (eps[b].astype(np.float64) - a[b])
+            se += float(np.sum(err ** 2))
+            err_sum += err.sum(axis=0)
+        n = B * 50 * 32
+        ol = se / n
+        # d loss / d b_out = 2 / n times the column sums of (v - target): exact from the forward
+        gb = 2.0 * err_sum / n
+        rel_b = np.linalg.norm(got["action_out.b"] - gb) / np.linalg.norm(gb)
         print(f"[parity] train16 b64 p257: loss {loss:.6f} vs oracle {ol:.6f} (rel {abs(loss - ol) / ol:.1e}); "
-              f"halves: loss {l_half:.6f}, worst gradient rel {worst:.2e}", flush=True)
+              f"action_out.b rel {rel_b:.2e}; halves: loss {l_half:.6f}, worst gradient rel {worst:.2e}", flush=True)
         assert abs(loss - ol) <= LOSS_RTOL * ol
+        assert rel_b <= G_RTOL
         assert abs(loss - l_half) <= 1e-5 * ol
         assert worst <= 2 * G_RTOL
     finally:
