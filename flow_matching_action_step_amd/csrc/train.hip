@@ -61,12 +61,8 @@ constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
 // 16 consecutive rows, one permutation, so they keep the stride's conflict-free pattern.
 __device__ inline int slab_off(int r, int k) { return r * GLD + ((((k >> 3) ^ (r >> 4)) & 7) << 3) + (k & 7); }
 
-// four consecutive values of one row, as floats
+// four consecutive fp32 values of one row
 __device__ inline float4 row4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ inline float4 row4(const bf16_t* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return make_float4(bf16_val(u.x & 0xFFFF), bf16_val(u.x >> 16), bf16_val(u.y & 0xFFFF), bf16_val(u.y >> 16));
-}
 
 // One operand's share of a slab, as NV x 4 bf16 per thread.  Stored along k (KC): 4-wide
 // vectors of one row.  Stored across k: 4 x 4 blocks (4 k-rows of 4 consecutive operand
@@ -268,11 +264,6 @@ __global__ __launch_bounds__(256) void tr_input_kernel(const float* act, const f
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 
