@@ -127,6 +127,8 @@ struct smolexp_handle {
   float* bias32 = nullptr;
   void* trmem = nullptr;
   int tr_B = 0, tr_P = 0;
+  hipStream_t tr_side = nullptr;     // the training step's second stream (default priority)
+  std::vector<hipEvent_t> tr_ev;     // its fork/join events
   TrainWs tws{};
 };
 
@@ -1026,8 +1028,19 @@ int smolexp_train_step(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
     h->tr_B = nb;
     h->tr_P = np;
   }
+  if (!h->tr_side) {
+    if (hipStreamCreateWithFlags(&h->tr_side, hipStreamNonBlocking) != hipSuccess)
+      return fail(h, SMOLEXP_E_HIP, "training side stream creation failed");
+    h->tr_ev.assign(8 * kMaxLayers, nullptr);
+    for (auto& ev : h->tr_ev)
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return fail(h, SMOLEXP_E_HIP, "training event creation failed");
+  }
   TrainArgs ta;
   memset(&ta, 0, sizeof(ta));
+  ta.side = h->tr_side;
+  ta.ev = h->tr_ev.data();
+  ta.n_ev = (int)h->tr_ev.size();
   ta.B = batch; ta.P = prefix_len; ta.L = L;
   ta.kv = static_cast<const bf16_t*>(prefix_kv); ta.mask = prefix_mask;
   ta.actions = actions; ta.noise = noise; ta.t = t; ta.grads = out_grads; ta.loss = out_loss;
@@ -1202,6 +1215,9 @@ void smolexp_destroy(smolexp_t h) {
   if (h->lmem) (void)hipFree(h->lmem);
   if (h->pfmem) (void)hipFree(h->pfmem);
   if (h->trmem) (void)hipFree(h->trmem);
+  for (auto ev : h->tr_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  if (h->tr_side) (void)hipStreamDestroy(h->tr_side);
   if (h->wraw) (void)hipFree(h->wraw);
   if (h->bias32) (void)hipFree(h->bias32);
   delete h;

@@ -61,6 +61,7 @@ struct TrainWs {
   bf16_t *dh16, *dgu;       // bf16 copy of dh, and the SwiGLU gradient (matrix-product operands only)
   bf16_t* dqkv16;           // the Q/K/V gradient after the rotation's transpose, bf16 (a product operand)
   float *split;             // k-split partial sums of the matrix products
+  float *split2;            // the same for the products on the side stream
   int *vidx, *nval;
 };
 size_t train_workspace_bytes(int B, int P, int L);
@@ -81,7 +82,10 @@ struct TrainArgs {
   const float2* rope;      // [pos][32] (cos, sin)
   const double* inv_period;  // [360]
   float rms_eps;
-  size_t split_cap;        // floats of ws.split (the workspace's batch)
+  size_t split_cap;        // floats of ws.split and ws.split2 (the workspace's batch)
+  hipStream_t side;        // second stream for the layers' weight gradients (default priority)
+  hipEvent_t* ev;          // events for its forks and joins, n_ev of them (4 pairs per layer)
+  int n_ev;
   TrainWs ws;
 };
 hipError_t train_enqueue(const TrainArgs& t, hipStream_t s);

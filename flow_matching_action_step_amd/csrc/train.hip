@@ -964,6 +964,7 @@ size_t train_carve(char* base, int B, int P, int L, TrainWs* w) {
   w->dkv = f((size_t)B * kHQ * 2 * kChunk * kHD);
   w->part = f(nblk * kGU + M);
   w->split = f(train_split_cap(B));
+  w->split2 = f(train_split_cap(B));  // the side stream's
   w->vidx = (int*)f((size_t)B * P);
   w->nval = (int*)f(B);
   return off;
@@ -978,12 +979,16 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   train_offsets(L, 0, &off);
   hipError_t e;
 #define TR_CHECK() do { if ((e = hipGetLastError()) != hipSuccess) return e; } while (0)
-  auto gemm = [&](int m, int n, int k, const void* A, int lda, bool ak, bool abf, const void* Bp, int ldb, bool bk,
-                  bool bbf, float* C, int ldc, const float* cin, const float* bias) {
+  auto gemm_on = [&](hipStream_t gs, float* scratch, int m, int n, int k, const void* A, int lda, bool ak, bool abf,
+                     const void* Bp, int ldb, bool bk, bool bbf, float* C, int ldc, const float* cin, const float* bias) {
     TrGemm g;
     g.M = m; g.N = n; g.K = k; g.A = A; g.lda = lda; g.B = Bp; g.ldb = ldb; g.C = C; g.ldc = ldc;
-    g.Cin = cin; g.bias = bias; g.alpha = 1.f; g.part = w.split; g.part_cap = t.split_cap;
-    return launch_tr_gemm(g, ak, abf, bk, bbf, st);
+    g.Cin = cin; g.bias = bias; g.alpha = 1.f; g.part = scratch; g.part_cap = t.split_cap;
+    return launch_tr_gemm(g, ak, abf, bk, bbf, gs);
+  };
+  auto gemm = [&](int m, int n, int k, const void* A, int lda, bool ak, bool abf, const void* Bp, int ldb, bool bk,
+                  bool bbf, float* C, int ldc, const float* cin, const float* bias) {
+    return gemm_on(st, w.split, m, n, k, A, lda, ak, abf, Bp, ldb, bk, bbf, C, ldc, cin, bias);
   };
   // y W^T (+ cin) (+ bias): activations (fp32, or the bf16 the product reads) along k, weights bf16 [out][in]
   auto fwd = [&](const void* x, bool xbf, int ldx, size_t woff, int n, int k, float* y, int ldy, const float* cin,
@@ -995,6 +1000,31 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   // dW [n_out][k_in] = dy^T x over the M rows (dy's rows ldy wide; dy and x fp32 or bf16)
   auto bwd_w = [&](const void* dy, bool dybf, int ldy, int n_out, const void* x, bool xbf, int k_in, size_t goff) {
     return gemm(n_out, k_in, M, dy, ldy, false, dybf, x, k_in, false, xbf, G + goff, k_in, nullptr, nullptr);
+  };
+  // The layers' weight gradients only feed the output: they run on the side stream, forked
+  // after their operands are written and joined before the main stream overwrites them.
+  int nev = 0;
+  auto fork = [&]() -> hipError_t {
+    if (nev >= t.n_ev) return hipErrorInvalidValue;
+    hipEvent_t ev = t.ev[nev++];
+    hipError_t r = hipEventRecord(ev, st);
+    return r == hipSuccess ? hipStreamWaitEvent(t.side, ev, 0) : r;
+  };
+  auto side_w = [&](const void* dy, int ldy, int n_out, const void* x, int k_in, size_t goff, hipEvent_t* done) -> hipError_t {
+    hipError_t r = fork();
+    if (r != hipSuccess) return r;
+    r = gemm_on(t.side, w.split2, n_out, k_in, M, dy, ldy, false, true, x, k_in, false, true, G + goff, k_in, nullptr,
+                nullptr);
+    if (r != hipSuccess) return r;
+    if (nev >= t.n_ev) return hipErrorInvalidValue;
+    *done = t.ev[nev++];
+    return hipEventRecord(*done, t.side);
+  };
+  auto join = [&](hipEvent_t& ev) -> hipError_t {
+    if (!ev) return hipSuccess;
+    hipError_t r = hipStreamWaitEvent(st, ev, 0);
+    ev = nullptr;
+    return r;
   };
   auto colsum = [&](const float* x, int n, float* out) -> hipError_t {
     hipLaunchKernelGGL(tr_colsum_kernel, dim3((n + 255) / 256, nblk), dim3(256), 0, st, x, M, n, w.part);
@@ -1074,6 +1104,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
   if ((e = colsum(w.dv, kAD, G + off.aout_b)) != hipSuccess) return e;
   if ((e = bwd_x(w.dv, false, kAD, off.aout_w, kD, kD, w.dn)) != hipSuccess) return e;
   if ((e = norm_bwd(w.dn, Hl(L), w.RF, off.fnorm, nullptr, w.dh)) != hipSuccess) return e;
+  hipEvent_t j_down = nullptr, j_gu = nullptr, j_o = nullptr, j_qkv = nullptr;  // side-stream work in flight
   for (int l = L - 1; l >= 0; --l) {
     TrOffsets ol;
     train_offsets(L, l, &ol);
@@ -1085,16 +1116,18 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     bf16_t *n1 = lay16(w.N1, l, kD), *n2 = lay16(w.N2, l, kD), *act = lay16(w.ACT, l, kFFN), *o16 = lay16(w.O16, l, kNQ);
     // MLP
     if ((e = bwd_x(w.dh16, true, kD, lo.down, kFFN, kFFN, w.dact)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh16, true, kD, kD, act, true, kFFN, lo.down)) != hipSuccess) return e;
+    if ((e = side_w(w.dh16, kD, kD, act, kFFN, lo.down, &j_down)) != hipSuccess) return e;
+    if ((e = join(j_gu)) != hipSuccess) return e;  // the previous layer's gate/up gradient read dgu
     hipLaunchKernelGGL(tr_swiglu_bwd_kernel, dim3(ew_grid((size_t)M * kFFN / 4)), dim3(256), 0, st, w.dact, gu, w.dgu,
                        (size_t)M * kFFN);
     TR_CHECK();
     if ((e = bwd_x(w.dgu, true, kGU, lo.gu, kD, kD, w.dn)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dgu, true, kGU, kGU, n2, true, kD, lo.gu)) != hipSuccess) return e;
+    if ((e = side_w(w.dgu, kGU, kGU, n2, kD, lo.gu, &j_gu)) != hipSuccess) return e;
+    if ((e = join(j_down)) != hipSuccess) return e;  // dh16 is about to change
     if ((e = norm_bwd(w.dn, hm, r2, lo.norm2, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(hm)
     // attention
     if ((e = bwd_x(w.dh16, true, kD, lo.o, kNQ, kNQ, w.dout)) != hipSuccess) return e;
-    if ((e = bwd_w(w.dh16, true, kD, kD, o16, true, kNQ, lo.o)) != hipSuccess) return e;
+    if ((e = side_w(w.dh16, kD, kD, o16, kNQ, lo.o, &j_o)) != hipSuccess) return e;
     TrAttn aa;
     aa.qkv = qkv; aa.ldq = kNQKV;
     aa.pk = t.kv + (size_t)l * 2 * B * kHKV * t.P * kHD;
@@ -1105,6 +1138,7 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     if (self) hipLaunchKernelGGL(tr_attn_bwd_kernel<true>, dim3(kHQ, B), dim3(256), 0, st, aa);
     else hipLaunchKernelGGL(tr_attn_bwd_kernel<false>, dim3(kHQ, B), dim3(256), 0, st, aa);
     TR_CHECK();
+    if ((e = join(j_qkv)) != hipSuccess) return e;  // the previous layer's Q/K/V gradient read dqkv16
     hipLaunchKernelGGL(tr_rope_kernel, dim3(M), dim3(256), 0, st, w.dqkv, kNQKV, kHQ, w.nval, t.rope, -1.f, w.dqkv16);
     TR_CHECK();
     if (self) {
@@ -1113,9 +1147,13 @@ hipError_t train_enqueue(const TrainArgs& t, hipStream_t st) {
     }
     if ((e = gemm(M, kD, nq, w.dqkv16, kNQKV, true, true, W + lo.qkv, kD, false, true, w.dn, kD, nullptr, nullptr)) != hipSuccess)
       return e;
-    if ((e = bwd_w(w.dqkv16, true, kNQKV, nq, n1, true, kD, lo.qkv)) != hipSuccess) return e;
+    if ((e = side_w(w.dqkv16, kNQKV, nq, n1, kD, lo.qkv, &j_qkv)) != hipSuccess) return e;
+    if ((e = join(j_o)) != hipSuccess) return e;  // dh16 is about to change
     if ((e = norm_bwd(w.dn, Hl(l), r1, lo.norm1, w.dh, w.dh)) != hipSuccess) return e;  // dh <- d(h_l)
   }
+  // everything on the side stream has finished before the step ends
+  if ((e = join(j_gu)) != hipSuccess) return e;
+  if ((e = join(j_qkv)) != hipSuccess) return e;
   // time MLP and action_in (dh = d h0)
   if ((e = bwd_w(w.dh16, true, kD, kD, w.sil, true, kD, off.tout_w)) != hipSuccess) return e;
   if ((e = colsum(w.dh, kD, G + off.tout_b)) != hipSuccess) return e;
