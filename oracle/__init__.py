@@ -41,6 +41,12 @@ Pins (what fixes each function other than itself; all in tests/):
   attention ....... float64 triple-loop brute force on tiny shapes; one valid
                     key returns that V row; equal keys give the mean of V;
                     torch scaled_dot_product_attention with GQA and a mask
+  embed ........... closed forms with degenerate weights: the time path alone
+                    (time_in = [0 | I]) and the action path alone (time_in =
+                    [I | 0], a selector action_in), and the action path pushed
+                    through identity layers and the head; copies of embed with
+                    a planted mistake (swapped concatenation, SiLU after
+                    time_out, a dropped b_in or b_t1) fail them
   expert layer .... composition of torch library routines (rms_norm, linear,
                     scaled_dot_product_attention(enable_gqa), silu) with a
                     complex-number rotary embedding

@@ -2,13 +2,13 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-noeira docs "SmolVLA", Architecture: the expert denoises the action chunk
-starting from Gaussian noise at t = 1, each of the Euler steps predicts a
-velocity and moves toward t = 0; the flow-matching path is
-x_t = t * eps + (1 - t) * a, whose velocity target is eps - a.
-"Paper vs hardware 11: SmolVLA", What I ran: at a chunk boundary the first
-d ~ 7 rows of the new chunk are overwritten from the previous chunk
-(gradient-free prefix overwrite).
+Sources: noeira docs "SmolVLA", Architecture (the chunk is integrated from
+pure noise at flow time 1 down to flow time 0 by explicit Euler, one velocity
+evaluation of the expert per step; training pairs noise eps with an action
+chunk a on the straight line x_t = t * eps + (1 - t) * a, so the velocity to
+learn is the constant eps - a).  "Paper vs hardware 11: SmolVLA", What I ran
+(when a new chunk starts, its first d ~ 7 rows are pinned to the previous
+chunk's tail without any gradient step: the prefix overwrite).
 """
 import numpy as np
 

@@ -436,3 +436,151 @@ def test_overwrite_closed_form_and_fixed_point():
     x_plain = oracle.euler_denoise(field, eps, 10)
     np.testing.assert_allclose(x_ow, x_plain, atol=1e-6)
     np.testing.assert_allclose(x_ow, a, atol=1e-6)
+
+
+# ---------------------------------------------------------------- action and time embedding (embed)
+#
+# What fixes embed (BASELINE's reduced-expert configuration and noeira docs "SmolVLA",
+# Architecture, action-head row): action_in 32 -> 720, the sinusoidal time embedding
+# concatenated after the action embedding, a 1440 -> 720 projection with SiLU, then
+# 720 -> 720.  Degenerate weights reduce embed to closed forms that depend on each of
+# those choices: which half of time_in reads the time embedding, where the SiLU sits,
+# and every one of the three biases it adds before the layers.
+
+def _silu_closed(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _embed_weights(rng, time_path):
+    """Weights for embed's closed forms.  time_path: time_in = [0 | I] (only the time
+    embedding reaches the hidden layer), time_out = c I, random b_t1 and b_t2.  Otherwise:
+    action_in a per-row-scaled selector of the 32 action dims with a random bias,
+    time_in = [I | 0], time_out = c I, no b_t1 / b_t2 (c = 1.75 in both: a SiLU placed
+    after time_out would see c z instead of z)."""
+    D, A = 720, 32
+    W = {}
+    if time_path:
+        W["action_in.w"] = np.zeros((D, A))
+        W["action_in.b"] = np.zeros(D)
+        W["time_in.w"] = np.concatenate([np.zeros((D, D)), np.eye(D)], axis=1)
+        W["time_in.b"] = rng.standard_normal(D) * 0.5
+        W["time_out.w"] = 1.75 * np.eye(D)
+        W["time_out.b"] = rng.standard_normal(D) * 0.5
+    else:
+        sel = np.zeros((D, A))
+        scale = 0.5 + np.arange(D) / D
+        sel[np.arange(D), np.arange(D) % A] = scale
+        W["action_in.w"] = sel
+        W["action_in.b"] = rng.standard_normal(D) * 0.5
+        W["time_in.w"] = np.concatenate([np.eye(D), np.zeros((D, D))], axis=1)
+        W["time_in.b"] = np.zeros(D)
+        W["time_out.w"] = 1.75 * np.eye(D)
+        W["time_out.b"] = np.zeros(D)
+    return W
+
+
+def _embed_closed_form(W, cfg, x, t, time_path):
+    if time_path:
+        e = oracle.time_embedding(t, cfg.d_model, cfg.t_min_period, cfg.t_max_period)
+        row = 1.75 * _silu_closed(e + W["time_in.b"]) + W["time_out.b"]
+        return np.broadcast_to(row, (x.shape[0], cfg.d_model))
+    D = cfg.d_model
+    cols = np.arange(D) % 32
+    scale = 0.5 + np.arange(D) / D
+    return 1.75 * _silu_closed(x[:, cols] * scale + W["action_in.b"])
+
+
+def _embed_pin_failures(embed_fn):
+    """Names of the closed forms that embed_fn violates (empty: all hold)."""
+    cfg = ExpertConfig(n_layers=1)
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((50, 32))
+    bad = []
+    for time_path in (True, False):
+        W = _embed_weights(rng, time_path)
+        for t in (1.0, 0.37, 0.1):
+            got = embed_fn(W, cfg, x, t)
+            want = _embed_closed_form(W, cfg, x, t, time_path)
+            if not np.allclose(got, want, rtol=1e-12, atol=1e-13):
+                bad.append(("time" if time_path else "action", t))
+    return bad
+
+
+# Plausible mistakes in embed, each planted in a copy of it on the CPU.
+def _embed_swapped_concat(W, cfg, x, t, act_round=None):
+    y = x @ W["action_in.w"].T + W["action_in.b"]
+    e = oracle.time_embedding(t, cfg.d_model, cfg.t_min_period, cfg.t_max_period)
+    z = np.concatenate([np.broadcast_to(e, (x.shape[0], e.shape[0])), y], axis=1)
+    return oracle.silu(z @ W["time_in.w"].T + W["time_in.b"]) @ W["time_out.w"].T + W["time_out.b"]
+
+
+def _embed_silu_after_time_out(W, cfg, x, t, act_round=None):
+    y = x @ W["action_in.w"].T + W["action_in.b"]
+    e = oracle.time_embedding(t, cfg.d_model, cfg.t_min_period, cfg.t_max_period)
+    z = np.concatenate([y, np.broadcast_to(e, (x.shape[0], e.shape[0]))], axis=1)
+    return oracle.silu((z @ W["time_in.w"].T + W["time_in.b"]) @ W["time_out.w"].T + W["time_out.b"])
+
+
+def _embed_no_action_bias(W, cfg, x, t, act_round=None):
+    y = x @ W["action_in.w"].T
+    e = oracle.time_embedding(t, cfg.d_model, cfg.t_min_period, cfg.t_max_period)
+    z = np.concatenate([y, np.broadcast_to(e, (x.shape[0], e.shape[0]))], axis=1)
+    return oracle.silu(z @ W["time_in.w"].T + W["time_in.b"]) @ W["time_out.w"].T + W["time_out.b"]
+
+
+def _embed_no_hidden_bias(W, cfg, x, t, act_round=None):
+    y = x @ W["action_in.w"].T + W["action_in.b"]
+    e = oracle.time_embedding(t, cfg.d_model, cfg.t_min_period, cfg.t_max_period)
+    z = np.concatenate([y, np.broadcast_to(e, (x.shape[0], e.shape[0]))], axis=1)
+    return oracle.silu(z @ W["time_in.w"].T) @ W["time_out.w"].T + W["time_out.b"]
+
+
+_EMBED_MUTANTS = [_embed_swapped_concat, _embed_silu_after_time_out, _embed_no_action_bias, _embed_no_hidden_bias]
+
+
+def test_embed_closed_forms():
+    """The time path alone gives h0 = 1.75 SiLU(e(t) + b_t1) + b_t2 on every row; the
+    action path alone gives h0[:, i] = 1.75 SiLU(s_i x[:, i mod 32] + b_in[i])."""
+    assert _embed_pin_failures(oracle.embed) == []
+
+
+@pytest.mark.parametrize("mutant", _EMBED_MUTANTS, ids=lambda f: f.__name__)
+def test_embed_closed_forms_catch_planted_mistakes(mutant):
+    assert _embed_pin_failures(mutant) != []
+
+
+def _velocity_through_identity_layers(W_embed, x, t):
+    """v from oracle.velocity with every layer made the identity (zero o and down
+    projections) and unit final-norm gains, on a 2-layer expert."""
+    cfg = ExpertConfig(n_layers=2)
+    W = oracle.decode_weights(synth.draw_weights(2))
+    W.update(W_embed)
+    for l in range(2):
+        W[f"layers.{l}.o.w"] = np.zeros_like(W[f"layers.{l}.o.w"])
+        W[f"layers.{l}.down.w"] = np.zeros_like(W[f"layers.{l}.down.w"])
+    W["final_norm.g"] = np.ones(720)
+    P = 9
+    kv = synth.draw_prefix_kv(2, 1, P)
+    pk, pv, pm = _query(kv, synth.make_mask(1, P, [6]), 0)
+    return oracle.velocity(W, cfg, x, t, pk, pv, pm), W, cfg
+
+
+def test_velocity_closed_form_through_embed_and_head(monkeypatch):
+    """The action-path embedding pushed through identity layers and the head:
+    v = h0 / sqrt(mean(h0^2) + eps) W_out^T + b_out with h0 in closed form.  The same
+    check fails when any planted mistake replaces embed inside the velocity field."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((50, 32))
+    W_embed = _embed_weights(rng, time_path=False)
+
+    def closed(W, cfg, t):
+        h0 = _embed_closed_form(W, cfg, x, t, time_path=False)
+        n = h0 / np.sqrt(np.mean(h0 * h0, axis=1, keepdims=True) + cfg.rms_eps)
+        return n @ W["action_out.w"].T + W["action_out.b"]
+
+    v, W, cfg = _velocity_through_identity_layers(W_embed, x, 0.37)
+    np.testing.assert_allclose(v, closed(W, cfg, 0.37), rtol=1e-11, atol=1e-13)
+    for mutant in _EMBED_MUTANTS[:3]:  # the action path has no b_t1 to drop
+        monkeypatch.setattr(oracle.expert, "embed", mutant)
+        v, W, cfg = _velocity_through_identity_layers(W_embed, x, 0.37)
+        assert not np.allclose(v, closed(W, cfg, 0.37), rtol=1e-6, atol=1e-8), mutant.__name__
