@@ -7,12 +7,12 @@
 //   checkpoint's bf16 values re-encoded exactly in fp16 with a power-of-two
 //   scale per matrix; activations are rounded to fp16 (8x finer than bf16).
 //   RMSNorm is fused: its gain is folded into the columns of the weight that
-//   follows it (host side), and the row scale 1/rms(h) multiplies either the
-//   operand as it is loaded (large M: from per-tile partial sums of squares
-//   written by the producer of the residual stream) or the accumulated sums
-//   (M <= 64: from the rows the workgroup loads anyway).  The A-operand load
-//   also fuses the prefix overwrite; epilogues fuse bias, SiLU, RoPE, SwiGLU,
-//   the residual add and the Euler update.
+//   follows it (host side); the GEMM multiplies the un-normalised fp16 copy of
+//   the residual and scales each finished row by 1/rms(h), whose sum of squares
+//   every kernel accumulates on the matrix cores from the A fragments it loads
+//   anyway (sumsq_mfma: the diagonal of A A^T).  The A-operand load also fuses
+//   the prefix overwrite; epilogues fuse bias, SiLU, RoPE, SwiGLU, the residual
+//   add and the Euler update.
 // Attention: block-masked grouped-query attention on v_mfma_f32_16x16x32_bf16
 //   over the bf16 prefix K/V cache and the chunk's own K/V, with an online
 //   softmax in fp32 and 64-key blocks staged in LDS.

@@ -119,7 +119,11 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems)
 
 /*
  * Denoise a batch of action chunks (the whole loop, asynchronous on hip_stream;
- * NULL = the null stream).
+ * NULL = the null stream).  noeira docs "SmolVLA", Architecture: a query's
+ * prefix is run once and its per-layer keys/values cached, then the expert is
+ * evaluated once per Euler step (ten times) on the chunk, from noise at t = 1
+ * toward t = 0; the block attention mask keeps the prefix blind to the actions,
+ * which is why the cached prefix suffices.
  *   prefix_kv    device bf16, [n_layers][2 (K, V)][batch][5][prefix_len][64]:
  *                each layer's cached prefix keys (already rotated at their
  *                prefix positions) and values.  Read only.
@@ -164,7 +168,9 @@ int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
 
 /*
  * One evaluation of the velocity field v(x, t | prefix) (the expert's forward
- * pass, no Euler update).  x and out_v are device fp32 [batch][50][32]; the other
+ * pass, no Euler update; noeira docs "SmolVLA", Architecture: the expert maps
+ * the noisy chunk at flow time t, the time embedding and the cached prefix to a
+ * velocity, whose training target is eps - a).  x and out_v are device fp32 [batch][50][32]; the other
  * arguments are as for smolexp_denoise.  Used to check a single step against
  * an oracle on the oracle's own x.  Asynchronous on hip_stream.
  */

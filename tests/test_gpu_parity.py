@@ -206,7 +206,7 @@ def test_denoise_16_layers_batch128_overwrite(ex16):
     wl = synth.make_workload("expert16_b128_p177_ow7", with_weights=False)
     gpu = run_gpu(ex16, to_device(wl), d=7)
     q = [0, 64, 127]
-    compare(gpu, run_oracle(ex16, wl, q, d=7), q, wl["noise"], "expert16_b128_p177_ow7")
+    compare(gpu, run_oracle(ex16, wl, q, d=7), q, wl["noise"], "expert16_b128_p177_ow7", d=7)
     # rows below d after the last step: the overwrite set them before step 9 and one Euler step followed
     ts, dt = oracle.schedule(10)
     t9 = float(ts[-1])
@@ -296,7 +296,7 @@ def test_edge_full_overwrite_and_four_steps():
         wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
         wl["prev_actions"] = synth.draw_prev_actions(2, 50)
         gpu = run_gpu(ex, to_device(wl), d=50)
-        compare(gpu, run_oracle(ex, wl, [0, 1], d=50), [0, 1], wl["noise"], "d=50 n=4")
+        compare(gpu, run_oracle(ex, wl, [0, 1], d=50), [0, 1], wl["noise"], "d=50 n=4", d=50)
     finally:
         ex.close()
 
