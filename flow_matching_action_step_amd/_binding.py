@@ -54,6 +54,7 @@ _sig = {
     "smolexp_denoise": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P]),
     "smolexp_denoise_ex": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
                                           ctypes.POINTER(smolexp_denoise_opts)]),
+    "smolexp_denoise_noalloc": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P]),
     "smolexp_velocity": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, ctypes.c_float, _P, ctypes.c_int, _P]),
     "smolexp_time_kernel": (ctypes.c_int, [_H, ctypes.c_int, ctypes.c_int, _P, ctypes.POINTER(ctypes.c_float)]),
     "smolexp_lm_weight_count": (ctypes.c_size_t, [ctypes.POINTER(smolexp_config)]),
@@ -167,6 +168,21 @@ def smolexp_denoise_ex(h, cfg, prefix_kv, prefix_mask, noise, out_actions, prev_
     rc = _lib.smolexp_denoise_ex(h, _ptr(prefix_kv), _ptr(prefix_mask), P, _ptr(noise), _ptr(out_actions), B,
                                  _stream(stream), ctypes.byref(opts))
     _check(rc, h, "smolexp_denoise_ex")
+
+
+def smolexp_denoise_noalloc(h, cfg, prefix_kv, prefix_mask, noise, out_actions, stream=None):
+    """As smolexp_denoise, on the library's fixed workspace (batch <= 16; allocates nothing)."""
+    import torch
+    B, P = prefix_mask.shape
+    _need(prefix_mask, "prefix_mask", torch.uint8)
+    if prefix_kv.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise ValueError("prefix_kv must hold bf16 values")
+    _need(prefix_kv, "prefix_kv", prefix_kv.dtype, _kv_shape(cfg, B, P))
+    _need(noise, "noise", torch.float32, (B, cfg.chunk, cfg.action_dim))
+    _need(out_actions, "out_actions", torch.float32, (B, cfg.chunk, cfg.action_dim))
+    rc = _lib.smolexp_denoise_noalloc(h, _ptr(prefix_kv), _ptr(prefix_mask), P, _ptr(noise), _ptr(out_actions), B,
+                                      _stream(stream))
+    _check(rc, h, "smolexp_denoise_noalloc")
 
 
 def smolexp_velocity(h, cfg, prefix_kv, prefix_mask, x, t, out_v, stream=None):

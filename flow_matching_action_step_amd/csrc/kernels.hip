@@ -25,6 +25,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace smolexp {
 
 typedef half_t f16x8 __attribute__((ext_vector_type(8)));
@@ -1795,6 +1797,52 @@ GemmPlan plan_prefill(int M, int N, int K, EMode em) {
     default:
       return big(128, 2);
   }
+}
+
+// ----------------------------------------------------------------------------
+// Workspace of the no-alloc denoise: a fixed array of device memory, one copy on every GPU
+// the library runs on, held until the process ends.  In host code `scratch` only names the
+// symbol: its device address is looked up once per device, with that device current, and
+// kept; kernels receive that address.
+// ----------------------------------------------------------------------------
+constexpr size_t kNoAllocBytes = call_ws_bytes(kNoAllocMaxBatch);
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(int device, char** ptr, size_t* bytes) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = static_cast<char*>(p);
+  }
+  *ptr = g_scratch_ptr[device];
+  *bytes = kNoAllocBytes;
+  return hipSuccess;
+}
+
+// Columns 720..767 of h16 are chunks 90..95 of each 16-row block: 6 x 256 contiguous bytes.
+__global__ __launch_bounds__(256) void zero_h16_pad_kernel(half_t* h16, int nblk) {
+  constexpr int kPieces = (kKPad - kD) / 8 * 16;  // 16-byte pieces per row block
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= nblk * kPieces) return;
+  const int rb = i / kPieces, j = i % kPieces;
+  reinterpret_cast<uint4*>(h16 + ((size_t)rb * (kKPad / 8) + kD / 8) * 128)[j] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero_h16_pad(half_t* h16, int rows, hipStream_t s) {
+  if (rows <= 0 || rows % 16 != 0) return hipErrorInvalidValue;
+  const int n = rows / 16 * ((kKPad - kD) / 8 * 16);
+  hipLaunchKernelGGL(zero_h16_pad_kernel, dim3((n + 255) / 256), dim3(256), 0, s, h16, rows / 16);
+  return hipGetLastError();
 }
 
 // Inverse periods of the time embedding: 1 / (p_min (p_max/p_min)^(i/359)), fp64.

@@ -81,13 +81,11 @@ struct smolexp_handle {
   float *b_t1 = nullptr, *b_t2 = nullptr, *b_out = nullptr;  // b_t1 holds b_t1 + W_t1[:, :720] b_in
   std::vector<LayerDev> layers;
 
-  // workspace
+  // workspace: the per-call activations for max_batch queries, then the handle's tables
   void* wsmem = nullptr;
-  float *x = nullptr, *h = nullptr, *cvec = nullptr;
-  half_t *s16 = nullptr, *o16 = nullptr, *u16 = nullptr, *h16 = nullptr;
-  bf16_t *q = nullptr, *kc = nullptr, *vc = nullptr;
+  CallWs ws{};
+  float* cvec = nullptr;    // time vectors of the schedule (+ one row for velocity calls)
   float2* rope = nullptr;   // [max_prefix + 50][32] (cos, sin) by position
-  float2* ropeq = nullptr;  // [B*50][32] per call: the rope rows of each chunk row's position
   double* inv_period = nullptr;
 
   hipStream_t cap = nullptr;
@@ -310,8 +308,8 @@ CallKey key_of(const CallArgs& c) {
   return k;
 }
 
-// The launch sequence of one call.
-int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
+// The launch sequence of one call, on the per-call workspace w.
+int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool record_probes) {
   const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
   // time vectors: the schedule's were computed when the weights were loaded; a velocity
@@ -333,9 +331,9 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   pa.mask = c.mask;
   pa.P = P;
   pa.rope = h->rope;
-  pa.ropeq = h->ropeq;
+  pa.ropeq = w.ropeq;
   pa.x_in = c.x_in;
-  pa.x = h->x;
+  pa.x = w.x;
   pa.w_t1e = h->w_t1e;
   pa.s_t1 = h->s_t1e;
   pa.b_t1 = h->b_t1;
@@ -357,7 +355,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
   // gate/up, action_out) read h16 = fp16(h), over the zero-padded K = 768 on the pipelined GEMM
   auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
     GemmArgs g = g0;
-    if (am == A_NORM) { g.A = h->h16; g.lda = kKPad; }
+    if (am == A_NORM) { g.A = w.h16; g.lda = kKPad; }
     const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em);
     if (plan.kind == 2) {
       if (am == A_NORM) g.K = kKPad;
@@ -382,16 +380,16 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     // W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read and stored back
     // into the state.  Then h = W_t2 s + b_t2.
     GemmArgs gt = g;
-    gt.N = kD; gt.K = kAD; gt.A = h->x; gt.lda = kAD;
-    gt.x = h->x; gt.noise = c.x_in; gt.prev = c.prev; gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
+    gt.N = kD; gt.K = kAD; gt.A = w.x; gt.lda = kAD;
+    gt.x = w.x; gt.noise = c.x_in; gt.prev = c.prev; gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
     gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
-    gt.out16 = h->s16; gt.ldo = kD;
+    gt.out16 = w.s16; gt.ldo = kD;
     if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
 
     GemmArgs go = g;
-    go.N = kD; go.K = kD; go.A = h->s16; go.lda = kD;
+    go.N = kD; go.K = kD; go.A = w.s16; go.lda = kD;
     go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
-    go.h = h->h; go.h16 = h->h16;
+    go.h = w.h; go.h16 = w.h16;
     if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
 
     for (int l = 0; l < L; ++l) {
@@ -402,19 +400,19 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
         GemmArgs gq = g;
         gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
         gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
-        gq.q = h->q; gq.kc = h->kc; gq.vc = h->vc; gq.ropeq = h->ropeq;
+        gq.q = w.q; gq.kc = w.kc; gq.vc = w.vc; gq.ropeq = w.ropeq;
         if ((e = norm_gemm(ld.self_attn ? PR_QKV : PR_QCROSS, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
       }
 
       AttnArgs aa;
       memset(&aa, 0, sizeof(aa));
-      aa.q = h->q; aa.kc = h->kc; aa.vc = h->vc;
+      aa.q = w.q; aa.kc = w.kc; aa.vc = w.vc;
       aa.pk = kv + (size_t)l * kvLayer;
       aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2;
-      aa.mask = c.mask; aa.out = h->o16; aa.B = B; aa.P = P;
+      aa.mask = c.mask; aa.out = w.o16; aa.B = B; aa.P = P;
       if (fold_q) {
         aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale;
-        aa.h16 = h->h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = h->ropeq;
+        aa.h16 = w.h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = w.ropeq;
       }
       const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
       if (record_probes && first_step) {
@@ -426,18 +424,18 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
       if ((e = launch_attention(ld.self_attn, aa, s)) != hipSuccess) return hip_fail(h, e, "attention launch");
 
       GemmArgs gop = g;
-      gop.N = kD; gop.K = kNQ; gop.A = h->o16; gop.lda = kNQ;
-      gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = h->h; gop.h16 = h->h16;
+      gop.N = kD; gop.K = kNQ; gop.A = w.o16; gop.lda = kNQ;
+      gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = w.h; gop.h16 = w.h16;
       if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
 
       GemmArgs gg = g;
       gg.N = kGU; gg.K = kD;
-      gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = h->u16; gg.ldo = kFFN;
+      gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = w.u16; gg.ldo = kFFN;
       if ((e = norm_gemm(PR_GU, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
 
       GemmArgs gd = g;
-      gd.N = kD; gd.K = kFFN; gd.A = h->u16; gd.lda = kFFN;
-      gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = h->h; gd.h16 = h->h16;
+      gd.N = kD; gd.K = kFFN; gd.A = w.u16; gd.lda = kFFN;
+      gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = w.h; gd.h16 = w.h16;
       if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
     }
 
@@ -445,7 +443,7 @@ int enqueue(smolexp_t h, const CallArgs& c, hipStream_t s, bool record_probes) {
     GemmArgs gv = g;
     gv.N = kAD; gv.K = kD;
     gv.W = h->w_out.w; gv.ldw = h->w_out.ld; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
-    gv.x = h->x; gv.dt = h->dt;
+    gv.x = w.x; gv.dt = h->dt;
     const size_t stepElems = (size_t)B * kChunk * kAD;
     if (c.velocity) {
       gv.vel_out = c.out;
@@ -510,8 +508,8 @@ int run_call(smolexp_t h, const CallArgs& c, hipStream_t s) {
   const CallKey key = key_of(c);
   h->last = key;
   h->have_last = true;
-  if (!h->cfg.use_graphs) return enqueue(h, c, s, true);
-  return run_cached(h, key, s, [&](hipStream_t cs) { return enqueue(h, c, cs, true); });
+  if (!h->cfg.use_graphs) return enqueue(h, c, h->ws, s, true);
+  return run_cached(h, key, s, [&](hipStream_t cs) { return enqueue(h, c, h->ws, cs, true); });
 }
 
 int check_call(smolexp_t h, const void* kv, const uint8_t* mask, int P, const float* x_in, float* out, int B) {
@@ -669,33 +667,28 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   h->device = hip_device;
   smolexp_schedule(cfg, h->ts, &h->dt);
 
-  const size_t Mmax = (size_t)cfg->max_batch * kChunk;
-  const size_t Mpad = (size_t)round16((int)Mmax);  // blocked operands hold whole 16-row blocks
+  const size_t Mpad = (size_t)round16(cfg->max_batch * kChunk);  // blocked operands hold whole 16-row blocks
   const int n_pos = cfg->max_prefix + kChunk;
-  size_t off = 0;
+  size_t off = call_ws_bytes(cfg->max_batch);
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const size_t o_x = take(Mmax * kAD * 4), o_h = take(Mpad * kD * 4);
   const size_t o_cv = take((size_t)(kMaxSteps + 1) * kD * 4);  // the schedule's time vectors + one for velocity calls
-  const size_t o_s = take(Mpad * kD * 2), o_o = take(Mpad * kNQ * 2);
-  const size_t o_u = take(Mpad * kFFN * 2), o_h16 = take(Mpad * kKPad * 2);
-  const size_t o_q = take(Mmax * kNQ * 2), o_kc = take(Mmax * kNKV * 2);
-  const size_t o_vc = take(Mmax * kNKV * 2), o_rq = take(Mmax * (kHD / 2) * sizeof(float2));
   const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
   const size_t o_invp = take((size_t)(kD / 2) * sizeof(double));
+  // the no-alloc entry point's fixed workspace on this device: its address, looked up once
+  char* scratch_base = nullptr;
+  size_t scratch_bytes = 0;
+  if (noalloc_scratch(hip_device, &scratch_base, &scratch_bytes) != hipSuccess) { delete h; return SMOLEXP_E_HIP; }
   hipError_t e = hipMalloc(&h->wsmem, off);
   if (e != hipSuccess) { delete h; return SMOLEXP_E_NOMEM; }
   char* base = static_cast<char*>(h->wsmem);
-  h->x = (float*)(base + o_x); h->h = (float*)(base + o_h);
-  h->cvec = (float*)(base + o_cv); h->s16 = (half_t*)(base + o_s);
-  h->o16 = (half_t*)(base + o_o); h->u16 = (half_t*)(base + o_u); h->h16 = (half_t*)(base + o_h16);
-  h->q = (bf16_t*)(base + o_q);
-  h->kc = (bf16_t*)(base + o_kc); h->vc = (bf16_t*)(base + o_vc); h->ropeq = (float2*)(base + o_rq);
+  h->ws = carve_call_ws(base, cfg->max_batch);
+  h->cvec = (float*)(base + o_cv);
   h->rope = (float2*)(base + o_rope);
   h->inv_period = (double*)(base + o_invp);
 
   e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
   // the columns 720..767 of h16 are read by the K = 768 GEMM and never written: zero them once
-  if (e == hipSuccess) e = hipMemsetAsync(h->h16, 0, Mpad * kKPad * 2, h->cap);
+  if (e == hipSuccess) e = hipMemsetAsync(h->ws.h16, 0, Mpad * kKPad * 2, h->cap);
   if (e == hipSuccess) e = launch_rope_table(h->rope, n_pos, cfg->rope_theta, h->cap);
   if (e == hipSuccess) e = launch_inv_period_table(h->inv_period, cfg->t_min_period, cfg->t_max_period, h->cap);
   if (e == hipSuccess) e = hipStreamSynchronize(h->cap);
@@ -1094,6 +1087,29 @@ int smolexp_denoise(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_ma
   return smolexp_denoise_ex(h, prefix_kv, prefix_mask, prefix_len, noise, out_actions, batch, hip_stream, nullptr);
 }
 
+int smolexp_denoise_noalloc(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
+                            const float* noise, float* out_actions, int batch, void* hip_stream) {
+  int rc = check_call(h, prefix_kv, prefix_mask, prefix_len, noise, out_actions, batch);
+  if (rc != SMOLEXP_OK) return rc;
+  if (batch > kNoAllocMaxBatch)
+    return fail(h, SMOLEXP_E_INVAL, "batch above the no-alloc workspace's maximum of 16 queries");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
+  char* base = nullptr;
+  size_t bytes = 0;
+  hipError_t e = noalloc_scratch(h->device, &base, &bytes);
+  if (e != hipSuccess) return hip_fail(h, e, "no-alloc workspace lookup");
+  const CallWs w = carve_call_ws(base, kNoAllocMaxBatch);
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  // the array keeps the last call's contents: the zero columns of h16 are cleared each call
+  e = launch_zero_h16_pad(w.h16, round16(batch * kChunk), s);
+  if (e != hipSuccess) return hip_fail(h, e, "no-alloc workspace clear");
+  CallArgs c;
+  memset(&c, 0, sizeof(c));
+  c.velocity = false;
+  c.kv = prefix_kv; c.mask = prefix_mask; c.P = prefix_len; c.x_in = noise; c.out = out_actions; c.B = batch;
+  return enqueue(h, c, w, s, false);
+}
+
 int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
                      const float* x, float t, float* out_v, int batch, void* hip_stream) {
   int rc = check_call(h, prefix_kv, prefix_mask, prefix_len, x, out_v, batch);
@@ -1124,7 +1140,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
   }
   if (kernel != PR_LOOP && (!h->have_probe || !same_key(h->probe_key, h->last))) {
     // the previous call was a graph replay of another key: enqueue it once directly to get its launches
-    int rc0 = enqueue(h, lastc, s, true);
+    int rc0 = enqueue(h, lastc, h->ws, s, true);
     if (rc0 != SMOLEXP_OK) return rc0;
   }
   if (kernel != PR_LOOP && h->probes[kernel].empty()) return fail(h, SMOLEXP_E_STATE, "kernel not part of the previous call");

@@ -142,6 +142,57 @@ struct PrologueArgs {
   const double* inv_period;  // [360] 1 / p_i of the time embedding
 };
 
+// Per-call activations of the denoising loop (device memory): the Euler state x, the fp32
+// residual h and its fp16 copy h16 (768 stored columns, 720.. zero), the time MLP's hidden
+// layer s16, the attention output o16, the SwiGLU output u16, the chunk's Q / K / V and the
+// RoPE rows of each chunk row.  Blocked operands hold whole 16-row blocks.
+struct CallWs {
+  float* x;
+  float* h;
+  half_t *s16, *o16, *u16, *h16;
+  bf16_t *q, *kc, *vc;
+  float2* ropeq;
+};
+constexpr size_t ws_align256(size_t n) { return (n + 255) & ~(size_t)255; }
+// Sizes of the CallWs buffers, in the order they are carved, for max_batch queries.
+constexpr int kCallWsParts = 10;
+constexpr size_t call_ws_part(int max_batch, int i) {
+  const size_t M = (size_t)max_batch * kChunk, Mp = (M + 15) & ~(size_t)15;
+  const size_t sz[kCallWsParts] = {M * kAD * 4,  Mp * kD * 4,    Mp * kD * 2,   Mp * kNQ * 2,  Mp * kFFN * 2,
+                                   Mp * 768 * 2, M * kNQ * 2,    M * kNKV * 2,  M * kNKV * 2,
+                                   M * (kHD / 2) * sizeof(float2)};
+  return ws_align256(sz[i]);
+}
+constexpr size_t call_ws_bytes(int max_batch) {
+  size_t n = 0;
+  for (int i = 0; i < kCallWsParts; ++i) n += call_ws_part(max_batch, i);
+  return n;
+}
+// Carve a CallWs for max_batch queries from base (call_ws_bytes(max_batch) bytes).
+inline CallWs carve_call_ws(char* base, int max_batch) {
+  char* p[kCallWsParts];
+  size_t off = 0;
+  for (int i = 0; i < kCallWsParts; ++i) {
+    p[i] = base + off;
+    off += call_ws_part(max_batch, i);
+  }
+  CallWs w;
+  w.x = (float*)p[0]; w.h = (float*)p[1];
+  w.s16 = (half_t*)p[2]; w.o16 = (half_t*)p[3]; w.u16 = (half_t*)p[4]; w.h16 = (half_t*)p[5];
+  w.q = (bf16_t*)p[6]; w.kc = (bf16_t*)p[7]; w.vc = (bf16_t*)p[8];
+  w.ropeq = (float2*)p[9];
+  return w;
+}
+
+// The no-alloc denoise (smolexp_denoise_noalloc) keeps its per-call workspace in a fixed
+// device array of the library, sized for this many queries.
+constexpr int kNoAllocMaxBatch = 16;
+// Address of that array on `device` (which must be current), looked up once per device;
+// nullptr with an error if the lookup failed.
+hipError_t noalloc_scratch(int device, char** ptr, size_t* bytes);
+// Zero columns 720..767 of rows 0 .. rows-1 (rows a multiple of 16) of an h16 buffer.
+hipError_t launch_zero_h16_pad(half_t* h16, int rows, hipStream_t s);
+
 // How one GEMM is cut up (kernels.hip decides, the host sizes workspaces from it).
 struct GemmPlan {
   int kind;      // 0: register-resident K split (skinny): 16 rb x 16 cb tiles, 8 waves split K;

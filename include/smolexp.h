@@ -143,6 +143,26 @@ int smolexp_denoise(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_ma
                     void* hip_stream);
 
 /*
+ * smolexp_denoise for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * kernels and launches as smolexp_denoise (launched directly, never through a
+ * cached graph), but the per-call activations live in a fixed array of device
+ * memory inside the library (one copy per GPU, about 12.4 MB, held until the
+ * process ends) instead of the handle's workspace; the handle's weights and
+ * tables are only read.  The call allocates nothing: no hipMalloc, no graph.
+ *   batch  1..16 (and <= the handle's max_batch); larger batches return
+ *          SMOLEXP_E_INVAL ("batch above the no-alloc workspace's maximum").
+ * Other arguments and errors as for smolexp_denoise.  Every call on one GPU
+ * shares that GPU's array, from any handle: calls that overlap on one GPU (on
+ * two streams, or from two threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The array keeps the last call's contents
+ * (what must start at zero is cleared by each call).
+ */
+int smolexp_denoise_noalloc(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask,
+                            int prefix_len, const float* noise, float* out_actions, int batch,
+                            void* hip_stream);
+
+/*
  * Options for smolexp_denoise_ex.  Every field may be zero/NULL.
  *   prev_actions    device fp32 [batch][overwrite_rows][32]: tail of the
  *                   previous chunk for prefix overwrite ("Paper vs hardware 11:
