@@ -4,9 +4,14 @@
 One "step" is one smolexp_denoise call: the whole Euler loop (10 steps, or
 --n-steps) of the 16-layer expert over one batch of synthetic inputs already
 resident in HBM.
-Prints one JSON line: chunks/s, ms per call, the roofline of the dominant
-kernel (timed live with HIP events on the library's stream), the whole-loop
-roofline, and the CPU oracle timed on the host as a baseline.
+Prints one JSON line: chunks/s and ms per call at batch 1 (the 16-layer expert,
+prefix 177), the roofline of the dominant kernel (its time per launch taken live
+with HIP events on the library's stream, its bytes counted algorithmically:
+parameters once, valid prefix K/V tokens), the whole-loop roofline, the
+prefix-overwrite difference, the large-batch workloads (batch 64 at prefix 257;
+batch 128 at prefix 177 with 7 overwritten rows: ms per call, chunks/s, MFMA
+fraction of the loop and of its dominant kernel), and the CPU oracle timed on the
+host as a baseline (all threads, and one).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--n-steps N]
 """
@@ -21,6 +26,7 @@ MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 RIDGE = MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 DEFAULT_WORKLOAD = "expert16_b1_p177"
+LARGE_BATCH_WORKLOADS = ("expert16_b64_p257", "expert16_b128_p177_ow7")
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
@@ -140,40 +146,41 @@ def summarize_pmc(fetch_csv, write_csv, workload, kernel):
 
 
 def kernel_costs(L, B, lengths, P):
-    """Algorithmic (bytes, flops) of ONE launch of each timed kernel, and launches per call per step.
+    """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
+    launches per Euler step.
 
-    Bytes count each operand once: fp16 weights (2 B/element, without the K
-    padding), the activation the kernel reads (the normed projections read the
-    fp16 copy of the residual), the activations it writes (o and down
-    read-modify-write the fp32 residual and write its fp16 copy), valid prefix
-    K/V tokens only.  Flops are 2 per multiply-add; attention counts unmasked
-    keys only.
+    Algorithmic bytes follow the counting of the loop's roofline: the parameters the launch
+    reads, once, at 2 bytes per element (the bf16 manifest; RMSNorm gains are folded into the
+    matrices that follow them, action_in into a [720, 32] matrix with the action half of
+    time_in, and the time-embedding half of time_in into one time vector per step, all when
+    the weights are loaded), plus the valid prefix K/V tokens the launch attends to.
+    Activation bytes (the fp16/bf16/fp32 rows each launch reads and writes) are counted apart.
+    Flops are 2 per multiply-add; attention counts unmasked keys only.
     """
     M = 50 * B
     sum_nb = float(sum(lengths))
-    c = {}
-    c["qkv_self"] = (1600 * 720 * 2 + M * 720 * 2 + M * 1600 * 2, 2.0 * M * 1600 * 720)
-    kv_self = 5 * 64 * 2 * 2 * (sum_nb + 50 * B)
+    kv = 5 * 64 * 2 * 2 * sum_nb            # one layer's valid prefix K and V
     keys_self = 50 * sum_nb + 1275 * B
-    c["attn_self"] = (M * 960 * 2 + kv_self + M * 960 * 2, 4.0 * 64 * 15 * keys_self)
-    kv_cross = 5 * 64 * 2 * 2 * sum_nb
+    c = {}
+    c["qkv_self"] = (1600 * 720 * 2, M * 720 * 2 + M * 1600 * 2, 2.0 * M * 1600 * 720)
+    c["attn_self"] = (kv, M * 960 * 2 + M * 640 * 2 + M * 960 * 2, 4.0 * 64 * 15 * keys_self)
     if B <= CROSS_Q_MAX_BATCH:  # the cross layers' Q projection runs inside the attention launch
-        c["attn_cross"] = (960 * 720 * 2 + M * 720 * 2 + kv_cross + M * 960 * 2,
+        c["attn_cross"] = (960 * 720 * 2 + kv, M * 720 * 2 + M * 960 * 2,
                            2.0 * M * 960 * 720 + 4.0 * 64 * 15 * 50 * sum_nb)
     else:
-        c["attn_cross"] = (M * 960 * 2 + kv_cross + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
-    c["o"] = (720 * 960 * 2 + M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
-    c["gate_up"] = (4096 * 720 * 2 + M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
-    c["down"] = (720 * 2048 * 2 + M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
-    c["action_out"] = (32 * 720 * 2 + M * 720 * 2 + M * 32 * 8, 2.0 * M * 32 * 720)
-    # the time MLP's first layer as the kernel computes it: action_in folded into its action half
-    # (a [720, 32] weight), the Euler state in, the step's time vector, fp16 activations out
-    c["time_in"] = (720 * 32 * 2 + M * 32 * 4 + 720 * 4 + M * 720 * 2, 2.0 * M * 720 * 32)
-    c["time_out"] = (720 * 720 * 2 + M * 720 * 2 + M * 720 * 6, 2.0 * M * 720 * 720)
+        c["attn_cross"] = (kv, M * 960 * 2 + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
+    # o and down read-modify-write the fp32 residual and write its fp16 copy (10 B per element)
+    c["o"] = (720 * 960 * 2, M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
+    c["gate_up"] = (4096 * 720 * 2, M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
+    c["down"] = (720 * 2048 * 2, M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
+    c["action_out"] = ((32 * 720 + 32) * 2, M * 720 * 2 + M * 32 * 8, 2.0 * M * 32 * 720)
+    # the time MLP's first layer: the folded [720, 32] matrix and the step's time vector
+    c["time_in"] = ((720 * 32 + 720) * 2, M * 32 * 4 + M * 720 * 2, 2.0 * M * 720 * 32)
+    c["time_out"] = ((720 * 720 + 720) * 2, M * 720 * 2 + M * 720 * 6, 2.0 * M * 720 * 720)
     per_step = {"qkv_self": L // 2 + L % 2, "attn_self": L // 2 + L % 2, "attn_cross": L // 2, "o": L,
                 "gate_up": L, "down": L, "action_out": 1, "time_in": 1, "time_out": 1}
     if B > CROSS_Q_MAX_BATCH:  # the cross layers' Q projection is a launch of its own
-        c["q_cross"] = (960 * 720 * 2 + M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
+        c["q_cross"] = (960 * 720 * 2, M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
         per_step["q_cross"] = L // 2
     return c, per_step
 
@@ -185,38 +192,143 @@ LOOP_ID = 7  # smolexp_time_kernel: the whole call
 
 
 def loop_algorithmic(L, B, lengths, n_steps):
-    """Whole-loop algorithmic bytes and flops per call: weights once per step (bf16,
-    2 B/element), valid prefix K/V once per step, 2 flops per weight MAC per chunk row,
-    attention over unmasked keys."""
-    import synth
-    wbytes = 2 * synth.weight_count(L)
-    sum_nb = float(sum(lengths))
-    kvbytes = L * 2 * 5 * 64 * 2 * sum_nb
-    macs_per_row = sum(int(__import__("numpy").prod(s)) for n, s, k in synth.manifest(L) if k == "w")
-    n_self, n_cross = (L + 1) // 2, L // 2
-    att = 4.0 * 64 * 15 * (n_self * (50 * sum_nb + 1275 * B) + n_cross * 50 * sum_nb)
-    flops = 2.0 * macs_per_row * 50 * B + att
-    return n_steps * (wbytes + kvbytes), n_steps * flops
+    """Whole-call algorithmic bytes and flops: per step, every launch's algorithmic bytes
+    (parameters once, valid prefix K/V once) and flops, from kernel_costs."""
+    c, per_step = kernel_costs(L, B, lengths, 0)
+    byt = sum(c[k][0] * n for k, n in per_step.items())
+    fl = sum(c[k][2] * n for k, n in per_step.items())
+    return n_steps * byt, n_steps * fl
 
 
-def cpu_baseline(wl, n_steps, min_seconds, max_seconds):
-    """The float64 numpy oracle on the host, on whole chunks of the workload's first queries."""
+def roofline_of(bytes_, flops, seconds):
+    """Bound by arithmetic intensity against the ridge of the published peaks."""
+    if flops / bytes_ < RIDGE:
+        r = {"bound": "hbm", "achieved": bytes_ / seconds / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": flops / seconds / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    return r
+
+
+def kernel_table(fm, h, cfg, L, B, lengths, P, reps):
+    """Per timed kernel: the hook's HIP-event time per launch (one graph of `reps` launches,
+    each repeating that kernel's launch of the next layer in the first step of the last call),
+    launches per call, and the launch's algorithmic bytes, activation bytes and flops."""
+    costs, per_step = kernel_costs(L, B, lengths, P)
+    kern = {}
+    for name, kid in KERNEL_IDS.items():
+        if name not in per_step:  # not launched at this batch (folded into another kernel)
+            continue
+        us = fm.smolexp_time_kernel(h, kid, reps)
+        byt, act, fl = costs[name]
+        n = per_step[name] * cfg.n_steps
+        kern[name] = {"avg_us": us, "launches_per_call": n, "us_per_call": us * n, "bytes": byt,
+                      "activation_bytes": act, "flops": fl}
+    return kern
+
+
+def timed_calls(call, n, warmup, stream):
+    """Per-call milliseconds of n calls, each bracketed by HIP events on the stream."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def device_inputs(wl):
     import numpy as np
+    import torch
+    d = {"kv": torch.from_numpy(np.ascontiguousarray(wl["prefix_kv"]).view(np.int16)).cuda(),
+         "mask": torch.from_numpy(wl["mask"]).cuda(), "noise": torch.from_numpy(wl["noise"]).cuda()}
+    d["prev"] = torch.from_numpy(wl["prev_actions"]).cuda() if wl["prev_actions"] is not None else None
+    return d
+
+
+def overwrite_delta(fm, h, cfg, dev, prev, d, calls, warmup, stream):
+    """Per-call time with the first d rows overwritten before every step against the same call
+    without the overwrite, on one handle: `calls` calls of each, alternating in rounds of 5."""
+    import torch
+    B = dev["mask"].shape[0]
+    out = torch.empty((B, 50, 32), device="cuda")
+    with_ow = lambda: fm.smolexp_denoise_ex(h, cfg, dev["kv"], dev["mask"], dev["noise"], out,  # noqa: E731
+                                            prev_actions=prev, overwrite_rows=d)
+    without = lambda: fm.smolexp_denoise_ex(h, cfg, dev["kv"], dev["mask"], dev["noise"], out)  # noqa: E731
+    a, b = [], []
+    for r in range((calls + 4) // 5):
+        a += timed_calls(with_ow, 5, warmup if r == 0 else 1, stream)
+        b += timed_calls(without, 5, warmup if r == 0 else 1, stream)
+    ma, mb = median(a), median(b)
+    return {"overwrite_rows": d, "ms_per_call_with": ma, "ms_per_call_without": mb, "calls_each": len(a),
+            "delta_ms_per_call": ma - mb, "delta_ms_per_chunk": (ma - mb) / B,
+            "note": "median of per-call HIP-event times; the call's latency is each chunk's latency, "
+                    "delta_ms_per_chunk spreads the call's difference over its batch"}
+
+
+def large_batch_entry(fm, h, cfg, wl, calls, warmup, reps, stream):
+    """One large-batch workload on the handle: per-call median, chunks/s, the loop's MFMA
+    fraction and the dominant kernel's (hook time), and the prefix-overwrite difference when
+    the workload overwrites rows."""
+    import torch
+    L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
+    dev = device_inputs(wl)
+    out = torch.empty((B, 50, 32), device="cuda")
+    call = lambda: fm.smolexp_denoise_ex(h, cfg, dev["kv"], dev["mask"], dev["noise"], out,  # noqa: E731
+                                         prev_actions=dev["prev"], overwrite_rows=d)
+    ms = timed_calls(call, calls, warmup, stream)
+    assert torch.isfinite(out).all().item(), "non-finite actions"
+    lb, lf = loop_algorithmic(L, B, wl["lengths"], cfg.n_steps)
+    med = median(ms)
+    kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, reps)
+    dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
+    dom = kern[dom_name]
+    e = {"batch": B, "prefix_len": P, "overwrite_rows": d, "calls": calls, "ms_per_call": med,
+         "ms_per_call_min": min(ms), "ms_per_call_max": max(ms), "chunks_per_s": B / (med * 1e-3),
+         "loop_algorithmic_flops_per_call": lf, "loop_algorithmic_bytes_per_call": lb,
+         "loop_tflops": lf / (med * 1e-3) / 1e12, "loop_mfma_frac": lf / (med * 1e-3) / (MFMA_F16_PEAK_TFS * 1e12),
+         "dominant_kernel": {"kernel": dom_name, "avg_us": dom["avg_us"], "us_per_call": dom["us_per_call"],
+                             "tflops": dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12,
+                             "mfma_frac": dom["flops"] / (dom["avg_us"] * 1e-6) / (MFMA_F16_PEAK_TFS * 1e12)},
+         "kernels": {k: {"avg_us": v["avg_us"], "us_per_call": v["us_per_call"],
+                         "mfma_frac": v["flops"] / (v["avg_us"] * 1e-6) / (MFMA_F16_PEAK_TFS * 1e12)}
+                     for k, v in kern.items()}}
+    if d > 0:
+        e["overwrite"] = overwrite_delta(fm, h, cfg, dev, dev["prev"], d, calls, 2, stream)
+    return e
+
+
+def cpu_baseline(wl, n_steps, min_seconds, max_seconds, threads=None):
+    """The float64 numpy oracle on the host, on whole chunks of the workload's first queries
+    (BLAS threads: all, or `threads`)."""
+    import contextlib
     import threadpoolctl
     import oracle
     W = oracle.decode_weights(wl["weights"])
     cfg = oracle.ExpertConfig(n_layers=wl["n_layers"])
     B = wl["batch"]
-    done, t0 = 0, time.perf_counter()
-    while True:
-        b = done % B
-        oracle.denoise_batch(W, cfg, wl["prefix_kv"], wl["mask"], wl["noise"], n_steps=n_steps,
-                             prev=wl["prev_actions"], d=wl["overwrite_rows"], queries=[b])
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or el + el / done > max_seconds:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    limit = threadpoolctl.threadpool_limits(threads) if threads else contextlib.nullcontext()
+    with limit:
+        done, t0 = 0, time.perf_counter()
+        while True:
+            b = done % B
+            oracle.denoise_batch(W, cfg, wl["prefix_kv"], wl["mask"], wl["noise"], n_steps=n_steps,
+                                 prev=wl["prev_actions"], d=wl["overwrite_rows"], queries=[b])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or el + el / done > max_seconds:
+                break
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {"value": done / el, "unit": "chunks/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} whole {n_steps}-step chunk(s) of the first {min(done, B)} quer(ies), {el:.1f} s, "
                       f"float64 numpy, {threads} BLAS thread(s), host {os.cpu_count()} logical CPUs"}
@@ -449,6 +561,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="launch kernels one by one instead of graph replay")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the workload's own line: no large-batch block and no overwrite difference")
+    ap.add_argument("--large-calls", type=int, default=20, help="timed calls per large-batch workload")
+    ap.add_argument("--large-kernel-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 256 MiB device-to-device three times (HBM counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
@@ -479,16 +595,15 @@ def main():
     cfg = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps, max_batch=B, max_prefix=P,
                                     use_graphs=0 if args.no_graphs else 1)
     h = fm.smolexp_create(cfg, 0)
-    fm.smolexp_load_weights(h, synth.pack_weights(wl["weights"], L))
-    kv = torch.from_numpy(np.ascontiguousarray(wl["prefix_kv"]).view(np.int16)).cuda()
-    mask = torch.from_numpy(wl["mask"]).cuda()
-    noise = torch.from_numpy(wl["noise"]).cuda()
-    prev = torch.from_numpy(wl["prev_actions"]).cuda() if d > 0 else None
+    packed = synth.pack_weights(wl["weights"], L)
+    fm.smolexp_load_weights(h, packed)
+    dev = device_inputs(wl)
     out = torch.empty((B, 50, 32), device="cuda")
     stream = torch.cuda.current_stream()
 
     def call():
-        fm.smolexp_denoise_ex(h, cfg, kv, mask, noise, out, prev_actions=prev, overwrite_rows=d)
+        fm.smolexp_denoise_ex(h, cfg, dev["kv"], dev["mask"], dev["noise"], out, prev_actions=dev["prev"],
+                              overwrite_rows=d)
 
     for _ in range(args.warmup):
         call()
@@ -506,39 +621,28 @@ def main():
     ev_ms = e0.elapsed_time(e1)
     assert torch.isfinite(out).all().item(), "non-finite actions"
 
-    # per-kernel average launch duration, HIP events on the library's stream
-    costs, per_step = kernel_costs(L, B, wl["lengths"], P)
-    kern = {}
-    for name, kid in KERNEL_IDS.items():
-        if name not in per_step:  # not launched at this batch (folded into another kernel)
-            continue
-        us = fm.smolexp_time_kernel(h, kid, args.kernel_reps)
-        byt, fl = costs[name]
-        kern[name] = {"avg_us": us, "launches_per_call": per_step[name] * cfg.n_steps,
-                      "us_per_call": us * per_step[name] * cfg.n_steps, "bytes": byt, "flops": fl}
+    # per-kernel time per launch: HIP events on the library's stream around one graph of launches
+    kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, args.kernel_reps)
     loop_us = fm.smolexp_time_kernel(h, LOOP_ID, max(3, args.steps // 5))
     dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
     dom = kern[dom_name]
-    intensity = dom["flops"] / dom["bytes"]
-    if intensity < RIDGE:
-        achieved = dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        achieved = dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof = roofline_of(dom["bytes"], dom["flops"], dom["avg_us"] * 1e-6)
     roof["traffic"] = stored_traffic(args.workload, dom_name)
     roof["kernel"] = dom_name
     roof["avg_us"] = dom["avg_us"]
     roof["algorithmic_bytes_per_launch"] = dom["bytes"]
     roof["algorithmic_flops_per_launch"] = dom["flops"]
+    roof["activation_bytes_per_launch"] = dom["activation_bytes"]
+    roof["timing"] = ("hook: HIP events around one graph of launches of this kernel, each repeating its "
+                      "launch of the next layer (the loop's weights in turn)")
 
     ms = wall / args.steps * 1e3
     lb, lf = loop_algorithmic(L, B, wl["lengths"], cfg.n_steps)
     loop = {"algorithmic_bytes_per_call": lb, "algorithmic_flops_per_call": lf,
             "hbm_frac": lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "mfma_frac": lf / (ms * 1e-3) / (MFMA_F16_PEAK_TFS * 1e12),
-            "event_ms_per_call": ev_ms / args.steps, "replay_us_per_call": loop_us}
+            "event_ms_per_call": ev_ms / args.steps, "replay_us_per_call": loop_us,
+            "launches_per_call": 1 + sum(v["launches_per_call"] for v in kern.values())}
 
     line = {
         "metric": f"action chunks/sec (50x32, {cfg.n_steps} Euler steps) + ms/chunk at B=1; % HBM/MFMA roofline",
@@ -552,9 +656,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "precision": "GEMM operands fp16 (bf16 weights re-encoded exactly; RMSNorm gains folded into the "
-                     "following weights, rounded once), attention bf16, fp32 accumulate, fp32 residual/norm "
-                     "scale/softmax/Euler",
+        "precision": "GEMM operands fp16 (the bf16 weights re-encoded exactly; RMSNorm gains folded into the "
+                     "following weights, rounded once; activations rounded to fp16), attention operands bf16 "
+                     "(the bf16 K/V cache as given, chunk Q/K/V and probabilities rounded to bf16), fp32 "
+                     "accumulate, fp32 residual/norm scale/softmax/Euler state",
         "data": "synthetic (seeded: weights N(0,0.02) bf16, prefix K/V N(0,1) bf16, noise N(0,1))",
         "config": {"workload": args.workload, "n_layers": L, "batch": B, "prefix_len": P,
                    "n_steps": cfg.n_steps, "chunk": 50, "action_dim": 32, "overwrite_rows": d,
@@ -564,6 +669,10 @@ def main():
         "kernels": kern,
         "gpu_state": gpu_state,
     }
+    if B == 1 and d == 0 and not args.no_extra:
+        # the prefix overwrite at batch 1 (the pages' per-chunk figure is a batch-1 latency)
+        prev1 = torch.from_numpy(synth.draw_prev_actions(1, 7)).cuda()
+        line["overwrite_b1"] = overwrite_delta(fm, h, cfg, dev, prev1, 7, 20, 3, stream)
     fm.smolexp_destroy(h)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, device="cuda")
@@ -571,8 +680,25 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+        # the large-batch workloads on one handle with the same weights
+        big = [synth.make_workload(n, with_weights=False) for n in LARGE_BATCH_WORKLOADS]
+        cfg2 = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps,
+                                         max_batch=max(w["batch"] for w in big),
+                                         max_prefix=max(w["prefix_len"] for w in big))
+        h2 = fm.smolexp_create(cfg2, 0)
+        fm.smolexp_load_weights(h2, packed)
+        line["large_batch"] = {}
+        for w in big:
+            line["large_batch"][w["name"]] = large_batch_entry(fm, h2, cfg2, w, args.large_calls, 3,
+                                                               args.large_kernel_reps, stream)
+            del w["prefix_kv"]
+        fm.smolexp_destroy(h2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, cfg.n_steps, args.cpu_seconds, 3 * args.cpu_seconds)
+        if B == 1:
+            line["cpu_baseline"]["single_thread"] = cpu_baseline(wl, cfg.n_steps, args.cpu_seconds / 2,
+                                                                 3 * args.cpu_seconds, threads=1)
     print(json.dumps(line), flush=True)
 
 

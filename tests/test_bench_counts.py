@@ -7,6 +7,8 @@ prefix K/V read twice."""
 import os
 import sys
 
+import numpy as np
+
 import synth
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -40,3 +42,44 @@ def _recount(L, B, lengths):
 def test_train_counts_match_a_recount_from_the_manifest():
     for L, B, lengths in ((16, 64, [257] * 64), (4, 3, [70, 33, 1]), (2, 1, [0])):
         assert bench.train_algorithmic(L, B, lengths) == _recount(L, B, lengths), (L, B)
+
+
+def _recount_denoise(L, B, lengths, n_steps):
+    """Per call: every manifest tensor the loop reads, once per step at 2 bytes per element,
+    except what the weight load folds away (RMSNorm gains into the following matrices;
+    action_in and its bias into a [720, 32] matrix and the bias of time_in; the time-embedding
+    half of time_in into one time vector per step, which stands in for time_in.b), plus each
+    layer's valid prefix K/V; flops 2 per multiply-add per chunk row for every matrix as the
+    loop applies it (the folded [720, 32] matrix for action_in and the action half of time_in),
+    attention over the unmasked keys."""
+    rows = B * synth.CHUNK
+    el = fl = 0
+    for name, shape, kind in synth.manifest(L):
+        if kind == "g" or name.startswith("action_in."):
+            continue
+        n = int(np.prod(shape))
+        if name == "time_in.w":
+            out_, _ = shape
+            el += out_ * synth.ACTION_DIM      # the folded [720, 32] matrix
+            fl += 2 * rows * out_ * synth.ACTION_DIM
+            continue
+        el += n
+        if kind == "w":
+            fl += 2 * rows * n
+    kv = L * 5 * 64 * 2 * 2 * sum(lengths)
+    C = synth.CHUNK
+    for nb in lengths:
+        for l in range(L):
+            keys = C * nb + (C * (C + 1) // 2 if synth.is_self_layer(l) else 0)
+            fl += 15 * keys * 4 * 64
+    return n_steps * (2 * el + kv), n_steps * fl
+
+
+def test_denoise_counts_match_a_recount_from_the_manifest():
+    for L, B, lengths in ((16, 1, [177]), (16, 64, [257] * 64), (4, 16, list(range(150, 166))), (2, 3, [70, 0, 1])):
+        byt, fl = bench.loop_algorithmic(L, B, lengths, 10)
+        rb, rf = _recount_denoise(L, B, lengths, 10)
+        assert byt == rb and abs(fl - rf) <= 1e-9 * rf, (L, B, byt, rb, fl, rf)
+    # per step at batch 1, prefix 177: 194.3 MB of parameters and 3.6 MB of valid K/V
+    byt, _ = bench.loop_algorithmic(16, 1, [177], 1)
+    assert byt == 2 * 97_149_632 + 16 * 1280 * 177
