@@ -212,18 +212,30 @@ def roofline_of(bytes_, flops, seconds):
 
 def kernel_table(fm, h, cfg, L, B, lengths, P, reps):
     """Per timed kernel: the hook's HIP-event time per launch (one graph of `reps` launches,
-    each repeating that kernel's launch of the next layer in the first step of the last call),
-    launches per call, and the launch's algorithmic bytes, activation bytes and flops."""
-    costs, per_step = kernel_costs(L, B, lengths, P)
+    each repeating that kernel's launch of the next layer, and of the next query group, in the
+    first step of the last call), launches per call, and the launch's algorithmic bytes,
+    activation bytes and flops (averaged over the call's query groups, which the library runs
+    as concurrent chains of launches)."""
+    groups = fm.smolexp_batch_groups(cfg, B)
+    tot, launches = {}, {}
+    b0 = 0
+    for bg in groups:
+        costs, per_step = kernel_costs(L, bg, lengths[b0:b0 + bg], P)
+        b0 += bg
+        for name, n in per_step.items():
+            t = tot.setdefault(name, [0.0, 0.0, 0.0])
+            for i in range(3):
+                t[i] += costs[name][i] * n
+            launches[name] = launches.get(name, 0) + n
     kern = {}
     for name, kid in KERNEL_IDS.items():
-        if name not in per_step:  # not launched at this batch (folded into another kernel)
+        if name not in launches:  # not launched at this batch (folded into another kernel)
             continue
         us = fm.smolexp_time_kernel(h, kid, reps)
-        byt, act, fl = costs[name]
-        n = per_step[name] * cfg.n_steps
-        kern[name] = {"avg_us": us, "launches_per_call": n, "us_per_call": us * n, "bytes": byt,
-                      "activation_bytes": act, "flops": fl}
+        n = launches[name]
+        byt, act, fl = (v / n for v in tot[name])
+        kern[name] = {"avg_us": us, "launches_per_call": n * cfg.n_steps, "us_per_call": us * n * cfg.n_steps,
+                      "bytes": byt, "activation_bytes": act, "flops": fl}
     return kern
 
 
@@ -293,7 +305,8 @@ def large_batch_entry(fm, h, cfg, wl, calls, warmup, reps, stream):
     kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, reps)
     dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
     dom = kern[dom_name]
-    e = {"batch": B, "prefix_len": P, "overwrite_rows": d, "calls": calls, "ms_per_call": med,
+    e = {"batch": B, "prefix_len": P, "overwrite_rows": d, "query_groups": fm.smolexp_batch_groups(cfg, B),
+         "calls": calls, "ms_per_call": med,
          "ms_per_call_min": min(ms), "ms_per_call_max": max(ms), "chunks_per_s": B / (med * 1e-3),
          "loop_algorithmic_flops_per_call": lf, "loop_algorithmic_bytes_per_call": lb,
          "loop_tflops": lf / (med * 1e-3) / 1e12, "loop_mfma_frac": lf / (med * 1e-3) / (MFMA_F16_PEAK_TFS * 1e12),
@@ -565,6 +578,8 @@ def main():
                     help="only the workload's own line: no large-batch block and no overwrite difference")
     ap.add_argument("--large-calls", type=int, default=20, help="timed calls per large-batch workload")
     ap.add_argument("--large-kernel-reps", type=int, default=20)
+    ap.add_argument("--batch-groups", type=int, default=0,
+                    help="concurrent query groups per call (0: the library's automatic choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement, copy 256 MiB device-to-device three times (HBM counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
@@ -593,7 +608,7 @@ def main():
     wl = synth.make_workload(args.workload)
     L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
     cfg = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps, max_batch=B, max_prefix=P,
-                                    use_graphs=0 if args.no_graphs else 1)
+                                    use_graphs=0 if args.no_graphs else 1, batch_groups=args.batch_groups)
     h = fm.smolexp_create(cfg, 0)
     packed = synth.pack_weights(wl["weights"], L)
     fm.smolexp_load_weights(h, packed)
@@ -663,7 +678,7 @@ def main():
         "data": "synthetic (seeded: weights N(0,0.02) bf16, prefix K/V N(0,1) bf16, noise N(0,1))",
         "config": {"workload": args.workload, "n_layers": L, "batch": B, "prefix_len": P,
                    "n_steps": cfg.n_steps, "chunk": 50, "action_dim": 32, "overwrite_rows": d,
-                   "graphs": not args.no_graphs},
+                   "graphs": not args.no_graphs, "query_groups": fm.smolexp_batch_groups(cfg, B)},
         "roofline": roof,
         "loop_roofline": loop,
         "kernels": kern,
@@ -685,7 +700,8 @@ def main():
         big = [synth.make_workload(n, with_weights=False) for n in LARGE_BATCH_WORKLOADS]
         cfg2 = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps,
                                          max_batch=max(w["batch"] for w in big),
-                                         max_prefix=max(w["prefix_len"] for w in big))
+                                         max_prefix=max(w["prefix_len"] for w in big),
+                                         batch_groups=args.batch_groups)
         h2 = fm.smolexp_create(cfg2, 0)
         fm.smolexp_load_weights(h2, packed)
         line["large_batch"] = {}

@@ -34,7 +34,7 @@ class smolexp_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
                                              "chunk", "action_dim", "n_steps", "max_batch", "max_prefix")] + \
                [(n, ctypes.c_float) for n in ("rope_theta", "rms_eps", "t_min_period", "t_max_period")] + \
-               [("use_graphs", ctypes.c_int)]
+               [("use_graphs", ctypes.c_int), ("batch_groups", ctypes.c_int)]
 
 
 class smolexp_denoise_opts(ctypes.Structure):
@@ -49,6 +49,8 @@ _sig = {
     "smolexp_weight_count": (ctypes.c_size_t, [ctypes.POINTER(smolexp_config)]),
     "smolexp_schedule": (ctypes.c_int, [ctypes.POINTER(smolexp_config), ctypes.POINTER(ctypes.c_float),
                                         ctypes.POINTER(ctypes.c_float)]),
+    "smolexp_batch_groups": (ctypes.c_int, [ctypes.POINTER(smolexp_config), ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_int)]),
     "smolexp_create": (ctypes.c_int, [ctypes.POINTER(smolexp_config), ctypes.c_int, ctypes.POINTER(_H)]),
     "smolexp_load_weights": (ctypes.c_int, [_H, _P, ctypes.c_size_t]),
     "smolexp_denoise": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P]),
@@ -122,6 +124,14 @@ def smolexp_schedule(cfg):
     dt = ctypes.c_float()
     _check(_lib.smolexp_schedule(ctypes.byref(cfg), t, ctypes.byref(dt)), what="smolexp_schedule")
     return [t[i] for i in range(cfg.n_steps)], dt.value
+
+
+def smolexp_batch_groups(cfg, batch):
+    """Queries per concurrent group of a call with `batch` queries (host only)."""
+    sizes = (ctypes.c_int * 8)()
+    n = _lib.smolexp_batch_groups(ctypes.byref(cfg), int(batch), sizes)
+    _check(min(n, 0), what="smolexp_batch_groups")
+    return [sizes[i] for i in range(n)]
 
 
 def smolexp_create(cfg, hip_device=0):

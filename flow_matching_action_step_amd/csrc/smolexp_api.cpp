@@ -90,6 +90,10 @@ struct smolexp_handle {
 
   hipStream_t cap = nullptr;
   std::vector<GraphEntry> graphs;
+  // large batches: side streams (default priority) of the query groups, and their
+  // fork / join events
+  std::vector<hipStream_t> grp_streams;
+  std::vector<hipEvent_t> grp_ev;
   uint64_t tick = 0;
 
   bool have_last = false;
@@ -153,6 +157,7 @@ bool check_config(const smolexp_config* c, std::string* why) {
   if (c->n_steps < 1 || c->n_steps > kMaxSteps) { *why = "n_steps must be 1..64"; return false; }
   if (c->max_batch < 1 || c->max_batch > 1024) { *why = "max_batch must be 1..1024"; return false; }
   if (c->max_prefix < 1 || c->max_prefix > 4096) { *why = "max_prefix must be 1..4096"; return false; }
+  if (c->batch_groups < 0 || c->batch_groups > 8) { *why = "batch_groups must be 0..8"; return false; }
   if (!(c->rope_theta > 0.f) || !(c->rms_eps > 0.f) || !(c->t_min_period > 0.f) ||
       !(c->t_max_period > c->t_min_period) || !isfinite(c->rope_theta) || !isfinite(c->t_max_period)) {
     *why = "rope_theta, rms_eps and 0 < t_min_period < t_max_period must be finite and positive";
@@ -308,9 +313,46 @@ CallKey key_of(const CallArgs& c) {
   return k;
 }
 
-// The launch sequence of one call, on the per-call workspace w.
-int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool record_probes) {
-  const int B = c.B, M = B * kChunk, P = c.P, L = h->cfg.n_layers;
+// Queries per group of a call (the groups' loops run concurrently): `batch_groups` groups
+// when the config sets it, else groups of at least 64 queries (B / 64 of them); every group
+// but the last holds a multiple of 8 queries (whole 16-row blocks of the blocked operands).
+// Measured (16 layers, 10 steps): batch 128 at prefix 177 takes 27.0 ms as one chain, 23.9 ms
+// as two groups of 64, 30.2 ms as four of 32; batch 64 at prefix 257 16.5 ms as one chain,
+// 16.9 ms as two groups of 32 (whose 1600-row products run less efficient kernels), 21.1 ms
+// as four.  Returns the count.
+constexpr int kMaxGroups = 8;
+int group_sizes(const smolexp_config& cfg, int B, int* sz) {
+  int G = cfg.batch_groups > 0 ? cfg.batch_groups : (B >= 128 ? B / 64 : 1);
+  G = G < kMaxGroups ? G : kMaxGroups;
+  auto base_of = [&](int g) { return ((B + g - 1) / g + 7) / 8 * 8; };
+  int base = base_of(G);
+  while (G > 1 && (G - 1) * base >= B) base = base_of(--G);
+  for (int i = 0; i < G - 1; ++i) sz[i] = base;
+  sz[G - 1] = B - (G - 1) * base;
+  return G;
+}
+
+int ensure_group_streams(smolexp_t h, int G) {
+  while ((int)h->grp_streams.size() < G - 1) {
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+      return fail(h, SMOLEXP_E_HIP, "group stream creation failed");
+    h->grp_streams.push_back(st);
+  }
+  while ((int)h->grp_ev.size() < G) {
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+      return fail(h, SMOLEXP_E_HIP, "group event creation failed");
+    h->grp_ev.push_back(ev);
+  }
+  return SMOLEXP_OK;
+}
+
+// The launch sequence of one call, on the per-call workspace w.  may_fork = false keeps
+// every launch on s (one group), as the no-alloc entry point needs.
+int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool record_probes,
+            bool may_fork = true) {
+  const int B = c.B, P = c.P, L = h->cfg.n_layers;
   const int n_t = c.velocity ? 1 : h->cfg.n_steps;
   // time vectors: the schedule's were computed when the weights were loaded; a velocity
   // call computes its own (one t) into the row after them
@@ -321,7 +363,6 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     h->probe_key = key_of(c);
     h->have_probe = true;
   }
-  bool first_step = true;  // probes are recorded in the first step only
 
   PrologueArgs pa;
   memset(&pa, 0, sizeof(pa));
@@ -343,6 +384,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
 
   const size_t kvLayer = (size_t)2 * B * kHKV * (size_t)P * kHD;  // elements per layer
   const bf16_t* kv = static_cast<const bf16_t*>(c.kv);
+  bool first_step = true;  // probes are recorded in the first step only
   auto record = [&](int probe, const GemmPlan& plan, AMode am, EMode em, const GemmArgs& g) {
     if (record_probes && first_step && probe >= 0) {
       smolexp_handle::Probe p;
@@ -351,111 +393,161 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
       h->probes[probe].push_back(p);
     }
   };
-  // every projection: the planned kernel (plan_for); RMSNorm'd projections (Q/K/V,
-  // gate/up, action_out) read h16 = fp16(h), over the zero-padded K = 768 on the pipelined GEMM
-  auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
-    GemmArgs g = g0;
-    if (am == A_NORM) { g.A = w.h16; g.lda = kKPad; }
-    const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em);
-    if (plan.kind == 2) {
-      if (am == A_NORM) g.K = kKPad;
+
+  // The loop of one group of queries: rows b0 * 50 .. (b0 + Bg) * 50 - 1 of every workspace
+  // buffer (b0 is a multiple of 8, so the blocked operands start on a 16-row block), the
+  // group's slices of the prefix cache, mask, noise and outputs, on stream gs.
+  auto run_group = [&](int b0, int Bg, hipStream_t gs) -> int {
+    const int Mg = Bg * kChunk, r0 = b0 * kChunk;
+    CallWs wg = w;
+    wg.x = w.x + (size_t)r0 * kAD;
+    wg.h = w.h + (size_t)r0 * kD;
+    wg.s16 = w.s16 + (size_t)r0 * kD;
+    wg.o16 = w.o16 + (size_t)r0 * kNQ;
+    wg.u16 = w.u16 + (size_t)r0 * kFFN;
+    wg.h16 = w.h16 + (size_t)r0 * kKPad;
+    wg.q = w.q + (size_t)r0 * kNQ;
+    wg.kc = w.kc + (size_t)r0 * kNKV;
+    wg.vc = w.vc + (size_t)r0 * kNKV;
+    wg.ropeq = w.ropeq + (size_t)r0 * (kHD / 2);
+    const size_t qOff = (size_t)r0 * kAD;                        // [b][50][32] arrays
+    const size_t kvOff = (size_t)b0 * kHKV * (size_t)P * kHD;    // inside each layer's K and V
+    const uint8_t* mask_g = c.mask + (size_t)b0 * P;
+    // every projection: the planned kernel (plan_for); RMSNorm'd projections (Q/K/V,
+    // gate/up, action_out) read h16 = fp16(h), over the zero-padded K = 768 on the pipelined GEMM
+    auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
+      GemmArgs g = g0;
+      if (am == A_NORM) { g.A = wg.h16; g.lda = kKPad; }
+      const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em);
+      if (plan.kind == 2) {
+        if (am == A_NORM) g.K = kKPad;
+        record(probe, plan, am, em, g);
+        return launch_gemm_big(plan, em, am == A_NORM, g, gs);
+      }
       record(probe, plan, am, em, g);
-      return launch_gemm_big(plan, em, am == A_NORM, g, s);
+      return launch_gemm(plan, am, em, g, gs);
+    };
+    auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t { return gemm(probe, A_NORM, em, g); };
+    hipError_t e;
+    for (int k = 0; k < n_t; ++k) {
+      first_step = k == 0;
+      const float t = c.velocity ? c.t_single : h->ts[k];
+      GemmArgs g;
+      memset(&g, 0, sizeof(g));
+      g.M = Mg;
+      g.inv_k = 1.0f / kD;
+      g.eps = h->cfg.rms_eps;
+
+      // action_in + time MLP, first layer: s = SiLU(W_t1[:, :720] (W_in x + b_in) + W_t1[:, 720:] e(t)
+      // + b_t1), computed as (W_t1[:, :720] W_in) x + the step's time vector (whose bias holds
+      // W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read and stored back
+      // into the state.  Then h = W_t2 s + b_t2.
+      GemmArgs gt = g;
+      gt.N = kD; gt.K = kAD; gt.A = wg.x; gt.lda = kAD;
+      gt.x = wg.x; gt.noise = c.x_in + qOff; gt.prev = c.prev ? c.prev + (size_t)b0 * c.d * kAD : nullptr;
+      gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
+      gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
+      gt.out16 = wg.s16; gt.ldo = kD;
+      if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
+
+      GemmArgs go = g;
+      go.N = kD; go.K = kD; go.A = wg.s16; go.lda = kD;
+      go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
+      go.h = wg.h; go.h16 = wg.h16;
+      if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
+
+      for (int l = 0; l < L; ++l) {
+        const LayerDev& ld = h->layers[l];
+        // cross layers of a small batch: the Q projection runs inside the attention launch
+        const bool fold_q = !ld.self_attn && use_cross_q(Bg);
+        if (!fold_q) {
+          GemmArgs gq = g;
+          gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
+          gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
+          gq.q = wg.q; gq.kc = wg.kc; gq.vc = wg.vc; gq.ropeq = wg.ropeq;
+          if ((e = norm_gemm(ld.self_attn ? PR_QKV : PR_QCROSS, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
+        }
+
+        AttnArgs aa;
+        memset(&aa, 0, sizeof(aa));
+        aa.q = wg.q; aa.kc = wg.kc; aa.vc = wg.vc;
+        aa.pk = kv + (size_t)l * kvLayer + kvOff;
+        aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2 + kvOff;
+        aa.mask = mask_g; aa.out = wg.o16; aa.B = Bg; aa.P = P;
+        if (fold_q) {
+          aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale;
+          aa.h16 = wg.h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = wg.ropeq;
+        }
+        const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
+        if (record_probes && first_step) {
+          smolexp_handle::Probe p;
+          memset(&p, 0, sizeof(p));
+          p.attn = true; p.a = aa;
+          h->probes[pr].push_back(p);
+        }
+        if ((e = launch_attention(ld.self_attn, aa, gs)) != hipSuccess) return hip_fail(h, e, "attention launch");
+
+        GemmArgs gop = g;
+        gop.N = kD; gop.K = kNQ; gop.A = wg.o16; gop.lda = kNQ;
+        gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = wg.h; gop.h16 = wg.h16;
+        if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
+
+        GemmArgs gg = g;
+        gg.N = kGU; gg.K = kD;
+        gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = wg.u16; gg.ldo = kFFN;
+        if ((e = norm_gemm(PR_GU, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
+
+        GemmArgs gd = g;
+        gd.N = kD; gd.K = kFFN; gd.A = wg.u16; gd.lda = kFFN;
+        gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = wg.h; gd.h16 = wg.h16;
+        if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
+      }
+
+      // final RMSNorm + action_out; Euler update x += dt v
+      GemmArgs gv = g;
+      gv.N = kAD; gv.K = kD;
+      gv.W = h->w_out.w; gv.ldw = h->w_out.ld; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
+      gv.x = wg.x; gv.dt = h->dt;
+      const size_t stepElems = (size_t)B * kChunk * kAD;
+      if (c.velocity) {
+        gv.vel_out = c.out + qOff;
+      } else {
+        gv.vel_out = c.vel ? c.vel + (size_t)k * stepElems + qOff : nullptr;
+        gv.st_out = c.st ? c.st + (size_t)k * stepElems + qOff : nullptr;
+        gv.final_out = (k == n_t - 1) ? c.out + qOff : nullptr;
+      }
+      if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
     }
-    record(probe, plan, am, em, g);
-    return launch_gemm(plan, am, em, g, s);
+    return SMOLEXP_OK;
   };
-  auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t { return gemm(probe, A_NORM, em, g); };
 
-  for (int k = 0; k < n_t; ++k) {
-    const float t = c.velocity ? c.t_single : h->ts[k];
-    GemmArgs g;
-    memset(&g, 0, sizeof(g));
-    g.M = M;
-    g.inv_k = 1.0f / kD;
-    g.eps = h->cfg.rms_eps;
-
-    // action_in + time MLP, first layer: s = SiLU(W_t1[:, :720] (W_in x + b_in) + W_t1[:, 720:] e(t)
-    // + b_t1), computed as (W_t1[:, :720] W_in) x + the step's time vector (whose bias holds
-    // W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read and stored back
-    // into the state.  Then h = W_t2 s + b_t2.
-    GemmArgs gt = g;
-    gt.N = kD; gt.K = kAD; gt.A = w.x; gt.lda = kAD;
-    gt.x = w.x; gt.noise = c.x_in; gt.prev = c.prev; gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
-    gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
-    gt.out16 = w.s16; gt.ldo = kD;
-    if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
-
-    GemmArgs go = g;
-    go.N = kD; go.K = kD; go.A = w.s16; go.lda = kD;
-    go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
-    go.h = w.h; go.h16 = w.h16;
-    if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
-
-    for (int l = 0; l < L; ++l) {
-      const LayerDev& ld = h->layers[l];
-      // cross layers of a small batch: the Q projection runs inside the attention launch
-      const bool fold_q = !ld.self_attn && use_cross_q(B);
-      if (!fold_q) {
-        GemmArgs gq = g;
-        gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
-        gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
-        gq.q = w.q; gq.kc = w.kc; gq.vc = w.vc; gq.ropeq = w.ropeq;
-        if ((e = norm_gemm(ld.self_attn ? PR_QKV : PR_QCROSS, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
-      }
-
-      AttnArgs aa;
-      memset(&aa, 0, sizeof(aa));
-      aa.q = w.q; aa.kc = w.kc; aa.vc = w.vc;
-      aa.pk = kv + (size_t)l * kvLayer;
-      aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2;
-      aa.mask = c.mask; aa.out = w.o16; aa.B = B; aa.P = P;
-      if (fold_q) {
-        aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale;
-        aa.h16 = w.h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = w.ropeq;
-      }
-      const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
-      if (record_probes && first_step) {
-        smolexp_handle::Probe p;
-        memset(&p, 0, sizeof(p));
-        p.attn = true; p.a = aa;
-        h->probes[pr].push_back(p);
-      }
-      if ((e = launch_attention(ld.self_attn, aa, s)) != hipSuccess) return hip_fail(h, e, "attention launch");
-
-      GemmArgs gop = g;
-      gop.N = kD; gop.K = kNQ; gop.A = w.o16; gop.lda = kNQ;
-      gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = w.h; gop.h16 = w.h16;
-      if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
-
-      GemmArgs gg = g;
-      gg.N = kGU; gg.K = kD;
-      gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = w.u16; gg.ldo = kFFN;
-      if ((e = norm_gemm(PR_GU, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
-
-      GemmArgs gd = g;
-      gd.N = kD; gd.K = kFFN; gd.A = w.u16; gd.lda = kFFN;
-      gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = w.h; gd.h16 = w.h16;
-      if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
-    }
-
-    // final RMSNorm + action_out; Euler update x += dt v
-    GemmArgs gv = g;
-    gv.N = kAD; gv.K = kD;
-    gv.W = h->w_out.w; gv.ldw = h->w_out.ld; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
-    gv.x = w.x; gv.dt = h->dt;
-    const size_t stepElems = (size_t)B * kChunk * kAD;
-    if (c.velocity) {
-      gv.vel_out = c.out;
-    } else {
-      gv.vel_out = c.vel ? c.vel + (size_t)k * stepElems : nullptr;
-      gv.st_out = c.st ? c.st + (size_t)k * stepElems : nullptr;
-      gv.final_out = (k == n_t - 1) ? c.out : nullptr;
-    }
-    if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
-    first_step = false;
+  // Large batches run as groups of queries whose loops are independent chains of launches:
+  // the groups after the first fork onto side streams after the prologue (parallel branches
+  // of the captured graph) and join the call's stream at the end, so each group's launches
+  // fill the CUs that another group's launch leaves idle.
+  int gsz[kMaxGroups];
+  int G = group_sizes(h->cfg, B, gsz);
+  if (!may_fork) {
+    G = 1;
+    gsz[0] = B;
   }
-  return SMOLEXP_OK;
+  if (G > 1) {
+    const int rc0 = ensure_group_streams(h, G);
+    if (rc0 != SMOLEXP_OK) return rc0;
+    if ((e = hipEventRecord(h->grp_ev[0], s)) != hipSuccess) return hip_fail(h, e, "group fork");
+    for (int gi = 1; gi < G; ++gi)
+      if ((e = hipStreamWaitEvent(h->grp_streams[gi - 1], h->grp_ev[0], 0)) != hipSuccess) return hip_fail(h, e, "group fork");
+  }
+  int rc = SMOLEXP_OK;
+  for (int gi = 0, b0 = 0; gi < G && rc == SMOLEXP_OK; b0 += gsz[gi], ++gi)
+    rc = run_group(b0, gsz[gi], gi == 0 ? s : h->grp_streams[gi - 1]);
+  // join every side stream, also after an error, so no group outlives the call's stream
+  for (int gi = 1; gi < G; ++gi) {
+    hipError_t ej = hipEventRecord(h->grp_ev[gi], h->grp_streams[gi - 1]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(s, h->grp_ev[gi], 0);
+    if (ej != hipSuccess && rc == SMOLEXP_OK) rc = hip_fail(h, ej, "group join");
+  }
+  return rc;
 }
 
 void drop_graphs(smolexp_t h) {
@@ -637,6 +729,16 @@ size_t smolexp_weight_count(const smolexp_config* cfg) {
   std::string why;
   if (!check_config(cfg, &why)) return 0;
   return count_weights(cfg->n_layers);
+}
+
+int smolexp_batch_groups(const smolexp_config* cfg, int batch, int* sizes) {
+  std::string why;
+  if (!check_config(cfg, &why) || batch < 1 || batch > cfg->max_batch) return SMOLEXP_E_INVAL;
+  int sz[kMaxGroups];
+  const int G = group_sizes(*cfg, batch, sz);
+  if (sizes)
+    for (int i = 0; i < G; ++i) sizes[i] = sz[i];
+  return G;
 }
 
 int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out) {
@@ -1107,7 +1209,7 @@ int smolexp_denoise_noalloc(smolexp_t h, const void* prefix_kv, const uint8_t* p
   memset(&c, 0, sizeof(c));
   c.velocity = false;
   c.kv = prefix_kv; c.mask = prefix_mask; c.P = prefix_len; c.x_in = noise; c.out = out_actions; c.B = batch;
-  return enqueue(h, c, w, s, false);
+  return enqueue(h, c, w, s, false, false);
 }
 
 int smolexp_velocity(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask, int prefix_len,
@@ -1226,6 +1328,8 @@ void smolexp_destroy(smolexp_t h) {
   (void)hipDeviceSynchronize();
   drop_graphs(h);
   if (h->cap) (void)hipStreamDestroy(h->cap);
+  for (auto st : h->grp_streams) (void)hipStreamDestroy(st);
+  for (auto ev : h->grp_ev) (void)hipEventDestroy(ev);
   if (h->wmem) (void)hipFree(h->wmem);
   if (h->wsmem) (void)hipFree(h->wsmem);
   if (h->lmem) (void)hipFree(h->lmem);

@@ -70,6 +70,13 @@ typedef struct smolexp_config {
   float t_min_period;
   float t_max_period;
   int use_graphs;    /* 1: capture each call's launch sequence once and replay it as a HIP graph */
+  int batch_groups;  /* 0..8: a call's queries run as this many groups whose loops proceed
+                        concurrently (on side streams of default priority, or as parallel
+                        branches of the graph); 0 = automatic (groups of at least 64
+                        queries: batch / 64 of them from 128 queries on).
+                        Every group but the last holds a multiple of 8 queries.  The results
+                        of a query depend on the size of its group only within the tolerances,
+                        as for any change of batch composition. */
 } smolexp_config;
 
 /* Fill *cfg with the SmolVLA expert (16 layers, 10 steps, max_batch 128, max_prefix 512). Host only. */
@@ -89,6 +96,14 @@ size_t smolexp_weight_count(const smolexp_config* cfg);
  * cfg->n_steps floats; dt_out may be NULL.
  */
 int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out);
+
+/*
+ * How a call of `batch` queries is split into concurrent groups (cfg->batch_groups):
+ * returns the number of groups (1..8) and, when sizes is not NULL, writes the queries of
+ * each group in call order (sizes has room for 8).  SMOLEXP_E_INVAL for an invalid cfg or
+ * batch outside 1..max_batch.  Host only; needs no GPU.
+ */
+int smolexp_batch_groups(const smolexp_config* cfg, int batch, int* sizes);
 
 /*
  * Create a handle on HIP device hip_device: validates cfg, allocates the

@@ -339,3 +339,51 @@ def test_time_kernel_hook(ex4):
     us = ctypes.c_float()
     assert fm.raw().smolexp_time_kernel(ex4.h, fm.K_Q_CROSS, 3, None, ctypes.byref(us)) == fm.SMOLEXP_E_STATE
     assert fm.raw().smolexp_time_kernel(ex4.h, 11, 3, None, ctypes.byref(us)) == fm.SMOLEXP_E_INVAL
+
+
+def test_query_groups_run_both_kernel_paths_in_one_call():
+    """A batch of 20 split into concurrent groups of 16 and 4 queries (batch_groups = 2): the
+    first group takes the larger-batch kernels (streamed attention, cross-layer Q projection as
+    its own launch), the second the small-batch ones (Q folded into cross attention), in one
+    call, with ragged prefixes and a 5-row prefix overwrite; queries from both groups against
+    the oracle, a teacher-forced velocity of a second-group query, and bitwise repeatability."""
+    _say("4 layers, batch 20 as query groups of 16 and 4")
+    ex = Expert(4, max_batch=20, max_prefix=160)
+    try:
+        cfg = fm.smolexp_default_config(n_layers=4, max_batch=20, max_prefix=160, batch_groups=2)
+        assert fm.smolexp_batch_groups(cfg, 20) == [16, 4]
+        h = fm.smolexp_create(cfg, 0)
+        try:
+            fm.smolexp_load_weights(h, synth.pack_weights(ex.named, 4))
+            ex2 = object.__new__(Expert)
+            ex2.cfg, ex2.h, ex2.W, ex2.ocfg, ex2.named = cfg, h, ex.W, ex.ocfg, ex.named
+            B, P, d = 20, 160, 5
+            wl = synth.make_workload("expert4_b1_p177", batch=B, with_weights=False)
+            wl["prefix_len"] = P
+            wl["prefix_kv"] = synth.draw_prefix_kv(4, B, P, seed=61)
+            lengths = [160, 7, 99, 160, 1, 150, 33, 80, 120, 64, 65, 128, 129, 2, 159, 100, 160, 17, 140, 88]
+            wl["lengths"] = np.array(lengths)
+            wl["mask"] = synth.make_mask(B, P, lengths)
+            wl["prev_actions"] = synth.draw_prev_actions(B, d)
+            dev = to_device(wl)
+            gpu = run_gpu(ex2, dev, d=d)
+            q = [0, 4, 15, 16, 17, 19]
+            compare(gpu, run_oracle(ex2, wl, q, d=d), q, wl["noise"], "query groups 16 + 4", d=d)
+            again = run_gpu(ex2, dev, d=d)
+            np.testing.assert_array_equal(again["out"], gpu["out"])
+            # one velocity evaluation at t = 0.6 of every query, checked on a second-group query
+            x = torch.from_numpy(gpu["st"][3]).cuda()
+            v = torch.empty_like(x)
+            fm.smolexp_velocity(h, cfg, dev["kv"], dev["mask"], x, 0.6, v)
+            torch.cuda.synchronize()
+            b = 17
+            want = oracle.velocity(ex.W, ex.ocfg, gpu["st"][3][b].astype(np.float64), np.float32(0.6),
+                                   oracle.bf16_bits_to_float(wl["prefix_kv"][:, 0, b]),
+                                   oracle.bf16_bits_to_float(wl["prefix_kv"][:, 1, b]), wl["mask"][b].astype(bool))
+            rel = np.linalg.norm(v.cpu().numpy()[b] - want) / np.linalg.norm(want)
+            print(f"[parity] query groups: velocity of query {b} at t = 0.6: rel {rel:.3e}", flush=True)
+            assert rel <= VEL_RTOL
+        finally:
+            fm.smolexp_destroy(h)
+    finally:
+        ex.close()
