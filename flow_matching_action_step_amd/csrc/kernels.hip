@@ -542,6 +542,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p;
   const int nks = (K + 31) / 32;
+  p.reg = 0;
   p.bm = 64;
   p.rb = 4;
   p.cb = 1;
@@ -644,6 +645,44 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 }
 
 
+// Epilogue of a transposed accumulator tile (the weight fragment as the MFMA's first operand),
+// for the residual projections: lane l of a wave holds, for each of its FMW x FN fragments, row
+// r0 + 16 fm + l % 16 and the four consecutive columns c0 + 16 fn + 4 (l / 16) .. + 3, which is
+// one 16-byte unit of the fp32 residual's 16 x 4 micro-tiles (and half of an 8-column chunk of
+// its fp16 copy), so the sums go to memory from the registers (nontemporal stores) without
+// staging the tile in LDS.  Measured against the staged epilogue, weights cycling through 256
+// MB: o at 3200 rows 13.1 -> 12.4 us, down 23.5 -> 22.9, at 6400 rows 23.9 -> 22.5 and 38.0 ->
+// 36.6; below 3200 rows and for the Q/K/V scatter (bf16 rows of 128 bytes, 27.6 against 18.4
+// us) and the SwiGLU output (equal) the staged epilogue is kept.  rs: the scale of the lane's
+// row in each row fragment.  PRE: the residual values were loaded before the main loop,
+// pre[fm FN + fn].  Swapping the operands changes the rounding of a few fp32 sums (the
+// matrix cores add the 32 products of a k-step in an order that depends on the operand
+// roles), so the result equals the staged kernel's up to rounding, not bit for bit.
+template <int FMW, int FN, bool PRE>
+__device__ __forceinline__ void epilogue_regs_resid(const GemmArgs& a, const f32x4 (&acc)[FMW][FN],
+                                                    const float (&rs)[FMW], int r0, int c0, int lane,
+                                                    const float4* pre) {
+  const int M = a.M, N = a.N;
+#pragma unroll
+  for (int fm = 0; fm < FMW; ++fm) {
+    const int row = r0 + fm * 16 + (lane & 15);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = c0 + fn * 16 + 4 * (lane >> 4);
+      if (row < M && col < N) {
+        float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, kD / 4));
+        const float4 hv = PRE ? pre[fm * FN + fn] : *hp;
+        const float4 o = make_float4(hv.x + acc[fm][fn][0] * rs[fm], hv.y + acc[fm][fn][1] * rs[fm],
+                                     hv.z + acc[fm][fn][2] * rs[fm], hv.w + acc[fm][fn][3] * rs[fm]);
+        st_out<true>(hp, o);
+        union { half_t e[4]; uint2 u; } o16;
+        o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
+        st_out<true>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)), o16.u);
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Large-M GEMM with a multi-stage LDS pipeline
 // ----------------------------------------------------------------------------
@@ -663,13 +702,14 @@ constexpr int kBigBN = 128, kBigBK = 64;
 // Column groups of the tile -> XCD map (the rows are cut into 8 / GC groups).
 __host__ __device__ constexpr int tile_col_groups(int em) { return em == E_SWIGLU ? 4 : 1; }
 
-template <int EM, bool NORM, int BM, int FMW, int WN, int S>
+template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG>
 __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const GemmArgs a) {
   constexpr int BN = kBigBN, BK = kBigBK, LDC = BN + 4;
   constexpr int WM = BM / (16 * FMW), NW = WM * WN, FN = BN / 16 / WN;
   static_assert(WM * 16 * FMW == BM && FN * 16 * WN == BN, "waves tile the block");
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
-  constexpr int SMEM = S * STAGE_BYTES > BM * LDC * 4 ? S * STAGE_BYTES : BM * LDC * 4;
+  // REG: the epilogue runs on the accumulators, the LDS holds only the ring
+  constexpr int SMEM = REG || S * STAGE_BYTES > BM * LDC * 4 ? S * STAGE_BYTES : BM * LDC * 4;
   constexpr int A_LOADS = A_BYTES / 1024 / NW, W_LOADS = W_BYTES / 1024 / NW;  // per wave per stage
   constexpr int LOADS = A_LOADS + W_LOADS;
   static_assert(A_LOADS * NW * 1024 == A_BYTES && W_LOADS * NW * 1024 == W_BYTES, "whole load instructions per wave");
@@ -711,7 +751,18 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   // occupancy (two workgroups per CU, 96 -> 132 VGPRs).
   constexpr bool PRE = (EM == E_H_RESID || EM == E_PF_RESID) && S > 2;
   float4 pre[PRE ? BN / 16 : 1];
-  if constexpr (PRE) {
+  if constexpr (PRE && REG) {
+    // REG mapping: lane l of wave (wm, wn) owns row m0 + (wm FMW + fm) 16 + l % 16 and columns
+    // n0 + (wn FN + fn) 16 + 4 (l / 16) .. + 3 (pre[fm FN + fn])
+    static_assert(FMW * FN <= BN / 16, "preloaded residual registers");
+#pragma unroll
+    for (int fm = 0; fm < FMW; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int row = m0 + (wm * FMW + fm) * 16 + (lane & 15), col = n0 + (wn * FN + fn) * 16 + 4 * (lane >> 4);
+        if (row < M && col < N) pre[fm * FN + fn] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, resid_k4(EM)));
+      }
+  } else if constexpr (PRE) {
     static_assert(BM / 16 <= NW, "one row block per wave");
     const int row = m0 + w * 16 + (lane & 15);
 #pragma unroll
@@ -774,12 +825,16 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
     for (int fn = 0; fn < FN; ++fn)
       bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * FN + fn) * 8 + ch) * 128 + (lane & 15) * 8);
   };
+  // REG: the weight fragment is the MFMA's first operand, so the accumulator tile is C^T and
+  // lane l holds row l % 16 with four consecutive columns 4 (l / 16) .. + 3
   auto mma = [&](const f16x8* af, const f16x8* bw) {
 #pragma unroll
     for (int fm = 0; fm < FMW; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+      for (int fn = 0; fn < FN; ++fn) {
+        if constexpr (REG) acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[fn], af[fm], acc[fm][fn], 0, 0, 0);
+        else acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+      }
     if constexpr (NORM) {
 #pragma unroll
       for (int fm = 0; fm < FMW; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
@@ -815,6 +870,14 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
+  if constexpr (REG) {
+    float rs[FMW];  // the weight scale (no RMSNorm on the residual projections)
+#pragma unroll
+    for (int fm = 0; fm < FMW; ++fm) rs[fm] = a.w_scale;
+    static_assert(EM == E_H_RESID && !NORM, "register epilogue: the residual projections");
+    epilogue_regs_resid<FMW, FN, PRE>(a, acc, rs, m0 + wm * FMW * 16, n0 + wn * FN * 16, lane, pre);
+    return;
+  }
   __syncthreads();
 
   const float ws = a.w_scale;
@@ -835,14 +898,14 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   epilogue_tile<EM, BM, BN, LDC, 64 * NW, PRE, true>(a, sC, m0, n0, pre);
 }
 
-template <int EM, bool NORM, int BM, int FMW, int WN, int S>
+template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG = false>
 static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 64 * (BM / (16 * FMW)) * WN, GC = tile_col_groups(EM), GR = 8 / GC;
   const int nM = (a.M + BM - 1) / BM, nN = (a.N + kBigBN - 1) / kBigBN;
   if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
   // every XCD gets as many workgroups as its largest share of tiles
   const int per = GC == 1 ? (nM * nN + 7) / 8 : ((nN + GC - 1) / GC) * ((nM + GR - 1) / GR);
-  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S>), dim3(8 * per), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S, REG>), dim3(8 * per), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -865,8 +928,10 @@ hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArg
       if (norm) return hipErrorInvalidValue;
       if (p.stages == 4) {
         if (p.bm == 64) return launch_gemm_dma<E_H_RESID, false, 64, 2, 2, 4>(a, s);
+        if (p.reg) return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4, true>(a, s);
         return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4>(a, s);
       }
+      if (p.reg) return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 2, true>(a, s);
       return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 2>(a, s);
     case E_PF_QKV:
       if (!norm) return hipErrorInvalidValue;
@@ -923,7 +988,11 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
         if (M <= 400) return skinny(2, 2);
         if (M <= 2400) return skinny(4, 2);
       }
-      return M <= 4800 ? big(128, 4) : big();
+      {
+        GemmPlan b = M <= 4800 ? big(128, 4) : big();
+        b.reg = M >= 3200;  // the epilogue from the accumulators (see epilogue_regs_resid)
+        return b;
+      }
     case E_ACTOUT:
       if (M <= 2400) return skinny(1, 1);
       return M <= 4800 ? skinny(4, 2) : plan_gemm(M, N, K);

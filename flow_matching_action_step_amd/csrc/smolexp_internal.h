@@ -203,6 +203,7 @@ struct GemmPlan {
   int cb;        // skinny: 16-column blocks per workgroup (1, 2 or 4)
   int stages;    // pipelined: LDS ring depth (2 or 4); bm = tile rows (64 or 128)
   int ntiles_n;  // output tiles (workgroups) along N
+  int reg;       // pipelined: 1 = epilogue from the accumulators (weight fragment as the first MFMA operand)
 };
 GemmPlan plan_gemm(int M, int N, int K);
 
