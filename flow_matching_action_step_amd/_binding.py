@@ -39,7 +39,11 @@ class smolexp_config(ctypes.Structure):
 
 class smolexp_denoise_opts(ctypes.Structure):
     _fields_ = [("prev_actions", ctypes.c_void_p), ("overwrite_rows", ctypes.c_int),
-                ("out_velocities", ctypes.c_void_p), ("out_states", ctypes.c_void_p)]
+                ("out_velocities", ctypes.c_void_p), ("out_states", ctypes.c_void_p),
+                ("out_status", ctypes.c_void_p)]
+
+
+SMOLEXP_RANGE_RESIDUAL, SMOLEXP_RANGE_FFN, SMOLEXP_RANGE_ATTENTION, SMOLEXP_RANGE_TIME = 1, 2, 4, 8
 
 
 _H = ctypes.c_void_p
@@ -156,7 +160,7 @@ def smolexp_denoise(h, cfg, prefix_kv, prefix_mask, noise, out_actions, stream=N
 
 
 def smolexp_denoise_ex(h, cfg, prefix_kv, prefix_mask, noise, out_actions, prev_actions=None,
-                       overwrite_rows=0, out_velocities=None, out_states=None, stream=None):
+                       overwrite_rows=0, out_velocities=None, out_states=None, out_status=None, stream=None):
     """prefix_kv: uint16/bfloat16 [L,2,B,5,P,64]; prefix_mask uint8 [B,P]; noise, out fp32 [B,50,32]."""
     import torch
     B, P = prefix_mask.shape
@@ -175,6 +179,9 @@ def smolexp_denoise_ex(h, cfg, prefix_kv, prefix_mask, noise, out_actions, prev_
         if t is not None:
             _need(t, name, torch.float32, (cfg.n_steps, B, cfg.chunk, cfg.action_dim))
             setattr(opts, name, t.data_ptr())
+    if out_status is not None:
+        _need(out_status, "out_status", torch.int32, (1,))
+        opts.out_status = out_status.data_ptr()
     rc = _lib.smolexp_denoise_ex(h, _ptr(prefix_kv), _ptr(prefix_mask), P, _ptr(noise), _ptr(out_actions), B,
                                  _stream(stream), ctypes.byref(opts))
     _check(rc, h, "smolexp_denoise_ex")

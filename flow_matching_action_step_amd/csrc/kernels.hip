@@ -45,6 +45,21 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// fp32 values of magnitude 65520 and up (and infinities) round to infinity in fp16.  Each
+// thread keeps the largest magnitude it rounds (a running max folds into v_max3 with abs
+// modifiers, which ignore NaN: NaN propagates from the inputs as NaN and is not counted) and
+// tests it once.
+constexpr float kF16Inf = 65520.f;
+__device__ __forceinline__ float absmax4(float m, float a, float b, float c, float d) {
+  return fmaxf(fmaxf(fmaxf(m, fabsf(a)), fmaxf(fabsf(b), fabsf(c))), fabsf(d));
+}
+
+// Report a range overflow seen by this thread (its largest rounded magnitude) to the call's
+// status word.
+__device__ __forceinline__ void report_range(int* status, float vmax, int bit) {
+  if (vmax >= kF16Inf && status) atomicOr(status, bit);
+}
+
 __device__ __forceinline__ uint4 pack8(const float* v) {
   union { half_t h[8]; uint4 u; } p;
 #pragma unroll
@@ -78,7 +93,7 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 // fp16 MFMA operand (ok = inside the matrix; otherwise zeros).
 template <int AM>
 __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool ok, float rscale,
-                                         bool write_x) {
+                                         bool write_x, float& vmax) {
   (void)rscale;
   if constexpr (AM == A_F16 || AM == A_NORM) {
     return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + t16_off(row, k, a.lda >> 3))
@@ -108,6 +123,7 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
       }
     }
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    vmax = absmax4(absmax4(vmax, v[0], v[1], v[2], v[3]), v[4], v[5], v[6], v[7]);
     return pack8(v);
   }
 }
@@ -219,6 +235,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     // 16-column block c of the tile holds gate (8) then up (8) of output chunk c.
     constexpr int NC = EM == E_SWIGLU ? BN / 16 : BN / 8;  // output chunks per tile row
     const int kco = a.ldo >> 3;
+    float vmax = 0.f;
     for (int g = threadIdx.x; g < BM * NC; g += NT) {
       const int r = (g & 15) + 16 * ((g >> 4) / NC), c = (g >> 4) % NC;
       const int row = m0 + r;
@@ -244,8 +261,10 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = silu(z[e]);
       }
+      vmax = absmax4(absmax4(vmax, v[0], v[1], v[2], v[3]), v[4], v[5], v[6], v[7]);
       st_out<NTS>(reinterpret_cast<uint4*>(a.out16 + t16_off(row, col, kco)), pack8(v));
     }
+    report_range(a.status, vmax, EM == E_SWIGLU ? kRangeFfn : kRangeTime);
     return;
   }
   if constexpr (EM == E_H_BIAS || EM == E_H_RESID || EM == E_PF_RESID) {
@@ -255,6 +274,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
     constexpr int NC4 = BN / 4, NWV = NT / 64, RB = BM / 16;
     static_assert(NC4 % 4 == 0 && NT % 64 == 0, "uniform trip counts");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, part = lane >> 4;
+    float vmax = 0.f;
     for (int rb = wv; rb < RB; rb += NWV) {
       const int r = rb * 16 + r16, row = m0 + r;
       const bool live = row < M;
@@ -273,12 +293,14 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
             o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
           }
           st_out<NTS>(hp, o);
+          vmax = absmax4(vmax, o.x, o.y, o.z, o.w);
           union { half_t e[4]; uint2 u; } o16;
           o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
           st_out<NTS>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, resid16_kc(EM))), o16.u);
         }
       }
     }
+    report_range(a.status, vmax, kRangeResidual);
     return;
   }
   if constexpr (EM == E_ACTOUT) {
@@ -356,6 +378,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   }
   uint4 wf[KPW][CB];
   uint4 af[KPW][RB];
+  float xmax = 0.f;  // A_X: the largest magnitude of the Euler state rounded to fp16
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int ks = w * KPW + i, k = ks * 32 + kl;
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     for (int fm = 0; fm < RB; ++fm) {
       const int row = m0 + fm * 16 + (lane & 15);
       const bool ok = kok && row < M;
-      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, nb == 0);
+      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, nb == 0, xmax);
     }
   }
   f32x4 acc[RB][CB];
@@ -420,6 +443,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     sC[i] = s * sc;
   }
   __syncthreads();
+  if constexpr (AM == A_X) report_range(a.status, xmax, kRangeTime);
   epilogue_tile<EM, BM, BN, LDC, 512, PRE>(a, sC, m0, n0, pre);
 }
 
@@ -452,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
   const int nk = (K + BK - 1) / BK;
 
   uint4 ra[GA], rw[GW];
+  float xmax = 0.f;  // A_X: the largest magnitude of the Euler state rounded to fp16
   // piece g of a tile: row (g / 128) * 16 + g % 16, chunk (g / 16) % 8
   auto prow = [](int g) { return ((g >> 7) << 4) | (g & 15); };
   auto pcol = [](int g) { return ((g >> 4) & (CPR - 1)) * 8; };
@@ -461,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
     for (int i = 0; i < GA; ++i) {
       const int g = tid + 256 * i, row = m0 + prow(g), k = kb + pcol(g);
       const bool ok = row < M && k < K;
-      ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0);
+      ra[i] = load_a8<AM>(a, row, k, ok, 1.f, nt == 0, xmax);
     }
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
@@ -536,6 +561,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {
       for (int fn = 0; fn < 4; ++fn) sC[rl * LDC + wn * 64 + fn * 16 + (lane & 15)] = acc[fm][fn][r] * sc;
     }
   __syncthreads();
+  if constexpr (AM == A_X) report_range(a.status, xmax, kRangeTime);
   epilogue_tile<EM, BM, BN, LDC, 256>(a, sC, m0, n0);
 }
 
@@ -663,6 +689,7 @@ __device__ __forceinline__ void epilogue_regs_resid(const GemmArgs& a, const f32
                                                     const float (&rs)[FMW], int r0, int c0, int lane,
                                                     const float4* pre) {
   const int M = a.M, N = a.N;
+  float vmax = 0.f;
 #pragma unroll
   for (int fm = 0; fm < FMW; ++fm) {
     const int row = r0 + fm * 16 + (lane & 15);
@@ -675,12 +702,14 @@ __device__ __forceinline__ void epilogue_regs_resid(const GemmArgs& a, const f32
         const float4 o = make_float4(hv.x + acc[fm][fn][0] * rs[fm], hv.y + acc[fm][fn][1] * rs[fm],
                                      hv.z + acc[fm][fn][2] * rs[fm], hv.w + acc[fm][fn][3] * rs[fm]);
         st_out<true>(hp, o);
+        vmax = absmax4(vmax, o.x, o.y, o.z, o.w);
         union { half_t e[4]; uint2 u; } o16;
         o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
         st_out<true>(reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, kKPad / 8)), o16.u);
       }
     }
   }
+  report_range(a.status, vmax, kRangeResidual);
 }
 
 // ----------------------------------------------------------------------------
@@ -1260,6 +1289,7 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
                  m_run, l_acc, lane);
   }
 
+  float vmax = 0.f;
   if constexpr (KS == 1) {
     if (rvalid) {
       const float l_run = l_acc[0];
@@ -1270,6 +1300,7 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
         union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
+        vmax = absmax4(vmax, o[m][0] * inv, o[m][1] * inv, o[m][2] * inv, o[m][3] * inv);
         *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
       }
     }
@@ -1307,9 +1338,11 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
       union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk4.h[e] = (half_t)(acc[e] * inv);
+      vmax = absmax4(vmax, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
       *reinterpret_cast<uint2*>(a.out + t16_off(b * kChunk + qi2, hq2 * kHD + d0, kNQ / 8)) = pk4.u;
     }
   }
+  report_range(a.status, vmax, kRangeAttention);
 }
 
 template <bool SELF, int QG, int KS>
@@ -1488,6 +1521,8 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk4.h[e] = (half_t)(acc4[e] * inv);
       *reinterpret_cast<uint2*>(a.out + t16_off(b * kChunk + qr, hq * kHD + d0, kNQ / 8)) = pk4.u;
+      report_range(a.status, absmax4(0.f, acc4[0] * inv, acc4[1] * inv, acc4[2] * inv, acc4[3] * inv),
+                   kRangeAttention);
     }
   }
 }
@@ -1607,13 +1642,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
     const float l_run = l_acc[0];
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     const int orow = b * seq + qi;
+    float vmax = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       union { half_t h[4]; uint2 u; } pk4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
+      vmax = absmax4(vmax, o[m][0] * inv, o[m][1] * inv, o[m][2] * inv, o[m][3] * inv);
       *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
     }
+    report_range(a.status, vmax, kRangeAttention);
   }
 }
 
@@ -1694,6 +1732,7 @@ constexpr int kTimeBlocks = kD / kTimeRowsPerBlock;  // 45
 __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
   __shared__ float se[kD];
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = 0;  // every later kernel of the call follows this one
   const int nMaskBlocks = (a.B + 3) / 4;
   const int timeBlocks = a.n_t > 0 ? kTimeBlocks : 0;
   if ((int)blockIdx.x < timeBlocks) {
@@ -1774,6 +1813,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // the query: a count of the mask before j0, then a running sum over the 64).
 __global__ __launch_bounds__(256) void prefill_rope_rows_kernel(const PrefillPrologueArgs a) {
   const int b = blockIdx.y, j0 = blockIdx.x * 64, tid = threadIdx.x, P = a.P;
+  if (b == 0 && blockIdx.x == 0 && tid == 0 && a.status) *a.status = 0;  // the prefill's first kernel
   const uint8_t* mk = a.mask + (size_t)b * P;
   __shared__ int sCnt[256];
   __shared__ int sPos[64];
@@ -1815,6 +1855,7 @@ __global__ __launch_bounds__(256) void prefill_embed_kernel(const PrefillPrologu
     const float4 v = make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                                  __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u));
     *reinterpret_cast<float4*>(a.h + t32_off((int)row, c4 * 4, kLmD / 4)) = v;
+    report_range(a.status, absmax4(0.f, v.x, v.y, v.z, v.w), kRangeResidual);
     union { half_t e[4]; uint2 u; } o16;
     o16.e[0] = (half_t)v.x; o16.e[1] = (half_t)v.y; o16.e[2] = (half_t)v.z; o16.e[3] = (half_t)v.w;
     *reinterpret_cast<uint2*>(a.h16 + t16_off((int)row, c4 * 4, kLmD / 8)) = o16.u;

@@ -43,12 +43,13 @@ struct CallKey {
   const float* prev;
   float* vel;
   float* st;
+  int* status;
 };
 
 bool same_key(const CallKey& a, const CallKey& b) {
   return a.velocity_mode == b.velocity_mode && a.B == b.B && a.P == b.P && a.d == b.d &&
          a.t_single == b.t_single && a.kv == b.kv && a.mask == b.mask && a.x_in == b.x_in &&
-         a.out == b.out && a.prev == b.prev && a.vel == b.vel && a.st == b.st;
+         a.out == b.out && a.prev == b.prev && a.vel == b.vel && a.st == b.st && a.status == b.status;
 }
 
 struct GraphEntry {
@@ -85,6 +86,7 @@ struct smolexp_handle {
   void* wsmem = nullptr;
   CallWs ws{};
   float* cvec = nullptr;    // time vectors of the schedule (+ one row for velocity calls)
+  int* status_dev = nullptr;  // the status word of calls that do not ask for theirs (kRange* bits)
   float2* rope = nullptr;   // [max_prefix + 50][32] (cos, sin) by position
   double* inv_period = nullptr;
 
@@ -302,6 +304,7 @@ struct CallArgs {
   float* vel;
   float* st;
   float t_single;
+  int* status;  // the caller's status word, or nullptr (the handle's)
 };
 
 CallKey key_of(const CallArgs& c) {
@@ -310,6 +313,7 @@ CallKey key_of(const CallArgs& c) {
   k.velocity_mode = c.velocity;
   k.B = c.B; k.P = c.P; k.d = c.d; k.t_single = c.velocity ? c.t_single : 0.f;
   k.kv = c.kv; k.mask = c.mask; k.x_in = c.x_in; k.out = c.out; k.prev = c.prev; k.vel = c.vel; k.st = c.st;
+  k.status = c.status;
   return k;
 }
 
@@ -364,8 +368,12 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     h->have_probe = true;
   }
 
+  // the call's status word: cleared by the prologue, kRange* bits set by any kernel that rounds
+  // an activation beyond fp16's range
+  int* const status = c.status ? c.status : h->status_dev;
   PrologueArgs pa;
   memset(&pa, 0, sizeof(pa));
+  pa.status = status;
   pa.B = B;
   pa.n_t = c.velocity ? 1 : 0;
   pa.t[0] = c.t_single;
@@ -434,6 +442,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
       const float t = c.velocity ? c.t_single : h->ts[k];
       GemmArgs g;
       memset(&g, 0, sizeof(g));
+      g.status = status;
       g.M = Mg;
       g.inv_k = 1.0f / kD;
       g.eps = h->cfg.rms_eps;
@@ -470,6 +479,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
 
         AttnArgs aa;
         memset(&aa, 0, sizeof(aa));
+        aa.status = status;
         aa.q = wg.q; aa.kc = wg.kc; aa.vc = wg.vc;
         aa.pk = kv + (size_t)l * kvLayer + kvOff;
         aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2 + kvOff;
@@ -650,6 +660,7 @@ int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, 
   hipError_t e;
   PrefillPrologueArgs pp;
   memset(&pp, 0, sizeof(pp));
+  pp.status = h->status_dev;
   pp.B = B; pp.P = P; pp.emb = emb; pp.mask = mask; pp.rope = h->rope;
   pp.h = h->pf_h; pp.h16 = h->pf_h16; pp.ropeq = h->pf_ropeq;
   if ((e = launch_prefill_prologue(pp, s)) != hipSuccess) return hip_fail(h, e, "prefill prologue launch");
@@ -665,6 +676,7 @@ int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, 
     bf16_t* vcache = kcache + kvLayer / 2;
     GemmArgs g;
     memset(&g, 0, sizeof(g));
+    g.status = h->status_dev;
     g.M = M;
     g.inv_k = 1.0f / kLmD;
     g.eps = h->cfg.rms_eps;
@@ -678,6 +690,7 @@ int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, 
 
     AttnArgs aa;
     memset(&aa, 0, sizeof(aa));
+    aa.status = h->status_dev;
     aa.q = h->pf_q; aa.pk = kcache; aa.pv = vcache; aa.mask = mask; aa.out = h->pf_o16;
     aa.B = B; aa.P = P; aa.seq = P;
     if ((e = launch_prefix_attention(aa, s)) != hipSuccess) return hip_fail(h, e, "prefill attention launch");
@@ -776,6 +789,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   const size_t o_cv = take((size_t)(kMaxSteps + 1) * kD * 4);  // the schedule's time vectors + one for velocity calls
   const size_t o_rope = take((size_t)n_pos * (kHD / 2) * sizeof(float2));
   const size_t o_invp = take((size_t)(kD / 2) * sizeof(double));
+  const size_t o_status = take(sizeof(int));
   // the no-alloc entry point's fixed workspace on this device: its address, looked up once
   char* scratch_base = nullptr;
   size_t scratch_bytes = 0;
@@ -787,6 +801,7 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out) {
   h->cvec = (float*)(base + o_cv);
   h->rope = (float2*)(base + o_rope);
   h->inv_period = (double*)(base + o_invp);
+  h->status_dev = (int*)(base + o_status);
 
   e = hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking);
   // the columns 720..767 of h16 are read by the K = 768 GEMM and never written: zero them once
@@ -1179,6 +1194,7 @@ int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix
     c.prev = c.d > 0 ? opts->prev_actions : nullptr;
     c.vel = opts->out_velocities;
     c.st = opts->out_states;
+    c.status = opts->out_status;
   }
   if (hipSetDevice(h->device) != hipSuccess) return fail(h, SMOLEXP_E_HIP, "hipSetDevice failed");
   return run_call(h, c, static_cast<hipStream_t>(hip_stream));
@@ -1239,6 +1255,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     lastc.velocity = k.velocity_mode; lastc.kv = k.kv; lastc.mask = k.mask; lastc.P = k.P; lastc.x_in = k.x_in;
     lastc.out = k.out; lastc.B = k.B; lastc.prev = k.prev; lastc.d = k.d; lastc.vel = k.vel; lastc.st = k.st;
     lastc.t_single = k.t_single;
+    lastc.status = k.status;
   }
   if (kernel != PR_LOOP && (!h->have_probe || !same_key(h->probe_key, h->last))) {
     // the previous call was a graph replay of another key: enqueue it once directly to get its launches

@@ -67,8 +67,17 @@ enum EMode : int {
   E_PF_RESID = 8,  // as E_H_RESID at the prefix model's width (960 stored columns)
 };
 
+// Bits of a call's status word: an activation that is rounded to fp16 for the matrix cores
+// (largest finite value 65504) was beyond that range, so it became infinite and the results are
+// not valid.  Set by the kernel that rounds it (atomicOr), cleared by the call's first kernel.
+constexpr int kRangeResidual = 1;   // the fp16 copy of the residual stream (RMSNorm'd products)
+constexpr int kRangeFfn = 2;        // the SwiGLU output
+constexpr int kRangeAttention = 4;  // the attention output
+constexpr int kRangeTime = 8;       // the time MLP's hidden layer, or the Euler state as its operand
+
 struct GemmArgs {
   int M, N, K;
+  int* status;          // the call's status word (kRange* bits), or nullptr
   const void* A;
   int lda;
   // A_NORM
@@ -102,6 +111,7 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
+  int* status;           // the call's status word (kRangeAttention), or nullptr
   const bf16_t* q;       // [B][15][seq][64]
   const bf16_t* kc;      // [B][5][50][64] (self only)
   const bf16_t* vc;
@@ -126,6 +136,7 @@ constexpr int kCrossQMaxBatch = 8;
 bool use_cross_q(int B);  // the cross layers of this batch size fold the Q projection into attention
 
 struct PrologueArgs {
+  int* status;             // cleared to 0 (when not nullptr)
   int B;                   // queries (0: time vectors only)
   int n_t;                 // number of flow times whose time vectors are computed (0: none)
   float t[kMaxSteps];
@@ -224,6 +235,7 @@ hipError_t launch_inv_period_table(double* tab, float p_min, float p_max, hipStr
 
 // Prefill of the prefix language model.
 struct PrefillPrologueArgs {
+  int* status;             // cleared to 0, then kRangeResidual if an embedding is beyond fp16's range
   int B, P;
   const bf16_t* emb;       // [B][P][960] token embeddings
   const uint8_t* mask;     // [B][P]

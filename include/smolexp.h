@@ -188,13 +188,34 @@ int smolexp_denoise_noalloc(smolexp_t h, const void* prefix_kv, const uint8_t* p
  *   overwrite_rows  d, 0..50.
  *   out_velocities  device fp32 [n_steps][batch][50][32] or NULL: v at each step.
  *   out_states      device fp32 [n_steps][batch][50][32] or NULL: x after each step.
+ *   out_status      device int [1] or NULL: the call's status word, 0 when every
+ *                   activation rounded to fp16 for the matrix cores stayed inside
+ *                   fp16's range; otherwise SMOLEXP_RANGE_* bits name what left it
+ *                   (it became infinite, and the call's results are not valid).
+ *                   Written by the call's kernels (cleared by its first one); read
+ *                   it after the stream work completes.
  */
 typedef struct smolexp_denoise_opts {
   const float* prev_actions;
   int overwrite_rows;
   float* out_velocities;
   float* out_states;
+  int* out_status;
 } smolexp_denoise_opts;
+
+/*
+ * Bits of a call's status word (smolexp_denoise_opts.out_status).  The GEMM operands are
+ * fp16 (largest finite value 65504); an activation of larger magnitude cannot be
+ * represented there.  The library detects this instead of scaling: values that large do
+ * not occur with SmolVLA-scale weights (the residual stream stays orders of magnitude
+ * below), and a checkpoint that produced them would need its own scaling.
+ */
+enum {
+  SMOLEXP_RANGE_RESIDUAL = 1,   /* the fp16 copy of the residual stream (also a prefill's embeddings) */
+  SMOLEXP_RANGE_FFN = 2,        /* the SwiGLU output */
+  SMOLEXP_RANGE_ATTENTION = 4,  /* an attention output */
+  SMOLEXP_RANGE_TIME = 8        /* the time MLP's hidden layer, or the Euler state */
+};
 
 /* smolexp_denoise with options (opts may be NULL = none). */
 int smolexp_denoise_ex(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_mask,

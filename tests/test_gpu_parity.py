@@ -387,3 +387,64 @@ def test_query_groups_run_both_kernel_paths_in_one_call():
             fm.smolexp_destroy(h)
     finally:
         ex.close()
+
+
+def test_fp16_range_overflow_is_reported():
+    """Activations beyond fp16's range (the matrix cores' operand type, largest finite value
+    65504) are reported in the call's status word with the documented bits, not returned as
+    silent infinities: a time_out bias of 1e5 (the residual stream), gate/up weights scaled by
+    300 (the SwiGLU output), prefix values of 1e6 (the attention output) and noise of 1e5 (the
+    Euler state).  The oracle (float64) stays finite on the first case; the weights of the
+    workloads report 0."""
+    _say("fp16 range reporting")
+    L, P = 2, 40
+    base = synth.draw_weights(L)
+    kv = synth.draw_prefix_kv(L, 1, P, seed=71)
+    mask = synth.make_mask(1, P, [33])
+    noise = synth.draw_noise(1, seed=72)
+
+    def bits(a):
+        return synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+    def run(named, kv_bits, noise_np):
+        cfg = fm.smolexp_default_config(n_layers=L, max_batch=1, max_prefix=P)
+        h = fm.smolexp_create(cfg, 0)
+        try:
+            fm.smolexp_load_weights(h, synth.pack_weights(named, L))
+            out = torch.empty((1, 50, 32), device="cuda")
+            st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+            fm.smolexp_denoise_ex(h, cfg, torch.from_numpy(kv_bits.view(np.int16)).cuda(), torch.from_numpy(mask).cuda(),
+                                  torch.from_numpy(noise_np).cuda(), out, out_status=st)
+            torch.cuda.synchronize()
+            return int(st.cpu()[0]), out.cpu().numpy()
+        finally:
+            fm.smolexp_destroy(h)
+
+    status, out = run(base, kv, noise)
+    assert status == 0 and np.isfinite(out).all()
+
+    big_b = dict(base)
+    big_b["time_out.b"] = bits(np.full(720, 1e5))
+    status, _ = run(big_b, kv, noise)
+    print(f"[range] time_out.b = 1e5: status {status}", flush=True)
+    assert status & fm.SMOLEXP_RANGE_RESIDUAL
+    W = oracle.decode_weights(big_b)
+    x = oracle.denoise_batch(W, oracle.ExpertConfig(n_layers=L), kv, mask, noise, n_steps=10)
+    assert np.isfinite(x).all()   # representable in the method's own arithmetic
+
+    big_ffn = dict(base)
+    for name in ("layers.0.gate.w", "layers.0.up.w"):
+        big_ffn[name] = bits(oracle.bf16_bits_to_float(base[name]) * 300.0)
+    status, _ = run(big_ffn, kv, noise)
+    print(f"[range] gate/up x 300: status {status}", flush=True)
+    assert status & fm.SMOLEXP_RANGE_FFN
+
+    kv_big = kv.copy()
+    kv_big[1, 1] = bits(np.full(kv_big[1, 1].shape, 1e6))   # layer 1 (cross) values
+    status, _ = run(base, kv_big, noise)
+    print(f"[range] prefix values 1e6: status {status}", flush=True)
+    assert status & fm.SMOLEXP_RANGE_ATTENTION
+
+    status, _ = run(base, kv, noise * np.float32(1e5))
+    print(f"[range] noise x 1e5: status {status}", flush=True)
+    assert status & fm.SMOLEXP_RANGE_TIME
