@@ -289,6 +289,38 @@ def test_edge_single_key_empty_prefix_and_ragged(ex4):
         compare(gpu, run_oracle(ex4, wl, [0, 1]), [0, 1], wl["noise"], f"P={P} lengths={lens}")
 
 
+def _nan_pads(wl):
+    kv = wl["prefix_kv"]
+    for b, p in zip(*np.nonzero(wl["mask"] == 0)):
+        kv[:, :, b, :, p, :] = 0x7FC0   # bf16 NaN in every masked slot
+
+
+def test_long_prefixes_take_several_key_rounds(ex4):
+    """Prefixes longer than one staged round of the small-batch attention kernels (320 keys):
+    batch 2 at P = 450 (self layers stage 500 keys, cross layers 450, in two rounds each) with
+    one full prefix and one of 300 valid tokens interleaved with NaN pads; P = 300, where the
+    chunk's keys straddle the round boundary; and the streamed kernel at batch 16 near the
+    handle's max_prefix (P = 512, 480..512 valid, NaN pads)."""
+    _say("long prefixes: several key rounds, NaN pads")
+    for P, B in ((450, 2), (300, 2), (512, 16)):
+        wl = synth.make_workload("expert4_b1_p177", batch=B, with_weights=False)
+        wl["prefix_kv"] = synth.draw_prefix_kv(4, B, P, seed=81 + P)
+        wl["prefix_len"] = P
+        if B == 2:
+            mask = synth.make_mask(2, P, [P, P])
+            mask[1] = (np.arange(P) % 3 != 1) if P == 450 else (np.arange(P) < 270)
+            wl["mask"] = mask.astype(np.uint8)
+        else:
+            lens = [int(x) for x in synth.draw_lengths(B, 480, 512, seed=83)]
+            wl["mask"] = synth.make_mask(B, P, lens)
+            wl["mask"][3, ::7] = 0   # interleaved pads in one query
+        wl["lengths"] = wl["mask"].sum(axis=1)
+        _nan_pads(wl)
+        gpu = run_gpu(ex4, to_device(wl))
+        q = [0, 1] if B == 2 else [0, 3, 15]
+        compare(gpu, run_oracle(ex4, wl, q), q, wl["noise"], f"P={P} batch {B} valid {[int(x) for x in wl['lengths'][q]]}")
+
+
 def test_edge_full_overwrite_and_four_steps():
     _say("edge cases: d = 50, 4 Euler steps")
     ex = Expert(4, n_steps=4, max_batch=4, max_prefix=256)
