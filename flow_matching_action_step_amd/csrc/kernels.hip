@@ -881,6 +881,9 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   __builtin_amdgcn_s_waitcnt(VM2 | (7 << 4) | (15 << 8));  // this wave's slab 0 landed
   __builtin_amdgcn_s_barrier();                            // ... every wave's
   f16x8 a0[FMW], b0[FN], a1[FMW], b1[FN];
+  // The expert's RMSNorm'd operands hold 720 columns in K = 768: the second k-step of the
+  // last slab (columns 736..767) is zero padding on both sides, and its MFMAs are skipped.
+  const bool pad_tail = NORM && EM != E_PF_QKV && K == kKPad;
   read_frags(0, 0, a0, b0);
   for (int kt = 0; kt < nk; ++kt) {
     read_frags(kt, 1, a1, b1);
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
       read_frags(kt + 1, 0, a0, b0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
+    if (kt + 1 < nk || !pad_tail) mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
