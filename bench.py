@@ -145,6 +145,70 @@ def summarize_pmc(fetch_csv, write_csv, workload, kernel):
     print(json.dumps(entry, indent=1))
 
 
+def summarize_trace(trace_csv):
+    """Per kernel, from the rocprofv3 --kernel-trace of one bench command: the dispatches of the
+    whole calls (warm-up, timed calls and the hook's whole-call replays: everything up to the
+    end of the last call, which starts with its prologue_kernel) and those of the per-kernel
+    timing graphs that follow them (bench.py's avg_us times those with HIP events).  Prints a
+    markdown table of calls and average durations."""
+    import csv
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    mine = [r for r in rows if "smolexp::" in r[2]]
+    pro = [i for i, r in enumerate(mine) if "prologue_kernel" in r[2]]
+    per_call = pro[-1] - pro[-2]                 # dispatches of one call
+    end_loop = pro[-1] + per_call                 # first dispatch after the last call
+    stats = {}
+    for i, (t0, t1, name) in enumerate(mine):
+        e = stats.setdefault(name, [0, 0.0, 0, 0.0])
+        k = 0 if i < end_loop else 2
+        e[k] += 1
+        e[k + 1] += (t1 - t0) / 1e3
+    loop_total = sum(e[1] for e in stats.values())
+    short = lambda n: n.replace("void ", "").replace("smolexp::", "").split("(")[0]  # noqa: E731
+    fmt = lambda t, c: f"{t / c:.2f}" if c else "-"  # noqa: E731
+    print(f"{per_call} dispatches per call; {end_loop} dispatches of whole calls, {len(mine) - end_loop} of timing graphs")
+    print()
+    print("| kernel | calls in whole calls | avg us | % of their GPU time | calls in timing graphs | avg us |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, e in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{short(name)}` | {e[0]} | {fmt(e[1], e[0])} | {100 * e[1] / loop_total:.1f} | {e[2]} | {fmt(e[3], e[2])} |")
+
+
+def summarize_mfma(counter_csv):
+    """Per kernel, from one rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_F16 and SQ_INSTS_VALU_MFMA_MOPS_BF16: matrix-core utilisation (busy
+    cycles summed over the 1024 SIMDs, over GUI_ACTIVE summed over the 8 XCDs / 8 x 1024) and the
+    matrix flops issued per dispatch (MOPS x 512).  Prints a markdown table."""
+    import csv
+    per = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            d = per.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    stats = {}
+    for (_, name), d in per.items():
+        e = stats.setdefault(name, [0, 0.0, 0.0, 0.0, 0.0])
+        e[0] += 1
+        e[1] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        e[2] += d.get("GRBM_GUI_ACTIVE", 0.0) / 8 * 1024
+        e[3] += (d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)) * 512
+        e[4] += d["dur"]
+    total = sum(e[4] for n, e in stats.items() if "smolexp::" in n)
+    short = lambda n: n.replace("void ", "").replace("smolexp::", "").split("(")[0]  # noqa: E731
+    print("| kernel | dispatches | MFMA utilisation | MFMA TFLOP per dispatch | % of GPU time |")
+    print("|---|---:|---:|---:|---:|")
+    for name, e in sorted(stats.items(), key=lambda kv: -kv[1][4]):
+        if "smolexp::" not in name:
+            continue
+        util = e[1] / e[2] if e[2] else 0.0
+        print(f"| `{short(name)}` | {e[0]} | {100 * util:.1f}% | {e[3] / e[0] / 1e12:.4f} | {100 * e[4] / total:.1f} |")
+
+
 def kernel_costs(L, B, lengths, P):
     """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
     launches per Euler step.
@@ -570,7 +634,8 @@ def main():
     ap.add_argument("--stage", choices=("denoise", "prefill", "train"), default="denoise",
                     help="prefill: time the prefix language model that fills the K/V cache instead; "
                          "train: the flow-matching training step (loss and weight gradients)")
-    ap.add_argument("--kernel-reps", type=int, default=200)
+    ap.add_argument("--kernel-reps", type=int, default=200,
+                    help="launches per kernel in the timing hook; 0: only the timed calls (loop-only profiling run)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="launch kernels one by one instead of graph replay")
@@ -584,7 +649,18 @@ def main():
                     help="after the measurement, copy 256 MiB device-to-device three times (HBM counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel averages of the whole calls and of the timing graphs, from a rocprofv3 "
+                         "--kernel-trace of a bench command")
+    ap.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
+                    help="per-kernel matrix-core utilisation from a rocprofv3 --pmc run of the MFMA counters")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.summarize_pmc[2])
         return
@@ -636,9 +712,17 @@ def main():
     ev_ms = e0.elapsed_time(e1)
     assert torch.isfinite(out).all().item(), "non-finite actions"
 
+    # the whole call replayed by the timing hook (HIP events around the replays)
+    loop_us = fm.smolexp_time_kernel(h, LOOP_ID, max(3, args.steps // 5))
+    if args.kernel_reps == 0:
+        # loop-only run (the reference for --summarize-trace): everything but the per-kernel timing
+        print(json.dumps({"metric": "loop-only run for a kernel trace (no per-kernel timing)",
+                          "ms_per_step": wall / args.steps * 1e3, "steps": args.steps, "warmup": args.warmup,
+                          "config": {"workload": args.workload, "batch": B, "prefix_len": P}}), flush=True)
+        fm.smolexp_destroy(h)
+        return
     # per-kernel time per launch: HIP events on the library's stream around one graph of launches
     kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, args.kernel_reps)
-    loop_us = fm.smolexp_time_kernel(h, LOOP_ID, max(3, args.steps // 5))
     dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
     dom = kern[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["avg_us"] * 1e-6)
