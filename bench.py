@@ -643,6 +643,8 @@ def main():
                     help="only the workload's own line: no large-batch block and no overwrite difference")
     ap.add_argument("--large-calls", type=int, default=20, help="timed calls per large-batch workload")
     ap.add_argument("--large-kernel-reps", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="override the workload's batch (the first queries of its seeded draws)")
     ap.add_argument("--batch-groups", type=int, default=0,
                     help="concurrent query groups per call (0: the library's automatic choice)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -681,7 +683,7 @@ def main():
     import synth
     import flow_matching_action_step_amd as fm
 
-    wl = synth.make_workload(args.workload)
+    wl = synth.make_workload(args.workload, batch=args.batch)
     L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
     cfg = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps, max_batch=B, max_prefix=P,
                                     use_graphs=0 if args.no_graphs else 1, batch_groups=args.batch_groups)
@@ -779,7 +781,7 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+    if args.workload == DEFAULT_WORKLOAD and args.batch is None and not args.no_extra:
         # the large-batch workloads on one handle with the same weights
         big = [synth.make_workload(n, with_weights=False) for n in LARGE_BATCH_WORKLOADS]
         cfg2 = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps,

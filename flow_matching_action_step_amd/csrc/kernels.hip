@@ -569,6 +569,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p;
   const int nks = (K + 31) / 32;
   p.reg = 0;
+  p.fmw = 2;
   p.bm = 64;
   p.rb = 4;
   p.cb = 1;
@@ -949,17 +950,20 @@ static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
 // tiles, a 4-stage ring up to M = 4800 (down at 3200: 21.8 against 24.1 us) and 64-row tiles
 // at M <= 2400 (down at 1600: 19.7 against 23.2).
 hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
+  const bool narrow = p.bm == 64 && p.fmw == 1;  // 64-row tiles of eight waves (16 rows each)
   switch (em) {
     case E_QKV:
       if (!norm) return hipErrorInvalidValue;
+      if (narrow) return launch_gemm_dma<E_QKV, true, 64, 1, 2, 4>(a, s);
       return launch_gemm_dma<E_QKV, true, 128, 2, 2, 2>(a, s);
     case E_SWIGLU:
       if (!norm) return hipErrorInvalidValue;
+      if (narrow) return launch_gemm_dma<E_SWIGLU, true, 64, 1, 2, 4>(a, s);
       return launch_gemm_dma<E_SWIGLU, true, 128, 2, 2, 2>(a, s);
     case E_H_RESID:
       if (norm) return hipErrorInvalidValue;
+      if (narrow) return launch_gemm_dma<E_H_RESID, false, 64, 1, 2, 4, true>(a, s);
       if (p.stages == 4) {
-        if (p.bm == 64) return launch_gemm_dma<E_H_RESID, false, 64, 2, 2, 4>(a, s);
         if (p.reg) return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4, true>(a, s);
         return launch_gemm_dma<E_H_RESID, false, 128, 2, 2, 4>(a, s);
       }
@@ -979,22 +983,32 @@ hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArg
   }
 }
 
-// The plan of one projection of the loop, from measurements at M = 50..3200 rows with the
-// weights cycling through a 250 MB footprint, as in the loop (us per launch, best kernel):
-//  * the register-resident K split (skinny) wins up to about 1600 rows for every projection
-//    (down at 800 rows: 12.0 us against 25.5 on 128 x 128 pipelined tiles, whose 42
-//    workgroups leave most CUs idle; o 6.6 against 12.9; Q/K/V 10.2 against 14.3);
-//  * the pipelined kernel wins from 1600-3200 rows on (gate/up from 800);
+// The plan of one projection of the loop, from measurements with the weights cycling through a
+// 256 MB footprint, as in the loop (us per launch, best kernel; the pipelined configurations are
+// BM-row x 128-column tiles, eight waves, an S-stage ring):
+//  * the register-resident K split (skinny) for the smallest row counts: Q/K/V 6.8 us at 400 rows
+//    (8.0 pipelined), cross-layer Q 7.6 at 800 (8.1), o 7.9 at 1200 (8.7), down 13.1 at 800 (14.5);
+//  * 64-row tiles of eight waves with a 4-stage ring (one workgroup per CU) wherever one round of
+//    their tiles fits on the 256 CUs: Q/K/V at 800-1200 rows (8.4 / 9.4 against 11.9 / 15.9 for the
+//    K split), cross-layer Q at 1200-2000 (8.6-9.2 against 10.4-16.2), gate/up at 400 (8.4 against
+//    11.2), o at 1600-2400 (9.0-9.7 against 10.9-16.6 for the K split), down at 1200-2400
+//    (15.1-17.6 against 17.9-20.2 for the 4-wave 64-row tiles);
+//  * 128 x 128 tiles beyond: two stages (two workgroups per CU) for Q/K/V and gate/up; for o and
+//    down, whose 720 columns give few tiles, four stages up to 4800 rows, with the epilogue from the
+//    accumulators from 3200 rows on (down at 3200: 22.2 us);
 //  * the register-staged tiled kernel only for the time MLP at 3200 rows and more.
+// Row counts of whole rounds: 64-row tiles of a 720-column product fit one round up to 2688 rows
+// (42 x 6 tiles), of the cross-layer Q (960 columns) up to 2048, of Q/K/V (1600) up to 1216, of
+// gate/up (4096) up to 512.
 GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
   GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);  // skinny base: k-steps per wave, column blocks
   auto skinny = [&](int rb, int cb) {
     p.kind = 0; p.rb = rb; p.cb = cb;
     return p;
   };
-  auto big = [&](int bm = 128, int stages = 2) {
+  auto big = [&](int bm = 128, int stages = 2, int fmw = 2, int reg = 0) {
     GemmPlan b = p;
-    b.kind = 2; b.bm = bm; b.stages = stages;
+    b.kind = 2; b.bm = bm; b.stages = stages; b.fmw = fmw; b.reg = reg;
     return b;
   };
   if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
@@ -1003,28 +1017,26 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
     case E_QKV:
       if (N == kNQ) {  // cross layers: Q only
         if (M <= 1000) return skinny(2, 4);
-        if (M <= 2400) return skinny(2, 2);
-      } else if (M <= 1200) {
-        return skinny(2, 2);
+        if (M <= 2048) return big(64, 4, 1);
+      } else {
+        if (M <= 600) return skinny(2, 2);
+        if (M <= 1216) return big(64, 4, 1);
       }
       return big();
     case E_SWIGLU:
-      return M <= 600 ? skinny(2, 2) : big();
+      if (M <= 300) return skinny(2, 2);
+      return M <= 512 ? big(64, 4, 1) : big();
     case E_H_RESID:
       if (K > 1024) {  // down
         if (M <= 100) return skinny(2, 1);
         if (M <= 200) return skinny(2, 2);
         if (M <= 1000) return skinny(4, 2);
-        if (M <= 2400) return big(64, 4);
       } else {  // o
         if (M <= 400) return skinny(2, 2);
-        if (M <= 2400) return skinny(4, 2);
+        if (M <= 1200) return skinny(4, 2);
       }
-      {
-        GemmPlan b = M <= 4800 ? big(128, 4) : big();
-        b.reg = M >= 3200;  // the epilogue from the accumulators (see epilogue_regs_resid)
-        return b;
-      }
+      if (M <= 2688) return big(64, 4, 1, 1);
+      return M <= 4800 ? big(128, 4, 2, M >= 3200) : big(128, 2, 2, 1);
     case E_ACTOUT:
       if (M <= 2400) return skinny(1, 1);
       return M <= 4800 ? skinny(4, 2) : plan_gemm(M, N, K);

@@ -318,15 +318,15 @@ CallKey key_of(const CallArgs& c) {
 }
 
 // Queries per group of a call (the groups' loops run concurrently): `batch_groups` groups
-// when the config sets it, else groups of at least 64 queries (B / 64 of them); every group
-// but the last holds a multiple of 8 queries (whole 16-row blocks of the blocked operands).
-// Measured (16 layers, 10 steps): batch 128 at prefix 177 takes 27.0 ms as one chain, 23.9 ms
-// as two groups of 64, 30.2 ms as four of 32; batch 64 at prefix 257 16.5 ms as one chain,
-// 16.9 ms as two groups of 32 (whose 1600-row products run less efficient kernels), 21.1 ms
-// as four.  Returns the count.
+// when the config sets it, else two groups from 64 queries on and one per 64 queries from 192
+// on; every group but the last holds a multiple of 8 queries (whole 16-row blocks of the
+// blocked operands).  Measured (16 layers, 10 steps, ms per call, one group / two / three /
+// four): batch 64 at prefix 257 16.65 / 15.25 / 18.0 / 21.0; batch 96 21.2 / 20.3 / 21.3; batch
+// 128 at prefix 177 27.0 / 24.0 / 26.4 / 26.7; batch 32 11.1 / 11.8; batch 24 10.0 / 11.0;
+// batch 16 8.70 / 8.92.  Returns the count.
 constexpr int kMaxGroups = 8;
 int group_sizes(const smolexp_config& cfg, int B, int* sz) {
-  int G = cfg.batch_groups > 0 ? cfg.batch_groups : (B >= 128 ? B / 64 : 1);
+  int G = cfg.batch_groups > 0 ? cfg.batch_groups : (B >= 192 ? B / 64 : B >= 64 ? 2 : 1);
   G = G < kMaxGroups ? G : kMaxGroups;
   auto base_of = [&](int g) { return ((B + g - 1) / g + 7) / 8 * 8; };
   int base = base_of(G);

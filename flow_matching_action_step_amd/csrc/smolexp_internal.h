@@ -215,6 +215,7 @@ struct GemmPlan {
   int stages;    // pipelined: LDS ring depth (2 or 4); bm = tile rows (64 or 128)
   int ntiles_n;  // output tiles (workgroups) along N
   int reg;       // pipelined: 1 = epilogue from the accumulators (weight fragment as the first MFMA operand)
+  int fmw;       // pipelined: 16-row fragments per wave along M (2; 1 = eight waves on 64-row tiles)
 };
 GemmPlan plan_gemm(int M, int N, int K);
 

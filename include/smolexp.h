@@ -72,8 +72,8 @@ typedef struct smolexp_config {
   int use_graphs;    /* 1: capture each call's launch sequence once and replay it as a HIP graph */
   int batch_groups;  /* 0..8: a call's queries run as this many groups whose loops proceed
                         concurrently (on side streams of default priority, or as parallel
-                        branches of the graph); 0 = automatic (groups of at least 64
-                        queries: batch / 64 of them from 128 queries on).
+                        branches of the graph); 0 = automatic (two groups from 64
+                        queries on, one per 64 queries from 192 on).
                         Every group but the last holds a multiple of 8 queries.  The results
                         of a query depend on the size of its group only within the tolerances,
                         as for any change of batch composition. */
