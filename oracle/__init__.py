@@ -78,6 +78,16 @@ Pins (what fixes each function other than itself; all in tests/):
                     through a composition of torch library routines; closed
                     form with a zero action_out matrix; the forward's velocity
                     is expert.velocity's; query shares add up to the batch
+  8-bit weights (quant.py: E4M3 codes with per-row power-of-two scales, and the expert
+  with its streamed matrices quantized)
+    e4m3 .......... the format's code points (largest finite, smallest normal and
+                    subnormal, NaN); every code round-trips; exhaustive nearest-value
+                    search with ties to even; torch's float8_e4m3fn cast; the rounding
+                    error bound
+    row scales .... powers of two putting each row's max in (224, 448]
+    streamed model  without rounding it is the float64 expert (to float64 rounding);
+                    copies with a planted mistake (a gain not folded, the time half
+                    dropped) fail that; quantized matrices sit on their rows' grid
 No function is left parity unpinned.
 """
 from .expert import (  # noqa: F401
@@ -85,6 +95,7 @@ from .expert import (  # noqa: F401
     attention, embed, expert_layer, head, velocity, ExpertConfig,
 )
 from .flow import schedule, overwrite_rows, euler_denoise, denoise_query, denoise_batch  # noqa: F401
+from . import quant  # noqa: F401
 from .prefill import (  # noqa: F401
     PrefillConfig, prefix_positions, prefill_layer, prefill, prefill_batch, round_to_bf16_bits,
 )
