@@ -34,7 +34,7 @@ class smolexp_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
                                              "chunk", "action_dim", "n_steps", "max_batch", "max_prefix")] + \
                [(n, ctypes.c_float) for n in ("rope_theta", "rms_eps", "t_min_period", "t_max_period")] + \
-               [("use_graphs", ctypes.c_int), ("batch_groups", ctypes.c_int)]
+               [("use_graphs", ctypes.c_int), ("batch_groups", ctypes.c_int), ("weight_format", ctypes.c_int)]
 
 
 class smolexp_denoise_opts(ctypes.Structure):
@@ -44,6 +44,7 @@ class smolexp_denoise_opts(ctypes.Structure):
 
 
 SMOLEXP_RANGE_RESIDUAL, SMOLEXP_RANGE_FFN, SMOLEXP_RANGE_ATTENTION, SMOLEXP_RANGE_TIME = 1, 2, 4, 8
+SMOLEXP_WEIGHTS_FP16, SMOLEXP_WEIGHTS_E4M3 = 0, 1
 
 
 _H = ctypes.c_void_p
@@ -55,6 +56,7 @@ _sig = {
                                         ctypes.POINTER(ctypes.c_float)]),
     "smolexp_batch_groups": (ctypes.c_int, [ctypes.POINTER(smolexp_config), ctypes.c_int,
                                             ctypes.POINTER(ctypes.c_int)]),
+    "smolexp_quantize_e4m3_rows": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P]),
     "smolexp_create": (ctypes.c_int, [ctypes.POINTER(smolexp_config), ctypes.c_int, ctypes.POINTER(_H)]),
     "smolexp_load_weights": (ctypes.c_int, [_H, _P, ctypes.c_size_t]),
     "smolexp_denoise": (ctypes.c_int, [_H, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P]),
@@ -136,6 +138,22 @@ def smolexp_batch_groups(cfg, batch):
     n = _lib.smolexp_batch_groups(ctypes.byref(cfg), int(batch), sizes)
     _check(min(n, 0), what="smolexp_batch_groups")
     return [sizes[i] for i in range(n)]
+
+
+def smolexp_quantize_e4m3_rows(w):
+    """E4M3 codes (uint8 [rows, cols]) and row scales (float32 [rows]) of a float64 numpy
+    matrix, as the library stores 8-bit weights (host only)."""
+    import numpy as np
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    if w.ndim != 2:
+        raise ValueError("w must be a 2-d matrix")
+    rows, cols = w.shape
+    codes = np.zeros((rows, cols), np.uint8)
+    scales = np.zeros(rows, np.float32)
+    _check(_lib.smolexp_quantize_e4m3_rows(w.ctypes.data_as(ctypes.c_void_p), rows, cols,
+                                           codes.ctypes.data_as(ctypes.c_void_p),
+                                           scales.ctypes.data_as(ctypes.c_void_p)), what="smolexp_quantize_e4m3_rows")
+    return codes, scales
 
 
 def smolexp_create(cfg, hip_device=0):

@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace smolexp {
 
@@ -58,6 +59,30 @@ __device__ __forceinline__ float absmax4(float m, float a, float b, float c, flo
 // status word.
 __device__ __forceinline__ void report_range(int* status, float vmax, int bit) {
   if (vmax >= kF16Inf && status) atomicOr(status, bit);
+}
+
+// Eight OCP E4M3 weight codes (byte j of c = element j) -> the eight fp16 values they encode,
+// exactly (every E4M3 value is an fp16 value), with gfx950's packed conversion (two codes per
+// instruction, scale 1).  The fp16 operand passes through unchanged.
+typedef half_t f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 w_to_f16x8(const uint4& w) { return w; }
+__device__ __forceinline__ uint4 w_to_f16x8(const uint2& c) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.x, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.x, 1.0f, true);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.y, 1.0f, false);
+  const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b), __builtin_bit_cast(unsigned, d),
+                    __builtin_bit_cast(unsigned, e));
+}
+// One lane's weight fragment (8 consecutive k of one row): 16 bytes of fp16 or 8 of E4M3.
+template <bool W8>
+using WFrag = typename std::conditional<W8, uint2, uint4>::type;
+template <bool W8>
+__device__ __forceinline__ WFrag<W8> load_wfrag(const half_t* W, size_t off, bool ok) {
+  if constexpr (W8)
+    return ok ? *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(W) + off) : make_uint2(0, 0);
+  else
+    return ok ? *reinterpret_cast<const uint4*>(W + off) : make_uint4(0, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint4 pack8(const float* v) {
@@ -333,7 +358,9 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
 // MFMA unscaled, so no load waits on the row scale; each wave also sums the
 // squares of its slice of every row, and 1/rms(row) scales the finished sums
 // (a per-row constant, so this equals normalising first up to rounding).
-template <int AM, int EM, int KPW, int RB, int CB = 1>
+// W8: the weights are E4M3 codes (8 bytes per lane and k-step, widened to fp16 in registers)
+// and each output column n is scaled by its row scale wrs[n] instead of w_scale.
+template <int AM, int EM, int KPW, int RB, int CB = 1, bool W8 = false>
 __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   constexpr int NW = 8, BM = 16 * RB, BN = 16 * CB, LDC = BN;
   static_assert(RB == 1 || RB == 2 || RB == 4, "row blocks per workgroup");
@@ -376,7 +403,14 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
       if (w < RB && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, resid_k4(EM)));
     }
   }
-  uint4 wf[KPW][CB];
+  // the weight scale of the one output column this thread reduces (BN divides 512)
+  static_assert(512 % BN == 0, "one reduction column per thread");
+  float wsc = a.w_scale;
+  if constexpr (W8) {
+    const int col = n0 + tid % BN;
+    wsc = col < N ? a.wrs[col] : 0.f;
+  }
+  WFrag<W8> wf[KPW][CB];
   uint4 af[KPW][RB];
   float xmax = 0.f;  // A_X: the largest magnitude of the Euler state rounded to fp16
 #pragma unroll
@@ -386,7 +420,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int n = n0 + cb * 16 + (lane & 15);
-      wf[i][cb] = (kok && n < N) ? *reinterpret_cast<const uint4*>(a.W + t16_off(n, k, a.ldw >> 3)) : make_uint4(0, 0, 0, 0);
+      wf[i][cb] = load_wfrag<W8>(a.W, t16_off(n, k, a.ldw >> 3), kok && n < N);
     }
 #pragma unroll
     for (int fm = 0; fm < RB; ++fm) {
@@ -404,7 +438,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   for (int i = 0; i < KPW; ++i) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const f16x8 bw = __builtin_bit_cast(f16x8, wf[i][cb]);
+      const f16x8 bw = __builtin_bit_cast(f16x8, w_to_f16x8(wf[i][cb]));
 #pragma unroll
       for (int fm = 0; fm < RB; ++fm)
         acc[fm][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i][fm]), bw, acc[fm][cb], 0, 0, 0);
@@ -428,12 +462,11 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
       for (int r = 0; r < 4; ++r)
         sRed[(w * BM + fm * 16 + (lane >> 4) * 4 + r) * BN + cb * 16 + (lane & 15)] = acc[fm][cb][r];
   __syncthreads();
-  const float ws = a.w_scale;
   for (int i = tid; i < BM * BN; i += 512) {
     float s = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) s += sRed[w2 * BM * BN + i];
-    float sc = ws;
+    float sc = wsc;
     if constexpr (AM == A_NORM) {  // RMSNorm: rows were multiplied unscaled, 1/rms(h) applied here
       float q = 0.f;
 #pragma unroll
@@ -596,29 +629,34 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return p;
 }
 
-template <int AM, int EM, int RB, int CB>
+template <int AM, int EM, int RB, int CB, bool W8 = false>
 static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  // E4M3 weights: the expert's projections only, at most two row and column blocks
+  if constexpr (W8 && (RB > 2 || CB > 2 || EM == E_PF_QKV || EM == E_PF_RESID)) {
+    (void)p; (void)a; (void)s;
+    return hipErrorInvalidValue;
+  } else {
   // column block groups rounded up to whole XCD rounds, times the row tiles (see gemm_skinny)
   const int groups = (p.ntiles_n + CB - 1) / CB, nrt = (a.M + 16 * RB - 1) / (16 * RB);
   const dim3 grid(8 * ((groups + 7) / 8) * nrt), block(512);
   switch (p.kpw) {
-    case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB, CB>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB, CB>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3, RB, CB>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4, RB, CB>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_skinny<AM, EM, 1, RB, CB, W8>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny<AM, EM, 2, RB, CB, W8>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny<AM, EM, 3, RB, CB, W8>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_skinny<AM, EM, 4, RB, CB, W8>), grid, block, 0, s, a); break;
     case 6:
     case 8:
       // only the fp16-operand GEMMs have K > 1024 (down: K = 2048); the fp32-input
       // variants would not fit their fragments in registers
       // (64 x 64 tiles at K = 2048 would not fit their fragments in registers either)
       if constexpr (AM == A_F16 && RB * CB < 16) {
-        if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB, CB>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB, CB>), grid, block, 0, s, a);
+        if (p.kpw == 6) hipLaunchKernelGGL((gemm_skinny<AM, EM, 6, RB, CB, W8>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_skinny<AM, EM, 8, RB, CB, W8>), grid, block, 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     case 10:  // the prefix model's down projection (K = 2560), at most two 16 x 16 tiles per workgroup
-      if constexpr (AM == A_F16 && EM == E_PF_RESID && RB * CB <= 2) {
+      if constexpr (!W8 && AM == A_F16 && EM == E_PF_RESID && RB * CB <= 2) {
         hipLaunchKernelGGL((gemm_skinny<AM, EM, 10, RB, CB>), grid, block, 0, s, a);
         break;
       }
@@ -626,27 +664,30 @@ static hipError_t launch_skinny(const GemmPlan& p, const GemmArgs& a, hipStream_
     default: return hipErrorInvalidValue;  // K beyond 8 waves x 8 k-steps x 32
   }
   return hipGetLastError();
+  }
 }
 
-template <int AM, int EM, int RB>
+template <int AM, int EM, int RB, bool W8>
 static hipError_t launch_skinny_cb(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   switch (p.cb) {
-    case 1: return launch_skinny<AM, EM, RB, 1>(p, a, s);
-    case 2: return launch_skinny<AM, EM, RB, 2>(p, a, s);
-    case 4: return launch_skinny<AM, EM, RB, 4>(p, a, s);
+    case 1: return launch_skinny<AM, EM, RB, 1, W8>(p, a, s);
+    case 2: return launch_skinny<AM, EM, RB, 2, W8>(p, a, s);
+    case 4: return launch_skinny<AM, EM, RB, 4, W8>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int AM, int EM>
+template <int AM, int EM, bool W8 = false>
 static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   if (p.kind == 0) {
     switch (p.rb) {
-      case 4: return launch_skinny_cb<AM, EM, 4>(p, a, s);
-      case 2: return launch_skinny_cb<AM, EM, 2>(p, a, s);
-      case 1: return launch_skinny_cb<AM, EM, 1>(p, a, s);
+      case 4: return launch_skinny_cb<AM, EM, 4, W8>(p, a, s);
+      case 2: return launch_skinny_cb<AM, EM, 2, W8>(p, a, s);
+      case 1: return launch_skinny_cb<AM, EM, 1, W8>(p, a, s);
       default: return hipErrorInvalidValue;
     }
+  } else if constexpr (W8) {
+    return hipErrorInvalidValue;  // E4M3 weights: register-resident kernels only
   } else {
     const int T = ((a.M + p.bm - 1) / p.bm) * p.ntiles_n;
     const dim3 grid(8 * ((T + 7) / 8));
@@ -658,7 +699,7 @@ static hipError_t launch_gemm_t(const GemmPlan& p, const GemmArgs& a, hipStream_
 
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s) {
 #define SMOLEXP_GEMM_CASE(AMV, EMV) \
-  if (am == AMV && em == EMV) return launch_gemm_t<AMV, EMV>(p, a, s);
+  if (am == AMV && em == EMV) return a.wrs ? launch_gemm_t<AMV, EMV, true>(p, a, s) : launch_gemm_t<AMV, EMV>(p, a, s);
   SMOLEXP_GEMM_CASE(A_X, E_TIMEIN)
   SMOLEXP_GEMM_CASE(A_F16, E_H_BIAS)
   SMOLEXP_GEMM_CASE(A_NORM, E_QKV)
@@ -1000,12 +1041,16 @@ hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArg
 // Row counts of whole rounds: 64-row tiles of a 720-column product fit one round up to 2688 rows
 // (42 x 6 tiles), of the cross-layer Q (960 columns) up to 2048, of Q/K/V (1600) up to 1216, of
 // gate/up (4096) up to 512.
-GemmPlan plan_for(int M, int N, int K, AMode am, EMode em) {
+GemmPlan plan_for(int M, int N, int K, AMode am, EMode em, bool w8) {
   GemmPlan p = plan_gemm(M <= 64 ? M : 64, N, K);  // skinny base: k-steps per wave, column blocks
   auto skinny = [&](int rb, int cb) {
     p.kind = 0; p.rb = rb; p.cb = cb;
     return p;
   };
+  if (w8) {  // E4M3 weights (batches of at most 8 queries): the register-resident K split only
+    if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
+    return skinny(2, em == E_ACTOUT ? 1 : 2);
+  }
   auto big = [&](int bm = 128, int stages = 2, int fmw = 2, int reg = 0) {
     GemmPlan b = p;
     b.kind = 2; b.bm = bm; b.stages = stages; b.fmw = fmw; b.reg = reg;
@@ -1398,7 +1443,8 @@ static void launch_ksplit(const AttnArgs& a, hipStream_t s) {
 //      merge their states in LDS.
 // The Q values equal those of the separate GEMM launch (same K split, same
 // order of the sums).
-template <int NBLK>
+// W8: the Q weights are E4M3 codes with row scales (as gemm_skinny's W8).
+template <int NBLK, bool W8 = false>
 __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   constexpr int NT = 512, NW = 8, RK = NBLK * kKB, OLD = kHD + 4, QLD = kHD + 8;
   constexpr int KPW = kKPad / 32 / NW;  // k-steps per wave
@@ -1426,17 +1472,25 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   const int g = u % kHKV, b = u / kHKV, hq = 3 * g + rr / RB, rb = rr % RB;
   const int P = a.P;
 
+  // the weight scales of the two output columns this thread finishes in (2)
+  float ws1 = a.w_scale, ws2 = a.w_scale;
+  if constexpr (W8) {
+    const int c1 = ((tid & 31) >> 3) * 16 + (tid & 7);
+    ws1 = a.wrs[hq * kHD + c1];
+    ws2 = a.wrs[hq * kHD + c1 + 8];
+  }
   // (1) projection operands of this wave's K slice, then the first round of keys
   const int qa = rb * 16 + (lane & 15);  // chunk row of this lane's A fragment
   const bool aok = qa < kChunk;
-  uint4 af[KPW], wf[KPW][4];
+  uint4 af[KPW];
+  WFrag<W8> wf[KPW][4];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int k = (w * KPW + i) * 32 + (lane >> 4) * 8;
     af[i] = aok ? *reinterpret_cast<const uint4*>(a.h16 + t16_off(b * kChunk + qa, k, kKPad / 8)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
-      wf[i][cb] = *reinterpret_cast<const uint4*>(a.wq + t16_off(hq * kHD + cb * 16 + (lane & 15), k, a.ldw >> 3));
+      wf[i][cb] = load_wfrag<W8>(a.wq, t16_off(hq * kHD + cb * 16 + (lane & 15), k, a.ldw >> 3), true);
   }
   AttnStage<false, RK, NT> st;
   st.issue(a, b, g, 0);
@@ -1450,7 +1504,7 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
     const f16x8 av = __builtin_bit_cast(f16x8, af[i]);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, wf[i][cb]), acc[cb], 0, 0, 0);
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, w_to_f16x8(wf[i][cb])), acc[cb], 0, 0, 0);
     sq = sumsq_mfma(av, sq);
   }
 #pragma unroll
@@ -1473,8 +1527,8 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
     }
     bf16_t lo = 0, hi = 0;
     if (qr < kChunk) {
-      const float sc = a.w_scale * rms_scale_qk(a.inv_k, a.eps, q);
-      const float v1 = s1 * sc, v2 = s2 * sc;
+      const float rs = rms_scale_qk(a.inv_k, a.eps, q);
+      const float v1 = s1 * (ws1 * rs), v2 = s2 * (ws2 * rs);
       const float2 cs = a.ropeq[(size_t)(b * kChunk + qr) * (kHD / 2) + d];
       lo = f2bf(v1 * cs.x - v2 * cs.y);
       hi = f2bf(v1 * cs.y + v2 * cs.x);
@@ -1705,16 +1759,22 @@ hipError_t launch_prefix_attention(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
+template <bool W8>
+static void launch_cross_q_t(const AttnArgs& a, hipStream_t s) {
   const int nblk = min(5, max(2, (a.P + kKB - 1) / kKB));
   const int RB = (kChunk + 15) / 16;
   const dim3 grid(8 * 3 * RB * ((kHKV * a.B + 7) / 8)), block(512);
   switch (nblk) {
-    case 2: hipLaunchKernelGGL((attn_cross_q_kernel<2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((attn_cross_q_kernel<3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_cross_q_kernel<4>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_cross_q_kernel<5>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_cross_q_kernel<2, W8>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((attn_cross_q_kernel<3, W8>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_cross_q_kernel<4, W8>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_cross_q_kernel<5, W8>), grid, block, 0, s, a); break;
   }
+}
+
+static void launch_cross_q(const AttnArgs& a, hipStream_t s) {
+  if (a.wrs) launch_cross_q_t<true>(a, s);
+  else launch_cross_q_t<false>(a, s);
 }
 
 bool use_cross_q(int B) { return B <= kCrossQMaxBatch; }

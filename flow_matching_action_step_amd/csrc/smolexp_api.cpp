@@ -8,6 +8,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -19,7 +20,12 @@ struct Mat {
   half_t* w = nullptr;  // blocked layout (t16_off) with ld stored columns
   int ld = 0;
   float scale = 1.f;  // real value = stored fp16 value * scale (a power of two)
+  float* rs = nullptr;  // 8-bit weights: w holds E4M3 codes, real value = code value * rs[row]
 };
+
+void set_w(GemmArgs& g, const Mat& m) {
+  g.W = m.w; g.ldw = m.ld; g.w_scale = m.scale; g.wrs = m.rs;
+}
 
 struct LayerDev {
   bool self_attn = false;
@@ -160,6 +166,14 @@ bool check_config(const smolexp_config* c, std::string* why) {
   if (c->max_batch < 1 || c->max_batch > 1024) { *why = "max_batch must be 1..1024"; return false; }
   if (c->max_prefix < 1 || c->max_prefix > 4096) { *why = "max_prefix must be 1..4096"; return false; }
   if (c->batch_groups < 0 || c->batch_groups > 8) { *why = "batch_groups must be 0..8"; return false; }
+  if (c->weight_format != SMOLEXP_WEIGHTS_FP16 && c->weight_format != SMOLEXP_WEIGHTS_E4M3) {
+    *why = "weight_format must be SMOLEXP_WEIGHTS_FP16 or SMOLEXP_WEIGHTS_E4M3";
+    return false;
+  }
+  if (c->weight_format == SMOLEXP_WEIGHTS_E4M3 && c->max_batch > kCrossQMaxBatch) {
+    *why = "8-bit weights serve batches of at most 8 queries (max_batch 1..8)";
+    return false;
+  }
   if (!(c->rope_theta > 0.f) || !(c->rms_eps > 0.f) || !(c->t_min_period > 0.f) ||
       !(c->t_max_period > c->t_min_period) || !isfinite(c->rope_theta) || !isfinite(c->t_max_period)) {
     *why = "rope_theta, rms_eps and 0 < t_min_period < t_max_period must be finite and positive";
@@ -204,6 +218,32 @@ int shift_for(float mx) {
   return 15 - e;
 }
 
+// OCP 8-bit floating point, E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// subnormals, largest finite value 448): the code of the value nearest to v (|v| <= 448),
+// ties to even.  The quantum of a magnitude a is 2^(max(floor(log2 a), -6) - 3); a / quantum
+// is exact and rounds to an integer n in [0, 16]; n = 16 carries into the next binade through
+// the code arithmetic ((exponent field) * 8 + mantissa).
+uint8_t e4m3_code(double v) {
+  const double a = fabs(v);
+  int b = -6;
+  if (a > 0) {
+    int ex;
+    frexp(a, &ex);  // a = f 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1
+    b = ex - 1 < -6 ? -6 : ex - 1;
+  }
+  const int n = (int)nearbyint(ldexp(a, 3 - b));  // round to nearest, ties to even
+  const int mag = (b == -6 && n < 8) ? n : (b + 7) * 8 + n - 8;
+  return (uint8_t)(mag | ((signbit(v) && mag > 0) ? 0x80 : 0));
+}
+
+// Exponent e of a row's scale 2^e: the smallest with max|row| / 2^e <= 448 (so the row's
+// largest magnitude lands in (224, 448]).  amax = 448 * 2^k gives exactly k.
+int e4m3_row_exp(double amax) {
+  int e = ilogb(amax) - 8;  // 448 is in [2^8, 2^9): the answer is this or the next
+  if (ldexp(amax, -e) > 448.0) ++e;
+  return e;
+}
+
 int pick_shift(const std::vector<std::pair<const uint16_t*, size_t>>& parts) {
   float mx = 0.f;
   for (auto& p : parts)
@@ -241,6 +281,29 @@ int pack_t16_gain(const std::vector<const uint16_t*>& rows, int K, int kstore, c
   for (size_t n = 0; n < rows.size(); ++n)
     for (int k = 0; k < K; ++k) dst[t16_off((int)n, k, kstore / 8)] = (half_t)(bf2f(rows[n][k]) * g[k] * m);
   return shift;
+}
+
+// Rows 0..N-1 of a matrix given by row(n, values) (K doubles each) as E4M3 codes in the
+// blocked layout with kstore stored columns (dst zero-filled, so the padding is code 0) and
+// their scales rs[n] (smolexp_quantize_e4m3_rows, one row at a time).  False if a row
+// cannot be quantized.
+bool pack_e4m3(int N, int K, int kstore, const std::function<void(int, double*)>& row, uint8_t* dst, float* rs) {
+  std::vector<double> v(K);
+  std::vector<uint8_t> c(K);
+  for (int n = 0; n < N; ++n) {
+    row(n, v.data());
+    if (smolexp_quantize_e4m3_rows(v.data(), 1, K, c.data(), rs + n) != SMOLEXP_OK) return false;
+    for (int k = 0; k < K; ++k) dst[t16_off(n, k, kstore / 8)] = c[k];
+  }
+  return true;
+}
+
+// A row source over bf16 rows (K values each), each value times gain[k] when gain is given
+// (the RMSNorm fold; the product of two bf16 values is exact in double).
+std::function<void(int, double*)> bf16_rows(std::vector<const uint16_t*> rows, int K, const uint16_t* gain = nullptr) {
+  return [rows, K, gain](int n, double* out) {
+    for (int k = 0; k < K; ++k) out[k] = (double)bf2f(rows[n][k]) * (gain ? (double)bf2f(gain[k]) : 1.0);
+  };
 }
 
 // Row pointers of a row-major [N][ld] bf16 matrix, starting at column c0.
@@ -426,7 +489,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     auto gemm = [&](int probe, AMode am, EMode em, const GemmArgs& g0) -> hipError_t {
       GemmArgs g = g0;
       if (am == A_NORM) { g.A = wg.h16; g.lda = kKPad; }
-      const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em);
+      const GemmPlan plan = plan_for(g.M, g.N, g.K, am, em, g.wrs != nullptr);
       if (plan.kind == 2) {
         if (am == A_NORM) g.K = kKPad;
         record(probe, plan, am, em, g);
@@ -455,13 +518,13 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
       gt.N = kD; gt.K = kAD; gt.A = wg.x; gt.lda = kAD;
       gt.x = wg.x; gt.noise = c.x_in + qOff; gt.prev = c.prev ? c.prev + (size_t)b0 * c.d * kAD : nullptr;
       gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
-      gt.W = h->w_tin.w; gt.ldw = h->w_tin.ld; gt.w_scale = h->w_tin.scale; gt.bias = cvec + (size_t)k * kD;
+      set_w(gt, h->w_tin); gt.bias = cvec + (size_t)k * kD;
       gt.out16 = wg.s16; gt.ldo = kD;
       if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
 
       GemmArgs go = g;
       go.N = kD; go.K = kD; go.A = wg.s16; go.lda = kD;
-      go.W = h->w_t2.w; go.ldw = h->w_t2.ld; go.w_scale = h->w_t2.scale; go.bias = h->b_t2;
+      set_w(go, h->w_t2); go.bias = h->b_t2;
       go.h = wg.h; go.h16 = wg.h16;
       if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
 
@@ -472,7 +535,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
         if (!fold_q) {
           GemmArgs gq = g;
           gq.N = ld.self_attn ? kNQKV : kNQ; gq.K = kD;
-          gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
+          set_w(gq, ld.qkv);
           gq.q = wg.q; gq.kc = wg.kc; gq.vc = wg.vc; gq.ropeq = wg.ropeq;
           if ((e = norm_gemm(ld.self_attn ? PR_QKV : PR_QCROSS, E_QKV, gq)) != hipSuccess) return hip_fail(h, e, "qkv launch");
         }
@@ -485,7 +548,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
         aa.pv = kv + (size_t)l * kvLayer + kvLayer / 2 + kvOff;
         aa.mask = mask_g; aa.out = wg.o16; aa.B = Bg; aa.P = P;
         if (fold_q) {
-          aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale;
+          aa.wq = ld.qkv.w; aa.ldw = ld.qkv.ld; aa.w_scale = ld.qkv.scale; aa.wrs = ld.qkv.rs;
           aa.h16 = wg.h16; aa.inv_k = g.inv_k; aa.eps = g.eps; aa.ropeq = wg.ropeq;
         }
         const int pr = ld.self_attn ? PR_ATTN_SELF : PR_ATTN_CROSS;
@@ -499,24 +562,24 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
 
         GemmArgs gop = g;
         gop.N = kD; gop.K = kNQ; gop.A = wg.o16; gop.lda = kNQ;
-        gop.W = ld.o.w; gop.ldw = ld.o.ld; gop.w_scale = ld.o.scale; gop.h = wg.h; gop.h16 = wg.h16;
+        set_w(gop, ld.o); gop.h = wg.h; gop.h16 = wg.h16;
         if ((e = gemm(PR_O, A_F16, E_H_RESID, gop)) != hipSuccess) return hip_fail(h, e, "o launch");
 
         GemmArgs gg = g;
         gg.N = kGU; gg.K = kD;
-        gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = wg.u16; gg.ldo = kFFN;
+        set_w(gg, ld.gu); gg.out16 = wg.u16; gg.ldo = kFFN;
         if ((e = norm_gemm(PR_GU, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "gate/up launch");
 
         GemmArgs gd = g;
         gd.N = kD; gd.K = kFFN; gd.A = wg.u16; gd.lda = kFFN;
-        gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = wg.h; gd.h16 = wg.h16;
+        set_w(gd, ld.down); gd.h = wg.h; gd.h16 = wg.h16;
         if ((e = gemm(PR_DOWN, A_F16, E_H_RESID, gd)) != hipSuccess) return hip_fail(h, e, "down launch");
       }
 
       // final RMSNorm + action_out; Euler update x += dt v
       GemmArgs gv = g;
       gv.N = kAD; gv.K = kD;
-      gv.W = h->w_out.w; gv.ldw = h->w_out.ld; gv.w_scale = h->w_out.scale; gv.bias = h->b_out;
+      set_w(gv, h->w_out); gv.bias = h->b_out;
       gv.x = wg.x; gv.dt = h->dt;
       const size_t stepElems = (size_t)B * kChunk * kAD;
       if (c.velocity) {
@@ -683,7 +746,7 @@ int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, 
 
     GemmArgs gq = g;
     gq.N = kNQKV; gq.K = kLmD; gq.A = h->pf_h16; gq.lda = kLmD;
-    gq.W = ld.qkv.w; gq.ldw = ld.qkv.ld; gq.w_scale = ld.qkv.scale;
+    set_w(gq, ld.qkv);
     gq.q = h->pf_q; gq.kc = kcache; gq.vc = vcache; gq.seq = P; gq.ropeq = h->pf_ropeq;
     if ((e = gemm(A_NORM, E_PF_QKV, gq)) != hipSuccess) return hip_fail(h, e, "prefill qkv launch");
     if (l == L - 1) break;  // the last layer's keys and values are all the cache needs
@@ -697,17 +760,17 @@ int enqueue_prefill(smolexp_t h, const bf16_t* emb, const uint8_t* mask, int P, 
 
     GemmArgs go = g;
     go.N = kLmD; go.K = kNQ; go.A = h->pf_o16; go.lda = kNQ;
-    go.W = ld.o.w; go.ldw = ld.o.ld; go.w_scale = ld.o.scale; go.h = h->pf_h; go.h16 = h->pf_h16;
+    set_w(go, ld.o); go.h = h->pf_h; go.h16 = h->pf_h16;
     if ((e = gemm(A_F16, E_PF_RESID, go)) != hipSuccess) return hip_fail(h, e, "prefill o launch");
 
     GemmArgs gg = g;
     gg.N = kLmGU; gg.K = kLmD; gg.A = h->pf_h16; gg.lda = kLmD;
-    gg.W = ld.gu.w; gg.ldw = ld.gu.ld; gg.w_scale = ld.gu.scale; gg.out16 = h->pf_u16; gg.ldo = kLmFFN;
+    set_w(gg, ld.gu); gg.out16 = h->pf_u16; gg.ldo = kLmFFN;
     if ((e = gemm(A_NORM, E_SWIGLU, gg)) != hipSuccess) return hip_fail(h, e, "prefill gate/up launch");
 
     GemmArgs gd = g;
     gd.N = kLmD; gd.K = kLmFFN; gd.A = h->pf_u16; gd.lda = kLmFFN;
-    gd.W = ld.down.w; gd.ldw = ld.down.ld; gd.w_scale = ld.down.scale; gd.h = h->pf_h; gd.h16 = h->pf_h16;
+    set_w(gd, ld.down); gd.h = h->pf_h; gd.h16 = h->pf_h16;
     if ((e = gemm(A_F16, E_PF_RESID, gd)) != hipSuccess) return hip_fail(h, e, "prefill down launch");
   }
   return SMOLEXP_OK;
@@ -752,6 +815,27 @@ int smolexp_batch_groups(const smolexp_config* cfg, int batch, int* sizes) {
   if (sizes)
     for (int i = 0; i < G; ++i) sizes[i] = sz[i];
   return G;
+}
+
+int smolexp_quantize_e4m3_rows(const double* w, int rows, int cols, uint8_t* codes, float* scales) {
+  if (rows < 0 || cols < 0) return SMOLEXP_E_INVAL;
+  if (rows > 0 && (!scales || (cols > 0 && (!w || !codes)))) return SMOLEXP_E_INVAL;
+  for (int r = 0; r < rows; ++r) {
+    const double* row = w + (size_t)r * cols;
+    double amax = 0.0;
+    for (int k = 0; k < cols; ++k) {
+      if (!isfinite(row[k])) return SMOLEXP_E_INVAL;
+      amax = fmax(amax, fabs(row[k]));
+    }
+    int e = 0;
+    if (amax > 0) {
+      e = e4m3_row_exp(amax);
+      if (e < -126 || e > 127) return SMOLEXP_E_INVAL;  // the scale must be a normal float
+    }
+    scales[r] = ldexpf(1.f, e);
+    for (int k = 0; k < cols; ++k) codes[(size_t)r * cols + k] = e4m3_code(ldexp(row[k], -e));
+  }
+  return SMOLEXP_OK;
 }
 
 int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out) {
@@ -828,20 +912,36 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
   // Device layout: fp16 GEMM matrices in the blocked layout (gate/up interleaved in 16-row
   // blocks, Q/K rows permuted per head; Q/K/V and gate/up with K padded to 768 for the
   // large-M GEMM; the RMSNorm gains folded into Q/K/V, gate/up and action_out), the
-  // time-embedding half of W_t1 row-major for the prologue, fp32 biases.
+  // time-embedding half of W_t1 row-major for the prologue, fp32 biases.  With 8-bit weights
+  // the streamed matrices hold E4M3 codes at the same element offsets (one byte each), and
+  // each has an fp32 scale per stored row.
+  const bool w8 = h->cfg.weight_format == SMOLEXP_WEIGHTS_E4M3;
+  const size_t eb = w8 ? 1 : 2;  // bytes per streamed weight element
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  const size_t o_wtin = take((size_t)kD * kAD * 2), o_wt1e = take((size_t)kD * kD * 2);
-  const size_t o_wt2 = take((size_t)kD * kD * 2);
+  const size_t o_wtin = take((size_t)kD * kAD * eb), o_wt1e = take((size_t)kD * kD * 2);
+  const size_t o_wt2 = take((size_t)kD * kD * eb);
   const size_t o_bt1 = take(kD * 4), o_bt2 = take(kD * 4);
   std::vector<size_t> o_qkv(L), o_o(L), o_gu(L), o_dn(L);
   for (int l = 0; l < L; ++l) {
-    o_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * kKPad * 2);
-    o_o[l] = take((size_t)kD * kNQ * 2);
-    o_gu[l] = take((size_t)kGU * kKPad * 2);
-    o_dn[l] = take((size_t)kD * kFFN * 2);
+    o_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * kKPad * eb);
+    o_o[l] = take((size_t)kD * kNQ * eb);
+    o_gu[l] = take((size_t)kGU * kKPad * eb);
+    o_dn[l] = take((size_t)kD * kFFN * eb);
   }
-  const size_t o_wout = take((size_t)kAD * kD * 2), o_bout = take(kAD * 4);
+  const size_t o_wout = take((size_t)kAD * kD * eb), o_bout = take(kAD * 4);
+  // row scales of the 8-bit matrices (every row count here is a multiple of 16)
+  size_t r_tin = 0, r_t2 = 0, r_out = 0;
+  std::vector<size_t> r_qkv(L, 0), r_o(L, 0), r_gu(L, 0), r_dn(L, 0);
+  if (w8) {
+    r_tin = take(kD * 4); r_t2 = take(kD * 4); r_out = take(kAD * 4);
+    for (int l = 0; l < L; ++l) {
+      r_qkv[l] = take((size_t)(l % 2 == 0 ? kNQKV : kNQ) * 4);
+      r_o[l] = take(kD * 4);
+      r_gu[l] = take(kGU * 4);
+      r_dn[l] = take(kD * 4);
+    }
+  }
   std::vector<char> hostbuf;
   try {
     hostbuf.assign(off, 0);
@@ -877,6 +977,7 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     for (size_t i = 0; i < win.size(); ++i) win[i] = bf2f(p_win[i]);
     for (int i = 0; i < kD; ++i) bin[i] = bf2f(p_bin[i]);
     std::vector<float> wtin((size_t)kD * kAD);
+    std::vector<double> wtin_d(w8 ? (size_t)kD * kAD : 0);
     float* bt1 = (float*)(hb + o_bt1);
     float mx = 0.f;
     for (int j = 0; j < kD; ++j) {
@@ -892,25 +993,43 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
       for (int c = 0; c < kAD; ++c) {
         wtin[(size_t)j * kAD + c] = (float)acc[c];
         mx = fmaxf(mx, fabsf((float)acc[c]));
+        if (w8) wtin_d[(size_t)j * kAD + c] = acc[c];
       }
       bt1[j] = (float)bsum;
     }
-    s = shift_for(mx);
-    const float m = ldexpf(1.f, s);
-    half_t* dst = (half_t*)(hb + o_wtin);
-    for (int j = 0; j < kD; ++j)
-      for (int c = 0; c < kAD; ++c) dst[t16_off(j, c, kAD / 8)] = (half_t)(wtin[(size_t)j * kAD + c] * m);
-    w_tin.scale = ldexpf(1.f, -s); w_tin.ld = kAD;
+    if (w8) {  // the double product, quantized once
+      const double* wd = wtin_d.data();
+      if (!pack_e4m3(kD, kAD, kAD, [wd](int n, double* o) { memcpy(o, wd + (size_t)n * kAD, kAD * sizeof(double)); },
+                     (uint8_t*)(hb + o_wtin), (float*)(hb + r_tin)))
+        return fail(h, SMOLEXP_E_INVAL, "a weight row cannot take an 8-bit row scale (largest magnitude at most 448 x 2^-127)");
+    } else {
+      s = shift_for(mx);
+      const float m = ldexpf(1.f, s);
+      half_t* dst = (half_t*)(hb + o_wtin);
+      for (int j = 0; j < kD; ++j)
+        for (int c = 0; c < kAD; ++c) dst[t16_off(j, c, kAD / 8)] = (half_t)(wtin[(size_t)j * kAD + c] * m);
+      w_tin.scale = ldexpf(1.f, -s);
+    }
+    w_tin.ld = kAD;
   }
+  bool q_ok = true;  // every 8-bit row quantized
+  auto q8 = [&](int N, int K, int kstore, const std::function<void(int, double*)>& row, size_t o, size_t r) {
+    q_ok = q_ok && pack_e4m3(N, K, kstore, row, (uint8_t*)(hb + o), (float*)(hb + r));
+  };
   // the time-embedding half, row-major for the prologue, with a scale of its own
   std::vector<std::pair<const uint16_t*, size_t>> t1e_rows(kD);
   for (int j = 0; j < kD; ++j) t1e_rows[j] = {p_wt1 + (size_t)j * 2 * kD + kD, (size_t)kD};
   s = pick_shift(t1e_rows);
   for (int j = 0; j < kD; ++j) to_f16(t1e_rows[j].first, kD, s, (half_t*)(hb + o_wt1e) + (size_t)j * kD);
   const float s_t1e = ldexpf(1.f, -s);
-  s = pick_shift({{p_wt2, (size_t)kD * kD}});
-  pack_t16(rows_of(p_wt2, kD, kD), kD, kD, s, (half_t*)(hb + o_wt2));
-  w_t2.scale = ldexpf(1.f, -s); w_t2.ld = kD;
+  if (w8) {
+    q8(kD, kD, kD, bf16_rows(rows_of(p_wt2, kD, kD), kD), o_wt2, r_t2);
+  } else {
+    s = pick_shift({{p_wt2, (size_t)kD * kD}});
+    pack_t16(rows_of(p_wt2, kD, kD), kD, kD, s, (half_t*)(hb + o_wt2));
+    w_t2.scale = ldexpf(1.f, -s);
+  }
+  w_t2.ld = kD;
   vec32(p_bt2, kD, o_bt2);
 
   for (int l = 0; l < L; ++l) {
@@ -927,23 +1046,37 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     const uint16_t* pu = next((size_t)kFFN * kD);
     const uint16_t* pd = next((size_t)kD * kFFN);
     // q, k, v are consecutive in the manifest: one [1600, 720] matrix (or q alone)
+    ld.qkv.ld = kKPad; ld.o.ld = kNQ; ld.gu.ld = kKPad; ld.down.ld = kFFN;
+    if (w8) {
+      q8(self_attn ? kNQKV : kNQ, kD, kKPad, bf16_rows(rope_paired_rows(pq, pk, pvv, kD), kD, g1), o_qkv[l], r_qkv[l]);
+      q8(kD, kNQ, kNQ, bf16_rows(rows_of(po, kD, kNQ), kNQ), o_o[l], r_o[l]);
+      q8(kGU, kD, kKPad, bf16_rows(gate_up_rows(pg, pu, kFFN, kD), kD, g2), o_gu[l], r_gu[l]);
+      q8(kD, kFFN, kFFN, bf16_rows(rows_of(pd, kD, kFFN), kFFN), o_dn[l], r_dn[l]);
+      continue;
+    }
     s = pack_t16_gain(rope_paired_rows(pq, pk, pvv, kD), kD, kKPad, g1, (half_t*)(hb + o_qkv[l]));
-    ld.qkv.scale = ldexpf(1.f, -s); ld.qkv.ld = kKPad;
+    ld.qkv.scale = ldexpf(1.f, -s);
     s = pick_shift({{po, (size_t)kD * kNQ}});
     pack_t16(rows_of(po, kD, kNQ), kNQ, kNQ, s, (half_t*)(hb + o_o[l]));
-    ld.o.scale = ldexpf(1.f, -s); ld.o.ld = kNQ;
+    ld.o.scale = ldexpf(1.f, -s);
     s = pack_t16_gain(gate_up_rows(pg, pu, kFFN, kD), kD, kKPad, g2, (half_t*)(hb + o_gu[l]));
-    ld.gu.scale = ldexpf(1.f, -s); ld.gu.ld = kKPad;
+    ld.gu.scale = ldexpf(1.f, -s);
     s = pick_shift({{pd, (size_t)kD * kFFN}});
     pack_t16(rows_of(pd, kD, kFFN), kFFN, kFFN, s, (half_t*)(hb + o_dn[l]));
-    ld.down.scale = ldexpf(1.f, -s); ld.down.ld = kFFN;
+    ld.down.scale = ldexpf(1.f, -s);
   }
   const uint16_t* p_gf = next(kD);
   const uint16_t* p_wout = next((size_t)kAD * kD);
   const uint16_t* p_bout = next(kAD);
-  s = pack_t16_gain(rows_of(p_wout, kAD, kD), kD, kD, p_gf, (half_t*)(hb + o_wout));
-  w_out.scale = ldexpf(1.f, -s); w_out.ld = kD;
+  if (w8) {
+    q8(kAD, kD, kD, bf16_rows(rows_of(p_wout, kAD, kD), kD, p_gf), o_wout, r_out);
+  } else {
+    s = pack_t16_gain(rows_of(p_wout, kAD, kD), kD, kD, p_gf, (half_t*)(hb + o_wout));
+    w_out.scale = ldexpf(1.f, -s);
+  }
+  w_out.ld = kD;
   vec32(p_bout, kAD, o_bout);
+  if (!q_ok) return fail(h, SMOLEXP_E_INVAL, "a weight row cannot take an 8-bit row scale (largest magnitude at most 448 x 2^-127)");
 
   if (h->wmem) {
     (void)hipDeviceSynchronize();
@@ -969,6 +1102,15 @@ int smolexp_load_weights(smolexp_t h, const uint16_t* src, size_t n_elems) {
     layers[l].o.w = (half_t*)(db + o_o[l]);
     layers[l].gu.w = (half_t*)(db + o_gu[l]);
     layers[l].down.w = (half_t*)(db + o_dn[l]);
+  }
+  if (w8) {
+    h->w_tin.rs = (float*)(db + r_tin); h->w_t2.rs = (float*)(db + r_t2); h->w_out.rs = (float*)(db + r_out);
+    for (int l = 0; l < L; ++l) {
+      layers[l].qkv.rs = (float*)(db + r_qkv[l]);
+      layers[l].o.rs = (float*)(db + r_o[l]);
+      layers[l].gu.rs = (float*)(db + r_gu[l]);
+      layers[l].down.rs = (float*)(db + r_dn[l]);
+    }
   }
   h->layers = layers;
   // the time vectors of the schedule: W_t1[:, 720:] e(t_k) + b_t1 depends on the weights

@@ -89,10 +89,13 @@ struct GemmArgs {
   const float* prev;
   int ow_rows;
   float t;
-  // weights: fp16 [N][K] blocked (t16_off) with ldw = stored K, values scaled by 1 / w_scale
+  // weights: fp16 [N][K] blocked (t16_off) with ldw = stored K, values scaled by 1 / w_scale;
+  // or, when wrs is not nullptr, OCP E4M3 codes (one byte per element, the same element
+  // offsets) with real value = code value * wrs[n] (one power of two per stored row)
   const half_t* W;
   int ldw;
   float w_scale;
+  const float* wrs;
   // epilogue
   const float* bias;   // bias, or the per-step time vector for E_TIMEIN
   half_t* out16;       // fp16 activations, blocked (t16_off), ldo = stored K
@@ -128,6 +131,7 @@ struct AttnArgs {
   const half_t* wq;
   int ldw;
   float w_scale;
+  const float* wrs;      // not nullptr: wq holds E4M3 codes with these row scales (as GemmArgs)
   const half_t* h16;
   float inv_k, eps;
   const float2* ropeq;
@@ -224,7 +228,8 @@ GemmPlan plan_gemm(int M, int N, int K);
 hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArgs& a, hipStream_t s);
 // The kernel and tiles for one projection of the loop (K = logical width).  kind 2 = the
 // pipelined GEMM, which reads RMSNorm'd operands over K = kKPad stored columns.
-GemmPlan plan_for(int M, int N, int K, AMode am, EMode em);
+// w8: the weights are E4M3 codes, which only the register-resident kernels read (rb, cb <= 2).
+GemmPlan plan_for(int M, int N, int K, AMode am, EMode em, bool w8 = false);
 constexpr int kKPad = 768;  // stored columns of h16 and of the weights that read it (a multiple of 64)
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.

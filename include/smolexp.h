@@ -77,7 +77,18 @@ typedef struct smolexp_config {
                         Every group but the last holds a multiple of 8 queries.  The results
                         of a query depend on the size of its group only within the tolerances,
                         as for any change of batch composition. */
+  int weight_format; /* SMOLEXP_WEIGHTS_FP16 (0, the default) or SMOLEXP_WEIGHTS_E4M3 (an explicit
+                        opt-in, batches of at most 8 queries: max_batch 1..8).  See
+                        smolexp_load_weights. */
 } smolexp_config;
+
+/* Storage of the streamed weight matrices.  PyPI "mlx-smolvla", Run a checkpoint: 8-bit and
+ * 4-bit weight presets exist only as explicit opt-ins; dense weights stay the default. */
+enum {
+  SMOLEXP_WEIGHTS_FP16 = 0, /* every bf16 value re-encoded exactly (fp16, a power-of-two scale per matrix) */
+  SMOLEXP_WEIGHTS_E4M3 = 1  /* OCP FP8 E4M3 codes, one power-of-two scale per output row
+                               (smolexp_quantize_e4m3_rows): half the bytes, rounded weights */
+};
 
 /* Fill *cfg with the SmolVLA expert (16 layers, 10 steps, max_batch 128, max_prefix 512). Host only. */
 void smolexp_default_config(smolexp_config* cfg);
@@ -106,6 +117,21 @@ int smolexp_schedule(const smolexp_config* cfg, float* t_out, float* dt_out);
 int smolexp_batch_groups(const smolexp_config* cfg, int batch, int* sizes);
 
 /*
+ * Quantize a row-major [rows][cols] float64 matrix to OCP 8-bit floating point E4M3 (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite value 448, no
+ * infinities) with one scale per row, as smolexp_load_weights does for
+ * SMOLEXP_WEIGHTS_E4M3 (the pages name 8-bit presets, PyPI "mlx-smolvla", Run a checkpoint,
+ * but no format; this is the reading taken).  Row r's scale is the power of two
+ * 2^e, e the smallest integer with max_k |w[r][k]| / 2^e <= 448 (1 for an all-zero row), and
+ * codes[r][k] is the E4M3 code nearest to w[r][k] / 2^e, ties to even; the code value times
+ * scales[r] is the weight's 8-bit value.  codes: rows x cols bytes (caller-owned),
+ * scales: rows floats.  SMOLEXP_E_INVAL for NULL buffers, negative sizes, a value that is
+ * not finite, or a row whose scale would fall outside float's normal range (2^-126 .. 2^127);
+ * the outputs are then unspecified.  Host only; needs no GPU.
+ */
+int smolexp_quantize_e4m3_rows(const double* w, int rows, int cols, uint8_t* codes, float* scales);
+
+/*
  * Create a handle on HIP device hip_device: validates cfg, allocates the
  * workspace for max_batch x max_prefix and the weight store, and builds the
  * RoPE table.  *out is set only on success.  Release with smolexp_destroy.
@@ -129,6 +155,11 @@ int smolexp_create(const smolexp_config* cfg, int hip_device, smolexp_t* out);
  * [720,32] matrix, rounded once to fp16, plus a bias term), and the time
  * vectors of the configured schedule are computed; the caller may free
  * bf16_host on return.  Synchronous.
+ * With weight_format SMOLEXP_WEIGHTS_E4M3 every matrix the loop streams is stored as the
+ * loop applies it (gains folded; the [720,32] product formed in float64) and quantized by
+ * rows (smolexp_quantize_e4m3_rows); the time-embedding half of time_in, which meets only
+ * the fixed flow times, and the biases stay exact.  SMOLEXP_E_INVAL if a row cannot be
+ * quantized.  The prefill and the training step do not read these matrices.
  */
 int smolexp_load_weights(smolexp_t h, const uint16_t* bf16_host, size_t n_elems);
 

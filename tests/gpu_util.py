@@ -16,14 +16,18 @@ class Expert:
     """A library handle with loaded weights plus the oracle's float64 copy of them."""
 
     def __init__(self, n_layers, n_steps=10, max_batch=16, max_prefix=512, gain_seed=None, use_graphs=1,
-                 with_oracle=True):
+                 with_oracle=True, weight_format=fm.SMOLEXP_WEIGHTS_FP16):
         self.cfg = fm.smolexp_default_config(n_layers=n_layers, n_steps=n_steps, max_batch=max_batch,
-                                             max_prefix=max_prefix, use_graphs=use_graphs)
+                                             max_prefix=max_prefix, use_graphs=use_graphs,
+                                             weight_format=weight_format)
         self.named = synth.draw_weights(n_layers, gain_seed=gain_seed)
         self.h = fm.smolexp_create(self.cfg, 0)
         fm.smolexp_load_weights(self.h, synth.pack_weights(self.named, n_layers))
-        self.W = oracle.decode_weights(self.named) if with_oracle else None
         self.ocfg = oracle.ExpertConfig(n_layers=n_layers)
+        self.W = oracle.decode_weights(self.named) if with_oracle else None
+        if self.W is not None and weight_format == fm.SMOLEXP_WEIGHTS_E4M3:
+            # the 8-bit model: the streamed matrices quantized by rows, as the oracle defines it
+            self.W = oracle.quant.streamed_weights(self.W, self.ocfg)
 
     def sibling(self, n_steps, max_batch=4, max_prefix=256):
         """Another handle on the same weights with a different number of Euler steps."""

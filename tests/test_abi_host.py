@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(smolexp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(smolexp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -71,7 +71,8 @@ def test_weight_count_matches_manifest():
                                          ("ffn", 4096), ("chunk", 32), ("action_dim", 16), ("n_layers", 0),
                                          ("n_layers", 65), ("n_steps", 0), ("n_steps", 65), ("max_batch", 0),
                                          ("max_batch", 1025), ("max_prefix", 0), ("rms_eps", 0.0),
-                                         ("rope_theta", -1.0), ("t_max_period", 1e-3)])
+                                         ("rope_theta", -1.0), ("t_max_period", 1e-3), ("weight_format", 2),
+                                         ("weight_format", -1), ("batch_groups", 9)])
 def test_invalid_config_is_rejected_before_any_device_call(field, value):
     cfg = fm.smolexp_default_config(**{field: value})
     assert fm.smolexp_weight_count(cfg) == 0
@@ -114,3 +115,41 @@ def test_create_without_a_gpu_reports_a_hip_error():
     h = ctypes.c_void_p()
     assert fm.raw().smolexp_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == fm.SMOLEXP_E_HIP
     assert not h.value
+
+
+def test_eight_bit_weights_take_batches_of_at_most_eight():
+    ok = fm.smolexp_default_config(weight_format=fm.SMOLEXP_WEIGHTS_E4M3, max_batch=8)
+    assert fm.smolexp_weight_count(ok) == 98_210_912
+    bad = fm.smolexp_default_config(weight_format=fm.SMOLEXP_WEIGHTS_E4M3)  # max_batch 128
+    assert fm.smolexp_weight_count(bad) == 0
+    assert fm.smolexp_weight_count(fm.smolexp_default_config(weight_format=fm.SMOLEXP_WEIGHTS_E4M3, max_batch=9)) == 0
+
+
+def test_e4m3_row_quantizer_matches_the_oracle_code_for_code():
+    rng = np.random.default_rng(7)
+    parts = [
+        rng.standard_normal((40, 96)) * 0.02,                                       # weight-like rows
+        rng.standard_normal((16, 96)) * np.exp(rng.uniform(-30, 30, 16))[:, None],  # any magnitude
+        np.zeros((2, 96)),                                                          # all-zero rows
+    ]
+    W = np.concatenate(parts)
+    # rows with exact ties (midpoints between neighbouring codes after the row scale) and
+    # values in the subnormal range of the codes
+    W[3, :8] = [448.0, 1 + 1 / 16, 1 + 3 / 16, -(1 + 5 / 16), 0.5 * 2 ** -9, 1.5 * 2 ** -9, 7.5 * 2 ** -9, -224.0]
+    W[4] = np.linspace(-448, 448, 96) * 2.0 ** -12
+    W[5, 0] = -0.0
+    codes, scales = fm.smolexp_quantize_e4m3_rows(W)
+    oc, os_ = oracle.quant.quantize_rows(W)
+    np.testing.assert_array_equal(codes, oc)
+    np.testing.assert_array_equal(scales.astype(np.float64), os_)
+    np.testing.assert_array_equal(fm.smolexp_quantize_e4m3_rows(np.zeros((0, 5)))[0].shape, (0, 5))
+
+
+def test_e4m3_row_quantizer_rejects_what_it_cannot_encode():
+    for bad in (np.array([[1.0, np.nan]]), np.array([[np.inf, 0.0]]), np.array([[1e-40, 0.0]]),
+                np.array([[1e300, 1.0]])):
+        with pytest.raises(fm.SmolexpError):
+            fm.smolexp_quantize_e4m3_rows(bad)
+    raw = fm.raw()
+    assert raw.smolexp_quantize_e4m3_rows(None, 1, 1, None, None) == fm.SMOLEXP_E_INVAL
+    assert raw.smolexp_quantize_e4m3_rows(None, -1, 3, None, None) == fm.SMOLEXP_E_INVAL
