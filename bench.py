@@ -209,7 +209,7 @@ def summarize_mfma(counter_csv):
         print(f"| `{short(name)}` | {e[0]} | {100 * util:.1f}% | {e[3] / e[0] / 1e12:.4f} | {100 * e[4] / total:.1f} |")
 
 
-def kernel_costs(L, B, lengths, P):
+def kernel_costs(L, B, lengths, P, w8=False):
     """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
     launches per Euler step.
 
@@ -217,34 +217,38 @@ def kernel_costs(L, B, lengths, P):
     reads, once, at 2 bytes per element (the bf16 manifest; RMSNorm gains are folded into the
     matrices that follow them, action_in into a [720, 32] matrix with the action half of
     time_in, and the time-embedding half of time_in into one time vector per step, all when
-    the weights are loaded), plus the valid prefix K/V tokens the launch attends to.
+    the weights are loaded), plus the valid prefix K/V tokens the launch attends to.  With
+    8-bit weights (w8) a matrix costs 1 byte per element plus a 4-byte scale per row.
     Activation bytes (the fp16/bf16/fp32 rows each launch reads and writes) are counted apart.
     Flops are 2 per multiply-add; attention counts unmasked keys only.
     """
+    def mat(n, k):  # bytes of one streamed [n, k] matrix
+        return n * k + 4 * n if w8 else 2 * n * k
+
     M = 50 * B
     sum_nb = float(sum(lengths))
     kv = 5 * 64 * 2 * 2 * sum_nb            # one layer's valid prefix K and V
     keys_self = 50 * sum_nb + 1275 * B
     c = {}
-    c["qkv_self"] = (1600 * 720 * 2, M * 720 * 2 + M * 1600 * 2, 2.0 * M * 1600 * 720)
+    c["qkv_self"] = (mat(1600, 720), M * 720 * 2 + M * 1600 * 2, 2.0 * M * 1600 * 720)
     c["attn_self"] = (kv, M * 960 * 2 + M * 640 * 2 + M * 960 * 2, 4.0 * 64 * 15 * keys_self)
     if B <= CROSS_Q_MAX_BATCH:  # the cross layers' Q projection runs inside the attention launch
-        c["attn_cross"] = (960 * 720 * 2 + kv, M * 720 * 2 + M * 960 * 2,
+        c["attn_cross"] = (mat(960, 720) + kv, M * 720 * 2 + M * 960 * 2,
                            2.0 * M * 960 * 720 + 4.0 * 64 * 15 * 50 * sum_nb)
     else:
         c["attn_cross"] = (kv, M * 960 * 2 + M * 960 * 2, 4.0 * 64 * 15 * 50 * sum_nb)
     # o and down read-modify-write the fp32 residual and write its fp16 copy (10 B per element)
-    c["o"] = (720 * 960 * 2, M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
-    c["gate_up"] = (4096 * 720 * 2, M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
-    c["down"] = (720 * 2048 * 2, M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
-    c["action_out"] = ((32 * 720 + 32) * 2, M * 720 * 2 + M * 32 * 8, 2.0 * M * 32 * 720)
+    c["o"] = (mat(720, 960), M * 960 * 2 + M * 720 * 10, 2.0 * M * 720 * 960)
+    c["gate_up"] = (mat(4096, 720), M * 720 * 2 + M * 2048 * 2, 2.0 * M * 4096 * 720)
+    c["down"] = (mat(720, 2048), M * 2048 * 2 + M * 720 * 10, 2.0 * M * 720 * 2048)
+    c["action_out"] = (mat(32, 720) + 32 * 2, M * 720 * 2 + M * 32 * 8, 2.0 * M * 32 * 720)
     # the time MLP's first layer: the folded [720, 32] matrix and the step's time vector
-    c["time_in"] = ((720 * 32 + 720) * 2, M * 32 * 4 + M * 720 * 2, 2.0 * M * 720 * 32)
-    c["time_out"] = ((720 * 720 + 720) * 2, M * 720 * 2 + M * 720 * 6, 2.0 * M * 720 * 720)
+    c["time_in"] = (mat(720, 32) + 720 * 2, M * 32 * 4 + M * 720 * 2, 2.0 * M * 720 * 32)
+    c["time_out"] = (mat(720, 720) + 720 * 2, M * 720 * 2 + M * 720 * 6, 2.0 * M * 720 * 720)
     per_step = {"qkv_self": L // 2 + L % 2, "attn_self": L // 2 + L % 2, "attn_cross": L // 2, "o": L,
                 "gate_up": L, "down": L, "action_out": 1, "time_in": 1, "time_out": 1}
     if B > CROSS_Q_MAX_BATCH:  # the cross layers' Q projection is a launch of its own
-        c["q_cross"] = (960 * 720 * 2, M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
+        c["q_cross"] = (mat(960, 720), M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
         per_step["q_cross"] = L // 2
     return c, per_step
 
@@ -255,10 +259,10 @@ KERNEL_IDS = {"qkv_self": 0, "attn_self": 1, "attn_cross": 2, "o": 3, "gate_up":
 LOOP_ID = 7  # smolexp_time_kernel: the whole call
 
 
-def loop_algorithmic(L, B, lengths, n_steps):
+def loop_algorithmic(L, B, lengths, n_steps, w8=False):
     """Whole-call algorithmic bytes and flops: per step, every launch's algorithmic bytes
     (parameters once, valid prefix K/V once) and flops, from kernel_costs."""
-    c, per_step = kernel_costs(L, B, lengths, 0)
+    c, per_step = kernel_costs(L, B, lengths, 0, w8)
     byt = sum(c[k][0] * n for k, n in per_step.items())
     fl = sum(c[k][2] * n for k, n in per_step.items())
     return n_steps * byt, n_steps * fl
@@ -274,7 +278,7 @@ def roofline_of(bytes_, flops, seconds):
     return r
 
 
-def kernel_table(fm, h, cfg, L, B, lengths, P, reps):
+def kernel_table(fm, h, cfg, L, B, lengths, P, reps, w8=False):
     """Per timed kernel: the hook's HIP-event time per launch (one graph of `reps` launches,
     each repeating that kernel's launch of the next layer, and of the next query group, in the
     first step of the last call), launches per call, and the launch's algorithmic bytes,
@@ -284,7 +288,7 @@ def kernel_table(fm, h, cfg, L, B, lengths, P, reps):
     tot, launches = {}, {}
     b0 = 0
     for bg in groups:
-        costs, per_step = kernel_costs(L, bg, lengths[b0:b0 + bg], P)
+        costs, per_step = kernel_costs(L, bg, lengths[b0:b0 + bg], P, w8)
         b0 += bg
         for name, n in per_step.items():
             t = tot.setdefault(name, [0.0, 0.0, 0.0])
@@ -383,6 +387,41 @@ def large_batch_entry(fm, h, cfg, wl, calls, warmup, reps, stream):
     if d > 0:
         e["overwrite"] = overwrite_delta(fm, h, cfg, dev, dev["prev"], d, calls, 2, stream)
     return e
+
+
+def e4m3_entry(fm, wl, packed, n_steps, calls, warmup, reps, stream):
+    """The same workload on a handle with 8-bit weights (E4M3 codes, a scale per row):
+    median per-call time of `calls` HIP-event-timed calls, the per-kernel hook times and the
+    dominant kernel's roofline at the 8-bit byte count."""
+    import torch
+    L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
+    cfg = fm.smolexp_default_config(n_layers=L, n_steps=n_steps, max_batch=B, max_prefix=P,
+                                    weight_format=fm.SMOLEXP_WEIGHTS_E4M3)
+    h = fm.smolexp_create(cfg, 0)
+    try:
+        fm.smolexp_load_weights(h, packed)
+        dev = device_inputs(wl)
+        out = torch.empty((B, 50, 32), device="cuda")
+
+        def call():
+            fm.smolexp_denoise_ex(h, cfg, dev["kv"], dev["mask"], dev["noise"], out, prev_actions=dev["prev"],
+                                  overwrite_rows=d)
+
+        ms = median(timed_calls(call, calls, warmup, stream))
+        assert torch.isfinite(out).all().item(), "non-finite actions (8-bit weights)"
+        kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, reps, w8=True)
+    finally:
+        fm.smolexp_destroy(h)
+    dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
+    dom = kern[dom_name]
+    roof = roofline_of(dom["bytes"], dom["flops"], dom["avg_us"] * 1e-6)
+    roof.update(kernel=dom_name, avg_us=dom["avg_us"], algorithmic_bytes_per_launch=dom["bytes"])
+    lb, _ = loop_algorithmic(L, B, wl["lengths"], n_steps, w8=True)
+    return {"weight_format": "OCP FP8 E4M3 codes, one power-of-two scale per output row (opt-in)",
+            "ms_per_call": ms, "chunks_per_s": B / (ms * 1e-3), "calls": calls,
+            "loop_algorithmic_bytes_per_call": lb, "loop_hbm_frac": lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "roofline": roof, "kernels": {k: {"avg_us": v["avg_us"], "us_per_call": v["us_per_call"]}
+                                          for k, v in kern.items()}}
 
 
 def cpu_baseline(wl, n_steps, min_seconds, max_seconds, threads=None):
@@ -645,6 +684,8 @@ def main():
     ap.add_argument("--large-kernel-reps", type=int, default=20)
     ap.add_argument("--batch", type=int, default=None,
                     help="override the workload's batch (the first queries of its seeded draws)")
+    ap.add_argument("--weights", choices=("fp16", "e4m3"), default="fp16",
+                    help="weight storage of the timed handle (e4m3: 8-bit, batches up to 8)")
     ap.add_argument("--batch-groups", type=int, default=0,
                     help="concurrent query groups per call (0: the library's automatic choice)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -685,8 +726,10 @@ def main():
 
     wl = synth.make_workload(args.workload, batch=args.batch)
     L, B, P, d = wl["n_layers"], wl["batch"], wl["prefix_len"], wl["overwrite_rows"]
+    w8 = args.weights == "e4m3"
     cfg = fm.smolexp_default_config(n_layers=L, n_steps=args.n_steps, max_batch=B, max_prefix=P,
-                                    use_graphs=0 if args.no_graphs else 1, batch_groups=args.batch_groups)
+                                    use_graphs=0 if args.no_graphs else 1, batch_groups=args.batch_groups,
+                                    weight_format=fm.SMOLEXP_WEIGHTS_E4M3 if w8 else fm.SMOLEXP_WEIGHTS_FP16)
     h = fm.smolexp_create(cfg, 0)
     packed = synth.pack_weights(wl["weights"], L)
     fm.smolexp_load_weights(h, packed)
@@ -724,11 +767,11 @@ def main():
         fm.smolexp_destroy(h)
         return
     # per-kernel time per launch: HIP events on the library's stream around one graph of launches
-    kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, args.kernel_reps)
+    kern = kernel_table(fm, h, cfg, L, B, wl["lengths"], P, args.kernel_reps, w8=w8)
     dom_name = max(kern, key=lambda k: kern[k]["us_per_call"])
     dom = kern[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["avg_us"] * 1e-6)
-    roof["traffic"] = stored_traffic(args.workload, dom_name)
+    roof["traffic"] = None if w8 else stored_traffic(args.workload, dom_name)
     roof["kernel"] = dom_name
     roof["avg_us"] = dom["avg_us"]
     roof["algorithmic_bytes_per_launch"] = dom["bytes"]
@@ -738,7 +781,7 @@ def main():
                       "launch of the next layer (the loop's weights in turn)")
 
     ms = wall / args.steps * 1e3
-    lb, lf = loop_algorithmic(L, B, wl["lengths"], cfg.n_steps)
+    lb, lf = loop_algorithmic(L, B, wl["lengths"], cfg.n_steps, w8=w8)
     loop = {"algorithmic_bytes_per_call": lb, "algorithmic_flops_per_call": lf,
             "hbm_frac": lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "mfma_frac": lf / (ms * 1e-3) / (MFMA_F16_PEAK_TFS * 1e12),
@@ -757,13 +800,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "precision": "GEMM operands fp16 (the bf16 weights re-encoded exactly; RMSNorm gains folded into the "
-                     "following weights, rounded once; activations rounded to fp16), attention operands bf16 "
+        "precision": ("GEMM weights OCP E4M3 with a power-of-two scale per output row (8-bit opt-in), widened "
+                      "exactly to fp16; " if w8 else
+                      "GEMM operands fp16 (the bf16 weights re-encoded exactly; RMSNorm gains folded into the "
+                      "following weights, rounded once; ") +
+                     "activations rounded to fp16), attention operands bf16 "
                      "(the bf16 K/V cache as given, chunk Q/K/V and probabilities rounded to bf16), fp32 "
                      "accumulate, fp32 residual/norm scale/softmax/Euler state",
         "data": "synthetic (seeded: weights N(0,0.02) bf16, prefix K/V N(0,1) bf16, noise N(0,1))",
         "config": {"workload": args.workload, "n_layers": L, "batch": B, "prefix_len": P,
                    "n_steps": cfg.n_steps, "chunk": 50, "action_dim": 32, "overwrite_rows": d,
+                   "weights": args.weights,
                    "graphs": not args.no_graphs, "query_groups": fm.smolexp_batch_groups(cfg, B)},
         "roofline": roof,
         "loop_roofline": loop,
@@ -775,6 +822,9 @@ def main():
         prev1 = torch.from_numpy(synth.draw_prev_actions(1, 7)).cuda()
         line["overwrite_b1"] = overwrite_delta(fm, h, cfg, dev, prev1, 7, 20, 3, stream)
     fm.smolexp_destroy(h)
+    if B <= CROSS_Q_MAX_BATCH and not w8 and not args.no_extra:
+        # the same workload with 8-bit weights (half the weight bytes, rounded weights)
+        line["weights_e4m3"] = e4m3_entry(fm, wl, packed, cfg.n_steps, 20, 5, min(args.kernel_reps, 50), stream)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, device="cuda")
         dst = torch.empty_like(src)

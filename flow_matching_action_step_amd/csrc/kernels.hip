@@ -77,12 +77,18 @@ __device__ __forceinline__ uint4 w_to_f16x8(const uint2& c) {
 // One lane's weight fragment (8 consecutive k of one row): 16 bytes of fp16 or 8 of E4M3.
 template <bool W8>
 using WFrag = typename std::conditional<W8, uint2, uint4>::type;
+// The load is issued unconditionally (from offset 0 when !ok, inside the buffer) and zeroed
+// afterwards: a load under a branch made the compiler wait for it before issuing the next
+// ones (a register copy out of the branch), serializing the round trips.
 template <bool W8>
 __device__ __forceinline__ WFrag<W8> load_wfrag(const half_t* W, size_t off, bool ok) {
-  if constexpr (W8)
-    return ok ? *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(W) + off) : make_uint2(0, 0);
-  else
-    return ok ? *reinterpret_cast<const uint4*>(W + off) : make_uint4(0, 0, 0, 0);
+  if constexpr (W8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(W) + (ok ? off : 0));
+    return make_uint2(ok ? v.x : 0u, ok ? v.y : 0u);
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + (ok ? off : 0));
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  }
 }
 
 __device__ __forceinline__ uint4 pack8(const float* v) {
@@ -116,11 +122,16 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 
 // Eight consecutive A elements of row `row`, columns k..k+7, converted to the
 // fp16 MFMA operand (ok = inside the matrix; otherwise zeros).
-template <int AM>
+// UNCOND (fp16 operands): issue the load for every lane (element 0 when !ok) and zero it
+// afterwards, with no branch around the load (see load_wfrag).
+template <int AM, bool UNCOND = false>
 __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool ok, float rscale,
                                          bool write_x, float& vmax) {
   (void)rscale;
-  if constexpr (AM == A_F16 || AM == A_NORM) {
+  if constexpr ((AM == A_F16 || AM == A_NORM) && UNCOND) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + (ok ? t16_off(row, k, a.lda >> 3) : 0));
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  } else if constexpr (AM == A_F16 || AM == A_NORM) {
     return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + t16_off(row, k, a.lda >> 3))
               : make_uint4(0, 0, 0, 0);
   } else {  // A_X: Euler state; rows i < ow_rows of each chunk take the flow-path point t*eps + (1-t)*prev
@@ -384,31 +395,36 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   // epilogue inputs, loaded with the operands, in epilogue_tile's unit mapping: E_QKV thread
   // g < BM * CB owns row m0 + g / CB, column block g % CB; E_H_RESID lane r + 16 p of wave
   // w < RB owns row m0 + 16 w + r, columns n0 + 4 (p + 4 t).. for t < CB
+  // Rows or columns past the end load from row 0 / column 0, which exist; the epilogue reads
+  // only the units it owns.  No branch inside a wave around the loads: one made the compiler
+  // wait for them before issuing the operand loads.
   float4 pre[4];
   if constexpr (EM == E_QKV || EM == E_PF_QKV) {
-    if (tid < BM * CB) {
-      const int row = m0 + tid / CB, cb0 = n0 + (tid % CB) * 16;
+    if (w < (BM * CB + 63) / 64) {  // the waves that own units (uniform per wave)
+      const int g = tid < BM * CB ? tid : 0;
+      const int row = m0 + g / CB, cb0 = n0 + (g % CB) * 16;
       const int d0 = ((cb0 % kHD) / 16) * 8;
-      if (row < M && cb0 < N && cb0 / kHD < kHQ + kHKV) {
-        const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)row * (kHD / 2) + d0);
+      const float4* cs4 = reinterpret_cast<const float4*>(a.ropeq + (size_t)(row < M ? row : 0) * (kHD / 2) + d0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
-      }
+      for (int jj = 0; jj < 4; ++jj) pre[jj] = cs4[jj];
     }
   } else if constexpr (EM == E_H_RESID || EM == E_PF_RESID) {
     const int row = m0 + w * 16 + (lane & 15);
+    const bool rok = w < RB && row < M;
 #pragma unroll
     for (int t = 0; t < CB; ++t) {
       const int col = n0 + ((lane >> 4) + 4 * t) * 4;
-      if (w < RB && row < M && col < N) pre[t] = *reinterpret_cast<const float4*>(a.h + t32_off(row, col, resid_k4(EM)));
+      const bool ok = rok && col < N;
+      pre[t] = *reinterpret_cast<const float4*>(a.h + (ok ? t32_off(row, col, resid_k4(EM)) : 0));
     }
   }
   // the weight scale of the one output column this thread reduces (BN divides 512)
   static_assert(512 % BN == 0, "one reduction column per thread");
   float wsc = a.w_scale;
-  if constexpr (W8) {
+  if constexpr (W8) {  // loaded unconditionally (a clamped index), as load_wfrag does
     const int col = n0 + tid % BN;
-    wsc = col < N ? a.wrs[col] : 0.f;
+    const float v = a.wrs[col < N ? col : N - 1];
+    wsc = col < N ? v : 0.f;
   }
   WFrag<W8> wf[KPW][CB];
   uint4 af[KPW][RB];
@@ -426,7 +442,7 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
     for (int fm = 0; fm < RB; ++fm) {
       const int row = m0 + fm * 16 + (lane & 15);
       const bool ok = kok && row < M;
-      af[i][fm] = load_a8<AM>(a, row, k, ok, 1.f, nb == 0, xmax);
+      af[i][fm] = load_a8<AM, true>(a, row, k, ok, 1.f, nb == 0, xmax);
     }
   }
   f32x4 acc[RB][CB];

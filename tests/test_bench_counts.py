@@ -83,3 +83,21 @@ def test_denoise_counts_match_a_recount_from_the_manifest():
     # per step at batch 1, prefix 177: 194.3 MB of parameters and 3.6 MB of valid K/V
     byt, _ = bench.loop_algorithmic(16, 1, [177], 1)
     assert byt == 2 * 97_149_632 + 16 * 1280 * 177
+
+
+def test_denoise_counts_with_8bit_weights():
+    """8-bit weights: every streamed matrix costs 1 byte per element plus a 4-byte row scale
+    instead of 2 bytes per element; K/V, biases, time vectors and flops are unchanged."""
+    rows = elems = 0
+    for name, shape, kind in synth.manifest(16):
+        if kind != "w" or name == "action_in.w":
+            continue
+        out_, in_ = shape
+        if name == "time_in.w":
+            in_ = synth.ACTION_DIM  # the folded [720, 32] matrix
+        rows += out_
+        elems += out_ * in_
+    b16, f16 = bench.loop_algorithmic(16, 1, [177], 1)
+    b8, f8 = bench.loop_algorithmic(16, 1, [177], 1, w8=True)
+    assert f8 == f16
+    assert b16 - b8 == elems - 4 * rows
