@@ -1251,25 +1251,31 @@ __device__ __forceinline__ void attn_block(const bf16_t* sKb, const bf16_t* sVb,
 // buffer and the loaded vector is zeroed afterwards for masked or missing
 // keys, so all loads are in flight together.  Split in two so that a caller
 // can issue the loads early and store them to LDS later.
+// The mask bytes are loaded unconditionally too (index clamped to P - 1; every call has P >= 1)
+// and kept raw until store(): a byte load under a branch, compared at once, made the compiler
+// wait for it, and so for every K/V load before it, one round trip per few vectors.
 template <bool SELF, int RK, int NT>
 struct AttnStage {
   static constexpr int NV = (RK * 8 + NT - 1) / NT;  // 16-byte vectors of K (and of V) per thread
   static constexpr int NKIND = (RK + NT - 1) / NT;
   uint4 kv[NV], vv[NV];
-  bool kok[NV];
-  uint8_t kind[NKIND];
+  unsigned mv[NV];     // mask byte of each vector's key (meaningful for prefix keys)
+  unsigned mk[NKIND];  // mask byte of each kind entry's key
+  int r0, P;
 
-  __device__ __forceinline__ void issue(const AttnArgs& a, int b, int g, int r0) {
-    const int tid = threadIdx.x, P = a.P;
+  __device__ __forceinline__ void issue(const AttnArgs& a, int b, int g, int r0_) {
+    const int tid = threadIdx.x;
+    r0 = r0_;
+    P = a.P;
     const bf16_t* pk = a.pk + ((size_t)b * kHKV + g) * (size_t)P * kHD;
     const bf16_t* pv = a.pv + ((size_t)b * kHKV + g) * (size_t)P * kHD;
     const bf16_t* ck = SELF ? a.kc + ((size_t)b * kHKV + g) * kChunk * kHD : pk;
     const bf16_t* cv = SELF ? a.vc + ((size_t)b * kHKV + g) * kChunk * kHD : pv;
-    const uint8_t* mk = a.mask + (size_t)b * P;
+    const uint8_t* m = a.mask + (size_t)b * P;
 #pragma unroll
     for (int it = 0; it < NKIND; ++it) {
       const int j = r0 + tid + NT * it;
-      kind[it] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+      mk[it] = m[j < P ? j : P - 1];
     }
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
@@ -1280,18 +1286,24 @@ struct AttnStage {
       const size_t po = pre ? (size_t)j * kHD + c : c, co = (size_t)(j - P) * kHD + c;
       kv[it] = *reinterpret_cast<const uint4*>(chunk ? ck + co : pk + po);
       vv[it] = *reinterpret_cast<const uint4*>(chunk ? cv + co : pv + po);
-      kok[it] = pre ? mk[j] != 0 : chunk;
+      mv[it] = m[pre ? j : P - 1];
     }
   }
   __device__ __forceinline__ void store(bf16_t* sK, bf16_t* sV, uint8_t* sKind) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int it = 0; it < NKIND; ++it)
-      if (tid + NT * it < RK) sKind[tid + NT * it] = kind[it];
+    for (int it = 0; it < NKIND; ++it) {
+      const int j = r0 + tid + NT * it;
+      const uint8_t kind = j < P ? (mk[it] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+      if (tid + NT * it < RK) sKind[tid + NT * it] = kind;
+    }
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
-      if (!kok[it]) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
       const int v = tid + NT * it;
+      const int j = r0 + (min(v, RK * 8 - 1) >> 3);
+      const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
+      const bool kok = pre ? mv[it] != 0 : chunk;
+      if (!kok) kv[it] = vv[it] = make_uint4(0, 0, 0, 0);
       if (NV * NT == RK * 8 || v < RK * 8) {
         *reinterpret_cast<uint4*>(sK + (v >> 3) * kALD + (v & 7) * 8) = kv[it];
         *reinterpret_cast<uint4*>(sV + (v >> 3) * kALD + (v & 7) * 8) = vv[it];
@@ -1341,11 +1353,13 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
 
   bf16x8 qf[2];
   {
+    // loaded for every lane (a row past the end reads row 0 of the group's first head) and
+    // zeroed after, with no branch around the loads
     const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * kChunk + qi) * kHD + (lane >> 4) * 8;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint4 u = rvalid ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, u);
+      const uint4 u = *reinterpret_cast<const uint4*>(qp + kk * 32);
+      qf[kk] = __builtin_bit_cast(bf16x8, rvalid ? u : make_uint4(0, 0, 0, 0));
     }
   }
   f32x4 o[4];
@@ -1503,7 +1517,10 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int k = (w * KPW + i) * 32 + (lane >> 4) * 8;
-    af[i] = aok ? *reinterpret_cast<const uint4*>(a.h16 + t16_off(b * kChunk + qa, k, kKPad / 8)) : make_uint4(0, 0, 0, 0);
+    // every lane loads (rows past the chunk read the query's row 0) and the value is zeroed
+    // after, with no branch around the load
+    const uint4 av = *reinterpret_cast<const uint4*>(a.h16 + t16_off(b * kChunk + (aok ? qa : 0), k, kKPad / 8));
+    af[i] = aok ? av : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
       wf[i][cb] = load_wfrag<W8>(a.wq, t16_off(hq * kHD + cb * 16 + (lane & 15), k, a.ldw >> 3), true);
