@@ -135,30 +135,32 @@ __device__ __forceinline__ uint4 load_a8(const GemmArgs& a, int row, int k, bool
     return ok ? *reinterpret_cast<const uint4*>(static_cast<const half_t*>(a.A) + t16_off(row, k, a.lda >> 3))
               : make_uint4(0, 0, 0, 0);
   } else {  // A_X: Euler state; rows i < ow_rows of each chunk take the flow-path point t*eps + (1-t)*prev
-    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-    if (ok) {
-      const int ci = row % kChunk;
-      if (ci < a.ow_rows) {
-        const int b = row / kChunk;
-        const float* ep = a.noise + (size_t)row * kAD + k;
-        const float* pp = a.prev + ((size_t)b * a.ow_rows + ci) * kAD + k;
-        const float4 e0 = *reinterpret_cast<const float4*>(ep), e1 = *reinterpret_cast<const float4*>(ep + 4);
-        const float4 p0 = *reinterpret_cast<const float4*>(pp), p1 = *reinterpret_cast<const float4*>(pp + 4);
-        const float t = a.t, u = 1.0f - a.t;
-        v0 = make_float4(t * e0.x + u * p0.x, t * e0.y + u * p0.y, t * e0.z + u * p0.z, t * e0.w + u * p0.w);
-        v1 = make_float4(t * e1.x + u * p1.x, t * e1.y + u * p1.y, t * e1.z + u * p1.z, t * e1.w + u * p1.w);
-        if (write_x) {  // one workgroup column stores the overwritten rows into the state
-          float* xp = a.x + (size_t)row * kAD + k;
-          *reinterpret_cast<float4*>(xp) = v0;
-          *reinterpret_cast<float4*>(xp + 4) = v1;
-        }
-      } else {
-        const float* p = static_cast<const float*>(a.A) + (size_t)row * a.lda + k;
-        v0 = *reinterpret_cast<const float4*>(p);
-        v1 = *reinterpret_cast<const float4*>(p + 4);
+    // Every lane loads its state row (row 0 past the end); with an overwrite (a uniform
+    // kernel argument) also the noise and previous-chunk rows (row 0 where not overwritten);
+    // the values are selected after all loads are issued, with no branch around a load.
+    const float* xs = static_cast<const float*>(a.A) + (size_t)(ok ? row : 0) * a.lda + k;
+    const float4 x0 = *reinterpret_cast<const float4*>(xs), x1 = *reinterpret_cast<const float4*>(xs + 4);
+    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if (a.ow_rows > 0) {
+      const int ci = row % kChunk, b = row / kChunk;
+      const bool ow = ok && ci < a.ow_rows;
+      const float* ep = a.noise + (size_t)(ow ? row : 0) * kAD + k;
+      const float* pp = a.prev + ((size_t)(ow ? b : 0) * a.ow_rows + (ow ? ci : 0)) * kAD + k;
+      const float4 e0 = *reinterpret_cast<const float4*>(ep), e1 = *reinterpret_cast<const float4*>(ep + 4);
+      const float4 p0 = *reinterpret_cast<const float4*>(pp), p1 = *reinterpret_cast<const float4*>(pp + 4);
+      const float t = a.t, u = 1.0f - a.t;
+      const float w[8] = {t * e0.x + u * p0.x, t * e0.y + u * p0.y, t * e0.z + u * p0.z, t * e0.w + u * p0.w,
+                          t * e1.x + u * p1.x, t * e1.y + u * p1.y, t * e1.z + u * p1.z, t * e1.w + u * p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = ow ? w[e] : v[e];
+      if (ow && write_x) {  // one workgroup column stores the overwritten rows into the state
+        float* xp = a.x + (size_t)row * kAD + k;
+        *reinterpret_cast<float4*>(xp) = make_float4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<float4*>(xp + 4) = make_float4(w[4], w[5], w[6], w[7]);
       }
     }
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
     vmax = absmax4(absmax4(vmax, v[0], v[1], v[2], v[3]), v[4], v[5], v[6], v[7]);
     return pack8(v);
   }
