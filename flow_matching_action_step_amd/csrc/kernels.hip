@@ -455,6 +455,20 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
       af[i][fm] = load_a8<AM, UNC>(a, row, k, ok, 1.f, nb == 0, xmax);
     }
   }
+  // the residual modes finish in the waves that own the units (below): their bias and (8-bit
+  // weights) the row scales of their four columns, issued after the operands (the youngest
+  // loads; only the epilogue waits for them)
+  constexpr bool FUSED = EM == E_H_RESID || EM == E_H_BIAS || EM == E_PF_RESID;
+  float4 bias4[FUSED ? CB : 1], wsc4[FUSED ? CB : 1];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+      const int col = n0 + ((lane >> 4) + 4 * t) * 4, cc = col < N ? col : 0;
+      if constexpr (EM == E_H_BIAS) bias4[t] = *reinterpret_cast<const float4*>(a.bias + cc);
+      if constexpr (W8) wsc4[t] = *reinterpret_cast<const float4*>(a.wrs + cc);
+      else wsc4[t] = make_float4(a.w_scale, a.w_scale, a.w_scale, a.w_scale);
+    }
+  }
   f32x4 acc[RB][CB];
 #pragma unroll
   for (int fm = 0; fm < RB; ++fm)
@@ -488,6 +502,44 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
       for (int r = 0; r < 4; ++r)
         sRed[(w * BM + fm * 16 + (lane >> 4) * 4 + r) * BN + cb * 16 + (lane & 15)] = acc[fm][cb][r];
   __syncthreads();
+  if constexpr (FUSED) {
+    // Residual modes: lane r16 + 16 p of wave w < RB sums its 16-byte units (row m0 + 16 w + r16,
+    // columns n0 + 4 (p + 4 t) .. + 3) straight from the waves' partials, in the same order as
+    // the tile reduction below, and applies the epilogue: no second LDS tile, one barrier fewer.
+    const int r16 = lane & 15, part = lane >> 4;
+    float vmax = 0.f;
+    if (w < RB) {
+      const int r = w * 16 + r16, row = m0 + r;
+#pragma unroll
+      for (int t = 0; t < CB; ++t) {
+        const int c = part + 4 * t, col = n0 + c * 4;
+        if (row < M && col < N) {
+          float4 sm = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) {
+            const float4 pv = *reinterpret_cast<const float4*>(sRed + (w2 * BM + r) * BN + c * 4);
+            sm.x += pv.x; sm.y += pv.y; sm.z += pv.z; sm.w += pv.w;
+          }
+          const float4 v = make_float4(sm.x * wsc4[t].x, sm.y * wsc4[t].y, sm.z * wsc4[t].z, sm.w * wsc4[t].w);
+          float4* hp = reinterpret_cast<float4*>(a.h + t32_off(row, col, resid_k4(EM)));
+          float4 o;
+          if constexpr (EM == E_H_BIAS) {
+            o = make_float4(v.x + bias4[t].x, v.y + bias4[t].y, v.z + bias4[t].z, v.w + bias4[t].w);
+          } else {
+            const float4 hv = PRE ? pre[t] : *hp;
+            o = make_float4(hv.x + v.x, hv.y + v.y, hv.z + v.z, hv.w + v.w);
+          }
+          *hp = o;
+          vmax = absmax4(vmax, o.x, o.y, o.z, o.w);
+          union { half_t e[4]; uint2 u; } o16;
+          o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
+          *reinterpret_cast<uint2*>(a.h16 + t16_off(row, col, resid16_kc(EM))) = o16.u;
+        }
+      }
+    }
+    report_range(a.status, vmax, kRangeResidual);
+    return;
+  }
   for (int i = tid; i < BM * BN; i += 512) {
     float s = 0.f;
 #pragma unroll
