@@ -100,3 +100,31 @@ def test_fp8_graphs_match_direct_launches_and_repeat_bitwise():
             ex.close()
     np.testing.assert_array_equal(outs[0], outs[1])
     assert np.isfinite(outs[0]).all()
+
+
+def test_fp8_noalloc_matches_denoise():
+    """The entry point that allocates nothing, on a handle with 8-bit weights: bitwise equal to
+    smolexp_denoise on the same handle (the same kernels, the workspace in the library's
+    fixed array)."""
+    import ctypes
+    _say("8-bit weights: no-alloc denoise against denoise, 4 layers, batch 5")
+    ex = Expert(4, max_batch=8, max_prefix=200, with_oracle=False, weight_format=E4M3)
+    try:
+        wl = synth.make_workload("expert16_b16_pvar241", batch=5, with_weights=False)
+        B, P = 5, 200
+        kv = torch.from_numpy(np.ascontiguousarray(synth.draw_prefix_kv(4, B, P)).view(np.int16)).cuda()
+        mask = torch.from_numpy(synth.make_mask(B, P, [200, 150, 1, 77, 199])).cuda()
+        noise = torch.from_numpy(wl["noise"]).cuda()
+        ref = torch.full((B, 50, 32), float("nan"), device="cuda")
+        got = torch.full((B, 50, 32), float("nan"), device="cuda")
+        fm.smolexp_denoise(ex.h, ex.cfg, kv, mask, noise, ref)
+        rc = fm.raw().smolexp_denoise_noalloc(ex.h, ctypes.c_void_p(kv.data_ptr()), ctypes.c_void_p(mask.data_ptr()),
+                                              P, ctypes.c_void_p(noise.data_ptr()), ctypes.c_void_p(got.data_ptr()),
+                                              B, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, fm.smolexp_last_error(ex.h)
+        torch.cuda.synchronize()
+        r, g = ref.cpu().numpy(), got.cpu().numpy()
+        assert np.isfinite(r).all()
+        np.testing.assert_array_equal(g, r)
+    finally:
+        ex.close()
