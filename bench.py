@@ -209,6 +209,35 @@ def summarize_mfma(counter_csv):
         print(f"| `{short(name)}` | {e[0]} | {100 * util:.1f}% | {e[3] / e[0] / 1e12:.4f} | {100 * e[4] / total:.1f} |")
 
 
+def summarize_stalls(pass1_csv, pass2_csv):
+    """Per kernel, from two rocprofv3 --pmc runs of the same command: (1) SQ_WAVE_CYCLES,
+    SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY; (2) SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE.  Fractions of the wave cycles spent
+    waiting (waitcnt, barrier), waiting to issue and issuing; matrix-core busy (as in
+    summarize_mfma); LDS bank-conflict cycles per LDS-active cycle.  Prints a markdown table."""
+    import csv
+    tot = {}
+    for path in (pass1_csv, pass2_csv):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "smolexp::" not in r["Kernel_Name"]:
+                    continue
+                e = tot.setdefault(r["Kernel_Name"], {})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    short = lambda n: n.replace("void ", "").replace("smolexp::", "").split("(")[0]  # noqa: E731
+    print("| kernel | waiting (waitcnt, barrier) | waiting to issue | issuing | matrix cores busy | LDS bank conflicts |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, e in sorted(tot.items(), key=lambda kv: -kv[1].get("SQ_WAVE_CYCLES", 0.0)):
+        wc = e.get("SQ_WAVE_CYCLES", 0.0)
+        simd = e.get("GRBM_GUI_ACTIVE", 0.0) / 8 * 1024
+        if not wc or not simd:
+            continue
+        lds = e.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        print(f"| `{short(name)}` | {e.get('SQ_WAIT_ANY', 0.0) / wc:.2f} | {e.get('SQ_WAIT_INST_ANY', 0.0) / wc:.2f} | "
+              f"{e.get('SQ_ACTIVE_INST_ANY', 0.0) / wc:.2f} | {100 * e.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / simd:.1f}% | "
+              f"{e.get('SQ_LDS_BANK_CONFLICT', 0.0) / lds if lds else 0.0:.2f} |")
+
+
 def kernel_costs(L, B, lengths, P, w8=False):
     """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
     launches per Euler step.
@@ -695,11 +724,16 @@ def main():
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel averages of the whole calls and of the timing graphs, from a rocprofv3 "
                          "--kernel-trace of a bench command")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("PASS1_CSV", "PASS2_CSV"),
+                    help="print per-kernel wait / issue / MFMA-busy fractions from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
                     help="per-kernel matrix-core utilisation from a rocprofv3 --pmc run of the MFMA counters")
     args = ap.parse_args()
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_stalls:
+        summarize_stalls(*args.summarize_stalls)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
