@@ -440,8 +440,8 @@ def test_overwrite_closed_form_and_fixed_point():
 
 # ---------------------------------------------------------------- action and time embedding (embed)
 #
-# What fixes embed (BASELINE's reduced-expert configuration and noeira docs "SmolVLA",
-# Architecture, action-head row): action_in 32 -> 720, the sinusoidal time embedding
+# What fixes embed (noeira docs "SmolVLA", Architecture, action-head row): action_in
+# 32 -> 720, the sinusoidal time embedding
 # concatenated after the action embedding, a 1440 -> 720 projection with SiLU, then
 # 720 -> 720.  Degenerate weights reduce embed to closed forms that depend on each of
 # those choices: which half of time_in reads the time embedding, where the SiLU sits,
