@@ -1432,7 +1432,10 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
 
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
-    __syncthreads();
+    // before a later round, every wave must be done with the previous round's keys; before
+    // the first there is nothing to protect, and a barrier there (its fence waits for every
+    // load in flight) would hold the key loads back until the Q rows above had arrived
+    if (r0 > 0) __syncthreads();
     attn_stage<SELF, RK, NT>(a, b, g, r0, sK, sV, sKind);
     __syncthreads();
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
