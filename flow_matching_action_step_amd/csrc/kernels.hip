@@ -1345,7 +1345,9 @@ struct AttnStage {
       // K and V rows: 8 lanes per key (whole 128-byte rows)
       const int j = r0 + (v >> 3), c = (v & 7) * 8;
       const bool pre = j < P, chunk = SELF && !pre && j - P < kChunk;
-      const size_t po = pre ? (size_t)j * kHD + c : c, co = (size_t)(j - P) * kHD + c;
+      // 32-bit element offsets from the head's base pointers (P <= 4096 keys of 64 elements):
+      // cheaper address arithmetic ahead of the loads than 64-bit offsets
+      const unsigned po = pre ? (unsigned)(j * kHD + c) : (unsigned)c, co = (unsigned)((j - P) * kHD + c);
       kv[it] = *reinterpret_cast<const uint4*>(chunk ? ck + co : pk + po);
       vv[it] = *reinterpret_cast<const uint4*>(chunk ? cv + co : pv + po);
       mv[it] = m[pre ? j : P - 1];
@@ -1408,6 +1410,11 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
   if (u >= kHKV * a.B) return;
   const int g = u % kHKV, b = u / kHKV;
   const int P = a.P;
+  // the first round's key loads go out first: the setup below (the loop's invariants
+  // included) runs while they are in flight
+  AttnStage<SELF, RK, NT> st;
+  st.issue(a, b, g, 0);
+  __builtin_amdgcn_sched_barrier(0);
   const int rq = rgx * (16 * QG) + qg * 16 + (lane & 15);
   const bool rvalid = rq < 3 * kChunk;
   const int hq = 3 * g + (rvalid ? rq / kChunk : 0);
@@ -1432,11 +1439,13 @@ __global__ __launch_bounds__(64 * QG * KS) void attn_small_kernel(const AttnArgs
 
   const int NK = P + (SELF ? kChunk : 0);
   for (int r0 = 0; r0 < NK; r0 += RK) {
-    // before a later round, every wave must be done with the previous round's keys; before
-    // the first there is nothing to protect, and a barrier there (its fence waits for every
-    // load in flight) would hold the key loads back until the Q rows above had arrived
-    if (r0 > 0) __syncthreads();
-    attn_stage<SELF, RK, NT>(a, b, g, r0, sK, sV, sKind);
+    // before a later round, every wave must be done with the previous round's keys (the first
+    // round's loads were issued above, with nothing in LDS to protect)
+    if (r0 > 0) {
+      __syncthreads();
+      st.issue(a, b, g, r0);
+    }
+    st.store(sK, sV, sKind);
     __syncthreads();
     const int nb = min(NBLK, (NK - r0 + kKB - 1) / kKB);
     for (int blk = ks; blk < nb; blk += KS)
@@ -1592,6 +1601,9 @@ __global__ __launch_bounds__(512) void attn_cross_q_kernel(const AttnArgs a) {
   }
   AttnStage<false, RK, NT> st;
   st.issue(a, b, g, 0);
+  // the key loads go out before the projection's MFMAs, whose operand waits would otherwise
+  // hold them back until the projection operands had arrived
+  __builtin_amdgcn_sched_barrier(0);
 
   // (2) Q = fp16(h) W'^T on the matrix cores, and the rows' sums of squares
   f32x4 acc[4], sq = f32x4{0.f, 0.f, 0.f, 0.f};
