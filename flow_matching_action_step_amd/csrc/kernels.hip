@@ -976,19 +976,24 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   };
   // REG: the weight fragment is the MFMA's first operand, so the accumulator tile is C^T and
   // lane l holds row l % 16 with four consecutive columns 4 (l / 16) .. + 3
-  auto mma = [&](const f16x8* af, const f16x8* bw) {
+  // MFMAs lo .. hi - 1 of a k-step (fm-major over the FMW x FN tiles; the row sums of squares
+  // with the last)
+  auto mma_part = [&](const f16x8* af, const f16x8* bw, int lo, int hi) {
 #pragma unroll
-    for (int fm = 0; fm < FMW; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        if constexpr (REG) acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[fn], af[fm], acc[fm][fn], 0, 0, 0);
-        else acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
-      }
+    for (int t = 0; t < FMW * FN; ++t) {
+      if (t < lo || t >= hi) continue;
+      const int fm = t / FN, fn = t % FN;
+      if constexpr (REG) acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bw[fn], af[fm], acc[fm][fn], 0, 0, 0);
+      else acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    }
     if constexpr (NORM) {
+      if (hi == FMW * FN) {
 #pragma unroll
-      for (int fm = 0; fm < FMW; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
+        for (int fm = 0; fm < FMW; ++fm) sq[fm] = sumsq_mfma(af[fm], sq[fm]);
+      }
     }
   };
+  auto mma = [&](const f16x8* af, const f16x8* bw) { mma_part(af, bw, 0, FMW * FN); };
   static_assert(BK == 64, "two k-steps per slab");
   // Slabs kt .. kt+2 are in flight while slab kt is multiplied; slab kt + 3 is issued into
   // slab kt's stage once every wave has finished reading it.  Past the end, issue() reloads
@@ -1005,22 +1010,37 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   // last slab (columns 736..767) is zero padding on both sides, and its MFMAs are skipped.
   const bool pad_tail = NORM && EM != E_PF_QKV && K == kKPad;
   read_frags(0, 0, a0, b0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // In each half of a slab the first MFMA goes out before the next k-step's fragment reads:
+  // the wait the compiler puts in front of it (always lgkmcnt(0) here: it counts the LDS-DMA
+  // loads on that counter too) then covers only the fragments being multiplied.  Issued
+  // before it, the reads were waited for as well, and every k-step waited for the next
+  // one's reads before multiplying.  The last slab is peeled off so that the loop body has
+  // no branch: at a branch's join the compiler assumes the worst path and waits again.
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    mma_part(a0, b0, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(kt, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
+    mma_part(a0, b0, 1, FMW * FN);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      // this wave's reads of slab kt are done and its slab kt + 1 landed; then every wave's
-      __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
-      __builtin_amdgcn_s_barrier();
-      issue(kt + S, kt % S);
-      read_frags(kt + 1, 0, a0, b0);
-    }
+    // this wave's reads of slab kt are done and its slab kt + 1 landed; then every wave's
+    __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(kt + S, kt % S);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk || !pad_tail) mma(a1, b1);
+    mma_part(a1, b1, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt + 1, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_part(a1, b1, 1, FMW * FN);
     __builtin_amdgcn_sched_barrier(0);
   }
+  mma_part(a0, b0, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (!pad_tail) read_frags(nk - 1, 1, a1, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_part(a0, b0, 1, FMW * FN);
+  if (!pad_tail) mma(a1, b1);
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
   if constexpr (REG) {
     float rs[FMW];  // the weight scale (no RMSNorm on the residual projections)
