@@ -836,7 +836,7 @@ __device__ __forceinline__ void epilogue_regs_resid(const GemmArgs& a, const f32
 // Large-M GEMM with a multi-stage LDS pipeline
 // ----------------------------------------------------------------------------
 // BM x 128 tiles; each wave owns 16 FMW rows x 128 / WN columns.  The k-slabs
-// (BK = 64) rotate through an S-stage LDS ring filled by direct global->LDS
+// (BK = 64 or 32 columns) rotate through an S-stage LDS ring filled by direct global->LDS
 // loads (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at
 // base + 16 l), so the next slabs are in flight while one is multiplied,
 // without staging registers.  One load instruction moves four 16-row x
@@ -844,16 +844,20 @@ __device__ __forceinline__ void epilogue_regs_resid(const GemmArgs& a, const f32
 // operands) and they land in LDS in the same blocked order, where the 16 lanes
 // of a fragment read cover 256 consecutive bytes (no bank conflicts, no
 // swizzle).  Requirements (checked by the launcher): A is fp16 with
-// K % 64 == 0 (K = 720 operands are zero-padded to 768).  Waits are explicit:
+// K % BK == 0 (K = 720 operands are zero-padded to 768).  With BK = 32 a stage holds half
+// the columns, so the same LDS holds twice the stages: loads run further ahead of the
+// matrix cores at the same occupancy, for one barrier per k-step instead of per two.  Waits are explicit:
 // s_waitcnt vmcnt(n) + s_barrier, not __syncthreads (whose fence would wait
 // for every load in flight).
-constexpr int kBigBN = 128, kBigBK = 64;
+constexpr int kBigBN = 128;
 // Column groups of the tile -> XCD map (the rows are cut into 8 / GC groups).
 __host__ __device__ constexpr int tile_col_groups(int em) { return em == E_SWIGLU ? 4 : 1; }
 
-template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG>
+template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG, int BK>
 __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const GemmArgs a) {
-  constexpr int BN = kBigBN, BK = kBigBK, LDC = BN + 4;
+  constexpr int BN = kBigBN, LDC = BN + 4;
+  constexpr int CH = BK / 8, LPR = CH / 4;  // 16-byte chunks per row of a slab; load instructions per row block
+  static_assert(BK == 64 || BK == 32, "one or two k-steps per slab");
   constexpr int WM = BM / (16 * FMW), NW = WM * WN, FN = BN / 16 / WN;
   static_assert(WM * 16 * FMW == BM && FN * 16 * WN == BN, "waves tile the block");
   constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2, STAGE_BYTES = A_BYTES + W_BYTES;
@@ -924,28 +928,28 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   // matrix cores (row sums of squares on the diagonal), and 1/rms of each row scales the
   // finished sums.
 
-  // Load instruction `blk` of a tile: row block blk / 2, chunks (blk % 2) * 4 .. +3 of the slab;
-  // lane l moves row l % 16 of chunk l / 16 of those.  Row blocks past the last one holding
+  // Load instruction `blk` of a tile: row block blk / LPR, chunks (blk % LPR) * 4 .. +3 of the
+  // slab; lane l moves row l % 16 of chunk l / 16 of those.  Row blocks past the last one holding
   // a row < M (or a column < N) are clamped to it: they only feed outputs that are not stored.
   const half_t* Ab = static_cast<const half_t*>(a.A);
   const int kcA = a.lda >> 3, kcW = a.ldw >> 3;
   const int rbA_last = (M - 1) >> 4, rbW_last = (N - 1) >> 4;
   auto issue = [&](int kt, int stage) {
-    const int c0 = min(kt, nk - 1) * (BK / 8);  // past the end: reload the last slab (never read)
+    const int c0 = min(kt, nk - 1) * CH;  // past the end: reload the last slab (never read)
     char* base = smem + stage * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int blk = w * A_LOADS + i;
-      const int rb = min((m0 >> 4) + (blk >> 1), rbA_last);
-      const half_t* src = Ab + ((size_t)rb * kcA + c0 + (blk & 1) * 4) * 128 + lane * 8;
+      const int rb = min((m0 >> 4) + blk / LPR, rbA_last);
+      const half_t* src = Ab + ((size_t)rb * kcA + c0 + (blk % LPR) * 4) * 128 + lane * 8;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) {
       const int blk = w * W_LOADS + i;
-      const int nb = min((n0 >> 4) + (blk >> 1), rbW_last);
-      const half_t* src = a.W + ((size_t)nb * kcW + c0 + (blk & 1) * 4) * 128 + lane * 8;
+      const int nb = min((n0 >> 4) + blk / LPR, rbW_last);
+      const half_t* src = a.W + ((size_t)nb * kcW + c0 + (blk % LPR) * 4) * 128 + lane * 8;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(base + A_BYTES + blk * 1024), 16, 0,
                                        0);
@@ -969,10 +973,10 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
     const int ch = s * 4 + (lane >> 4);  // 16-byte chunk of this lane's fragment within the slab
 #pragma unroll
     for (int fm = 0; fm < FMW; ++fm)
-      af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * FMW + fm) * 8 + ch) * 128 + (lane & 15) * 8);
+      af[fm] = *reinterpret_cast<const f16x8*>(sA + ((wm * FMW + fm) * CH + ch) * 128 + (lane & 15) * 8);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
-      bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * FN + fn) * 8 + ch) * 128 + (lane & 15) * 8);
+      bw[fn] = *reinterpret_cast<const f16x8*>(sW + ((wn * FN + fn) * CH + ch) * 128 + (lane & 15) * 8);
   };
   // REG: the weight fragment is the MFMA's first operand, so the accumulator tile is C^T and
   // lane l holds row l % 16 with four consecutive columns 4 (l / 16) .. + 3
@@ -994,10 +998,10 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
     }
   };
   auto mma = [&](const f16x8* af, const f16x8* bw) { mma_part(af, bw, 0, FMW * FN); };
-  static_assert(BK == 64, "two k-steps per slab");
-  // Slabs kt .. kt+2 are in flight while slab kt is multiplied; slab kt + 3 is issued into
-  // slab kt's stage once every wave has finished reading it.  Past the end, issue() reloads
-  // the last slab into a stage nobody reads any more, which keeps the counts uniform.
+  // Slabs kt + 1 .. kt + S - 1 are in flight while slab kt is multiplied; slab kt + S is
+  // issued into slab kt's stage once every wave has finished reading it.  Past the end,
+  // issue() reloads the last slab into a stage nobody reads any more, which keeps the counts
+  // uniform.
   constexpr int WAIT1 = LOADS * (S - 2), WAIT2 = LOADS * (S - 1);
   static_assert(WAIT2 < 64, "vmcnt immediate range");
   constexpr int VM1 = (WAIT1 & 15) | ((WAIT1 >> 4) << 14), VM2 = (WAIT2 & 15) | ((WAIT2 >> 4) << 14);
@@ -1010,37 +1014,65 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   // last slab (columns 736..767) is zero padding on both sides, and its MFMAs are skipped.
   const bool pad_tail = NORM && EM != E_PF_QKV && K == kKPad;
   read_frags(0, 0, a0, b0);
-  // In each half of a slab the first MFMA goes out before the next k-step's fragment reads:
-  // the wait the compiler puts in front of it (always lgkmcnt(0) here: it counts the LDS-DMA
-  // loads on that counter too) then covers only the fragments being multiplied.  Issued
-  // before it, the reads were waited for as well, and every k-step waited for the next
-  // one's reads before multiplying.  The last slab is peeled off so that the loop body has
-  // no branch: at a branch's join the compiler assumes the worst path and waits again.
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  if constexpr (BK == 64) {
+    // In each half of a slab the first MFMA goes out before the next k-step's fragment reads:
+    // the wait the compiler puts in front of it (always lgkmcnt(0) here: it counts the LDS-DMA
+    // loads on that counter too) then covers only the fragments being multiplied.  Issued
+    // before it, the reads were waited for as well, and every k-step waited for the next
+    // one's reads before multiplying.  The last slab is peeled off so that the loop body has
+    // no branch: at a branch's join the compiler assumes the worst path and waits again.
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      mma_part(a0, b0, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt, 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_part(a0, b0, 1, FMW * FN);
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave's reads of slab kt are done and its slab kt + 1 landed; then every wave's
+      __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + S, kt % S);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_part(a1, b1, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt + 1, 0, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_part(a1, b1, 1, FMW * FN);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mma_part(a0, b0, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(kt, 1, a1, b1);
+    if (!pad_tail) read_frags(nk - 1, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     mma_part(a0, b0, 1, FMW * FN);
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave's reads of slab kt are done and its slab kt + 1 landed; then every wave's
-    __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-    issue(kt + S, kt % S);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_part(a1, b1, 0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(kt + 1, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_part(a1, b1, 1, FMW * FN);
-    __builtin_amdgcn_sched_barrier(0);
+    if (!pad_tail) mma(a1, b1);
+  } else {
+    // one k-step per slab: the same order (first MFMA, then the next slab's reads, then the
+    // rest), with the barrier between the first MFMA and the reads
+    const int nkc = pad_tail ? nk - 1 : nk;  // slabs multiplied
+    auto step = [&](int kt, const f16x8* ca, const f16x8* cb, f16x8* na, f16x8* nb) {
+      mma_part(ca, cb, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(VM1 | (7 << 4) | (0 << 8));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + S, kt % S);
+      read_frags(kt + 1, 0, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_part(ca, cb, 1, FMW * FN);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 2 < nkc; kt += 2) {
+      step(kt, a0, b0, a1, b1);
+      step(kt + 1, a1, b1, a0, b0);
+    }
+    if (kt + 1 < nkc) {
+      step(kt, a0, b0, a1, b1);
+      mma(a1, b1);
+    } else {
+      mma(a0, b0);
+    }
   }
-  mma_part(a0, b0, 0, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  if (!pad_tail) read_frags(nk - 1, 1, a1, b1);
-  __builtin_amdgcn_sched_barrier(0);
-  mma_part(a0, b0, 1, FMW * FN);
-  if (!pad_tail) mma(a1, b1);
   __builtin_amdgcn_s_waitcnt(0);  // the trailing (unused) slabs must land before LDS is reused
   if constexpr (REG) {
     float rs[FMW];  // the weight scale (no RMSNorm on the residual projections)
@@ -1070,34 +1102,41 @@ __global__ __launch_bounds__(64 * (BM / (16 * FMW)) * WN, 1) void gemm_big(const
   epilogue_tile<EM, BM, BN, LDC, 64 * NW, PRE, true>(a, sC, m0, n0, pre);
 }
 
-template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG = false>
+template <int EM, bool NORM, int BM, int FMW, int WN, int S, bool REG = false, int BK = 64>
 static hipError_t launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 64 * (BM / (16 * FMW)) * WN, GC = tile_col_groups(EM), GR = 8 / GC;
   const int nM = (a.M + BM - 1) / BM, nN = (a.N + kBigBN - 1) / kBigBN;
-  if (a.K % kBigBK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
+  if (a.K % BK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
   // every XCD gets as many workgroups as its largest share of tiles
   const int per = GC == 1 ? (nM * nN + 7) / 8 : ((nN + GC - 1) / GC) * ((nM + GR - 1) / GR);
-  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S, REG>), dim3(8 * per), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gemm_big<EM, NORM, BM, FMW, WN, S, REG, BK>), dim3(8 * per), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 // Configurations: BM x 128 tiles of waves of 32 x 64 (eight waves at BM = 128, four at 64)
 // and an S-stage ring.  Measured with the weights cycling through a 250 MB footprint,
 // against 256-row tiles, four-wave 64 x 64 shapes and 3/4-stage rings: 128 rows and two
-// stages (64 KB of LDS, two workgroups per CU) for Q/K/V and gate/up everywhere (gate/up at
+// 64-column stages (64 KB of LDS, two workgroups per CU) for Q/K/V and gate/up (gate/up at
 // M = 3200: 29 us against 39 with a 4-stage ring); for o and down, whose 720 columns give few
 // tiles, a 4-stage ring up to M = 4800 (down at 3200: 21.8 against 24.1 us) and 64-row tiles
-// at M <= 2400 (down at 1600: 19.7 against 23.2).
+// at M <= 2400 (down at 1600: 19.7 against 23.2).  Up to the denoising loop's 6400 rows the
+// 128 x 128 Q/K/V and gate/up tiles hold four 32-column stages instead (the same 64 KB; three
+// k-steps of loads ahead instead of two): batch 64 14.81 -> 14.66 ms, batch 128 23.57 ->
+// 23.39, same bits; five stages were slower, and so was the prefix prefill's gate/up at 16448
+// rows (7.665 -> 7.686 ms a call), which keeps the two 64-column stages.
+constexpr int kSlab32MaxRows = 6400;
 hipError_t launch_gemm_big(const GemmPlan& p, EMode em, bool norm, const GemmArgs& a, hipStream_t s) {
   const bool narrow = p.bm == 64 && p.fmw == 1;  // 64-row tiles of eight waves (16 rows each)
   switch (em) {
     case E_QKV:
       if (!norm) return hipErrorInvalidValue;
       if (narrow) return launch_gemm_dma<E_QKV, true, 64, 1, 2, 4>(a, s);
+      if (a.M <= kSlab32MaxRows) return launch_gemm_dma<E_QKV, true, 128, 2, 2, 4, false, 32>(a, s);
       return launch_gemm_dma<E_QKV, true, 128, 2, 2, 2>(a, s);
     case E_SWIGLU:
       if (!norm) return hipErrorInvalidValue;
       if (narrow) return launch_gemm_dma<E_SWIGLU, true, 64, 1, 2, 4>(a, s);
+      if (a.M <= kSlab32MaxRows) return launch_gemm_dma<E_SWIGLU, true, 128, 2, 2, 4, false, 32>(a, s);
       return launch_gemm_dma<E_SWIGLU, true, 128, 2, 2, 2>(a, s);
     case E_H_RESID:
       if (norm) return hipErrorInvalidValue;
