@@ -1185,7 +1185,8 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em, bool w8) {
     return p;
   };
   if (w8) {  // E4M3 weights (batches of at most 8 queries): the register-resident K split only
-    if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
+    // batch 1: the fp16 splits below (3.134 -> 3.095 ms a chunk)
+    if (M <= 64) return em == E_SWIGLU ? skinny(2, 2) : em == E_QKV ? skinny(1, 2) : skinny(1, 1);
     return skinny(2, em == E_ACTOUT ? 1 : 2);
   }
   auto big = [&](int bm = 128, int stages = 2, int fmw = 2, int reg = 0) {
@@ -1193,7 +1194,12 @@ GemmPlan plan_for(int M, int N, int K, AMode am, EMode em, bool w8) {
     b.kind = 2; b.bm = bm; b.stages = stages; b.fmw = fmw; b.reg = reg;
     return b;
   };
-  if (M <= 64) return skinny(1, em == E_SWIGLU ? 2 : 1);
+  // batch 1 (measured against one or two row blocks x one or two column blocks for each
+  // projection, and 4 x 1, 1 x 4 for gate/up): gate/up on 32-row tiles of two column blocks
+  // (4.38 -> 4.34 us a launch: half the workgroups reload the rows), Q/K/V on 16-row tiles of
+  // two column blocks (3.34 -> 3.20 us); o, down and the time MLP keep one 16 x 16 block
+  // (3.173 -> 3.153 ms a chunk)
+  if (M <= 64) return em == E_SWIGLU ? skinny(2, 2) : em == E_QKV ? skinny(1, 2) : skinny(1, 1);
   (void)am;
   switch (em) {
     case E_QKV:
