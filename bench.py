@@ -33,7 +33,7 @@ COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
 KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed kernel
     "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_small_kernel<true,", "attn_cross": "attn_cross_q_kernel<",
     "o": "gemm_skinny<0, 3, 4,", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8,",
-    "action_out": "gemm_skinny<1, 6,", "time_in": "gemm_skinny<2, 1,", "time_out": "gemm_skinny<0, 2,",
+    "action_out": "step_boundary_kernel<", "time_in": "gemm_skinny<2, 1,", "time_out": "gemm_skinny<0, 2,",
 }
 
 
@@ -242,6 +242,13 @@ def kernel_costs(L, B, lengths, P, w8=False):
     """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
     launches per Euler step.
 
+    Up to BOUNDARY_MAX_ROWS chunk rows (the library's register-resident K split of action_out and
+    of the time MLP's first layer) the end of one step and the start of the next are one launch:
+    "action_out" then stands for that step-boundary launch (action_out + Euler + the next step's
+    overwrite and time-MLP first layer) and "time_in" is not a kernel of its own.  Counted as one
+    such launch per step (the call's first time_in and last action_out run alone, which adds up
+    to the same work per call).
+
     Algorithmic bytes follow the counting of the loop's roofline: the parameters the launch
     reads, once, at 2 bytes per element (the bf16 manifest; RMSNorm gains are folded into the
     matrices that follow them, action_in into a [720, 32] matrix with the action half of
@@ -276,6 +283,9 @@ def kernel_costs(L, B, lengths, P, w8=False):
     c["time_out"] = (mat(720, 720) + 720 * 2, M * 720 * 2 + M * 720 * 6, 2.0 * M * 720 * 720)
     per_step = {"qkv_self": L // 2 + L % 2, "attn_self": L // 2 + L % 2, "attn_cross": L // 2, "o": L,
                 "gate_up": L, "down": L, "action_out": 1, "time_in": 1, "time_out": 1}
+    if M <= BOUNDARY_MAX_ROWS:  # the step boundary: action_out and the next time_in in one launch
+        c["action_out"] = tuple(x + y for x, y in zip(c["action_out"], c.pop("time_in")))
+        del per_step["time_in"]
     if B > CROSS_Q_MAX_BATCH:  # the cross layers' Q projection is a launch of its own
         c["q_cross"] = (mat(960, 720), M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
         per_step["q_cross"] = L // 2
@@ -283,6 +293,7 @@ def kernel_costs(L, B, lengths, P, w8=False):
 
 
 CROSS_Q_MAX_BATCH = 8  # largest batch whose cross layers fold the Q projection into attention (library constant)
+BOUNDARY_MAX_ROWS = 2400  # largest query group (chunk rows) whose step boundary is one launch (library plan)
 KERNEL_IDS = {"qkv_self": 0, "attn_self": 1, "attn_cross": 2, "o": 3, "gate_up": 4, "down": 5, "action_out": 6,
               "q_cross": 8, "time_in": 9, "time_out": 10}
 LOOP_ID = 7  # smolexp_time_kernel: the whole call

@@ -558,6 +558,178 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
   epilogue_tile<EM, BM, BN, LDC, 512, PRE>(a, sC, m0, n0, pre);
 }
 
+// ----------------------------------------------------------------------------
+// Step boundary: the final RMSNorm + action_out + Euler update of step k, then the prefix
+// overwrite and the time MLP's first layer (action_in folded in) of step k + 1
+// ----------------------------------------------------------------------------
+// Both halves are row-local: an action row needs one row of fp16(h) and the whole of
+// action_out's weights, and the next step's time-MLP row needs that action row and the whole
+// [720][32] matrix.  A workgroup of eight waves takes 16 rows and one of G groups of the time
+// MLP's 45 column tiles: the waves split action_out's K as gemm_skinny does (three k-steps
+// each, both 16-column blocks; the G workgroups of a row block repeat this small product), the
+// partial sums meet in LDS, one thread per (row, action column) finishes the Euler update and
+// the overwrite (group 0 stores the state and the records), and the waves then multiply the 16
+// updated rows by the group's column tiles (K = 32, one MFMA per tile).  The state of step k
+// is read from v.x and that of step k + 1 written to t.x, another buffer, since every
+// workgroup of a row block reads the old state.  Every sum is formed from the same operands in the same order as
+// in the two separate launches (action_out, then time_in), so the results are the same bits.
+// v: action_out's arguments (A_NORM operand h16, bias, x, dt, records); t: the next step's
+// time_in arguments (its flow time, time vector, overwrite rows, output s16).
+struct BoundaryArgs {
+  GemmArgs v, t;
+};
+
+// a * b + c with the product rounded before the sum (no fused multiply-add), as when the product
+// is stored and the sum formed later
+__device__ __forceinline__ float mul_add_rounded(float a, float b, float c) {
+#pragma clang fp contract(off)
+  return a * b + c;
+}
+
+template <bool W8>
+__global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs ba) {
+  constexpr int NW = 8, KPW = 3, NCB = kAD / 16, NTT = kD / 16, TPW = (NTT + NW - 1) / NW;
+  static_assert(NCB * 16 == kAD && NTT * 16 == kD && 16 * kAD == 512, "one (row, action column) per thread");
+  const GemmArgs& a = ba.v;
+  const GemmArgs& t = ba.t;
+  __shared__ float sRed[NW * 16 * kAD];
+  __shared__ float sQ[NW][16];
+  __shared__ __attribute__((aligned(16))) float sX[16][kAD];
+  __shared__ __attribute__((aligned(16))) half_t sZ[16][kD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = gridDim.x / ((a.M + 15) / 16), rb = blockIdx.x / G, cg = blockIdx.x % G;
+  const int M = a.M, K = a.K, m0 = rb * 16;
+  const int nks = (K + 31) / 32, kl = (lane >> 4) * 8;
+  const int t_lo = cg * NTT / G, t_hi = (cg + 1) * NTT / G;  // this workgroup's column tiles
+
+  // every load first: action_out's operands (as gemm_skinny<A_NORM, E_ACTOUT, 3, 1, 2>), the time
+  // MLP's weight fragments and time-vector entries of this wave's column tiles, the thread's
+  // Euler-update inputs and its overwrite inputs (unconditional, clamped to row 0)
+  WFrag<W8> wf[KPW][NCB];
+  uint4 af[KPW];
+  float unused_max = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int ks = w * KPW + i, k = ks * 32 + kl;
+    const bool kok = ks < nks && k < K;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      wf[i][cb] = load_wfrag<W8, true>(a.W, t16_off(cb * 16 + (lane & 15), k, a.ldw >> 3), kok);
+    const int row = m0 + (lane & 15);
+    af[i] = load_a8<A_NORM, true>(a, row, k, kok && row < M, 1.f, false, unused_max);
+  }
+  WFrag<W8> wt[TPW];
+  float tb[TPW], ts[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int n = t_lo + w + NW * i, col = (n < t_hi ? n : 0) * 16 + (lane & 15);
+    wt[i] = load_wfrag<W8, true>(t.W, t16_off(col, kl, t.ldw >> 3), n < t_hi);
+    tb[i] = t.bias[col];
+    ts[i] = W8 ? t.wrs[col] : t.w_scale;
+  }
+  const int r = tid / kAD, c = tid % kAD, row = m0 + r;
+  const bool rok = row < M;
+  const size_t xi = (size_t)(rok ? row : 0) * kAD + c;
+  const float xold = a.x[xi], bo = a.bias[c], vsc = W8 ? a.wrs[c] : a.w_scale;
+  const int ci = row % kChunk, bq = row / kChunk;
+  const bool ow = rok && ci < t.ow_rows;
+  float e_ow = 0.f, p_ow = 0.f;
+  if (t.ow_rows > 0) {  // uniform kernel argument
+    e_ow = t.noise[(size_t)(ow ? row : 0) * kAD + c];
+    p_ow = t.prev[((size_t)(ow ? bq : 0) * t.ow_rows + (ow ? ci : 0)) * kAD + c];
+  }
+
+  // action_out: this wave's K slice of both column blocks, and of each row's sum of squares
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[i]),
+                                                       __builtin_bit_cast(f16x8, w_to_f16x8(wf[i][cb])), acc[cb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) sq = sumsq_mfma(__builtin_bit_cast(f16x8, af[i]), sq);
+  if (((lane & 15) >> 2) == (lane >> 4)) sQ[w][lane & 15] = sq[lane & 3];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sRed[(w * 16 + (lane >> 4) * 4 + rr) * kAD + cb * 16 + (lane & 15)] = acc[cb][rr];
+  __syncthreads();
+
+  // thread (r, c): the velocity, the Euler step, the records, then the next step's overwrite
+  {
+    float sm = 0.f, q = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) sm += sRed[(w2 * 16 + r) * kAD + c];
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) q += sQ[w2][r];
+    const float u = mul_add_rounded(sm, vsc * rms_scale(a, q), bo);
+    const float x1 = xold + a.dt * u;
+    const float tt = t.t, om = 1.0f - t.t;
+    const float xn = ow ? __builtin_fmaf(tt, e_ow, om * p_ow) : x1;  // t eps + (1 - t) prev, as time_in forms it
+    if (rok && cg == 0) {
+      t.x[xi] = xn;
+      if (a.vel_out) a.vel_out[xi] = u;
+      if (a.st_out) a.st_out[xi] = x1;
+    }
+    sX[r][c] = rok ? xn : 0.f;
+  }
+  __syncthreads();
+
+  // time MLP, first layer: z = SiLU(W x + time vector) for this wave's column tiles
+  float v8[8];
+  {
+    const float4 x0 = *reinterpret_cast<const float4*>(&sX[lane & 15][kl]);
+    const float4 x4 = *reinterpret_cast<const float4*>(&sX[lane & 15][kl + 4]);
+    v8[0] = x0.x; v8[1] = x0.y; v8[2] = x0.z; v8[3] = x0.w; v8[4] = x4.x; v8[5] = x4.y; v8[6] = x4.z; v8[7] = x4.w;
+  }
+  const float xmax = absmax4(absmax4(0.f, v8[0], v8[1], v8[2], v8[3]), v8[4], v8[5], v8[6], v8[7]);
+  const f16x8 xa = __builtin_bit_cast(f16x8, pack8(v8));
+  float zmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int n = t_lo + w + NW * i;
+    if (n >= t_hi) break;  // uniform per wave
+    const f32x4 z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(f16x8, w_to_f16x8(wt[i])),
+                                                           f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float sv = silu(mul_add_rounded(z[rr], ts[i], tb[i]));
+      zmax = fmaxf(zmax, fabsf(sv));
+      sZ[(lane >> 4) * 4 + rr][n * 16 + (lane & 15)] = (half_t)sv;
+    }
+  }
+  report_range(t.status, fmaxf(xmax, zmax), kRangeTime);
+  __syncthreads();
+  const int kco = t.ldo >> 3;
+  const int nch = (t_hi - t_lo) * 2;  // 8-column chunks of the group
+  for (int uu = tid; uu < 16 * nch; uu += 512) {
+    const int rr = uu / nch, ch = t_lo * 2 + uu % nch;
+    if (m0 + rr < M)
+      *reinterpret_cast<uint4*>(t.out16 + t16_off(m0 + rr, ch * 8, kco)) = *reinterpret_cast<const uint4*>(&sZ[rr][ch * 8]);
+  }
+}
+
+hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, hipStream_t s) {
+  if (v.M < 1 || v.M != t.M || v.N != kAD || v.K < 1 || v.K > 8 * 3 * 32 || t.N != kD || t.K != kAD ||
+      (v.wrs == nullptr) != (t.wrs == nullptr) || v.final_out || !v.x || !t.x || v.x == t.x ||
+      (t.ow_rows > 0 && (!t.noise || !t.prev)))
+    return hipErrorInvalidValue;
+  BoundaryArgs ba;
+  ba.v = v;
+  ba.t = t;
+  // column groups: up to 8 while the grid stays within one workgroup per CU
+  const int nrb = (v.M + 15) / 16, G = nrb >= 128 ? 1 : (256 / nrb < 8 ? 256 / nrb : 8);
+  const dim3 grid(nrb * G), block(512);
+  if (v.wrs) hipLaunchKernelGGL((step_boundary_kernel<true>), grid, block, 0, s, ba);
+  else hipLaunchKernelGGL((step_boundary_kernel<false>), grid, block, 0, s, ba);
+  return hipGetLastError();
+}
+
 // FM = 16-row MFMA tiles per wave along M: BM = 32 * FM rows (two waves along M).
 template <int AM, int EM, int FM>
 __global__ __launch_bounds__(256, 2) void gemm_tiled(const GemmArgs a) {

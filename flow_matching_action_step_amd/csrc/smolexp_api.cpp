@@ -110,7 +110,8 @@ struct smolexp_handle {
   // one per layer (smolexp_time_kernel replays them)
   struct Probe {
     bool attn;
-    GemmArgs g;
+    bool boundary;  // the step boundary launch: g = action_out's arguments, g2 = the next time_in's
+    GemmArgs g, g2;
     AttnArgs a;
     GemmPlan plan;
     AMode am;
@@ -481,6 +482,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     wg.kc = w.kc + (size_t)r0 * kNKV;
     wg.vc = w.vc + (size_t)r0 * kNKV;
     wg.ropeq = w.ropeq + (size_t)r0 * (kHD / 2);
+    wg.x2 = w.x2 + (size_t)r0 * kAD;
     const size_t qOff = (size_t)r0 * kAD;                        // [b][50][32] arrays
     const size_t kvOff = (size_t)b0 * kHKV * (size_t)P * kHD;    // inside each layer's K and V
     const uint8_t* mask_g = c.mask + (size_t)b0 * P;
@@ -500,27 +502,40 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     };
     auto norm_gemm = [&](int probe, EMode em, const GemmArgs& g) -> hipError_t { return gemm(probe, A_NORM, em, g); };
     hipError_t e;
-    for (int k = 0; k < n_t; ++k) {
-      first_step = k == 0;
-      const float t = c.velocity ? c.t_single : h->ts[k];
-      GemmArgs g;
-      memset(&g, 0, sizeof(g));
-      g.status = status;
-      g.M = Mg;
-      g.inv_k = 1.0f / kD;
-      g.eps = h->cfg.rms_eps;
-
-      // action_in + time MLP, first layer: s = SiLU(W_t1[:, :720] (W_in x + b_in) + W_t1[:, 720:] e(t)
-      // + b_t1), computed as (W_t1[:, :720] W_in) x + the step's time vector (whose bias holds
-      // W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read and stored back
-      // into the state.  Then h = W_t2 s + b_t2.
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.status = status;
+    g.M = Mg;
+    g.inv_k = 1.0f / kD;
+    g.eps = h->cfg.rms_eps;
+    // action_in + time MLP, first layer, of step k: s = SiLU(W_t1[:, :720] (W_in x + b_in) +
+    // W_t1[:, 720:] e(t) + b_t1), computed as (W_t1[:, :720] W_in) x + the step's time vector
+    // (whose bias holds W_t1[:, :720] b_in); the prefix overwrite is applied to x as it is read
+    // and stored back into the state.
+    // Where action_out and the time MLP's first layer both take the register-resident K split,
+    // the end of step k and the start of step k + 1 run as one launch (both are row-local), and
+    // the Euler state of step k lives in x (k even) or x2 (k odd); otherwise always in x.
+    const bool w8 = h->w_out.rs != nullptr;
+    const bool fuse_boundary = plan_for(Mg, kAD, kD, A_NORM, E_ACTOUT, w8).kind == 0 &&
+                               plan_for(Mg, kD, kAD, A_X, E_TIMEIN, w8).kind == 0;
+    auto state = [&](int k) { return fuse_boundary && (k & 1) ? wg.x2 : wg.x; };
+    auto time_in_args = [&](int k) {
       GemmArgs gt = g;
-      gt.N = kD; gt.K = kAD; gt.A = wg.x; gt.lda = kAD;
-      gt.x = wg.x; gt.noise = c.x_in + qOff; gt.prev = c.prev ? c.prev + (size_t)b0 * c.d * kAD : nullptr;
-      gt.ow_rows = c.velocity ? 0 : c.d; gt.t = t;
+      gt.N = kD; gt.K = kAD; gt.A = state(k); gt.lda = kAD;
+      gt.x = state(k); gt.noise = c.x_in + qOff; gt.prev = c.prev ? c.prev + (size_t)b0 * c.d * kAD : nullptr;
+      gt.ow_rows = c.velocity ? 0 : c.d; gt.t = c.velocity ? c.t_single : h->ts[k];
       set_w(gt, h->w_tin); gt.bias = cvec + (size_t)k * kD;
       gt.out16 = wg.s16; gt.ldo = kD;
-      if ((e = gemm(PR_TIN, A_X, E_TIMEIN, gt)) != hipSuccess) return hip_fail(h, e, "time_in launch");
+      return gt;
+    };
+    for (int k = 0; k < n_t; ++k) {
+      first_step = k == 0;
+
+      // time MLP: the first layer (unless the previous step's boundary launch ran it), then
+      // h = W_t2 s + b_t2
+      if (k == 0 || !fuse_boundary) {
+        if ((e = gemm(PR_TIN, A_X, E_TIMEIN, time_in_args(k))) != hipSuccess) return hip_fail(h, e, "time_in launch");
+      }
 
       GemmArgs go = g;
       go.N = kD; go.K = kD; go.A = wg.s16; go.lda = kD;
@@ -580,7 +595,7 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
       GemmArgs gv = g;
       gv.N = kAD; gv.K = kD;
       set_w(gv, h->w_out); gv.bias = h->b_out;
-      gv.x = wg.x; gv.dt = h->dt;
+      gv.x = state(k); gv.dt = h->dt;
       const size_t stepElems = (size_t)B * kChunk * kAD;
       if (c.velocity) {
         gv.vel_out = c.out + qOff;
@@ -589,7 +604,19 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
         gv.st_out = c.st ? c.st + (size_t)k * stepElems + qOff : nullptr;
         gv.final_out = (k == n_t - 1) ? c.out + qOff : nullptr;
       }
-      if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) return hip_fail(h, e, "action_out launch");
+      if (fuse_boundary && k + 1 < n_t) {
+        gv.A = wg.h16; gv.lda = kKPad;
+        const GemmArgs gt = time_in_args(k + 1);
+        if (record_probes && first_step) {
+          smolexp_handle::Probe p;
+          memset(&p, 0, sizeof(p));
+          p.boundary = true; p.g = gv; p.g2 = gt;
+          h->probes[PR_ACTOUT].push_back(p);
+        }
+        if ((e = launch_step_boundary(gv, gt, gs)) != hipSuccess) return hip_fail(h, e, "step boundary launch");
+      } else if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) {
+        return hip_fail(h, e, "action_out launch");
+      }
     }
     return SMOLEXP_OK;
   };
@@ -1410,6 +1437,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     const std::vector<smolexp_handle::Probe>& v = h->probes[kernel];
     const smolexp_handle::Probe& p = v[(size_t)i % v.size()];
     if (p.attn) return launch_attention(kernel == PR_ATTN_SELF, p.a, st);
+    if (p.boundary) return launch_step_boundary(p.g, p.g2, st);
     if (p.plan.kind == 2) return launch_gemm_big(p.plan, p.em, p.am == A_NORM, p.g, st);
     return launch_gemm(p.plan, p.am, p.em, p.g, st);
   };

@@ -159,23 +159,26 @@ struct PrologueArgs {
 
 // Per-call activations of the denoising loop (device memory): the Euler state x, the fp32
 // residual h and its fp16 copy h16 (768 stored columns, 720.. zero), the time MLP's hidden
-// layer s16, the attention output o16, the SwiGLU output u16, the chunk's Q / K / V and the
-// RoPE rows of each chunk row.  Blocked operands hold whole 16-row blocks.
+// layer s16, the attention output o16, the SwiGLU output u16, the chunk's Q / K / V, the
+// RoPE rows of each chunk row, and a second Euler-state buffer x2 (the step-boundary launch
+// reads step k's state from one of x, x2 and writes step k + 1's to the other: several of its
+// workgroups read each state row).  Blocked operands hold whole 16-row blocks.
 struct CallWs {
   float* x;
   float* h;
   half_t *s16, *o16, *u16, *h16;
   bf16_t *q, *kc, *vc;
   float2* ropeq;
+  float* x2;
 };
 constexpr size_t ws_align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Sizes of the CallWs buffers, in the order they are carved, for max_batch queries.
-constexpr int kCallWsParts = 10;
+constexpr int kCallWsParts = 11;
 constexpr size_t call_ws_part(int max_batch, int i) {
   const size_t M = (size_t)max_batch * kChunk, Mp = (M + 15) & ~(size_t)15;
   const size_t sz[kCallWsParts] = {M * kAD * 4,  Mp * kD * 4,    Mp * kD * 2,   Mp * kNQ * 2,  Mp * kFFN * 2,
                                    Mp * 768 * 2, M * kNQ * 2,    M * kNKV * 2,  M * kNKV * 2,
-                                   M * (kHD / 2) * sizeof(float2)};
+                                   M * (kHD / 2) * sizeof(float2), M * kAD * 4};
   return ws_align256(sz[i]);
 }
 constexpr size_t call_ws_bytes(int max_batch) {
@@ -196,6 +199,7 @@ inline CallWs carve_call_ws(char* base, int max_batch) {
   w.s16 = (half_t*)p[2]; w.o16 = (half_t*)p[3]; w.u16 = (half_t*)p[4]; w.h16 = (half_t*)p[5];
   w.q = (bf16_t*)p[6]; w.kc = (bf16_t*)p[7]; w.vc = (bf16_t*)p[8];
   w.ropeq = (float2*)p[9];
+  w.x2 = (float*)p[10];
   return w;
 }
 
@@ -234,6 +238,11 @@ constexpr int kKPad = 768;  // stored columns of h16 and of the weights that rea
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
+// The step boundary in one launch (batches whose action_out and time-MLP first layer both take
+// the register-resident K split): v = action_out's arguments (A = fp16(h), lda = 768; no final
+// output; the state of step k is read from v.x), t = the next step's time_in arguments (the
+// state of step k + 1 is written to t.x, which must be another buffer).
+hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, hipStream_t s);
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int n_pos, float theta, hipStream_t s);

@@ -193,7 +193,7 @@ int smolexp_denoise(smolexp_t h, const void* prefix_kv, const uint8_t* prefix_ma
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * kernels and launches as smolexp_denoise (launched directly, never through a
  * cached graph), but the per-call activations live in a fixed array of device
- * memory inside the library (one copy per GPU, about 12.4 MB, held until the
+ * memory inside the library (one copy per GPU, about 12.5 MB, held until the
  * process ends) instead of the handle's workspace; the handle's weights and
  * tables are only read.  The call allocates nothing: no hipMalloc, no graph.
  *   batch  1..16 (and <= the handle's max_batch); larger batches return
