@@ -245,9 +245,10 @@ def kernel_costs(L, B, lengths, P, w8=False):
     Up to BOUNDARY_MAX_ROWS chunk rows (the library's register-resident K split of action_out and
     of the time MLP's first layer) the end of one step and the start of the next are one launch:
     "action_out" then stands for that step-boundary launch (action_out + Euler + the next step's
-    overwrite and time-MLP first layer) and "time_in" is not a kernel of its own.  Counted as one
-    such launch per step (the call's first time_in and last action_out run alone, which adds up
-    to the same work per call).
+    overwrite and time-MLP first layer) and "time_in" has no launch per step: only the call's first
+    step runs it alone (kernel_table adds that launch once per call).  The last step's action_out
+    also runs alone; counting it as a boundary launch keeps the per-step work, and so the loop's
+    totals, exact.
 
     Algorithmic bytes follow the counting of the loop's roofline: the parameters the launch
     reads, once, at 2 bytes per element (the bf16 manifest; RMSNorm gains are folded into the
@@ -284,8 +285,8 @@ def kernel_costs(L, B, lengths, P, w8=False):
     per_step = {"qkv_self": L // 2 + L % 2, "attn_self": L // 2 + L % 2, "attn_cross": L // 2, "o": L,
                 "gate_up": L, "down": L, "action_out": 1, "time_in": 1, "time_out": 1}
     if M <= BOUNDARY_MAX_ROWS:  # the step boundary: action_out and the next time_in in one launch
-        c["action_out"] = tuple(x + y for x, y in zip(c["action_out"], c.pop("time_in")))
-        del per_step["time_in"]
+        c["action_out"] = tuple(x + y for x, y in zip(c["action_out"], c["time_in"]))
+        del per_step["time_in"]  # c["time_in"] stays: the first step's time_in runs alone
     if B > CROSS_Q_MAX_BATCH:  # the cross layers' Q projection is a launch of its own
         c["q_cross"] = (mat(960, 720), M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
         per_step["q_cross"] = L // 2
@@ -326,6 +327,7 @@ def kernel_table(fm, h, cfg, L, B, lengths, P, reps, w8=False):
     as concurrent chains of launches)."""
     groups = fm.smolexp_batch_groups(cfg, B)
     tot, launches = {}, {}
+    first_tin = [0.0, 0.0, 0.0, 0]  # groups whose step boundary is one launch: the first step's time_in
     b0 = 0
     for bg in groups:
         costs, per_step = kernel_costs(L, bg, lengths[b0:b0 + bg], P, w8)
@@ -335,14 +337,21 @@ def kernel_table(fm, h, cfg, L, B, lengths, P, reps, w8=False):
             for i in range(3):
                 t[i] += costs[name][i] * n
             launches[name] = launches.get(name, 0) + n
+        if "time_in" not in per_step:
+            for i in range(3):
+                first_tin[i] += costs["time_in"][i]
+            first_tin[3] += 1
     kern = {}
     for name, kid in KERNEL_IDS.items():
-        if name not in launches:  # not launched at this batch (folded into another kernel)
+        if name in launches:
+            n, n_call, sums = launches[name], launches[name] * cfg.n_steps, tot[name]
+        elif name == "time_in" and first_tin[3]:  # once per call and group
+            n, n_call, sums = first_tin[3], first_tin[3], first_tin[:3]
+        else:  # not launched at this batch (folded into another kernel)
             continue
         us = fm.smolexp_time_kernel(h, kid, reps)
-        n = launches[name]
-        byt, act, fl = (v / n for v in tot[name])
-        kern[name] = {"avg_us": us, "launches_per_call": n * cfg.n_steps, "us_per_call": us * n * cfg.n_steps,
+        byt, act, fl = (v / n for v in sums)
+        kern[name] = {"avg_us": us, "launches_per_call": n_call, "us_per_call": us * n_call,
                       "bytes": byt, "activation_bytes": act, "flops": fl}
     return kern
 
