@@ -2201,14 +2201,33 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
     }
   } else if ((int)blockIdx.x < timeBlocks + nMaskBlocks) {
     // query b: its valid prefix count n, then the RoPE rows of chunk positions n .. n + 49
+    // Loads are issued in batches before their values are used: a loop that loads and then
+    // stores (or accumulates) each element in turn waits for every load on its own, since the
+    // compiler cannot move a load above a store that may alias it.
     const int b = (blockIdx.x - timeBlocks) * 4 + (tid >> 6), lane = tid & 63;
     if (b < a.B) {
+      const uint8_t* mrow = a.mask + (size_t)b * a.P;
+      constexpr int MU = 4;  // mask bytes per lane and batch: P <= 256 in one
       int c = 0;
-      for (int j = lane; j < a.P; j += 64) c += a.mask[(size_t)b * a.P + j] != 0;
+      for (int j0 = 0; j0 < a.P; j0 += 64 * MU) {
+        unsigned mb[MU];
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+          const int j = j0 + lane + 64 * u;
+          mb[u] = mrow[j < a.P ? j : a.P - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < MU; ++u) c += (j0 + lane + 64 * u < a.P) && mb[u] != 0u;
+      }
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-      for (int i = lane; i < kChunk * (kHD / 2); i += 64)
-        a.ropeq[((size_t)b * kChunk) * (kHD / 2) + i] = a.rope[(size_t)c * (kHD / 2) + i];
+      constexpr int RU = kChunk * (kHD / 2) / 64;  // RoPE entries per lane
+      static_assert(RU * 64 == kChunk * (kHD / 2), "whole rows per lane");
+      float2 rv[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) rv[u] = a.rope[(size_t)c * (kHD / 2) + lane + 64 * u];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) a.ropeq[((size_t)b * kChunk) * (kHD / 2) + lane + 64 * u] = rv[u];
     }
   } else {
     const int first = timeBlocks + nMaskBlocks;
