@@ -242,8 +242,8 @@ def kernel_costs(L, B, lengths, P, w8=False):
     """Per launch of each timed kernel: (algorithmic bytes, activation bytes, flops), and its
     launches per Euler step.
 
-    Up to BOUNDARY_MAX_ROWS chunk rows (the library's register-resident K split of action_out and
-    of the time MLP's first layer) the end of one step and the start of the next are one launch:
+    Up to BOUNDARY_MAX_ROWS chunk rows per query group (the library's register-resident K split of
+    action_out) the end of one step and the start of the next are one launch:
     "action_out" then stands for that step-boundary launch (action_out + Euler + the next step's
     overwrite and time-MLP first layer) and "time_in" has no launch per step: only the call's first
     step runs it alone (kernel_table adds that launch once per call).  The last step's action_out
@@ -294,7 +294,7 @@ def kernel_costs(L, B, lengths, P, w8=False):
 
 
 CROSS_Q_MAX_BATCH = 8  # largest batch whose cross layers fold the Q projection into attention (library constant)
-BOUNDARY_MAX_ROWS = 2400  # largest query group (chunk rows) whose step boundary is one launch (library plan)
+BOUNDARY_MAX_ROWS = 4800  # largest query group (chunk rows) whose step boundary is one launch (library plan)
 KERNEL_IDS = {"qkv_self": 0, "attn_self": 1, "attn_cross": 2, "o": 3, "gate_up": 4, "down": 5, "action_out": 6,
               "q_cross": 8, "time_in": 9, "time_out": 10}
 LOOP_ID = 7  # smolexp_time_kernel: the whole call

@@ -238,8 +238,8 @@ constexpr int kKPad = 768;  // stored columns of h16 and of the weights that rea
 
 // Launchers (kernels.hip).  Each returns the hipGetLastError() after launch.
 hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a, hipStream_t s);
-// The step boundary in one launch (batches whose action_out and time-MLP first layer both take
-// the register-resident K split): v = action_out's arguments (A = fp16(h), lda = 768; no final
+// The step boundary in one launch (query groups whose action_out takes the register-resident K
+// split, up to 4800 rows): v = action_out's arguments (A = fp16(h), lda = 768; no final
 // output; the state of step k is read from v.x), t = the next step's time_in arguments (the
 // state of step k + 1 is written to t.x, which must be another buffer).
 hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, hipStream_t s);
