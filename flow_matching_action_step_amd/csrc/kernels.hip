@@ -2071,6 +2071,146 @@ __global__ __launch_bounds__(64 * NW, MINB) void attn_pipe_kernel(const AttnArgs
   }
 }
 
+// The same streamed attention with the K/V blocks staged through registers into two LDS
+// stages: while block j is multiplied, block j + 1 is already in LDS and block j + 2 is in
+// flight in registers, stored to LDS after block j (keys that are not attended zeroed on the
+// way).  With direct global->LDS loads in flight the compiler
+// makes the block's LDS reads (the transposing V^T reads among them) wait for every load, so the
+// next block's loads never overlapped the current block's arithmetic; register loads carry no
+// such wait.  Same scores, same sums, same bits as attn_pipe_kernel.
+// One 64-key block of K and V staged through registers: vector i of a thread is v = tid + NT i
+// (v < 512), key row v / 8, 16-byte chunk v % 8.  issue(): every load unconditional, keys past
+// the last clamped to it; store(): into an LDS stage in the swizzled layout of kv_at<true>
+// (chunk c of row r at c ^ (r % 8)), keys whose kind (the LDS key-kind table) is 0 zeroed.
+template <bool SELF, int NT>
+struct StreamStage {
+  static constexpr int NVEC = kKB * kHD / 8, NV = (NVEC + NT - 1) / NT;
+  uint4 k[NV], v[NV];
+  __device__ __forceinline__ void issue(const bf16_t* pk, const bf16_t* pv, const bf16_t* ck, const bf16_t* cv,
+                                        int P, int NK, int bb) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vv = min(tid + NT * i, NVEC - 1);
+      const int key = min(bb * kKB + (vv >> 3), NK - 1), c = (vv & 7) * 8;
+      const bool pre = !SELF || key < P;
+      const unsigned po = (unsigned)(key * kHD + c), co = (unsigned)((key - P) * kHD + c);
+      k[i] = *reinterpret_cast<const uint4*>(pre ? pk + po : ck + co);
+      v[i] = *reinterpret_cast<const uint4*>(pre ? pv + po : cv + co);
+    }
+  }
+  __device__ __forceinline__ void store(char* base, int blk_bytes, const uint8_t* kind) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vv = tid + NT * i;
+      const int row = (vv >> 3) & (kKB - 1);
+      const bool ok = kind[row] != 0;
+      const int off = row * 128 + ((((vv & 7) ^ row) & 7) << 4);
+      // component-wise selects: a select of whole uint4 values became a select of their
+      // addresses and kept the staging registers in scratch memory
+      const unsigned keep = ok ? ~0u : 0u;
+      if (NVEC % NT == 0 || vv < NVEC) {
+        *reinterpret_cast<uint4*>(base + off) = make_uint4(k[i].x & keep, k[i].y & keep, k[i].z & keep, k[i].w & keep);
+        *reinterpret_cast<uint4*>(base + blk_bytes + off) =
+            make_uint4(v[i].x & keep, v[i].y & keep, v[i].z & keep, v[i].w & keep);
+      }
+    }
+  }
+};
+
+// The same streamed attention with the K/V blocks staged through registers into two LDS
+// stages: while block j is multiplied, block j + 1 is already in LDS and block j + 2 is in
+// flight in registers, stored to LDS after block j (keys that are not attended zeroed on the
+// way, the mask bytes loaded with them).  With direct global->LDS loads in flight the compiler
+// makes the block's LDS reads (the transposing V^T reads among them) wait for every load, so the
+// next block's loads never overlapped the current block's arithmetic; register loads carry no
+// such wait.  Same scores, same sums, same bits as attn_pipe_kernel.
+template <bool SELF, int MINB = 1, int NW = 4, bool PF = false>
+__global__ __launch_bounds__(64 * NW, MINB) void attn_stream_kernel(const AttnArgs a) {
+  static_assert(!(PF && SELF), "a prefill's keys are the prefix alone");
+  constexpr int NT = 64 * NW, BLK_BYTES = kKB * kHD * 2, STAGE = 2 * BLK_BYTES;
+  constexpr int RW = 16 * NW;                   // query rows per workgroup
+  __shared__ __attribute__((aligned(1024))) char ring[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sKind[kMaxKeys];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // grid: as attn_pipe_kernel (the RG row groups of a (query, KV head) unit on one XCD)
+  const int seq = PF ? a.seq : kChunk;
+  const int RG = (3 * seq + RW - 1) / RW;
+  const int xcd = (int)(blockIdx.x & 7), jx = (int)(blockIdx.x >> 3);
+  const int u = 8 * (jx / RG) + xcd, rgi = jx % RG;
+  if (u >= kHKV * a.B) return;
+  const int g = u % kHKV, b = u / kHKV, P = a.P;
+  const int NK = P + (SELF ? kChunk : 0), nblk = (NK + kKB - 1) / kKB;
+  const int rq = rgi * RW + w * 16 + (lane & 15);
+  const bool rvalid = rq < 3 * seq;
+  const int hq = 3 * g + (rvalid ? rq / seq : 0);
+  const int qi = rvalid ? rq % seq : 0;
+
+  const uint8_t* mk = a.mask + (size_t)b * P;
+  const size_t head = (size_t)b * kHKV + g;
+  const bf16_t* pk = a.pk + head * (size_t)P * kHD;
+  const bf16_t* pv = a.pv + head * (size_t)P * kHD;
+  const bf16_t* ck = SELF ? a.kc + head * kChunk * kHD : pk;
+  const bf16_t* cv = SELF ? a.vc + head * kChunk * kHD : pv;
+  StreamStage<SELF, NT> st;
+
+  // The first block's keys and the Q rows go out together (a row past the last reads query row 0
+  // of head 3 g: its results are never stored); the key-kind fill waits for them (its mask loads
+  // are conditional), then the first block goes into LDS and the second block's loads are issued,
+  // in flight through the first block's arithmetic.
+  st.issue(pk, pv, ck, cv, P, NK, 0);
+  bf16x8 qf[2];
+  {
+    const bf16_t* qp = a.q + (((size_t)b * kHQ + hq) * seq + qi) * kHD + (lane >> 4) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kk * 32));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // key kinds: 0 = none, 1 = valid prefix key, 2 = chunk key
+  for (int j = tid; j < nblk * kKB; j += NT)
+    sKind[j] = j < P ? (mk[j] ? 1 : 0) : ((SELF && j - P < kChunk) ? 2 : 0);
+  __syncthreads();  // the kinds, for every thread's stores
+  // every load so far has landed (the first block's store needs them anyway): the loop then
+  // never waits for the Q fragments behind the next block's loads
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  st.store(ring, BLK_BYTES, sKind);
+  if (nblk > 1) st.issue(pk, pv, ck, cv, P, NK, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  f32x4 l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < nblk; ++j) {
+    __syncthreads();  // block j stored by every thread; block j - 1 finished by every wave
+    const bf16_t* sK = reinterpret_cast<const bf16_t*>(ring + (j & 1) * STAGE);
+    attn_block<true>(sK, sK + BLK_BYTES / 2, sKind + j * kKB, j * kKB - P, qi, qf, o, m_run, l_acc, lane);
+    if (j + 1 < nblk) {  // uniform
+      st.store(ring + ((j + 1) & 1) * STAGE, BLK_BYTES, sKind + (j + 1) * kKB);  // the stage block j - 1 used
+      if (j + 2 < nblk) st.issue(pk, pv, ck, cv, P, NK, j + 2);
+    }
+  }
+
+  if (rvalid) {
+    const float l_run = l_acc[0];
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    const int orow = b * seq + qi;
+    float vmax = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      union { half_t h[4]; uint2 u; } pk4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pk4.h[r] = (half_t)(o[m][r] * inv);
+      vmax = absmax4(vmax, o[m][0] * inv, o[m][1] * inv, o[m][2] * inv, o[m][3] * inv);
+      *reinterpret_cast<uint2*>(a.out + t16_off(orow, hq * kHD + m * 16 + (lane >> 4) * 4, kNQ / 8)) = pk4.u;
+    }
+    report_range(a.status, vmax, kRangeAttention);
+  }
+}
+
 // Grid of attn_pipe_kernel: 8 XCD lanes x RG row groups x ceil(5 B / 8) units.
 static dim3 pipe_grid(int B, int NW, int seq = kChunk) {
   const int RG = (3 * seq + 16 * NW - 1) / (16 * NW);
@@ -2086,14 +2226,19 @@ static dim3 pipe_grid(int B, int NW, int seq = kChunk) {
 // registers capped for four workgroups per CU (batch 64: 13.2 / 9.7 against 16.5 /
 // 12.3 with ten; batch 128: 23.5 / 17.5 against 25.2 / 19.4).  Before the grid kept
 // the row groups of a (query, KV head) on one XCD, batch 64 took 20.0 / 19.1 us at
-// P = 257 in the loop against 15.8 / 14.5 now.
+// P = 257 in the loop against 15.8 / 14.5 now.  The register-staged kernel (attn_stream_kernel)
+// replaces the ring where its registers still allow the same workgroups per CU: up to batch 24
+// (batch 16, variable prefixes <= 241, whole call 8.48 -> 8.21 ms; batch 24 9.80 -> 9.60) and
+// with ten waves (batch 40 10.89 -> 10.75); with four waves and four workgroups per CU it would
+// spill, and at three per CU batch 32 (two per call at batch 64) measured equal and batch 64 (at
+// batch 128) slower (15.5 / 11.6 -> 15.8 / 12.4 us per launch, two rounds of workgroups).
 template <bool SELF>
 static void launch_pipe(const AttnArgs& a, hipStream_t s) {
   const int B = a.B;
-  if (B <= 16) hipLaunchKernelGGL((attn_pipe_kernel<SELF, 3>), pipe_grid(B, 4), dim3(256), 0, s, a);
-  else if (B <= 24) hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 2, 5>), pipe_grid(B, 5), dim3(320), 0, s, a);
+  if (B <= 16) hipLaunchKernelGGL((attn_stream_kernel<SELF, 1, 4>), pipe_grid(B, 4), dim3(256), 0, s, a);
+  else if (B <= 24) hipLaunchKernelGGL((attn_stream_kernel<SELF, 2, 5>), pipe_grid(B, 5), dim3(320), 0, s, a);
   else if ((B > 32 && B <= 48) || (B > 64 && B <= 96))
-    hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 1, 10>), pipe_grid(B, 10), dim3(640), 0, s, a);
+    hipLaunchKernelGGL((attn_stream_kernel<SELF, 1, 10>), pipe_grid(B, 10), dim3(640), 0, s, a);
   else hipLaunchKernelGGL((attn_pipe_kernel<SELF, 2, 4>), pipe_grid(B, 4), dim3(256), 0, s, a);
 }
 
