@@ -24,8 +24,8 @@ def _workload(L, B, P, lengths, seed_shift=0):
 
 
 def test_largest_prefix_4096_both_attention_families():
-    """P = 4096 = max_prefix: at batch 9 the streamed-ring attention (4146 keys in the self
-    layers fill its key-kind array exactly), at batch 1 the staged kernels (13 key rounds in the
+    """P = 4096 = max_prefix: at batch 9 the register-staged streamed attention (4146 keys in the
+    self layers fill its key-kind array exactly), at batch 1 the staged kernels (13 key rounds in the
     self layers, 13 in the cross layers' fused Q-projection kernel), with ragged valid lengths
     (all, most, one token) and NaN pads."""
     L, P = 2, 4096
@@ -61,5 +61,22 @@ def test_largest_batch_1024():
         q = [0, 127, 128, 511, 896, 1023]
         compare(gpu, run_oracle(ex, wl, q), q, wl["noise"], "batch 1024")
         assert np.isfinite(gpu["out"]).all()
+    finally:
+        ex.close()
+
+
+def test_largest_prefix_4096_ring_attention():
+    """P = 4096 at batch 25: the streamed attention of direct global->LDS loads through an LDS ring
+    (the kernel of 25-32, 49-64 and more than 96 queries per group), ragged lengths from all to
+    one valid token, NaN pads."""
+    L, P, B = 2, 4096, 25
+    ex = Expert(L, max_batch=B, max_prefix=P)
+    try:
+        lengths = [4096, 1, 3999, 2048, 4095] + [64 * (i + 1) for i in range(B - 5)]
+        wl = _workload(L, B, P, lengths, seed_shift=5)
+        _say("P = 4096, batch 25 (ring attention)")
+        gpu = run_gpu(ex, to_device(wl))
+        q = [0, 1, 2, 24]
+        compare(gpu, run_oracle(ex, wl, q), q, wl["noise"], "P=4096 batch 25")
     finally:
         ex.close()
