@@ -101,3 +101,30 @@ def test_denoise_counts_with_8bit_weights():
     b8, f8 = bench.loop_algorithmic(16, 1, [177], 1, w8=True)
     assert f8 == f16
     assert b16 - b8 == elems - 4 * rows
+
+
+class _FakeLib:
+    """The two library calls kernel_table makes, answered on the host: the library's query-group
+    split (two groups from 64 queries on, one per 64 from 192 on) and a constant kernel time."""
+
+    def smolexp_batch_groups(self, cfg, B):
+        G = B // 64 if B >= 192 else 2 if B >= 64 else 1
+        base = ((B + G - 1) // G + 7) // 8 * 8
+        return [base] * (G - 1) + [B - (G - 1) * base]
+
+    def smolexp_time_kernel(self, h, kid, reps):
+        return 1.0
+
+
+def test_launch_counts_per_call_match_the_kernel_traces():
+    """Launches per call of the 16-layer, 10-step loop as bench.py counts them (the prologue, then
+    every timed kernel's launches per call), against the dispatches per call the rocprofv3 traces
+    of the library show: batch 1 742 (the step boundary one launch from the first step to the
+    last, the cross layers' Q projection inside attention), batch 64 1643 (two groups of 32, each
+    with its step boundary in one launch; the cross layers' Q projection a launch of its own),
+    batch 128 1643 (two groups of 64 at 3200 rows, the boundary still one launch)."""
+    import types
+    cfg = types.SimpleNamespace(n_steps=10)
+    for B, want in ((1, 742), (64, 1643), (128, 1643)):
+        kern = bench.kernel_table(_FakeLib(), None, cfg, 16, B, [177] * B, 177, 1)
+        assert 1 + sum(v["launches_per_call"] for v in kern.values()) == want, B
