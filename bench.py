@@ -245,8 +245,9 @@ def kernel_costs(L, B, lengths, P, w8=False):
     Up to BOUNDARY_MAX_ROWS chunk rows per query group (the library's register-resident K split of
     action_out) the end of one step and the start of the next are one launch:
     "action_out" then stands for that step-boundary launch (action_out + Euler + the next step's
-    overwrite and time-MLP first layer) and "time_in" has no launch per step: only the call's first
-    step runs it alone (kernel_table adds that launch once per call).  The last step's action_out
+    overwrite and time-MLP first layer; for one query, BOUNDARY_TIME_OUT_MAX_ROWS, the time MLP's
+    second layer too) and "time_in" (and "time_out") have no launch per step: only the call's first
+    step runs them alone (kernel_table adds those launches once per call).  The last step's action_out
     also runs alone; counting it as a boundary launch keeps the per-step work, and so the loop's
     totals, exact.
 
@@ -287,6 +288,9 @@ def kernel_costs(L, B, lengths, P, w8=False):
     if M <= BOUNDARY_MAX_ROWS:  # the step boundary: action_out and the next time_in in one launch
         c["action_out"] = tuple(x + y for x, y in zip(c["action_out"], c["time_in"]))
         del per_step["time_in"]  # c["time_in"] stays: the first step's time_in runs alone
+        if M <= BOUNDARY_TIME_OUT_MAX_ROWS:  # ... and the next time_out (one query)
+            c["action_out"] = tuple(x + y for x, y in zip(c["action_out"], c["time_out"]))
+            del per_step["time_out"]
     if B > CROSS_Q_MAX_BATCH:  # the cross layers' Q projection is a launch of its own
         c["q_cross"] = (mat(960, 720), M * 720 * 2 + M * 960 * 2, 2.0 * M * 960 * 720)
         per_step["q_cross"] = L // 2
@@ -295,6 +299,7 @@ def kernel_costs(L, B, lengths, P, w8=False):
 
 CROSS_Q_MAX_BATCH = 8  # largest batch whose cross layers fold the Q projection into attention (library constant)
 BOUNDARY_MAX_ROWS = 4800  # largest query group (chunk rows) whose step boundary is one launch (library plan)
+BOUNDARY_TIME_OUT_MAX_ROWS = 64  # largest group whose boundary launch also runs the time MLP's second layer
 KERNEL_IDS = {"qkv_self": 0, "attn_self": 1, "attn_cross": 2, "o": 3, "gate_up": 4, "down": 5, "action_out": 6,
               "q_cross": 8, "time_in": 9, "time_out": 10}
 LOOP_ID = 7  # smolexp_time_kernel: the whole call
@@ -327,7 +332,8 @@ def kernel_table(fm, h, cfg, L, B, lengths, P, reps, w8=False):
     as concurrent chains of launches)."""
     groups = fm.smolexp_batch_groups(cfg, B)
     tot, launches = {}, {}
-    first_tin = [0.0, 0.0, 0.0, 0]  # groups whose step boundary is one launch: the first step's time_in
+    # groups whose step boundary runs the time MLP's layers: the first step's launches of them
+    first = {"time_in": [0.0, 0.0, 0.0, 0], "time_out": [0.0, 0.0, 0.0, 0]}
     b0 = 0
     for bg in groups:
         costs, per_step = kernel_costs(L, bg, lengths[b0:b0 + bg], P, w8)
@@ -337,16 +343,17 @@ def kernel_table(fm, h, cfg, L, B, lengths, P, reps, w8=False):
             for i in range(3):
                 t[i] += costs[name][i] * n
             launches[name] = launches.get(name, 0) + n
-        if "time_in" not in per_step:
-            for i in range(3):
-                first_tin[i] += costs["time_in"][i]
-            first_tin[3] += 1
+        for name, f in first.items():
+            if name not in per_step:
+                for i in range(3):
+                    f[i] += costs[name][i]
+                f[3] += 1
     kern = {}
     for name, kid in KERNEL_IDS.items():
         if name in launches:
             n, n_call, sums = launches[name], launches[name] * cfg.n_steps, tot[name]
-        elif name == "time_in" and first_tin[3]:  # once per call and group
-            n, n_call, sums = first_tin[3], first_tin[3], first_tin[:3]
+        elif name in first and first[name][3]:  # once per call and group
+            n, n_call, sums = first[name][3], first[name][3], first[name][:3]
         else:  # not launched at this batch (folded into another kernel)
             continue
         us = fm.smolexp_time_kernel(h, kid, reps)

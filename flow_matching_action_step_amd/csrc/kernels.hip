@@ -25,6 +25,7 @@
 
 #include <math.h>
 
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -575,8 +576,13 @@ __global__ __launch_bounds__(512) void gemm_skinny(const GemmArgs a) {
 // in the two separate launches (action_out, then time_in), so the results are the same bits.
 // v: action_out's arguments (A_NORM operand h16, bias, x, dt, records); t: the next step's
 // time_in arguments (its flow time, time vector, overwrite rows, output s16).
+// TOUT (one query's 50 rows): the time MLP's second layer too (o: time_out's arguments, the
+// residual stream h0 = W_t2 s + b_t2 and its fp16 copy).  Workgroup (row block, c) then computes
+// all 45 column tiles of the hidden layer s into LDS and the 16 output columns 16 c .. of the
+// second layer from them, as gemm_skinny<A_F16, E_H_BIAS, 3, 1, 1> would from the stored s (same
+// k-steps per wave, same order of the partial sums, same epilogue), so again the same bits.
 struct BoundaryArgs {
-  GemmArgs v, t;
+  GemmArgs v, t, o;
 };
 
 // a * b + c with the product rounded before the sum (no fused multiply-add), as when the product
@@ -586,7 +592,7 @@ __device__ __forceinline__ float mul_add_rounded(float a, float b, float c) {
   return a * b + c;
 }
 
-template <bool W8>
+template <bool W8, bool TOUT = false>
 __global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs ba) {
   constexpr int NW = 8, KPW = 3, NCB = kAD / 16, NTT = kD / 16, TPW = (NTT + NW - 1) / NW;
   static_assert(NCB * 16 == kAD && NTT * 16 == kD && 16 * kAD == 512, "one (row, action column) per thread");
@@ -596,11 +602,14 @@ __global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs b
   __shared__ float sQ[NW][16];
   __shared__ __attribute__((aligned(16))) float sX[16][kAD];
   __shared__ __attribute__((aligned(16))) half_t sZ[16][kD];
+  __shared__ __attribute__((aligned(16))) float sRedO[TOUT ? NW * 16 * 16 : 1];  // TOUT: the waves' partial tiles
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // G workgroups per row block: the hidden layer's column groups, or (TOUT) the second layer's
+  // 16-column blocks, each with the whole hidden layer
   const int G = gridDim.x / ((a.M + 15) / 16), rb = blockIdx.x / G, cg = blockIdx.x % G;
   const int M = a.M, K = a.K, m0 = rb * 16;
   const int nks = (K + 31) / 32, kl = (lane >> 4) * 8;
-  const int t_lo = cg * NTT / G, t_hi = (cg + 1) * NTT / G;  // this workgroup's column tiles
+  const int t_lo = TOUT ? 0 : cg * NTT / G, t_hi = TOUT ? NTT : (cg + 1) * NTT / G;  // hidden-layer column tiles
 
   // every load first: action_out's operands (as gemm_skinny<A_NORM, E_ACTOUT, 3, 1, 2>), the time
   // MLP's weight fragments and time-vector entries of this wave's column tiles, the thread's
@@ -626,6 +635,23 @@ __global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs b
     wt[i] = load_wfrag<W8, true>(t.W, t16_off(col, kl, t.ldw >> 3), n < t_hi);
     tb[i] = t.bias[col];
     ts[i] = W8 ? t.wrs[col] : t.w_scale;
+  }
+  // TOUT: the second layer's weight fragments of this wave's k-steps (16 rows of column block cg)
+  // and, for wave 0 (which finishes the tile), its bias and weight scales
+  const GemmArgs& go = ba.o;
+  WFrag<W8> wo[TOUT ? KPW : 1];
+  float4 bias4 = make_float4(0.f, 0.f, 0.f, 0.f), wsc4 = bias4;
+  if constexpr (TOUT) {
+    const int nksO = (go.K + 31) / 32;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int ks = w * KPW + i, k = ks * 32 + kl;
+      wo[i] = load_wfrag<W8, true>(go.W, t16_off(cg * 16 + (lane & 15), k, go.ldw >> 3), ks < nksO && k < go.K);
+    }
+    const int col = cg * 16 + (lane >> 4) * 4;
+    bias4 = *reinterpret_cast<const float4*>(go.bias + col);
+    if constexpr (W8) wsc4 = *reinterpret_cast<const float4*>(go.wrs + col);
+    else wsc4 = make_float4(go.w_scale, go.w_scale, go.w_scale, go.w_scale);
   }
   const int r = tid / kAD, c = tid % kAD, row = m0 + r;
   const bool rok = row < M;
@@ -705,6 +731,44 @@ __global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs b
   }
   report_range(t.status, fmaxf(xmax, zmax), kRangeTime);
   __syncthreads();
+  if constexpr (TOUT) {
+    // the second layer: this wave's three k-steps of the hidden layer (from LDS) against the
+    // weight fragments, the partial tiles summed in wave order, bias added, h0 and fp16(h0) stored
+    const int nksO = (go.K + 31) / 32;
+    f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int ks = w * KPW + i, k = ks * 32 + kl;
+      const bool kok = ks < nksO && k < go.K;
+      const uint4 zf = kok ? *reinterpret_cast<const uint4*>(&sZ[lane & 15][k]) : make_uint4(0, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, zf),
+                                                    __builtin_bit_cast(f16x8, w_to_f16x8(wo[i])), acc2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sRedO[(w * 16 + (lane >> 4) * 4 + rr) * 16 + (lane & 15)] = acc2[rr];
+    __syncthreads();
+    if (w == 0) {
+      const int r16 = lane & 15, part = lane >> 4, orow = m0 + r16, col = cg * 16 + part * 4;
+      float vmax = 0.f;
+      if (orow < M && col < go.N) {
+        float4 sm = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const float4 pv = *reinterpret_cast<const float4*>(sRedO + (w2 * 16 + r16) * 16 + part * 4);
+          sm.x += pv.x; sm.y += pv.y; sm.z += pv.z; sm.w += pv.w;
+        }
+        const float4 v = make_float4(sm.x * wsc4.x, sm.y * wsc4.y, sm.z * wsc4.z, sm.w * wsc4.w);
+        const float4 o = make_float4(v.x + bias4.x, v.y + bias4.y, v.z + bias4.z, v.w + bias4.w);
+        *reinterpret_cast<float4*>(go.h + t32_off(orow, col, kD / 4)) = o;
+        vmax = absmax4(vmax, o.x, o.y, o.z, o.w);
+        union { half_t e[4]; uint2 u; } o16;
+        o16.e[0] = (half_t)o.x; o16.e[1] = (half_t)o.y; o16.e[2] = (half_t)o.z; o16.e[3] = (half_t)o.w;
+        *reinterpret_cast<uint2*>(go.h16 + t16_off(orow, col, kKPad / 8)) = o16.u;
+      }
+      report_range(go.status, vmax, kRangeResidual);
+    }
+    return;  // the hidden layer stays in LDS: nothing else reads it
+  }
   const int kco = t.ldo >> 3;
   const int nch = (t_hi - t_lo) * 2;  // 8-column chunks of the group
   for (int uu = tid; uu < 16 * nch; uu += 512) {
@@ -714,16 +778,28 @@ __global__ __launch_bounds__(512) void step_boundary_kernel(const BoundaryArgs b
   }
 }
 
-hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, hipStream_t s) {
+hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, const GemmArgs* o, hipStream_t s) {
   if (v.M < 1 || v.M != t.M || v.N != kAD || v.K < 1 || v.K > 8 * 3 * 32 || t.N != kD || t.K != kAD ||
       (v.wrs == nullptr) != (t.wrs == nullptr) || v.final_out || !v.x || !t.x || v.x == t.x ||
       (t.ow_rows > 0 && (!t.noise || !t.prev)))
     return hipErrorInvalidValue;
+  if (o && (v.M > kBoundaryTimeOutMaxRows || o->M != v.M || o->N != kD || o->K != kD || !o->h || !o->h16 ||
+            !o->bias || (o->wrs == nullptr) != (v.wrs == nullptr)))
+    return hipErrorInvalidValue;
   BoundaryArgs ba;
   ba.v = v;
   ba.t = t;
+  if (o) ba.o = *o;
+  else memset(&ba.o, 0, sizeof(ba.o));
+  const int nrb = (v.M + 15) / 16;
+  if (o) {  // one workgroup per row block and 16-column block of the second layer
+    const dim3 grid(nrb * (kD / 16)), block(512);
+    if (v.wrs) hipLaunchKernelGGL((step_boundary_kernel<true, true>), grid, block, 0, s, ba);
+    else hipLaunchKernelGGL((step_boundary_kernel<false, true>), grid, block, 0, s, ba);
+    return hipGetLastError();
+  }
   // column groups: up to 8 while the grid stays within one workgroup per CU
-  const int nrb = (v.M + 15) / 16, G = nrb >= 128 ? 1 : (256 / nrb < 8 ? 256 / nrb : 8);
+  const int G = nrb >= 128 ? 1 : (256 / nrb < 8 ? 256 / nrb : 8);
   const dim3 grid(nrb * G), block(512);
   if (v.wrs) hipLaunchKernelGGL((step_boundary_kernel<true>), grid, block, 0, s, ba);
   else hipLaunchKernelGGL((step_boundary_kernel<false>), grid, block, 0, s, ba);

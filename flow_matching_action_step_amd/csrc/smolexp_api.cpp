@@ -111,7 +111,8 @@ struct smolexp_handle {
   struct Probe {
     bool attn;
     bool boundary;  // the step boundary launch: g = action_out's arguments, g2 = the next time_in's
-    GemmArgs g, g2;
+    bool tout;      // ... and g3 = the next time_out's
+    GemmArgs g, g2, g3;
     AttnArgs a;
     GemmPlan plan;
     AMode am;
@@ -519,6 +520,16 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
     const bool w8 = h->w_out.rs != nullptr;
     const bool fuse_boundary = plan_for(Mg, kAD, kD, A_NORM, E_ACTOUT, w8).kind == 0;
     auto state = [&](int k) { return fuse_boundary && (k & 1) ? wg.x2 : wg.x; };
+    // one query (50 rows): the boundary launch also runs the time MLP's second layer of step k + 1
+    // (every workgroup holds the 16 rows' whole hidden layer in LDS)
+    const bool fuse_time_out = fuse_boundary && Mg <= kBoundaryTimeOutMaxRows;
+    auto time_out_args = [&]() {
+      GemmArgs go = g;
+      go.N = kD; go.K = kD; go.A = wg.s16; go.lda = kD;
+      set_w(go, h->w_t2); go.bias = h->b_t2;
+      go.h = wg.h; go.h16 = wg.h16;
+      return go;
+    };
     auto time_in_args = [&](int k) {
       GemmArgs gt = g;
       gt.N = kD; gt.K = kAD; gt.A = state(k); gt.lda = kAD;
@@ -537,11 +548,9 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
         if ((e = gemm(PR_TIN, A_X, E_TIMEIN, time_in_args(k))) != hipSuccess) return hip_fail(h, e, "time_in launch");
       }
 
-      GemmArgs go = g;
-      go.N = kD; go.K = kD; go.A = wg.s16; go.lda = kD;
-      set_w(go, h->w_t2); go.bias = h->b_t2;
-      go.h = wg.h; go.h16 = wg.h16;
-      if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, go)) != hipSuccess) return hip_fail(h, e, "time_out launch");
+      if (k == 0 || !fuse_time_out) {
+        if ((e = gemm(PR_TOUT, A_F16, E_H_BIAS, time_out_args())) != hipSuccess) return hip_fail(h, e, "time_out launch");
+      }
 
       for (int l = 0; l < L; ++l) {
         const LayerDev& ld = h->layers[l];
@@ -606,14 +615,15 @@ int enqueue(smolexp_t h, const CallArgs& c, const CallWs& w, hipStream_t s, bool
       }
       if (fuse_boundary && k + 1 < n_t) {
         gv.A = wg.h16; gv.lda = kKPad;
-        const GemmArgs gt = time_in_args(k + 1);
+        const GemmArgs gt = time_in_args(k + 1), go = time_out_args();
         if (record_probes && first_step) {
           smolexp_handle::Probe p;
           memset(&p, 0, sizeof(p));
-          p.boundary = true; p.g = gv; p.g2 = gt;
+          p.boundary = true; p.tout = fuse_time_out; p.g = gv; p.g2 = gt; p.g3 = go;
           h->probes[PR_ACTOUT].push_back(p);
         }
-        if ((e = launch_step_boundary(gv, gt, gs)) != hipSuccess) return hip_fail(h, e, "step boundary launch");
+        if ((e = launch_step_boundary(gv, gt, fuse_time_out ? &go : nullptr, gs)) != hipSuccess)
+          return hip_fail(h, e, "step boundary launch");
       } else if ((e = norm_gemm(PR_ACTOUT, E_ACTOUT, gv)) != hipSuccess) {
         return hip_fail(h, e, "action_out launch");
       }
@@ -1437,7 +1447,7 @@ int smolexp_time_kernel(smolexp_t h, int kernel, int reps, void* hip_stream, flo
     const std::vector<smolexp_handle::Probe>& v = h->probes[kernel];
     const smolexp_handle::Probe& p = v[(size_t)i % v.size()];
     if (p.attn) return launch_attention(kernel == PR_ATTN_SELF, p.a, st);
-    if (p.boundary) return launch_step_boundary(p.g, p.g2, st);
+    if (p.boundary) return launch_step_boundary(p.g, p.g2, p.tout ? &p.g3 : nullptr, st);
     if (p.plan.kind == 2) return launch_gemm_big(p.plan, p.em, p.am == A_NORM, p.g, st);
     return launch_gemm(p.plan, p.am, p.em, p.g, st);
   };

@@ -241,8 +241,10 @@ hipError_t launch_gemm(const GemmPlan& p, AMode am, EMode em, const GemmArgs& a,
 // The step boundary in one launch (query groups whose action_out takes the register-resident K
 // split, up to 4800 rows): v = action_out's arguments (A = fp16(h), lda = 768; no final
 // output; the state of step k is read from v.x), t = the next step's time_in arguments (the
-// state of step k + 1 is written to t.x, which must be another buffer).
-hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, hipStream_t s);
+// state of step k + 1 is written to t.x, which must be another buffer).  o: the time MLP's
+// second layer too (its arguments; groups of at most kBoundaryTimeOutMaxRows rows), or nullptr.
+constexpr int kBoundaryTimeOutMaxRows = 64;
+hipError_t launch_step_boundary(const GemmArgs& v, const GemmArgs& t, const GemmArgs* o, hipStream_t s);
 hipError_t launch_attention(bool self_layer, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float2* tab, int n_pos, float theta, hipStream_t s);

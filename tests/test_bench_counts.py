@@ -119,12 +119,13 @@ class _FakeLib:
 def test_launch_counts_per_call_match_the_kernel_traces():
     """Launches per call of the 16-layer, 10-step loop as bench.py counts them (the prologue, then
     every timed kernel's launches per call), against the dispatches per call the rocprofv3 traces
-    of the library show: batch 1 742 (the step boundary one launch from the first step to the
-    last, the cross layers' Q projection inside attention), batch 64 1643 (two groups of 32, each
+    of the library show: batch 1 733 (the step boundary, with both time-MLP layers of the next
+    step, one launch from the first step to the last; the cross layers' Q projection inside
+    attention), batch 64 1643 (two groups of 32, each
     with its step boundary in one launch; the cross layers' Q projection a launch of its own),
     batch 128 1643 (two groups of 64 at 3200 rows, the boundary still one launch)."""
     import types
     cfg = types.SimpleNamespace(n_steps=10)
-    for B, want in ((1, 742), (64, 1643), (128, 1643)):
+    for B, want in ((1, 733), (64, 1643), (128, 1643)):
         kern = bench.kernel_table(_FakeLib(), None, cfg, 16, B, [177] * B, 177, 1)
         assert 1 + sum(v["launches_per_call"] for v in kern.values()) == want, B
