@@ -2196,9 +2196,9 @@ struct StreamStage {
 };
 
 // The same streamed attention with the K/V blocks staged through registers into two LDS
-// stages: while block j is multiplied, block j + 1 is already in LDS and block j + 2 is in
-// flight in registers, stored to LDS after block j (keys that are not attended zeroed on the
-// way, the mask bytes loaded with them).  With direct global->LDS loads in flight the compiler
+// stages: while block j is multiplied from one stage, block j + 1 is in flight in registers and
+// is stored into the other stage after block j (keys that are not attended zeroed on the way,
+// from the key-kind table), then block j + 2's loads are issued.  With direct global->LDS loads in flight the compiler
 // makes the block's LDS reads (the transposing V^T reads among them) wait for every load, so the
 // next block's loads never overlapped the current block's arithmetic; register loads carry no
 // such wait.  Same scores, same sums, same bits as attn_pipe_kernel.
