@@ -54,6 +54,15 @@ def test_fp8_denoise_batch8_overwrite_full_batch(ex16_w8):
     compare(gpu, run_oracle(ex16_w8, wl, q, d=7), q, wl["noise"], "8-bit b8 overwrite 7", d=7)
 
 
+def test_fp8_denoise_batch1_overwrite(ex16_w8):
+    """Batch 1 with 8-bit weights and 7 overwritten rows: the step-boundary launch with both
+    time-MLP layers of the next step reads the 8-bit codes of action_out and of both layers."""
+    _say("8-bit weights: denoise at batch 1 with 7 overwritten rows")
+    wl = synth.make_workload("expert16_b128_p177_ow7", batch=1, with_weights=False)
+    gpu = run_gpu(ex16_w8, to_device(wl), d=7)
+    compare(gpu, run_oracle(ex16_w8, wl, [0], d=7), [0], wl["noise"], "8-bit b1 overwrite 7", d=7)
+
+
 def test_fp8_velocity_ragged_batch3_two_layers():
     """One velocity evaluation through a self and a cross layer, batch 3 with ragged prefixes,
     at t = 1 and an off-schedule t, gains drawn away from 1 (the fold into the quantized rows)."""

@@ -333,6 +333,21 @@ def test_edge_full_overwrite_and_four_steps():
         ex.close()
 
 
+def test_batch1_boundary_with_time_mlp_overwrite_four_steps():
+    """Batch 1: the step-boundary launch runs action_out, the Euler update, the overwrite and both
+    layers of the next step's time MLP (its hidden layer kept in LDS); with 7 overwritten rows
+    and 4 Euler steps, against the oracle per step."""
+    _say("batch 1, step boundary with both time-MLP layers: d = 7, 4 Euler steps")
+    ex = Expert(4, n_steps=4, max_batch=1, max_prefix=256)
+    try:
+        wl = synth.make_workload("expert4_b1_p177", batch=1, with_weights=False)
+        wl["prev_actions"] = synth.draw_prev_actions(1, 7)
+        gpu = run_gpu(ex, to_device(wl), d=7)
+        compare(gpu, run_oracle(ex, wl, [0], d=7), [0], wl["noise"], "b1 d=7 n=4", d=7)
+    finally:
+        ex.close()
+
+
 def test_gain_variant_parity():
     _say("RMSNorm gains 1 + N(0, 0.1)")
     ex = Expert(4, max_batch=4, max_prefix=256, gain_seed=synth.gen.SEED_GAINS)
