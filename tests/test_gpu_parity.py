@@ -348,6 +348,27 @@ def test_batch1_boundary_with_time_mlp_overwrite_four_steps():
         ex.close()
 
 
+def test_step_counts_one_three_and_sixty_four():
+    """Step counts at the ends of the accepted range and an odd one, 7 overwritten rows: one step
+    (no step-boundary launch at all: the first step's time MLP, then the last step's action_out),
+    three (the state moves between its two buffers twice and the last step reads the first buffer
+    again) and 64, the largest; batch 1 (the boundary launch runs both time-MLP layers) and, for
+    1 and 3 steps, batch 3 (the first layer only); against the oracle per step."""
+    for n in (1, 3, 64):
+        ex = Expert(4, n_steps=n, max_batch=4, max_prefix=256)
+        try:
+            for B in ((1, 3) if n < 64 else (1,)):
+                _say(f"step count n = {n}, batch {B}, d = 7")
+                wl = synth.make_workload("expert4_b1_p177", batch=B, with_weights=False)
+                wl["prev_actions"] = synth.draw_prev_actions(B, 7)
+                gpu = run_gpu(ex, to_device(wl), d=7)
+                assert gpu["vel"].shape[0] == n
+                q = list(range(B))
+                compare(gpu, run_oracle(ex, wl, q, d=7), q, wl["noise"], f"b{B} d=7 n={n}", d=7)
+        finally:
+            ex.close()
+
+
 def test_gain_variant_parity():
     _say("RMSNorm gains 1 + N(0, 0.1)")
     ex = Expert(4, max_batch=4, max_prefix=256, gain_seed=synth.gen.SEED_GAINS)
