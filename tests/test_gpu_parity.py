@@ -321,6 +321,30 @@ def test_long_prefixes_take_several_key_rounds(ex4):
         compare(gpu, run_oracle(ex4, wl, q), q, wl["noise"], f"P={P} batch {B} valid {[int(x) for x in wl['lengths'][q]]}")
 
 
+def test_key_block_and_round_boundaries(ex4):
+    """Key counts on either side of a 64-key block and of a staged round (five blocks at batch <= 8):
+    self layers see P + 50 keys, cross layers P.  Batch 2: P = 14 (self 64, one whole block), 64
+    (cross one whole block), 78 (self 128), 270 (self 320, one whole round), 271 (self 321: the
+    second round holds only the last chunk key), 320 (cross one whole round), 321 (cross 321);
+    batch 16 (the streamed kernel): P = 206 (self 256) and 257 (cross 257).  Each second query has a
+    shorter valid prefix; NaN in every masked slot."""
+    cases = ((14, 2, [14, 13]), (64, 2, [64, 63]), (78, 2, [78, 1]), (270, 2, [270, 269]),
+             (271, 2, [271, 200]), (320, 2, [320, 319]), (321, 2, [321, 1]), (206, 16, None), (257, 16, None))
+    for P, B, lens in cases:
+        _say(f"key boundaries: P = {P}, batch {B}")
+        wl = synth.make_workload("expert4_b1_p177", batch=B, with_weights=False)
+        wl["prefix_kv"] = synth.draw_prefix_kv(4, B, P, seed=91 + P)
+        wl["prefix_len"] = P
+        if lens is None:
+            lens = [P] + [int(x) for x in synth.draw_lengths(B - 1, P - 63, P, seed=93 + P)]
+        wl["mask"] = synth.make_mask(B, P, lens)
+        wl["lengths"] = wl["mask"].sum(axis=1)
+        _nan_pads(wl)
+        gpu = run_gpu(ex4, to_device(wl))
+        q = [0, 1] if B == 2 else [0, int(np.argmin(wl["lengths"]))]
+        compare(gpu, run_oracle(ex4, wl, q), q, wl["noise"], f"P={P} batch {B} valid {[int(x) for x in wl['lengths'][q]]}")
+
+
 def test_edge_full_overwrite_and_four_steps():
     _say("edge cases: d = 50, 4 Euler steps")
     ex = Expert(4, n_steps=4, max_batch=4, max_prefix=256)
