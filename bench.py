@@ -26,7 +26,7 @@ MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 RIDGE = MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 DEFAULT_WORKLOAD = "expert16_b1_p177"
-LARGE_BATCH_WORKLOADS = ("expert16_b64_p257", "expert16_b128_p177_ow7")
+LARGE_BATCH_WORKLOADS = ("expert16_b64_p257", "expert16_b128_p177_ow7", "expert16_b16_pvar241")
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
