@@ -106,17 +106,19 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 // ----------------------------------------------------------------------------
 // GEMM
 // ----------------------------------------------------------------------------
-// Three kernels share the A-operand loaders and the epilogues:
-//  * gemm_skinny (M <= 64, one query): one 512-thread workgroup per 16 output
-//    columns and 16-row block.  Its 8 waves split K; each wave issues every
-//    load it needs (its weight fragments and A fragments) at once, so the
-//    kernel waits for memory about once, then the waves' partial tiles meet in
-//    LDS.
-//  * gemm_tiled (M > 64): 64/128 x 128 output tiles, four waves, BK = 64 slabs
-//    double-buffered in LDS through registers.
-//  * gemm_big (M > 64, K % 64 == 0): 128 x 128 tiles, eight waves, an LDS ring
+// Three kernels share the A-operand loaders and the epilogues (plan_for picks one per
+// projection and row count):
+//  * gemm_skinny (one query at batch 1; up to a few thousand rows for the narrow
+//    products): one 512-thread workgroup per 1, 2 or 4 16-column blocks and 1, 2 or 4
+//    16-row blocks.  Its 8 waves split K; each wave issues every load it needs (its
+//    weight fragments and A fragments) at once, so the kernel waits for memory about
+//    once, then the waves' partial tiles meet in LDS.
+//  * gemm_tiled: 64/128 x 128 output tiles, four waves, BK = 64 slabs
+//    double-buffered in LDS through registers (the time MLP at large row counts).
+//  * gemm_big (K a multiple of its 32- or 64-column slab): 64 or 128 x 128 tiles, eight waves, an LDS ring
 //    filled by direct global->LDS loads.
-// Epilogues run on the finished fp32 tile staged in LDS.
+// Epilogues run on the finished fp32 tile, staged in LDS or (the residual projections)
+// taken from the waves' partials or accumulators.
 //
 // Weight row order inside each 16-row block (set by the host when it loads
 // the weights) keeps every pair an epilogue needs in one block:
@@ -366,13 +368,12 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* sC
   }
 }
 
-// M <= 64.  A workgroup computes 16 output columns for RB 16-row blocks
-// (rows m0 .. m0 + 16 RB - 1); wave w takes k-steps w*KPW .. w*KPW+KPW-1 (32
-// wide each).  What bounds these launches is the bytes one workgroup streams
-// through its CU (A rows + 16 weight rows), so the rows of a small batch are
-// split over 64 / (16 RB) workgroups per column block.  The workgroups of one
-// column block sit on one XCD (workgroup i runs on XCD i % 8), so that XCD's
-// L2 fetches those weight rows once.  A_NORM: the rows of fp16(h) go to the
+// A workgroup computes CB 16-column blocks for RB 16-row blocks (rows m0 .. m0 + 16 RB - 1);
+// wave w takes k-steps w*KPW .. w*KPW+KPW-1 (32 wide each), so every fragment of the
+// product stays in registers (K <= 8 x KPW x 32).  What bounds these launches is the bytes
+// one workgroup streams through its CU (its A rows and weight rows), so the rows are split
+// over row tiles of 16 RB rows per column-block group.  The row tiles of one group sit on one
+// XCD (workgroup i runs on XCD i % 8), so that XCD's L2 fetches those weight rows once.  A_NORM: the rows of fp16(h) go to the
 // MFMA unscaled, so no load waits on the row scale; each wave also sums the
 // squares of its slice of every row, and 1/rms(row) scales the finished sums
 // (a per-row constant, so this equals normalising first up to rounding).
