@@ -137,3 +137,26 @@ def test_fp8_noalloc_matches_denoise():
         np.testing.assert_array_equal(g, r)
     finally:
         ex.close()
+
+
+def test_fp8_key_round_boundaries_three_steps_overwrite():
+    """8-bit weights on a 4-layer expert with three Euler steps and 7 overwritten rows, at prefix
+    lengths on either side of a staged key round: P = 270 (self layers 320 keys, one whole round)
+    and 321 (cross layers 321 keys: the second round holds one key); the second query's valid
+    prefix is shorter and every masked slot holds NaN."""
+    ex = Expert(4, n_steps=3, max_batch=2, max_prefix=512, weight_format=E4M3)
+    try:
+        for P, lens in ((270, [270, 135]), (321, [321, 160])):
+            _say(f"8-bit weights: P = {P}, 3 Euler steps, d = 7")
+            wl = synth.make_workload("expert4_b1_p177", batch=2, with_weights=False)
+            wl["prefix_kv"] = synth.draw_prefix_kv(4, 2, P, seed=97 + P)
+            wl["prefix_len"] = P
+            wl["mask"] = synth.make_mask(2, P, lens)
+            wl["lengths"] = wl["mask"].sum(axis=1)
+            wl["prev_actions"] = synth.draw_prev_actions(2, 7)
+            for b, p in zip(*np.nonzero(wl["mask"] == 0)):
+                wl["prefix_kv"][:, :, b, :, p, :] = 0x7FC0   # bf16 NaN in every masked slot
+            gpu = run_gpu(ex, to_device(wl), d=7)
+            compare(gpu, run_oracle(ex, wl, [0, 1], d=7), [0, 1], wl["noise"], f"8-bit P={P} n=3 d=7", d=7)
+    finally:
+        ex.close()
