@@ -34,6 +34,8 @@ KERNEL_SYMBOLS = {       # kernel name fragments in a rocprofv3 trace, per timed
     "qkv_self": "gemm_skinny<1, 4,", "attn_self": "attn_small_kernel<true,", "attn_cross": "attn_cross_q_kernel<",
     "o": "gemm_skinny<0, 3, 4,", "gate_up": "gemm_skinny<1, 5,", "down": "gemm_skinny<0, 3, 8,",
     "action_out": "step_boundary_kernel<", "time_in": "gemm_skinny<2, 1,", "time_out": "gemm_skinny<0, 2,",
+    # the pipelined 128 x 128 gate/up of the large batches (traffic counters only)
+    "gate_up_big": "gemm_big<5, true, 128,",
 }
 
 
