@@ -438,7 +438,10 @@ def large_batch_entry(fm, h, cfg, wl, calls, warmup, reps, stream):
          "loop_tflops": lf / (med * 1e-3) / 1e12, "loop_mfma_frac": lf / (med * 1e-3) / (MFMA_F16_PEAK_TFS * 1e12),
          "dominant_kernel": {"kernel": dom_name, "avg_us": dom["avg_us"], "us_per_call": dom["us_per_call"],
                              "tflops": dom["flops"] / (dom["avg_us"] * 1e-6) / 1e12,
-                             "mfma_frac": dom["flops"] / (dom["avg_us"] * 1e-6) / (MFMA_F16_PEAK_TFS * 1e12)},
+                             "mfma_frac": dom["flops"] / (dom["avg_us"] * 1e-6) / (MFMA_F16_PEAK_TFS * 1e12),
+                             # fabric bytes per launch from the calibrated FETCH/WRITE counters, where
+                             # profiles/ holds them for this workload and the current kernel sources
+                             "traffic": stored_traffic(wl["name"], "gate_up_big") if dom_name == "gate_up" else None},
          "kernels": {k: {"avg_us": v["avg_us"], "us_per_call": v["us_per_call"],
                          "mfma_frac": v["flops"] / (v["avg_us"] * 1e-6) / (MFMA_F16_PEAK_TFS * 1e12)}
                      for k, v in kern.items()}}
